@@ -1,0 +1,204 @@
+"""Float64 CPU oracle for the quantized expert-FFN MoE layer.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow definition that the
+GPU library is checked against.  Only the test suite, the smoke check in
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+it; the library under ``quantized_expert_ffn_moe_amd/`` never does, and this
+module imports nothing from that package.
+
+What it computes, and where the pages say so
+--------------------------------------------
+* Router: a softmax over all routed experts' logits, the top 6 picked greedily,
+  no renormalisation of the picked weights (browser demo page "A
+  3-billion-parameter OCR model. In this tab.", section "One forward pass, left
+  to right", step 6; franken_ocr README, section "Architecture": router 1280 to
+  64, top 6 of 64).
+* Experts: SiLU-gated (SwiGLU) MLPs 1280 -> 896 -> 1280, plus two always-on
+  shared experts fused into one SwiGLU of intermediate 1792 (same passages; the
+  README's "focr convert" section counts the FFN/expert matrices, which fixes
+  one fused shared triple per layer).
+* Weights: integer codes, int4 as two's-complement nibbles or int8, each group
+  of consecutive weights sharing one f32 scale (demo page, section "Four bits,
+  one shared scale"; README, "CPU Backend and Optimizations", quantisation
+  policy: router and norms stay high precision).
+* RMSNorm of the residual stream before each chained layer (the decoder's
+  RMSNorm, demo page step 7; README "Architecture").
+
+Readings where the pages are silent (each restated where it is used):
+ties in the greedy pick go to the lower expert index; the ids are returned in
+pick order; a group runs along the reduction axis K from column 0; codes are
+symmetric (W = s * q, no zero point); SiLU(v) = v * sigmoid(v) applied to the
+gate projection, multiplied by the up projection; RMSNorm has no learned gain
+(gamma = 1) with eps inside the square root; in bf16-input chains the layer
+input is the RMSNorm output rounded to bf16 (nearest, ties to even).
+
+Parity pins: every function here is checked in ``tests/test_oracle.py`` against
+closed forms, brute force, library routines on special cases, invariants and a
+hand-worked fixture (``tests/golden/tiny_layer.json``); none is unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+f64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# rounding and normalisation
+# --------------------------------------------------------------------------
+def bf16_round(a) -> np.ndarray:
+    """Round to the nearest bfloat16 value, ties to even, computed exactly in f64.
+
+    bfloat16 keeps 8 significant bits.  With a = m * 2**e and 0.5 <= |m| < 1,
+    m * 256 is an exact f64 value whose integer part is the kept significand;
+    ``np.rint`` rounds half to even.  (Normal range only; the workloads never
+    reach bf16 subnormals.)
+    """
+    a = np.asarray(a, dtype=f64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def rmsnorm(h, eps: float) -> np.ndarray:
+    """z = h / sqrt(mean(h^2) + eps) over the last axis (gamma = 1)."""
+    h = np.asarray(h, dtype=f64)
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    return h / np.sqrt(ms + eps)
+
+
+# --------------------------------------------------------------------------
+# router
+# --------------------------------------------------------------------------
+def router_logits(X, router_w, router_b=None) -> np.ndarray:
+    """l[t, e] = sum_k W_r[e, k] * x[t, k] (+ b[e]) for every token."""
+    X = np.atleast_2d(np.asarray(X, dtype=f64))
+    logits = X @ np.asarray(router_w, dtype=f64).T
+    if router_b is not None:
+        logits = logits + np.asarray(router_b, dtype=f64)[None, :]
+    return logits
+
+
+def softmax(logits) -> np.ndarray:
+    """p_e = exp(l_e - m) / sum_j exp(l_j - m), m = max_j l_j, over all experts."""
+    logits = np.atleast_2d(np.asarray(logits, dtype=f64))
+    m = logits.max(axis=1, keepdims=True)
+    ex = np.exp(logits - m)
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
+def greedy_topk(P, k: int):
+    """k rounds of "take the largest remaining probability".
+
+    ``np.argmax`` returns the first index among equal maxima, so a tie goes to
+    the lower expert index.  Ids come back in pick order; the weights are the
+    picked probabilities themselves (no renormalisation, no scaling).
+    """
+    P = np.atleast_2d(np.asarray(P, dtype=f64))
+    T, E = P.shape
+    remaining = P.copy()
+    ids = np.empty((T, k), dtype=np.int32)
+    for i in range(k):
+        pick = np.argmax(remaining, axis=1)
+        ids[:, i] = pick
+        remaining[np.arange(T), pick] = -np.inf
+    w = np.take_along_axis(P, ids.astype(np.int64), axis=1)
+    return ids, w
+
+
+# --------------------------------------------------------------------------
+# quantised weights and the expert FFN
+# --------------------------------------------------------------------------
+def dequantize(codes, scales, group: int) -> np.ndarray:
+    """W[r, c] = S[r, c // group] * Q[r, c] in f64 (exact: at most 32 significant bits)."""
+    Q = np.asarray(codes)
+    S = np.asarray(scales, dtype=np.float32)
+    N, K = Q.shape
+    if K % group or S.shape != (N, K // group):
+        raise ValueError(f"codes {Q.shape} / scales {S.shape} do not match group {group}")
+    return Q.astype(f64) * np.repeat(S.astype(f64), group, axis=1)
+
+
+def silu(v) -> np.ndarray:
+    """SiLU(v) = v * sigmoid(v) = v / (1 + exp(-v))."""
+    v = np.asarray(v, dtype=f64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu_ffn(Wg, Wu, Wd, X) -> np.ndarray:
+    """y = W_d (SiLU(W_g x) * (W_u x)) for each row x of X."""
+    X = np.atleast_2d(np.asarray(X, dtype=f64))
+    g = X @ Wg.T
+    u = X @ Wu.T
+    return (silu(g) * u) @ Wd.T
+
+
+def expert_weights(layer: dict, e: int):
+    """Dequantised (W_g, W_u, W_d) of routed expert e."""
+    G = layer["routed_fmt"].group
+    return (dequantize(layer["gate_q"][e], layer["gate_s"][e], G),
+            dequantize(layer["up_q"][e], layer["up_s"][e], G),
+            dequantize(layer["down_q"][e], layer["down_s"][e], G))
+
+
+def shared_weights(layer: dict):
+    """Dequantised (W_g, W_u, W_d) of the fused shared expert."""
+    G = layer["shared_fmt"].group
+    return (dequantize(layer["shared_gate_q"], layer["shared_gate_s"], G),
+            dequantize(layer["shared_up_q"], layer["shared_up_s"], G),
+            dequantize(layer["shared_down_q"], layer["shared_down_s"], G))
+
+
+# --------------------------------------------------------------------------
+# the layer and the chain
+# --------------------------------------------------------------------------
+def moe_layer(X, layer: dict, top_k: int = 6, forced_ids=None):
+    """One MoE layer over the rows of X.
+
+    y[t] = FFN_shared(x_t) + sum_i w[t, i] * FFN_{ids[t, i]}(x_t)
+
+    Returns (ids [T,k] int32, w [T,k] f64, y [T,H] f64, P [T,E] f64).  With
+    ``forced_ids`` the routing decision is taken from the caller (used when a
+    near-tie admits two correct answers); w is still this oracle's own
+    probability of each forced expert.
+    """
+    X = np.atleast_2d(np.asarray(X, dtype=f64))
+    T = X.shape[0]
+    P = softmax(router_logits(X, layer["router_w"], layer.get("router_b")))
+    if forced_ids is None:
+        ids, w = greedy_topk(P, top_k)
+    else:
+        ids = np.asarray(forced_ids, dtype=np.int32).reshape(T, -1)
+        w = np.take_along_axis(P, ids.astype(np.int64), axis=1)
+
+    Y = swiglu_ffn(*shared_weights(layer), X)
+    routed = {}
+    for e in np.unique(ids):
+        rows = np.nonzero((ids == e).any(axis=1))[0]
+        Ye = swiglu_ffn(*expert_weights(layer, int(e)), X[rows])
+        routed[int(e)] = dict(zip(rows.tolist(), Ye))
+    for t in range(T):
+        for i in range(ids.shape[1]):
+            Y[t] = Y[t] + w[t, i] * routed[int(ids[t, i])][t]
+    return ids, w, Y, P
+
+
+def moe_chain(X0, layers, eps: float, norm_bf16: bool, top_k: int = 6,
+              forced_ids=None):
+    """Layers chained on a residual stream.
+
+    h_0 = x; for each layer l: z = RMSNorm(h_{l-1}) (rounded to bf16 when
+    ``norm_bf16``), h_l = h_{l-1} + MoE_l(z).  Returns h_L and the per-layer
+    (ids, w, z) so that callers can check each layer on its own.
+    """
+    h = np.atleast_2d(np.asarray(X0, dtype=f64))
+    trace = []
+    for li, layer in enumerate(layers):
+        z = rmsnorm(h, eps)
+        if norm_bf16:
+            z = bf16_round(z)
+        fi = None if forced_ids is None else forced_ids[li]
+        ids, w, y, _ = moe_layer(z, layer, top_k, fi)
+        h = h + y
+        trace.append((ids, w, z))
+    return h, trace

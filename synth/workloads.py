@@ -1,0 +1,184 @@
+"""Workload definitions and seeded generators.
+
+Shapes follow the decoder described on the franken_ocr pages: hidden 1280,
+64 routed experts with top-6 routing, expert intermediate 896 and the two
+shared experts fused into one SwiGLU of intermediate 1792 ("DeepSeek-V2 MoE
+decoder" in the Architecture section of the franken_ocr README; "One forward
+pass, left to right", step 6, of the browser demo page).  The five workloads
+are the synthetic stand-ins for the pages' workloads: one decode token, the
+11-layer decode step, 32 concurrent pages, the 273-row visual prefill
+(splice layout in the I/O contract of the Unlimited-OCR DeepEncoder ONNX
+model card) and an 8-page multi-page prefill.
+
+Every tensor comes from its own numpy ``SeedSequence(0, spawn_key=(w, l, t))``
+stream (w = workload index, l = layer, t = tensor id), so any layer can be
+regenerated alone and a smaller token count is a prefix of nothing: tokens
+are drawn from their own stream keyed by the batch index.
+
+Codes are returned unpacked, one signed code per int8 byte, row-major
+``[rows][K]`` with K the reduction axis; scales are float32 ``[rows][K/G]``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+HIDDEN = 1280
+N_EXPERTS = 64
+TOP_K = 6
+INTER = 896
+SHARED_INTER = 1792
+NORM_EPS = 1e-6
+
+# tensor ids inside one layer's seed space
+_T_ROUTER, _T_BIAS = 0, 1
+_T_GATE, _T_UP, _T_DOWN = 2, 3, 4
+_T_GATE_S, _T_UP_S, _T_DOWN_S = 5, 6, 7
+_T_SGATE, _T_SUP, _T_SDOWN = 8, 9, 10
+_T_SGATE_S, _T_SUP_S, _T_SDOWN_S = 11, 12, 13
+_TOKEN_LAYER = 0xFFFF  # "layer" slot used for token batches
+
+
+@dataclass(frozen=True)
+class QFmt:
+    bits: int   # 4 or 8
+    group: int  # consecutive K elements that share one f32 scale
+
+    @property
+    def code_range(self):
+        return (-8, 7) if self.bits == 4 else (-127, 127)
+
+
+@dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    n_tokens: int
+    n_layers: int
+    x_dtype: str            # "f32" or "bf16"
+    routed: QFmt
+    shared: QFmt
+    bias: str               # "none", "normal1.5" or "zipf2"
+    chained: bool           # RMSNorm before each layer + residual add
+    norm_bf16: bool         # layer input rounded to bf16 after the norm
+
+    def with_tokens(self, n: int) -> "Workload":
+        return replace(self, n_tokens=n)
+
+    def with_layers(self, n: int) -> "Workload":
+        return replace(self, n_layers=n)
+
+
+WORKLOADS = [
+    Workload(0, "decode_1tok_1layer_int8g128", 1, 1, "f32",
+             QFmt(8, 128), QFmt(8, 128), "none", False, False),
+    Workload(1, "decode_1tok_11layers_int4g64_shared_int8g128", 1, 11, "f32",
+             QFmt(4, 64), QFmt(8, 128), "none", True, False),
+    Workload(2, "batched_decode_32tok_int4g32_biased", 32, 1, "bf16",
+             QFmt(4, 32), QFmt(4, 32), "normal1.5", False, False),
+    Workload(3, "visual_prefill_273tok_int4g128", 273, 1, "bf16",
+             QFmt(4, 128), QFmt(4, 128), "none", False, False),
+    Workload(4, "multipage_prefill_2184tok_11layers_int4g64_zipf", 2184, 11, "bf16",
+             QFmt(4, 64), QFmt(4, 64), "zipf2", True, True),
+]
+
+
+def workload(i: int) -> Workload:
+    return WORKLOADS[i]
+
+
+def _rng(w: int, layer: int, tensor: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(0, spawn_key=(w, layer, tensor)))
+
+
+def _codes(rng, shape, fmt: QFmt) -> np.ndarray:
+    lo, hi = fmt.code_range
+    return rng.integers(lo, hi, size=shape, endpoint=True, dtype=np.int8)
+
+
+def _scales(rng, shape) -> np.ndarray:
+    return rng.uniform(0.002, 0.02, size=shape).astype(np.float32)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even) and return the 16-bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def make_tokens(wl: Workload, batch: int = 0, n_tokens: int | None = None):
+    """Input activations of one batch: (values f32 [T,H], bf16 bits or None)."""
+    T = wl.n_tokens if n_tokens is None else n_tokens
+    x = _rng(wl.index, _TOKEN_LAYER, batch).standard_normal((T, HIDDEN)).astype(np.float32)
+    if wl.x_dtype == "bf16":
+        bits = f32_to_bf16_bits(x)
+        return bf16_bits_to_f32(bits), bits
+    return x, None
+
+
+def _bias(wl: Workload, layer: int):
+    if wl.bias == "none":
+        return None
+    if wl.bias == "normal1.5":
+        return _rng(wl.index, layer, _T_BIAS).normal(0.0, 1.5, N_EXPERTS).astype(np.float32)
+    if wl.bias == "zipf2":
+        rank = np.arange(1, N_EXPERTS + 1, dtype=np.float64)
+        return (2.0 * np.log(1.0 / rank)).astype(np.float32)
+    raise ValueError(wl.bias)
+
+
+def make_layer(wl: Workload, layer: int) -> dict:
+    """All tensors of one MoE layer (layer counts from 0 within the workload)."""
+    w, l = wl.index, layer
+    E, H, I, Is = N_EXPERTS, HIDDEN, INTER, SHARED_INTER
+    rf, sf = wl.routed, wl.shared
+    d = {
+        "router_w": (_rng(w, l, _T_ROUTER).standard_normal((E, H)) * 0.02).astype(np.float32),
+        "router_b": _bias(wl, l),
+        "gate_q": _codes(_rng(w, l, _T_GATE), (E, I, H), rf),
+        "up_q": _codes(_rng(w, l, _T_UP), (E, I, H), rf),
+        "down_q": _codes(_rng(w, l, _T_DOWN), (E, H, I), rf),
+        "gate_s": _scales(_rng(w, l, _T_GATE_S), (E, I, H // rf.group)),
+        "up_s": _scales(_rng(w, l, _T_UP_S), (E, I, H // rf.group)),
+        "down_s": _scales(_rng(w, l, _T_DOWN_S), (E, H, I // rf.group)),
+        "shared_gate_q": _codes(_rng(w, l, _T_SGATE), (Is, H), sf),
+        "shared_up_q": _codes(_rng(w, l, _T_SUP), (Is, H), sf),
+        "shared_down_q": _codes(_rng(w, l, _T_SDOWN), (H, Is), sf),
+        "shared_gate_s": _scales(_rng(w, l, _T_SGATE_S), (Is, H // sf.group)),
+        "shared_up_s": _scales(_rng(w, l, _T_SUP_S), (Is, H // sf.group)),
+        "shared_down_s": _scales(_rng(w, l, _T_SDOWN_S), (H, Is // sf.group)),
+        "routed_fmt": rf,
+        "shared_fmt": sf,
+    }
+    return d
+
+
+def make_tiny_layer(seed: int, E: int, H: int, I: int, Is: int, fmt: QFmt,
+                    shared_fmt: QFmt | None = None, bias_std: float = 0.0) -> dict:
+    """A small layer of arbitrary shape for oracle tests (same tensor names)."""
+    sf = shared_fmt or fmt
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(99,)))
+    return {
+        "router_w": (rng.standard_normal((E, H)) * 0.5).astype(np.float32),
+        "router_b": (rng.normal(0, bias_std, E).astype(np.float32) if bias_std else None),
+        "gate_q": _codes(rng, (E, I, H), fmt),
+        "up_q": _codes(rng, (E, I, H), fmt),
+        "down_q": _codes(rng, (E, H, I), fmt),
+        "gate_s": _scales(rng, (E, I, H // fmt.group)),
+        "up_s": _scales(rng, (E, I, H // fmt.group)),
+        "down_s": _scales(rng, (E, H, I // fmt.group)),
+        "shared_gate_q": _codes(rng, (Is, H), sf),
+        "shared_up_q": _codes(rng, (Is, H), sf),
+        "shared_down_q": _codes(rng, (H, Is), sf),
+        "shared_gate_s": _scales(rng, (Is, H // sf.group)),
+        "shared_up_s": _scales(rng, (Is, H // sf.group)),
+        "shared_down_s": _scales(rng, (H, Is // sf.group)),
+        "routed_fmt": fmt,
+        "shared_fmt": sf,
+    }
