@@ -1,0 +1,166 @@
+/*
+ * moe.h -- C ABI of the quantized expert-FFN MoE layer library (libmoe.so).
+ *
+ * The layer is the mixture-of-experts FFN of the Unlimited-OCR DeepSeek-V2
+ * decoder: hidden 1280, a softmax router over 64 routed experts, the top 6
+ * picked greedily with no renormalisation, SiLU-gated (SwiGLU) experts of
+ * intermediate 896, and two always-on shared experts fused into one SwiGLU of
+ * intermediate 1792, all combined with the router weights.  Sources: browser
+ * demo page "A 3-billion-parameter OCR model. In this tab.", section "One
+ * forward pass, left to right", step 6; franken_ocr README, sections
+ * "Architecture" and "Design Philosophy" (fixed dimensions: 64 experts, top-6,
+ * MoE intermediate 896, hidden 1280).  Expert weights are integer codes, int4
+ * two's-complement nibbles or int8, with one f32 scale per group of
+ * consecutive weights along the reduction axis (demo page, section "Four bits,
+ * one shared scale"; README "CPU Backend and Optimizations", quantisation
+ * policy: router and norms stay high precision, so the router is f32 here).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Shapes are fixed (the MOE_* constants below); other shapes are rejected.
+ * - Device pointers are plain device addresses (e.g. torch.Tensor.data_ptr()).
+ *   The caller owns every buffer; the library never allocates, frees or keeps
+ *   a pointer after the call returns.
+ * - GPU entry points are stream ordered: they validate on the host, enqueue
+ *   kernels on `stream` (a hipStream_t; NULL = the default stream) and return
+ *   without synchronising.  Launch errors are reported as MOE_E_HIP.
+ * - Errors are status codes, never exceptions or aborts.  All argument checks
+ *   happen before anything is enqueued, so a non-OK status means nothing ran.
+ * - Calls are re-entrant; concurrent calls need distinct workspaces.
+ * - All device pointers must be 16-byte aligned (MOE_E_ALIGN otherwise).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_HIDDEN 1280
+#define MOE_EXPERTS 64
+#define MOE_TOPK 6
+#define MOE_INTER 896
+#define MOE_SHARED_INTER 1792
+#define MOE_MAX_TOKENS 8192
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_NULLPTR = 1,   /* a required pointer is NULL */
+  MOE_E_SHAPE = 2,     /* token count or intermediate size out of range */
+  MOE_E_FORMAT = 3,    /* bits not in {4, 8}, group not in {32, 64, 128}, or a code out of range */
+  MOE_E_ALIGN = 4,     /* a device pointer is not 16-byte aligned */
+  MOE_E_WORKSPACE = 5, /* workspace smaller than moe_workspace_bytes() */
+  MOE_E_HIP = 6,       /* the HIP runtime reported an error while enqueueing */
+  MOE_E_ARG = 7        /* any other invalid argument (dtype, flags, aliasing) */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* moe_layer_forward flags */
+enum {
+  /* y += layer(x) instead of y = layer(x): the residual add of a chained
+     decoder.  x may then be the same buffer as y (in-place residual stream). */
+  MOE_ACCUMULATE = 1u,
+  /* The layer input is RMSNorm(x) = x / sqrt(mean(x^2) + eps) with eps =
+     1e-6 and no learned gain, computed inside the call (the decoder's RMSNorm;
+     demo page step 7).  Requires x in f32. */
+  MOE_NORM_INPUT = 2u,
+  /* With MOE_NORM_INPUT: round the normalised input to bf16 (nearest, ties to
+     even) before it reaches the router and the experts. */
+  MOE_NORM_BF16 = 4u,
+  /* Force the per-token GEMV path / the grouped MFMA path regardless of the
+     token count (both give the same result up to fp32 rounding order). */
+  MOE_FORCE_DECODE = 8u,
+  MOE_FORCE_GROUPED = 16u
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_str(int32_t status);
+
+/* ------------------------------------------------------------------------
+ * Weight packing (host memory in, host memory out; no GPU involved).
+ *
+ * Canonical input layout of one expert (routed: inter = 896; the fused
+ * shared expert: inter = 1792):
+ *   gate codes [inter][1280], up codes [inter][1280], down codes [1280][inter],
+ *   one signed code per int8 byte, row-major, K (the reduction axis) last;
+ *   scales gate [inter][1280/G], up [inter][1280/G], down [1280][inter/G] f32,
+ *   scale (r, g) applying to codes (r, g*G .. g*G+G-1)  (W = scale * code,
+ *   no zero point).
+ * int4 codes must lie in [-8, 7]; int8 codes in [-128, 127].
+ *
+ * Packed layout written to codes_out (moe_expert_code_bytes() bytes):
+ *   [gate | up | down], each matrix [N rows][K] stored as 1 KiB tiles of 16
+ *   rows x KB columns (KB = 128 for int4, 64 for int8), tile (nt, kb) at byte
+ *   1024 * (nt * (K/KB) + kb).  Inside a tile, lane l = 0..63 owns bytes
+ *   16l..16l+15 for row 16nt + (l % 16); its four 32-bit words hold, for
+ *   lane group q = l / 16:
+ *     int4: word j = the 8 codes k = 128kb + 32j + 8q + i (i = 0..7) in
+ *           nibble i (bits 4i..4i+3), stored as code + 8;
+ *     int8: word j = the 4 codes k = 64kb + 32(j/2) + 8q + 4(j%2) + i
+ *           (i = 0..3) in byte i, stored as code + 128.
+ * Packed scales written to scales_out (moe_expert_scale_count() floats):
+ *   [gate | up | down], each [N/16][K/G][16]: entry (nt, g, r) = scale of row
+ *   16nt + r, group g.
+ * Experts of a layer are concatenated: expert e at byte e * code_bytes and
+ * float e * scale_count.
+ * ------------------------------------------------------------------------ */
+size_t moe_expert_code_bytes(int32_t bits, int32_t inter);
+size_t moe_expert_scale_count(int32_t group_size, int32_t inter);
+moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t* down,
+                             const float* gate_scales, const float* up_scales,
+                             const float* down_scales, int32_t inter, int32_t bits,
+                             int32_t group_size, void* codes_out, float* scales_out);
+
+/* Bytes of device workspace moe_layer_forward needs for n_tokens tokens. */
+size_t moe_workspace_bytes(int32_t n_tokens);
+
+/* ------------------------------------------------------------------------
+ * One MoE layer over n_tokens tokens (0 <= n_tokens <= MOE_MAX_TOKENS).
+ * With n_tokens == 0 nothing is enqueued and x, y, topk_ids and topk_w may be
+ * NULL; the other arguments are still validated.
+ *
+ *   y[t] (+)= FFN_shared(x'[t]) + sum_{i<6} w[t,i] * FFN_{ids[t,i]}(x'[t])
+ *
+ * x'           = x, or RMSNorm(x) with MOE_NORM_INPUT (see the flags).
+ * x            [n_tokens][1280], dtype x_dtype (MOE_F32 or MOE_BF16).
+ * router_w     [64][1280] f32.  router_b: [64] f32 added to the logits, or NULL.
+ * expert_q     64 packed experts (moe_pack_expert, inter = 896), format
+ *              (expert_bits, expert_group).  expert_scales: their packed scales.
+ * shared_q     the packed fused shared expert (inter = 1792), format
+ *              (shared_bits, shared_group).  shared_scales: its packed scales.
+ * y            [n_tokens][1280] f32 output (read too with MOE_ACCUMULATE).
+ * topk_ids     [n_tokens][6] int32 out: expert ids in pick order (descending
+ *              probability; equal probabilities go to the lower index).
+ * topk_w       [n_tokens][6] f32 out: the picked softmax probabilities (over
+ *              all 64 experts, not renormalised; they sum to at most 1).
+ * workspace    device scratch of at least moe_workspace_bytes(n_tokens)
+ *              bytes; its contents need no initialisation and are garbage
+ *              after the call.
+ * Routing is computed in f32; expert arithmetic multiplies exact integer codes
+ * by the inputs with fp32 accumulation and applies each group scale to the
+ * fp32 partial sum of its group.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
+                               const float* router_w, const float* router_b,
+                               const void* expert_q, const float* expert_scales,
+                               int32_t expert_bits, int32_t expert_group,
+                               const void* shared_q, const float* shared_scales,
+                               int32_t shared_bits, int32_t shared_group,
+                               float* y, int32_t* topk_ids, float* topk_w,
+                               void* workspace, size_t workspace_bytes,
+                               uint32_t flags, void* stream);
+
+/* z[t] = h[t] / sqrt(mean(h[t]^2) + eps) over the 1280 features (no gain);
+ * h [n_tokens][1280] f32, z [n_tokens][1280] of z_dtype (bf16: nearest, ties
+ * to even).  The decoder's RMSNorm (demo page step 7; README "Architecture"). */
+moe_status_t moe_rmsnorm(const float* h, void* z, int32_t z_dtype, int32_t n_tokens,
+                         float eps, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

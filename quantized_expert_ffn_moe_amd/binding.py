@@ -1,0 +1,162 @@
+"""Thin ctypes binding of libmoe.so (the C ABI in include/moe.h).
+
+Argument marshalling only: torch tensors become device addresses and the
+current HIP stream, numpy arrays become host addresses.  Every step of the
+layer runs in the library's own kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HIDDEN, EXPERTS, TOPK, INTER, SHARED_INTER = 1280, 64, 6, 896, 1792
+MOE_F32, MOE_BF16 = 0, 1
+MOE_ACCUMULATE, MOE_NORM_INPUT, MOE_NORM_BF16 = 1, 2, 4
+MOE_FORCE_DECODE, MOE_FORCE_GROUPED = 8, 16
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+EXPORTS = ("moe_status_str", "moe_expert_code_bytes", "moe_expert_scale_count", "moe_pack_expert",
+           "moe_workspace_bytes", "moe_layer_forward", "moe_rmsnorm")
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def load():
+    """Load the in-tree library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MoeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_status_str.argtypes = [i32]
+    L.moe_expert_code_bytes.restype = sz
+    L.moe_expert_code_bytes.argtypes = [i32, i32]
+    L.moe_expert_scale_count.restype = sz
+    L.moe_expert_scale_count.argtypes = [i32, i32]
+    L.moe_pack_expert.restype = i32
+    L.moe_pack_expert.argtypes = [vp] * 6 + [i32, i32, i32, vp, vp]
+    L.moe_workspace_bytes.restype = sz
+    L.moe_workspace_bytes.argtypes = [i32]
+    L.moe_layer_forward.restype = i32
+    L.moe_layer_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32,
+                                    vp, vp, vp, vp, sz, u32, vp]
+    L.moe_rmsnorm.restype = i32
+    L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, ctypes.c_float, vp]
+    _lib = L
+    return L
+
+
+def check(status: int):
+    if status != 0:
+        raise MoeError(load().moe_status_str(status).decode())
+
+
+def _np_ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ----------------------------------------------------------------- packing (host)
+def moe_expert_code_bytes(bits: int, inter: int) -> int:
+    return load().moe_expert_code_bytes(bits, inter)
+
+
+def moe_expert_scale_count(group: int, inter: int) -> int:
+    return load().moe_expert_scale_count(group, inter)
+
+
+def moe_pack_expert(gate, up, down, gate_s, up_s, down_s, bits: int, group: int):
+    """Pack one expert (host numpy in, host numpy out)."""
+    inter = gate.shape[0]
+    arrs = [np.ascontiguousarray(a, dtype=np.int8) for a in (gate, up, down)]
+    scs = [np.ascontiguousarray(a, dtype=np.float32) for a in (gate_s, up_s, down_s)]
+    codes = np.empty(moe_expert_code_bytes(bits, inter), np.uint8)
+    scales = np.empty(moe_expert_scale_count(group, inter), np.float32)
+    check(load().moe_pack_expert(*[_np_ptr(a) for a in arrs], *[_np_ptr(a) for a in scs],
+                                 inter, bits, group, _np_ptr(codes), _np_ptr(scales)))
+    return codes, scales
+
+
+def pack_layer(layer: dict, device="cuda"):
+    """Pack one layer's codes/scales on the host and move them to the device."""
+    import torch
+    rf, sf = layer["routed_fmt"], layer["shared_fmt"]
+    E = layer["gate_q"].shape[0]
+    cb, sc = moe_expert_code_bytes(rf.bits, INTER), moe_expert_scale_count(rf.group, INTER)
+    codes = np.empty(E * cb, np.uint8)
+    scales = np.empty(E * sc, np.float32)
+    for e in range(E):
+        c, s = moe_pack_expert(layer["gate_q"][e], layer["up_q"][e], layer["down_q"][e],
+                               layer["gate_s"][e], layer["up_s"][e], layer["down_s"][e], rf.bits, rf.group)
+        codes[e * cb:(e + 1) * cb] = c
+        scales[e * sc:(e + 1) * sc] = s
+    scodes, sscales = moe_pack_expert(layer["shared_gate_q"], layer["shared_up_q"], layer["shared_down_q"],
+                                      layer["shared_gate_s"], layer["shared_up_s"], layer["shared_down_s"],
+                                      sf.bits, sf.group)
+    t = lambda a: torch.from_numpy(a).to(device)
+    return {
+        "router_w": t(np.ascontiguousarray(layer["router_w"], np.float32)),
+        "router_b": None if layer.get("router_b") is None else t(np.ascontiguousarray(layer["router_b"], np.float32)),
+        "expert_q": t(codes), "expert_s": t(scales), "expert_bits": rf.bits, "expert_group": rf.group,
+        "shared_q": t(scodes), "shared_s": t(sscales), "shared_bits": sf.bits, "shared_group": sf.group,
+    }
+
+
+# ----------------------------------------------------------------- GPU entry points
+def moe_workspace_bytes(n_tokens: int) -> int:
+    return load().moe_workspace_bytes(n_tokens)
+
+
+def workspace(n_tokens: int, device="cuda"):
+    import torch
+    return torch.empty(max(moe_workspace_bytes(n_tokens), 256), dtype=torch.uint8, device=device)
+
+
+def moe_layer_forward(x, packed: dict, y, topk_ids, topk_w, ws, flags: int = 0, stream=None):
+    """Enqueue one layer: x [T,1280] f32/bf16 -> y [T,1280] f32, ids/weights [T,6]."""
+    import torch
+    T = x.shape[0] if x.dim() == 2 else 0
+    x_dtype = MOE_BF16 if x.dtype == torch.bfloat16 else MOE_F32
+    check(load().moe_layer_forward(
+        _ptr(x), x_dtype, T, _ptr(packed["router_w"]), _ptr(packed["router_b"]),
+        _ptr(packed["expert_q"]), _ptr(packed["expert_s"]), packed["expert_bits"], packed["expert_group"],
+        _ptr(packed["shared_q"]), _ptr(packed["shared_s"]), packed["shared_bits"], packed["shared_group"],
+        _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), flags, _stream(stream)))
+
+
+def moe_rmsnorm(h, z, eps: float = 1e-6, stream=None):
+    import torch
+    z_dtype = MOE_BF16 if z.dtype == torch.bfloat16 else MOE_F32
+    check(load().moe_rmsnorm(_ptr(h), _ptr(z), z_dtype, h.shape[0], eps, _stream(stream)))
+
+
+def layer(x, packed: dict, flags: int = 0, y=None, ws=None):
+    """Convenience: allocate outputs (torch) and run one layer; returns (ids, w, y)."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    y = torch.empty(T, HIDDEN, dtype=torch.float32, device=dev) if y is None else y
+    ids = torch.empty(T, TOPK, dtype=torch.int32, device=dev)
+    w = torch.empty(T, TOPK, dtype=torch.float32, device=dev)
+    ws = workspace(T, dev) if ws is None else ws
+    moe_layer_forward(x, packed, y, ids, w, ws, flags)
+    return ids, w, y

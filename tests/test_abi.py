@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI: exports, packing layout, argument validation.
+Nothing here launches a kernel, so it runs without a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from quantized_expert_ffn_moe_amd import binding as B
+from synth import QFmt, make_tiny_layer
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def test_every_declared_symbol_is_exported(lib):
+    text = open(HEADER).read()
+    names = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, re.M))
+    assert names == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n) and getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.moe_status_str(s)
+    assert b"unknown" in lib.moe_status_str(99)
+
+
+def _unpack_matrix(buf, N, K, bits):
+    """Decode the packed tile layout described in include/moe.h (independent of the packer)."""
+    KB = 128 if bits == 4 else 64
+    out = np.zeros((N, K), np.int64)
+    words = np.frombuffer(buf, dtype="<u4")
+    for nt in range(N // 16):
+        for kb in range(K // KB):
+            base = (nt * (K // KB) + kb) * 256
+            for lane in range(64):
+                row, q = nt * 16 + lane % 16, lane // 16
+                for j in range(4):
+                    w = int(words[base + lane * 4 + j])
+                    if bits == 4:
+                        for i in range(8):
+                            out[row, kb * KB + 32 * j + 8 * q + i] = ((w >> (4 * i)) & 15) - 8
+                    else:
+                        for i in range(4):
+                            out[row, kb * KB + 32 * (j // 2) + 8 * q + 4 * (j % 2) + i] = ((w >> (8 * i)) & 255) - 128
+    return out
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (8, 128)])
+def test_pack_round_trip(lib, bits, group):
+    rng = np.random.default_rng(bits)
+    lo, hi = QFmt(bits, group).code_range
+    inter = 896
+    gate = rng.integers(lo, hi, (inter, 1280), endpoint=True, dtype=np.int8)
+    up = rng.integers(lo, hi, (inter, 1280), endpoint=True, dtype=np.int8)
+    down = rng.integers(lo, hi, (1280, inter), endpoint=True, dtype=np.int8)
+    if bits == 8:
+        gate[0, :5] = [-128, -127, 0, 126, 127]
+    gs = rng.uniform(0.002, 0.02, (inter, 1280 // group)).astype(np.float32)
+    us = rng.uniform(0.002, 0.02, (inter, 1280 // group)).astype(np.float32)
+    ds = rng.uniform(0.002, 0.02, (1280, inter // group)).astype(np.float32)
+    codes, scales = B.moe_pack_expert(gate, up, down, gs, us, ds, bits, group)
+    mb = inter * 1280 * bits // 8
+    assert codes.size == 3 * mb
+    # decode only a slice of tiles of each matrix to keep the pure-Python decoder fast
+    np.testing.assert_array_equal(_unpack_matrix(codes[:mb][: 16 * 1280 * bits // 8 * 2], 32, 1280, bits), gate[:32])
+    np.testing.assert_array_equal(_unpack_matrix(codes[mb:2 * mb][: 16 * 1280 * bits // 8], 16, 1280, bits), up[:16])
+    np.testing.assert_array_equal(_unpack_matrix(codes[2 * mb:][: 16 * inter * bits // 8], 16, inter, bits), down[:16])
+    ng = 1280 // group
+    sg = scales[: inter * ng].reshape(inter // 16, ng, 16)
+    np.testing.assert_array_equal(sg.transpose(0, 2, 1).reshape(inter, ng), gs)
+    sd = scales[2 * inter * ng:].reshape(1280 // 16, inter // group, 16)
+    np.testing.assert_array_equal(sd.transpose(0, 2, 1).reshape(1280, inter // group), ds)
+
+
+def test_pack_rejects_bad_codes_and_formats(lib):
+    lay = make_tiny_layer(1, E=1, H=1280, I=896, Is=896, fmt=QFmt(4, 64))
+    args = [lay["gate_q"][0], lay["up_q"][0], lay["down_q"][0], lay["gate_s"][0], lay["up_s"][0], lay["down_s"][0]]
+    bad = args[0].copy(); bad[3, 7] = 8
+    with pytest.raises(B.MoeError, match="FORMAT"):
+        B.moe_pack_expert(bad, *args[1:], 4, 64)
+    with pytest.raises(B.MoeError, match="FORMAT"):
+        B.moe_pack_expert(*args, 4, 48)
+    assert B.moe_expert_code_bytes(5, 896) == 0 and B.moe_expert_scale_count(16, 896) == 0
+
+
+def _fwd(lib, **kw):
+    A = 0x10000  # fake, aligned device addresses: validation never dereferences them
+    a = dict(x=A, x_dtype=0, T=4, rw=A, rb=None, eq=A, es=A, eb=4, eg=64, sq=A, ss=A, sb=8, sg=128,
+             y=A * 2, ids=A, w=A, ws=A, wsb=1 << 40, flags=0, stream=None)
+    a.update(kw)
+    return lib.moe_layer_forward(a["x"], a["x_dtype"], a["T"], a["rw"], a["rb"], a["eq"], a["es"], a["eb"], a["eg"],
+                                 a["sq"], a["ss"], a["sb"], a["sg"], a["y"], a["ids"], a["w"], a["ws"], a["wsb"],
+                                 a["flags"], a["stream"])
+
+
+def test_forward_validation_codes(lib):
+    assert _fwd(lib, x=None) == 1
+    assert _fwd(lib, ws=None) == 1
+    assert _fwd(lib, T=-1) == 2
+    assert _fwd(lib, T=8193) == 2
+    assert _fwd(lib, eb=5) == 3
+    assert _fwd(lib, sg=16) == 3
+    assert _fwd(lib, y=0x10008) == 4
+    assert _fwd(lib, rb=0x10004) == 4
+    assert _fwd(lib, wsb=16) == 5
+    assert _fwd(lib, flags=1 << 9) == 7
+    assert _fwd(lib, flags=B.MOE_FORCE_DECODE | B.MOE_FORCE_GROUPED) == 7
+    assert _fwd(lib, flags=B.MOE_NORM_BF16) == 7
+    assert _fwd(lib, flags=B.MOE_NORM_INPUT, x_dtype=1) == 7
+    assert _fwd(lib, x_dtype=2) == 7
+    assert _fwd(lib, y=0x10000) == 7                        # aliasing without accumulate
+    assert _fwd(lib, T=0) == 0                               # empty call: nothing enqueued
+    assert _fwd(lib, T=0, x=None, y=None, ids=None, w=None) == 0
+    assert _fwd(lib, T=0, ws=None) == 1
+
+
+def test_workspace_bytes(lib):
+    assert B.moe_workspace_bytes(-1) == 0 and B.moe_workspace_bytes(8193) == 0
+    small, big = B.moe_workspace_bytes(1), B.moe_workspace_bytes(2184)
+    assert 0 < small < big
+    # ysorted + h_routed dominate: T*6*(1280+896)*4
+    assert big >= 2184 * 6 * (1280 + 896) * 4
+
+
+def test_rmsnorm_validation(lib):
+    assert lib.moe_rmsnorm(None, 0x100, 0, 1, 1e-6, None) == 1
+    assert lib.moe_rmsnorm(0x100, 0x104, 0, 1, 1e-6, None) == 4
+    assert lib.moe_rmsnorm(0x100, 0x200, 3, 1, 1e-6, None) == 7
+    assert lib.moe_rmsnorm(0x100, 0x200, 0, 0, 1e-6, None) == 0

@@ -1,0 +1,176 @@
+"""GPU library vs the float64 oracle, through the C ABI (needs an MI355X)."""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from synth import NORM_EPS, WORKLOADS, make_layer, make_tokens
+from tests.conftest import gpu_available
+from tests.parity import check_layer, check_output
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print("[parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=None)
+def layer_of(wi: int, li: int):
+    return make_layer(WORKLOADS[wi], li)
+
+
+@functools.lru_cache(maxsize=None)
+def packed_of(wi: int, li: int):
+    from quantized_expert_ffn_moe_amd import binding as B
+    return B.pack_layer(layer_of(wi, li))
+
+
+def tokens(wi, n=None, batch=0):
+    x, bits = make_tokens(WORKLOADS[wi], batch=batch, n_tokens=n)
+    if bits is not None:
+        xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        xt = torch.from_numpy(x).cuda()
+    return x.astype(np.float64), xt
+
+
+def run(xt, packed, flags=0):
+    from quantized_expert_ffn_moe_amd import binding as B
+    ids, w, y = B.layer(xt, packed, flags)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
+
+
+@pytest.mark.parametrize("wi,path", [(0, "decode"), (0, "grouped"), (2, "grouped"), (2, "decode"),
+                                     (3, "grouped")])
+def test_single_layer_full_size(lib, wi, path):
+    from quantized_expert_ffn_moe_amd import binding as B
+    flags = B.MOE_FORCE_DECODE if path == "decode" else B.MOE_FORCE_GROUPED
+    say(f"workload {WORKLOADS[wi].name} path {path}")
+    x, xt = tokens(wi)
+    ids, w, y = run(xt, packed_of(wi, 0), flags)
+    ratio, near = check_layer(x, layer_of(wi, 0), ids, w, y)
+    say(f"  err/rms {ratio:.2e} near-ties {near}")
+
+
+@pytest.mark.parametrize("T", [2, 3, 5, 7, 31, 33, 65, 100])
+def test_ragged_token_counts_both_paths(lib, T):
+    from quantized_expert_ffn_moe_amd import binding as B
+    x, xt = tokens(2, n=T, batch=7)
+    say(f"T={T}")
+    res = {}
+    for name, flags in (("decode", B.MOE_FORCE_DECODE), ("grouped", B.MOE_FORCE_GROUPED)):
+        ids, w, y = run(xt, packed_of(2, 0), flags)
+        ratio, _ = check_layer(x, layer_of(2, 0), ids, w, y)
+        res[name] = (ids, y)
+        say(f"  {name}: err/rms {ratio:.2e}")
+    np.testing.assert_array_equal(res["decode"][0], res["grouped"][0])
+
+
+def test_mixed_formats_f32_input_grouped(lib):
+    """int4 G64 routed + int8 G128 shared with f32 activations (hi/lo split operands)."""
+    from quantized_expert_ffn_moe_amd import binding as B
+    x, xt = tokens(1, n=40, batch=3)
+    ids, w, y = run(xt, packed_of(1, 0), B.MOE_FORCE_GROUPED)
+    ratio, _ = check_layer(x, layer_of(1, 0), ids, w, y)
+    say(f"mixed formats grouped err/rms {ratio:.2e}")
+
+
+def test_all_tokens_on_few_experts(lib):
+    """A huge bias on experts 0..5 sends every token to them: several tiles per expert."""
+    from quantized_expert_ffn_moe_amd import binding as B
+    lay = dict(layer_of(3, 0))
+    b = np.zeros(64, np.float32); b[:6] = 60.0 - 8.0 * np.arange(6)
+    lay["router_b"] = b
+    packed = dict(packed_of(3, 0)); packed["router_b"] = torch.from_numpy(b).cuda()
+    x, xt = tokens(3, n=150, batch=5)
+    ids, w, y = run(xt, packed, B.MOE_FORCE_GROUPED)
+    assert np.all(ids == np.arange(6)[None, :])
+    ratio, _ = check_layer(x, lay, ids, w, y)
+    say(f"skewed err/rms {ratio:.2e}")
+
+
+def test_deterministic_and_empty(lib):
+    from quantized_expert_ffn_moe_amd import binding as B
+    x, xt = tokens(3)
+    a = run(xt, packed_of(3, 0))
+    b = run(xt, packed_of(3, 0))
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    ids, w, y = B.layer(xt[:0], packed_of(3, 0))
+    assert y.shape == (0, 1280)
+
+
+@pytest.mark.parametrize("zdt", ["f32", "bf16"])
+def test_rmsnorm(lib, zdt):
+    from quantized_expert_ffn_moe_amd import binding as B
+    h = np.random.default_rng(3).normal(0, 3, (37, 1280)).astype(np.float32)
+    ht = torch.from_numpy(h).cuda()
+    z = torch.empty(37, 1280, dtype=torch.float32 if zdt == "f32" else torch.bfloat16, device="cuda")
+    B.moe_rmsnorm(ht, z, NORM_EPS)
+    zg = z.float().cpu().numpy().astype(np.float64)
+    zo = O.rmsnorm(h.astype(np.float64), NORM_EPS)
+    if zdt == "f32":
+        np.testing.assert_allclose(zg, zo, rtol=2e-6, atol=0)
+    else:
+        # the rounding decision is taken on an fp32 z: at most one bf16 ulp apart
+        np.testing.assert_allclose(zg, zo, rtol=2 ** -8 + 2e-6, atol=0)
+        assert np.mean(zg == O.bf16_round(zo)) > 0.999
+
+
+def _chain(wi, T, sample):
+    """Run the whole chain in place (RMSNorm + residual inside each call), then
+    check every layer on the sampled tokens against the oracle, teacher-forced
+    with the GPU's own residual stream and normalised input."""
+    from quantized_expert_ffn_moe_amd import binding as B
+    wl = WORKLOADS[wi]
+    x, xt = tokens(wi, n=T)
+    h = xt.float().contiguous()
+    flags = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE | (B.MOE_NORM_BF16 if wl.norm_bf16 else 0)
+    ws = B.workspace(T)
+    ids_l, w_l, h_l = [], [], [h.clone()]
+    ids = torch.empty(T, 6, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, 6, dtype=torch.float32, device="cuda")
+    for li in range(wl.n_layers):
+        B.moe_layer_forward(h, packed_of(wi, li), h, ids, w, ws, flags)
+        ids_l.append(ids.cpu().numpy()); w_l.append(w.cpu().numpy()); h_l.append(h.clone())
+    torch.cuda.synchronize()
+    zdt = torch.bfloat16 if wl.norm_bf16 else torch.float32
+    worst = 0.0
+    for li in range(wl.n_layers):
+        hin = h_l[li][sample].contiguous()
+        z = torch.empty(len(sample), 1280, dtype=zdt, device="cuda")
+        B.moe_rmsnorm(hin, z, NORM_EPS)
+        zin = z.float().cpu().numpy().astype(np.float64)
+        out = (h_l[li + 1][sample] - h_l[li][sample]).cpu().numpy()
+        ratio, near = check_layer(zin, layer_of(wi, li), ids_l[li][sample], w_l[li][sample], out)
+        worst = max(worst, ratio)
+        say(f"  layer {li + 1}: err/rms {ratio:.2e} near-ties {near}")
+    # end to end, from the same input, without teacher forcing
+    # (only on tokens whose routing agrees at every layer: a near-tie may
+    # legitimately send the two sides down different experts)
+    h_o, trace = O.moe_chain(x[sample], [layer_of(wi, li) for li in range(wl.n_layers)], NORM_EPS, wl.norm_bf16)
+    same = np.ones(len(sample), bool)
+    for li in range(wl.n_layers):
+        same &= np.all(trace[li][0] == ids_l[li][sample], axis=1)
+    assert same.sum() >= len(sample) // 2
+    e2e = check_output(h_l[-1][sample][same].cpu().numpy() - x[sample][same], h_o[same] - x[sample][same], tol=1e-2)
+    say(f"  end-to-end err/rms {e2e:.2e} on {same.sum()}/{len(sample)} tokens (worst layer {worst:.2e})")
+
+
+def test_chain_decode_11_layers(lib):
+    say("11-layer decode chain, 1 token")
+    _chain(1, 1, np.array([0]))
+
+
+def test_chain_multipage_prefill_11_layers_sampled(lib):
+    say("11-layer multi-page prefill, 2184 tokens, 24 sampled")
+    sample = np.sort(np.random.default_rng(0).choice(2184, 24, replace=False))
+    _chain(4, 2184, sample)
