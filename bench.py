@@ -1,0 +1,167 @@
+"""Benchmark: MoE-layer decode tokens/s and achieved HBM bandwidth on one MI355X.
+
+Workload (one step = one token through the 11 chained MoE layers of the
+decoder: RMSNorm, router, top-6 routed int4 G64 experts, int8 G128 fused shared
+expert, weighted combine, residual add; all kernels of the library):
+synthetic seeded weights and tokens, distinct token every step, R replicas of
+the 11-layer weight set rotated step by step so that the 256 MiB last-level
+cache cannot serve a step's weights from the previous visit.
+
+Prints one JSON line.  The CPU baseline is the float64 oracle, timed on the
+host on a bounded sample of tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s (% peak), int4 G=64, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+
+def layer_bytes(layer_ids, routed_fmt, shared_fmt):
+    """Algorithmic bytes of one decode layer for one token: the packed codes and
+    scales of the 6 picked experts, the shared expert and the router, plus the
+    token's activations in and out."""
+    H, I, IS, E = 1280, 896, 1792, 64
+    per_expert = 3 * H * I * routed_fmt.bits // 8 + 3 * H * I // routed_fmt.group * 4
+    shared = 3 * H * IS * shared_fmt.bits // 8 + 3 * H * IS // shared_fmt.group * 4
+    router = E * H * 4
+    acts = H * 4 * 3 + 6 * 8  # h read, y read-modify-write, ids/w out
+    return len(set(layer_ids)) * per_expert + shared + router + acts
+
+
+def cpu_baseline(layers, tokens, budget_s=20.0):
+    """The oracle as it is, on the host cores, over as many tokens as fit the budget."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+    from synth import NORM_EPS
+    done, t0 = 0, time.perf_counter()
+    while done < len(tokens):
+        O.moe_chain(tokens[done:done + 1].astype(np.float64), layers, NORM_EPS, False)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} decode tokens through the 11 layers (float64 numpy oracle), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--path", choices=["chain", "layers"], default="chain")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is a design note.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_expert_ffn_moe_amd import binding as B
+    from synth import WORKLOADS, make_layer, make_tokens
+
+    wl = WORKLOADS[1]
+    L = wl.n_layers
+    layers = [make_layer(wl, li) for li in range(L)]
+    base = [B.pack_layer(layer) for layer in layers]
+    sets = [base]
+    for _ in range(args.replicas - 1):
+        sets.append([{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in p.items()} for p in base])
+    n_tok = args.warmup + args.steps
+    xs = np.concatenate([make_tokens(wl, batch=i)[0] for i in range(n_tok)])
+    x_dev = torch.from_numpy(xs).cuda()
+
+    flags = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE
+    h = torch.empty(1, 1280, dtype=torch.float32, device="cuda")
+    ids = torch.empty(L, 1, 6, dtype=torch.int32, device="cuda")
+    w = torch.empty(L, 1, 6, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    if args.path == "chain":
+        ws = B.decode_workspace(stream=stream)
+        warr = [B.layer_weights(sset) for sset in sets]
+
+        def step(i):
+            B.moe_decode_forward(x_dev[i:i + 1], h, sets[i % args.replicas], ids, w, ws, flags,
+                                 weights=warr[i % args.replicas], stream=stream)
+        kernel_name = "chain_kernel (persistent decode step, one launch per token)"
+    else:
+        ws = B.workspace(1)
+
+        def step(i):
+            h.copy_(x_dev[i:i + 1])
+            for li in range(L):
+                B.moe_layer_forward(h, sets[i % args.replicas][li], h, ids[li], w[li], ws, flags, stream=stream)
+        kernel_name = "per-layer kernels (router, decode items, reduce) x 11"
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.warmup, n_tok):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+
+    # per-launch kernel duration: an event pair around each launch, on the launch stream
+    with torch.cuda.stream(stream):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for k, i in enumerate(range(args.warmup, n_tok)):
+            evs[k][0].record(stream)
+            step(i)
+            evs[k][1].record(stream)
+        torch.cuda.synchronize()
+    ms_kernel = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    ids_last = ids.cpu().numpy()
+    step_bytes = sum(layer_bytes(ids_last[li, 0].tolist(), wl.routed, wl.shared) for li in range(L))
+    achieved = step_bytes / (ms_kernel * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": 1000.0 / ms_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded weights and tokens)",
+        "config": {"workload": wl.name, "tokens_per_step": 1, "layers": L,
+                   "routed": f"int{wl.routed.bits} g{wl.routed.group}",
+                   "shared": f"int{wl.shared.bits} g{wl.shared.group}",
+                   "weight_replicas": args.replicas, "path": args.path},
+        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": step_bytes, "ms_per_launch": ms_kernel},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layers, xs[: args.warmup + args.steps])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,7 +27,9 @@
  * - Errors are status codes, never exceptions or aborts.  All argument checks
  *   happen before anything is enqueued, so a non-OK status means nothing ran.
  * - Calls are re-entrant; concurrent calls need distinct workspaces.
- * - All device pointers must be 16-byte aligned (MOE_E_ALIGN otherwise).
+ * - Activation, weight-code, router-weight and workspace pointers must be
+ *   16-byte aligned; scales, bias, ids and weights 4-byte aligned
+ *   (MOE_E_ALIGN otherwise).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -71,8 +73,9 @@ enum {
   /* With MOE_NORM_INPUT: round the normalised input to bf16 (nearest, ties to
      even) before it reaches the router and the experts. */
   MOE_NORM_BF16 = 4u,
-  /* Force the per-token GEMV path / the grouped MFMA path regardless of the
-     token count (both give the same result up to fp32 rounding order). */
+  /* Force the per-token GEMV path (at most 64 tokens) / the grouped MFMA
+     path regardless of the token count (both give the same result up to fp32
+     rounding order). */
   MOE_FORCE_DECODE = 8u,
   MOE_FORCE_GROUPED = 16u
 };
@@ -93,18 +96,27 @@ const char* moe_status_str(int32_t status);
  * int4 codes must lie in [-8, 7]; int8 codes in [-128, 127].
  *
  * Packed layout written to codes_out (moe_expert_code_bytes() bytes):
- *   [gate | up | down], each matrix [N rows][K] stored as 1 KiB tiles of 16
- *   rows x KB columns (KB = 128 for int4, 64 for int8), tile (nt, kb) at byte
- *   1024 * (nt * (K/KB) + kb).  Inside a tile, lane l = 0..63 owns bytes
- *   16l..16l+15 for row 16nt + (l % 16); its four 32-bit words hold, for
- *   lane group q = l / 16:
- *     int4: word j = the 8 codes k = 128kb + 32j + 8q + i (i = 0..7) in
- *           nibble i (bits 4i..4i+3), stored as code + 8;
- *     int8: word j = the 4 codes k = 64kb + 32(j/2) + 8q + 4(j%2) + i
- *           (i = 0..3) in byte i, stored as code + 128.
+ *   [gate | up | down]; every matrix is a sequence of 1 KiB tiles, and inside
+ *   a tile lane l = 0..63 owns bytes 16l..16l+15, i.e. four 32-bit words
+ *   w0..w3, with r = l % 16 and q = l / 16.  Codes are stored offset-binary
+ *   (int4: code + 8 in one nibble; int8: code + 128 in one byte).
+ *   gate and up ([N = inter rows][K = 1280]): tiles of 16 rows x KB columns,
+ *     KB = 128 (int4) or 64 (int8), tile (nt, kb) at byte 1024*(nt*(K/KB) + kb);
+ *     row 16nt + r;
+ *       int4: word j = codes k = 128kb + 32j + 8q + i (i = 0..7) in nibble i;
+ *       int8: word j = codes k = 64kb + 32(j/2) + 8q + 4(j%2) + i (i = 0..3)
+ *             in byte i.
+ *   down ([N = 1280 rows][K = inter]): tiles of DR rows x 32 columns, DR = 64
+ *     (int4) or 32 (int8), tile (kc, rt) at byte 1024*(kc*(1280/DR) + rt);
+ *       int4: word j = row DR*rt + 16j + r, codes k = 32kc + 8q + i in nibble i;
+ *       int8: word j = row DR*rt + 16(j/2) + r, codes k = 32kc + 8q + 4(j%2) + i
+ *             in byte i.
+ *   (A 32-column slab of the down matrix, which is what one slice of the
+ *   intermediate dimension multiplies, is contiguous.)
  * Packed scales written to scales_out (moe_expert_scale_count() floats):
- *   [gate | up | down], each [N/16][K/G][16]: entry (nt, g, r) = scale of row
- *   16nt + r, group g.
+ *   [gate | up | down]; gate and up are [N/16][K/G][16] with entry (nt, g, r)
+ *   = scale of row 16nt + r, group g; down is [K/G][1280/DR][16][DR/16] with
+ *   entry (g, rt, r, j) = scale of row DR*rt + 16j + r, group g.
  * Experts of a layer are concatenated: expert e at byte e * code_bytes and
  * float e * scale_count.
  * ------------------------------------------------------------------------ */
@@ -159,6 +171,51 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
  * to even).  The decoder's RMSNorm (demo page step 7; README "Architecture"). */
 moe_status_t moe_rmsnorm(const float* h, void* z, int32_t z_dtype, int32_t n_tokens,
                          float eps, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode step: one token through n_layers chained MoE layers in a single
+ * persistent (cooperative) kernel launch -- the decoder's per-token path
+ * (demo page step 6: layers 1..11 are MoE; step 7: greedy decoding runs one
+ * token at a time).  With MOE_NORM_INPUT | MOE_ACCUMULATE each layer computes
+ *   h_l = h_{l-1} + MoE_l(RMSNorm(h_{l-1})),   h_0 = x,   y = h_L,
+ * which is exactly n_layers calls of moe_layer_forward with those flags.
+ * Without MOE_ACCUMULATE, h_l = MoE_l(...); without MOE_NORM_INPUT the layer
+ * input is h_{l-1} itself.  MOE_NORM_BF16 and the FORCE flags are not accepted.
+ *
+ * x          [1280] f32 or bf16 (x_dtype); may equal y when f32.
+ * y          [1280] f32 output (the residual stream after the last layer).
+ * layers     host array of n_layers (1..MOE_DECODE_MAX_LAYERS) device-pointer
+ *            sets, each laid out as for moe_layer_forward; all layers share the
+ *            routed format (expert_bits, expert_group) and the shared format.
+ * topk_ids   [n_layers][6] int32 out, topk_w [n_layers][6] f32 out: each
+ *            layer's routing, as moe_layer_forward reports it.
+ * workspace  >= moe_decode_workspace_bytes() bytes, 16-byte aligned, cleared
+ *            once with moe_decode_workspace_init() after allocation and then
+ *            reused across calls without further initialisation (it carries a
+ *            call counter).  Calls sharing a workspace must be stream ordered.
+ *            Word 2 of the workspace becomes nonzero if a wait inside the
+ *            kernel gave up (a bug guard; results are then invalid).
+ * The launch is cooperative: all 256 workgroups must be co-resident, else
+ * MOE_E_HIP is returned and nothing runs.
+ * ------------------------------------------------------------------------ */
+#define MOE_DECODE_MAX_LAYERS 16
+
+typedef struct {
+  const float* router_w;       /* [64][1280] f32 */
+  const float* router_b;       /* [64] f32 or NULL */
+  const void* expert_q;        /* 64 packed routed experts */
+  const float* expert_scales;  /* their packed scales */
+  const void* shared_q;        /* the packed fused shared expert */
+  const float* shared_scales;  /* its packed scales */
+} moe_layer_weights_t;
+
+size_t moe_decode_workspace_bytes(void);
+moe_status_t moe_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+moe_status_t moe_decode_forward(const void* x, int32_t x_dtype, float* y, int32_t n_layers,
+                                const moe_layer_weights_t* layers, int32_t expert_bits,
+                                int32_t expert_group, int32_t shared_bits, int32_t shared_group,
+                                int32_t* topk_ids, float* topk_w, void* workspace,
+                                size_t workspace_bytes, uint32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

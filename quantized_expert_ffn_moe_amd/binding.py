@@ -18,7 +18,16 @@ MOE_FORCE_DECODE, MOE_FORCE_GROUPED = 8, 16
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 EXPORTS = ("moe_status_str", "moe_expert_code_bytes", "moe_expert_scale_count", "moe_pack_expert",
-           "moe_workspace_bytes", "moe_layer_forward", "moe_rmsnorm")
+           "moe_workspace_bytes", "moe_layer_forward", "moe_rmsnorm", "moe_decode_workspace_bytes",
+           "moe_decode_workspace_init", "moe_decode_forward")
+DECODE_MAX_LAYERS = 16
+
+
+class LayerWeights(ctypes.Structure):
+    """moe_layer_weights_t: device pointers of one layer."""
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+                ("expert_q", ctypes.c_void_p), ("expert_scales", ctypes.c_void_p),
+                ("shared_q", ctypes.c_void_p), ("shared_scales", ctypes.c_void_p)]
 
 _lib = None
 
@@ -51,6 +60,13 @@ def load():
                                     vp, vp, vp, vp, sz, u32, vp]
     L.moe_rmsnorm.restype = i32
     L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, ctypes.c_float, vp]
+    L.moe_decode_workspace_bytes.restype = sz
+    L.moe_decode_workspace_bytes.argtypes = []
+    L.moe_decode_workspace_init.restype = i32
+    L.moe_decode_workspace_init.argtypes = [vp, sz, vp]
+    L.moe_decode_forward.restype = i32
+    L.moe_decode_forward.argtypes = [vp, i32, vp, i32, ctypes.POINTER(LayerWeights), i32, i32, i32, i32,
+                                     vp, vp, vp, sz, u32, vp]
     _lib = L
     return L
 
@@ -160,3 +176,37 @@ def layer(x, packed: dict, flags: int = 0, y=None, ws=None):
     ws = workspace(T, dev) if ws is None else ws
     moe_layer_forward(x, packed, y, ids, w, ws, flags)
     return ids, w, y
+
+
+# ----------------------------------------------------------------- decode step
+def moe_decode_workspace_bytes() -> int:
+    return load().moe_decode_workspace_bytes()
+
+
+def decode_workspace(device="cuda", stream=None):
+    """Allocate and initialise a decode-step workspace."""
+    import torch
+    ws = torch.empty(moe_decode_workspace_bytes(), dtype=torch.uint8, device=device)
+    check(load().moe_decode_workspace_init(_ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def layer_weights(packed_layers):
+    arr = (LayerWeights * len(packed_layers))()
+    for i, p in enumerate(packed_layers):
+        arr[i] = LayerWeights(p["router_w"].data_ptr(),
+                              None if p["router_b"] is None else p["router_b"].data_ptr(),
+                              p["expert_q"].data_ptr(), p["expert_s"].data_ptr(),
+                              p["shared_q"].data_ptr(), p["shared_s"].data_ptr())
+    return arr
+
+
+def moe_decode_forward(x, y, packed_layers, topk_ids, topk_w, ws, flags=0, weights=None, stream=None):
+    """Enqueue one token through len(packed_layers) chained layers (one launch)."""
+    import torch
+    p0 = packed_layers[0]
+    arr = layer_weights(packed_layers) if weights is None else weights
+    x_dtype = MOE_BF16 if x.dtype == torch.bfloat16 else MOE_F32
+    check(load().moe_decode_forward(_ptr(x), x_dtype, _ptr(y), len(packed_layers), arr,
+                                    p0["expert_bits"], p0["expert_group"], p0["shared_bits"], p0["shared_group"],
+                                    _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), flags, _stream(stream)))

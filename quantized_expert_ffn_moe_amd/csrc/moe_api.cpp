@@ -20,7 +20,8 @@ bool fmt_ok(int bits, int group) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Workspace {
-  float* z;          // [T][H]
+  float* z;          // [T][H] normalised input
+  // grouped path
   float* h_routed;   // [T*6][I]
   float* h_shared;   // [T][IS]
   float* ysorted;    // [T*6][H]
@@ -31,32 +32,63 @@ struct Workspace {
   int32_t* tiles;    // [max_tiles][2]
   int32_t* perm;     // [T*6]
   int32_t* pos_of;   // [T*6]
+  // decode path (aliases the grouped buffers)
+  float* part;       // [T][N_ITEMS][H]
   size_t bytes;
   int max_tiles;
 };
 
-Workspace carve(void* base, int T) {
-  Workspace w;
-  size_t off = 0;
-  auto take = [&](size_t bytes) -> void* {
+constexpr int DECODE_FORCE_MAX_T = 64;   // largest token count the per-token path accepts
+
+struct Carver {
+  char* base; size_t off;
+  void* take(size_t bytes) {
     const size_t o = off;
     off += (bytes + 255) & ~(size_t)255;
-    return base ? (void*)((char*)base + o) : nullptr;
-  };
+    return base ? (void*)(base + o) : nullptr;
+  }
+};
+
+Workspace carve(void* base, int T) {
+  Workspace w;
+  Carver c{(char*)base, 0};
   const size_t slots = (size_t)T * TOPK;
   w.max_tiles = (int)(slots / MT) + E + 1;
-  w.z = (float*)take((size_t)T * H * 4);
-  w.h_routed = (float*)take(slots * I * 4);
-  w.h_shared = (float*)take((size_t)T * IS * 4);
-  w.ysorted = (float*)take(slots * H * 4);
-  w.ys = (float*)take((size_t)T * H * 4);
-  w.counts = (int32_t*)take(E * 4);
-  w.offsets = (int32_t*)take((E + 1) * 4);
-  w.ntiles = (int32_t*)take(4);
-  w.tiles = (int32_t*)take((size_t)w.max_tiles * 2 * 4);
-  w.perm = (int32_t*)take(slots * 4);
-  w.pos_of = (int32_t*)take(slots * 4);
-  w.bytes = off;
+  w.z = (float*)c.take((size_t)T * H * 4);
+  const size_t union_start = c.off;
+  w.h_routed = (float*)c.take(slots * I * 4);
+  w.h_shared = (float*)c.take((size_t)T * IS * 4);
+  w.ysorted = (float*)c.take(slots * H * 4);
+  w.ys = (float*)c.take((size_t)T * H * 4);
+  w.counts = (int32_t*)c.take(E * 4);
+  w.offsets = (int32_t*)c.take((E + 1) * 4);
+  w.ntiles = (int32_t*)c.take(4);
+  w.tiles = (int32_t*)c.take((size_t)w.max_tiles * 2 * 4);
+  w.perm = (int32_t*)c.take(slots * 4);
+  w.pos_of = (int32_t*)c.take(slots * 4);
+  const size_t grouped_end = c.off;
+  c.off = union_start;
+  w.part = T <= DECODE_FORCE_MAX_T ? (float*)c.take((size_t)T * N_ITEMS * H * 4) : nullptr;
+  w.bytes = c.off > grouped_end ? c.off : grouped_end;
+  return w;
+}
+
+struct DecodeWorkspace {
+  uint32_t* hdr; uint32_t* item_flag; uint32_t* red_flag; float* part; float* q;
+  size_t flag_words;   // words cleared by moe_decode_workspace_init
+  size_t bytes;
+};
+
+DecodeWorkspace carve_decode(void* base) {
+  DecodeWorkspace w;
+  Carver c{(char*)base, 0};
+  w.hdr = (uint32_t*)c.take(64 * 4);
+  w.item_flag = (uint32_t*)c.take(N_ITEMS * 4);
+  w.red_flag = (uint32_t*)c.take(N_RED * 4);
+  w.flag_words = c.off / 4;
+  w.part = (float*)c.take((size_t)N_ITEMS * H * 4);
+  w.q = (float*)c.take((size_t)N_RED * Q_STRIDE * 4);
+  w.bytes = c.off;
   return w;
 }
 
@@ -72,7 +104,8 @@ QW make_qw(const void* q, const float* s, int bits, int group, int inter, bool r
   return w;
 }
 
-void pack_matrix(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
+// gate/up matrices: 1 KiB tiles of 16 rows x KB columns, tile (nt, kb)
+void pack_rows(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
   const int KB = kb_cols(bits), nkb = K / KB;
   for (int nt = 0; nt < N / 16; ++nt)
     for (int kb = 0; kb < nkb; ++kb) {
@@ -80,31 +113,57 @@ void pack_matrix(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
       for (int lane = 0; lane < 64; ++lane) {
         const int row = nt * 16 + (lane & 15), q = lane >> 4;
         const int8_t* src = Q + (size_t)row * K + (size_t)kb * KB;
-        uint8_t* dst = tile + lane * 16;
         for (int j = 0; j < 4; ++j) {
           uint32_t word = 0;
           if (bits == 4) {
-            for (int i = 0; i < 8; ++i) {
-              const int k = 32 * j + 8 * q + i;
-              word |= (uint32_t)(src[k] + 8) << (4 * i);
-            }
+            for (int i = 0; i < 8; ++i) word |= (uint32_t)(src[32 * j + 8 * q + i] + 8) << (4 * i);
           } else {
-            for (int i = 0; i < 4; ++i) {
-              const int k = 32 * (j >> 1) + 8 * q + 4 * (j & 1) + i;
-              word |= (uint32_t)(uint8_t)(src[k] + 128) << (8 * i);
-            }
+            for (int i = 0; i < 4; ++i)
+              word |= (uint32_t)(uint8_t)(src[32 * (j >> 1) + 8 * q + 4 * (j & 1) + i] + 128) << (8 * i);
           }
-          memcpy(dst + 4 * j, &word, 4);
+          memcpy(tile + lane * 16 + 4 * j, &word, 4);
         }
       }
     }
 }
 
-void pack_scales(const float* S, int N, int K, int group, float* out) {
+// down matrices: 1 KiB tiles of DR rows x 32 columns, tile (kc, rt)
+void pack_slabs(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
+  const int DR = down_rows(bits), nrt = N / DR, nkc = K / 32;
+  for (int kc = 0; kc < nkc; ++kc)
+    for (int rt = 0; rt < nrt; ++rt) {
+      uint8_t* tile = out + ((size_t)kc * nrt + rt) * TILE;
+      for (int lane = 0; lane < 64; ++lane) {
+        const int r = lane & 15, q = lane >> 4;
+        for (int j = 0; j < 4; ++j) {
+          uint32_t word = 0;
+          if (bits == 4) {
+            const int8_t* src = Q + (size_t)(DR * rt + 16 * j + r) * K + 32 * kc + 8 * q;
+            for (int i = 0; i < 8; ++i) word |= (uint32_t)(src[i] + 8) << (4 * i);
+          } else {
+            const int8_t* src = Q + (size_t)(DR * rt + 16 * (j >> 1) + r) * K + 32 * kc + 8 * q + 4 * (j & 1);
+            for (int i = 0; i < 4; ++i) word |= (uint32_t)(uint8_t)(src[i] + 128) << (8 * i);
+          }
+          memcpy(tile + lane * 16 + 4 * j, &word, 4);
+        }
+      }
+    }
+}
+
+void pack_row_scales(const float* S, int N, int K, int group, float* out) {
   const int ng = K / group;
   for (int nt = 0; nt < N / 16; ++nt)
     for (int g = 0; g < ng; ++g)
       for (int r = 0; r < 16; ++r) out[((size_t)nt * ng + g) * 16 + r] = S[(size_t)(nt * 16 + r) * ng + g];
+}
+
+void pack_slab_scales(const float* S, int N, int K, int group, int bits, float* out) {
+  const int DR = down_rows(bits), nrt = N / DR, ns = DR / 16, ng = K / group;
+  for (int g = 0; g < ng; ++g)
+    for (int rt = 0; rt < nrt; ++rt)
+      for (int r = 0; r < 16; ++r)
+        for (int j = 0; j < ns; ++j)
+          out[(((size_t)g * nrt + rt) * 16 + r) * ns + j] = S[(size_t)(DR * rt + 16 * j + r) * ng + g];
 }
 
 bool codes_in_range(const int8_t* Q, size_t n, int bits) {
@@ -155,13 +214,13 @@ moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t*
     return MOE_E_FORMAT;
   uint8_t* out = (uint8_t*)codes_out;
   const size_t mb = matrix_bytes(bits, inter, H);
-  pack_matrix(gate, inter, H, bits, out);
-  pack_matrix(up, inter, H, bits, out + mb);
-  pack_matrix(down, H, inter, bits, out + 2 * mb);
+  pack_rows(gate, inter, H, bits, out);
+  pack_rows(up, inter, H, bits, out + mb);
+  pack_slabs(down, H, inter, bits, out + 2 * mb);
   const size_t ms = (size_t)inter * H / group_size;
-  pack_scales(gate_scales, inter, H, group_size, scales_out);
-  pack_scales(up_scales, inter, H, group_size, scales_out + ms);
-  pack_scales(down_scales, H, inter, group_size, scales_out + 2 * ms);
+  pack_row_scales(gate_scales, inter, H, group_size, scales_out);
+  pack_row_scales(up_scales, inter, H, group_size, scales_out + ms);
+  pack_slab_scales(down_scales, H, inter, group_size, bits, scales_out + 2 * ms);
   return MOE_OK;
 }
 
@@ -189,13 +248,16 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   const uint32_t known = MOE_ACCUMULATE | MOE_NORM_INPUT | MOE_NORM_BF16 | MOE_FORCE_DECODE | MOE_FORCE_GROUPED;
   if ((flags & ~known) || (x_dtype != MOE_F32 && x_dtype != MOE_BF16)) return MOE_E_ARG;
   if ((flags & MOE_FORCE_DECODE) && (flags & MOE_FORCE_GROUPED)) return MOE_E_ARG;
+  if ((flags & MOE_FORCE_DECODE) && T > DECODE_FORCE_MAX_T) return MOE_E_SHAPE;
   if ((flags & MOE_NORM_BF16) && !(flags & MOE_NORM_INPUT)) return MOE_E_ARG;
   if ((flags & MOE_NORM_INPUT) && x_dtype != MOE_F32) return MOE_E_ARG;
   if (x && x == (const void*)y && !((flags & MOE_ACCUMULATE) && x_dtype == MOE_F32)) return MOE_E_ARG;
-  const void* ptrs[] = {x, router_w, router_b, expert_q, expert_scales, shared_q, shared_scales,
-                        y, topk_ids, topk_w, workspace};
-  for (const void* p : ptrs)
+  const void* vec_ptrs[] = {x, router_w, expert_q, shared_q, y, workspace};  // read/written 16 B at a time
+  for (const void* p : vec_ptrs)
     if (p && !aligned16(p)) return MOE_E_ALIGN;
+  const void* word_ptrs[] = {router_b, expert_scales, shared_scales, topk_ids, topk_w};
+  for (const void* p : word_ptrs)
+    if (p && ((uintptr_t)p & 3u)) return MOE_E_ALIGN;
   const Workspace ws = carve(workspace, T);
   if (workspace_bytes < ws.bytes) return MOE_E_WORKSPACE;
   if (T == 0) return MOE_OK;
@@ -219,16 +281,12 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
 
   const bool decode = (flags & MOE_FORCE_DECODE) || (!(flags & MOE_FORCE_GROUPED) && T <= DECODE_MAX_T);
   if (decode) {
-    DecGateUpArgs g;
-    g.xf = xf; g.xb = xb;
-    g.units_per_token = TOPK; g.ids = topk_ids; g.w = rw; g.h = ws.h_routed;
-    if (launch_dec_gateup(g, T * TOPK, s) != hipSuccess) return MOE_E_HIP;
-    g.units_per_token = 1; g.ids = nullptr; g.w = sw; g.h = ws.h_shared;
-    if (launch_dec_gateup(g, T, s) != hipSuccess) return MOE_E_HIP;
-    DecDownArgs d;
-    d.ids = topk_ids; d.tw = topk_w; d.h_routed = ws.h_routed; d.h_shared = ws.h_shared;
-    d.rw = rw; d.sw = sw; d.y = y; d.accumulate = accumulate;
-    if (launch_dec_down(d, T, s) != hipSuccess) return MOE_E_HIP;
+    DecItemsArgs d;
+    d.xf = xf; d.xb = xb; d.ids = topk_ids; d.tw = topk_w; d.rw = rw; d.sw = sw; d.part = ws.part;
+    if (launch_dec_items(d, T, s) != hipSuccess) return MOE_E_HIP;
+    DecReduceArgs rd;
+    rd.part = ws.part; rd.y = y; rd.accumulate = accumulate;
+    if (launch_dec_reduce(rd, T, s) != hipSuccess) return MOE_E_HIP;
     return MOE_OK;
   }
 
@@ -266,6 +324,56 @@ moe_status_t moe_rmsnorm(const float* h, void* z, int32_t z_dtype, int32_t n_tok
   if (n_tokens == 0) return MOE_OK;
   (void)hipGetLastError();
   if (launch_rmsnorm(h, z, z_dtype == MOE_BF16, n_tokens, eps, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
+  return MOE_OK;
+}
+
+size_t moe_decode_workspace_bytes(void) { return carve_decode(nullptr).bytes; }
+
+moe_status_t moe_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return MOE_E_NULLPTR;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  const DecodeWorkspace dw = carve_decode(workspace);
+  if (workspace_bytes < dw.bytes) return MOE_E_WORKSPACE;
+  (void)hipGetLastError();
+  if (launch_zero_words((uint32_t*)workspace, dw.flag_words, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
+  return MOE_OK;
+}
+
+moe_status_t moe_decode_forward(const void* x, int32_t x_dtype, float* y, int32_t n_layers,
+                                const moe_layer_weights_t* layers, int32_t expert_bits, int32_t expert_group,
+                                int32_t shared_bits, int32_t shared_group, int32_t* topk_ids, float* topk_w,
+                                void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  if (!x || !y || !layers || !topk_ids || !topk_w || !workspace) return MOE_E_NULLPTR;
+  if (n_layers < 1 || n_layers > MOE_DECODE_MAX_LAYERS) return MOE_E_SHAPE;
+  if (!fmt_ok(expert_bits, expert_group) || !fmt_ok(shared_bits, shared_group)) return MOE_E_FORMAT;
+  if (flags & ~(uint32_t)(MOE_ACCUMULATE | MOE_NORM_INPUT)) return MOE_E_ARG;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_E_ARG;
+  if (x == (const void*)y && x_dtype != MOE_F32) return MOE_E_ARG;
+  if (!aligned16(workspace) || ((uintptr_t)x & 3u) || ((uintptr_t)y & 3u) || ((uintptr_t)topk_ids & 3u) ||
+      ((uintptr_t)topk_w & 3u))
+    return MOE_E_ALIGN;
+  ChainArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer_weights_t& L = layers[l];
+    if (!L.router_w || !L.expert_q || !L.expert_scales || !L.shared_q || !L.shared_scales) return MOE_E_NULLPTR;
+    if (!aligned16(L.expert_q) || !aligned16(L.shared_q) || ((uintptr_t)L.router_w & 3u) ||
+        ((uintptr_t)L.router_b & 3u) || ((uintptr_t)L.expert_scales & 3u) || ((uintptr_t)L.shared_scales & 3u))
+      return MOE_E_ALIGN;
+    a.layer[l].wr = L.router_w; a.layer[l].bias = L.router_b;
+    a.layer[l].eq = (const uint8_t*)L.expert_q; a.layer[l].es = L.expert_scales;
+    a.layer[l].sq = (const uint8_t*)L.shared_q; a.layer[l].ss = L.shared_scales;
+  }
+  const DecodeWorkspace dw = carve_decode(workspace);
+  if (workspace_bytes < dw.bytes) return MOE_E_WORKSPACE;
+  a.n_layers = n_layers;
+  a.x = x; a.x_bf16 = x_dtype == MOE_BF16; a.y = y;
+  a.norm = (flags & MOE_NORM_INPUT) != 0; a.accumulate = (flags & MOE_ACCUMULATE) != 0; a.eps = 1e-6f;
+  a.rbits = expert_bits; a.rgroup = expert_group; a.sbits = shared_bits; a.sgroup = shared_group;
+  a.ids = topk_ids; a.tw = topk_w;
+  a.hdr = dw.hdr; a.item_flag = dw.item_flag; a.red_flag = dw.red_flag; a.part = dw.part; a.q = dw.q;
+  (void)hipGetLastError();
+  if (launch_chain(a, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
   return MOE_OK;
 }
 

@@ -18,6 +18,8 @@ constexpr int MAX_T = 8192;      // largest token count of one call
 constexpr int MOE_MAX_SLOTS = MAX_T * TOPK;
 
 __host__ __device__ constexpr int kb_cols(int bits) { return bits == 4 ? 128 : 64; }
+// rows of one packed down-projection tile (tiles cover 32 K columns)
+__host__ __device__ constexpr int down_rows(int bits) { return bits == 4 ? 64 : 32; }
 __host__ __device__ constexpr size_t matrix_bytes(int bits, int n, int k) { return (size_t)n * k * bits / 8; }
 
 struct QW {            // one packed expert set (routed experts or the shared expert)
@@ -36,20 +38,50 @@ struct RouterArgs {
   int32_t* ids; float* w;
 };
 
-struct DecGateUpArgs {
-  const float* xf; const uint16_t* xb;  // layer input, exactly one non-null
-  int units_per_token;                  // 6 (routed) or 1 (shared)
-  const int32_t* ids;                   // [T*6] expert of each routed unit, null for shared
-  QW w;
-  float* h;                             // [units][inter]
+// Decode items: one item = 32 intermediate columns of one (token, expert):
+// gate/up for those columns, then their split-K share of the down projection,
+// written as a 1280-float partial.  Routed picks give I/32 = 28 items each,
+// the shared expert IS/32 = 56.
+constexpr int SLICE = 32;
+constexpr int R_ITEMS = TOPK * (I / SLICE);       // 168
+constexpr int S_ITEMS = IS / SLICE;               // 56
+constexpr int N_ITEMS = R_ITEMS + S_ITEMS;        // 224 per token
+
+struct DecItemsArgs {
+  const float* xf; const uint16_t* xb;  // layer input rows (f32 or bf16), exactly one non-null
+  const int32_t* ids; const float* tw;  // routing [T][6]
+  QW rw, sw;
+  float* part;                          // [T][N_ITEMS][H]
 };
 
-struct DecDownArgs {
-  const int32_t* ids; const float* tw;  // routing of each token
-  const float* h_routed;                // [T*6][I]
-  const float* h_shared;                // [T][IS]
-  QW rw, sw;
-  float* y; int accumulate;
+struct DecReduceArgs {
+  const float* part; float* y; int accumulate;
+};
+
+// Persistent decode step (one token, n_layers chained layers).
+constexpr int MAX_LAYERS = 16;
+constexpr int N_RED = 32;                 // reducer workgroups
+constexpr int RED_ROWS = H / N_RED;       // 40 rows each
+constexpr int Q_STRIDE = 68;              // 64 partial logits + sum of squares, padded
+struct LayerPtrs {
+  const float* wr; const float* bias;
+  const uint8_t* eq; const float* es;
+  const uint8_t* sq; const float* ss;
+};
+struct ChainArgs {
+  LayerPtrs layer[MAX_LAYERS];
+  int n_layers;
+  const void* x; int x_bf16;
+  float* y;                               // residual stream / output [H]
+  int norm, accumulate;
+  float eps;
+  int rbits, rgroup, sbits, sgroup;
+  int32_t* ids; float* tw;                // [n_layers][6]
+  uint32_t* hdr;                          // [0] call sequence, [1] done count, [2] error
+  uint32_t* item_flag;                    // [N_ITEMS]
+  uint32_t* red_flag;                     // [N_RED]
+  float* part;                            // [N_ITEMS][H]
+  float* q;                               // [N_RED][Q_STRIDE]
 };
 
 struct HistArgs {
@@ -76,8 +108,10 @@ struct CombineArgs {
 };
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
-hipError_t launch_dec_gateup(const DecGateUpArgs& a, int units, hipStream_t s);
-hipError_t launch_dec_down(const DecDownArgs& a, int T, hipStream_t s);
+hipError_t launch_dec_items(const DecItemsArgs& a, int T, hipStream_t s);
+hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s);
+hipError_t launch_chain(const ChainArgs& a, hipStream_t s);
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_hist(const HistArgs& a, hipStream_t s);
 hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, hipStream_t s);

@@ -190,175 +190,390 @@ __device__ __forceinline__ float dot8<8>(const uint4& v, int c, const float* xv)
 
 template <int BITS> __device__ constexpr float code_offset() { return BITS == 4 ? 8.f : 128.f; }
 
-// One workgroup = one (token, expert) unit x 32 intermediate columns
-// (gate and up tiles 2cb, 2cb+1).  The four waves split the K tiles.
+// ---------------------------------------------------------------------------
+// Decode items.  An item is 32 intermediate columns (slice J) of one expert for
+// one token: gate/up rows 32J..32J+31 over all 1280 inputs, h = SiLU(g) * u,
+// then the split-K share of the down projection,
+//   part[r] = coef * sum_{j in slice} W_d[r, j] h_j   for all 1280 rows r,
+// coef being the router weight of the pick (1 for the shared expert).  The
+// partials of all items of a token add up to the layer output.  A workgroup of
+// 512 threads (8 waves) runs one item; all of the item's weight bytes are
+// requested up front (ItemRegs) so that they are in flight together.
+// ---------------------------------------------------------------------------
 template <int BITS>
-__global__ __launch_bounds__(256) void dec_gateup_kernel(DecGateUpArgs a) {
-  constexpr int KB = kb_cols(BITS), NKB = H / KB, CPT = KB / 32, KPW = (NKB + 3) / 4;
-  constexpr float OFF = code_offset<BITS>();
-  const int inter = a.w.inter;
-  const int ncb = inter / 32;
-  const int unit = blockIdx.x / ncb, cb = blockIdx.x % ncb;
-  const int t = unit / a.units_per_token;
-  const int e = a.ids ? a.ids[unit] : 0;
-  const uint8_t* gq = a.w.q + (size_t)e * a.w.e_bytes;
-  const float* gs = a.w.s + (size_t)e * a.w.e_scales;
+struct ItemRegs {
+  static constexpr int KB = kb_cols(BITS), NKB = H / KB, CPT = KB / 32;
+  static constexpr int GU_TILES = 4 * NKB, GU_TPW = GU_TILES / 8;   // gate 2 tiles + up 2 tiles per K block
+  static constexpr int DR = down_rows(BITS), NRT = H / DR, D_TPW = (NRT + 7) / 8, RS = DR / 16;
+  uint4 gu[GU_TPW];
+  float gus[GU_TPW][CPT];
+  uint4 dn[D_TPW];
+  float dns[D_TPW][RS];
+};
+
+template <int BITS>
+__device__ __forceinline__ void item_load(ItemRegs<BITS>& R, const uint8_t* eq, const float* es, int inter,
+                                          int group, int J, int wv, int lane) {
+  using IR = ItemRegs<BITS>;
   const size_t mbytes = matrix_bytes(BITS, inter, H);
-  const int ng = H / a.w.group;
-  const int gshift = __builtin_ctz(a.w.group);
+  const int ng = H / group, gsh = __builtin_ctz(group);
   const size_t mscales = (size_t)inter * ng;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q4 = lane >> 4;
-  __shared__ float xs[H];
-  __shared__ float red[4][4][16];
-
-  uint4 code[4][KPW];
-  float sc[4][KPW][CPT];
+  const int r = lane & 15;
 #pragma unroll
-  for (int kk = 0; kk < KPW; ++kk) {
-    const int kb = wv + 4 * kk;
+  for (int m = 0; m < IR::GU_TPW; ++m) {
+    const int t = wv + 8 * m, i = t / IR::NKB, kb = t % IR::NKB;
+    const int ntile = 2 * J + (i & 1), mat = i >> 1;
+    R.gu[m] = *(const uint4*)(eq + mat * mbytes + ((size_t)ntile * IR::NKB + kb) * TILE + lane * 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ntile = 2 * cb + (i & 1);
-      const uint8_t* mq = gq + (i >= 2 ? mbytes : 0);
-      const float* ms = gs + (i >= 2 ? mscales : 0);
-      if (kb < NKB) {
-        code[i][kk] = *(const uint4*)(mq + ((size_t)ntile * NKB + kb) * TILE + lane * 16);
+    for (int c = 0; c < IR::CPT; ++c)
+      R.gus[m][c] = es[mat * mscales + ((size_t)ntile * ng + ((kb * IR::KB + 32 * c) >> gsh)) * 16 + r];
+  }
+  const uint8_t* dq = eq + 2 * mbytes;
+  const float* ds = es + 2 * mscales;
+  const int gd = (SLICE * J) >> gsh;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          const int grp = (kb * KB + 32 * c) >> gshift;
-          sc[i][kk][c] = ms[((size_t)ntile * ng + grp) * 16 + r];
-        }
-      }
+  for (int m = 0; m < IR::D_TPW; ++m) {
+    const int rt = wv + 8 * m;
+    if (rt < IR::NRT) {
+      R.dn[m] = *(const uint4*)(dq + ((size_t)J * IR::NRT + rt) * TILE + lane * 16);
+      const float* sp = ds + (((size_t)gd * IR::NRT + rt) * 16 + r) * IR::RS;
+#pragma unroll
+      for (int j = 0; j < IR::RS; ++j) R.dns[m][j] = sp[j];
     }
-  }
-  for (int k = tid; k < H; k += 256)
-    xs[k] = a.xf ? a.xf[(size_t)t * H + k] : bf16_to_f32(a.xb[(size_t)t * H + k]);
-  __syncthreads();
-
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < KPW; ++kk) {
-    const int kb = wv + 4 * kk;
-    if (kb < NKB) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const float* xp = xs + kb * KB + 32 * c + 8 * q4;
-        float xv[8];
-        *(float4*)&xv[0] = *(const float4*)xp;
-        *(float4*)&xv[4] = *(const float4*)(xp + 4);
-        const float X = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float d = dot8<BITS>(code[i][kk], c, xv);
-          acc[i] += sc[i][kk][c] * (d - OFF * X);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float v = acc[i];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    if (q4 == 0) red[wv][i][r] = v;
-  }
-  __syncthreads();
-  if (tid < 32) {
-    const int ti = tid >> 4, rr = tid & 15;
-    const float g = (red[0][ti][rr] + red[1][ti][rr]) + (red[2][ti][rr] + red[3][ti][rr]);
-    const float u = (red[0][2 + ti][rr] + red[1][2 + ti][rr]) + (red[2][2 + ti][rr] + red[3][2 + ti][rr]);
-    a.h[(size_t)unit * inter + cb * 32 + tid] = silu_mul(g, u);
   }
 }
 
-// One workgroup = one token x 16 output rows; its 8 waves share the
-// (source, K tile) items of the six routed down projections and the shared one,
-// and the partial sums are added in a fixed order (deterministic).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct ItemLds {
+  float part[80 * 16];   // per-tile gate/up partial sums (int8: 80 tiles)
+  float gu[64];          // gate (2x16) and up (2x16) totals
+  float h[SLICE];        // SiLU(g) * u of the slice
+};
+
+// z: the layer input in LDS; out: 1280 partials (coherent stores when the
+// partials are read by other workgroups of the same kernel).
+template <int BITS, bool COHERENT>
+__device__ __forceinline__ void item_compute(const ItemRegs<BITS>& R, const float* z, float coef, float* out,
+                                             ItemLds& L) {
+  using IR = ItemRegs<BITS>;
+  constexpr float OFF = code_offset<BITS>();
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < IR::GU_TPW; ++m) {
+    const int t = wv + 8 * m, kb = t % IR::NKB;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < IR::CPT; ++c) {
+      const float* xp = z + kb * IR::KB + 32 * c + 8 * q;
+      float xv[8];
+      *(float4*)&xv[0] = *(const float4*)xp;
+      *(float4*)&xv[4] = *(const float4*)(xp + 4);
+      const float X = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
+      acc += R.gus[m][c] * (dot8<BITS>(R.gu[m], c, xv) - OFF * X);
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    if (q == 0) L.part[t * 16 + r] = acc;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int i = tid >> 4, rr = tid & 15;
+    float sum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < IR::NKB; ++kb) sum += L.part[(i * IR::NKB + kb) * 16 + rr];
+    L.gu[tid] = sum;
+  }
+  __syncthreads();
+  if (tid < SLICE) L.h[tid] = silu_mul(L.gu[tid], L.gu[32 + tid]);
+  __syncthreads();
+  float xv[8];
+  *(float4*)&xv[0] = *(const float4*)&L.h[8 * q];
+  *(float4*)&xv[4] = *(const float4*)&L.h[8 * q + 4];
+  const float X = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
+#pragma unroll
+  for (int m = 0; m < IR::D_TPW; ++m) {
+    const int rt = wv + 8 * m;
+    if (rt < IR::NRT) {
+#pragma unroll
+      for (int j = 0; j < IR::RS; ++j) {
+        float v = R.dns[m][j] * (dot8<BITS>(R.dn[m], j, xv) - OFF * X);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (q == 0) {
+          float* o = out + IR::DR * rt + 16 * j + r;
+          if (COHERENT) store_coherent(o, coef * v);
+          else *o = coef * v;
+        }
+      }
+    }
+  }
+}
+
+// Decode path of moe_layer_forward: one workgroup per (token, item).
 template <int BR, int BS>
-__global__ __launch_bounds__(512) void dec_down_kernel(DecDownArgs a) {
-  constexpr int KBR = kb_cols(BR), NKR = I / KBR, CPR = KBR / 32;
-  constexpr int KBS = kb_cols(BS), NKS = IS / KBS, CPS = KBS / 32;
-  constexpr int CPM = CPR > CPS ? CPR : CPS;
-  constexpr int ITEMS = TOPK * NKR + NKS, IPW = (ITEMS + 7) / 8;
-  constexpr float OFFR = code_offset<BR>(), OFFS = code_offset<BS>();
-  const int t = blockIdx.x / (H / 16), ntile = blockIdx.x % (H / 16);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q4 = lane >> 4;
-  __shared__ float hs[TOPK * I + IS];
-  __shared__ float red[8][16];
+__global__ __launch_bounds__(512) void dec_items_kernel(DecItemsArgs a) {
+  __shared__ __attribute__((aligned(16))) float z[H];
+  __shared__ __attribute__((aligned(16))) ItemLds L;
+  const int t = blockIdx.x / N_ITEMS, item = blockIdx.x % N_ITEMS;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  float* out = a.part + ((size_t)t * N_ITEMS + item) * H;
+  if (item < R_ITEMS) {
+    const int p = item / (I / SLICE), J = item % (I / SLICE);
+    const int e = a.ids[(size_t)t * TOPK + p];
+    ItemRegs<BR> R;
+    item_load<BR>(R, a.rw.q + (size_t)e * a.rw.e_bytes, a.rw.s + (size_t)e * a.rw.e_scales, I, a.rw.group, J, wv, lane);
+    for (int k = tid; k < H; k += 512) z[k] = a.xf ? a.xf[(size_t)t * H + k] : bf16_to_f32(a.xb[(size_t)t * H + k]);
+    __syncthreads();
+    item_compute<BR, false>(R, z, a.tw[(size_t)t * TOPK + p], out, L);
+  } else {
+    const int J = item - R_ITEMS;
+    ItemRegs<BS> R;
+    item_load<BS>(R, a.sw.q, a.sw.s, IS, a.sw.group, J, wv, lane);
+    for (int k = tid; k < H; k += 512) z[k] = a.xf ? a.xf[(size_t)t * H + k] : bf16_to_f32(a.xb[(size_t)t * H + k]);
+    __syncthreads();
+    item_compute<BS, false>(R, z, 1.0f, out, L);
+  }
+}
 
-  const size_t rdown = 2 * matrix_bytes(BR, I, H), sdown = 2 * matrix_bytes(BS, IS, H);
-  const int ngr = I / a.rw.group, ngs = IS / a.sw.group;
-  const int shr = __builtin_ctz(a.rw.group), shs = __builtin_ctz(a.sw.group);
-  const size_t rdown_s = 2 * (size_t)I * (H / a.rw.group), sdown_s = 2 * (size_t)IS * (H / a.sw.group);
+// y[t][r] (+)= sum over the token's items of part[t][item][r], items in order.
+__global__ __launch_bounds__(256) void dec_reduce_kernel(DecReduceArgs a) {
+  __shared__ float red[8][32];
+  const int t = blockIdx.x / (H / 32), r0 = (blockIdx.x % (H / 32)) * 32;
+  const int tid = threadIdx.x, r = tid & 31, ig = tid >> 5;
+  const float* base = a.part + (size_t)t * N_ITEMS * H + r0 + r;
+  float s = 0.f;
+#pragma unroll 4
+  for (int it = ig; it < N_ITEMS; it += 8) s += base[(size_t)it * H];
+  red[ig][r] = s;
+  __syncthreads();
+  if (tid < 32) {
+    float v = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) v += red[g][tid];
+    const size_t yi = (size_t)t * H + r0 + tid;
+    a.y[yi] = (a.accumulate ? a.y[yi] : 0.f) + v;
+  }
+}
 
-  uint4 code[IPW];
-  float sc[IPW][CPM];
-#pragma unroll
-  for (int m = 0; m < IPW; ++m) {
-    const int it = wv + 8 * m;
-    if (it < TOPK * NKR) {
-      const int j = it / NKR, kb = it % NKR;
-      const int e = a.ids[(size_t)t * TOPK + j];
-      const uint8_t* base = a.rw.q + (size_t)e * a.rw.e_bytes + rdown;
-      const float* sbase = a.rw.s + (size_t)e * a.rw.e_scales + rdown_s;
-      code[m] = *(const uint4*)(base + ((size_t)ntile * NKR + kb) * TILE + lane * 16);
-#pragma unroll
-      for (int c = 0; c < CPR; ++c)
-        sc[m][c] = sbase[((size_t)ntile * ngr + ((kb * KBR + 32 * c) >> shr)) * 16 + r];
-    } else if (it < ITEMS) {
-      const int kb = it - TOPK * NKR;
-      const uint8_t* base = a.sw.q + sdown;
-      const float* sbase = a.sw.s + sdown_s;
-      code[m] = *(const uint4*)(base + ((size_t)ntile * NKS + kb) * TILE + lane * 16);
-#pragma unroll
-      for (int c = 0; c < CPS; ++c)
-        sc[m][c] = sbase[((size_t)ntile * ngs + ((kb * KBS + 32 * c) >> shs)) * 16 + r];
+// ---------------------------------------------------------------------------
+// Persistent decode step: one token through n_layers chained layers in one
+// cooperative launch.  Workgroups 0..223 are items (routed picks 0..5 x 28
+// slices, then 56 shared slices), workgroups 224..255 are reducers owning 40
+// rows of the residual stream each.  Per layer:
+//   reducers (stage s): h_s = (h_{s-1}) + sum of the items' partials of layer
+//     s-1, written to y; partial router logits W_r[:, rows] h_s[rows] and the
+//     partial sum of squares, then a flag;
+//   items (layer s): wait for all reducer flags, rebuild RMSNorm(h_s), the
+//     64 logits, softmax and top-6 from the partials (every routed item
+//     computes the same routing), stream their expert slice and write their
+//     partial, then a flag.
+// No grid-wide barrier: each side polls only the flags it depends on.  Flags
+// carry epoch numbers (call sequence * 64 + stage + 1), so nothing has to be
+// cleared between calls.  Data exchanged inside the kernel uses device-scope
+// (L2-coherent) loads and stores.
+// ---------------------------------------------------------------------------
+constexpr long SPIN_LIMIT = 1L << 20;  // polls before a wait gives up (about a second)
+
+__device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* err) {
+  const int lane = threadIdx.x & 63;
+  long spins = 0;
+  while (true) {
+    bool ok = true;
+    for (int i = lane; i < n; i += 64) ok &= load_coherent_u32(flags + i) == epoch;
+    if (__all(ok)) break;
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > SPIN_LIMIT) {
+      if (lane == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
     }
   }
-  for (int k = tid; k < TOPK * I; k += 512) hs[k] = a.h_routed[(size_t)t * TOPK * I + k];
-  for (int k = tid; k < IS; k += 512) hs[TOPK * I + k] = a.h_shared[(size_t)t * IS + k];
-  __syncthreads();
+}
 
-  float acc = 0.f;
+struct ChainLds {
+  float z[H];
+  ItemLds item;
+  float qs[N_RED * Q_STRIDE];
+  float red[12][RED_ROWS];
+  float hrow[RED_ROWS];
+  int pick_e[TOPK];
+  float pick_w[TOPK];
+  float inv;
+};
+
+// Wait for the reducers of stage l, then rebuild this layer's input z (in
+// LDS) and, for routed items, the routing.  Identical arithmetic in every
+// workgroup, so every item sees the same z and the same picks.
+__device__ __forceinline__ void chain_layer_input(const ChainArgs& a, ChainLds& S, int l, uint32_t epoch,
+                                                  bool routed, bool report, uint32_t* err) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (wv == 0) wait_flags(a.red_flag, N_RED, epoch, err);
+  __syncthreads();
+  for (int k = tid; k < H; k += 512) S.z[k] = load_coherent(a.y + k);
+  for (int k = tid; k < N_RED * Q_STRIDE; k += 512) S.qs[k] = load_coherent(a.q + k);
+  __syncthreads();
+  if (wv == 0) {
+    float ss = 0.f;
+    for (int rr = 0; rr < N_RED; ++rr) ss += S.qs[rr * Q_STRIDE + 64];
+    const float inv = a.norm ? 1.0f / sqrtf(ss / (float)H + a.eps) : 1.0f;
+    if (lane == 0) S.inv = inv;
+    if (routed) {
+      const float* bias = a.layer[l].bias;
+      float lg = 0.f;
+      for (int rr = 0; rr < N_RED; ++rr) lg += S.qs[rr * Q_STRIDE + lane];
+      lg = lg * inv + (bias ? bias[lane] : 0.f);
+      const float m = wave_max(lg);
+      const float ex = expf(lg - m);
+      const float pr = ex / wave_sum(ex);
+      bool taken = false;
+      for (int j = 0; j < TOPK; ++j) {
+        float bv = taken ? -1.f : pr;
+        int bi = lane;
 #pragma unroll
-  for (int m = 0; m < IPW; ++m) {
-    const int it = wv + 8 * m;
-    if (it < TOPK * NKR) {
-      const int j = it / NKR, kb = it % NKR;
-      const float coef = a.tw[(size_t)t * TOPK + j];
-#pragma unroll
-      for (int c = 0; c < CPR; ++c) {
-        const float* xp = hs + j * I + kb * KBR + 32 * c + 8 * q4;
-        float xv[8];
-        *(float4*)&xv[0] = *(const float4*)xp;
-        *(float4*)&xv[4] = *(const float4*)(xp + 4);
-        const float X = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
-        acc += coef * sc[m][c] * (dot8<BR>(code[m], c, xv) - OFFR * X);
-      }
-    } else if (it < ITEMS) {
-      const int kb = it - TOPK * NKR;
-#pragma unroll
-      for (int c = 0; c < CPS; ++c) {
-        const float* xp = hs + TOPK * I + kb * KBS + 32 * c + 8 * q4;
-        float xv[8];
-        *(float4*)&xv[0] = *(const float4*)xp;
-        *(float4*)&xv[4] = *(const float4*)(xp + 4);
-        const float X = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
-        acc += sc[m][c] * (dot8<BS>(code[m], c, xv) - OFFS * X);
+        for (int o = 32; o >= 1; o >>= 1) {
+          const float ov = __shfl_xor(bv, o);
+          const int oi = __shfl_xor(bi, o);
+          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+        }
+        if (lane == bi) taken = true;
+        if (lane == 0) {
+          S.pick_e[j] = bi;
+          S.pick_w[j] = bv;
+          if (report) { a.ids[l * TOPK + j] = bi; a.tw[l * TOPK + j] = bv; }
+        }
       }
     }
   }
-  acc += __shfl_xor(acc, 16);
-  acc += __shfl_xor(acc, 32);
-  if (q4 == 0) red[wv][r] = acc;
   __syncthreads();
-  if (tid < 16) {
-    float total = 0.f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) total += red[w][tid];
-    const size_t yi = (size_t)t * H + ntile * 16 + tid;
-    a.y[yi] = (a.accumulate ? a.y[yi] : 0.f) + total;
+  const float inv = S.inv;
+  for (int k = tid; k < H; k += 512) S.z[k] = S.z[k] * inv;
+  __syncthreads();
+}
+
+__device__ __forceinline__ void chain_item_done(const ChainArgs& a, int b, uint32_t epoch) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) store_coherent_u32(a.item_flag + b, epoch);
+}
+
+template <int BR>
+__device__ void chain_routed(const ChainArgs& a, ChainLds& S, int b, uint32_t base, uint32_t* err) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int p = b / (I / SLICE), J = b % (I / SLICE);
+  const size_t ebytes = 3 * matrix_bytes(BR, I, H), escales = 3 * (size_t)I * H / a.rgroup;
+  for (int l = 0; l < a.n_layers; ++l) {
+    chain_layer_input(a, S, l, base + l + 1, true, b == 0, err);
+    const int e = S.pick_e[p];
+    ItemRegs<BR> R;
+    item_load<BR>(R, a.layer[l].eq + (size_t)e * ebytes, a.layer[l].es + (size_t)e * escales, I, a.rgroup, J, wv, lane);
+    item_compute<BR, true>(R, S.z, S.pick_w[p], a.part + (size_t)b * H, S.item);
+    chain_item_done(a, b, base + l + 1);
   }
+  (void)tid;
+}
+
+template <int BS>
+__device__ void chain_shared(const ChainArgs& a, ChainLds& S, int b, uint32_t base, uint32_t* err) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int J = b - R_ITEMS;
+  for (int l = 0; l < a.n_layers; ++l) {
+    ItemRegs<BS> R;
+    item_load<BS>(R, a.layer[l].sq, a.layer[l].ss, IS, a.sgroup, J, wv, lane);  // routing-independent: before the wait
+    chain_layer_input(a, S, l, base + l + 1, false, false, err);
+    item_compute<BS, true>(R, S.z, 1.0f, a.part + (size_t)b * H, S.item);
+    chain_item_done(a, b, base + l + 1);
+  }
+  (void)tid;
+}
+
+__device__ void chain_reducer(const ChainArgs& a, ChainLds& S, int rid, uint32_t base, uint32_t* err) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r0 = rid * RED_ROWS;
+  const int e = tid >> 3, sub = tid & 7;   // partial logits: expert e, rows sub + 8m
+  for (int s = 0; s <= a.n_layers; ++s) {
+    float wr[5];
+    if (s < a.n_layers) {
+#pragma unroll
+      for (int m = 0; m < 5; ++m) wr[m] = a.layer[s].wr[(size_t)e * H + r0 + sub + 8 * m];
+    }
+    if (s == 0) {
+      if (tid < RED_ROWS) {
+        const int k = r0 + tid;
+        S.hrow[tid] = a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x)[k]) : ((const float*)a.x)[k];
+      }
+    } else {
+      if (wv == 0) wait_flags(a.item_flag, N_ITEMS, base + s, err);
+      __syncthreads();
+      if (tid < 12 * RED_ROWS) {
+        const int rr = tid % RED_ROWS, ig = tid / RED_ROWS;
+        float acc = 0.f;
+        for (int it = ig; it < N_ITEMS; it += 12) acc += load_coherent(a.part + (size_t)it * H + r0 + rr);
+        S.red[ig][rr] = acc;
+      }
+      __syncthreads();
+      if (tid < RED_ROWS) {
+        float v = 0.f;
+#pragma unroll
+        for (int g = 0; g < 12; ++g) v += S.red[g][tid];
+        S.hrow[tid] = (a.accumulate ? S.hrow[tid] : 0.f) + v;
+      }
+    }
+    __syncthreads();
+    if (tid < RED_ROWS) store_coherent(a.y + r0 + tid, S.hrow[tid]);
+    if (s < a.n_layers) {
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < 5; ++m) part += wr[m] * S.hrow[sub + 8 * m];
+      part += __shfl_xor(part, 1);
+      part += __shfl_xor(part, 2);
+      part += __shfl_xor(part, 4);
+      if (sub == 0) store_coherent(a.q + rid * Q_STRIDE + e, part);
+      if (wv == 0) {
+        const float v = lane < RED_ROWS ? S.hrow[lane] : 0.f;
+        const float ss = wave_sum(v * v);
+        if (lane == 0) store_coherent(a.q + rid * Q_STRIDE + 64, ss);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) store_coherent_u32(a.red_flag + rid, base + s + 1);
+    }
+  }
+}
+
+template <int BR, int BS>
+__global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
+  __shared__ __attribute__((aligned(16))) ChainLds S;
+  const int b = blockIdx.x;
+  const uint32_t base = load_coherent_u32(a.hdr) * 64u;
+  uint32_t* err = a.hdr + 2;
+  if (b < R_ITEMS) chain_routed<BR>(a, S, b, base, err);
+  else if (b < N_ITEMS) chain_shared<BS>(a, S, b, base, err);
+  else chain_reducer(a, S, b - N_ITEMS, base, err);
+  // the last workgroup to finish advances the call sequence
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(a.hdr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gridDim.x - 1) {
+      store_coherent_u32(a.hdr + 1, 0u);
+      store_coherent_u32(a.hdr, load_coherent_u32(a.hdr) + 1u);
+    }
+  }
+}
+
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -612,13 +827,15 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
     }
 }
 
-// Down: a workgroup owns one 32-row tile and 128 output columns; wave w
-// computes n-subtiles 8cb + 2w and 8cb + 2w + 1.  A = h (fp32) split hi/lo.
+// Down: a workgroup owns one 32-row tile of A (h, fp32 split hi/lo) and four
+// packed down tiles' worth of output rows: wave w covers row tile 4cb + w,
+// i.e. 64 (int4) or 32 (int8) output columns, one 16-column MFMA n-subtile
+// per 16 rows.  Each 16-byte lane load of a down tile feeds every n-subtile of
+// the row tile for one 32-wide K chunk.
 template <int BITS>
 __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
-  constexpr int KB = kb_cols(BITS);
-  const int inter = a.w.inter, nkb = inter / KB, nstage = inter / KS;
-  constexpr int NCB = H / 128;
+  constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4;
+  const int inter = a.w.inter, nstage = inter / KS;
   const int tile = blockIdx.x / NCB, cb = blockIdx.x % NCB;
   const TileInfo ti = tile_info(a, tile);
   if (!ti.valid) return;
@@ -626,27 +843,24 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[2 * 32 * LDS_ROW];
   __shared__ int arow[MT];
   if (tid < MT) arow[tid] = tid < ti.nrows ? (a.shared ? ti.row0 + tid : ti.pbase + tid) : -1;
-  const uint8_t* dq = a.w.q + (size_t)ti.e * a.w.e_bytes + 2 * matrix_bytes(BITS, inter, H);
-  const int ng = inter / a.w.group, cpg = a.w.group / 32;
+  const size_t mbytes = matrix_bytes(BITS, inter, H);
+  const uint8_t* dq = a.w.q + (size_t)ti.e * a.w.e_bytes + 2 * mbytes;
+  const int cpg = a.w.group / 32;
   const float* ds = a.w.s + (size_t)ti.e * a.w.e_scales + 2 * (size_t)inter * (H / a.w.group);
-  const int nt0 = 8 * cb + 2 * wv;
+  const int rt = 4 * cb + wv;
 
-  float4v acc[2][2], ctmp[2][2];
+  float4v acc[NSUB][2], ctmp[NSUB][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < NSUB; ++j)
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) { acc[i][ms] = float4v{0, 0, 0, 0}; ctmp[i][ms] = float4v{0, 0, 0, 0}; }
+    for (int ms = 0; ms < 2; ++ms) { acc[j][ms] = float4v{0, 0, 0, 0}; ctmp[j][ms] = float4v{0, 0, 0, 0}; }
   __syncthreads();
 
   for (int st = 0; st < nstage; ++st) {
-    uint4 bq[2][2];
+    uint4 bq[KS / 32];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int h = 0; h < (BITS == 4 ? 1 : 2); ++h) {
-        const int kb = st * (KS / KB) + h;
-        bq[i][h] = *(const uint4*)(dq + ((size_t)(nt0 + i) * nkb + kb) * TILE + lane * 16);
-      }
+    for (int c = 0; c < KS / 32; ++c)
+      bq[c] = *(const uint4*)(dq + ((size_t)(st * (KS / 32) + c) * NRT + rt) * TILE + lane * 16);
     __syncthreads();
     stage_a<BITS, true>(lds, a.af, nullptr, arow, inter, st * KS);
     __syncthreads();
@@ -654,32 +868,32 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
     for (int c = 0; c < KS / 32; ++c) {
       const int gc = st * (KS / 32) + c;
       const bool first = (gc % cpg) == 0, last = (gc % cpg) == cpg - 1;
-      half8 bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (BITS == 4) bfr[i] = unpack_int4(word_of(bq[i][0], c));
-        else bfr[i] = unpack_int8(word_of(bq[i][c >> 1], 2 * (c & 1)), word_of(bq[i][c >> 1], 2 * (c & 1) + 1));
-      }
+      const int lcol = 32 * c + 8 * q4;
+      half8 ahi[2], alo[2];
 #pragma unroll
       for (int ms = 0; ms < 2; ++ms) {
-        const int lrow = ms * 16 + r, lcol = 32 * c + 8 * q4;
-        const half8 ahi = *(const half8*)(lds + lrow * LDS_ROW + lcol);
-        const half8 alo = *(const half8*)(lds + 32 * LDS_ROW + lrow * LDS_ROW + lcol);
+        ahi[ms] = *(const half8*)(lds + (ms * 16 + r) * LDS_ROW + lcol);
+        alo[ms] = *(const half8*)(lds + 32 * LDS_ROW + (ms * 16 + r) * LDS_ROW + lcol);
+      }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[i][ms];
-          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bfr[i], cc, 0, 0, 0);
-          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bfr[i], cc, 0, 0, 0);
-          ctmp[i][ms] = cc;
+      for (int j = 0; j < NSUB; ++j) {
+        const half8 bfr = BITS == 4 ? unpack_int4(word_of(bq[c], j))
+                                    : unpack_int8(word_of(bq[c], 2 * j), word_of(bq[c], 2 * j + 1));
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+          float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[j][ms];
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ms], bfr, cc, 0, 0, 0);
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ms], bfr, cc, 0, 0, 0);
+          ctmp[j][ms] = cc;
         }
       }
       if (last) {
-        const int grp = gc / cpg;
+        const float* sp = ds + (((size_t)(gc / cpg) * NRT + rt) * 16 + r) * NSUB;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const float s = ds[((size_t)(nt0 + i) * ng + grp) * 16 + r];
+        for (int j = 0; j < NSUB; ++j) {
+          const float sj = sp[j];
 #pragma unroll
-          for (int ms = 0; ms < 2; ++ms) acc[i][ms] += s * ctmp[i][ms];
+          for (int ms = 0; ms < 2; ++ms) acc[j][ms] += sj * ctmp[j][ms];
         }
       }
     }
@@ -692,7 +906,7 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
       if (m < ti.nrows) {
         const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a.out[orow * H + 16 * (nt0 + i) + r] = acc[i][ms][k];
+        for (int j = 0; j < NSUB; ++j) a.out[orow * H + DR * rt + 16 * j + r] = acc[j][ms][k];
       }
     }
 }
@@ -742,22 +956,38 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_dec_gateup(const DecGateUpArgs& a, int units, hipStream_t s) {
-  const dim3 grid(units * (a.w.inter / 32));
-  if (a.w.bits == 4) hipLaunchKernelGGL(dec_gateup_kernel<4>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(dec_gateup_kernel<8>, grid, dim3(256), 0, s, a);
+hipError_t launch_dec_items(const DecItemsArgs& a, int T, hipStream_t s) {
+  const dim3 grid(T * N_ITEMS);
+  const int key = (a.rw.bits == 8) * 2 + (a.sw.bits == 8);
+  switch (key) {
+    case 0: hipLaunchKernelGGL((dec_items_kernel<4, 4>), grid, dim3(512), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dec_items_kernel<4, 8>), grid, dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dec_items_kernel<8, 4>), grid, dim3(512), 0, s, a); break;
+    default: hipLaunchKernelGGL((dec_items_kernel<8, 8>), grid, dim3(512), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_dec_down(const DecDownArgs& a, int T, hipStream_t s) {
-  const dim3 grid(T * (H / 16));
-  const int key = (a.rw.bits == 8) * 2 + (a.sw.bits == 8);
+hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s) {
+  hipLaunchKernelGGL(dec_reduce_kernel, dim3(T * (H / 32)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chain(const ChainArgs& a, hipStream_t s) {
+  void* args[] = {(void*)&a};
+  const void* fn;
+  const int key = (a.rbits == 8) * 2 + (a.sbits == 8);
   switch (key) {
-    case 0: hipLaunchKernelGGL((dec_down_kernel<4, 4>), grid, dim3(512), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((dec_down_kernel<4, 8>), grid, dim3(512), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dec_down_kernel<8, 4>), grid, dim3(512), 0, s, a); break;
-    default: hipLaunchKernelGGL((dec_down_kernel<8, 8>), grid, dim3(512), 0, s, a); break;
+    case 0: fn = (const void*)chain_kernel<4, 4>; break;
+    case 1: fn = (const void*)chain_kernel<4, 8>; break;
+    case 2: fn = (const void*)chain_kernel<8, 4>; break;
+    default: fn = (const void*)chain_kernel<8, 8>; break;
   }
+  return hipLaunchCooperativeKernel(fn, dim3(N_ITEMS + N_RED), dim3(512), args, 0, s);
+}
+
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 
@@ -780,7 +1010,7 @@ hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, hipStream_
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, hipStream_t s) {
-  const dim3 grid(max_tiles * (H / 128));
+  const dim3 grid(max_tiles * (H / (4 * down_rows(a.w.bits))));
   if (a.w.bits == 4) hipLaunchKernelGGL(grouped_down_kernel<4>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(grouped_down_kernel<8>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

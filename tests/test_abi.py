@@ -27,8 +27,8 @@ def test_status_strings(lib):
     assert b"unknown" in lib.moe_status_str(99)
 
 
-def _unpack_matrix(buf, N, K, bits):
-    """Decode the packed tile layout described in include/moe.h (independent of the packer)."""
+def _unpack_rows(buf, N, K, bits):
+    """Decode the gate/up tile layout described in include/moe.h (independent of the packer)."""
     KB = 128 if bits == 4 else 64
     out = np.zeros((N, K), np.int64)
     words = np.frombuffer(buf, dtype="<u4")
@@ -48,6 +48,29 @@ def _unpack_matrix(buf, N, K, bits):
     return out
 
 
+def _unpack_slabs(buf, K, bits, n_kc):
+    """Decode the first n_kc 32-column slabs of a down matrix ([1280][K])."""
+    DR = 64 if bits == 4 else 32
+    nrt = 1280 // DR
+    out = np.zeros((1280, 32 * n_kc), np.int64)
+    words = np.frombuffer(buf, dtype="<u4")
+    for kc in range(n_kc):
+        for rt in range(nrt):
+            base = (kc * nrt + rt) * 256
+            for lane in range(64):
+                r, q = lane % 16, lane // 16
+                for j in range(4):
+                    w = int(words[base + lane * 4 + j])
+                    if bits == 4:
+                        for i in range(8):
+                            out[DR * rt + 16 * j + r, 32 * kc + 8 * q + i] = ((w >> (4 * i)) & 15) - 8
+                    else:
+                        for i in range(4):
+                            out[DR * rt + 16 * (j // 2) + r, 32 * kc + 8 * q + 4 * (j % 2) + i] = \
+                                ((w >> (8 * i)) & 255) - 128
+    return out
+
+
 @pytest.mark.parametrize("bits,group", [(4, 32), (8, 128)])
 def test_pack_round_trip(lib, bits, group):
     rng = np.random.default_rng(bits)
@@ -64,15 +87,17 @@ def test_pack_round_trip(lib, bits, group):
     codes, scales = B.moe_pack_expert(gate, up, down, gs, us, ds, bits, group)
     mb = inter * 1280 * bits // 8
     assert codes.size == 3 * mb
-    # decode only a slice of tiles of each matrix to keep the pure-Python decoder fast
-    np.testing.assert_array_equal(_unpack_matrix(codes[:mb][: 16 * 1280 * bits // 8 * 2], 32, 1280, bits), gate[:32])
-    np.testing.assert_array_equal(_unpack_matrix(codes[mb:2 * mb][: 16 * 1280 * bits // 8], 16, 1280, bits), up[:16])
-    np.testing.assert_array_equal(_unpack_matrix(codes[2 * mb:][: 16 * inter * bits // 8], 16, inter, bits), down[:16])
+    # decode only the first tiles of each matrix to keep the pure-Python decoder fast
+    np.testing.assert_array_equal(_unpack_rows(codes[:mb][: 16 * 1280 * bits // 8 * 2], 32, 1280, bits), gate[:32])
+    np.testing.assert_array_equal(_unpack_rows(codes[mb:2 * mb][: 16 * 1280 * bits // 8], 16, 1280, bits), up[:16])
+    np.testing.assert_array_equal(_unpack_slabs(codes[2 * mb:], inter, bits, 2), down[:, :64])
     ng = 1280 // group
     sg = scales[: inter * ng].reshape(inter // 16, ng, 16)
     np.testing.assert_array_equal(sg.transpose(0, 2, 1).reshape(inter, ng), gs)
-    sd = scales[2 * inter * ng:].reshape(1280 // 16, inter // group, 16)
-    np.testing.assert_array_equal(sd.transpose(0, 2, 1).reshape(1280, inter // group), ds)
+    DR = 64 if bits == 4 else 32
+    sd = scales[2 * inter * ng:].reshape(inter // group, 1280 // DR, 16, DR // 16)
+    # entry (g, rt, r, j) is row DR*rt + 16j + r
+    np.testing.assert_array_equal(sd.transpose(1, 3, 2, 0).reshape(1280, inter // group), ds)
 
 
 def test_pack_rejects_bad_codes_and_formats(lib):
@@ -104,7 +129,9 @@ def test_forward_validation_codes(lib):
     assert _fwd(lib, eb=5) == 3
     assert _fwd(lib, sg=16) == 3
     assert _fwd(lib, y=0x10008) == 4
-    assert _fwd(lib, rb=0x10004) == 4
+    assert _fwd(lib, rb=0x10002) == 4
+    assert _fwd(lib, T=0, ids=0x10004, w=0x10008) == 0   # 4-byte aligned ids/weights are accepted
+    assert _fwd(lib, eq=0x10004) == 4
     assert _fwd(lib, wsb=16) == 5
     assert _fwd(lib, flags=1 << 9) == 7
     assert _fwd(lib, flags=B.MOE_FORCE_DECODE | B.MOE_FORCE_GROUPED) == 7
@@ -130,3 +157,29 @@ def test_rmsnorm_validation(lib):
     assert lib.moe_rmsnorm(0x100, 0x104, 0, 1, 1e-6, None) == 4
     assert lib.moe_rmsnorm(0x100, 0x200, 3, 1, 1e-6, None) == 7
     assert lib.moe_rmsnorm(0x100, 0x200, 0, 0, 1e-6, None) == 0
+
+
+def test_decode_forward_validation(lib):
+    A = 0x10000
+    L = (B.LayerWeights * 2)(B.LayerWeights(A, None, A, A, A, A), B.LayerWeights(A, None, A, A, A, A))
+    def fwd(**kw):
+        a = dict(x=A, xd=0, y=A, n=2, layers=L, eb=4, eg=64, sb=8, sg=128, ids=A, w=A, ws=A, wsb=1 << 30,
+                 flags=0, stream=None)
+        a.update(kw)
+        return lib.moe_decode_forward(a["x"], a["xd"], a["y"], a["n"], a["layers"], a["eb"], a["eg"], a["sb"],
+                                      a["sg"], a["ids"], a["w"], a["ws"], a["wsb"], a["flags"], a["stream"])
+    assert fwd(x=None) == 1
+    assert fwd(n=0) == 2 and fwd(n=17) == 2
+    assert fwd(eg=16) == 3
+    assert fwd(flags=B.MOE_NORM_BF16 | B.MOE_NORM_INPUT) == 7
+    assert fwd(flags=B.MOE_FORCE_DECODE) == 7
+    assert fwd(xd=1) == 7                    # bf16 input cannot alias the f32 output
+    assert fwd(ws=0x10008) == 4
+    assert fwd(wsb=100) == 5
+    bad = (B.LayerWeights * 2)(B.LayerWeights(A, None, A, A, A, A), B.LayerWeights(A, None, 0x10008, A, A, A))
+    assert fwd(layers=bad) == 4
+    nul = (B.LayerWeights * 2)(B.LayerWeights(A, None, A, A, A, A), B.LayerWeights(None, None, A, A, A, A))
+    assert fwd(layers=nul) == 1
+    assert lib.moe_decode_workspace_init(None, 0, None) == 1
+    assert lib.moe_decode_workspace_init(A, 16, None) == 5
+    assert B.moe_decode_workspace_bytes() > 224 * 1280 * 4
