@@ -98,8 +98,8 @@ const char* moe_status_str(int32_t status);
  * Packed layout written to codes_out (moe_expert_code_bytes() bytes):
  *   [gate | up | down]; every matrix is a sequence of 1 KiB tiles, and inside
  *   a tile lane l = 0..63 owns bytes 16l..16l+15, i.e. four 32-bit words
- *   w0..w3, with r = l % 16 and q = l / 16.  Codes are stored offset-binary
- *   (int4: code + 8 in one nibble; int8: code + 128 in one byte).
+ *   w0..w3, with r = l % 16 and q = l / 16.  Codes are stored as two's
+ *   complement (int4: one nibble; int8: one byte).
  *   gate and up ([N = inter rows][K = 1280]): tiles of 16 rows x KB columns,
  *     KB = 128 (int4) or 64 (int8), tile (nt, kb) at byte 1024*(nt*(K/KB) + kb);
  *     row 16nt + r;
@@ -114,9 +114,9 @@ const char* moe_status_str(int32_t status);
  *   (A 32-column slab of the down matrix, which is what one slice of the
  *   intermediate dimension multiplies, is contiguous.)
  * Packed scales written to scales_out (moe_expert_scale_count() floats):
- *   [gate | up | down]; gate and up are [N/16][K/G][16] with entry (nt, g, r)
- *   = scale of row 16nt + r, group g; down is [K/G][1280/DR][16][DR/16] with
- *   entry (g, rt, r, j) = scale of row DR*rt + 16j + r, group g.
+ *   [gate | up | down]; gate and up keep the canonical row-major [N][K/G];
+ *   down is [K/G][1280/DR][16][DR/16] with entry (g, rt, r, j) = scale of row
+ *   DR*rt + 16j + r, group g.
  * Experts of a layer are concatenated: expert e at byte e * code_bytes and
  * float e * scale_count.
  * ------------------------------------------------------------------------ */
@@ -152,9 +152,12 @@ size_t moe_workspace_bytes(int32_t n_tokens);
  * workspace    device scratch of at least moe_workspace_bytes(n_tokens)
  *              bytes; its contents need no initialisation and are garbage
  *              after the call.
- * Routing is computed in f32; expert arithmetic multiplies exact integer codes
- * by the inputs with fp32 accumulation and applies each group scale to the
- * fp32 partial sum of its group.
+ * Routing is computed in f32.  Expert arithmetic: the grouped (MFMA) path
+ * multiplies exact integer codes by f16 inputs (f32 inputs split into two f16
+ * halves) with fp32 accumulation; the per-token path writes each input block
+ * in block floating point (19-bit mantissa for int4 weights, 23-bit for int8,
+ * one shared power of two per scale group) and forms exact integer dot
+ * products.  Both apply each group scale to the partial sum of its group.
  * ------------------------------------------------------------------------ */
 moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
                                const float* router_w, const float* router_b,

@@ -116,10 +116,10 @@ void pack_rows(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
         for (int j = 0; j < 4; ++j) {
           uint32_t word = 0;
           if (bits == 4) {
-            for (int i = 0; i < 8; ++i) word |= (uint32_t)(src[32 * j + 8 * q + i] + 8) << (4 * i);
+            for (int i = 0; i < 8; ++i) word |= (uint32_t)(src[32 * j + 8 * q + i] & 15) << (4 * i);
           } else {
             for (int i = 0; i < 4; ++i)
-              word |= (uint32_t)(uint8_t)(src[32 * (j >> 1) + 8 * q + 4 * (j & 1) + i] + 128) << (8 * i);
+              word |= (uint32_t)(uint8_t)src[32 * (j >> 1) + 8 * q + 4 * (j & 1) + i] << (8 * i);
           }
           memcpy(tile + lane * 16 + 4 * j, &word, 4);
         }
@@ -139,10 +139,10 @@ void pack_slabs(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
           uint32_t word = 0;
           if (bits == 4) {
             const int8_t* src = Q + (size_t)(DR * rt + 16 * j + r) * K + 32 * kc + 8 * q;
-            for (int i = 0; i < 8; ++i) word |= (uint32_t)(src[i] + 8) << (4 * i);
+            for (int i = 0; i < 8; ++i) word |= (uint32_t)(src[i] & 15) << (4 * i);
           } else {
             const int8_t* src = Q + (size_t)(DR * rt + 16 * (j >> 1) + r) * K + 32 * kc + 8 * q + 4 * (j & 1);
-            for (int i = 0; i < 4; ++i) word |= (uint32_t)(uint8_t)(src[i] + 128) << (8 * i);
+            for (int i = 0; i < 4; ++i) word |= (uint32_t)(uint8_t)src[i] << (8 * i);
           }
           memcpy(tile + lane * 16 + 4 * j, &word, 4);
         }
@@ -150,11 +150,9 @@ void pack_slabs(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
     }
 }
 
+// gate/up scales stay row-major [row][group]
 void pack_row_scales(const float* S, int N, int K, int group, float* out) {
-  const int ng = K / group;
-  for (int nt = 0; nt < N / 16; ++nt)
-    for (int g = 0; g < ng; ++g)
-      for (int r = 0; r < 16; ++r) out[((size_t)nt * ng + g) * 16 + r] = S[(size_t)(nt * 16 + r) * ng + g];
+  memcpy(out, S, (size_t)N * (K / group) * sizeof(float));
 }
 
 void pack_slab_scales(const float* S, int N, int K, int group, int bits, float* out) {

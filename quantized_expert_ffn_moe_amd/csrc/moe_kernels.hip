@@ -8,9 +8,10 @@
 //
 // Two expert paths:
 //  * GEMV path (few tokens): every (token, pick) streams its expert's packed
-//    1 KiB tiles with 16-byte loads per lane, converts the offset-binary codes
-//    in registers (v_cvt_f32_ubyte*) and accumulates in fp32 on the VALU.  The
-//    group scale multiplies the fp32 partial sum of its group.
+//    1 KiB tiles with 16-byte loads per lane and multiplies the codes as they
+//    are (two's complement) with integer dot-product instructions against a
+//    block-floating-point digit expansion of the input; the group scale
+//    multiplies the exact integer partial sum of its group.
 //  * Grouped path (many tokens): tokens are bucketed per expert (histogram +
 //    stable permutation) and each expert's bucket runs as a dense GEMM on the
 //    MFMA units (v_mfma_f32_16x16x32_f16).  The codes become exact f16 integers
@@ -21,6 +22,16 @@
 #include "moe_internal.h"
 
 namespace moe {
+
+// Optional device timestamps for timeline studies: compiled only when
+// MOE_DEVICE_TRACE is defined (never in the shipped library).
+#ifdef MOE_DEVICE_TRACE
+__device__ unsigned long long* g_trace;
+#define MOE_TRACE(b, l, e) \
+  do { if (threadIdx.x == 0 && g_trace) g_trace[((b) * 16 + (l)) * 16 + (e)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#else
+#define MOE_TRACE(b, l, e) do { } while (0)
+#endif
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -152,43 +163,99 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMV path helpers.  A lane of a packed tile holds, per 32-wide K chunk, the
-// 8 codes k = 32c + 8q + i (q = lane / 16) of row lane % 16.
-// dot8 returns sum_i code_i * x_i over those 8 codes, codes read offset-binary.
+// GEMV arithmetic: exact integer dot products.  The input vector is written in
+// block floating point: a block of consecutive elements shares 2^e with
+// max|x| < 2^e, and each element becomes a signed integer mantissa
+// m = rint(x * 2^(F - e)), |m| <= 2^F, split into balanced digits
+// (int4 weights: 5 base-16 digits in [-8, 7], F = 18; int8 weights: 3 base-256
+// digits in [-128, 127], F = 22).  v_dot8_i32_i4 / v_dot4_i32_i8 multiply the
+// two's-complement weight codes by one digit plane at a time with exact int32
+// sums; the planes are recombined per scale group and the group's f32 scale
+// and 2^(e - F) are applied once.  The only rounding is that of m (half a unit
+// of 2^(e - F), i.e. 2^-19 or 2^-23 of the block maximum) and the f32
+// accumulation across groups.
+//
+// Plane layout (LDS, u32 words, 8 per group of 8 consecutive elements kg):
+//   int4: word j < 5  = digit j of elements 8kg..8kg+7 in nibbles 0..7
+//   int8: word 2j + h = digit j of elements 8kg+4h..8kg+4h+3 in bytes 0..3
+// which matches the code order of a lane's word(s) in a packed tile.
 // ---------------------------------------------------------------------------
+template <int BITS> struct Digits {
+  static constexpr int ND = BITS == 4 ? 5 : 3;     // digit planes
+  static constexpr int F = BITS == 4 ? 18 : 22;    // mantissa magnitude bits
+};
+
+// One thread per group of 8 elements (kg < n/8); blocks of `blk` elements
+// (blk / 8 consecutive threads, at most 16, all in one wave).
 template <int BITS>
-__device__ __forceinline__ float dot8(const uint4& v, int c, const float* xv);
-
-template <>
-__device__ __forceinline__ float dot8<4>(const uint4& v, int c, const float* xv) {
-  const uint32_t w = word_of(v, c);
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  float d = (float)(lo & 0xFFu) * xv[0];
-  d += (float)(hi & 0xFFu) * xv[1];
-  d += (float)((lo >> 8) & 0xFFu) * xv[2];
-  d += (float)((hi >> 8) & 0xFFu) * xv[3];
-  d += (float)((lo >> 16) & 0xFFu) * xv[4];
-  d += (float)((hi >> 16) & 0xFFu) * xv[5];
-  d += (float)(lo >> 24) * xv[6];
-  d += (float)(hi >> 24) * xv[7];
-  return d;
+__device__ __forceinline__ void make_planes(const float* x, float mul, int kg, int blk, uint32_t* xw, float* xs,
+                                            bool active) {
+  float v[8];
+  float amax = 0.f;
+  if (active) {
+    *(float4*)&v[0] = *(const float4*)&x[8 * kg];
+    *(float4*)&v[4] = *(const float4*)&x[8 * kg + 4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] *= mul;
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+  }
+  for (int o = 1; o < blk / 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if (!active) return;
+  int e;
+  frexpf(amax, &e);                       // amax < 2^e (e = 0 when the block is zero)
+  constexpr int F = Digits<BITS>::F;
+  if ((kg & (blk / 8 - 1)) == 0) xs[(8 * kg) / blk] = ldexpf(1.0f, e - F);
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int m = (int)rintf(ldexpf(v[i], F - e));
+#pragma unroll
+    for (int j = 0; j < Digits<BITS>::ND; ++j) {
+      if (BITS == 4) {
+        const int d = ((m + 8) & 15) - 8;
+        w[j] |= (uint32_t)(d & 15) << (4 * i);
+        m = (m - d) >> 4;
+      } else {
+        const int d = ((m + 128) & 255) - 128;
+        w[2 * j + (i >> 2)] |= (uint32_t)(d & 255) << (8 * (i & 3));
+        m = (m - d) >> 8;
+      }
+    }
+  }
+  *(uint4*)&xw[8 * kg] = make_uint4(w[0], w[1], w[2], w[3]);
+  *(uint4*)&xw[8 * kg + 4] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
-template <>
-__device__ __forceinline__ float dot8<8>(const uint4& v, int c, const float* xv) {
-  const uint32_t w0 = word_of(v, 2 * c), w1 = word_of(v, 2 * c + 1);
-  float d = (float)(w0 & 0xFFu) * xv[0];
-  d += (float)((w0 >> 8) & 0xFFu) * xv[1];
-  d += (float)((w0 >> 16) & 0xFFu) * xv[2];
-  d += (float)(w0 >> 24) * xv[3];
-  d += (float)(w1 & 0xFFu) * xv[4];
-  d += (float)((w1 >> 8) & 0xFFu) * xv[5];
-  d += (float)((w1 >> 16) & 0xFFu) * xv[6];
-  d += (float)(w1 >> 24) * xv[7];
-  return d;
+// Per-plane integer partial sums of one lane's 8 codes (chunk c of its 16-byte
+// tile slice) against the matching plane words pw[0..7].
+template <int BITS>
+__device__ __forceinline__ void dot_planes(const uint4& v, int c, const uint32_t* pw, int* P) {
+  if (BITS == 4) {
+    const int w = (int)word_of(v, c);
+#pragma unroll
+    for (int j = 0; j < 5; ++j) P[j] = __builtin_amdgcn_sdot8(w, (int)pw[j], P[j], false);
+  } else {
+    const int w0 = (int)word_of(v, 2 * c), w1 = (int)word_of(v, 2 * c + 1);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      P[j] = __builtin_amdgcn_sdot4(w0, (int)pw[2 * j], P[j], false);
+      P[j] = __builtin_amdgcn_sdot4(w1, (int)pw[2 * j + 1], P[j], false);
+    }
+  }
 }
 
-template <int BITS> __device__ constexpr float code_offset() { return BITS == 4 ? 8.f : 128.f; }
+// Recombine the digit planes: sum_j base^j * P[j] (exact in int32 for int4).
+template <int BITS>
+__device__ __forceinline__ float planes_value(const int* P) {
+  if (BITS == 4) {
+    const int v = P[0] + (P[1] << 4) + (P[2] << 8) + (P[3] << 12) + (P[4] << 16);
+    return (float)v;
+  } else {
+    return (float)P[0] + 256.0f * ((float)P[1] + 256.0f * (float)P[2]);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Decode items.  An item is 32 intermediate columns (slice J) of one expert for
@@ -200,45 +267,50 @@ template <int BITS> __device__ constexpr float code_offset() { return BITS == 4 
 // 512 threads (8 waves) runs one item; all of the item's weight bytes are
 // requested up front (ItemRegs) so that they are in flight together.
 // ---------------------------------------------------------------------------
-template <int BITS>
+template <int BITS, int G>
 struct ItemRegs {
   static constexpr int KB = kb_cols(BITS), NKB = H / KB, CPT = KB / 32;
-  static constexpr int GU_TILES = 4 * NKB, GU_TPW = GU_TILES / 8;   // gate 2 tiles + up 2 tiles per K block
+  static constexpr int GU_TPW = NKB / 2;   // wave w: n-tile w/2 (gate 2J, gate 2J+1, up 2J, up 2J+1), K half w%2
+  static constexpr int NGW = (H / 2) / G;  // scale groups in a K half
   static constexpr int DR = down_rows(BITS), NRT = H / DR, D_TPW = (NRT + 7) / 8, RS = DR / 16;
   uint4 gu[GU_TPW];
-  float gus[GU_TPW][CPT];
+  float gsc[NGW];
   uint4 dn[D_TPW];
   float dns[D_TPW][RS];
 };
 
-template <int BITS>
-__device__ __forceinline__ void item_load(ItemRegs<BITS>& R, const uint8_t* eq, const float* es, int inter,
-                                          int group, int J, int wv, int lane) {
-  using IR = ItemRegs<BITS>;
+template <int BITS, int G>
+__device__ __forceinline__ void item_load(ItemRegs<BITS, G>& R, const uint8_t* eq, const float* es, int inter,
+                                          int J, int wv, int lane) {
+  using IR = ItemRegs<BITS, G>;
+  constexpr int NG = H / G;
   const size_t mbytes = matrix_bytes(BITS, inter, H);
-  const int ng = H / group, gsh = __builtin_ctz(group);
-  const size_t mscales = (size_t)inter * ng;
+  const size_t mscales = (size_t)inter * NG;
   const int r = lane & 15;
+  const int i = wv >> 1, ntile = 2 * J + (i & 1), mat = i >> 1, kb0 = (wv & 1) * IR::GU_TPW;
 #pragma unroll
-  for (int m = 0; m < IR::GU_TPW; ++m) {
-    const int t = wv + 8 * m, i = t / IR::NKB, kb = t % IR::NKB;
-    const int ntile = 2 * J + (i & 1), mat = i >> 1;
-    R.gu[m] = *(const uint4*)(eq + mat * mbytes + ((size_t)ntile * IR::NKB + kb) * TILE + lane * 16);
+  for (int m = 0; m < IR::GU_TPW; ++m)
+    R.gu[m] = *(const uint4*)(eq + mat * mbytes + ((size_t)ntile * IR::NKB + kb0 + m) * TILE + lane * 16);
+  // gate/up scales are row-major [row][group]: this lane's row, this wave's K half
+  const float* gp = es + mat * mscales + (size_t)(16 * ntile + r) * NG + (wv & 1) * IR::NGW;
+  if (IR::NGW % 4 == 0) {
 #pragma unroll
-    for (int c = 0; c < IR::CPT; ++c)
-      R.gus[m][c] = es[mat * mscales + ((size_t)ntile * ng + ((kb * IR::KB + 32 * c) >> gsh)) * 16 + r];
+    for (int g = 0; g < IR::NGW; g += 4) *(float4*)&R.gsc[g] = *(const float4*)(gp + g);
+  } else {
+#pragma unroll
+    for (int g = 0; g < IR::NGW; ++g) R.gsc[g] = gp[g];
   }
   const uint8_t* dq = eq + 2 * mbytes;
   const float* ds = es + 2 * mscales;
-  const int gd = (SLICE * J) >> gsh;
+  const int gd = (SLICE * J) / G;
 #pragma unroll
   for (int m = 0; m < IR::D_TPW; ++m) {
     const int rt = wv + 8 * m;
     if (rt < IR::NRT) {
       R.dn[m] = *(const uint4*)(dq + ((size_t)J * IR::NRT + rt) * TILE + lane * 16);
       const float* sp = ds + (((size_t)gd * IR::NRT + rt) * 16 + r) * IR::RS;
-#pragma unroll
-      for (int j = 0; j < IR::RS; ++j) R.dns[m][j] = sp[j];
+      if (IR::RS == 4) *(float4*)&R.dns[m][0] = *(const float4*)sp;
+      else *(float2*)&R.dns[m][0] = *(const float2*)sp;
     }
   }
 }
@@ -256,68 +328,147 @@ __device__ __forceinline__ void store_coherent_u32(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte device-scope (L2-coherent, sc1) loads through a bounds-checked buffer
+// descriptor: used for everything one workgroup of the persistent kernel reads
+// that another one wrote during the same launch.
+typedef unsigned int u32x4 __attribute__((vector_size(16)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;
+__device__ __forceinline__ u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ float4 as_float4(u32x4 v) {
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
 struct ItemLds {
-  float part[80 * 16];   // per-tile gate/up partial sums (int8: 80 tiles)
-  float gu[64];          // gate (2x16) and up (2x16) totals
-  float h[SLICE];        // SiLU(g) * u of the slice
+  uint32_t xw[(H / 8) * 8];   // digit planes of the layer input
+  float xs[H / 32];           // per-block unit 2^(e - F)
+  float gpart[8][64];         // per-wave, per-lane gate/up partial sums
+  float gu[64];               // gate (2x16) and up (2x16) totals
+  float h[SLICE];             // SiLU(g) * u of the slice
+  uint32_t hw[4 * 8];         // digit planes of h
+  float hs;
+  float dpart[H * 4];         // down partials: [row][lane group]
+  int tr_layer;               // layer index, for MOE_TRACE only
 };
 
-// z: the layer input in LDS; out: 1280 partials (coherent stores when the
-// partials are read by other workgroups of the same kernel).
-template <int BITS, bool COHERENT>
-__device__ __forceinline__ void item_compute(const ItemRegs<BITS>& R, const float* z, float coef, float* out,
-                                             ItemLds& L) {
-  using IR = ItemRegs<BITS>;
-  constexpr float OFF = code_offset<BITS>();
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q = lane >> 4;
+// Digit planes of the layer input z (in LDS) for weights of format (BITS, G).
+template <int BITS, int G>
+__device__ __forceinline__ void item_planes(const float* z, float mul, ItemLds& L) {
+  const int tid = threadIdx.x;
+  make_planes<BITS>(z, mul, tid, G, L.xw, L.xs, tid < H / 8);
+  __syncthreads();
+}
+
+// z planes in L.xw/L.xs (item_planes); out: 1280 partials (coherent stores
+// when they are read by other workgroups of the same kernel).  Cross-lane sums
+// go through LDS in a fixed order.
+template <int BITS, int G, bool COHERENT>
+__device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, float coef, float* out, ItemLds& L) {
+  using IR = ItemRegs<BITS, G>;
+  constexpr int ND = Digits<BITS>::ND, CPG = G / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, q = lane >> 4;
+  const int kb0 = (wv & 1) * IR::GU_TPW;
+  float acc = 0.f;
+  int P[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) P[j] = 0;
 #pragma unroll
   for (int m = 0; m < IR::GU_TPW; ++m) {
-    const int t = wv + 8 * m, kb = t % IR::NKB;
-    float acc = 0.f;
+    // all plane words of this tile's chunks first (one LDS round trip per tile)
+    uint32_t pw[IR::CPT][8];
 #pragma unroll
     for (int c = 0; c < IR::CPT; ++c) {
-      const float* xp = z + kb * IR::KB + 32 * c + 8 * q;
-      float xv[8];
-      *(float4*)&xv[0] = *(const float4*)xp;
-      *(float4*)&xv[4] = *(const float4*)(xp + 4);
-      const float X = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
-      acc += R.gus[m][c] * (dot8<BITS>(R.gu[m], c, xv) - OFF * X);
+      const int k0 = (kb0 + m) * IR::KB + 32 * c;
+      *(uint4*)&pw[c][0] = *(const uint4*)&L.xw[k0 + 8 * q];
+      if (BITS == 8) *(uint4*)&pw[c][4] = *(const uint4*)&L.xw[k0 + 8 * q + 4];
+      else pw[c][4] = L.xw[k0 + 8 * q + 4];
     }
-    acc += __shfl_xor(acc, 16);
-    acc += __shfl_xor(acc, 32);
-    if (q == 0) L.part[t * 16 + r] = acc;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const int i = tid >> 4, rr = tid & 15;
-    float sum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < IR::NKB; ++kb) sum += L.part[(i * IR::NKB + kb) * 16 + rr];
-    L.gu[tid] = sum;
+    for (int c = 0; c < IR::CPT; ++c) {
+      const int ch = m * IR::CPT + c;              // chunk index within this wave's K half
+      dot_planes<BITS>(R.gu[m], c, pw[c], P);
+      if ((ch + 1) % CPG == 0) {                   // last chunk of a scale group
+        const int gl = ch / CPG;
+        acc = fmaf(R.gsc[gl] * L.xs[(kb0 * IR::KB) / G + gl], planes_value<BITS>(P), acc);
+#pragma unroll
+        for (int j = 0; j < ND; ++j) P[j] = 0;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  MOE_TRACE(blockIdx.x, L.tr_layer, 6);
+  L.gpart[wv][lane] = acc;
+  __syncthreads();
+  if (tid < 64) {                       // wave 0: gate/up totals, h, and the planes of h
+    if (tid < SLICE) {
+      const int ti = tid >> 4, rr = tid & 15;   // column 16 ti + rr of the slice
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          g += L.gpart[2 * ti + hh][16 * qq + rr];
+          u += L.gpart[4 + 2 * ti + hh][16 * qq + rr];
+        }
+      L.h[tid] = silu_mul(g, u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    MOE_TRACE(blockIdx.x, L.tr_layer, 7);
+    make_planes<BITS>(L.h, 1.0f, tid, SLICE, L.hw, &L.hs, tid < SLICE / 8);
   }
   __syncthreads();
-  if (tid < SLICE) L.h[tid] = silu_mul(L.gu[tid], L.gu[32 + tid]);
-  __syncthreads();
-  float xv[8];
-  *(float4*)&xv[0] = *(const float4*)&L.h[8 * q];
-  *(float4*)&xv[4] = *(const float4*)&L.h[8 * q + 4];
-  const float X = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
+  MOE_TRACE(blockIdx.x, L.tr_layer, 8);
+  uint32_t pw[8];
+  *(uint4*)&pw[0] = *(const uint4*)&L.hw[8 * q];
+  *(uint4*)&pw[4] = *(const uint4*)&L.hw[8 * q + 4];
 #pragma unroll
   for (int m = 0; m < IR::D_TPW; ++m) {
     const int rt = wv + 8 * m;
     if (rt < IR::NRT) {
 #pragma unroll
       for (int j = 0; j < IR::RS; ++j) {
-        float v = R.dns[m][j] * (dot8<BITS>(R.dn[m], j, xv) - OFF * X);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (q == 0) {
-          float* o = out + IR::DR * rt + 16 * j + r;
-          if (COHERENT) store_coherent(o, coef * v);
-          else *o = coef * v;
-        }
+        int Pd[ND];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) Pd[d] = 0;
+        dot_planes<BITS>(R.dn[m], j, pw, Pd);
+        L.dpart[(IR::DR * rt + 16 * j + (lane & 15)) * 4 + q] = R.dns[m][j] * planes_value<BITS>(Pd);
       }
     }
+  }
+  __syncthreads();
+  MOE_TRACE(blockIdx.x, L.tr_layer, 9);
+  const float cs = coef * L.hs;
+#pragma unroll
+  for (int row = tid; row < H; row += 512) {
+    const float4 p4 = *(const float4*)&L.dpart[4 * row];
+    const float v = cs * ((p4.x + p4.y) + (p4.z + p4.w));
+    if (COHERENT) store_coherent(out + row, v);
+    else out[row] = v;
+  }
+}
+
+// One decode item end to end (loads, planes, compute) for format (BITS, G).
+template <int BITS, int G, bool COHERENT>
+__device__ __forceinline__ void run_item(const uint8_t* eq, const float* es, int inter, int J, const float* z,
+                                         float coef, float* out, ItemLds& L) {
+  const int tid = threadIdx.x;
+  ItemRegs<BITS, G> R;
+  item_load<BITS, G>(R, eq, es, inter, J, tid >> 6, tid & 63);
+  item_planes<BITS, G>(z, 1.0f, L);
+  item_compute<BITS, G, COHERENT>(R, coef, out, L);
+}
+
+template <int BITS, bool COHERENT>
+__device__ __forceinline__ void run_item_g(int group, const uint8_t* eq, const float* es, int inter, int J,
+                                           const float* z, float coef, float* out, ItemLds& L) {
+  switch (group) {
+    case 32: run_item<BITS, 32, COHERENT>(eq, es, inter, J, z, coef, out, L); break;
+    case 64: run_item<BITS, 64, COHERENT>(eq, es, inter, J, z, coef, out, L); break;
+    default: run_item<BITS, 128, COHERENT>(eq, es, inter, J, z, coef, out, L); break;
   }
 }
 
@@ -327,23 +478,17 @@ __global__ __launch_bounds__(512) void dec_items_kernel(DecItemsArgs a) {
   __shared__ __attribute__((aligned(16))) float z[H];
   __shared__ __attribute__((aligned(16))) ItemLds L;
   const int t = blockIdx.x / N_ITEMS, item = blockIdx.x % N_ITEMS;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
   float* out = a.part + ((size_t)t * N_ITEMS + item) * H;
+  for (int k = tid; k < H; k += 512) z[k] = a.xf ? a.xf[(size_t)t * H + k] : bf16_to_f32(a.xb[(size_t)t * H + k]);
+  __syncthreads();
   if (item < R_ITEMS) {
     const int p = item / (I / SLICE), J = item % (I / SLICE);
     const int e = a.ids[(size_t)t * TOPK + p];
-    ItemRegs<BR> R;
-    item_load<BR>(R, a.rw.q + (size_t)e * a.rw.e_bytes, a.rw.s + (size_t)e * a.rw.e_scales, I, a.rw.group, J, wv, lane);
-    for (int k = tid; k < H; k += 512) z[k] = a.xf ? a.xf[(size_t)t * H + k] : bf16_to_f32(a.xb[(size_t)t * H + k]);
-    __syncthreads();
-    item_compute<BR, false>(R, z, a.tw[(size_t)t * TOPK + p], out, L);
+    run_item_g<BR, false>(a.rw.group, a.rw.q + (size_t)e * a.rw.e_bytes, a.rw.s + (size_t)e * a.rw.e_scales, I, J, z,
+                          a.tw[(size_t)t * TOPK + p], out, L);
   } else {
-    const int J = item - R_ITEMS;
-    ItemRegs<BS> R;
-    item_load<BS>(R, a.sw.q, a.sw.s, IS, a.sw.group, J, wv, lane);
-    for (int k = tid; k < H; k += 512) z[k] = a.xf ? a.xf[(size_t)t * H + k] : bf16_to_f32(a.xb[(size_t)t * H + k]);
-    __syncthreads();
-    item_compute<BS, false>(R, z, 1.0f, out, L);
+    run_item_g<BS, false>(a.sw.group, a.sw.q, a.sw.s, IS, item - R_ITEMS, z, 1.0f, out, L);
   }
 }
 
@@ -386,12 +531,17 @@ __global__ __launch_bounds__(256) void dec_reduce_kernel(DecReduceArgs a) {
 // ---------------------------------------------------------------------------
 constexpr long SPIN_LIMIT = 1L << 20;  // polls before a wait gives up (about a second)
 
+// Wave-wide poll until all n (a multiple of 4, at most 256) flags equal epoch.
 __device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* err) {
   const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(flags, n * 4);
   long spins = 0;
   while (true) {
     bool ok = true;
-    for (int i = lane; i < n; i += 64) ok &= load_coherent_u32(flags + i) == epoch;
+    if (lane < n / 4) {
+      const u32x4 v = load16_coherent(rs, lane * 16);
+      ok = v[0] == epoch && v[1] == epoch && v[2] == epoch && v[3] == epoch;
+    }
     if (__all(ok)) break;
     __builtin_amdgcn_s_sleep(1);
     if (++spins > SPIN_LIMIT) {
@@ -401,64 +551,110 @@ __device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_
   }
 }
 
-struct ChainLds {
+// LDS of the persistent kernel: items and reducers use disjoint parts.
+struct ItemSide {
   float z[H];
   ItemLds item;
   float qs[N_RED * Q_STRIDE];
-  float red[12][RED_ROWS];
-  float hrow[RED_ROWS];
+  float lg[E];            // logits
+  float ex[E];            // exp(logit - max)
   int pick_e[TOPK];
   float pick_w[TOPK];
   float inv;
 };
+struct ReducerSide {
+  float parts[N_ITEMS * RED_ROWS];
+  float red[12][RED_ROWS];
+  float hrow[RED_ROWS];
+  float sq[RED_ROWS];
+};
+union ChainLds {
+  ItemSide it;
+  ReducerSide rd;
+};
 
-// Wait for the reducers of stage l, then rebuild this layer's input z (in
-// LDS) and, for routed items, the routing.  Identical arithmetic in every
-// workgroup, so every item sees the same z and the same picks.
-__device__ __forceinline__ void chain_layer_input(const ChainArgs& a, ChainLds& S, int l, uint32_t epoch,
-                                                  bool routed, bool report, uint32_t* err) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+__device__ __forceinline__ float sum8(float v) {   // identical result in all 8 lanes of a group
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  return v;
+}
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  return fmaxf(v, __shfl_xor(v, 4));
+}
+
+// Wait for the reducers of stage l, then rebuild this layer's input in LDS (z
+// = h, to be multiplied by the returned 1/rms) and, for routed items, the
+// routing.  Every workgroup runs identical arithmetic, so every item sees the
+// same z and the same picks.  The 512 threads work as 64 groups of 8 (group e
+// = expert e): logits and the sum of squares come from the 32 reducer partials
+// in a fixed order; the softmax is increasing in the logit, so the 6 largest
+// logits (ties to the lower index) are the 6 largest probabilities.
+__device__ __forceinline__ float chain_layer_input(const ChainArgs& a, ItemSide& S, int l, uint32_t epoch,
+                                                   bool routed, bool report, uint32_t* err) {
+  const int tid = threadIdx.x, wv = tid >> 6;
   if (wv == 0) wait_flags(a.red_flag, N_RED, epoch, err);
   __syncthreads();
-  for (int k = tid; k < H; k += 512) S.z[k] = load_coherent(a.y + k);
-  for (int k = tid; k < N_RED * Q_STRIDE; k += 512) S.qs[k] = load_coherent(a.q + k);
-  __syncthreads();
-  if (wv == 0) {
-    float ss = 0.f;
-    for (int rr = 0; rr < N_RED; ++rr) ss += S.qs[rr * Q_STRIDE + 64];
-    const float inv = a.norm ? 1.0f / sqrtf(ss / (float)H + a.eps) : 1.0f;
-    if (lane == 0) S.inv = inv;
-    if (routed) {
-      const float* bias = a.layer[l].bias;
-      float lg = 0.f;
-      for (int rr = 0; rr < N_RED; ++rr) lg += S.qs[rr * Q_STRIDE + lane];
-      lg = lg * inv + (bias ? bias[lane] : 0.f);
-      const float m = wave_max(lg);
-      const float ex = expf(lg - m);
-      const float pr = ex / wave_sum(ex);
-      bool taken = false;
-      for (int j = 0; j < TOPK; ++j) {
-        float bv = taken ? -1.f : pr;
-        int bi = lane;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const float ov = __shfl_xor(bv, o);
-          const int oi = __shfl_xor(bi, o);
-          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
-        if (lane == bi) taken = true;
-        if (lane == 0) {
-          S.pick_e[j] = bi;
-          S.pick_w[j] = bv;
-          if (report) { a.ids[l * TOPK + j] = bi; a.tw[l * TOPK + j] = bv; }
-        }
-      }
-    }
+  MOE_TRACE(blockIdx.x, l, 1);
+  {
+    const __amdgpu_buffer_rsrc_t ry = coherent_rsrc(a.y, H * 4);
+    const __amdgpu_buffer_rsrc_t rq = coherent_rsrc(a.q, N_RED * Q_STRIDE * 4);
+    constexpr int NQ4 = N_RED * Q_STRIDE / 4;   // 544
+    u32x4 zv, q0, q1;
+    if (tid < H / 4) zv = load16_coherent(ry, tid * 16);
+    q0 = load16_coherent(rq, tid * 16);
+    if (tid + 512 < NQ4) q1 = load16_coherent(rq, (tid + 512) * 16);
+    if (tid < H / 4) *(float4*)&S.z[4 * tid] = as_float4(zv);
+    *(float4*)&S.qs[4 * tid] = as_float4(q0);
+    if (tid + 512 < NQ4) *(float4*)&S.qs[4 * (tid + 512)] = as_float4(q1);
   }
   __syncthreads();
-  const float inv = S.inv;
-  for (int k = tid; k < H; k += 512) S.z[k] = S.z[k] * inv;
-  __syncthreads();
+  MOE_TRACE(blockIdx.x, l, 11);
+  const int e = tid >> 3, sub = tid & 7;
+  float part = 0.f, sq = 0.f;
+#pragma unroll
+  for (int m = 0; m < N_RED / 8; ++m) {
+    part += S.qs[(sub + 8 * m) * Q_STRIDE + e];
+    sq += S.qs[(sub + 8 * m) * Q_STRIDE + 64];
+  }
+  part = sum8(part);
+  sq = sum8(sq);
+  const float inv = a.norm ? 1.0f / sqrtf(sq / (float)H + a.eps) : 1.0f;
+  if (routed) {
+    const float* bias = a.layer[l].bias;
+    const float lge = part * inv + (bias ? bias[e] : 0.f);
+    if (sub == 0) S.lg[e] = lge;
+    __syncthreads();
+    float mx = -INFINITY;
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = sub + 8 * j;
+      const float lk = S.lg[k];
+      mx = fmaxf(mx, lk);
+      rank += (lk > lge || (lk == lge && k < e)) ? 1 : 0;
+    }
+    mx = max8(mx);
+    rank = (int)sum8((float)rank);
+    const float ex = expf(lge - mx);
+    if (sub == 0) S.ex[e] = ex;
+    __syncthreads();
+    float sm = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm += S.ex[sub + 8 * j];
+    sm = sum8(sm);
+    if (sub == 0 && rank < TOPK) {
+      const float pr = ex / sm;
+      S.pick_e[rank] = e;
+      S.pick_w[rank] = pr;
+      if (report) { a.ids[l * TOPK + rank] = e; a.tw[l * TOPK + rank] = pr; }
+    }
+    __syncthreads();
+  }
+  MOE_TRACE(blockIdx.x, l, 12);
+  return inv;
 }
 
 __device__ __forceinline__ void chain_item_done(const ChainArgs& a, int b, uint32_t epoch) {
@@ -467,46 +663,63 @@ __device__ __forceinline__ void chain_item_done(const ChainArgs& a, int b, uint3
   if (threadIdx.x == 0) store_coherent_u32(a.item_flag + b, epoch);
 }
 
-template <int BR>
-__device__ void chain_routed(const ChainArgs& a, ChainLds& S, int b, uint32_t base, uint32_t* err) {
+template <int BR, int GR>
+__device__ void chain_routed(const ChainArgs& a, ItemSide& S, int b, uint32_t base, uint32_t* err) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int p = b / (I / SLICE), J = b % (I / SLICE);
-  const size_t ebytes = 3 * matrix_bytes(BR, I, H), escales = 3 * (size_t)I * H / a.rgroup;
+  const size_t ebytes = 3 * matrix_bytes(BR, I, H), escales = 3 * (size_t)I * H / GR;
   for (int l = 0; l < a.n_layers; ++l) {
-    chain_layer_input(a, S, l, base + l + 1, true, b == 0, err);
+    MOE_TRACE(b, l, 0);
+    S.item.tr_layer = l;
+    const float inv = chain_layer_input(a, S, l, base + l + 1, true, b == 0, err);
+    MOE_TRACE(b, l, 2);
     const int e = S.pick_e[p];
-    ItemRegs<BR> R;
-    item_load<BR>(R, a.layer[l].eq + (size_t)e * ebytes, a.layer[l].es + (size_t)e * escales, I, a.rgroup, J, wv, lane);
-    item_compute<BR, true>(R, S.z, S.pick_w[p], a.part + (size_t)b * H, S.item);
+    ItemRegs<BR, GR> R;
+    item_load<BR, GR>(R, a.layer[l].eq + (size_t)e * ebytes, a.layer[l].es + (size_t)e * escales, I, J, wv, lane);
+    MOE_TRACE(b, l, 3);
+    item_planes<BR, GR>(S.z, inv, S.item);
+    MOE_TRACE(b, l, 13);
+    item_compute<BR, GR, true>(R, S.pick_w[p], a.part + (size_t)b * H, S.item);
+    MOE_TRACE(b, l, 4);
     chain_item_done(a, b, base + l + 1);
+    MOE_TRACE(b, l, 5);
   }
-  (void)tid;
 }
 
-template <int BS>
-__device__ void chain_shared(const ChainArgs& a, ChainLds& S, int b, uint32_t base, uint32_t* err) {
+template <int BS, int GS>
+__device__ void chain_shared(const ChainArgs& a, ItemSide& S, int b, uint32_t base, uint32_t* err) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int J = b - R_ITEMS;
   for (int l = 0; l < a.n_layers; ++l) {
-    ItemRegs<BS> R;
-    item_load<BS>(R, a.layer[l].sq, a.layer[l].ss, IS, a.sgroup, J, wv, lane);  // routing-independent: before the wait
-    chain_layer_input(a, S, l, base + l + 1, false, false, err);
-    item_compute<BS, true>(R, S.z, 1.0f, a.part + (size_t)b * H, S.item);
+    MOE_TRACE(b, l, 0);
+    S.item.tr_layer = l;
+    ItemRegs<BS, GS> R;
+    item_load<BS, GS>(R, a.layer[l].sq, a.layer[l].ss, IS, J, wv, lane);  // routing-independent: before the wait
+    const float inv = chain_layer_input(a, S, l, base + l + 1, false, false, err);
+    MOE_TRACE(b, l, 2);
+    item_planes<BS, GS>(S.z, inv, S.item);
+    MOE_TRACE(b, l, 13);
+    item_compute<BS, GS, true>(R, 1.0f, a.part + (size_t)b * H, S.item);
+    MOE_TRACE(b, l, 4);
     chain_item_done(a, b, base + l + 1);
+    MOE_TRACE(b, l, 5);
   }
-  (void)tid;
 }
 
-__device__ void chain_reducer(const ChainArgs& a, ChainLds& S, int rid, uint32_t base, uint32_t* err) {
+__device__ void chain_reducer(const ChainArgs& a, ReducerSide& S, int rid, uint32_t base, uint32_t* err) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r0 = rid * RED_ROWS;
   const int e = tid >> 3, sub = tid & 7;   // partial logits: expert e, rows sub + 8m
+  constexpr int NF4 = N_ITEMS * RED_ROWS / 4;          // 2240 float4 of partials per stage
+  constexpr int F4_PER_T = (NF4 + 511) / 512;          // 5
+  const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(a.part, N_ITEMS * H * 4);
   for (int s = 0; s <= a.n_layers; ++s) {
     float wr[5];
     if (s < a.n_layers) {
 #pragma unroll
       for (int m = 0; m < 5; ++m) wr[m] = a.layer[s].wr[(size_t)e * H + r0 + sub + 8 * m];
     }
+    MOE_TRACE(N_ITEMS + rid, s, 0);
     if (s == 0) {
       if (tid < RED_ROWS) {
         const int k = r0 + tid;
@@ -515,18 +728,39 @@ __device__ void chain_reducer(const ChainArgs& a, ChainLds& S, int rid, uint32_t
     } else {
       if (wv == 0) wait_flags(a.item_flag, N_ITEMS, base + s, err);
       __syncthreads();
+      MOE_TRACE(N_ITEMS + rid, s, 1);
+      // all partials of this reducer's rows, 16 bytes per load, all loads in flight together
+      u32x4 v[F4_PER_T];
+#pragma unroll
+      for (int m = 0; m < F4_PER_T; ++m) {
+        const int f = tid + 512 * m;
+        if (f < NF4) {
+          const int it = f / (RED_ROWS / 4), qd = f % (RED_ROWS / 4);
+          v[m] = load16_coherent(rp, ((uint32_t)it * H + r0 + 4 * qd) * 4);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < F4_PER_T; ++m) {
+        const int f = tid + 512 * m;
+        if (f < NF4) *(float4*)&S.parts[4 * f] = as_float4(v[m]);
+      }
+      __syncthreads();
       if (tid < 12 * RED_ROWS) {
         const int rr = tid % RED_ROWS, ig = tid / RED_ROWS;
         float acc = 0.f;
-        for (int it = ig; it < N_ITEMS; it += 12) acc += load_coherent(a.part + (size_t)it * H + r0 + rr);
+#pragma unroll
+        for (int j = 0; j < (N_ITEMS + 11) / 12; ++j) {
+          const int it = ig + 12 * j;
+          if (it < N_ITEMS) acc += S.parts[it * RED_ROWS + rr];
+        }
         S.red[ig][rr] = acc;
       }
       __syncthreads();
       if (tid < RED_ROWS) {
-        float v = 0.f;
+        float vv = 0.f;
 #pragma unroll
-        for (int g = 0; g < 12; ++g) v += S.red[g][tid];
-        S.hrow[tid] = (a.accumulate ? S.hrow[tid] : 0.f) + v;
+        for (int g = 0; g < 12; ++g) vv += S.red[g][tid];
+        S.hrow[tid] = (a.accumulate ? S.hrow[tid] : 0.f) + vv;
       }
     }
     __syncthreads();
@@ -540,14 +774,23 @@ __device__ void chain_reducer(const ChainArgs& a, ChainLds& S, int rid, uint32_t
       part += __shfl_xor(part, 4);
       if (sub == 0) store_coherent(a.q + rid * Q_STRIDE + e, part);
       if (wv == 0) {
-        const float v = lane < RED_ROWS ? S.hrow[lane] : 0.f;
-        const float ss = wave_sum(v * v);
-        if (lane == 0) store_coherent(a.q + rid * Q_STRIDE + 64, ss);
+        if (lane < RED_ROWS) S.sq[lane] = S.hrow[lane] * S.hrow[lane];
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) {
+          float ss = 0.f;
+#pragma unroll
+          for (int k = 0; k < RED_ROWS; k += 4) {
+            const float4 v = *(const float4*)&S.sq[k];
+            ss += (v.x + v.y) + (v.z + v.w);
+          }
+          store_coherent(a.q + rid * Q_STRIDE + 64, ss);
+        }
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) store_coherent_u32(a.red_flag + rid, base + s + 1);
     }
+    MOE_TRACE(N_ITEMS + rid, s, 5);
   }
 }
 
@@ -557,9 +800,21 @@ __global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
   const int b = blockIdx.x;
   const uint32_t base = load_coherent_u32(a.hdr) * 64u;
   uint32_t* err = a.hdr + 2;
-  if (b < R_ITEMS) chain_routed<BR>(a, S, b, base, err);
-  else if (b < N_ITEMS) chain_shared<BS>(a, S, b, base, err);
-  else chain_reducer(a, S, b - N_ITEMS, base, err);
+  if (b < R_ITEMS) {
+    switch (a.rgroup) {
+      case 32: chain_routed<BR, 32>(a, S.it, b, base, err); break;
+      case 64: chain_routed<BR, 64>(a, S.it, b, base, err); break;
+      default: chain_routed<BR, 128>(a, S.it, b, base, err); break;
+    }
+  } else if (b < N_ITEMS) {
+    switch (a.sgroup) {
+      case 32: chain_shared<BS, 32>(a, S.it, b, base, err); break;
+      case 64: chain_shared<BS, 64>(a, S.it, b, base, err); break;
+      default: chain_shared<BS, 128>(a, S.it, b, base, err); break;
+    }
+  } else {
+    chain_reducer(a, S.rd, b - N_ITEMS, base, err);
+  }
   // the last workgroup to finish advances the call sequence
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -636,10 +891,12 @@ __global__ __launch_bounds__(1024) void hist_kernel(HistArgs a) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
-// int4 word (codes k0..k7 in nibbles 0..7, offset-binary) -> exact f16 codes
-// in MFMA operand order [k0, k4, k1, k5, k2, k6, k3, k7]:
-// 0x6400 | n is the f16 value 1024 + n, and 0x6400 | (n << 4) is 1024 + 16n.
+// int4 word (codes k0..k7 in nibbles 0..7, two's complement) -> exact f16
+// codes in MFMA operand order [k0, k4, k1, k5, k2, k6, k3, k7].  The XOR turns
+// every nibble into n = code + 8; 0x6400 | n is the f16 value 1024 + n, and
+// 0x6400 | (n << 4) is 1024 + 16n.
 __device__ __forceinline__ half8 unpack_int4(uint32_t w) {
+  w ^= 0x88888888u;
   const half2v m1032 = {(_Float16)-1032.f, (_Float16)-1032.f};
   const half2v m72 = {(_Float16)-72.f, (_Float16)-72.f};
   const half2v inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
@@ -651,9 +908,11 @@ __device__ __forceinline__ half8 unpack_int4(uint32_t w) {
   return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-// two int8 words (codes k0..k3, k4..k7 in bytes, offset-binary) -> exact f16
-// codes in order [k0, k2, k1, k3, k4, k6, k5, k7].
+// two int8 words (codes k0..k3, k4..k7 in bytes, two's complement) -> exact
+// f16 codes in order [k0, k2, k1, k3, k4, k6, k5, k7] (XOR: byte = code + 128).
 __device__ __forceinline__ half8 unpack_int8(uint32_t w0, uint32_t w1) {
+  w0 ^= 0x80808080u;
+  w1 ^= 0x80808080u;
   const half2v m1152 = {(_Float16)-1152.f, (_Float16)-1152.f};
   const half2v a = as_h2((w0 & 0x00FF00FFu) | 0x64006400u) + m1152;
   const half2v b = as_h2(((w0 >> 8) & 0x00FF00FFu) | 0x64006400u) + m1152;
@@ -808,7 +1067,7 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
         const int grp = gc / cpg;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const float s = es[(i ? mscales : 0) + ((size_t)ntile * ng + grp) * 16 + r];
+          const float s = es[(i ? mscales : 0) + (size_t)(16 * ntile + r) * ng + grp];
 #pragma unroll
           for (int ms = 0; ms < 2; ++ms) acc[i][ms] += s * ctmp[i][ms];
         }
@@ -1027,3 +1286,9 @@ hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps,
 }
 
 }  // namespace moe
+
+#ifdef MOE_DEVICE_TRACE
+extern "C" int moe_debug_set_trace(void* p) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(moe::g_trace), &p, sizeof(p));
+}
+#endif

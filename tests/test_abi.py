@@ -27,6 +27,14 @@ def test_status_strings(lib):
     assert b"unknown" in lib.moe_status_str(99)
 
 
+def _s4(v):
+    return v - 16 if v >= 8 else v
+
+
+def _s8(v):
+    return v - 256 if v >= 128 else v
+
+
 def _unpack_rows(buf, N, K, bits):
     """Decode the gate/up tile layout described in include/moe.h (independent of the packer)."""
     KB = 128 if bits == 4 else 64
@@ -41,10 +49,10 @@ def _unpack_rows(buf, N, K, bits):
                     w = int(words[base + lane * 4 + j])
                     if bits == 4:
                         for i in range(8):
-                            out[row, kb * KB + 32 * j + 8 * q + i] = ((w >> (4 * i)) & 15) - 8
+                            out[row, kb * KB + 32 * j + 8 * q + i] = _s4((w >> (4 * i)) & 15)
                     else:
                         for i in range(4):
-                            out[row, kb * KB + 32 * (j // 2) + 8 * q + 4 * (j % 2) + i] = ((w >> (8 * i)) & 255) - 128
+                            out[row, kb * KB + 32 * (j // 2) + 8 * q + 4 * (j % 2) + i] = _s8((w >> (8 * i)) & 255)
     return out
 
 
@@ -63,11 +71,11 @@ def _unpack_slabs(buf, K, bits, n_kc):
                     w = int(words[base + lane * 4 + j])
                     if bits == 4:
                         for i in range(8):
-                            out[DR * rt + 16 * j + r, 32 * kc + 8 * q + i] = ((w >> (4 * i)) & 15) - 8
+                            out[DR * rt + 16 * j + r, 32 * kc + 8 * q + i] = _s4((w >> (4 * i)) & 15)
                     else:
                         for i in range(4):
                             out[DR * rt + 16 * (j // 2) + r, 32 * kc + 8 * q + 4 * (j % 2) + i] = \
-                                ((w >> (8 * i)) & 255) - 128
+                                _s8((w >> (8 * i)) & 255)
     return out
 
 
@@ -92,8 +100,8 @@ def test_pack_round_trip(lib, bits, group):
     np.testing.assert_array_equal(_unpack_rows(codes[mb:2 * mb][: 16 * 1280 * bits // 8], 16, 1280, bits), up[:16])
     np.testing.assert_array_equal(_unpack_slabs(codes[2 * mb:], inter, bits, 2), down[:, :64])
     ng = 1280 // group
-    sg = scales[: inter * ng].reshape(inter // 16, ng, 16)
-    np.testing.assert_array_equal(sg.transpose(0, 2, 1).reshape(inter, ng), gs)
+    np.testing.assert_array_equal(scales[: inter * ng].reshape(inter, ng), gs)
+    np.testing.assert_array_equal(scales[inter * ng: 2 * inter * ng].reshape(inter, ng), us)
     DR = 64 if bits == 4 else 32
     sd = scales[2 * inter * ng:].reshape(inter // group, 1280 // DR, 16, DR // 16)
     # entry (g, rt, r, j) is row DR*rt + 16j + r
