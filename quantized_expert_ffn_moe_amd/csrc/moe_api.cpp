@@ -13,6 +13,10 @@ static_assert(MOE_HIDDEN == H && MOE_EXPERTS == E && MOE_TOPK == TOPK && MOE_INT
 
 namespace {
 
+#ifdef MOE_DEVICE_TRACE
+unsigned long long* g_trace_buffer = nullptr;
+#endif
+
 bool fmt_ok(int bits, int group) {
   return (bits == 4 || bits == 8) && (group == 32 || group == 64 || group == 128);
 }
@@ -370,9 +374,19 @@ moe_status_t moe_decode_forward(const void* x, int32_t x_dtype, float* y, int32_
   a.rbits = expert_bits; a.rgroup = expert_group; a.sbits = shared_bits; a.sgroup = shared_group;
   a.ids = topk_ids; a.tw = topk_w;
   a.hdr = dw.hdr; a.item_flag = dw.item_flag; a.red_flag = dw.red_flag; a.part = dw.part; a.q = dw.q;
+#ifdef MOE_DEVICE_TRACE
+  a.trace = g_trace_buffer;
+#endif
   (void)hipGetLastError();
   if (launch_chain(a, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
   return MOE_OK;
 }
 
 }  // extern "C"
+
+#ifdef MOE_DEVICE_TRACE
+extern "C" int moe_debug_set_trace(void* p) {
+  g_trace_buffer = (unsigned long long*)p;
+  return 0;
+}
+#endif

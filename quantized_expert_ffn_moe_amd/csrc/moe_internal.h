@@ -82,6 +82,9 @@ struct ChainArgs {
   uint32_t* red_flag;                     // [N_RED]
   float* part;                            // [N_ITEMS][H]
   float* q;                               // [N_RED][Q_STRIDE]
+#ifdef MOE_DEVICE_TRACE
+  unsigned long long* trace;              // [256][16][16] timestamps (timeline studies only)
+#endif
 };
 
 struct HistArgs {

@@ -26,11 +26,10 @@ namespace moe {
 // Optional device timestamps for timeline studies: compiled only when
 // MOE_DEVICE_TRACE is defined (never in the shipped library).
 #ifdef MOE_DEVICE_TRACE
-__device__ unsigned long long* g_trace;
-#define MOE_TRACE(b, l, e) \
-  do { if (threadIdx.x == 0 && g_trace) g_trace[((b) * 16 + (l)) * 16 + (e)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#define MOE_TRACE(a, b, l, e) \
+  do { if (threadIdx.x == 0 && (a).trace) (a).trace[((b) * 16 + (l)) * 16 + (e)] = __builtin_amdgcn_s_memrealtime(); } while (0)
 #else
-#define MOE_TRACE(b, l, e) do { } while (0)
+#define MOE_TRACE(a, b, l, e) do { } while (0)
 #endif
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -352,7 +351,6 @@ struct ItemLds {
   uint32_t hw[4 * 8];         // digit planes of h
   float hs;
   float dpart[H * 4];         // down partials: [row][lane group]
-  int tr_layer;               // layer index, for MOE_TRACE only
 };
 
 // Digit planes of the layer input z (in LDS) for weights of format (BITS, G).
@@ -400,7 +398,6 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, float c
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  MOE_TRACE(blockIdx.x, L.tr_layer, 6);
   L.gpart[wv][lane] = acc;
   __syncthreads();
   if (tid < 64) {                       // wave 0: gate/up totals, h, and the planes of h
@@ -417,11 +414,9 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, float c
       L.h[tid] = silu_mul(g, u);
     }
     __builtin_amdgcn_wave_barrier();
-    MOE_TRACE(blockIdx.x, L.tr_layer, 7);
     make_planes<BITS>(L.h, 1.0f, tid, SLICE, L.hw, &L.hs, tid < SLICE / 8);
   }
   __syncthreads();
-  MOE_TRACE(blockIdx.x, L.tr_layer, 8);
   uint32_t pw[8];
   *(uint4*)&pw[0] = *(const uint4*)&L.hw[8 * q];
   *(uint4*)&pw[4] = *(const uint4*)&L.hw[8 * q + 4];
@@ -440,7 +435,6 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, float c
     }
   }
   __syncthreads();
-  MOE_TRACE(blockIdx.x, L.tr_layer, 9);
   const float cs = coef * L.hs;
 #pragma unroll
   for (int row = tid; row < H; row += 512) {
@@ -597,7 +591,7 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, ItemSide&
   const int tid = threadIdx.x, wv = tid >> 6;
   if (wv == 0) wait_flags(a.red_flag, N_RED, epoch, err);
   __syncthreads();
-  MOE_TRACE(blockIdx.x, l, 1);
+  MOE_TRACE(a, blockIdx.x, l, 1);
   {
     const __amdgpu_buffer_rsrc_t ry = coherent_rsrc(a.y, H * 4);
     const __amdgpu_buffer_rsrc_t rq = coherent_rsrc(a.q, N_RED * Q_STRIDE * 4);
@@ -611,7 +605,7 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, ItemSide&
     if (tid + 512 < NQ4) *(float4*)&S.qs[4 * (tid + 512)] = as_float4(q1);
   }
   __syncthreads();
-  MOE_TRACE(blockIdx.x, l, 11);
+  MOE_TRACE(a, blockIdx.x, l, 11);
   const int e = tid >> 3, sub = tid & 7;
   float part = 0.f, sq = 0.f;
 #pragma unroll
@@ -653,7 +647,7 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, ItemSide&
     }
     __syncthreads();
   }
-  MOE_TRACE(blockIdx.x, l, 12);
+  MOE_TRACE(a, blockIdx.x, l, 12);
   return inv;
 }
 
@@ -669,20 +663,19 @@ __device__ void chain_routed(const ChainArgs& a, ItemSide& S, int b, uint32_t ba
   const int p = b / (I / SLICE), J = b % (I / SLICE);
   const size_t ebytes = 3 * matrix_bytes(BR, I, H), escales = 3 * (size_t)I * H / GR;
   for (int l = 0; l < a.n_layers; ++l) {
-    MOE_TRACE(b, l, 0);
-    S.item.tr_layer = l;
+    MOE_TRACE(a, b, l, 0);
     const float inv = chain_layer_input(a, S, l, base + l + 1, true, b == 0, err);
-    MOE_TRACE(b, l, 2);
+    MOE_TRACE(a, b, l, 2);
     const int e = S.pick_e[p];
     ItemRegs<BR, GR> R;
     item_load<BR, GR>(R, a.layer[l].eq + (size_t)e * ebytes, a.layer[l].es + (size_t)e * escales, I, J, wv, lane);
-    MOE_TRACE(b, l, 3);
+    MOE_TRACE(a, b, l, 3);
     item_planes<BR, GR>(S.z, inv, S.item);
-    MOE_TRACE(b, l, 13);
+    MOE_TRACE(a, b, l, 13);
     item_compute<BR, GR, true>(R, S.pick_w[p], a.part + (size_t)b * H, S.item);
-    MOE_TRACE(b, l, 4);
+    MOE_TRACE(a, b, l, 4);
     chain_item_done(a, b, base + l + 1);
-    MOE_TRACE(b, l, 5);
+    MOE_TRACE(a, b, l, 5);
   }
 }
 
@@ -691,18 +684,17 @@ __device__ void chain_shared(const ChainArgs& a, ItemSide& S, int b, uint32_t ba
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int J = b - R_ITEMS;
   for (int l = 0; l < a.n_layers; ++l) {
-    MOE_TRACE(b, l, 0);
-    S.item.tr_layer = l;
+    MOE_TRACE(a, b, l, 0);
     ItemRegs<BS, GS> R;
     item_load<BS, GS>(R, a.layer[l].sq, a.layer[l].ss, IS, J, wv, lane);  // routing-independent: before the wait
     const float inv = chain_layer_input(a, S, l, base + l + 1, false, false, err);
-    MOE_TRACE(b, l, 2);
+    MOE_TRACE(a, b, l, 2);
     item_planes<BS, GS>(S.z, inv, S.item);
-    MOE_TRACE(b, l, 13);
+    MOE_TRACE(a, b, l, 13);
     item_compute<BS, GS, true>(R, 1.0f, a.part + (size_t)b * H, S.item);
-    MOE_TRACE(b, l, 4);
+    MOE_TRACE(a, b, l, 4);
     chain_item_done(a, b, base + l + 1);
-    MOE_TRACE(b, l, 5);
+    MOE_TRACE(a, b, l, 5);
   }
 }
 
@@ -719,7 +711,7 @@ __device__ void chain_reducer(const ChainArgs& a, ReducerSide& S, int rid, uint3
 #pragma unroll
       for (int m = 0; m < 5; ++m) wr[m] = a.layer[s].wr[(size_t)e * H + r0 + sub + 8 * m];
     }
-    MOE_TRACE(N_ITEMS + rid, s, 0);
+    MOE_TRACE(a, N_ITEMS + rid, s, 0);
     if (s == 0) {
       if (tid < RED_ROWS) {
         const int k = r0 + tid;
@@ -728,7 +720,7 @@ __device__ void chain_reducer(const ChainArgs& a, ReducerSide& S, int rid, uint3
     } else {
       if (wv == 0) wait_flags(a.item_flag, N_ITEMS, base + s, err);
       __syncthreads();
-      MOE_TRACE(N_ITEMS + rid, s, 1);
+      MOE_TRACE(a, N_ITEMS + rid, s, 1);
       // all partials of this reducer's rows, 16 bytes per load, all loads in flight together
       u32x4 v[F4_PER_T];
 #pragma unroll
@@ -790,7 +782,7 @@ __device__ void chain_reducer(const ChainArgs& a, ReducerSide& S, int rid, uint3
       __syncthreads();
       if (tid == 0) store_coherent_u32(a.red_flag + rid, base + s + 1);
     }
-    MOE_TRACE(N_ITEMS + rid, s, 5);
+    MOE_TRACE(a, N_ITEMS + rid, s, 5);
   }
 }
 
@@ -1287,8 +1279,3 @@ hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps,
 
 }  // namespace moe
 
-#ifdef MOE_DEVICE_TRACE
-extern "C" int moe_debug_set_trace(void* p) {
-  return (int)hipMemcpyToSymbol(HIP_SYMBOL(moe::g_trace), &p, sizeof(p));
-}
-#endif
