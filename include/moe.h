@@ -198,8 +198,11 @@ moe_status_t moe_rmsnorm(const float* h, void* z, int32_t z_dtype, int32_t n_tok
  *            call counter).  Calls sharing a workspace must be stream ordered.
  *            Word 2 of the workspace becomes nonzero if a wait inside the
  *            kernel gave up (a bug guard; results are then invalid).
- * The launch is cooperative: all 256 workgroups must be co-resident, else
- * MOE_E_HIP is returned and nothing runs.
+ * The kernel's 256 workgroups (one per compute unit on MI355X) must all be
+ * resident at once: the call returns MOE_E_HIP without launching when the
+ * device cannot hold them, and the caller must not run other kernels on the
+ * device concurrently with it (a workgroup kept waiting for a CU would make
+ * the others' bounded waits give up and set the error word).
  * ------------------------------------------------------------------------ */
 #define MOE_DECODE_MAX_LAYERS 16
 

@@ -1224,8 +1224,14 @@ hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The persistent kernel needs all N_ITEMS + N_RED workgroups resident at once.
+// hipLaunchCooperativeKernel guarantees that but costs ~15 us per launch on
+// this stack, so the launch is a plain one, preceded by a check that one
+// compute unit holds at least one workgroup and the device has enough compute
+// units (the workgroup size and LDS use make it one workgroup per CU).  Every
+// wait inside the kernel is bounded, so a violated assumption (e.g. other
+// kernels occupying CUs) ends in the workspace error word, not in a hang.
 hipError_t launch_chain(const ChainArgs& a, hipStream_t s) {
-  void* args[] = {(void*)&a};
   const void* fn;
   const int key = (a.rbits == 8) * 2 + (a.sbits == 8);
   switch (key) {
@@ -1234,7 +1240,14 @@ hipError_t launch_chain(const ChainArgs& a, hipStream_t s) {
     case 2: fn = (const void*)chain_kernel<8, 4>; break;
     default: fn = (const void*)chain_kernel<8, 8>; break;
   }
-  return hipLaunchCooperativeKernel(fn, dim3(N_ITEMS + N_RED), dim3(512), args, 0, s);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, 0);
+  if (e != hipSuccess) return e;
+  if ((long)cus * per_cu < N_ITEMS + N_RED) return hipErrorCooperativeLaunchTooLarge;
+  void* args[] = {(void*)&a};
+  return hipLaunchKernel(fn, dim3(N_ITEMS + N_RED), dim3(512), args, 0, s);
 }
 
 hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s) {
