@@ -63,6 +63,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--path", choices=["chain", "layers"], default="chain")
+    ap.add_argument("--workload", choices=["decode", "prefill273", "multipage2184"], default="decode",
+                    help="decode = the headline 11-layer decode step; the prefill workloads report MFMA figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
@@ -89,6 +91,9 @@ def main():
 
     from quantized_expert_ffn_moe_amd import binding as B
     from synth import WORKLOADS, make_layer, make_tokens
+
+    if args.workload != "decode":
+        return bench_prefill(args)
 
     wl = WORKLOADS[1]
     L = wl.n_layers
@@ -175,6 +180,63 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, xs[: args.warmup + args.steps])
     print(json.dumps(out), flush=True)
+
+
+def prefill_flops(T, ids, routed_fmt):
+    """Algorithmic FLOPs of one prefill layer: 2 per multiply-add of the
+    routed gate/up/down products over all (token, pick) pairs and of the shared
+    expert over all tokens, plus the router."""
+    H, I, IS, E = 1280, 896, 1792, 64
+    return 2 * (T * 6 * 3 * H * I + T * 3 * H * IS + T * E * H)
+
+
+def bench_prefill(args):
+    import numpy as np
+    import torch
+
+    from quantized_expert_ffn_moe_amd import binding as B
+    from synth import WORKLOADS, make_layer, make_tokens
+
+    wl = WORKLOADS[3] if args.workload == "prefill273" else WORKLOADS[4]
+    L = wl.n_layers
+    layers = [make_layer(wl, li) for li in range(L)]
+    packed = [B.pack_layer(layer) for layer in layers]
+    T = wl.n_tokens
+    x, bits = make_tokens(wl)
+    xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    h = torch.empty(T, 1280, dtype=torch.float32, device="cuda")
+    ids = torch.empty(L, T, 6, dtype=torch.int32, device="cuda")
+    w = torch.empty(L, T, 6, dtype=torch.float32, device="cuda")
+    ws = B.workspace(T)
+    stream = torch.cuda.Stream()
+    if wl.chained:
+        flags = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE | (B.MOE_NORM_BF16 if wl.norm_bf16 else 0)
+
+        def step():
+            h.copy_(xt.float())
+            for li in range(L):
+                B.moe_layer_forward(h, packed[li], h, ids[li], w[li], ws, flags, stream=stream)
+    else:
+        def step():
+            B.moe_layer_forward(xt, packed[0], h, ids[0], w[0], ws, 0, stream=stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = L * prefill_flops(T, None, wl.routed)
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({"metric": f"{wl.name}: tokens/s", "value": T / (ms * 1e-3), "unit": "tokens/s",
+                      "ms_per_step": ms, "steps": args.steps, "warmup": args.warmup, "dtype": "f16 MFMA, fp32 acc",
+                      "config": {"workload": wl.name, "tokens": T, "layers": L},
+                      "achieved_tflops": tflops, "bf16_peak_tflops": 2500.0, "mfma_frac": tflops / 2500.0}),
+          flush=True)
 
 
 if __name__ == "__main__":

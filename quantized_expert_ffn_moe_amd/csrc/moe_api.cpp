@@ -274,9 +274,11 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   ra.z = ws.z; ra.ids = topk_ids; ra.w = topk_w;
   if (launch_router(ra, s) != hipSuccess) return MOE_E_HIP;
 
-  // input rows of the experts: the normalised z (f32) or x itself
-  const float* xf = norm ? ws.z : (x_dtype == MOE_F32 ? (const float*)x : nullptr);
-  const uint16_t* xb = (!norm && x_dtype == MOE_BF16) ? (const uint16_t*)x : nullptr;
+  // input rows of the experts: the normalised z (f32, or bf16 when rounded to
+  // bf16, which the grouped path then feeds to the MFMAs without a lo half)
+  const bool zb = norm && (flags & MOE_NORM_BF16);
+  const float* xf = norm ? (zb ? nullptr : ws.z) : (x_dtype == MOE_F32 ? (const float*)x : nullptr);
+  const uint16_t* xb = zb ? (const uint16_t*)ws.z : ((!norm && x_dtype == MOE_BF16) ? (const uint16_t*)x : nullptr);
   const QW rw = make_qw(expert_q, expert_scales, expert_bits, expert_group, I, true);
   const QW sw = make_qw(shared_q, shared_scales, shared_bits, shared_group, IS, false);
   const int accumulate = (flags & MOE_ACCUMULATE) != 0;
@@ -292,24 +294,27 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
     return MOE_OK;
   }
 
+  // token rows per GEMM tile
+  const int mtl = MT;   // 32 rows: measured faster than 64 (occupancy) on the multi-page workload
+  const int max_tiles = (int)((size_t)T * TOPK / mtl) + E + 1;
   HistArgs ha;
   ha.ids = topk_ids; ha.T = T; ha.counts = ws.counts; ha.offsets = ws.offsets;
-  ha.perm = ws.perm; ha.pos_of = ws.pos_of; ha.tiles = ws.tiles; ha.ntiles = ws.ntiles;
+  ha.perm = ws.perm; ha.pos_of = ws.pos_of; ha.tiles = ws.tiles; ha.ntiles = ws.ntiles; ha.mt = mtl;
   if (launch_hist(ha, s) != hipSuccess) return MOE_E_HIP;
 
   GroupedArgs ga;
   ga.T = T; ga.tiles = ws.tiles; ga.ntiles = ws.ntiles; ga.offsets = ws.offsets; ga.perm = ws.perm;
   // routed gate/up: A rows are tokens gathered through the permutation
   ga.af = xf; ga.ab = xb; ga.shared = 0; ga.a_by_token = 1; ga.w = rw; ga.out = ws.h_routed;
-  if (launch_grouped_gateup(ga, ws.max_tiles, s) != hipSuccess) return MOE_E_HIP;
+  if (launch_grouped_gateup(ga, max_tiles, mtl, s) != hipSuccess) return MOE_E_HIP;
   // shared gate/up over all tokens
   ga.shared = 1; ga.w = sw; ga.out = ws.h_shared;
-  if (launch_grouped_gateup(ga, (T + MT - 1) / MT, s) != hipSuccess) return MOE_E_HIP;
+  if (launch_grouped_gateup(ga, (T + mtl - 1) / mtl, mtl, s) != hipSuccess) return MOE_E_HIP;
   // routed down: A rows are h in sorted order
   ga.af = ws.h_routed; ga.ab = nullptr; ga.shared = 0; ga.a_by_token = 0; ga.w = rw; ga.out = ws.ysorted;
-  if (launch_grouped_down(ga, ws.max_tiles, s) != hipSuccess) return MOE_E_HIP;
+  if (launch_grouped_down(ga, max_tiles, mtl, s) != hipSuccess) return MOE_E_HIP;
   ga.af = ws.h_shared; ga.shared = 1; ga.w = sw; ga.out = ws.ys;
-  if (launch_grouped_down(ga, (T + MT - 1) / MT, s) != hipSuccess) return MOE_E_HIP;
+  if (launch_grouped_down(ga, (T + mtl - 1) / mtl, mtl, s) != hipSuccess) return MOE_E_HIP;
   CombineArgs ca;
   ca.ys = ws.ys; ca.ysorted = ws.ysorted; ca.pos_of = ws.pos_of; ca.tw = topk_w;
   ca.y = y; ca.T = T; ca.accumulate = accumulate;

@@ -12,7 +12,7 @@ constexpr int TOPK = 6;      // experts picked per token
 constexpr int I = 896;       // routed expert intermediate
 constexpr int IS = 1792;     // fused shared expert intermediate
 constexpr int TILE = 1024;   // bytes of one packed 16-row tile
-constexpr int MT = 32;       // token rows per grouped-GEMM tile
+constexpr int MT = 32;       // smallest token-row tile of the grouped GEMMs (64 for big batches)
 constexpr int DECODE_MAX_T = 4;  // largest token count routed to the GEMV path by default
 constexpr int MAX_T = 8192;      // largest token count of one call
 constexpr int MOE_MAX_SLOTS = MAX_T * TOPK;
@@ -34,7 +34,7 @@ struct RouterArgs {
   const void* x; int x_bf16; int T;
   const float* wr; const float* bias;
   int norm, norm_bf16; float eps;
-  float* z;            // [T][H] normalised input (written when norm)
+  void* z;             // [T][H] normalised input (written when norm): f32, or bf16 with norm_bf16
   int32_t* ids; float* w;
 };
 
@@ -92,6 +92,7 @@ struct HistArgs {
   int32_t* counts; int32_t* offsets;    // [E], [E+1]
   int32_t* perm; int32_t* pos_of;       // [T*6]: sorted slot -> (t*6+j); (t*6+j) -> sorted position
   int32_t* tiles; int32_t* ntiles;      // [max][2] (expert, first row), count
+  int mt;                               // rows per tile
 };
 
 struct GroupedArgs {
@@ -116,8 +117,8 @@ hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s);
 hipError_t launch_chain(const ChainArgs& a, hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_hist(const HistArgs& a, hipStream_t s);
-hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, hipStream_t s);
-hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, hipStream_t s);
+hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, int mtl, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int mtl, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps, hipStream_t s);
 

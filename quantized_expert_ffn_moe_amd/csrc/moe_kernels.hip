@@ -77,87 +77,127 @@ __device__ __forceinline__ float inv_rms(const float* red4, float eps) {
 
 // ---------------------------------------------------------------------------
 // Router: (optional RMSNorm) -> 64 logits -> softmax -> greedy top-6.
-// One workgroup per 8 tokens; wave w owns experts 16w..16w+15 for the logits
-// and tokens w, w+4 for the selection (one lane per expert).
+// One workgroup of 256 threads per 16 tokens.  Pass 1 normalises the rows and
+// writes z; pass 2 accumulates the logits over K chunks staged in LDS (W_r
+// transposed so that a lane reads its expert's 4 consecutive k as one float4;
+// thread = (expert e = tid % 64, token group tid / 64 of 4 tokens)); the
+// selection ranks every expert against the others from LDS.  The softmax is
+// increasing in the logit, so the 6 largest logits (ties to the lower index)
+// are the 6 largest probabilities.
 // ---------------------------------------------------------------------------
-constexpr int RT_TB = 8;
+constexpr int RT_TB = 16;      // tokens per workgroup
+constexpr int RT_KC = 128;     // K chunk staged in LDS
 
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  __shared__ float zs[RT_TB][H];
-  __shared__ float lg[RT_TB][E];
+  __shared__ __attribute__((aligned(16))) float wt[RT_KC / 4][E][4];   // 32 KB
+  __shared__ __attribute__((aligned(16))) float zc[RT_TB][RT_KC];      // 8 KB
+  __shared__ float inv_s[RT_TB];
   __shared__ float red[RT_TB][4];
+  __shared__ __attribute__((aligned(16))) float lg[RT_TB][E];
+  __shared__ float exs[RT_TB][E];
   const int t0 = blockIdx.x * RT_TB;
   const int nt = min(RT_TB, a.T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-
-  for (int tt = 0; tt < nt; ++tt) {
-    float v[5];
+  auto xval = [&](int t, int k) -> float {
+    const size_t idx = (size_t)(t0 + t) * H + k;
+    return a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x)[idx]) : ((const float*)a.x)[idx];
+  };
+  // pass 1: 1/rms per token and the normalised rows (written once to z)
+  if (a.norm) {
+    for (int tt = 0; tt < nt; ++tt) {
+      float v[5];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const size_t idx = (size_t)(t0 + tt) * H + tid + 256 * i;
-      v[i] = a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x)[idx]) : ((const float*)a.x)[idx];
-      zs[tt][tid + 256 * i] = v[i];
-    }
-    if (a.norm) {
+      for (int i = 0; i < 5; ++i) v[i] = xval(tt, tid + 256 * i);
       const float ss = wave_sum(thread_sumsq(v));
       if (lane == 0) red[tt][wv] = ss;
     }
-  }
-  __syncthreads();
-  if (a.norm) {
+    __syncthreads();
+    if (tid < nt) inv_s[tid] = inv_rms(red[tid], a.eps);
+    __syncthreads();
     for (int tt = 0; tt < nt; ++tt) {
-      const float inv = inv_rms(red[tt], a.eps);
+      const float inv = inv_s[tt];
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
         const int k = tid + 256 * i;
-        float z = zs[tt][k] * inv;
-        if (a.norm_bf16) z = bf16_rne(z);
-        zs[tt][k] = z;
-        a.z[(size_t)(t0 + tt) * H + k] = z;
+        const float z = xval(tt, k) * inv;
+        if (a.norm_bf16) ((uint16_t*)a.z)[(size_t)(t0 + tt) * H + k] = (uint16_t)(__float_as_uint(bf16_rne(z)) >> 16);
+        else ((float*)a.z)[(size_t)(t0 + tt) * H + k] = z;
       }
+    }
+  }
+  // pass 2: logits
+  const int e = tid & 63, tg = tid >> 6;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < H; k0 += RT_KC) {
+    __syncthreads();
+    for (int i = tid; i < E * RT_KC / 4; i += 256) {            // W_r[e'][k0 + 4c .. +3] -> wt[c][e']
+      const int ee = i / (RT_KC / 4), c = i % (RT_KC / 4);
+      *(float4*)&wt[c][ee][0] = *(const float4*)(a.wr + (size_t)ee * H + k0 + 4 * c);
+    }
+    for (int i = tid; i < RT_TB * RT_KC; i += 256) {
+      const int tt = i / RT_KC, kk = i % RT_KC;
+      float z = 0.f;
+      if (tt < nt) {
+        z = xval(tt, k0 + kk);
+        if (a.norm) {
+          z *= inv_s[tt];
+          if (a.norm_bf16) z = bf16_rne(z);
+        }
+      }
+      zc[tt][kk] = z;
     }
     __syncthreads();
-  }
-  for (int ei = 0; ei < 16; ++ei) {
-    const int e = wv * 16 + ei;
-    const float4* wrow = (const float4*)(a.wr + (size_t)e * H);
-    float4 wr4[5];
+#pragma unroll 4
+    for (int c = 0; c < RT_KC / 4; ++c) {
+      const float4 w4 = *(const float4*)&wt[c][e][0];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) wr4[i] = wrow[lane + 64 * i];
-    const float b = a.bias ? a.bias[e] : 0.f;
-    for (int tt = 0; tt < nt; ++tt) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const float4 z4 = *(const float4*)&zs[tt][4 * (lane + 64 * i)];
-        acc += wr4[i].x * z4.x + wr4[i].y * z4.y + wr4[i].z * z4.z + wr4[i].w * z4.w;
+      for (int j = 0; j < 4; ++j) {
+        const float4 z4 = *(const float4*)&zc[4 * tg + j][4 * c];
+        acc[j] += w4.x * z4.x + w4.y * z4.y + w4.z * z4.z + w4.w * z4.w;
       }
-      acc = wave_sum(acc);
-      if (lane == 0) lg[tt][e] = acc + b;
     }
   }
+  const float b = a.bias ? a.bias[e] : 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lg[4 * tg + j][e] = acc[j] + b;
   __syncthreads();
-  for (int tt = wv; tt < nt; tt += 4) {
-    const float v = lg[tt][lane];
-    const float m = wave_max(v);
-    const float ex = expf(v - m);
-    const float p = ex / wave_sum(ex);
-    bool taken = false;
-    for (int j = 0; j < TOPK; ++j) {
-      float bv = taken ? -1.f : p;
-      int bi = lane;
+  // selection: thread = (token tid / 16, experts tid % 16 + 16 i)
+  const int tt = tid >> 4, e0 = tid & 15;
+  if (tt < nt) {
+    float le[4];
+    int rank[4] = {0, 0, 0, 0};
+    float mx = -INFINITY;
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (lane == bi) taken = true;
-      if (lane == 0) {
-        a.ids[(size_t)(t0 + tt) * TOPK + j] = bi;
-        a.w[(size_t)(t0 + tt) * TOPK + j] = bv;
+    for (int i = 0; i < 4; ++i) le[i] = lg[tt][e0 + 16 * i];
+#pragma unroll
+    for (int k = 0; k < E; k += 4) {
+      const float4 v = *(const float4*)&lg[tt][k];
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        mx = fmaxf(mx, vv[u]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ei = e0 + 16 * i;
+          rank[i] += (vv[u] > le[i] || (vv[u] == le[i] && k + u < ei)) ? 1 : 0;
+        }
       }
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) exs[tt][e0 + 16 * i] = expf(le[i] - mx);
+    __builtin_amdgcn_wave_barrier();
+    float sm = 0.f;
+#pragma unroll
+    for (int k = 0; k < E; k += 4) {
+      const float4 v = *(const float4*)&exs[tt][k];
+      sm += (v.x + v.y) + (v.z + v.w);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (rank[i] < TOPK) {
+        a.ids[(size_t)(t0 + tt) * TOPK + rank[i]] = e0 + 16 * i;
+        a.w[(size_t)(t0 + tt) * TOPK + rank[i]] = exs[tt][e0 + 16 * i] / sm;
+      }
   }
 }
 
@@ -824,56 +864,73 @@ __global__ void zero_words_kernel(uint32_t* p, size_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Histogram + stable permutation of the (token, pick) slots by expert.
+// Histogram + stable permutation of the (token, pick) slots by expert, one
+// workgroup of 16 waves.  Wave w owns a contiguous chunk of slots: per-wave
+// counts (LDS atomics), an exclusive scan over (expert, wave) gives every
+// wave its starting position per expert, then each wave walks its chunk in
+// order, 64 slots at a time, and places the slots of one expert at a time
+// (ballot + prefix popcount), which keeps the order of slots within an expert.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void hist_kernel(HistArgs a) {
   __shared__ uint8_t sid[MOE_MAX_SLOTS];
-  __shared__ int cnt[E], off[E + 1];
+  __shared__ int cntw[16][E];
+  __shared__ int basew[16][E];
+  __shared__ int cnt[E], off[E + 1], toff[E + 1];
   const int N = a.T * TOPK;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int chunk = ((N + 15) / 16 + 63) / 64 * 64;
+  const int c0 = wv * chunk, c1 = min(N, c0 + chunk);
   for (int i = tid; i < N; i += 1024) sid[i] = (uint8_t)a.ids[i];
+  for (int i = tid; i < 16 * E; i += 1024) (&cntw[0][0])[i] = 0;
   __syncthreads();
-  for (int ee = 0; ee < 4; ++ee) {
-    const int e = wv * 4 + ee;
-    int c = 0;
-    for (int base = 0; base < N; base += 64) {
-      const int i = base + lane;
-      c += __popcll(__ballot(i < N && sid[i] == e));
-    }
-    if (lane == 0) cnt[e] = c;
+  for (int i = c0 + lane; i < c1; i += 64) atomicAdd(&cntw[wv][sid[i]], 1);
+  __syncthreads();
+  if (tid < E) {
+    int run = 0;
+    for (int w = 0; w < 16; ++w) { basew[w][tid] = run; run += cntw[w][tid]; }
+    cnt[tid] = run;
   }
   __syncthreads();
   if (tid == 0) {
-    off[0] = 0;
-    int n = 0;
+    off[0] = 0; toff[0] = 0;
     for (int e = 0; e < E; ++e) {
       off[e + 1] = off[e] + cnt[e];
-      a.counts[e] = cnt[e];
-      a.offsets[e] = off[e];
-      for (int r0 = 0; r0 < cnt[e]; r0 += MT) {
-        a.tiles[2 * n] = e;
-        a.tiles[2 * n + 1] = r0;
-        ++n;
-      }
+      toff[e + 1] = toff[e] + (cnt[e] + a.mt - 1) / a.mt;
     }
+    *a.ntiles = toff[E];
     a.offsets[E] = off[E];
-    *a.ntiles = n;
+  }
+  __syncthreads();
+  if (tid < E) {
+    a.counts[tid] = cnt[tid];
+    a.offsets[tid] = off[tid];
+    for (int j = 0; j < toff[tid + 1] - toff[tid]; ++j) {
+      a.tiles[2 * (toff[tid] + j)] = tid;
+      a.tiles[2 * (toff[tid] + j) + 1] = j * a.mt;
+    }
+    for (int w = 0; w < 16; ++w) basew[w][tid] += off[tid];
   }
   __syncthreads();
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int ee = 0; ee < 4; ++ee) {
-    const int e = wv * 4 + ee;
-    int run = off[e];
-    for (int base = 0; base < N; base += 64) {
-      const int i = base + lane;
-      const bool m = i < N && sid[i] == e;
-      const uint64_t mask = __ballot(m);
-      if (m) {
-        const int p = run + __popcll(mask & below);
+  for (int g = c0; g < c1; g += 64) {
+    const int i = g + lane;
+    const bool valid = i < c1;
+    const int my_e = valid ? sid[i] : -1;
+    uint64_t todo = __ballot(valid);
+    while (todo) {
+      const int leader = __ffsll((unsigned long long)todo) - 1;
+      const int e0 = __shfl(my_e, leader);
+      const uint64_t m = __ballot(my_e == e0);
+      const int base = basew[wv][e0];
+      if (my_e == e0) {
+        const int p = base + __popcll(m & below);
         a.perm[p] = i;
         a.pos_of[i] = p;
       }
-      run += __popcll(mask);
+      __builtin_amdgcn_wave_barrier();
+      if (lane == leader) basew[wv][e0] = base + __popcll(m);
+      __builtin_amdgcn_wave_barrier();
+      todo &= ~m;
     }
   }
 }
@@ -921,28 +978,49 @@ template <int BITS> __device__ __forceinline__ int perm_k(int p) {
 constexpr int KS = 128;             // K staged in LDS per step
 constexpr int LDS_ROW = KS + 8;     // f16 per LDS row (16-byte pad against bank conflicts)
 
-// Stage A rows [row tile][k0 .. k0+KS) into LDS as f16 (hi plane, and lo plane
-// when SPLIT), permuted within each 8-group to the B operand order.
-template <int BITS, bool SPLIT>
-__device__ __forceinline__ void stage_a(_Float16* lds, const float* af, const uint16_t* ab, const int* arow,
-                                        int K, int k0) {
+// A-operand staging, split into a global fetch (into registers, issued one
+// stage ahead) and an LDS store (f16 hi plane, and lo plane when SPLIT,
+// permuted within each 8-group into the B operand order).  Thread tid owns the
+// 8-element segments tid + 256 j: row = seg / 16, k = 8 (seg % 16).
+template <int MTL, bool F32>
+struct AFetch {
+  static constexpr int NSEG = MTL / 16;
+  uint4 raw[NSEG][F32 ? 2 : 1];
+};
+
+template <int MTL, bool F32>
+__device__ __forceinline__ void fetch_a(AFetch<MTL, F32>& A, const void* src_base, const int* arow, int K, int k0) {
   const int tid = threadIdx.x;
-  const int row = tid >> 3, seg = tid & 7;           // 32 rows x 8 segments of 16
-  const int src = arow[row];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int kk = 16 * seg + 8 * h;
-    float v[8];
+  for (int j = 0; j < AFetch<MTL, F32>::NSEG; ++j) {
+    const int seg = tid + 256 * j, row = seg >> 4, kk = 8 * (seg & 15);
+    const int src = arow[row];
     if (src < 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    } else if (af) {
-      const float4* p = (const float4*)(af + (size_t)src * K + k0 + kk);
-      const float4 a0 = p[0], a1 = p[1];
-      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
-      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+      A.raw[j][0] = make_uint4(0, 0, 0, 0);
+      if (F32) A.raw[j][F32 ? 1 : 0] = make_uint4(0, 0, 0, 0);
+    } else if (F32) {
+      const uint4* p = (const uint4*)((const float*)src_base + (size_t)src * K + k0 + kk);
+      A.raw[j][0] = p[0];
+      A.raw[j][F32 ? 1 : 0] = p[1];
     } else {
-      const uint4 u = *(const uint4*)(ab + (size_t)src * K + k0 + kk);
+      A.raw[j][0] = *(const uint4*)((const uint16_t*)src_base + (size_t)src * K + k0 + kk);
+    }
+  }
+}
+
+template <int BITS, int MTL, bool F32, bool SPLIT>
+__device__ __forceinline__ void store_a(_Float16* lds, const AFetch<MTL, F32>& A) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < AFetch<MTL, F32>::NSEG; ++j) {
+    const int seg = tid + 256 * j, row = seg >> 4, kk = 8 * (seg & 15);
+    float v[8];
+    if (F32) {
+      const uint4 a0 = A.raw[j][0], a1 = A.raw[j][F32 ? 1 : 0];
+      v[0] = __uint_as_float(a0.x); v[1] = __uint_as_float(a0.y); v[2] = __uint_as_float(a0.z); v[3] = __uint_as_float(a0.w);
+      v[4] = __uint_as_float(a1.x); v[5] = __uint_as_float(a1.y); v[6] = __uint_as_float(a1.z); v[7] = __uint_as_float(a1.w);
+    } else {
+      const uint4 u = A.raw[j][0];
       const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -959,18 +1037,18 @@ __device__ __forceinline__ void stage_a(_Float16* lds, const float* af, const ui
       lo[p] = (_Float16)(x - (float)xh);
     }
     *(half8*)(lds + row * LDS_ROW + kk) = hi;
-    if (SPLIT) *(half8*)(lds + 32 * LDS_ROW + row * LDS_ROW + kk) = lo;
+    if (SPLIT) *(half8*)(lds + MTL * LDS_ROW + row * LDS_ROW + kk) = lo;
   }
 }
 
 struct TileInfo { int valid, nrows, pbase, row0, e; };
 
-__device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile) {
+__device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile, int mtl) {
   TileInfo ti;
   if (a.shared) {
-    ti.row0 = tile * MT;
+    ti.row0 = tile * mtl;
     ti.valid = ti.row0 < a.T;
-    ti.nrows = min(MT, a.T - ti.row0);
+    ti.nrows = min(mtl, a.T - ti.row0);
     ti.pbase = 0; ti.e = 0;
   } else {
     ti.valid = tile < *a.ntiles;
@@ -978,28 +1056,31 @@ __device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile) {
     ti.e = a.tiles[2 * tile];
     const int r0 = a.tiles[2 * tile + 1];
     const int cnt = a.offsets[ti.e + 1] - a.offsets[ti.e];
-    ti.nrows = min(MT, cnt - r0);
+    ti.nrows = min(mtl, cnt - r0);
     ti.pbase = a.offsets[ti.e] + r0;
     ti.row0 = 0;
   }
   return ti;
 }
 
-// Gate/up: a workgroup owns one 32-row tile of one expert and 64 intermediate
-// columns; wave w computes gate and up for the 16 columns of n-subtile
-// 4cb + w, then writes h = SiLU(gate) * up.
-template <int BITS, bool SPLIT>
+// Gate/up: a workgroup owns one MTL-row tile of one expert and 128
+// intermediate columns; wave w computes gate and up for columns 32w..32w+31
+// of them (n-subtiles 8cb + 2w, 8cb + 2w + 1 of both matrices) and writes
+// h = SiLU(gate) * up.  A and B of the next K stage are fetched into registers
+// while the current stage computes.
+template <int BITS, bool SPLIT, int MTL>
 __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
-  constexpr int KB = kb_cols(BITS), NKB = H / KB;
-  constexpr int NSTAGE = H / KS;
-  const int inter = a.w.inter, ncb = inter / 64;
+  constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB;   // uint4 per B tile per stage
+  constexpr int NSTAGE = H / KS, MS = MTL / 16;
+  constexpr bool F32 = SPLIT;
+  const int inter = a.w.inter, ncb = inter / 128;
   const int tile = blockIdx.x / ncb, cb = blockIdx.x % ncb;
-  const TileInfo ti = tile_info(a, tile);
+  const TileInfo ti = tile_info(a, tile, MTL);
   if (!ti.valid) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q4 = lane >> 4;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[(SPLIT ? 2 : 1) * 32 * LDS_ROW];
-  __shared__ int arow[MT];
-  if (tid < MT) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[(SPLIT ? 2 : 1) * MTL * LDS_ROW];
+  __shared__ int arow[MTL];
+  if (tid < MTL) {
     int src = -1;
     if (tid < ti.nrows) src = a.shared ? ti.row0 + tid : a.perm[ti.pbase + tid] / TOPK;
     arow[tid] = src;
@@ -1009,46 +1090,61 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
   const size_t mbytes = matrix_bytes(BITS, inter, H);
   const int ng = H / a.w.group, cpg = a.w.group / 32;
   const size_t mscales = (size_t)inter * ng;
-  const int ntile = 4 * cb + wv;
+  const void* asrc = F32 ? (const void*)a.af : (const void*)a.ab;
+  // B tiles of this wave: i = 0,1 gate n-subtiles, 2,3 up n-subtiles
+  auto btile = [&](int i, int kb) -> const uint4* {
+    const int nt = 8 * cb + 2 * wv + (i & 1);
+    return (const uint4*)(eq + (i >> 1) * mbytes + ((size_t)nt * NKB + kb) * TILE + lane * 16);
+  };
 
-  float4v acc[2][2], ctmp[2][2];
+  float4v acc[4][MS], ctmp[4][MS];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) { acc[i][ms] = float4v{0, 0, 0, 0}; ctmp[i][ms] = float4v{0, 0, 0, 0}; }
+    for (int ms = 0; ms < MS; ++ms) { acc[i][ms] = float4v{0, 0, 0, 0}; ctmp[i][ms] = float4v{0, 0, 0, 0}; }
   __syncthreads();
 
+  AFetch<MTL, F32> An;
+  uint4 bn[4][NB], bc[4][NB];
+  fetch_a<MTL, F32>(An, asrc, arow, H, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < NB; ++h) bn[i][h] = *btile(i, h);
+
   for (int st = 0; st < NSTAGE; ++st) {
-    // B tiles of this stage: int4 -> 1 tile (128 K), int8 -> 2 tiles (64 K each)
-    uint4 bq[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int h = 0; h < (BITS == 4 ? 1 : 2); ++h) {
-        const int kb = st * (KS / KB) + h;
-        bq[i][h] = *(const uint4*)(eq + (i ? mbytes : 0) + ((size_t)ntile * NKB + kb) * TILE + lane * 16);
-      }
     __syncthreads();
-    stage_a<BITS, SPLIT>(lds, a.af, a.ab, arow, H, st * KS);
+    store_a<BITS, MTL, F32, SPLIT>(lds, An);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < NB; ++h) bc[i][h] = bn[i][h];
+    if (st + 1 < NSTAGE) {
+      fetch_a<MTL, F32>(An, asrc, arow, H, (st + 1) * KS);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < NB; ++h) bn[i][h] = *btile(i, (st + 1) * NB + h);
+    }
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
       const int gc = st * (KS / 32) + c;
       const bool first = (gc % cpg) == 0, last = (gc % cpg) == cpg - 1;
-      half8 bfr[2];
+      half8 bfr[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (BITS == 4) bfr[i] = unpack_int4(word_of(bq[i][0], c));
-        else bfr[i] = unpack_int8(word_of(bq[i][c >> 1], 2 * (c & 1)), word_of(bq[i][c >> 1], 2 * (c & 1) + 1));
+      for (int i = 0; i < 4; ++i) {
+        if (BITS == 4) bfr[i] = unpack_int4(word_of(bc[i][0], c));
+        else bfr[i] = unpack_int8(word_of(bc[i][c >> 1], 2 * (c & 1)), word_of(bc[i][c >> 1], 2 * (c & 1) + 1));
       }
 #pragma unroll
-      for (int ms = 0; ms < 2; ++ms) {
+      for (int ms = 0; ms < MS; ++ms) {
         const int lrow = ms * 16 + r, lcol = 32 * c + 8 * q4;
         const half8 ahi = *(const half8*)(lds + lrow * LDS_ROW + lcol);
         half8 alo;
-        if (SPLIT) alo = *(const half8*)(lds + 32 * LDS_ROW + lrow * LDS_ROW + lcol);
+        if (SPLIT) alo = *(const half8*)(lds + MTL * LDS_ROW + lrow * LDS_ROW + lcol);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 4; ++i) {
           float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[i][ms];
           cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bfr[i], cc, 0, 0, 0);
           if (SPLIT) cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bfr[i], cc, 0, 0, 0);
@@ -1058,80 +1154,93 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
       if (last) {
         const int grp = gc / cpg;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const float s = es[(i ? mscales : 0) + (size_t)(16 * ntile + r) * ng + grp];
+        for (int i = 0; i < 4; ++i) {
+          const int nt = 8 * cb + 2 * wv + (i & 1);
+          const float sv = es[(i >> 1) * mscales + (size_t)(16 * nt + r) * ng + grp];
 #pragma unroll
-          for (int ms = 0; ms < 2; ++ms) acc[i][ms] += s * ctmp[i][ms];
+          for (int ms = 0; ms < MS; ++ms) acc[i][ms] += sv * ctmp[i][ms];
         }
       }
     }
   }
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms)
+  for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int m = ms * 16 + 4 * q4 + k;
       if (m < ti.nrows) {
         const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
-        a.out[orow * inter + 16 * ntile + r] = silu_mul(acc[0][ms][k], acc[1][ms][k]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          a.out[orow * inter + 16 * (8 * cb + 2 * wv + j) + r] = silu_mul(acc[j][ms][k], acc[2 + j][ms][k]);
       }
     }
 }
 
-// Down: a workgroup owns one 32-row tile of A (h, fp32 split hi/lo) and four
+// Down: a workgroup owns one MTL-row tile of A (h, fp32 split hi/lo) and four
 // packed down tiles' worth of output rows: wave w covers row tile 4cb + w,
 // i.e. 64 (int4) or 32 (int8) output columns, one 16-column MFMA n-subtile
 // per 16 rows.  Each 16-byte lane load of a down tile feeds every n-subtile of
-// the row tile for one 32-wide K chunk.
-template <int BITS>
+// the row tile for one 32-wide K chunk.  Next-stage A and B are fetched ahead.
+template <int BITS, int MTL>
 __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
-  constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4;
+  constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4, MS = MTL / 16;
   const int inter = a.w.inter, nstage = inter / KS;
   const int tile = blockIdx.x / NCB, cb = blockIdx.x % NCB;
-  const TileInfo ti = tile_info(a, tile);
+  const TileInfo ti = tile_info(a, tile, MTL);
   if (!ti.valid) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q4 = lane >> 4;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2 * 32 * LDS_ROW];
-  __shared__ int arow[MT];
-  if (tid < MT) arow[tid] = tid < ti.nrows ? (a.shared ? ti.row0 + tid : ti.pbase + tid) : -1;
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2 * MTL * LDS_ROW];
+  __shared__ int arow[MTL];
+  if (tid < MTL) arow[tid] = tid < ti.nrows ? (a.shared ? ti.row0 + tid : ti.pbase + tid) : -1;
   const size_t mbytes = matrix_bytes(BITS, inter, H);
   const uint8_t* dq = a.w.q + (size_t)ti.e * a.w.e_bytes + 2 * mbytes;
   const int cpg = a.w.group / 32;
   const float* ds = a.w.s + (size_t)ti.e * a.w.e_scales + 2 * (size_t)inter * (H / a.w.group);
   const int rt = 4 * cb + wv;
 
-  float4v acc[NSUB][2], ctmp[NSUB][2];
+  float4v acc[NSUB][MS], ctmp[NSUB][MS];
 #pragma unroll
   for (int j = 0; j < NSUB; ++j)
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) { acc[j][ms] = float4v{0, 0, 0, 0}; ctmp[j][ms] = float4v{0, 0, 0, 0}; }
+    for (int ms = 0; ms < MS; ++ms) { acc[j][ms] = float4v{0, 0, 0, 0}; ctmp[j][ms] = float4v{0, 0, 0, 0}; }
   __syncthreads();
 
-  for (int st = 0; st < nstage; ++st) {
-    uint4 bq[KS / 32];
+  AFetch<MTL, true> An;
+  uint4 bn[KS / 32], bc[KS / 32];
+  fetch_a<MTL, true>(An, a.af, arow, inter, 0);
 #pragma unroll
-    for (int c = 0; c < KS / 32; ++c)
-      bq[c] = *(const uint4*)(dq + ((size_t)(st * (KS / 32) + c) * NRT + rt) * TILE + lane * 16);
+  for (int c = 0; c < KS / 32; ++c) bn[c] = *(const uint4*)(dq + ((size_t)c * NRT + rt) * TILE + lane * 16);
+
+  for (int st = 0; st < nstage; ++st) {
     __syncthreads();
-    stage_a<BITS, true>(lds, a.af, nullptr, arow, inter, st * KS);
+    store_a<BITS, MTL, true, true>(lds, An);
+#pragma unroll
+    for (int c = 0; c < KS / 32; ++c) bc[c] = bn[c];
+    if (st + 1 < nstage) {
+      fetch_a<MTL, true>(An, a.af, arow, inter, (st + 1) * KS);
+#pragma unroll
+      for (int c = 0; c < KS / 32; ++c)
+        bn[c] = *(const uint4*)(dq + ((size_t)((st + 1) * (KS / 32) + c) * NRT + rt) * TILE + lane * 16);
+    }
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
       const int gc = st * (KS / 32) + c;
       const bool first = (gc % cpg) == 0, last = (gc % cpg) == cpg - 1;
       const int lcol = 32 * c + 8 * q4;
-      half8 ahi[2], alo[2];
+      half8 ahi[MS], alo[MS];
 #pragma unroll
-      for (int ms = 0; ms < 2; ++ms) {
+      for (int ms = 0; ms < MS; ++ms) {
         ahi[ms] = *(const half8*)(lds + (ms * 16 + r) * LDS_ROW + lcol);
-        alo[ms] = *(const half8*)(lds + 32 * LDS_ROW + (ms * 16 + r) * LDS_ROW + lcol);
+        alo[ms] = *(const half8*)(lds + MTL * LDS_ROW + (ms * 16 + r) * LDS_ROW + lcol);
       }
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
-        const half8 bfr = BITS == 4 ? unpack_int4(word_of(bq[c], j))
-                                    : unpack_int8(word_of(bq[c], 2 * j), word_of(bq[c], 2 * j + 1));
+        const half8 bfr = BITS == 4 ? unpack_int4(word_of(bc[c], j))
+                                    : unpack_int8(word_of(bc[c], 2 * j), word_of(bc[c], 2 * j + 1));
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms) {
+        for (int ms = 0; ms < MS; ++ms) {
           float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[j][ms];
           cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ms], bfr, cc, 0, 0, 0);
           cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ms], bfr, cc, 0, 0, 0);
@@ -1144,13 +1253,13 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
         for (int j = 0; j < NSUB; ++j) {
           const float sj = sp[j];
 #pragma unroll
-          for (int ms = 0; ms < 2; ++ms) acc[j][ms] += sj * ctmp[j][ms];
+          for (int ms = 0; ms < MS; ++ms) acc[j][ms] += sj * ctmp[j][ms];
         }
       }
     }
   }
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms)
+  for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int m = ms * 16 + 4 * q4 + k;
@@ -1260,23 +1369,34 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, hipStream_t s) {
-  const dim3 grid(max_tiles * (a.w.inter / 64));
+template <int MTL>
+static void gateup_dispatch(const GroupedArgs& a, dim3 grid, hipStream_t s) {
   const bool split = a.af != nullptr;
   if (a.w.bits == 4) {
-    if (split) hipLaunchKernelGGL((grouped_gateup_kernel<4, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((grouped_gateup_kernel<4, false>), grid, dim3(256), 0, s, a);
+    if (split) hipLaunchKernelGGL((grouped_gateup_kernel<4, true, MTL>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((grouped_gateup_kernel<4, false, MTL>), grid, dim3(256), 0, s, a);
   } else {
-    if (split) hipLaunchKernelGGL((grouped_gateup_kernel<8, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((grouped_gateup_kernel<8, false>), grid, dim3(256), 0, s, a);
+    if (split) hipLaunchKernelGGL((grouped_gateup_kernel<8, true, MTL>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((grouped_gateup_kernel<8, false, MTL>), grid, dim3(256), 0, s, a);
   }
+}
+
+hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, int mtl, hipStream_t s) {
+  const dim3 grid(max_tiles * (a.w.inter / 128));
+  if (mtl == 64) gateup_dispatch<64>(a, grid, s);
+  else gateup_dispatch<32>(a, grid, s);
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, hipStream_t s) {
+hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int mtl, hipStream_t s) {
   const dim3 grid(max_tiles * (H / (4 * down_rows(a.w.bits))));
-  if (a.w.bits == 4) hipLaunchKernelGGL(grouped_down_kernel<4>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(grouped_down_kernel<8>, grid, dim3(256), 0, s, a);
+  if (mtl == 64) {
+    if (a.w.bits == 4) hipLaunchKernelGGL((grouped_down_kernel<4, 64>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((grouped_down_kernel<8, 64>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.w.bits == 4) hipLaunchKernelGGL((grouped_down_kernel<4, 32>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((grouped_down_kernel<8, 32>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
