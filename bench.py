@@ -37,6 +37,33 @@ def layer_bytes(layer_ids, routed_fmt, shared_fmt):
     return len(set(layer_ids)) * per_expert + shared + router + acts
 
 
+KERNEL_SOURCES = ("quantized_expert_ffn_moe_amd/csrc/moe_kernels.hip", "quantized_expert_ffn_moe_amd/csrc/moe_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_chain_kernel_11layers_traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic():
+    """HBM bytes per dispatch of the decode kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes (scaled by the copy-kernel calibration), or
+    None when the kernel sources have changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec["hbm_bytes_per_dispatch"]
+
+
 def cpu_baseline(layers, tokens, budget_s=20.0):
     """The oracle as it is, on the host cores, over as many tokens as fit the budget."""
     import numpy as np
@@ -175,7 +202,7 @@ def main():
                    "weight_replicas": args.replicas, "path": args.path},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": step_bytes, "ms_per_launch": ms_kernel},
+                     "traffic": counted_traffic(), "bytes_per_launch": step_bytes, "ms_per_launch": ms_kernel},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, xs[: args.warmup + args.steps])

@@ -158,6 +158,10 @@ size_t moe_workspace_bytes(int32_t n_tokens);
  * in block floating point (19-bit mantissa for int4 weights, 23-bit for int8,
  * one shared power of two per scale group) and forms exact integer dot
  * products.  Both apply each group scale to the partial sum of its group.
+ * Domain of the grouped path: every input element (after the optional
+ * RMSNorm, which bounds it by sqrt(1280)) must be below 65504 in magnitude,
+ * the f16 range; larger inputs give non-finite outputs there.  The per-token
+ * path has no such limit.
  * ------------------------------------------------------------------------ */
 moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
                                const float* router_w, const float* router_b,
@@ -177,7 +181,7 @@ moe_status_t moe_rmsnorm(const float* h, void* z, int32_t z_dtype, int32_t n_tok
 
 /* ------------------------------------------------------------------------
  * Decode step: one token through n_layers chained MoE layers in a single
- * persistent (cooperative) kernel launch -- the decoder's per-token path
+ * persistent kernel launch -- the decoder's per-token path
  * (demo page step 6: layers 1..11 are MoE; step 7: greedy decoding runs one
  * token at a time).  With MOE_NORM_INPUT | MOE_ACCUMULATE each layer computes
  *   h_l = h_{l-1} + MoE_l(RMSNorm(h_{l-1})),   h_0 = x,   y = h_L,

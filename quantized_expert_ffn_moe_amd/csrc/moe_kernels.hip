@@ -548,9 +548,10 @@ __global__ __launch_bounds__(256) void dec_reduce_kernel(DecReduceArgs a) {
 
 // ---------------------------------------------------------------------------
 // Persistent decode step: one token through n_layers chained layers in one
-// cooperative launch.  Workgroups 0..223 are items (routed picks 0..5 x 28
-// slices, then 56 shared slices), workgroups 224..255 are reducers owning 40
-// rows of the residual stream each.  Per layer:
+// launch of 256 co-resident workgroups (one per compute unit).  Workgroups
+// 0..223 are items (routed picks 0..5 x 28 slices, then 56 shared slices),
+// workgroups 224..255 are reducers owning 40 rows of the residual stream
+// each.  Per layer:
 //   reducers (stage s): h_s = (h_{s-1}) + sum of the items' partials of layer
 //     s-1, written to y; partial router logits W_r[:, rows] h_s[rows] and the
 //     partial sum of squares, then a flag;
