@@ -78,8 +78,8 @@ Workspace carve(void* base, int T) {
 }
 
 struct DecodeWorkspace {
-  uint32_t* hdr; uint32_t* item_flag; uint32_t* red_flag; float* part; float* q;
-  size_t flag_words;   // words cleared by moe_decode_workspace_init
+  uint32_t* hdr; uint32_t* ipart; uint32_t* rec;
+  size_t clear_words;  // words cleared by moe_decode_workspace_init (all of it: tags must start stale)
   size_t bytes;
 };
 
@@ -87,12 +87,10 @@ DecodeWorkspace carve_decode(void* base) {
   DecodeWorkspace w;
   Carver c{(char*)base, 0};
   w.hdr = (uint32_t*)c.take(64 * 4);
-  w.item_flag = (uint32_t*)c.take(N_ITEMS * 4);
-  w.red_flag = (uint32_t*)c.take(N_RED * 4);
-  w.flag_words = c.off / 4;
-  w.part = (float*)c.take((size_t)N_ITEMS * H * 4);
-  w.q = (float*)c.take((size_t)N_RED * Q_STRIDE * 4);
+  w.ipart = (uint32_t*)c.take((size_t)N_ITEMS * ITEM_U4 * 16);
+  w.rec = (uint32_t*)c.take((size_t)N_RED * REC_U4 * 16);
   w.bytes = c.off;
+  w.clear_words = c.off / 4;
   return w;
 }
 
@@ -342,7 +340,7 @@ moe_status_t moe_decode_workspace_init(void* workspace, size_t workspace_bytes, 
   const DecodeWorkspace dw = carve_decode(workspace);
   if (workspace_bytes < dw.bytes) return MOE_E_WORKSPACE;
   (void)hipGetLastError();
-  if (launch_zero_words((uint32_t*)workspace, dw.flag_words, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
+  if (launch_zero_words((uint32_t*)workspace, dw.clear_words, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
   return MOE_OK;
 }
 
@@ -378,7 +376,7 @@ moe_status_t moe_decode_forward(const void* x, int32_t x_dtype, float* y, int32_
   a.norm = (flags & MOE_NORM_INPUT) != 0; a.accumulate = (flags & MOE_ACCUMULATE) != 0; a.eps = 1e-6f;
   a.rbits = expert_bits; a.rgroup = expert_group; a.sbits = shared_bits; a.sgroup = shared_group;
   a.ids = topk_ids; a.tw = topk_w;
-  a.hdr = dw.hdr; a.item_flag = dw.item_flag; a.red_flag = dw.red_flag; a.part = dw.part; a.q = dw.q;
+  a.hdr = dw.hdr; a.ipart = dw.ipart; a.rec = dw.rec;
 #ifdef MOE_DEVICE_TRACE
   a.trace = g_trace_buffer;
 #endif

@@ -63,6 +63,11 @@ constexpr int MAX_LAYERS = 16;
 constexpr int N_RED = 32;                 // reducer workgroups
 constexpr int RED_ROWS = H / N_RED;       // 40 rows each
 constexpr int Q_STRIDE = 68;              // 64 partial logits + sum of squares, padded
+// Tagged 16-byte words (three f32 values + the epoch tag of the writer's stage).
+constexpr int PART_U4 = (RED_ROWS + 2) / 3;      // 14 words: one item's partial for one reducer
+constexpr int ITEM_U4 = N_RED * PART_U4;         // 448 words per item
+constexpr int REC_VALS = RED_ROWS + E + 1;       // reducer record: h rows, partial logits, sum of squares
+constexpr int REC_U4 = (REC_VALS + 2) / 3;       // 35 words
 struct LayerPtrs {
   const float* wr; const float* bias;
   const uint8_t* eq; const float* es;
@@ -78,10 +83,8 @@ struct ChainArgs {
   int rbits, rgroup, sbits, sgroup;
   int32_t* ids; float* tw;                // [n_layers][6]
   uint32_t* hdr;                          // [0] call sequence, [1] done count, [2] error
-  uint32_t* item_flag;                    // [N_ITEMS]
-  uint32_t* red_flag;                     // [N_RED]
-  float* part;                            // [N_ITEMS][H]
-  float* q;                               // [N_RED][Q_STRIDE]
+  uint32_t* ipart;                        // [N_ITEMS][N_RED][PART_U4] tagged words (16 B each)
+  uint32_t* rec;                          // [N_RED][REC_U4] tagged words
 #ifdef MOE_DEVICE_TRACE
   unsigned long long* trace;              // [256][16][16] timestamps (timeline studies only)
 #endif

@@ -44,16 +44,45 @@ __device__ __forceinline__ float bf16_rne(float v) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+// Cross-lane butterflies on DPP (no LDS round trip).  Partner lanes: quad_perm
+// [1,0,3,2] -> lane ^ 1, [2,3,0,1] -> lane ^ 2, row_half_mirror -> 7 - i
+// inside each group of 8, row_mirror -> 15 - i inside each row of 16.  After
+// the steps for a group of N lanes every lane of the group holds the same
+// value: + and max are commutative, so both partners of a step compute the
+// identical result.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int N>   // N in {2, 4, 8, 16}: groups of N consecutive lanes
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<DPP_XOR1>(v);
+  if (N >= 4) v += dpp<DPP_XOR2>(v);
+  if (N >= 8) v += dpp<DPP_HALF_MIRROR>(v);
+  if (N >= 16) v += dpp<DPP_MIRROR>(v);
   return v;
 }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  if (N >= 4) v = fmaxf(v, dpp<DPP_XOR2>(v));
+  if (N >= 8) v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  if (N >= 16) v = fmaxf(v, dpp<DPP_MIRROR>(v));
   return v;
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+// Whole-wave reductions (all 64 lanes active): rows of 16, then the four row
+// results in a fixed order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<16>(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
@@ -205,23 +234,26 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 // GEMV arithmetic: exact integer dot products.  The input vector is written in
 // block floating point: a block of consecutive elements shares 2^e with
 // max|x| < 2^e, and each element becomes a signed integer mantissa
-// m = rint(x * 2^(F - e)), |m| <= 2^F, split into balanced digits
-// (int4 weights: 5 base-16 digits in [-8, 7], F = 18; int8 weights: 3 base-256
-// digits in [-128, 127], F = 22).  v_dot8_i32_i4 / v_dot4_i32_i8 multiply the
-// two's-complement weight codes by one digit plane at a time with exact int32
-// sums; the planes are recombined per scale group and the group's f32 scale
-// and 2^(e - F) are applied once.  The only rounding is that of m (half a unit
-// of 2^(e - F), i.e. 2^-19 or 2^-23 of the block maximum) and the f32
-// accumulation across groups.
+// m = rint(x * 2^(F - e)), |m| <= 2^F, split into balanced digits (int4
+// weights: 5 base-16 digits in [-8, 7], F = 18; int8 weights: 3 base-256
+// digits in [-128, 127], F = 22).  v_dot8_i32_i4 / v_dot4_i32_i8 multiply the two's-complement
+// weight codes by one digit plane at a time with exact int32 sums; the planes
+// are recombined per scale group and the group's f32 scale and 2^(e - F) are
+// applied once.  The only rounding is that of m (at most 2^-(F+1) of 2^e,
+// i.e. 2^-F of the block maximum) and the f32 accumulation across groups.
 //
-// Plane layout (LDS, u32 words, 8 per group of 8 consecutive elements kg):
-//   int4: word j < 5  = digit j of elements 8kg..8kg+7 in nibbles 0..7
+// Plane layout (LDS, NW = 8 u32 words per group of 8 consecutive elements kg):
+//   int4: word j      = digit j of elements 8kg..8kg+7 in nibbles 0..7
 //   int8: word 2j + h = digit j of elements 8kg+4h..8kg+4h+3 in bytes 0..3
 // which matches the code order of a lane's word(s) in a packed tile.
 // ---------------------------------------------------------------------------
 template <int BITS> struct Digits {
   static constexpr int ND = BITS == 4 ? 5 : 3;     // digit planes
   static constexpr int F = BITS == 4 ? 18 : 22;    // mantissa magnitude bits
+  // m + OFF has the ordinary digits of m's balanced digits plus base/2
+  static constexpr uint32_t OFF = BITS == 4 ? 0x88888u : 0x808080u;
+  static constexpr uint32_t FLIP = BITS == 4 ? 0x88888888u : 0x80808080u;
+  static constexpr int NW = 8;                     // plane words per group of 8 elements (5 or 6 used)
 };
 
 // One thread per group of 8 elements (kg < n/8); blocks of `blk` elements
@@ -240,35 +272,88 @@ __device__ __forceinline__ void make_planes(const float* x, float mul, int kg, i
       amax = fmaxf(amax, fabsf(v[i]));
     }
   }
-  for (int o = 1; o < blk / 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  // block maximum over the blk / 8 lanes of the block (4, 8 or 16)
+  amax = blk >= 128 ? group_max<16>(amax) : blk >= 64 ? group_max<8>(amax) : group_max<4>(amax);
   if (!active) return;
   int e;
   frexpf(amax, &e);                       // amax < 2^e (e = 0 when the block is zero)
   constexpr int F = Digits<BITS>::F;
   if ((kg & (blk / 8 - 1)) == 0) xs[(8 * kg) / blk] = ldexpf(1.0f, e - F);
-  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // The balanced digits of m (each in [-base/2, base/2)) are the ordinary
+  // base-`base` digits of m + OFF, OFF = (base/2)(1 + base + ...), each minus
+  // base/2; as a two's-complement digit that is the ordinary digit with its
+  // top bit flipped.  |m| <= 2^F keeps m + OFF in [0, base^ND).
+  uint32_t M[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int m = (int)rintf(ldexpf(v[i], F - e));
+  for (int i = 0; i < 8; ++i) M[i] = (uint32_t)((int)rintf(ldexpf(v[i], F - e)) + (int)Digits<BITS>::OFF);
+  constexpr int NW = Digits<BITS>::NW;
+  uint32_t w[NW];
+  if constexpr (BITS == 4) {
 #pragma unroll
-    for (int j = 0; j < Digits<BITS>::ND; ++j) {
-      if (BITS == 4) {
-        const int d = ((m + 8) & 15) - 8;
-        w[j] |= (uint32_t)(d & 15) << (4 * i);
-        m = (m - d) >> 4;
-      } else {
-        const int d = ((m + 128) & 255) - 128;
-        w[2 * j + (i >> 2)] |= (uint32_t)(d & 255) << (8 * (i & 3));
-        m = (m - d) >> 8;
+    for (int j = 0; j < 5; ++j) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t |= ((M[i] >> (4 * j)) & 15u) << (4 * i);
+      w[j] = t ^ Digits<BITS>::FLIP;
+    }
+    w[5] = w[6] = w[7] = 0u;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t |= ((M[4 * hh + i] >> (8 * j)) & 255u) << (8 * i);
+        w[2 * j + hh] = t ^ Digits<BITS>::FLIP;
       }
+    w[6] = w[7] = 0u;
+  }
+  *(uint4*)&xw[NW * kg] = make_uint4(w[0], w[1], w[2], w[3]);
+  *(uint4*)&xw[NW * kg + 4] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int N>   // bitwise OR over groups of N in {4, 8} consecutive lanes
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+  v |= dpp_u<DPP_XOR1>(v);
+  v |= dpp_u<DPP_XOR2>(v);
+  if (N >= 8) v |= dpp_u<DPP_HALF_MIRROR>(v);
+  return v;
+}
+
+// Digit planes of the 32 values of an item's slice (one block, one exponent),
+// one value per lane of a whole wave (lanes 32..63 pass 0): the same planes as
+// make_planes with blk = 32, built one element per lane and merged with OR.
+template <int BITS>
+__device__ __forceinline__ void slice_planes(float hv, int lane, uint32_t* hw, float* hs) {
+  constexpr int F = Digits<BITS>::F;
+  const float amax = wave_max(fabsf(hv));
+  int e;
+  frexpf(amax, &e);
+  if (lane == 0) *hs = ldexpf(1.0f, e - F);
+  const uint32_t M = (uint32_t)((int)rintf(ldexpf(hv, F - e)) + (int)Digits<BITS>::OFF);
+  if (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const uint32_t w = group_or<8>(((M >> (4 * j)) & 15u) << (4 * (lane & 7)));
+      if ((lane & 7) == 0 && lane < SLICE) hw[Digits<BITS>::NW * (lane >> 3) + j] = w ^ Digits<BITS>::FLIP;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const uint32_t w = group_or<4>(((M >> (8 * j)) & 255u) << (8 * (lane & 3)));
+      if ((lane & 3) == 0 && lane < SLICE)
+        hw[Digits<BITS>::NW * (lane >> 3) + 2 * j + ((lane >> 2) & 1)] = w ^ Digits<BITS>::FLIP;
     }
   }
-  *(uint4*)&xw[8 * kg] = make_uint4(w[0], w[1], w[2], w[3]);
-  *(uint4*)&xw[8 * kg + 4] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
 // Per-plane integer partial sums of one lane's 8 codes (chunk c of its 16-byte
-// tile slice) against the matching plane words pw[0..7].
+// tile slice) against the matching plane words pw[0..NW).
 template <int BITS>
 __device__ __forceinline__ void dot_planes(const uint4& v, int c, const uint32_t* pw, int* P) {
   if (BITS == 4) {
@@ -335,6 +420,9 @@ __device__ __forceinline__ void item_load(ItemRegs<BITS, G>& R, const uint8_t* e
   if (IR::NGW % 4 == 0) {
 #pragma unroll
     for (int g = 0; g < IR::NGW; g += 4) *(float4*)&R.gsc[g] = *(const float4*)(gp + g);
+  } else if (IR::NGW % 2 == 0) {
+#pragma unroll
+    for (int g = 0; g < IR::NGW; g += 2) *(float2*)&R.gsc[g] = *(const float2*)(gp + g);
   } else {
 #pragma unroll
     for (int g = 0; g < IR::NGW; ++g) R.gsc[g] = gp[g];
@@ -387,7 +475,6 @@ struct ItemLds {
   float xs[H / 32];           // per-block unit 2^(e - F)
   float gpart[8][64];         // per-wave, per-lane gate/up partial sums
   float gu[64];               // gate (2x16) and up (2x16) totals
-  float h[SLICE];             // SiLU(g) * u of the slice
   uint32_t hw[4 * 8];         // digit planes of h
   float hs;
   float dpart[H * 4];         // down partials: [row][lane group]
@@ -401,11 +488,11 @@ __device__ __forceinline__ void item_planes(const float* z, float mul, ItemLds& 
   __syncthreads();
 }
 
-// z planes in L.xw/L.xs (item_planes); out: 1280 partials (coherent stores
-// when they are read by other workgroups of the same kernel).  Cross-lane sums
-// go through LDS in a fixed order.
-template <int BITS, int G, bool COHERENT>
-__device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, float coef, float* out, ItemLds& L) {
+// z planes in L.xw/L.xs (item_planes) -> L.dpart (down partials per row and
+// lane group) and L.hs (the block unit of h).  Cross-lane sums go through LDS
+// in a fixed order.  Ends with a workgroup barrier.
+template <int BITS, int G>
+__device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds& L) {
   using IR = ItemRegs<BITS, G>;
   constexpr int ND = Digits<BITS>::ND, CPG = G / 32;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, q = lane >> 4;
@@ -417,13 +504,14 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, float c
 #pragma unroll
   for (int m = 0; m < IR::GU_TPW; ++m) {
     // all plane words of this tile's chunks first (one LDS round trip per tile)
-    uint32_t pw[IR::CPT][8];
+    constexpr int NW = Digits<BITS>::NW;
+    uint32_t pw[IR::CPT][NW];
 #pragma unroll
     for (int c = 0; c < IR::CPT; ++c) {
       const int k0 = (kb0 + m) * IR::KB + 32 * c;
-      *(uint4*)&pw[c][0] = *(const uint4*)&L.xw[k0 + 8 * q];
-      if (BITS == 8) *(uint4*)&pw[c][4] = *(const uint4*)&L.xw[k0 + 8 * q + 4];
-      else pw[c][4] = L.xw[k0 + 8 * q + 4];
+      *(uint4*)&pw[c][0] = *(const uint4*)&L.xw[(k0 + 8 * q) / 8 * NW];
+      if (BITS == 8) *(uint4*)&pw[c][4] = *(const uint4*)&L.xw[(k0 + 8 * q) / 8 * NW + 4];
+      else pw[c][4] = L.xw[(k0 + 8 * q) / 8 * NW + 4];
     }
 #pragma unroll
     for (int c = 0; c < IR::CPT; ++c) {
@@ -441,6 +529,7 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, float c
   L.gpart[wv][lane] = acc;
   __syncthreads();
   if (tid < 64) {                       // wave 0: gate/up totals, h, and the planes of h
+    float hv = 0.f;
     if (tid < SLICE) {
       const int ti = tid >> 4, rr = tid & 15;   // column 16 ti + rr of the slice
       float g = 0.f, u = 0.f;
@@ -451,15 +540,16 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, float c
           g += L.gpart[2 * ti + hh][16 * qq + rr];
           u += L.gpart[4 + 2 * ti + hh][16 * qq + rr];
         }
-      L.h[tid] = silu_mul(g, u);
+      hv = silu_mul(g, u);
     }
-    __builtin_amdgcn_wave_barrier();
-    make_planes<BITS>(L.h, 1.0f, tid, SLICE, L.hw, &L.hs, tid < SLICE / 8);
+    slice_planes<BITS>(hv, tid, L.hw, &L.hs);
   }
   __syncthreads();
-  uint32_t pw[8];
-  *(uint4*)&pw[0] = *(const uint4*)&L.hw[8 * q];
-  *(uint4*)&pw[4] = *(const uint4*)&L.hw[8 * q + 4];
+  constexpr int NWH = Digits<BITS>::NW;
+  uint32_t pw[NWH];
+  *(uint4*)&pw[0] = *(const uint4*)&L.hw[NWH * q];
+  if (BITS == 8) *(uint4*)&pw[4] = *(const uint4*)&L.hw[NWH * q + 4];
+  else pw[4] = L.hw[NWH * q + 4];
 #pragma unroll
   for (int m = 0; m < IR::D_TPW; ++m) {
     const int rt = wv + 8 * m;
@@ -475,34 +565,35 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, float c
     }
   }
   __syncthreads();
-  const float cs = coef * L.hs;
-#pragma unroll
-  for (int row = tid; row < H; row += 512) {
-    const float4 p4 = *(const float4*)&L.dpart[4 * row];
-    const float v = cs * ((p4.x + p4.y) + (p4.z + p4.w));
-    if (COHERENT) store_coherent(out + row, v);
-    else out[row] = v;
-  }
 }
 
-// One decode item end to end (loads, planes, compute) for format (BITS, G).
-template <int BITS, int G, bool COHERENT>
+// Final value of down row `row` of an item: coef * unit(h) * sum of the four
+// lane-group partials.
+__device__ __forceinline__ float item_row(const ItemLds& L, float cs, int row) {
+  const float4 p4 = *(const float4*)&L.dpart[4 * row];
+  return cs * ((p4.x + p4.y) + (p4.z + p4.w));
+}
+
+// One decode item end to end (loads, planes, compute), 1280 rows to out.
+template <int BITS, int G>
 __device__ __forceinline__ void run_item(const uint8_t* eq, const float* es, int inter, int J, const float* z,
                                          float coef, float* out, ItemLds& L) {
   const int tid = threadIdx.x;
   ItemRegs<BITS, G> R;
   item_load<BITS, G>(R, eq, es, inter, J, tid >> 6, tid & 63);
   item_planes<BITS, G>(z, 1.0f, L);
-  item_compute<BITS, G, COHERENT>(R, coef, out, L);
+  item_compute<BITS, G>(R, L);
+  const float cs = coef * L.hs;
+  for (int row = tid; row < H; row += 512) out[row] = item_row(L, cs, row);
 }
 
-template <int BITS, bool COHERENT>
+template <int BITS>
 __device__ __forceinline__ void run_item_g(int group, const uint8_t* eq, const float* es, int inter, int J,
                                            const float* z, float coef, float* out, ItemLds& L) {
   switch (group) {
-    case 32: run_item<BITS, 32, COHERENT>(eq, es, inter, J, z, coef, out, L); break;
-    case 64: run_item<BITS, 64, COHERENT>(eq, es, inter, J, z, coef, out, L); break;
-    default: run_item<BITS, 128, COHERENT>(eq, es, inter, J, z, coef, out, L); break;
+    case 32: run_item<BITS, 32>(eq, es, inter, J, z, coef, out, L); break;
+    case 64: run_item<BITS, 64>(eq, es, inter, J, z, coef, out, L); break;
+    default: run_item<BITS, 128>(eq, es, inter, J, z, coef, out, L); break;
   }
 }
 
@@ -519,10 +610,10 @@ __global__ __launch_bounds__(512) void dec_items_kernel(DecItemsArgs a) {
   if (item < R_ITEMS) {
     const int p = item / (I / SLICE), J = item % (I / SLICE);
     const int e = a.ids[(size_t)t * TOPK + p];
-    run_item_g<BR, false>(a.rw.group, a.rw.q + (size_t)e * a.rw.e_bytes, a.rw.s + (size_t)e * a.rw.e_scales, I, J, z,
+    run_item_g<BR>(a.rw.group, a.rw.q + (size_t)e * a.rw.e_bytes, a.rw.s + (size_t)e * a.rw.e_scales, I, J, z,
                           a.tw[(size_t)t * TOPK + p], out, L);
   } else {
-    run_item_g<BS, false>(a.sw.group, a.sw.q, a.sw.s, IS, item - R_ITEMS, z, 1.0f, out, L);
+    run_item_g<BS>(a.sw.group, a.sw.q, a.sw.s, IS, item - R_ITEMS, z, 1.0f, out, L);
   }
 }
 
@@ -553,34 +644,58 @@ __global__ __launch_bounds__(256) void dec_reduce_kernel(DecReduceArgs a) {
 // workgroups 224..255 are reducers owning 40 rows of the residual stream
 // each.  Per layer:
 //   reducers (stage s): h_s = (h_{s-1}) + sum of the items' partials of layer
-//     s-1, written to y; partial router logits W_r[:, rows] h_s[rows] and the
-//     partial sum of squares, then a flag;
-//   items (layer s): wait for all reducer flags, rebuild RMSNorm(h_s), the
-//     64 logits, softmax and top-6 from the partials (every routed item
-//     computes the same routing), stream their expert slice and write their
-//     partial, then a flag.
-// No grid-wide barrier: each side polls only the flags it depends on.  Flags
-// carry epoch numbers (call sequence * 64 + stage + 1), so nothing has to be
-// cleared between calls.  Data exchanged inside the kernel uses device-scope
-// (L2-coherent) loads and stores.
+//     s-1 for their rows; then a record of those rows of h_s, the partial
+//     router logits W_r[:, rows] h_s[rows] and the partial sum of squares;
+//   items (layer s): read all 32 records, rebuild RMSNorm(h_s), the 64
+//     logits, softmax and top-6 (every routed item computes the same routing),
+//     stream their expert slice and write their partial for each reducer.
+// Exchange without flags: every 16-byte word carries three f32 values and the
+// epoch tag of the stage that wrote it (call sequence * 64 + stage + 1).  A
+// 16-byte aligned vector store lands as one piece, so a reader that sees the
+// current tag in a word also sees that word's values; it polls the words
+// themselves with device-scope (L2-coherent) loads.  Writers never wait for
+// their stores, and nothing is cleared between calls.
 // ---------------------------------------------------------------------------
 constexpr long SPIN_LIMIT = 1L << 20;  // polls before a wait gives up (about a second)
 
-// Wave-wide poll until all n (a multiple of 4, at most 256) flags equal epoch.
-__device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* err) {
+__device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, CPOL_SC1);
+}
+
+// Lane 0 of each wave polls one word (off[0], valid in lane 0) until it
+// carries `tag`: a few bytes per wave while the writers are still busy.  The
+// full loads follow (load_tagged), which check every word.
+__device__ __forceinline__ void wait_first(__amdgpu_buffer_rsrc_t r, uint32_t off0, uint32_t tag, long& spins) {
   const int lane = threadIdx.x & 63;
-  const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(flags, n * 4);
-  long spins = 0;
   while (true) {
     bool ok = true;
-    if (lane < n / 4) {
-      const u32x4 v = load16_coherent(rs, lane * 16);
-      ok = v[0] == epoch && v[1] == epoch && v[2] == epoch && v[3] == epoch;
-    }
+    if (lane == 0) ok = load16_coherent(r, off0)[3] == tag;
     if (__all(ok)) break;
     __builtin_amdgcn_s_sleep(1);
+    if (++spins > SPIN_LIMIT) break;
+  }
+}
+
+// Load the tagged words at off[m] (where valid[m]) and poll until every one
+// carries `tag` (after wait_first this usually takes one round trip).  Wave-uniform exit; a wait that runs out sets the error word.
+template <int N>
+__device__ __forceinline__ void load_tagged(__amdgpu_buffer_rsrc_t r, const uint32_t* off, const bool* valid,
+                                            u32x4* v, uint32_t tag, long& spins, uint32_t* err) {
+#pragma unroll
+  for (int m = 0; m < N; ++m)
+    if (valid[m]) v[m] = load16_coherent(r, off[m]);
+  while (true) {
+    bool done = true;
+#pragma unroll
+    for (int m = 0; m < N; ++m)
+      if (valid[m] && v[m][3] != tag) done = false;
+    if (__all(done)) break;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int m = 0; m < N; ++m)
+      if (valid[m] && v[m][3] != tag) v[m] = load16_coherent(r, off[m]);
     if (++spins > SPIN_LIMIT) {
-      if (lane == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
   }
@@ -592,96 +707,94 @@ struct ItemSide {
   ItemLds item;
   float qs[N_RED * Q_STRIDE];
   float lg[E];            // logits
-  float ex[E];            // exp(logit - max)
   int pick_e[TOPK];
   float pick_w[TOPK];
-  float inv;
 };
 struct ReducerSide {
-  float parts[N_ITEMS * RED_ROWS];
-  float red[12][RED_ROWS];
+  float red[N_ITEMS / 7][PART_U4 * 3];   // per item group, per row (42 slots, 40 used)
   float hrow[RED_ROWS];
-  float sq[RED_ROWS];
+  float rec[REC_U4 * 3];
 };
 union ChainLds {
   ItemSide it;
   ReducerSide rd;
 };
 
-__device__ __forceinline__ float sum8(float v) {   // identical result in all 8 lanes of a group
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  return v;
-}
-__device__ __forceinline__ float max8(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  return fmaxf(v, __shfl_xor(v, 4));
-}
-
-// Wait for the reducers of stage l, then rebuild this layer's input in LDS (z
-// = h, to be multiplied by the returned 1/rms) and, for routed items, the
-// routing.  Every workgroup runs identical arithmetic, so every item sees the
-// same z and the same picks.  The 512 threads work as 64 groups of 8 (group e
-// = expert e): logits and the sum of squares come from the 32 reducer partials
-// in a fixed order; the softmax is increasing in the logit, so the 6 largest
-// logits (ties to the lower index) are the 6 largest probabilities.
-__device__ __forceinline__ float chain_layer_input(const ChainArgs& a, ItemSide& S, int l, uint32_t epoch,
-                                                   bool routed, bool report, uint32_t* err) {
-  const int tid = threadIdx.x, wv = tid >> 6;
-  if (wv == 0) wait_flags(a.red_flag, N_RED, epoch, err);
-  __syncthreads();
-  MOE_TRACE(a, blockIdx.x, l, 1);
+// Wait for the reducer records of stage l, then rebuild this layer's input in
+// LDS (z = h, to be multiplied by the returned 1/rms) and, for routed items,
+// the routing.  Every workgroup runs identical arithmetic, so every item sees
+// the same z and the same picks.  The 512 threads work as 64 groups of 8
+// (group e = expert e): logits and the sum of squares come from the 32 reducer
+// partials in a fixed order; the softmax is increasing in the logit, so the 6
+// largest logits (ties to the lower index) are the 6 largest probabilities.
+__device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const LayerPtrs* LP, ItemSide& S, int l,
+                                                   uint32_t epoch, bool routed, bool report, uint32_t* err) {
+  const int tid = threadIdx.x;
   {
-    const __amdgpu_buffer_rsrc_t ry = coherent_rsrc(a.y, H * 4);
-    const __amdgpu_buffer_rsrc_t rq = coherent_rsrc(a.q, N_RED * Q_STRIDE * 4);
-    constexpr int NQ4 = N_RED * Q_STRIDE / 4;   // 544
-    u32x4 zv, q0, q1;
-    if (tid < H / 4) zv = load16_coherent(ry, tid * 16);
-    q0 = load16_coherent(rq, tid * 16);
-    if (tid + 512 < NQ4) q1 = load16_coherent(rq, (tid + 512) * 16);
-    if (tid < H / 4) *(float4*)&S.z[4 * tid] = as_float4(zv);
-    *(float4*)&S.qs[4 * tid] = as_float4(q0);
-    if (tid + 512 < NQ4) *(float4*)&S.qs[4 * (tid + 512)] = as_float4(q1);
+    constexpr int NR = N_RED * REC_U4;          // 1120 words
+    constexpr int PT = (NR + 511) / 512;        // 3 per thread
+    const __amdgpu_buffer_rsrc_t rr = coherent_rsrc(a.rec, NR * 16);
+    uint32_t off[PT];
+    bool valid[PT];
+    u32x4 v[PT];
+#pragma unroll
+    for (int m = 0; m < PT; ++m) {
+      const int f = tid + 512 * m;
+      valid[m] = f < NR;
+      off[m] = (uint32_t)f * 16;
+    }
+    long spins = 0;
+    wait_first(rr, off[0], epoch, spins);
+    load_tagged<PT>(rr, off, valid, v, epoch, spins, err);
+    MOE_TRACE(a, blockIdx.x, l, 1);
+#pragma unroll
+    for (int m = 0; m < PT; ++m) {
+      if (!valid[m]) continue;
+      const int f = tid + 512 * m, rid = f / REC_U4, k = f % REC_U4;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int vi = 3 * k + i;
+        const float val = __uint_as_float(v[m][i]);
+        if (vi < RED_ROWS) S.z[RED_ROWS * rid + vi] = val;
+        else if (vi < RED_ROWS + E) S.qs[rid * Q_STRIDE + vi - RED_ROWS] = val;
+        else if (vi == REC_VALS - 1) S.qs[rid * Q_STRIDE + E] = val;
+      }
+    }
   }
   __syncthreads();
-  MOE_TRACE(a, blockIdx.x, l, 11);
+  MOE_TRACE(a, blockIdx.x, l, 6);
   const int e = tid >> 3, sub = tid & 7;
   float part = 0.f, sq = 0.f;
 #pragma unroll
   for (int m = 0; m < N_RED / 8; ++m) {
     part += S.qs[(sub + 8 * m) * Q_STRIDE + e];
-    sq += S.qs[(sub + 8 * m) * Q_STRIDE + 64];
+    sq += S.qs[(sub + 8 * m) * Q_STRIDE + E];
   }
-  part = sum8(part);
-  sq = sum8(sq);
+  part = group_sum<8>(part);
+  sq = group_sum<8>(sq);
   const float inv = a.norm ? 1.0f / sqrtf(sq / (float)H + a.eps) : 1.0f;
   if (routed) {
-    const float* bias = a.layer[l].bias;
+    const float* bias = LP[l].bias;
     const float lge = part * inv + (bias ? bias[e] : 0.f);
     if (sub == 0) S.lg[e] = lge;
     __syncthreads();
-    float mx = -INFINITY;
+    MOE_TRACE(a, blockIdx.x, l, 7);
+    // every wave: max and softmax denominator over the 64 logits, lane i
+    // holding logit i (the same arithmetic in every wave and workgroup)
+    const float li = S.lg[tid & 63];
+    const float mx = wave_max(li);
+    const float sm = wave_sum(expf(li - mx));
+    // rank of expert e among the 64 (ties to the lower index): 8 per lane
     int rank = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = sub + 8 * j;
       const float lk = S.lg[k];
-      mx = fmaxf(mx, lk);
       rank += (lk > lge || (lk == lge && k < e)) ? 1 : 0;
     }
-    mx = max8(mx);
-    rank = (int)sum8((float)rank);
-    const float ex = expf(lge - mx);
-    if (sub == 0) S.ex[e] = ex;
-    __syncthreads();
-    float sm = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sm += S.ex[sub + 8 * j];
-    sm = sum8(sm);
+    rank = (int)group_sum<8>((float)rank);
     if (sub == 0 && rank < TOPK) {
-      const float pr = ex / sm;
+      const float pr = expf(lge - mx) / sm;
       S.pick_e[rank] = e;
       S.pick_w[rank] = pr;
       if (report) { a.ids[l * TOPK + rank] = e; a.tw[l * TOPK + rank] = pr; }
@@ -692,136 +805,150 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, ItemSide&
   return inv;
 }
 
-__device__ __forceinline__ void chain_item_done(const ChainArgs& a, int b, uint32_t epoch) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) store_coherent_u32(a.item_flag + b, epoch);
+// An item's partial (item_compute done, cs = coef * unit of h) as tagged words
+// [reducer][14]: word c of reducer r holds rows 40r + 3c .. 40r + 3c + 2.
+__device__ __forceinline__ void chain_item_store(const ChainArgs& a, const ItemLds& L, float cs, int b,
+                                                 uint32_t tag) {
+  const int tid = threadIdx.x;
+  if (tid < ITEM_U4) {
+    const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(a.ipart, N_ITEMS * ITEM_U4 * 16);
+    const int r = tid / PART_U4, c = tid % PART_U4;
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int rr = 3 * c + i;
+      w[i] = __float_as_uint(rr < RED_ROWS ? item_row(L, cs, RED_ROWS * r + rr) : 0.f);
+    }
+    w[3] = tag;
+    store16_coherent(rp, ((uint32_t)b * ITEM_U4 + tid) * 16, w);
+  }
 }
 
 template <int BR, int GR>
-__device__ void chain_routed(const ChainArgs& a, ItemSide& S, int b, uint32_t base, uint32_t* err) {
+__device__ void chain_routed(const ChainArgs& a, const LayerPtrs* LP, ItemSide& S, int b, uint32_t base, uint32_t* err) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int p = b / (I / SLICE), J = b % (I / SLICE);
   const size_t ebytes = 3 * matrix_bytes(BR, I, H), escales = 3 * (size_t)I * H / GR;
   for (int l = 0; l < a.n_layers; ++l) {
     MOE_TRACE(a, b, l, 0);
-    const float inv = chain_layer_input(a, S, l, base + l + 1, true, b == 0, err);
+    const float inv = chain_layer_input(a, LP, S, l, base + l + 1, true, b == 0, err);
     MOE_TRACE(a, b, l, 2);
     const int e = S.pick_e[p];
     ItemRegs<BR, GR> R;
-    item_load<BR, GR>(R, a.layer[l].eq + (size_t)e * ebytes, a.layer[l].es + (size_t)e * escales, I, J, wv, lane);
+    item_load<BR, GR>(R, LP[l].eq + (size_t)e * ebytes, LP[l].es + (size_t)e * escales, I, J, wv, lane);
     MOE_TRACE(a, b, l, 3);
     item_planes<BR, GR>(S.z, inv, S.item);
     MOE_TRACE(a, b, l, 13);
-    item_compute<BR, GR, true>(R, S.pick_w[p], a.part + (size_t)b * H, S.item);
+    item_compute<BR, GR>(R, S.item);
     MOE_TRACE(a, b, l, 4);
-    chain_item_done(a, b, base + l + 1);
+    chain_item_store(a, S.item, S.pick_w[p] * S.item.hs, b, base + l + 1);
     MOE_TRACE(a, b, l, 5);
   }
 }
 
 template <int BS, int GS>
-__device__ void chain_shared(const ChainArgs& a, ItemSide& S, int b, uint32_t base, uint32_t* err) {
+__device__ void chain_shared(const ChainArgs& a, const LayerPtrs* LP, ItemSide& S, int b, uint32_t base, uint32_t* err) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int J = b - R_ITEMS;
   for (int l = 0; l < a.n_layers; ++l) {
     MOE_TRACE(a, b, l, 0);
     ItemRegs<BS, GS> R;
-    item_load<BS, GS>(R, a.layer[l].sq, a.layer[l].ss, IS, J, wv, lane);  // routing-independent: before the wait
-    const float inv = chain_layer_input(a, S, l, base + l + 1, false, false, err);
+    item_load<BS, GS>(R, LP[l].sq, LP[l].ss, IS, J, wv, lane);  // routing-independent: before the wait
+    const float inv = chain_layer_input(a, LP, S, l, base + l + 1, false, false, err);
     MOE_TRACE(a, b, l, 2);
     item_planes<BS, GS>(S.z, inv, S.item);
     MOE_TRACE(a, b, l, 13);
-    item_compute<BS, GS, true>(R, 1.0f, a.part + (size_t)b * H, S.item);
+    item_compute<BS, GS>(R, S.item);
     MOE_TRACE(a, b, l, 4);
-    chain_item_done(a, b, base + l + 1);
+    chain_item_store(a, S.item, S.item.hs, b, base + l + 1);
     MOE_TRACE(a, b, l, 5);
   }
 }
 
-__device__ void chain_reducer(const ChainArgs& a, ReducerSide& S, int rid, uint32_t base, uint32_t* err) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+__device__ void chain_reducer(const ChainArgs& a, const LayerPtrs* LP, ReducerSide& S, int rid, uint32_t base, uint32_t* err) {
+  const int tid = threadIdx.x;
   const int r0 = rid * RED_ROWS;
-  const int e = tid >> 3, sub = tid & 7;   // partial logits: expert e, rows sub + 8m
-  constexpr int NF4 = N_ITEMS * RED_ROWS / 4;          // 2240 float4 of partials per stage
-  constexpr int F4_PER_T = (NF4 + 511) / 512;          // 5
-  const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(a.part, N_ITEMS * H * 4);
+  const int e = tid >> 3, sub = tid & 7;      // partial logits: expert e, rows sub + 8m
+  // summation: thread t < 448 owns word c = t % 14 (rows 3c..3c+2 of this
+  // reducer) of items ig + 32j, ig = t / 14, j = 0..6
+  constexpr int NG = N_ITEMS / 7;             // 32 item groups
+  const bool summer = tid < NG * PART_U4;
+  const int c = tid % PART_U4, ig = tid / PART_U4;
+  const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(a.ipart, N_ITEMS * ITEM_U4 * 16);
+  const __amdgpu_buffer_rsrc_t rr = coherent_rsrc(a.rec, N_RED * REC_U4 * 16);
+  uint32_t off[7];
+  bool valid[7];
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const int it = summer ? ig + NG * j : NG * j;
+    valid[j] = summer;
+    off[j] = (((uint32_t)it * N_RED + rid) * PART_U4 + (summer ? c : 0)) * 16;
+  }
   for (int s = 0; s <= a.n_layers; ++s) {
     float wr[5];
     if (s < a.n_layers) {
 #pragma unroll
-      for (int m = 0; m < 5; ++m) wr[m] = a.layer[s].wr[(size_t)e * H + r0 + sub + 8 * m];
+      for (int m = 0; m < 5; ++m) wr[m] = LP[s].wr[(size_t)e * H + r0 + sub + 8 * m];
     }
     MOE_TRACE(a, N_ITEMS + rid, s, 0);
     if (s == 0) {
       if (tid < RED_ROWS) {
         const int k = r0 + tid;
-        S.hrow[tid] = a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x)[k]) : ((const float*)a.x)[k];
+        const float hv = a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x)[k]) : ((const float*)a.x)[k];
+        S.hrow[tid] = hv;
+        S.rec[tid] = hv;
       }
     } else {
-      if (wv == 0) wait_flags(a.item_flag, N_ITEMS, base + s, err);
-      __syncthreads();
+      u32x4 v[7];
+      long spins = 0;
+      wait_first(rp, off[0], base + s, spins);
+      load_tagged<7>(rp, off, valid, v, base + s, spins, err);
       MOE_TRACE(a, N_ITEMS + rid, s, 1);
-      // all partials of this reducer's rows, 16 bytes per load, all loads in flight together
-      u32x4 v[F4_PER_T];
+      if (summer) {
+        float acc[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < F4_PER_T; ++m) {
-        const int f = tid + 512 * m;
-        if (f < NF4) {
-          const int it = f / (RED_ROWS / 4), qd = f % (RED_ROWS / 4);
-          v[m] = load16_coherent(rp, ((uint32_t)it * H + r0 + 4 * qd) * 4);
-        }
-      }
+        for (int j = 0; j < 7; ++j)
 #pragma unroll
-      for (int m = 0; m < F4_PER_T; ++m) {
-        const int f = tid + 512 * m;
-        if (f < NF4) *(float4*)&S.parts[4 * f] = as_float4(v[m]);
-      }
-      __syncthreads();
-      if (tid < 12 * RED_ROWS) {
-        const int rr = tid % RED_ROWS, ig = tid / RED_ROWS;
-        float acc = 0.f;
+          for (int i = 0; i < 3; ++i) acc[i] += __uint_as_float(v[j][i]);
 #pragma unroll
-        for (int j = 0; j < (N_ITEMS + 11) / 12; ++j) {
-          const int it = ig + 12 * j;
-          if (it < N_ITEMS) acc += S.parts[it * RED_ROWS + rr];
-        }
-        S.red[ig][rr] = acc;
+        for (int i = 0; i < 3; ++i) S.red[ig][3 * c + i] = acc[i];
       }
       __syncthreads();
       if (tid < RED_ROWS) {
         float vv = 0.f;
 #pragma unroll
-        for (int g = 0; g < 12; ++g) vv += S.red[g][tid];
-        S.hrow[tid] = (a.accumulate ? S.hrow[tid] : 0.f) + vv;
+        for (int g = 0; g < NG; ++g) vv += S.red[g][tid];
+        const float hv = (a.accumulate ? S.hrow[tid] : 0.f) + vv;
+        S.hrow[tid] = hv;
+        S.rec[tid] = hv;
       }
     }
     __syncthreads();
-    if (tid < RED_ROWS) store_coherent(a.y + r0 + tid, S.hrow[tid]);
-    if (s < a.n_layers) {
-      float part = 0.f;
+    if (s == a.n_layers) {
+      if (tid < RED_ROWS) a.y[r0 + tid] = S.hrow[tid];
+    } else {
+      float part = 0.f, sq = 0.f;
 #pragma unroll
-      for (int m = 0; m < 5; ++m) part += wr[m] * S.hrow[sub + 8 * m];
-      part += __shfl_xor(part, 1);
-      part += __shfl_xor(part, 2);
-      part += __shfl_xor(part, 4);
-      if (sub == 0) store_coherent(a.q + rid * Q_STRIDE + e, part);
-      if (wv == 0) {
-        if (lane < RED_ROWS) S.sq[lane] = S.hrow[lane] * S.hrow[lane];
-        __builtin_amdgcn_wave_barrier();
-        if (lane == 0) {
-          float ss = 0.f;
-#pragma unroll
-          for (int k = 0; k < RED_ROWS; k += 4) {
-            const float4 v = *(const float4*)&S.sq[k];
-            ss += (v.x + v.y) + (v.z + v.w);
-          }
-          store_coherent(a.q + rid * Q_STRIDE + 64, ss);
-        }
+      for (int m = 0; m < 5; ++m) {
+        const float hv = S.hrow[sub + 8 * m];
+        part += wr[m] * hv;
+        sq += hv * hv;
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      part = group_sum<8>(part);
+      sq = group_sum<8>(sq);
+      if (sub == 0) S.rec[RED_ROWS + e] = part;
+      if (tid == 0) S.rec[REC_VALS - 1] = sq;
       __syncthreads();
-      if (tid == 0) store_coherent_u32(a.red_flag + rid, base + s + 1);
+      if (tid < REC_U4) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const int vi = 3 * tid + i;
+          w[i] = vi < REC_VALS ? __float_as_uint(S.rec[vi]) : 0u;
+        }
+        w[3] = base + s + 1;
+        store16_coherent(rr, ((uint32_t)rid * REC_U4 + tid) * 16, w);
+      }
     }
     MOE_TRACE(a, N_ITEMS + rid, s, 5);
   }
@@ -830,23 +957,30 @@ __device__ void chain_reducer(const ChainArgs& a, ReducerSide& S, int rid, uint3
 template <int BR, int BS>
 __global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
   __shared__ __attribute__((aligned(16))) ChainLds S;
+  // the per-layer pointer table, read once from the kernel arguments
+  __shared__ __attribute__((aligned(16))) LayerPtrs LP[MAX_LAYERS];
+  static_assert(sizeof(LayerPtrs) % 8 == 0, "pointer table copy");
+  constexpr int LPW = sizeof(LayerPtrs) / 8;
+  if ((int)threadIdx.x < a.n_layers * LPW)
+    ((uint64_t*)LP)[threadIdx.x] = ((const uint64_t*)a.layer)[threadIdx.x];
+  __syncthreads();
   const int b = blockIdx.x;
   const uint32_t base = load_coherent_u32(a.hdr) * 64u;
   uint32_t* err = a.hdr + 2;
   if (b < R_ITEMS) {
     switch (a.rgroup) {
-      case 32: chain_routed<BR, 32>(a, S.it, b, base, err); break;
-      case 64: chain_routed<BR, 64>(a, S.it, b, base, err); break;
-      default: chain_routed<BR, 128>(a, S.it, b, base, err); break;
+      case 32: chain_routed<BR, 32>(a, LP, S.it, b, base, err); break;
+      case 64: chain_routed<BR, 64>(a, LP, S.it, b, base, err); break;
+      default: chain_routed<BR, 128>(a, LP, S.it, b, base, err); break;
     }
   } else if (b < N_ITEMS) {
     switch (a.sgroup) {
-      case 32: chain_shared<BS, 32>(a, S.it, b, base, err); break;
-      case 64: chain_shared<BS, 64>(a, S.it, b, base, err); break;
-      default: chain_shared<BS, 128>(a, S.it, b, base, err); break;
+      case 32: chain_shared<BS, 32>(a, LP, S.it, b, base, err); break;
+      case 64: chain_shared<BS, 64>(a, LP, S.it, b, base, err); break;
+      default: chain_shared<BS, 128>(a, LP, S.it, b, base, err); break;
     }
   } else {
-    chain_reducer(a, S.rd, b - N_ITEMS, base, err);
+    chain_reducer(a, LP, S.rd, b - N_ITEMS, base, err);
   }
   // the last workgroup to finish advances the call sequence
   __builtin_amdgcn_s_waitcnt(0);
