@@ -391,6 +391,32 @@ __device__ __forceinline__ float planes_value(const int* P) {
 // 512 threads (8 waves) runs one item; all of the item's weight bytes are
 // requested up front (ItemRegs) so that they are in flight together.
 // ---------------------------------------------------------------------------
+// 16-byte device-scope (L2-coherent, sc1) loads through a bounds-checked buffer
+// descriptor: used for everything one workgroup of the persistent kernel reads
+// that another one wrote during the same launch.
+typedef unsigned int u32x4 __attribute__((vector_size(16)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;
+__device__ __forceinline__ u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ float4 as_float4(u32x4 v) {
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
+// Plain (cached) loads through a buffer descriptor of `bytes` bytes: offsets
+// at or beyond the end return zeros without touching memory, which lets a
+// wave issue a fixed number of loads with no branches around them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 wload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int BITS, int G>
 struct ItemRegs {
   static constexpr int KB = kb_cols(BITS), NKB = H / KB, CPT = KB / 32;
@@ -403,42 +429,82 @@ struct ItemRegs {
   float dns[D_TPW][RS];
 };
 
+// A pointer or index the whole wave agrees on, as a scalar value (lets buffer
+// descriptors live in scalar registers).
+template <typename T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 template <int BITS, int G>
 __device__ __forceinline__ void item_load(ItemRegs<BITS, G>& R, const uint8_t* eq, const float* es, int inter,
                                           int J, int wv, int lane) {
   using IR = ItemRegs<BITS, G>;
+  eq = wave_uniform(eq);
+  es = wave_uniform(es);
+  J = wave_uniform(J);
+  wv = wave_uniform(wv);
   constexpr int NG = H / G;
   const size_t mbytes = matrix_bytes(BITS, inter, H);
   const size_t mscales = (size_t)inter * NG;
   const int r = lane & 15;
   const int i = wv >> 1, ntile = 2 * J + (i & 1), mat = i >> 1, kb0 = (wv & 1) * IR::GU_TPW;
-#pragma unroll
-  for (int m = 0; m < IR::GU_TPW; ++m)
-    R.gu[m] = *(const uint4*)(eq + mat * mbytes + ((size_t)ntile * IR::NKB + kb0 + m) * TILE + lane * 16);
+  // Issue order = use order (loads return in order): the gate/up scales, the
+  // gate/up tiles, then the down scales and tiles, so that the first tiles can
+  // be multiplied while later ones are still in flight.  No branches: the
+  // down tiles past the end of the slab read as zeros (buffer range check).
   // gate/up scales are row-major [row][group]: this lane's row, this wave's K half
-  const float* gp = es + mat * mscales + (size_t)(16 * ntile + r) * NG + (wv & 1) * IR::NGW;
+  // (buffer loads throughout: a pending flat load would make the compiler wait
+  // for every outstanding load before the first use of any of them)
+  const __amdgpu_buffer_rsrc_t rgs =
+      weight_rsrc(es + mat * mscales + (size_t)(16 * ntile) * NG + (wv & 1) * IR::NGW, 16 * NG * 4);
+  const uint32_t go = (uint32_t)(r * NG) * 4;
   if (IR::NGW % 4 == 0) {
 #pragma unroll
-    for (int g = 0; g < IR::NGW; g += 4) *(float4*)&R.gsc[g] = *(const float4*)(gp + g);
+    for (int g = 0; g < IR::NGW; g += 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rgs, go + 4 * g, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) R.gsc[(g + t) % IR::NGW] = __uint_as_float(v[t]);
+    }
   } else if (IR::NGW % 2 == 0) {
 #pragma unroll
-    for (int g = 0; g < IR::NGW; g += 2) *(float2*)&R.gsc[g] = *(const float2*)(gp + g);
+    for (int g = 0; g < IR::NGW; g += 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rgs, go + 4 * g, 0, 0);
+      R.gsc[g] = __uint_as_float(v[0]);
+      R.gsc[(g + 1) % IR::NGW] = __uint_as_float(v[1]);
+    }
   } else {
 #pragma unroll
-    for (int g = 0; g < IR::NGW; ++g) R.gsc[g] = gp[g];
+    for (int g = 0; g < IR::NGW; ++g) R.gsc[g] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rgs, go + 4 * g, 0, 0));
   }
-  const uint8_t* dq = eq + 2 * mbytes;
-  const float* ds = es + 2 * mscales;
+  const __amdgpu_buffer_rsrc_t rg =
+      weight_rsrc(eq + mat * mbytes + ((size_t)ntile * IR::NKB + kb0) * TILE, IR::GU_TPW * TILE);
+#pragma unroll
+  for (int m = 0; m < IR::GU_TPW; ++m) R.gu[m] = wload16(rg, m * TILE + lane * 16);
   const int gd = (SLICE * J) / G;
+  const __amdgpu_buffer_rsrc_t rds =
+      weight_rsrc(es + 2 * mscales + (size_t)gd * IR::NRT * 16 * IR::RS, IR::NRT * 16 * IR::RS * 4);
+  const __amdgpu_buffer_rsrc_t rd = weight_rsrc(eq + 2 * mbytes + (size_t)J * IR::NRT * TILE, IR::NRT * TILE);
 #pragma unroll
   for (int m = 0; m < IR::D_TPW; ++m) {
-    const int rt = wv + 8 * m;
-    if (rt < IR::NRT) {
-      R.dn[m] = *(const uint4*)(dq + ((size_t)J * IR::NRT + rt) * TILE + lane * 16);
-      const float* sp = ds + (((size_t)gd * IR::NRT + rt) * 16 + r) * IR::RS;
-      if (IR::RS == 4) *(float4*)&R.dns[m][0] = *(const float4*)sp;
-      else *(float2*)&R.dns[m][0] = *(const float2*)sp;
+    const uint32_t rt = wv + 8 * m;
+    const uint32_t so = ((rt * 16 + r) * IR::RS) * 4;
+    if (IR::RS == 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rds, so, 0, 0);
+      R.dns[m][0] = __uint_as_float(v[0]);
+      R.dns[m][1 % IR::RS] = __uint_as_float(v[1]);
+      R.dns[m][2 % IR::RS] = __uint_as_float(v[2]);
+      R.dns[m][3 % IR::RS] = __uint_as_float(v[3]);
+    } else {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rds, so, 0, 0);
+      R.dns[m][0] = __uint_as_float(v[0]);
+      R.dns[m][1] = __uint_as_float(v[1]);
     }
+    R.dn[m] = wload16(rd, rt * TILE + lane * 16);
   }
 }
 
@@ -453,21 +519,6 @@ __device__ __forceinline__ uint32_t load_coherent_u32(const uint32_t* p) {
 }
 __device__ __forceinline__ void store_coherent_u32(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// 16-byte device-scope (L2-coherent, sc1) loads through a bounds-checked buffer
-// descriptor: used for everything one workgroup of the persistent kernel reads
-// that another one wrote during the same launch.
-typedef unsigned int u32x4 __attribute__((vector_size(16)));
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
-}
-constexpr int CPOL_SC1 = 16;
-__device__ __forceinline__ u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL_SC1);
-}
-__device__ __forceinline__ float4 as_float4(u32x4 v) {
-  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
 }
 
 struct ItemLds {
@@ -677,7 +728,8 @@ __device__ __forceinline__ void wait_first(__amdgpu_buffer_rsrc_t r, uint32_t of
 }
 
 // Load the tagged words at off[m] (where valid[m]) and poll until every one
-// carries `tag` (after wait_first this usually takes one round trip).  Wave-uniform exit; a wait that runs out sets the error word.
+// carries `tag` (after wait_first this usually takes one round trip).
+// Wave-uniform exit; a wait that runs out sets the error word.
 template <int N>
 __device__ __forceinline__ void load_tagged(__amdgpu_buffer_rsrc_t r, const uint32_t* off, const bool* valid,
                                             u32x4* v, uint32_t tag, long& spins, uint32_t* err) {
@@ -900,8 +952,7 @@ __device__ void chain_reducer(const ChainArgs& a, const LayerPtrs* LP, ReducerSi
       }
     } else {
       u32x4 v[7];
-      long spins = 0;
-      wait_first(rp, off[0], base + s, spins);
+      long spins = 0;   // each reducer polls its own data directly (nobody else reads it)
       load_tagged<7>(rp, off, valid, v, base + s, spins, err);
       MOE_TRACE(a, N_ITEMS + rid, s, 1);
       if (summer) {
