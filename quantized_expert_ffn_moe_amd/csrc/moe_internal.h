@@ -12,7 +12,7 @@ constexpr int TOPK = 6;      // experts picked per token
 constexpr int I = 896;       // routed expert intermediate
 constexpr int IS = 1792;     // fused shared expert intermediate
 constexpr int TILE = 1024;   // bytes of one packed 16-row tile
-constexpr int MT = 32;       // smallest token-row tile of the grouped GEMMs (64 for big batches)
+constexpr int MT = 32;       // token rows per tile of the grouped GEMMs
 constexpr int DECODE_MAX_T = 4;  // largest token count routed to the GEMV path by default
 constexpr int MAX_T = 8192;      // largest token count of one call
 constexpr int MOE_MAX_SLOTS = MAX_T * TOPK;
@@ -105,6 +105,7 @@ struct GroupedArgs {
   int shared;                           // 1: rows are tokens 0..T-1 of the shared expert
   const int32_t* tiles; const int32_t* ntiles; const int32_t* offsets; const int32_t* perm;
   int a_by_token;                       // routed A rows: 1 = token rows (gate/up), 0 = sorted rows (down)
+  int a_rows;                           // rows of the A matrix (bounds its buffer descriptor)
   QW w;
   float* out;                           // routed: [T*6][N] by sorted position; shared: [T][N]
 };
@@ -120,8 +121,8 @@ hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s);
 hipError_t launch_chain(const ChainArgs& a, hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_hist(const HistArgs& a, hipStream_t s);
-hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, int mtl, hipStream_t s);
-hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int mtl, hipStream_t s);
+hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps, hipStream_t s);
 

@@ -106,24 +106,22 @@ __device__ __forceinline__ float inv_rms(const float* red4, float eps) {
 
 // ---------------------------------------------------------------------------
 // Router: (optional RMSNorm) -> 64 logits -> softmax -> greedy top-6.
-// One workgroup of 256 threads per 16 tokens.  Pass 1 normalises the rows and
-// writes z; pass 2 accumulates the logits over K chunks staged in LDS (W_r
-// transposed so that a lane reads its expert's 4 consecutive k as one float4;
-// thread = (expert e = tid % 64, token group tid / 64 of 4 tokens)); the
-// selection ranks every expert against the others from LDS.  The softmax is
-// increasing in the logit, so the 6 largest logits (ties to the lower index)
-// are the 6 largest probabilities.
+// One workgroup of 256 threads per 4 tokens, so that even a few hundred tokens
+// spread over many compute units.  Pass 1 normalises the rows (the same
+// per-thread sums and reduction order as the standalone RMSNorm, so both give
+// bit-identical z) into LDS and to z; pass 2: 16 lanes per expert row read
+// W_r in coalesced float4 runs (the 327 KB matrix stays in L2) against z from
+// LDS and add up across the 16 lanes in a fixed order.  The selection
+// ranks every expert against the others: the softmax is increasing in the
+// logit, so the 6 largest logits (ties to the lower index) are the 6 largest
+// probabilities.
 // ---------------------------------------------------------------------------
-constexpr int RT_TB = 16;      // tokens per workgroup
-constexpr int RT_KC = 128;     // K chunk staged in LDS
+constexpr int RT_TB = 4;       // tokens per workgroup
 
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  __shared__ __attribute__((aligned(16))) float wt[RT_KC / 4][E][4];   // 32 KB
-  __shared__ __attribute__((aligned(16))) float zc[RT_TB][RT_KC];      // 8 KB
-  __shared__ float inv_s[RT_TB];
+  __shared__ __attribute__((aligned(16))) float zs[RT_TB][H];          // 20 KB
   __shared__ float red[RT_TB][4];
   __shared__ __attribute__((aligned(16))) float lg[RT_TB][E];
-  __shared__ float exs[RT_TB][E];
   const int t0 = blockIdx.x * RT_TB;
   const int nt = min(RT_TB, a.T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -131,102 +129,88 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     const size_t idx = (size_t)(t0 + t) * H + k;
     return a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x)[idx]) : ((const float*)a.x)[idx];
   };
-  // pass 1: 1/rms per token and the normalised rows (written once to z)
-  if (a.norm) {
-    for (int tt = 0; tt < nt; ++tt) {
-      float v[5];
+  // pass 1: rows into LDS; with the norm, 1/rms per token and z (also written out)
+  for (int tt = 0; tt < RT_TB; ++tt) {
+    float v[5];
 #pragma unroll
-      for (int i = 0; i < 5; ++i) v[i] = xval(tt, tid + 256 * i);
+    for (int i = 0; i < 5; ++i) v[i] = tt < nt ? xval(tt, tid + 256 * i) : 0.f;
+    if (a.norm) {
       const float ss = wave_sum(thread_sumsq(v));
       if (lane == 0) red[tt][wv] = ss;
     }
-    __syncthreads();
-    if (tid < nt) inv_s[tid] = inv_rms(red[tid], a.eps);
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 5; ++i) zs[tt][tid + 256 * i] = v[i];
+  }
+  __syncthreads();
+  if (a.norm) {
     for (int tt = 0; tt < nt; ++tt) {
-      const float inv = inv_s[tt];
+      const float inv = inv_rms(red[tt], a.eps);
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
         const int k = tid + 256 * i;
-        const float z = xval(tt, k) * inv;
-        if (a.norm_bf16) ((uint16_t*)a.z)[(size_t)(t0 + tt) * H + k] = (uint16_t)(__float_as_uint(bf16_rne(z)) >> 16);
-        else ((float*)a.z)[(size_t)(t0 + tt) * H + k] = z;
+        float z = zs[tt][k] * inv;
+        if (a.norm_bf16) {
+          z = bf16_rne(z);
+          ((uint16_t*)a.z)[(size_t)(t0 + tt) * H + k] = (uint16_t)(__float_as_uint(z) >> 16);
+        } else {
+          ((float*)a.z)[(size_t)(t0 + tt) * H + k] = z;
+        }
+        zs[tt][k] = z;
       }
     }
-  }
-  // pass 2: logits
-  const int e = tid & 63, tg = tid >> 6;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < H; k0 += RT_KC) {
     __syncthreads();
-    for (int i = tid; i < E * RT_KC / 4; i += 256) {            // W_r[e'][k0 + 4c .. +3] -> wt[c][e']
-      const int ee = i / (RT_KC / 4), c = i % (RT_KC / 4);
-      *(float4*)&wt[c][ee][0] = *(const float4*)(a.wr + (size_t)ee * H + k0 + 4 * c);
-    }
-    for (int i = tid; i < RT_TB * RT_KC; i += 256) {
-      const int tt = i / RT_KC, kk = i % RT_KC;
-      float z = 0.f;
-      if (tt < nt) {
-        z = xval(tt, k0 + kk);
-        if (a.norm) {
-          z *= inv_s[tt];
-          if (a.norm_bf16) z = bf16_rne(z);
+  }
+  // pass 2: wave w owns experts 16w..16w+15, four at a time; lane = (expert
+  // eg = lane / 16 of the four, column group kk = lane % 16), so one wave load
+  // reads four 256-byte runs of W_r rows; the 16 column groups of each row add
+  // up with DPP in a fixed order.
+  {
+    const int eg = lane >> 4, kk = lane & 15;
+#pragma unroll 1
+    for (int it = 0; it < 4; ++it) {
+      const int e = 16 * wv + 4 * it + eg;
+      const float* wr = a.wr + (size_t)e * H;
+      float acc[RT_TB] = {0.f, 0.f, 0.f, 0.f};
+      float4 w[H / 64];   // the whole row slice in flight at once
+#pragma unroll
+      for (int j = 0; j < H / 64; ++j) w[j] = *(const float4*)(wr + 4 * (16 * j + kk));
+#pragma unroll
+      for (int j = 0; j < H / 64; ++j) {
+        const int k = 4 * (16 * j + kk);
+        const float4 w4 = w[j];
+#pragma unroll
+        for (int t = 0; t < RT_TB; ++t) {
+          const float4 z4 = *(const float4*)&zs[t][k];
+          acc[t] += w4.x * z4.x + w4.y * z4.y + w4.z * z4.z + w4.w * z4.w;
         }
       }
-      zc[tt][kk] = z;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < RT_KC / 4; ++c) {
-      const float4 w4 = *(const float4*)&wt[c][e][0];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 z4 = *(const float4*)&zc[4 * tg + j][4 * c];
-        acc[j] += w4.x * z4.x + w4.y * z4.y + w4.z * z4.z + w4.w * z4.w;
+      for (int t = 0; t < RT_TB; ++t) {
+        const float v = group_sum<16>(acc[t]);
+        if (kk == 0) lg[t][e] = v + (a.bias ? a.bias[e] : 0.f);
       }
     }
   }
-  const float b = a.bias ? a.bias[e] : 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) lg[4 * tg + j][e] = acc[j] + b;
   __syncthreads();
-  // selection: thread = (token tid / 16, experts tid % 16 + 16 i)
-  const int tt = tid >> 4, e0 = tid & 15;
-  if (tt < nt) {
-    float le[4];
-    int rank[4] = {0, 0, 0, 0};
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) le[i] = lg[tt][e0 + 16 * i];
-#pragma unroll
-    for (int k = 0; k < E; k += 4) {
-      const float4 v = *(const float4*)&lg[tt][k];
-      const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        mx = fmaxf(mx, vv[u]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ei = e0 + 16 * i;
-          rank[i] += (vv[u] > le[i] || (vv[u] == le[i] && k + u < ei)) ? 1 : 0;
-        }
+  // selection: wave = token, lane = expert
+  {
+    const int tt = wv, e = lane;
+    if (tt < nt) {
+      const float le = lg[tt][e];
+      const float mx = wave_max(le);
+      const float ex = expf(le - mx);
+      const float sm = wave_sum(ex);
+      int rank = 0;
+#pragma unroll 4
+      for (int k = 0; k < E; ++k) {
+        const float lk = lg[tt][k];
+        rank += (lk > le || (lk == le && k < e)) ? 1 : 0;
+      }
+      if (rank < TOPK) {
+        a.ids[(size_t)(t0 + tt) * TOPK + rank] = e;
+        a.w[(size_t)(t0 + tt) * TOPK + rank] = ex / sm;
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) exs[tt][e0 + 16 * i] = expf(le[i] - mx);
-    __builtin_amdgcn_wave_barrier();
-    float sm = 0.f;
-#pragma unroll
-    for (int k = 0; k < E; k += 4) {
-      const float4 v = *(const float4*)&exs[tt][k];
-      sm += (v.x + v.y) + (v.z + v.w);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (rank[i] < TOPK) {
-        a.ids[(size_t)(t0 + tt) * TOPK + rank[i]] = e0 + 16 * i;
-        a.w[(size_t)(t0 + tt) * TOPK + rank[i]] = exs[tt][e0 + 16 * i] / sm;
-      }
   }
 }
 
@@ -1067,24 +1051,30 @@ __global__ __launch_bounds__(1024) void hist_kernel(HistArgs a) {
   const int chunk = ((N + 15) / 16 + 63) / 64 * 64;
   const int c0 = wv * chunk, c1 = min(N, c0 + chunk);
   for (int i = tid; i < N; i += 1024) sid[i] = (uint8_t)a.ids[i];
-  for (int i = tid; i < 16 * E; i += 1024) (&cntw[0][0])[i] = 0;
+  (&cntw[0][0])[tid] = 0;   // 16 x 64 = 1024 entries
   __syncthreads();
   for (int i = c0 + lane; i < c1; i += 64) atomicAdd(&cntw[wv][sid[i]], 1);
   __syncthreads();
-  if (tid < E) {
+  {   // thread (w, e): slots of expert e in the chunks of waves before w
+    const int w = wv, e = lane;
     int run = 0;
-    for (int w = 0; w < 16; ++w) { basew[w][tid] = run; run += cntw[w][tid]; }
-    cnt[tid] = run;
+    for (int u = 0; u < w; ++u) run += cntw[u][e];
+    basew[w][e] = run;
+    if (w == 15) cnt[e] = run + cntw[15][e];
   }
   __syncthreads();
-  if (tid == 0) {
-    off[0] = 0; toff[0] = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e + 1] = off[e] + cnt[e];
-      toff[e + 1] = toff[e] + (cnt[e] + a.mt - 1) / a.mt;
+  if (wv == 0) {   // exclusive scans over the experts (wave 0, lane = expert)
+    const int c = cnt[lane], tl = (c + a.mt - 1) / a.mt;
+    int inc = c, tinc = tl;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {   // Hillis-Steele in registers via lane shuffles
+      const int o = __shfl_up(inc, d), to = __shfl_up(tinc, d);
+      if (lane >= d) { inc += o; tinc += to; }
     }
-    *a.ntiles = toff[E];
-    a.offsets[E] = off[E];
+    off[lane + 1] = inc;
+    toff[lane + 1] = tinc;
+    if (lane == 0) { off[0] = 0; toff[0] = 0; }
+    if (lane == 63) { *a.ntiles = tinc; a.offsets[E] = inc; }
   }
   __syncthreads();
   if (tid < E) {
@@ -1094,30 +1084,34 @@ __global__ __launch_bounds__(1024) void hist_kernel(HistArgs a) {
       a.tiles[2 * (toff[tid] + j)] = tid;
       a.tiles[2 * (toff[tid] + j) + 1] = j * a.mt;
     }
-    for (int w = 0; w < 16; ++w) basew[w][tid] += off[tid];
   }
+  basew[wv][lane] += off[lane];
   __syncthreads();
+  // stable placement, 64 slots at a time per wave: the lanes holding the same
+  // expert are found with one ballot per bit of the 6-bit expert id; a lane's
+  // position is its expert's running base plus the number of such lanes below
+  // it, and the lowest of them advances the base.
   const uint64_t below = (1ull << lane) - 1ull;
   for (int g = c0; g < c1; g += 64) {
     const int i = g + lane;
     const bool valid = i < c1;
-    const int my_e = valid ? sid[i] : -1;
-    uint64_t todo = __ballot(valid);
-    while (todo) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int e0 = __shfl(my_e, leader);
-      const uint64_t m = __ballot(my_e == e0);
-      const int base = basew[wv][e0];
-      if (my_e == e0) {
-        const int p = base + __popcll(m & below);
-        a.perm[p] = i;
-        a.pos_of[i] = p;
-      }
-      __builtin_amdgcn_wave_barrier();
-      if (lane == leader) basew[wv][e0] = base + __popcll(m);
-      __builtin_amdgcn_wave_barrier();
-      todo &= ~m;
+    const int my_e = valid ? sid[i] : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bt = 0; bt < 6; ++bt) {
+      const uint64_t ones = __ballot(valid && ((my_e >> bt) & 1));
+      same &= ((my_e >> bt) & 1) ? ones : ~ones;
     }
+    const int base = basew[wv][my_e];
+    const int rank = __popcll(same & below);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      const int p = base + rank;
+      a.perm[p] = i;
+      a.pos_of[i] = p;
+      if (rank == 0) basew[wv][my_e] = base + __popcll(same);
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -1164,41 +1158,39 @@ template <int BITS> __device__ __forceinline__ int perm_k(int p) {
 constexpr int KS = 128;             // K staged in LDS per step
 constexpr int LDS_ROW = KS + 8;     // f16 per LDS row (16-byte pad against bank conflicts)
 
-// A-operand staging, split into a global fetch (into registers, issued one
-// stage ahead) and an LDS store (f16 hi plane, and lo plane when SPLIT,
+// A-operand staging, split into a global fetch (into registers, issued two
+// stages ahead) and an LDS store (f16 hi plane, and lo plane when SPLIT,
 // permuted within each 8-group into the B operand order).  Thread tid owns the
-// 8-element segments tid + 256 j: row = seg / 16, k = 8 (seg % 16).
+// 8-element segments tid + 256 j: row = seg / 16, k = 8 (seg % 16).  The loads
+// go through a buffer descriptor: padding rows (arow < 0) and stages past the
+// end read zeros without a branch, so the compiler can count the loads in
+// flight precisely.
 template <int MTL, bool F32>
-struct AFetch {
+struct AStage {
   static constexpr int NSEG = MTL / 16;
   uint4 raw[NSEG][F32 ? 2 : 1];
 };
 
 template <int MTL, bool F32>
-__device__ __forceinline__ void fetch_a(AFetch<MTL, F32>& A, const void* src_base, const int* arow, int K, int k0) {
+__device__ __forceinline__ void fetch_a(AStage<MTL, F32>& A, __amdgpu_buffer_rsrc_t ra, const int* arow, int K,
+                                        int k0, bool live) {
   const int tid = threadIdx.x;
+  constexpr uint32_t ELT = F32 ? 4 : 2;
 #pragma unroll
-  for (int j = 0; j < AFetch<MTL, F32>::NSEG; ++j) {
+  for (int j = 0; j < AStage<MTL, F32>::NSEG; ++j) {
     const int seg = tid + 256 * j, row = seg >> 4, kk = 8 * (seg & 15);
     const int src = arow[row];
-    if (src < 0) {
-      A.raw[j][0] = make_uint4(0, 0, 0, 0);
-      if (F32) A.raw[j][F32 ? 1 : 0] = make_uint4(0, 0, 0, 0);
-    } else if (F32) {
-      const uint4* p = (const uint4*)((const float*)src_base + (size_t)src * K + k0 + kk);
-      A.raw[j][0] = p[0];
-      A.raw[j][F32 ? 1 : 0] = p[1];
-    } else {
-      A.raw[j][0] = *(const uint4*)((const uint16_t*)src_base + (size_t)src * K + k0 + kk);
-    }
+    const uint32_t off = (live && src >= 0) ? ((uint32_t)src * K + k0 + kk) * ELT : 0x80000000u;
+    A.raw[j][0] = wload16(ra, off);
+    if (F32) A.raw[j][F32 ? 1 : 0] = wload16(ra, off + 16);
   }
 }
 
 template <int BITS, int MTL, bool F32, bool SPLIT>
-__device__ __forceinline__ void store_a(_Float16* lds, const AFetch<MTL, F32>& A) {
+__device__ __forceinline__ void store_a(_Float16* lds, const AStage<MTL, F32>& A) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < AFetch<MTL, F32>::NSEG; ++j) {
+  for (int j = 0; j < AStage<MTL, F32>::NSEG; ++j) {
     const int seg = tid + 256 * j, row = seg >> 4, kk = 8 * (seg & 15);
     float v[8];
     if (F32) {
@@ -1227,6 +1219,10 @@ __device__ __forceinline__ void store_a(_Float16* lds, const AFetch<MTL, F32>& A
   }
 }
 
+__device__ __forceinline__ float wload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 struct TileInfo { int valid, nrows, pbase, row0, e; };
 
 __device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile, int mtl) {
@@ -1249,86 +1245,99 @@ __device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile, in
   return ti;
 }
 
-// Gate/up: a workgroup owns one MTL-row tile of one expert and 128
+// Gate/up: a workgroup owns one MT-row tile of one expert and 128
 // intermediate columns; wave w computes gate and up for columns 32w..32w+31
 // of them (n-subtiles 8cb + 2w, 8cb + 2w + 1 of both matrices) and writes
-// h = SiLU(gate) * up.  A and B of the next K stage are fetched into registers
-// while the current stage computes.
-template <int BITS, bool SPLIT, int MTL>
+// h = SiLU(gate) * up.  Software pipeline over K stages of 128: the packed B
+// tiles and their group scales are fetched D stages ahead into a register
+// ring, A two stages ahead into registers and one stage ahead into a double
+// buffer in LDS, so that the memory latency hides behind the MFMA work.
+template <int BITS, bool SPLIT, int G>
 __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
-  constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB;   // uint4 per B tile per stage
-  constexpr int NSTAGE = H / KS, MS = MTL / 16;
+  constexpr int MTL = MT;
+  constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MTL / 16;
+  constexpr int CPG = G / 32, GPS = KS / G, NG = H / G;
+  constexpr int D = BITS == 4 ? 3 : 2;      // B stages in flight
   constexpr bool F32 = SPLIT;
+  constexpr int APL = SPLIT ? 2 : 1;
   const int inter = a.w.inter, ncb = inter / 128;
   const int tile = blockIdx.x / ncb, cb = blockIdx.x % ncb;
   const TileInfo ti = tile_info(a, tile, MTL);
   if (!ti.valid) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q4 = lane >> 4;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[(SPLIT ? 2 : 1) * MTL * LDS_ROW];
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
+            q4 = lane >> 4;
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2][APL * MTL * LDS_ROW];
   __shared__ int arow[MTL];
   if (tid < MTL) {
     int src = -1;
     if (tid < ti.nrows) src = a.shared ? ti.row0 + tid : a.perm[ti.pbase + tid] / TOPK;
     arow[tid] = src;
   }
-  const uint8_t* eq = a.w.q + (size_t)ti.e * a.w.e_bytes;
-  const float* es = a.w.s + (size_t)ti.e * a.w.e_scales;
-  const size_t mbytes = matrix_bytes(BITS, inter, H);
-  const int ng = H / a.w.group, cpg = a.w.group / 32;
-  const size_t mscales = (size_t)inter * ng;
-  const void* asrc = F32 ? (const void*)a.af : (const void*)a.ab;
-  // B tiles of this wave: i = 0,1 gate n-subtiles, 2,3 up n-subtiles
-  auto btile = [&](int i, int kb) -> const uint4* {
+  const int e = wave_uniform(ti.e);
+  const uint8_t* eq = a.w.q + (size_t)e * a.w.e_bytes;
+  const float* es = a.w.s + (size_t)e * a.w.e_scales;
+  const size_t mbytes = matrix_bytes(BITS, inter, H), mscales = (size_t)inter * NG;
+  // B tiles of this wave: i = 0,1 gate n-subtiles, 2,3 up n-subtiles; each
+  // descriptor spans one n-tile's row of K tiles (later stages read zeros)
+  __amdgpu_buffer_rsrc_t rb[4], rs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
     const int nt = 8 * cb + 2 * wv + (i & 1);
-    return (const uint4*)(eq + (i >> 1) * mbytes + ((size_t)nt * NKB + kb) * TILE + lane * 16);
-  };
+    rb[i] = weight_rsrc(eq + (i >> 1) * mbytes + (size_t)nt * NKB * TILE, NKB * TILE);
+    rs[i] = weight_rsrc(es + (i >> 1) * mscales + (size_t)16 * nt * NG, 16 * NG * 4);
+  }
+  const __amdgpu_buffer_rsrc_t ra =
+      weight_rsrc(F32 ? (const void*)a.af : (const void*)a.ab, (uint32_t)a.a_rows * H * (F32 ? 4 : 2));
 
+  uint4 bq[D][4][NB];
+  float sq[D][4][GPS];
+  auto load_b = [&](uint4 (&bd)[4][NB], float (&sd)[4][GPS], int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int g = 0; g < GPS; ++g) sd[i][g] = wload4(rs[i], (uint32_t)(r * NG + st * GPS + g) * 4);
+#pragma unroll
+      for (int h = 0; h < NB; ++h) bd[i][h] = wload16(rb[i], (uint32_t)(st * NB + h) * TILE + lane * 16);
+    }
+  };
   float4v acc[4][MS], ctmp[4][MS];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) { acc[i][ms] = float4v{0, 0, 0, 0}; ctmp[i][ms] = float4v{0, 0, 0, 0}; }
-  __syncthreads();
+  __syncthreads();   // arow
 
-  AFetch<MTL, F32> An;
-  uint4 bn[4][NB], bc[4][NB];
-  fetch_a<MTL, F32>(An, asrc, arow, H, 0);
+  // Fully unrolled stage loop: every ring slot is a fixed register set, so no
+  // value is copied while its load is still in flight.
+  AStage<MTL, F32> A[3];   // A(s) lives in slot s % 3 until it is stored to LDS
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int s0 = 0; s0 < 3; ++s0) fetch_a<MTL, F32>(A[s0], ra, arow, H, s0 * KS, s0 < NSTAGE);
 #pragma unroll
-    for (int h = 0; h < NB; ++h) bn[i][h] = *btile(i, h);
+  for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
+  store_a<BITS, MTL, F32, SPLIT>(lds[0], A[0]);
 
+#pragma unroll
   for (int st = 0; st < NSTAGE; ++st) {
-    __syncthreads();
-    store_a<BITS, MTL, F32, SPLIT>(lds, An);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int h = 0; h < NB; ++h) bc[i][h] = bn[i][h];
-    if (st + 1 < NSTAGE) {
-      fetch_a<MTL, F32>(An, asrc, arow, H, (st + 1) * KS);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < NB; ++h) bn[i][h] = *btile(i, (st + 1) * NB + h);
-    }
-    __syncthreads();
+    __syncthreads();   // lds[st & 1] holds A(st); lds[(st + 1) & 1] is free
+    if (st + 1 < NSTAGE) store_a<BITS, MTL, F32, SPLIT>(lds[(st + 1) & 1], A[(st + 1) % 3]);
+    if (st + 3 < NSTAGE) fetch_a<MTL, F32>(A[st % 3], ra, arow, H, (st + 3) * KS, true);
+    const _Float16* la = lds[st & 1];
+    const int sl = st % D;
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
-      const int gc = st * (KS / 32) + c;
-      const bool first = (gc % cpg) == 0, last = (gc % cpg) == cpg - 1;
+      const bool first = (c % CPG) == 0, last = (c % CPG) == CPG - 1;
       half8 bfr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (BITS == 4) bfr[i] = unpack_int4(word_of(bc[i][0], c));
-        else bfr[i] = unpack_int8(word_of(bc[i][c >> 1], 2 * (c & 1)), word_of(bc[i][c >> 1], 2 * (c & 1) + 1));
+        if (BITS == 4) bfr[i] = unpack_int4(word_of(bq[sl][i][0], c));
+        else bfr[i] = unpack_int8(word_of(bq[sl][i][c >> 1], 2 * (c & 1)), word_of(bq[sl][i][c >> 1], 2 * (c & 1) + 1));
       }
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) {
         const int lrow = ms * 16 + r, lcol = 32 * c + 8 * q4;
-        const half8 ahi = *(const half8*)(lds + lrow * LDS_ROW + lcol);
+        const half8 ahi = *(const half8*)(la + lrow * LDS_ROW + lcol);
         half8 alo;
-        if (SPLIT) alo = *(const half8*)(lds + MTL * LDS_ROW + lrow * LDS_ROW + lcol);
+        if (SPLIT) alo = *(const half8*)(la + MTL * LDS_ROW + lrow * LDS_ROW + lcol);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[i][ms];
@@ -1338,16 +1347,15 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
         }
       }
       if (last) {
-        const int grp = gc / cpg;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int nt = 8 * cb + 2 * wv + (i & 1);
-          const float sv = es[(i >> 1) * mscales + (size_t)(16 * nt + r) * ng + grp];
+          const float sv = sq[sl][i][c / CPG];
 #pragma unroll
           for (int ms = 0; ms < MS; ++ms) acc[i][ms] += sv * ctmp[i][ms];
         }
       }
     }
+    if (st + D < NSTAGE) load_b(bq[sl], sq[sl], st + D);   // the slot just used takes stage st + D
   }
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
@@ -1363,68 +1371,89 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
     }
 }
 
-// Down: a workgroup owns one MTL-row tile of A (h, fp32 split hi/lo) and four
+// Down: a workgroup owns one MT-row tile of A (h, fp32 split hi/lo) and four
 // packed down tiles' worth of output rows: wave w covers row tile 4cb + w,
 // i.e. 64 (int4) or 32 (int8) output columns, one 16-column MFMA n-subtile
 // per 16 rows.  Each 16-byte lane load of a down tile feeds every n-subtile of
-// the row tile for one 32-wide K chunk.  Next-stage A and B are fetched ahead.
-template <int BITS, int MTL>
+// the row tile for one 32-wide K chunk.  Same software pipeline as gate/up.
+template <int BITS, int G, int INTER>
 __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
+  constexpr int MTL = MT;
   constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4, MS = MTL / 16;
-  const int inter = a.w.inter, nstage = inter / KS;
+  constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS;
+  constexpr int D = 3;
+  const int inter = INTER;
   const int tile = blockIdx.x / NCB, cb = blockIdx.x % NCB;
   const TileInfo ti = tile_info(a, tile, MTL);
   if (!ti.valid) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q4 = lane >> 4;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2 * MTL * LDS_ROW];
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
+            q4 = lane >> 4;
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2][2 * MTL * LDS_ROW];
   __shared__ int arow[MTL];
   if (tid < MTL) arow[tid] = tid < ti.nrows ? (a.shared ? ti.row0 + tid : ti.pbase + tid) : -1;
+  const int e = wave_uniform(ti.e);
   const size_t mbytes = matrix_bytes(BITS, inter, H);
-  const uint8_t* dq = a.w.q + (size_t)ti.e * a.w.e_bytes + 2 * mbytes;
-  const int cpg = a.w.group / 32;
-  const float* ds = a.w.s + (size_t)ti.e * a.w.e_scales + 2 * (size_t)inter * (H / a.w.group);
+  const int ngk = inter / G;
   const int rt = 4 * cb + wv;
+  const __amdgpu_buffer_rsrc_t rb = weight_rsrc(a.w.q + (size_t)e * a.w.e_bytes + 2 * mbytes, (uint32_t)mbytes);
+  const __amdgpu_buffer_rsrc_t rs =
+      weight_rsrc(a.w.s + (size_t)e * a.w.e_scales + 2 * (size_t)inter * (H / G), (uint32_t)ngk * H * 4);
+  const __amdgpu_buffer_rsrc_t ra = weight_rsrc(a.af, (uint32_t)a.a_rows * inter * 4);
 
+  uint4 bq[D][KS / 32];
+  float sq[D][GPS][NSUB];
+  auto load_b = [&](uint4 (&bd)[KS / 32], float (&sd)[GPS][NSUB], int st) {
+#pragma unroll
+    for (int g = 0; g < GPS; ++g) {
+      const uint32_t so = ((((uint32_t)(st * GPS + g) * NRT + rt) * 16 + r) * NSUB) * 4;
+      if (NSUB == 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j) sd[g][j] = __uint_as_float(v[j]);
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j) sd[g][j] = __uint_as_float(v[j]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < KS / 32; ++c) bd[c] = wload16(rb, ((uint32_t)(st * (KS / 32) + c) * NRT + rt) * TILE + lane * 16);
+  };
   float4v acc[NSUB][MS], ctmp[NSUB][MS];
 #pragma unroll
   for (int j = 0; j < NSUB; ++j)
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) { acc[j][ms] = float4v{0, 0, 0, 0}; ctmp[j][ms] = float4v{0, 0, 0, 0}; }
-  __syncthreads();
+  __syncthreads();   // arow
 
-  AFetch<MTL, true> An;
-  uint4 bn[KS / 32], bc[KS / 32];
-  fetch_a<MTL, true>(An, a.af, arow, inter, 0);
+  AStage<MTL, true> A[3];
 #pragma unroll
-  for (int c = 0; c < KS / 32; ++c) bn[c] = *(const uint4*)(dq + ((size_t)c * NRT + rt) * TILE + lane * 16);
+  for (int s0 = 0; s0 < 3; ++s0) fetch_a<MTL, true>(A[s0], ra, arow, INTER, s0 * KS, s0 < NSTAGE);
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
+  store_a<BITS, MTL, true, true>(lds[0], A[0]);
 
-  for (int st = 0; st < nstage; ++st) {
-    __syncthreads();
-    store_a<BITS, MTL, true, true>(lds, An);
 #pragma unroll
-    for (int c = 0; c < KS / 32; ++c) bc[c] = bn[c];
-    if (st + 1 < nstage) {
-      fetch_a<MTL, true>(An, a.af, arow, inter, (st + 1) * KS);
-#pragma unroll
-      for (int c = 0; c < KS / 32; ++c)
-        bn[c] = *(const uint4*)(dq + ((size_t)((st + 1) * (KS / 32) + c) * NRT + rt) * TILE + lane * 16);
-    }
+  for (int st = 0; st < NSTAGE; ++st) {
     __syncthreads();
+    if (st + 1 < NSTAGE) store_a<BITS, MTL, true, true>(lds[(st + 1) & 1], A[(st + 1) % 3]);
+    if (st + 3 < NSTAGE) fetch_a<MTL, true>(A[st % 3], ra, arow, INTER, (st + 3) * KS, true);
+    const _Float16* la = lds[st & 1];
+    const int sl = st % D;
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
-      const int gc = st * (KS / 32) + c;
-      const bool first = (gc % cpg) == 0, last = (gc % cpg) == cpg - 1;
+      const bool first = (c % CPG) == 0, last = (c % CPG) == CPG - 1;
       const int lcol = 32 * c + 8 * q4;
       half8 ahi[MS], alo[MS];
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) {
-        ahi[ms] = *(const half8*)(lds + (ms * 16 + r) * LDS_ROW + lcol);
-        alo[ms] = *(const half8*)(lds + MTL * LDS_ROW + (ms * 16 + r) * LDS_ROW + lcol);
+        ahi[ms] = *(const half8*)(la + (ms * 16 + r) * LDS_ROW + lcol);
+        alo[ms] = *(const half8*)(la + MTL * LDS_ROW + (ms * 16 + r) * LDS_ROW + lcol);
       }
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
-        const half8 bfr = BITS == 4 ? unpack_int4(word_of(bc[c], j))
-                                    : unpack_int8(word_of(bc[c], 2 * j), word_of(bc[c], 2 * j + 1));
+        const half8 bfr = BITS == 4 ? unpack_int4(word_of(bq[sl][c], j))
+                                    : unpack_int8(word_of(bq[sl][c], 2 * j), word_of(bq[sl][c], 2 * j + 1));
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
           float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[j][ms];
@@ -1434,15 +1463,15 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
         }
       }
       if (last) {
-        const float* sp = ds + (((size_t)(gc / cpg) * NRT + rt) * 16 + r) * NSUB;
 #pragma unroll
         for (int j = 0; j < NSUB; ++j) {
-          const float sj = sp[j];
+          const float sj = sq[sl][c / CPG][j];
 #pragma unroll
           for (int ms = 0; ms < MS; ++ms) acc[j][ms] += sj * ctmp[j][ms];
         }
       }
     }
+    if (st + D < NSTAGE) load_b(bq[sl], sq[sl], st + D);
   }
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
@@ -1555,33 +1584,42 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int MTL>
+template <int BITS, int G>
 static void gateup_dispatch(const GroupedArgs& a, dim3 grid, hipStream_t s) {
-  const bool split = a.af != nullptr;
-  if (a.w.bits == 4) {
-    if (split) hipLaunchKernelGGL((grouped_gateup_kernel<4, true, MTL>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((grouped_gateup_kernel<4, false, MTL>), grid, dim3(256), 0, s, a);
-  } else {
-    if (split) hipLaunchKernelGGL((grouped_gateup_kernel<8, true, MTL>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((grouped_gateup_kernel<8, false, MTL>), grid, dim3(256), 0, s, a);
-  }
+  if (a.af) hipLaunchKernelGGL((grouped_gateup_kernel<BITS, true, G>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((grouped_gateup_kernel<BITS, false, G>), grid, dim3(256), 0, s, a);
 }
 
-hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, int mtl, hipStream_t s) {
+hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, hipStream_t s) {
   const dim3 grid(max_tiles * (a.w.inter / 128));
-  if (mtl == 64) gateup_dispatch<64>(a, grid, s);
-  else gateup_dispatch<32>(a, grid, s);
+  const int key = (a.w.bits == 8) * 3 + (a.w.group == 64) + 2 * (a.w.group == 128);
+  switch (key) {
+    case 0: gateup_dispatch<4, 32>(a, grid, s); break;
+    case 1: gateup_dispatch<4, 64>(a, grid, s); break;
+    case 2: gateup_dispatch<4, 128>(a, grid, s); break;
+    case 3: gateup_dispatch<8, 32>(a, grid, s); break;
+    case 4: gateup_dispatch<8, 64>(a, grid, s); break;
+    default: gateup_dispatch<8, 128>(a, grid, s); break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int mtl, hipStream_t s) {
+template <int BITS, int G>
+static void down_dispatch(const GroupedArgs& a, dim3 grid, hipStream_t s) {
+  if (a.w.inter == IS) hipLaunchKernelGGL((grouped_down_kernel<BITS, G, IS>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((grouped_down_kernel<BITS, G, I>), grid, dim3(256), 0, s, a);
+}
+
+hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, hipStream_t s) {
   const dim3 grid(max_tiles * (H / (4 * down_rows(a.w.bits))));
-  if (mtl == 64) {
-    if (a.w.bits == 4) hipLaunchKernelGGL((grouped_down_kernel<4, 64>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((grouped_down_kernel<8, 64>), grid, dim3(256), 0, s, a);
-  } else {
-    if (a.w.bits == 4) hipLaunchKernelGGL((grouped_down_kernel<4, 32>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((grouped_down_kernel<8, 32>), grid, dim3(256), 0, s, a);
+  const int key = (a.w.bits == 8) * 3 + (a.w.group == 64) + 2 * (a.w.group == 128);
+  switch (key) {
+    case 0: down_dispatch<4, 32>(a, grid, s); break;
+    case 1: down_dispatch<4, 64>(a, grid, s); break;
+    case 2: down_dispatch<4, 128>(a, grid, s); break;
+    case 3: down_dispatch<8, 32>(a, grid, s); break;
+    case 4: down_dispatch<8, 64>(a, grid, s); break;
+    default: down_dispatch<8, 128>(a, grid, s); break;
   }
   return hipGetLastError();
 }
