@@ -57,7 +57,7 @@ Workspace carve(void* base, int T) {
   Workspace w;
   Carver c{(char*)base, 0};
   const size_t slots = (size_t)T * TOPK;
-  w.max_tiles = (int)(slots / MT) + E + 1;
+  w.max_tiles = (int)(slots / MT_SMALL) + E + 1;   // enough for either tile height
   w.z = (float*)c.take((size_t)T * H * 4);
   const size_t union_start = c.off;
   w.h_routed = (float*)c.take(slots * I * 4);
@@ -292,8 +292,10 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
     return MOE_OK;
   }
 
-  // token rows per GEMM tile
-  const int mtl = MT;
+  // tile shape: 32-row tiles while the experts see few rows each (about 64 or
+  // fewer on average), 64-row tiles beyond
+  const bool small = (size_t)T * TOPK <= (size_t)SMALL_TILE_MAX_SLOTS;
+  const int mtl = small ? MT_SMALL : MT;
   const int max_tiles = (int)((size_t)T * TOPK / mtl) + E + 1;
   HistArgs ha;
   ha.ids = topk_ids; ha.T = T; ha.counts = ws.counts; ha.offsets = ws.offsets;
@@ -304,16 +306,16 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   ga.T = T; ga.tiles = ws.tiles; ga.ntiles = ws.ntiles; ga.offsets = ws.offsets; ga.perm = ws.perm;
   // routed gate/up: A rows are tokens gathered through the permutation
   ga.af = xf; ga.ab = xb; ga.shared = 0; ga.a_by_token = 1; ga.a_rows = T; ga.w = rw; ga.out = ws.h_routed;
-  if (launch_grouped_gateup(ga, max_tiles, s) != hipSuccess) return MOE_E_HIP;
+  if (launch_grouped_gateup(ga, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
   // shared gate/up over all tokens
   ga.shared = 1; ga.w = sw; ga.out = ws.h_shared;
-  if (launch_grouped_gateup(ga, (T + mtl - 1) / mtl, s) != hipSuccess) return MOE_E_HIP;
+  if (launch_grouped_gateup(ga, (T + mtl - 1) / mtl, small, s) != hipSuccess) return MOE_E_HIP;
   // routed down: A rows are h in sorted order
   ga.af = ws.h_routed; ga.ab = nullptr; ga.shared = 0; ga.a_by_token = 0; ga.a_rows = T * TOPK; ga.w = rw;
   ga.out = ws.ysorted;
-  if (launch_grouped_down(ga, max_tiles, s) != hipSuccess) return MOE_E_HIP;
+  if (launch_grouped_down(ga, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
   ga.af = ws.h_shared; ga.shared = 1; ga.a_rows = T; ga.w = sw; ga.out = ws.ys;
-  if (launch_grouped_down(ga, (T + mtl - 1) / mtl, s) != hipSuccess) return MOE_E_HIP;
+  if (launch_grouped_down(ga, (T + mtl - 1) / mtl, small, s) != hipSuccess) return MOE_E_HIP;
   CombineArgs ca;
   ca.ys = ws.ys; ca.ysorted = ws.ysorted; ca.pos_of = ws.pos_of; ca.tw = topk_w;
   ca.y = y; ca.T = T; ca.accumulate = accumulate;

@@ -12,7 +12,9 @@ constexpr int TOPK = 6;      // experts picked per token
 constexpr int I = 896;       // routed expert intermediate
 constexpr int IS = 1792;     // fused shared expert intermediate
 constexpr int TILE = 1024;   // bytes of one packed 16-row tile
-constexpr int MT = 32;       // token rows per tile of the grouped GEMMs
+constexpr int MT = 64;       // token rows per tile of the grouped GEMMs (large tiles)
+constexpr int MT_SMALL = 32; // rows per tile when experts see few rows each
+constexpr int SMALL_TILE_MAX_SLOTS = 64 * 64;   // (token, pick) slots up to which the small tiles run
 constexpr int DECODE_MAX_T = 4;  // largest token count routed to the GEMV path by default
 constexpr int MAX_T = 8192;      // largest token count of one call
 constexpr int MOE_MAX_SLOTS = MAX_T * TOPK;
@@ -121,8 +123,8 @@ hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s);
 hipError_t launch_chain(const ChainArgs& a, hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_hist(const HistArgs& a, hipStream_t s);
-hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, hipStream_t s);
-hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, hipStream_t s);
+hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps, hipStream_t s);
 

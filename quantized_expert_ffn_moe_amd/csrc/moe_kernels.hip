@@ -1158,7 +1158,12 @@ template <int BITS> __device__ __forceinline__ int perm_k(int p) {
 constexpr int KS = 128;             // K staged in LDS per step
 constexpr int LDS_ROW = KS + 8;     // f16 per LDS row (16-byte pad against bank conflicts)
 
-// A-operand staging, split into a global fetch (into registers, issued two
+// Grouped GEMMs come in two tile shapes: 32-row tiles with 4 waves (two
+// workgroups per compute unit) when experts see few rows each, 64 x 256 tiles
+// with 8 waves when they see many.  Both stage A (f16, hi and lo planes for
+// f32 inputs, permuted within each 8-group into the B operand order) and use
+// the same exact-integer B unpacking; the large tiles share B through LDS.
+// Small-tile A staging, split into a global fetch (into registers, issued two
 // stages ahead) and an LDS store (f16 hi plane, and lo plane when SPLIT,
 // permuted within each 8-group into the B operand order).  Thread tid owns the
 // 8-element segments tid + 256 j: row = seg / 16, k = 8 (seg % 16).  The loads
@@ -1166,18 +1171,18 @@ constexpr int LDS_ROW = KS + 8;     // f16 per LDS row (16-byte pad against bank
 // end read zeros without a branch, so the compiler can count the loads in
 // flight precisely.
 template <int MTL, bool F32>
-struct AStage {
+struct AStageS {
   static constexpr int NSEG = MTL / 16;
   uint4 raw[NSEG][F32 ? 2 : 1];
 };
 
 template <int MTL, bool F32>
-__device__ __forceinline__ void fetch_a(AStage<MTL, F32>& A, __amdgpu_buffer_rsrc_t ra, const int* arow, int K,
+__device__ __forceinline__ void fetch_a_s(AStageS<MTL, F32>& A, __amdgpu_buffer_rsrc_t ra, const int* arow, int K,
                                         int k0, bool live) {
   const int tid = threadIdx.x;
   constexpr uint32_t ELT = F32 ? 4 : 2;
 #pragma unroll
-  for (int j = 0; j < AStage<MTL, F32>::NSEG; ++j) {
+  for (int j = 0; j < AStageS<MTL, F32>::NSEG; ++j) {
     const int seg = tid + 256 * j, row = seg >> 4, kk = 8 * (seg & 15);
     const int src = arow[row];
     const uint32_t off = (live && src >= 0) ? ((uint32_t)src * K + k0 + kk) * ELT : 0x80000000u;
@@ -1187,10 +1192,10 @@ __device__ __forceinline__ void fetch_a(AStage<MTL, F32>& A, __amdgpu_buffer_rsr
 }
 
 template <int BITS, int MTL, bool F32, bool SPLIT>
-__device__ __forceinline__ void store_a(_Float16* lds, const AStage<MTL, F32>& A) {
+__device__ __forceinline__ void store_a_s(_Float16* lds, const AStageS<MTL, F32>& A) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < AStage<MTL, F32>::NSEG; ++j) {
+  for (int j = 0; j < AStageS<MTL, F32>::NSEG; ++j) {
     const int seg = tid + 256 * j, row = seg >> 4, kk = 8 * (seg & 15);
     float v[8];
     if (F32) {
@@ -1219,8 +1224,75 @@ __device__ __forceinline__ void store_a(_Float16* lds, const AStage<MTL, F32>& A
   }
 }
 
+// Grouped GEMM tiles: a workgroup of 8 waves computes MT = 64 rows x 256
+// output columns over K stages of KS = 128.  Per stage the workgroup stages
+// the A rows (f16, hi and lo planes for f32 inputs, permuted within each
+// 8-group into the B operand order) and the packed B tiles (raw, 1 KiB each)
+// in LDS, double-buffered; global loads run two stages ahead in registers so
+// that the memory latency hides behind the MFMA work.  Wave (wm, wn) = (w % 2,
+// w / 2) owns rows 32 wm .. 32 wm + 31 and four 16-column n-subtiles.  All
+// global loads go through buffer descriptors: padding rows and stages past the
+// end read zeros without branches, so the compiler counts loads in flight
+// exactly.
+constexpr int GT = 512;                    // threads per grouped workgroup
+constexpr int A_SEG = MT * KS / 8 / GT;    // 8-element A segments per thread per stage (2)
+
+template <bool F32>
+struct AStage {
+  uint4 raw[A_SEG][F32 ? 2 : 1];
+};
+
 __device__ __forceinline__ float wload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+template <bool F32>
+__device__ __forceinline__ void fetch_a(AStage<F32>& A, __amdgpu_buffer_rsrc_t ra, const int* arow, int K, int k0,
+                                        bool live) {
+  const int tid = threadIdx.x;
+  constexpr uint32_t ELT = F32 ? 4 : 2;
+#pragma unroll
+  for (int j = 0; j < A_SEG; ++j) {
+    const int seg = tid + GT * j, row = seg >> 4, kk = 8 * (seg & 15);
+    const int src = arow[row];
+    const uint32_t off = (live && src >= 0) ? ((uint32_t)src * K + k0 + kk) * ELT : 0x80000000u;
+    A.raw[j][0] = wload16(ra, off);
+    if (F32) A.raw[j][F32 ? 1 : 0] = wload16(ra, off + 16);
+  }
+}
+
+// A plane layout in LDS: [row][LDS_ROW] f16 (hi), then the lo plane.
+template <int BITS, bool F32, bool SPLIT>
+__device__ __forceinline__ void store_a(_Float16* lds, const AStage<F32>& A) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < A_SEG; ++j) {
+    const int seg = tid + GT * j, row = seg >> 4, kk = 8 * (seg & 15);
+    float v[8];
+    if (F32) {
+      const uint4 a0 = A.raw[j][0], a1 = A.raw[j][F32 ? 1 : 0];
+      v[0] = __uint_as_float(a0.x); v[1] = __uint_as_float(a0.y); v[2] = __uint_as_float(a0.z); v[3] = __uint_as_float(a0.w);
+      v[4] = __uint_as_float(a1.x); v[5] = __uint_as_float(a1.y); v[6] = __uint_as_float(a1.z); v[7] = __uint_as_float(a1.w);
+    } else {
+      const uint4 u = A.raw[j][0];
+      const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(uw[i] << 16);
+        v[2 * i + 1] = __uint_as_float(uw[i] & 0xFFFF0000u);
+      }
+    }
+    half8 hi, lo;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const float x = v[perm_k<BITS>(p)];
+      const _Float16 xh = (_Float16)x;
+      hi[p] = xh;
+      lo[p] = (_Float16)(x - (float)xh);
+    }
+    *(half8*)(lds + row * LDS_ROW + kk) = hi;
+    if (SPLIT) *(half8*)(lds + MT * LDS_ROW + row * LDS_ROW + kk) = lo;
+  }
 }
 
 struct TileInfo { int valid, nrows, pbase, row0, e; };
@@ -1245,7 +1317,308 @@ __device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile, in
   return ti;
 }
 
-// Gate/up: a workgroup owns one MT-row tile of one expert and 128
+// Gate/up: output block cb covers intermediate columns 128 cb .. 128 cb + 127
+// of both the gate and the up matrix, so that h = SiLU(gate) * up is formed
+// in registers.  Wave (wm, wn): n-subtiles gate 8cb + 2wn + {0, 1} and the same
+// two of up.  B per stage: 16 n-tiles x NB packed tiles.
+template <int BITS, bool SPLIT, int G>
+__global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
+  constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = 2;
+  constexpr int CPG = G / 32, GPS = KS / G, NG = H / G;
+  constexpr bool F32 = SPLIT;
+  constexpr int APL = SPLIT ? 2 : 1;
+  constexpr int BT = 16 * NB;                       // B tiles per stage
+  constexpr int BU = BT * 64 / GT;                  // B uint4 per thread per stage (2 or 4)
+  const int inter = a.w.inter, ncb = inter / 128;
+  const int tile = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+  const TileInfo ti = tile_info(a, tile, MT);
+  if (!ti.valid) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
+            q4 = lane >> 4, wm = wv & 1, wn = wv >> 1;
+  __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][APL * MT * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint4 lds_b[2][BT * 64];
+  __shared__ int arow[MT];
+  if (tid < MT) {
+    int src = -1;
+    if (tid < ti.nrows) src = a.shared ? ti.row0 + tid : a.perm[ti.pbase + tid] / TOPK;
+    arow[tid] = src;
+  }
+  const int e = wave_uniform(ti.e);
+  const uint8_t* eq = a.w.q + (size_t)e * a.w.e_bytes;
+  const float* es = a.w.s + (size_t)e * a.w.e_scales;
+  const size_t mbytes = matrix_bytes(BITS, inter, H), mscales = (size_t)inter * NG;
+  // B: the 16 n-tiles of this block (gate 8cb.., then up 8cb..), each a row of NKB tiles
+  const __amdgpu_buffer_rsrc_t rbg = weight_rsrc(eq + (size_t)(8 * cb) * NKB * TILE, 8 * NKB * TILE);
+  const __amdgpu_buffer_rsrc_t rbu = weight_rsrc(eq + mbytes + (size_t)(8 * cb) * NKB * TILE, 8 * NKB * TILE);
+  // scales of this wave's four n-subtiles (row 16 nt + r of gate or up)
+  __amdgpu_buffer_rsrc_t rs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int nt = 8 * cb + 2 * wn + (i & 1);
+    rs[i] = weight_rsrc(es + (i >> 1) * mscales + (size_t)16 * nt * NG, 16 * NG * 4);
+  }
+  const __amdgpu_buffer_rsrc_t ra =
+      weight_rsrc(F32 ? (const void*)a.af : (const void*)a.ab, (uint32_t)a.a_rows * H * (F32 ? 4 : 2));
+
+  struct Stage {
+    AStage<F32> A;
+    uint4 B[BU];
+    float S[4][GPS];
+  };
+  // uint4 u = tid + GT k of the stage's B: tile bt = u / 64 = (m * 8 + ntl) * NB + h, lane slot u % 64
+  auto fetch = [&](Stage& R, int st) {
+    fetch_a<F32>(R.A, ra, arow, H, st * KS, st < NSTAGE);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < GPS; ++g) R.S[i][g] = wload4(rs[i], (uint32_t)(r * NG + st * GPS + g) * 4);
+#pragma unroll
+    for (int k = 0; k < BU; ++k) {
+      const int u = tid + GT * k, bt = u >> 6, sl = u & 63;
+      const int h = bt % NB, ntl = (bt / NB) & 7, m = bt / (8 * NB);
+      const uint32_t off = (st < NSTAGE) ? ((uint32_t)(ntl * NKB + st * NB + h) * TILE + sl * 16) : 0x80000000u;
+      R.B[k] = wload16(m ? rbu : rbg, off);
+    }
+  };
+  auto put = [&](const Stage& R, int buf) {
+    store_a<BITS, F32, SPLIT>(lds_a[buf], R.A);
+#pragma unroll
+    for (int k = 0; k < BU; ++k) lds_b[buf][tid + GT * k] = R.B[k];
+  };
+
+  float4v acc[4][MS], ctmp[4][MS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) { acc[i][ms] = float4v{0, 0, 0, 0}; ctmp[i][ms] = float4v{0, 0, 0, 0}; }
+  __syncthreads();   // arow
+
+  // one stage: the registers of stage st (already in LDS) take stage st + 2,
+  // the waves multiply stage st, then stage st + 1 (in registers since the
+  // previous stage) goes to the other LDS buffer, so every global load has
+  // two stages of MFMA work to arrive.  Stages past the end read zeros.
+  auto step = [&](int st, Stage& cur, Stage& nxt, int buf) {
+    __syncthreads();   // buffer buf holds stage st; buffer buf ^ 1 is free
+    float sq[4][GPS];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < GPS; ++g) sq[i][g] = cur.S[i][g];
+    fetch(cur, st + 2);
+    const _Float16* la = lds_a[buf];
+    const uint4* lb = lds_b[buf];
+    uint4 bw[4][NB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < NB; ++h) bw[i][h] = lb[(((i >> 1) * 8 + 2 * wn + (i & 1)) * NB + h) * 64 + lane];
+#pragma unroll
+    for (int c = 0; c < KS / 32; ++c) {
+      const bool first = (c % CPG) == 0, last = (c % CPG) == CPG - 1;
+      half8 bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (BITS == 4) bfr[i] = unpack_int4(word_of(bw[i][0], c));
+        else bfr[i] = unpack_int8(word_of(bw[i][c >> 1], 2 * (c & 1)), word_of(bw[i][c >> 1], 2 * (c & 1) + 1));
+      }
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        const int lrow = 32 * wm + 16 * ms + r, lcol = 32 * c + 8 * q4;
+        const half8 ahi = *(const half8*)(la + lrow * LDS_ROW + lcol);
+        half8 alo;
+        if (SPLIT) alo = *(const half8*)(la + MT * LDS_ROW + lrow * LDS_ROW + lcol);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[i][ms];
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bfr[i], cc, 0, 0, 0);
+          if (SPLIT) cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bfr[i], cc, 0, 0, 0);
+          ctmp[i][ms] = cc;
+        }
+      }
+      if (last) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sv = sq[i][c / CPG];
+#pragma unroll
+          for (int ms = 0; ms < MS; ++ms) acc[i][ms] += sv * ctmp[i][ms];
+        }
+      }
+    }
+    put(nxt, buf ^ 1);
+  };
+  Stage R0, R1;
+  fetch(R0, 0);
+  fetch(R1, 1);
+  put(R0, 0);
+  static_assert(NSTAGE % 2 == 0, "stage pairs");
+#pragma unroll 1
+  for (int st = 0; st < NSTAGE; st += 2) {
+    step(st, R0, R1, 0);
+    step(st + 1, R1, R0, 1);
+  }
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int m = 32 * wm + 16 * ms + 4 * q4 + k;
+      if (m < ti.nrows) {
+        const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          a.out[orow * inter + 16 * (8 * cb + 2 * wn + j) + r] = silu_mul(acc[j][ms][k], acc[2 + j][ms][k]);
+      }
+    }
+}
+
+// Down: output block cb covers rows 256 cb .. 256 cb + 255 of W_d (output
+// columns of the layer), i.e. NRTB packed row tiles of DR rows; wave (wm, wn)
+// owns 64 of them (four 16-row n-subtiles).  A = h in f32 (hi and lo planes).
+// B per stage: 4 K-chunks of 32 x NRTB row tiles.
+template <int BITS, int G, int INTER>
+__global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
+  constexpr int DR = down_rows(BITS), NRT = H / DR, NRTB = 256 / DR, MS = 2, NSUB = DR / 16;
+  constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS, NCB = H / 256;
+  constexpr int BT = 4 * NRTB;                      // B tiles per stage (16 or 32)
+  constexpr int BU = BT * 64 / GT;
+  constexpr int WRT = 4 / NSUB;                     // row tiles per wave (1 or 2)
+  const int tile = blockIdx.x / NCB, cb = blockIdx.x % NCB;
+  const TileInfo ti = tile_info(a, tile, MT);
+  if (!ti.valid) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
+            q4 = lane >> 4, wm = wv & 1, wn = wv >> 1;
+  __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][2 * MT * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint4 lds_b[2][BT * 64];
+  __shared__ int arow[MT];
+  if (tid < MT) arow[tid] = tid < ti.nrows ? (a.shared ? ti.row0 + tid : ti.pbase + tid) : -1;
+  const int e = wave_uniform(ti.e);
+  const size_t mbytes = matrix_bytes(BITS, INTER, H);
+  const int ngk = INTER / G;
+  const __amdgpu_buffer_rsrc_t rb = weight_rsrc(a.w.q + (size_t)e * a.w.e_bytes + 2 * mbytes, (uint32_t)mbytes);
+  const __amdgpu_buffer_rsrc_t rs =
+      weight_rsrc(a.w.s + (size_t)e * a.w.e_scales + 2 * (size_t)INTER * (H / G), (uint32_t)ngk * H * 4);
+  const __amdgpu_buffer_rsrc_t ra = weight_rsrc(a.af, (uint32_t)a.a_rows * INTER * 4);
+
+  struct Stage {
+    AStage<true> A;
+    uint4 B[BU];
+    float S[GPS][4];
+  };
+  // B uint4 u: tile bt = u / 64 = c * NRTB + rtl, lane slot u % 64
+  auto fetch = [&](Stage& R, int st) {
+    fetch_a<true>(R.A, ra, arow, INTER, st * KS, st < NSTAGE);
+#pragma unroll
+    for (int g = 0; g < GPS; ++g)
+#pragma unroll
+      for (int w2 = 0; w2 < WRT; ++w2) {
+        const int rt = cb * NRTB + WRT * wn + w2;
+        const uint32_t so = ((((uint32_t)(st * GPS + g) * NRT + rt) * 16 + r) * NSUB) * 4;
+        if (NSUB == 4) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) R.S[g][j] = __uint_as_float(v[j]);
+        } else {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0);
+          R.S[g][2 * w2] = __uint_as_float(v[0]);
+          R.S[g][2 * w2 + 1] = __uint_as_float(v[1]);
+        }
+      }
+#pragma unroll
+    for (int k = 0; k < BU; ++k) {
+      const int u = tid + GT * k, bt = u >> 6, sl = u & 63;
+      const int c = bt / NRTB, rtl = bt % NRTB;
+      const uint32_t off =
+          (st < NSTAGE) ? ((uint32_t)((4 * st + c) * NRT + cb * NRTB + rtl) * TILE + sl * 16) : 0x80000000u;
+      R.B[k] = wload16(rb, off);
+    }
+  };
+  auto put = [&](const Stage& R, int buf) {
+    store_a<BITS, true, true>(lds_a[buf], R.A);
+#pragma unroll
+    for (int k = 0; k < BU; ++k) lds_b[buf][tid + GT * k] = R.B[k];
+  };
+
+  float4v acc[4][MS], ctmp[4][MS];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) { acc[j][ms] = float4v{0, 0, 0, 0}; ctmp[j][ms] = float4v{0, 0, 0, 0}; }
+  __syncthreads();   // arow
+
+  auto step = [&](int st, Stage& cur, Stage& nxt, int buf) {
+    __syncthreads();
+    float sq[GPS][4];
+#pragma unroll
+    for (int g = 0; g < GPS; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sq[g][j] = cur.S[g][j];
+    fetch(cur, st + 2);
+    const _Float16* la = lds_a[buf];
+    const uint4* lb = lds_b[buf];
+#pragma unroll
+    for (int c = 0; c < KS / 32; ++c) {
+      const bool first = (c % CPG) == 0, last = (c % CPG) == CPG - 1;
+      const int lcol = 32 * c + 8 * q4;
+      half8 ahi[MS], alo[MS];
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        ahi[ms] = *(const half8*)(la + (32 * wm + 16 * ms + r) * LDS_ROW + lcol);
+        alo[ms] = *(const half8*)(la + MT * LDS_ROW + (32 * wm + 16 * ms + r) * LDS_ROW + lcol);
+      }
+      uint4 bw[WRT];
+#pragma unroll
+      for (int w2 = 0; w2 < WRT; ++w2) bw[w2] = lb[(c * NRTB + WRT * wn + w2) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int w2 = j / NSUB, jj = j % NSUB;
+        const half8 bfr = BITS == 4 ? unpack_int4(word_of(bw[w2], jj))
+                                    : unpack_int8(word_of(bw[w2], 2 * jj), word_of(bw[w2], 2 * jj + 1));
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[j][ms];
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ms], bfr, cc, 0, 0, 0);
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ms], bfr, cc, 0, 0, 0);
+          ctmp[j][ms] = cc;
+        }
+      }
+      if (last) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sj = sq[c / CPG][j];
+#pragma unroll
+          for (int ms = 0; ms < MS; ++ms) acc[j][ms] += sj * ctmp[j][ms];
+        }
+      }
+    }
+    put(nxt, buf ^ 1);
+  };
+  Stage R0, R1;
+  fetch(R0, 0);
+  fetch(R1, 1);
+  put(R0, 0);
+#pragma unroll 1
+  for (int st = 0; st + 1 < NSTAGE; st += 2) {
+    step(st, R0, R1, 0);
+    step(st + 1, R1, R0, 1);
+  }
+  if (NSTAGE % 2) step(NSTAGE - 1, R0, R1, 0);
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int m = 32 * wm + 16 * ms + 4 * q4 + k;
+      if (m < ti.nrows) {
+        const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rt = cb * NRTB + WRT * wn + j / NSUB;
+          a.out[orow * H + DR * rt + 16 * (j % NSUB) + r] = acc[j][ms][k];
+        }
+      }
+    }
+}
+
+// Small tiles (few rows per expert): gate/up, a workgroup of 4 waves owns one
+// 32-row tile of one expert and 128
 // intermediate columns; wave w computes gate and up for columns 32w..32w+31
 // of them (n-subtiles 8cb + 2w, 8cb + 2w + 1 of both matrices) and writes
 // h = SiLU(gate) * up.  Software pipeline over K stages of 128: the packed B
@@ -1253,8 +1626,8 @@ __device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile, in
 // ring, A two stages ahead into registers and one stage ahead into a double
 // buffer in LDS, so that the memory latency hides behind the MFMA work.
 template <int BITS, bool SPLIT, int G>
-__global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
-  constexpr int MTL = MT;
+__global__ __launch_bounds__(256) void gateup_small_kernel(GroupedArgs a) {
+  constexpr int MTL = MT_SMALL;
   constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MTL / 16;
   constexpr int CPG = G / 32, GPS = KS / G, NG = H / G;
   constexpr int D = BITS == 4 ? 3 : 2;      // B stages in flight
@@ -1309,18 +1682,18 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
 
   // Fully unrolled stage loop: every ring slot is a fixed register set, so no
   // value is copied while its load is still in flight.
-  AStage<MTL, F32> A[3];   // A(s) lives in slot s % 3 until it is stored to LDS
+  AStageS<MTL, F32> A[3];   // A(s) lives in slot s % 3 until it is stored to LDS
 #pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0) fetch_a<MTL, F32>(A[s0], ra, arow, H, s0 * KS, s0 < NSTAGE);
+  for (int s0 = 0; s0 < 3; ++s0) fetch_a_s<MTL, F32>(A[s0], ra, arow, H, s0 * KS, s0 < NSTAGE);
 #pragma unroll
   for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
-  store_a<BITS, MTL, F32, SPLIT>(lds[0], A[0]);
+  store_a_s<BITS, MTL, F32, SPLIT>(lds[0], A[0]);
 
 #pragma unroll
   for (int st = 0; st < NSTAGE; ++st) {
     __syncthreads();   // lds[st & 1] holds A(st); lds[(st + 1) & 1] is free
-    if (st + 1 < NSTAGE) store_a<BITS, MTL, F32, SPLIT>(lds[(st + 1) & 1], A[(st + 1) % 3]);
-    if (st + 3 < NSTAGE) fetch_a<MTL, F32>(A[st % 3], ra, arow, H, (st + 3) * KS, true);
+    if (st + 1 < NSTAGE) store_a_s<BITS, MTL, F32, SPLIT>(lds[(st + 1) & 1], A[(st + 1) % 3]);
+    if (st + 3 < NSTAGE) fetch_a_s<MTL, F32>(A[st % 3], ra, arow, H, (st + 3) * KS, true);
     const _Float16* la = lds[st & 1];
     const int sl = st % D;
 #pragma unroll
@@ -1371,14 +1744,14 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
     }
 }
 
-// Down: a workgroup owns one MT-row tile of A (h, fp32 split hi/lo) and four
+// Small tiles: down, a workgroup owns one 32-row tile of A (h, fp32 split hi/lo) and four
 // packed down tiles' worth of output rows: wave w covers row tile 4cb + w,
 // i.e. 64 (int4) or 32 (int8) output columns, one 16-column MFMA n-subtile
 // per 16 rows.  Each 16-byte lane load of a down tile feeds every n-subtile of
 // the row tile for one 32-wide K chunk.  Same software pipeline as gate/up.
 template <int BITS, int G, int INTER>
-__global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
-  constexpr int MTL = MT;
+__global__ __launch_bounds__(256) void down_small_kernel(GroupedArgs a) {
+  constexpr int MTL = MT_SMALL;
   constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4, MS = MTL / 16;
   constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS;
   constexpr int D = 3;
@@ -1426,18 +1799,18 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
     for (int ms = 0; ms < MS; ++ms) { acc[j][ms] = float4v{0, 0, 0, 0}; ctmp[j][ms] = float4v{0, 0, 0, 0}; }
   __syncthreads();   // arow
 
-  AStage<MTL, true> A[3];
+  AStageS<MTL, true> A[3];
 #pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0) fetch_a<MTL, true>(A[s0], ra, arow, INTER, s0 * KS, s0 < NSTAGE);
+  for (int s0 = 0; s0 < 3; ++s0) fetch_a_s<MTL, true>(A[s0], ra, arow, INTER, s0 * KS, s0 < NSTAGE);
 #pragma unroll
   for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
-  store_a<BITS, MTL, true, true>(lds[0], A[0]);
+  store_a_s<BITS, MTL, true, true>(lds[0], A[0]);
 
 #pragma unroll
   for (int st = 0; st < NSTAGE; ++st) {
     __syncthreads();
-    if (st + 1 < NSTAGE) store_a<BITS, MTL, true, true>(lds[(st + 1) & 1], A[(st + 1) % 3]);
-    if (st + 3 < NSTAGE) fetch_a<MTL, true>(A[st % 3], ra, arow, INTER, (st + 3) * KS, true);
+    if (st + 1 < NSTAGE) store_a_s<BITS, MTL, true, true>(lds[(st + 1) & 1], A[(st + 1) % 3]);
+    if (st + 3 < NSTAGE) fetch_a_s<MTL, true>(A[st % 3], ra, arow, INTER, (st + 3) * KS, true);
     const _Float16* la = lds[st & 1];
     const int sl = st % D;
 #pragma unroll
@@ -1585,41 +1958,53 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
 }
 
 template <int BITS, int G>
-static void gateup_dispatch(const GroupedArgs& a, dim3 grid, hipStream_t s) {
-  if (a.af) hipLaunchKernelGGL((grouped_gateup_kernel<BITS, true, G>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((grouped_gateup_kernel<BITS, false, G>), grid, dim3(256), 0, s, a);
+static void gateup_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
+  if (small) {
+    const dim3 grid(max_tiles * (a.w.inter / 128));
+    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<BITS, true, G>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gateup_small_kernel<BITS, false, G>), grid, dim3(256), 0, s, a);
+  } else {
+    const dim3 grid(max_tiles * (a.w.inter / 128));   // 128 gate + 128 up columns per workgroup
+    if (a.af) hipLaunchKernelGGL((grouped_gateup_kernel<BITS, true, G>), grid, dim3(GT), 0, s, a);
+    else hipLaunchKernelGGL((grouped_gateup_kernel<BITS, false, G>), grid, dim3(GT), 0, s, a);
+  }
 }
 
-hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, hipStream_t s) {
-  const dim3 grid(max_tiles * (a.w.inter / 128));
+hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
   const int key = (a.w.bits == 8) * 3 + (a.w.group == 64) + 2 * (a.w.group == 128);
   switch (key) {
-    case 0: gateup_dispatch<4, 32>(a, grid, s); break;
-    case 1: gateup_dispatch<4, 64>(a, grid, s); break;
-    case 2: gateup_dispatch<4, 128>(a, grid, s); break;
-    case 3: gateup_dispatch<8, 32>(a, grid, s); break;
-    case 4: gateup_dispatch<8, 64>(a, grid, s); break;
-    default: gateup_dispatch<8, 128>(a, grid, s); break;
+    case 0: gateup_dispatch<4, 32>(a, max_tiles, small, s); break;
+    case 1: gateup_dispatch<4, 64>(a, max_tiles, small, s); break;
+    case 2: gateup_dispatch<4, 128>(a, max_tiles, small, s); break;
+    case 3: gateup_dispatch<8, 32>(a, max_tiles, small, s); break;
+    case 4: gateup_dispatch<8, 64>(a, max_tiles, small, s); break;
+    default: gateup_dispatch<8, 128>(a, max_tiles, small, s); break;
   }
   return hipGetLastError();
 }
 
 template <int BITS, int G>
-static void down_dispatch(const GroupedArgs& a, dim3 grid, hipStream_t s) {
-  if (a.w.inter == IS) hipLaunchKernelGGL((grouped_down_kernel<BITS, G, IS>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((grouped_down_kernel<BITS, G, I>), grid, dim3(256), 0, s, a);
+static void down_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
+  if (small) {
+    const dim3 grid(max_tiles * (H / (4 * down_rows(BITS))));
+    if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<BITS, G, IS>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((down_small_kernel<BITS, G, I>), grid, dim3(256), 0, s, a);
+  } else {
+    const dim3 grid(max_tiles * (H / 256));             // 256 output columns per workgroup
+    if (a.w.inter == IS) hipLaunchKernelGGL((grouped_down_kernel<BITS, G, IS>), grid, dim3(GT), 0, s, a);
+    else hipLaunchKernelGGL((grouped_down_kernel<BITS, G, I>), grid, dim3(GT), 0, s, a);
+  }
 }
 
-hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, hipStream_t s) {
-  const dim3 grid(max_tiles * (H / (4 * down_rows(a.w.bits))));
+hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
   const int key = (a.w.bits == 8) * 3 + (a.w.group == 64) + 2 * (a.w.group == 128);
   switch (key) {
-    case 0: down_dispatch<4, 32>(a, grid, s); break;
-    case 1: down_dispatch<4, 64>(a, grid, s); break;
-    case 2: down_dispatch<4, 128>(a, grid, s); break;
-    case 3: down_dispatch<8, 32>(a, grid, s); break;
-    case 4: down_dispatch<8, 64>(a, grid, s); break;
-    default: down_dispatch<8, 128>(a, grid, s); break;
+    case 0: down_dispatch<4, 32>(a, max_tiles, small, s); break;
+    case 1: down_dispatch<4, 64>(a, max_tiles, small, s); break;
+    case 2: down_dispatch<4, 128>(a, max_tiles, small, s); break;
+    case 3: down_dispatch<8, 32>(a, max_tiles, small, s); break;
+    case 4: down_dispatch<8, 64>(a, max_tiles, small, s); break;
+    default: down_dispatch<8, 128>(a, max_tiles, small, s); break;
   }
   return hipGetLastError();
 }
