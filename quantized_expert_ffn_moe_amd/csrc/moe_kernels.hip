@@ -1319,11 +1319,12 @@ __device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile, in
 
 // Gate/up: output block cb covers intermediate columns 128 cb .. 128 cb + 127
 // of both the gate and the up matrix, so that h = SiLU(gate) * up is formed
-// in registers.  Wave (wm, wn): n-subtiles gate 8cb + 2wn + {0, 1} and the same
-// two of up.  B per stage: 16 n-tiles x NB packed tiles.
+// in registers.  Wave w owns all 64 rows of the tile and one 16-column
+// n-subtile of each matrix (n-tile 8 cb + w): every packed B word is unpacked
+// by exactly one wave.  B per stage: 16 n-tiles x NB packed tiles.
 template <int BITS, bool SPLIT, int G>
 __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
-  constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = 2;
+  constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MT / 16;
   constexpr int CPG = G / 32, GPS = KS / G, NG = H / G;
   constexpr bool F32 = SPLIT;
   constexpr int APL = SPLIT ? 2 : 1;
@@ -1334,7 +1335,7 @@ __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
   const TileInfo ti = tile_info(a, tile, MT);
   if (!ti.valid) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
-            q4 = lane >> 4, wm = wv & 1, wn = wv >> 1;
+            q4 = lane >> 4;
   __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][APL * MT * LDS_ROW];
   __shared__ __attribute__((aligned(16))) uint4 lds_b[2][BT * 64];
   __shared__ int arow[MT];
@@ -1350,28 +1351,26 @@ __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
   // B: the 16 n-tiles of this block (gate 8cb.., then up 8cb..), each a row of NKB tiles
   const __amdgpu_buffer_rsrc_t rbg = weight_rsrc(eq + (size_t)(8 * cb) * NKB * TILE, 8 * NKB * TILE);
   const __amdgpu_buffer_rsrc_t rbu = weight_rsrc(eq + mbytes + (size_t)(8 * cb) * NKB * TILE, 8 * NKB * TILE);
-  // scales of this wave's four n-subtiles (row 16 nt + r of gate or up)
-  __amdgpu_buffer_rsrc_t rs[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nt = 8 * cb + 2 * wn + (i & 1);
-    rs[i] = weight_rsrc(es + (i >> 1) * mscales + (size_t)16 * nt * NG, 16 * NG * 4);
-  }
+  // scales of this wave's gate and up n-subtile (row 16 nt + r)
+  const int nt = 8 * cb + wv;
+  const __amdgpu_buffer_rsrc_t rsg = weight_rsrc(es + (size_t)16 * nt * NG, 16 * NG * 4);
+  const __amdgpu_buffer_rsrc_t rsu = weight_rsrc(es + mscales + (size_t)16 * nt * NG, 16 * NG * 4);
   const __amdgpu_buffer_rsrc_t ra =
       weight_rsrc(F32 ? (const void*)a.af : (const void*)a.ab, (uint32_t)a.a_rows * H * (F32 ? 4 : 2));
 
   struct Stage {
     AStage<F32> A;
     uint4 B[BU];
-    float S[4][GPS];
+    float S[2][GPS];
   };
   // uint4 u = tid + GT k of the stage's B: tile bt = u / 64 = (m * 8 + ntl) * NB + h, lane slot u % 64
   auto fetch = [&](Stage& R, int st) {
     fetch_a<F32>(R.A, ra, arow, H, st * KS, st < NSTAGE);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < GPS; ++g) R.S[i][g] = wload4(rs[i], (uint32_t)(r * NG + st * GPS + g) * 4);
+    for (int g = 0; g < GPS; ++g) {
+      R.S[0][g] = wload4(rsg, (uint32_t)(r * NG + st * GPS + g) * 4);
+      R.S[1][g] = wload4(rsu, (uint32_t)(r * NG + st * GPS + g) * 4);
+    }
 #pragma unroll
     for (int k = 0; k < BU; ++k) {
       const int u = tid + GT * k, bt = u >> 6, sl = u & 63;
@@ -1386,9 +1385,9 @@ __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
     for (int k = 0; k < BU; ++k) lds_b[buf][tid + GT * k] = R.B[k];
   };
 
-  float4v acc[4][MS], ctmp[4][MS];
+  float4v acc[2][MS], ctmp[2][MS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) { acc[i][ms] = float4v{0, 0, 0, 0}; ctmp[i][ms] = float4v{0, 0, 0, 0}; }
   __syncthreads();   // arow
@@ -1399,36 +1398,36 @@ __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
   // two stages of MFMA work to arrive.  Stages past the end read zeros.
   auto step = [&](int st, Stage& cur, Stage& nxt, int buf) {
     __syncthreads();   // buffer buf holds stage st; buffer buf ^ 1 is free
-    float sq[4][GPS];
+    float sq[2][GPS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int g = 0; g < GPS; ++g) sq[i][g] = cur.S[i][g];
     fetch(cur, st + 2);
     const _Float16* la = lds_a[buf];
     const uint4* lb = lds_b[buf];
-    uint4 bw[4][NB];
+    uint4 bw[2][NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int h = 0; h < NB; ++h) bw[i][h] = lb[(((i >> 1) * 8 + 2 * wn + (i & 1)) * NB + h) * 64 + lane];
+      for (int h = 0; h < NB; ++h) bw[i][h] = lb[((i * 8 + wv) * NB + h) * 64 + lane];
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
       const bool first = (c % CPG) == 0, last = (c % CPG) == CPG - 1;
-      half8 bfr[4];
+      half8 bfr[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         if (BITS == 4) bfr[i] = unpack_int4(word_of(bw[i][0], c));
         else bfr[i] = unpack_int8(word_of(bw[i][c >> 1], 2 * (c & 1)), word_of(bw[i][c >> 1], 2 * (c & 1) + 1));
       }
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) {
-        const int lrow = 32 * wm + 16 * ms + r, lcol = 32 * c + 8 * q4;
+        const int lrow = 16 * ms + r, lcol = 32 * c + 8 * q4;
         const half8 ahi = *(const half8*)(la + lrow * LDS_ROW + lcol);
         half8 alo;
         if (SPLIT) alo = *(const half8*)(la + MT * LDS_ROW + lrow * LDS_ROW + lcol);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
           float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[i][ms];
           cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bfr[i], cc, 0, 0, 0);
           if (SPLIT) cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bfr[i], cc, 0, 0, 0);
@@ -1437,7 +1436,7 @@ __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
       }
       if (last) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
           const float sv = sq[i][c / CPG];
 #pragma unroll
           for (int ms = 0; ms < MS; ++ms) acc[i][ms] += sv * ctmp[i][ms];
@@ -1460,12 +1459,10 @@ __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
   for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int m = 32 * wm + 16 * ms + 4 * q4 + k;
+      const int m = 16 * ms + 4 * q4 + k;
       if (m < ti.nrows) {
         const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          a.out[orow * inter + 16 * (8 * cb + 2 * wn + j) + r] = silu_mul(acc[j][ms][k], acc[2 + j][ms][k]);
+        a.out[orow * inter + 16 * nt + r] = silu_mul(acc[0][ms][k], acc[1][ms][k]);
       }
     }
 }
