@@ -36,6 +36,21 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
+// 16-byte device-scope (L2-coherent, sc1) loads through a bounds-checked buffer
+// descriptor: used for everything one workgroup of the persistent kernel reads
+// that another one wrote during the same launch.
+typedef unsigned int u32x4 __attribute__((vector_size(16)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;
+__device__ __forceinline__ u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ float4 as_float4(u32x4 v) {
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ float bf16_rne(float v) {
@@ -116,6 +131,81 @@ __device__ __forceinline__ float inv_rms(const float* red4, float eps) {
 // logit, so the 6 largest logits (ties to the lower index) are the 6 largest
 // probabilities.
 // ---------------------------------------------------------------------------
+// Pass 1 of both routers (256 threads): the TB rows of x starting at token t0
+// into LDS as f32 (all loads issued at once; rows past the end read zeros),
+// and with the norm, z = RMSNorm(x) (bf16-rounded when asked) both in LDS and
+// written out.  The per-token sums of squares use the standalone RMSNorm's
+// per-thread order and reduction, so the two give bit-identical z.
+template <int TB, int ROW>
+__device__ __forceinline__ void router_rows(const RouterArgs& a, int t0, float* zs, float* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nt = min(TB, a.T - t0);
+  const uint32_t elt = a.x_bf16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.x), (short)0, (uint32_t)a.T * H * elt, 0x00020000);
+  if (a.x_bf16) {
+    constexpr int NU = TB * H / 8, NV = (NU + 255) / 256;   // uint4 (8 bf16) in all, per thread
+    u32x4 v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int u = tid + 256 * j;
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, u < NU ? ((uint32_t)t0 * H + 8 * u) * 2 : 0x80000000u, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if (tid + 256 * j >= NU) continue;
+      const int f0 = 8 * (tid + 256 * j), f = (f0 / H) * ROW + f0 % H;
+      float4 lo, hi;
+      lo.x = bf16_to_f32((uint16_t)v[j][0]); lo.y = bf16_to_f32((uint16_t)(v[j][0] >> 16));
+      lo.z = bf16_to_f32((uint16_t)v[j][1]); lo.w = bf16_to_f32((uint16_t)(v[j][1] >> 16));
+      hi.x = bf16_to_f32((uint16_t)v[j][2]); hi.y = bf16_to_f32((uint16_t)(v[j][2] >> 16));
+      hi.z = bf16_to_f32((uint16_t)v[j][3]); hi.w = bf16_to_f32((uint16_t)(v[j][3] >> 16));
+      *(float4*)&zs[f] = lo;
+      *(float4*)&zs[f + 4] = hi;
+    }
+  } else {
+    constexpr int NU = TB * H / 4, NV = (NU + 255) / 256;   // uint4 (4 f32) in all, per thread
+    u32x4 v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int u = tid + 256 * j;
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, u < NU ? ((uint32_t)t0 * H + 4 * u) * 4 : 0x80000000u, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (tid + 256 * j < NU) {
+        const int f0 = 4 * (tid + 256 * j);
+        *(float4*)&zs[(f0 / H) * ROW + f0 % H] = as_float4(v[j]);
+      }
+  }
+  __syncthreads();
+  if (!a.norm) return;
+  for (int tt = 0; tt < TB; ++tt) {
+    float v[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) v[i] = zs[tt * ROW + tid + 256 * i];
+    const float ss = wave_sum(thread_sumsq(v));
+    if (lane == 0) red[tt * 4 + wv] = ss;
+  }
+  __syncthreads();
+  for (int tt = 0; tt < nt; ++tt) {
+    const float inv = inv_rms(&red[tt * 4], a.eps);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int k = tid + 256 * i;
+      float z = zs[tt * ROW + k] * inv;
+      if (a.norm_bf16) {
+        z = bf16_rne(z);
+        ((uint16_t*)a.z)[(size_t)(t0 + tt) * H + k] = (uint16_t)(__float_as_uint(z) >> 16);
+      } else {
+        ((float*)a.z)[(size_t)(t0 + tt) * H + k] = z;
+      }
+      zs[tt * ROW + k] = z;
+    }
+  }
+  __syncthreads();
+}
+
 constexpr int RT_TB = 4;       // tokens per workgroup
 
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
@@ -125,41 +215,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   const int t0 = blockIdx.x * RT_TB;
   const int nt = min(RT_TB, a.T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  auto xval = [&](int t, int k) -> float {
-    const size_t idx = (size_t)(t0 + t) * H + k;
-    return a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x)[idx]) : ((const float*)a.x)[idx];
-  };
-  // pass 1: rows into LDS; with the norm, 1/rms per token and z (also written out)
-  for (int tt = 0; tt < RT_TB; ++tt) {
-    float v[5];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) v[i] = tt < nt ? xval(tt, tid + 256 * i) : 0.f;
-    if (a.norm) {
-      const float ss = wave_sum(thread_sumsq(v));
-      if (lane == 0) red[tt][wv] = ss;
-    }
-#pragma unroll
-    for (int i = 0; i < 5; ++i) zs[tt][tid + 256 * i] = v[i];
-  }
-  __syncthreads();
-  if (a.norm) {
-    for (int tt = 0; tt < nt; ++tt) {
-      const float inv = inv_rms(red[tt], a.eps);
-#pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const int k = tid + 256 * i;
-        float z = zs[tt][k] * inv;
-        if (a.norm_bf16) {
-          z = bf16_rne(z);
-          ((uint16_t*)a.z)[(size_t)(t0 + tt) * H + k] = (uint16_t)(__float_as_uint(z) >> 16);
-        } else {
-          ((float*)a.z)[(size_t)(t0 + tt) * H + k] = z;
-        }
-        zs[tt][k] = z;
-      }
-    }
-    __syncthreads();
-  }
+  router_rows<RT_TB, H>(a, t0, &zs[0][0], &red[0][0]);
   // pass 2: wave w owns experts 16w..16w+15, four at a time; lane = (expert
   // eg = lane / 16 of the four, column group kk = lane % 16), so one wave load
   // reads four 256-byte runs of W_r rows; the 16 column groups of each row add
@@ -375,21 +431,6 @@ __device__ __forceinline__ float planes_value(const int* P) {
 // 512 threads (8 waves) runs one item; all of the item's weight bytes are
 // requested up front (ItemRegs) so that they are in flight together.
 // ---------------------------------------------------------------------------
-// 16-byte device-scope (L2-coherent, sc1) loads through a bounds-checked buffer
-// descriptor: used for everything one workgroup of the persistent kernel reads
-// that another one wrote during the same launch.
-typedef unsigned int u32x4 __attribute__((vector_size(16)));
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
-}
-constexpr int CPOL_SC1 = 16;
-__device__ __forceinline__ u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL_SC1);
-}
-__device__ __forceinline__ float4 as_float4(u32x4 v) {
-  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
-}
-
 // Plain (cached) loads through a buffer descriptor of `bytes` bytes: offsets
 // at or beyond the end return zeros without touching memory, which lets a
 // wave issue a fixed number of loads with no branches around them.
@@ -1031,6 +1072,78 @@ __global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
 
 __global__ void zero_words_kernel(uint32_t* p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Router for many tokens: 16 tokens per workgroup, logits on the fp32 matrix
+// cores (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 accumulation).
+// Wave w computes the 16 x 16 tile of experts 16w .. 16w + 15: lane (r, q)
+// feeds token r / expert 16w + r with inputs kb + 4q + j of each 16-wide K
+// step (component j of a float4), so one float4 of z (LDS) and one of W_r
+// (global, L2-resident) per lane feed four MFMAs.  Pass 1 and the selection
+// are those of router_kernel.
+// ---------------------------------------------------------------------------
+constexpr int RM_TB = 16;
+constexpr int RM_ROW = H + 4;   // padded z rows: the 16 rows an MFMA operand read touches hit distinct banks
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
+  __shared__ __attribute__((aligned(16))) float zs[RM_TB][RM_ROW];     // 80 KB
+  __shared__ float red[RM_TB][4];
+  __shared__ __attribute__((aligned(16))) float lg[RM_TB][E];
+  const int t0 = blockIdx.x * RM_TB;
+  const int nt = min(RM_TB, a.T - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  router_rows<RM_TB, RM_ROW>(a, t0, &zs[0][0], &red[0][0]);
+  {
+    const int r = lane & 15, q = lane >> 4, e = 16 * wv + r;
+    // W_r rows of this wave's experts through a buffer descriptor (reads past
+    // the row end return zeros), eight 16-wide K steps in flight
+    const __amdgpu_buffer_rsrc_t rw = weight_rsrc(a.wr + (size_t)16 * wave_uniform(wv) * H, 16 * H * 4);
+    const uint32_t wo = (uint32_t)(r * H + 4 * q) * 4;
+    const float* zr = &zs[r][4 * q];
+    constexpr int PF = 8;
+    u32x4 wq[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) wq[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64 * j, 0, 0);
+    // four independent accumulation chains (component j of each float4)
+    float4v acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 1
+    for (int kb0 = 0; kb0 < H; kb0 += 16 * PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const u32x4 w4 = wq[j];
+        const uint32_t nk = (uint32_t)(kb0 + 16 * PF + 16 * j);
+        wq[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, nk < (uint32_t)H ? wo + 4 * nk : 0x80000000u, 0, 0);
+        const float4 z4 = *(const float4*)(zr + kb0 + 16 * j);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(z4.x, __uint_as_float(w4[0]), acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(z4.y, __uint_as_float(w4[1]), acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(z4.z, __uint_as_float(w4[2]), acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(z4.w, __uint_as_float(w4[3]), acc[3], 0, 0, 0);
+      }
+    }
+    const float b = a.bias ? a.bias[e] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lg[4 * q + j][e] = ((acc[0][j] + acc[1][j]) + (acc[2][j] + acc[3][j])) + b;
+  }
+  __syncthreads();
+  // selection: wave w handles tokens w, w + 4, w + 8, w + 12; lane = expert
+  for (int tt = wv; tt < nt; tt += 4) {
+    const int e = lane;
+    const float le = lg[tt][e];
+    const float mx = wave_max(le);
+    const float ex = expf(le - mx);
+    const float sm = wave_sum(ex);
+    int rank = 0;
+#pragma unroll 4
+    for (int k = 0; k < E; ++k) {
+      const float lk = lg[tt][k];
+      rank += (lk > le || (lk == le && k < e)) ? 1 : 0;
+    }
+    if (rank < TOPK) {
+      a.ids[(size_t)(t0 + tt) * TOPK + rank] = e;
+      a.w[(size_t)(t0 + tt) * TOPK + rank] = ex / sm;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1897,7 +2010,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, void* z, i
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(router_kernel, dim3((a.T + RT_TB - 1) / RT_TB), dim3(256), 0, s, a);
+  // measured: 4-token VALU workgroups win up to about a thousand tokens, where
+  // re-reading W_r per workgroup starts to dominate and the 16-token MFMA
+  // workgroups take over
+  if (a.T >= 1024) hipLaunchKernelGGL(router_mfma_kernel, dim3((a.T + RM_TB - 1) / RM_TB), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(router_kernel, dim3((a.T + RT_TB - 1) / RT_TB), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
