@@ -271,36 +271,75 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMV arithmetic: exact integer dot products.  The input vector is written in
-// block floating point: a block of consecutive elements shares 2^e with
-// max|x| < 2^e, and each element becomes a signed integer mantissa
-// m = rint(x * 2^(F - e)), |m| <= 2^F, split into balanced digits (int4
-// weights: 5 base-16 digits in [-8, 7], F = 18; int8 weights: 3 base-256
-// digits in [-128, 127], F = 22).  v_dot8_i32_i4 / v_dot4_i32_i8 multiply the two's-complement
-// weight codes by one digit plane at a time with exact int32 sums; the planes
-// are recombined per scale group and the group's f32 scale and 2^(e - F) are
-// applied once.  The only rounding is that of m (at most 2^-(F+1) of 2^e,
-// i.e. 2^-F of the block maximum) and the f32 accumulation across groups.
+// GEMV arithmetic: exact integer products on the matrix cores.  A vector is
+// written in block floating point: a block of consecutive elements shares 2^e
+// with max|x| < 2^e, and each element becomes a signed integer mantissa
+// m = rint(x * 2^(XF - e)), |m| <= 2^XF, XF = 22, held as three balanced
+// base-256 digits d_p in [-128, 128): m = d_0 + 256 d_1 + 65536 d_2.  The
+// digits are int8, so v_mfma_i32_16x16x{64,32}_i8 multiplies them by int8
+// weight codes with exact int32 sums: the three digit planes are rows 0..2 of
+// the A operand and the 16 rows of a packed weight tile are the 16 columns of
+// B.  A 4-bit code enters B as 16 * code (its nibble moved to the top of an
+// int8), which the block unit absorbs (2^-4).  The planes are recombined in
+// f32 per scale group, f = C_0 + 256 C_1 + 65536 C_2, and the group's f32
+// scale applied once.  The only roundings are that of m (at most 2^-(XF+1) of
+// 2^e) and the f32 recombination and accumulation across groups.
 //
-// Plane layout (LDS, NW = 8 u32 words per group of 8 consecutive elements kg):
-//   int4: word j      = digit j of elements 8kg..8kg+7 in nibbles 0..7
-//   int8: word 2j + h = digit j of elements 8kg+4h..8kg+4h+3 in bytes 0..3
-// which matches the code order of a lane's word(s) in a packed tile.
+// Operand layout.  A lane l of a 16x16 product supplies A row l % 16 and
+// B column l % 16 for lane group q = l / 16, and the same K positions in both;
+// C[4 q + v][l % 16] comes back in register v of lane l, so lanes 0..15 hold
+// the three recombinable sums of weight row l % 16.  In a packed tile, lane
+// (r, q) holds row r at columns 32 c + 8 q + (0..7) of its word(s) of chunk c,
+// so one 64-column unit (x64 product) of a lane is chunks 0 and 1 of the unit:
+// the digits of A are stored in that same order.  int8 words are used as
+// they are; a 4-bit word splits into its even codes (one int8 operand word)
+// and its odd codes (another), so the A digits of each 8-element block are
+// stored even elements first.
 // ---------------------------------------------------------------------------
-template <int BITS> struct Digits {
-  static constexpr int ND = BITS == 4 ? 5 : 3;     // digit planes
-  static constexpr int F = BITS == 4 ? 18 : 22;    // mantissa magnitude bits
-  // m + OFF has the ordinary digits of m's balanced digits plus base/2
-  static constexpr uint32_t OFF = BITS == 4 ? 0x88888u : 0x808080u;
-  static constexpr uint32_t FLIP = BITS == 4 ? 0x88888888u : 0x80808080u;
-  static constexpr int NW = 8;                     // plane words per group of 8 elements (5 or 6 used)
-};
+constexpr int XF = 22;
+constexpr uint32_t XOFF = 0x808080u;   // m + XOFF has digits d_p + 128 (ordinary base-256 digits)
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// One thread per group of 8 elements (kg < n/8); blocks of `blk` elements
-// (blk / 8 consecutive threads, at most 16, all in one wave).
+__device__ __forceinline__ i32x4 mfma_x64(const i32x4& a, const i32x4& b, const i32x4& c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ i32x4 mfma_x32(uint64_t a, uint64_t b) {
+  const i32x4 z = {0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, z, 0, 0, 0);
+}
+__device__ __forceinline__ uint64_t pack64(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
+
+// int8 operand words of a 4-bit code word: 16 * even codes, 16 * odd codes
+__device__ __forceinline__ uint32_t even_codes(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t odd_codes(uint32_t w) { return w & 0xF0F0F0F0u; }
+
+// B operand of x64 unit u (0 or 1 for int4, 0 for int8) of a lane's tile words
 template <int BITS>
-__device__ __forceinline__ void make_planes(const float* x, float mul, int kg, int blk, uint32_t* xw, float* xs,
-                                            bool active) {
+__device__ __forceinline__ i32x4 unit_b(const uint4& v, int u) {
+  if (BITS == 8) return (i32x4){(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  const uint32_t w0 = word_of(v, 2 * u), w1 = word_of(v, 2 * u + 1);
+  return (i32x4){(int)even_codes(w0), (int)odd_codes(w0), (int)even_codes(w1), (int)odd_codes(w1)};
+}
+
+// f32 value of the three digit-plane sums in registers 0..2 of C
+__device__ __forceinline__ float digits_value(const i32x4& c) {
+  return fmaf(65536.0f, (float)c[2], (float)(c[0] + 256 * c[1]));
+}
+
+// Byte position of element i (0..7) of an 8-element block in an A operand
+template <int BITS>
+__device__ __forceinline__ int digit_pos(int i) {
+  return BITS == 4 ? ((i & 1) ? 4 + (i >> 1) : (i >> 1)) : i;
+}
+
+// Digits of the input vector x * mul for weights of BITS: thread kg < n/8 owns
+// elements 8kg..8kg+7; blocks of `blk` elements (blk / 8 consecutive lanes of
+// one wave) share an exponent.  xa: [unit k / 64][plane 0..3][q][4 words] (the
+// unused plane 3 is never written: it only feeds C rows that are not read);
+// xs[block] = 2^(e - XF) (2^(e - XF - 4) for int4: the 16x codes).
+template <int BITS>
+__device__ __forceinline__ void x_digits(const float* x, float mul, int kg, int blk, uint32_t* xa, float* xs,
+                                         bool active) {
   float v[8];
   float amax = 0.f;
   if (active) {
@@ -312,112 +351,24 @@ __device__ __forceinline__ void make_planes(const float* x, float mul, int kg, i
       amax = fmaxf(amax, fabsf(v[i]));
     }
   }
-  // block maximum over the blk / 8 lanes of the block (4, 8 or 16)
   amax = blk >= 128 ? group_max<16>(amax) : blk >= 64 ? group_max<8>(amax) : group_max<4>(amax);
   if (!active) return;
   int e;
   frexpf(amax, &e);                       // amax < 2^e (e = 0 when the block is zero)
-  constexpr int F = Digits<BITS>::F;
-  if ((kg & (blk / 8 - 1)) == 0) xs[(8 * kg) / blk] = ldexpf(1.0f, e - F);
-  // The balanced digits of m (each in [-base/2, base/2)) are the ordinary
-  // base-`base` digits of m + OFF, OFF = (base/2)(1 + base + ...), each minus
-  // base/2; as a two's-complement digit that is the ordinary digit with its
-  // top bit flipped.  |m| <= 2^F keeps m + OFF in [0, base^ND).
+  if ((kg & (blk / 8 - 1)) == 0) xs[(8 * kg) / blk] = ldexpf(1.0f, e - XF - (BITS == 4 ? 4 : 0));
   uint32_t M[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) M[i] = (uint32_t)((int)rintf(ldexpf(v[i], F - e)) + (int)Digits<BITS>::OFF);
-  constexpr int NW = Digits<BITS>::NW;
-  uint32_t w[NW];
-  if constexpr (BITS == 4) {
+  for (int i = 0; i < 8; ++i) M[i] = (uint32_t)((int)rintf(ldexpf(v[i], XF - e)) + (int)XOFF);
+  const int unit = kg >> 3, half = (kg >> 2) & 1, q = kg & 3;
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      uint32_t t = 0;
+  for (int p = 0; p < 3; ++p) {
+    uint32_t w[2] = {0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) t |= ((M[i] >> (4 * j)) & 15u) << (4 * i);
-      w[j] = t ^ Digits<BITS>::FLIP;
+    for (int i = 0; i < 8; ++i) {
+      const int pos = digit_pos<BITS>(i);
+      w[pos >> 2] |= ((M[i] >> (8 * p)) & 255u) << (8 * (pos & 3));
     }
-    w[5] = w[6] = w[7] = 0u;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t t = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t |= ((M[4 * hh + i] >> (8 * j)) & 255u) << (8 * i);
-        w[2 * j + hh] = t ^ Digits<BITS>::FLIP;
-      }
-    w[6] = w[7] = 0u;
-  }
-  *(uint4*)&xw[NW * kg] = make_uint4(w[0], w[1], w[2], w[3]);
-  *(uint4*)&xw[NW * kg + 4] = make_uint4(w[4], w[5], w[6], w[7]);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-template <int N>   // bitwise OR over groups of N in {4, 8} consecutive lanes
-__device__ __forceinline__ uint32_t group_or(uint32_t v) {
-  v |= dpp_u<DPP_XOR1>(v);
-  v |= dpp_u<DPP_XOR2>(v);
-  if (N >= 8) v |= dpp_u<DPP_HALF_MIRROR>(v);
-  return v;
-}
-
-// Digit planes of the 32 values of an item's slice (one block, one exponent),
-// one value per lane of a whole wave (lanes 32..63 pass 0): the same planes as
-// make_planes with blk = 32, built one element per lane and merged with OR.
-template <int BITS>
-__device__ __forceinline__ void slice_planes(float hv, int lane, uint32_t* hw, float* hs) {
-  constexpr int F = Digits<BITS>::F;
-  const float amax = wave_max(fabsf(hv));
-  int e;
-  frexpf(amax, &e);
-  if (lane == 0) *hs = ldexpf(1.0f, e - F);
-  const uint32_t M = (uint32_t)((int)rintf(ldexpf(hv, F - e)) + (int)Digits<BITS>::OFF);
-  if (BITS == 4) {
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      const uint32_t w = group_or<8>(((M >> (4 * j)) & 15u) << (4 * (lane & 7)));
-      if ((lane & 7) == 0 && lane < SLICE) hw[Digits<BITS>::NW * (lane >> 3) + j] = w ^ Digits<BITS>::FLIP;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const uint32_t w = group_or<4>(((M >> (8 * j)) & 255u) << (8 * (lane & 3)));
-      if ((lane & 3) == 0 && lane < SLICE)
-        hw[Digits<BITS>::NW * (lane >> 3) + 2 * j + ((lane >> 2) & 1)] = w ^ Digits<BITS>::FLIP;
-    }
-  }
-}
-
-// Per-plane integer partial sums of one lane's 8 codes (chunk c of its 16-byte
-// tile slice) against the matching plane words pw[0..NW).
-template <int BITS>
-__device__ __forceinline__ void dot_planes(const uint4& v, int c, const uint32_t* pw, int* P) {
-  if (BITS == 4) {
-    const int w = (int)word_of(v, c);
-#pragma unroll
-    for (int j = 0; j < 5; ++j) P[j] = __builtin_amdgcn_sdot8(w, (int)pw[j], P[j], false);
-  } else {
-    const int w0 = (int)word_of(v, 2 * c), w1 = (int)word_of(v, 2 * c + 1);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      P[j] = __builtin_amdgcn_sdot4(w0, (int)pw[2 * j], P[j], false);
-      P[j] = __builtin_amdgcn_sdot4(w1, (int)pw[2 * j + 1], P[j], false);
-    }
-  }
-}
-
-// Recombine the digit planes: sum_j base^j * P[j] (exact in int32 for int4).
-template <int BITS>
-__device__ __forceinline__ float planes_value(const int* P) {
-  if (BITS == 4) {
-    const int v = P[0] + (P[1] << 4) + (P[2] << 8) + (P[3] << 12) + (P[4] << 16);
-    return (float)v;
-  } else {
-    return (float)P[0] + 256.0f * ((float)P[1] + 256.0f * (float)P[2]);
+    *(uint2*)&xa[((unit * 4 + p) * 4 + q) * 4 + 2 * half] = make_uint2(w[0] ^ 0x80808080u, w[1] ^ 0x80808080u);
   }
 }
 
@@ -547,108 +498,107 @@ __device__ __forceinline__ void store_coherent_u32(uint32_t* p, uint32_t v) {
 }
 
 struct ItemLds {
-  uint32_t xw[(H / 8) * 8];   // digit planes of the layer input
-  float xs[H / 32];           // per-block unit 2^(e - F)
-  float gpart[8][64];         // per-wave, per-lane gate/up partial sums
-  float gu[64];               // gate (2x16) and up (2x16) totals
-  uint32_t hw[4 * 8];         // digit planes of h
-  float hs;
-  float dpart[H * 4];         // down partials: [row][lane group]
+  uint32_t xa[(H / 64) * 4 * 4 * 4];   // A-operand digits of the layer input: [unit][plane][q][4]
+  float xs[H / 32];                    // per-block unit of the input digits
+  float gpart[8][16];                  // per-wave gate/up sums of the wave's 16 rows (one K half)
+  uint32_t ha[4 * 4 * 2];              // A-operand digits of h: [plane][q][2]
+  float hs;                            // unit of the h digits (times 2^-4 for int4 codes)
+  float dout[H];                       // down rows of the item in units of hs
 };
 
-// Digit planes of the layer input z (in LDS) for weights of format (BITS, G).
+// Digits of the layer input z (in LDS) for weights of format (BITS, G).
 template <int BITS, int G>
 __device__ __forceinline__ void item_planes(const float* z, float mul, ItemLds& L) {
   const int tid = threadIdx.x;
-  make_planes<BITS>(z, mul, tid, G, L.xw, L.xs, tid < H / 8);
+  x_digits<BITS>(z, mul, tid, G, L.xa, L.xs, tid < H / 8);
   __syncthreads();
 }
 
-// z planes in L.xw/L.xs (item_planes) -> L.dpart (down partials per row and
-// lane group) and L.hs (the block unit of h).  Cross-lane sums go through LDS
-// in a fixed order.  Ends with a workgroup barrier.
+// Input digits in L.xa/L.xs (item_planes) -> L.dout (the item's down rows) and
+// L.hs.  Wave w multiplies the 16 gate/up rows of its n-tile over its K half
+// (x64 products, one scale group per G/64 of them; G = 32 splits each into two
+// x32 products), wave 0 forms h = SiLU(g) * u and its digits, then each wave
+// takes its down tiles (x32 products over the 32-column slice).  Ends with a
+// workgroup barrier.
 template <int BITS, int G>
 __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds& L) {
   using IR = ItemRegs<BITS, G>;
-  constexpr int ND = Digits<BITS>::ND, CPG = G / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, q = lane >> 4;
-  const int kb0 = (wv & 1) * IR::GU_TPW;
+  constexpr int UPT = BITS == 4 ? 2 : 1;          // x64 units per tile
+  constexpr int NU = IR::GU_TPW * UPT;            // units in a K half
+  constexpr int UPG = G >= 64 ? G / 64 : 1;       // units per scale group (G >= 64)
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, q = lane >> 4, pl = lane & 3;
+  const int u0 = (wv & 1) * NU;                   // first unit of the wave's K half
+  const i32x4 zero = {0, 0, 0, 0};
   float acc = 0.f;
-  int P[ND];
+  i32x4 C = zero;
 #pragma unroll
-  for (int j = 0; j < ND; ++j) P[j] = 0;
-#pragma unroll
-  for (int m = 0; m < IR::GU_TPW; ++m) {
-    // all plane words of this tile's chunks first (one LDS round trip per tile)
-    constexpr int NW = Digits<BITS>::NW;
-    uint32_t pw[IR::CPT][NW];
-#pragma unroll
-    for (int c = 0; c < IR::CPT; ++c) {
-      const int k0 = (kb0 + m) * IR::KB + 32 * c;
-      *(uint4*)&pw[c][0] = *(const uint4*)&L.xw[(k0 + 8 * q) / 8 * NW];
-      if (BITS == 8) *(uint4*)&pw[c][4] = *(const uint4*)&L.xw[(k0 + 8 * q) / 8 * NW + 4];
-      else pw[c][4] = L.xw[(k0 + 8 * q) / 8 * NW + 4];
-    }
-#pragma unroll
-    for (int c = 0; c < IR::CPT; ++c) {
-      const int ch = m * IR::CPT + c;              // chunk index within this wave's K half
-      dot_planes<BITS>(R.gu[m], c, pw[c], P);
-      if ((ch + 1) % CPG == 0) {                   // last chunk of a scale group
-        const int gl = ch / CPG;
-        acc = fmaf(R.gsc[gl] * L.xs[(kb0 * IR::KB) / G + gl], planes_value<BITS>(P), acc);
-#pragma unroll
-        for (int j = 0; j < ND; ++j) P[j] = 0;
+  for (int u = 0; u < NU; ++u) {
+    const uint32_t* ap = &L.xa[(((u0 + u) * 4 + pl) * 4 + q) * 4];
+    const i32x4 B = unit_b<BITS>(R.gu[u / UPT], u % UPT);
+    if (G >= 64) {
+      C = mfma_x64(*(const i32x4*)ap, B, u % UPG == 0 ? zero : C);
+      if (u % UPG == UPG - 1) {
+        const int gl = u / UPG;
+        acc = fmaf(R.gsc[gl] * L.xs[(u0 * 64) / G + gl], digits_value(C), acc);
       }
+    } else {
+      const uint4 a4 = *(const uint4*)ap;
+      const i32x4 c0 = mfma_x32(pack64(a4.x, a4.y), pack64((uint32_t)B[0], (uint32_t)B[1]));
+      const i32x4 c1 = mfma_x32(pack64(a4.z, a4.w), pack64((uint32_t)B[2], (uint32_t)B[3]));
+      acc = fmaf(R.gsc[2 * u] * L.xs[2 * u0 + 2 * u], digits_value(c0), acc);
+      acc = fmaf(R.gsc[2 * u + 1] * L.xs[2 * u0 + 2 * u + 1], digits_value(c1), acc);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
-  L.gpart[wv][lane] = acc;
+  if (lane < 16) L.gpart[wv][lane] = acc;
   __syncthreads();
-  if (tid < 64) {                       // wave 0: gate/up totals, h, and the planes of h
+  if (tid < 64) {                       // wave 0: h for the 32 slice columns and its digits
     float hv = 0.f;
-    if (tid < SLICE) {
-      const int ti = tid >> 4, rr = tid & 15;   // column 16 ti + rr of the slice
-      float g = 0.f, u = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          g += L.gpart[2 * ti + hh][16 * qq + rr];
-          u += L.gpart[4 + 2 * ti + hh][16 * qq + rr];
-        }
+    if (lane < SLICE) {
+      const int ti = lane >> 4, rr = lane & 15;   // column 16 ti + rr of the slice
+      const float g = L.gpart[2 * ti][rr] + L.gpart[2 * ti + 1][rr];
+      const float u = L.gpart[4 + 2 * ti][rr] + L.gpart[4 + 2 * ti + 1][rr];
       hv = silu_mul(g, u);
     }
-    slice_planes<BITS>(hv, tid, L.hw, &L.hs);
+    const float amax = wave_max(fabsf(hv));
+    int e;
+    frexpf(amax, &e);
+    if (lane == 0) L.hs = ldexpf(1.0f, e - XF - (BITS == 4 ? 4 : 0));
+    if (lane < SLICE) {
+      const uint32_t M = (uint32_t)((int)rintf(ldexpf(hv, XF - e)) + (int)XOFF);
+      uint8_t* hb = (uint8_t*)L.ha;
+      const int at = (lane >> 3) * 8 + digit_pos<BITS>(lane & 7);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) hb[p * 32 + at] = (uint8_t)(((M >> (8 * p)) & 255u) ^ 0x80u);
+    }
   }
   __syncthreads();
-  constexpr int NWH = Digits<BITS>::NW;
-  uint32_t pw[NWH];
-  *(uint4*)&pw[0] = *(const uint4*)&L.hw[NWH * q];
-  if (BITS == 8) *(uint4*)&pw[4] = *(const uint4*)&L.hw[NWH * q + 4];
-  else pw[4] = L.hw[NWH * q + 4];
+  const uint64_t Ah = *(const uint64_t*)&L.ha[(pl * 4 + q) * 2];
+  // all products first, then the recombination (lanes 0..15 hold the rows);
+  // the last tile of waves with one tile fewer is all zeros (range-checked loads)
+  float dv[IR::D_TPW][IR::RS];
 #pragma unroll
-  for (int m = 0; m < IR::D_TPW; ++m) {
-    const int rt = wv + 8 * m;
-    if (rt < IR::NRT) {
+  for (int m = 0; m < IR::D_TPW; ++m)
 #pragma unroll
-      for (int j = 0; j < IR::RS; ++j) {
-        int Pd[ND];
+    for (int j = 0; j < IR::RS; ++j) {
+      const uint64_t Bd = BITS == 4 ? pack64(even_codes(word_of(R.dn[m], j)), odd_codes(word_of(R.dn[m], j)))
+                                    : pack64(word_of(R.dn[m], 2 * j), word_of(R.dn[m], 2 * j + 1));
+      dv[m][j] = R.dns[m][j] * digits_value(mfma_x32(Ah, Bd));
+    }
+  if (lane < 16) {
 #pragma unroll
-        for (int d = 0; d < ND; ++d) Pd[d] = 0;
-        dot_planes<BITS>(R.dn[m], j, pw, Pd);
-        L.dpart[(IR::DR * rt + 16 * j + (lane & 15)) * 4 + q] = R.dns[m][j] * planes_value<BITS>(Pd);
+    for (int m = 0; m < IR::D_TPW; ++m) {
+      const int rt = wv + 8 * m;
+      if (m < IR::D_TPW - 1 || rt < IR::NRT) {
+#pragma unroll
+        for (int j = 0; j < IR::RS; ++j) L.dout[IR::DR * rt + 16 * j + lane] = dv[m][j];
       }
     }
   }
   __syncthreads();
 }
 
-// Final value of down row `row` of an item: coef * unit(h) * sum of the four
-// lane-group partials.
-__device__ __forceinline__ float item_row(const ItemLds& L, float cs, int row) {
-  const float4 p4 = *(const float4*)&L.dpart[4 * row];
-  return cs * ((p4.x + p4.y) + (p4.z + p4.w));
-}
+// Final value of down row `row` of an item: coef * unit(h) * its down sum.
+__device__ __forceinline__ float item_row(const ItemLds& L, float cs, int row) { return cs * L.dout[row]; }
 
 // One decode item end to end (loads, planes, compute), 1280 rows to out.
 template <int BITS, int G>
