@@ -735,7 +735,6 @@ struct ItemSide {
   float qs[N_RED * Q_STRIDE];
   float lg[E];            // logits
   int pick_e[TOPK];
-  float pick_w[TOPK];
 };
 struct ReducerSide {
   float red[N_ITEMS / 7][PART_U4 * 3];   // per item group, per row (42 slots, 40 used)
@@ -749,8 +748,8 @@ union ChainLds {
 
 // Wait for the reducer records of stage l, then rebuild this layer's input in
 // LDS (z = h, to be multiplied by the returned 1/rms) and, for routed items,
-// the routing.  Every workgroup runs identical arithmetic, so every item sees
-// the same z and the same picks.  The 512 threads work as 64 groups of 8
+// the picks (softmax_weight gives their weights).  Every workgroup runs identical
+// arithmetic, so every item sees the same z, picks and weights.  The 512 threads work as 64 groups of 8
 // (group e = expert e): logits and the sum of squares come from the 32 reducer
 // partials in a fixed order; the softmax is increasing in the logit, so the 6
 // largest logits (ties to the lower index) are the 6 largest probabilities.
@@ -806,11 +805,6 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const Lay
     if (sub == 0) S.lg[e] = lge;
     __syncthreads();
     MOE_TRACE(a, blockIdx.x, l, 7);
-    // every wave: max and softmax denominator over the 64 logits, lane i
-    // holding logit i (the same arithmetic in every wave and workgroup)
-    const float li = S.lg[tid & 63];
-    const float mx = wave_max(li);
-    const float sm = wave_sum(expf(li - mx));
     // rank of expert e among the 64 (ties to the lower index): 8 per lane
     int rank = 0;
 #pragma unroll
@@ -821,10 +815,8 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const Lay
     }
     rank = (int)group_sum<8>((float)rank);
     if (sub == 0 && rank < TOPK) {
-      const float pr = expf(lge - mx) / sm;
       S.pick_e[rank] = e;
-      S.pick_w[rank] = pr;
-      if (report) { a.ids[l * TOPK + rank] = e; a.tw[l * TOPK + rank] = pr; }
+      if (report) a.ids[l * TOPK + rank] = e;
     }
     __syncthreads();
   }
@@ -851,6 +843,17 @@ __device__ __forceinline__ void chain_item_store(const ChainArgs& a, const ItemL
   }
 }
 
+// Softmax weight of the logit of expert e among the 64 logits in S.lg (lane i
+// of every wave takes logit i: the same arithmetic in every wave and
+// workgroup).  Called by all lanes of a wave, after the pick's weight loads are
+// issued: only the final scaling of the item's partial needs it.
+__device__ __forceinline__ float softmax_weight(const ItemSide& S, int e) {
+  const float li = S.lg[threadIdx.x & 63];
+  const float mx = wave_max(li);
+  const float sm = wave_sum(expf(li - mx));
+  return expf(S.lg[e] - mx) / sm;
+}
+
 template <int BR, int GR>
 __device__ void chain_routed(const ChainArgs& a, const LayerPtrs* LP, ItemSide& S, int b, uint32_t base, uint32_t* err) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -864,11 +867,16 @@ __device__ void chain_routed(const ChainArgs& a, const LayerPtrs* LP, ItemSide& 
     ItemRegs<BR, GR> R;
     item_load<BR, GR>(R, LP[l].eq + (size_t)e * ebytes, LP[l].es + (size_t)e * escales, I, J, wv, lane);
     MOE_TRACE(a, b, l, 3);
+    const float coef = softmax_weight(S, e);
+    if (b == 0) {
+      const float wt = softmax_weight(S, S.pick_e[tid < TOPK ? tid : 0]);
+      if (tid < TOPK) a.tw[l * TOPK + tid] = wt;
+    }
     item_planes<BR, GR>(S.z, inv, S.item);
     MOE_TRACE(a, b, l, 13);
     item_compute<BR, GR>(R, S.item);
     MOE_TRACE(a, b, l, 4);
-    chain_item_store(a, S.item, S.pick_w[p] * S.item.hs, b, base + l + 1);
+    chain_item_store(a, S.item, coef * S.item.hs, b, base + l + 1);
     MOE_TRACE(a, b, l, 5);
   }
 }
@@ -940,13 +948,16 @@ __device__ void chain_reducer(const ChainArgs& a, const LayerPtrs* LP, ReducerSi
         for (int i = 0; i < 3; ++i) S.red[ig][3 * c + i] = acc[i];
       }
       __syncthreads();
-      if (tid < RED_ROWS) {
-        float vv = 0.f;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) vv += S.red[g][tid];
-        const float hv = (a.accumulate ? S.hrow[tid] : 0.f) + vv;
-        S.hrow[tid] = hv;
-        S.rec[tid] = hv;
+      // row r = t / 8: groups k, k + 8, k + 16, k + 24 (k = t % 8), then over the 8 lanes
+      if (tid < RED_ROWS * 8) {
+        const int row = tid >> 3, k = tid & 7;
+        float vv = (S.red[k][row] + S.red[k + 8][row]) + (S.red[k + 16][row] + S.red[k + 24][row]);
+        vv = group_sum<8>(vv);
+        if (k == 0) {
+          const float hv = (a.accumulate ? S.hrow[row] : 0.f) + vv;
+          S.hrow[row] = hv;
+          S.rec[row] = hv;
+        }
       }
     }
     __syncthreads();
