@@ -704,23 +704,32 @@ __device__ __forceinline__ void wait_first(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 // Load the tagged words at off[m] (where valid[m]) and poll until every one
 // carries `tag` (after wait_first this usually takes one round trip).
+// Branch-free: every round issues all N loads back to back, a word that is
+// not wanted (invalid, or already carrying the tag) at an offset past the end
+// of the buffer, which returns zeros without a memory access; a conditional
+// load would be followed by a wait of its own, serialising the round.
 // Wave-uniform exit; a wait that runs out sets the error word.
 template <int N>
 __device__ __forceinline__ void load_tagged(__amdgpu_buffer_rsrc_t r, const uint32_t* off, const bool* valid,
                                             u32x4* v, uint32_t tag, long& spins, uint32_t* err) {
+  constexpr uint32_t SKIP = 0x80000000u;
+  bool need[N];
 #pragma unroll
-  for (int m = 0; m < N; ++m)
-    if (valid[m]) v[m] = load16_coherent(r, off[m]);
+  for (int m = 0; m < N; ++m) need[m] = valid[m];
   while (true) {
+    u32x4 nv[N];
+#pragma unroll
+    for (int m = 0; m < N; ++m) nv[m] = load16_coherent(r, need[m] ? off[m] : SKIP);
     bool done = true;
 #pragma unroll
-    for (int m = 0; m < N; ++m)
-      if (valid[m] && v[m][3] != tag) done = false;
+    for (int m = 0; m < N; ++m) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[m][k] = need[m] ? nv[m][k] : v[m][k];
+      need[m] = need[m] && v[m][3] != tag;
+      done = done && !need[m];
+    }
     if (__all(done)) break;
     __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-    for (int m = 0; m < N; ++m)
-      if (valid[m] && v[m][3] != tag) v[m] = load16_coherent(r, off[m]);
     if (++spins > SPIN_LIMIT) {
       if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
