@@ -765,6 +765,11 @@ union ChainLds {
 __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const LayerPtrs* LP, ItemSide& S, int l,
                                                    uint32_t epoch, bool routed, bool report, uint32_t* err) {
   const int tid = threadIdx.x;
+  // the router bias of this thread's expert, requested before the wait (a
+  // layer without bias reads zeros through an empty buffer range)
+  const float* bias = LP[l].bias;
+  const float bias_e = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      coherent_rsrc(bias, bias ? E * 4 : 0), (uint32_t)(tid >> 3) * 4, 0, 0));
   {
     constexpr int NR = N_RED * REC_U4;          // 1120 words
     constexpr int PT = (NR + 511) / 512;        // 3 per thread
@@ -809,8 +814,7 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const Lay
   sq = group_sum<8>(sq);
   const float inv = a.norm ? 1.0f / sqrtf(sq / (float)H + a.eps) : 1.0f;
   if (routed) {
-    const float* bias = LP[l].bias;
-    const float lge = part * inv + (bias ? bias[e] : 0.f);
+    const float lge = part * inv + bias_e;
     if (sub == 0) S.lg[e] = lge;
     __syncthreads();
     MOE_TRACE(a, blockIdx.x, l, 7);
