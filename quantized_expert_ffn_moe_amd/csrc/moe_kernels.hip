@@ -104,7 +104,11 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// SiLU(g) * u with the hardware exp2 and reciprocal (about 1 ulp each; the
+// decode step has it on the path between its gate/up and down products)
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * g)) * u;
+}
 
 // RMSNorm pieces shared by the router and the standalone norm so that both
 // produce bit-identical z: thread tid owns features tid + 256 i (i < 5).
@@ -501,7 +505,7 @@ struct ItemLds {
   uint32_t xa[(H / 64) * 4 * 4 * 4];   // A-operand digits of the layer input: [unit][plane][q][4]
   float xs[H / 32];                    // per-block unit of the input digits
   float gpart[8][16];                  // per-wave gate/up sums of the wave's 16 rows (one K half)
-  uint32_t ha[4 * 4 * 2];              // A-operand digits of h: [plane][q][2]
+  uint32_t ha[8][4 * 4 * 2];           // per wave: A-operand digits of h: [plane][q][2]
   float hs;                            // unit of the h digits (times 2^-4 for int4 codes)
   float dout[H];                       // down rows of the item in units of hs
 };
@@ -517,7 +521,7 @@ __device__ __forceinline__ void item_planes(const float* z, float mul, ItemLds& 
 // Input digits in L.xa/L.xs (item_planes) -> L.dout (the item's down rows) and
 // L.hs.  Wave w multiplies the 16 gate/up rows of its n-tile over its K half
 // (x64 products, one scale group per G/64 of them; G = 32 splits each into two
-// x32 products), wave 0 forms h = SiLU(g) * u and its digits, then each wave
+// x32 products), every wave forms h = SiLU(g) * u and its digits, then each wave
 // takes its down tiles (x32 products over the 32-column slice).  Ends with a
 // workgroup barrier.
 template <int BITS, int G>
@@ -551,7 +555,11 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds
   }
   if (lane < 16) L.gpart[wv][lane] = acc;
   __syncthreads();
-  if (tid < 64) {                       // wave 0: h for the 32 slice columns and its digits
+  // every wave: h for the 32 slice columns and its digits, into its own copy
+  // of the A operand (identical arithmetic in every wave; a wave reads back its
+  // own LDS writes in order, so no workgroup barrier is needed)
+  uint64_t Ah;
+  {
     float hv = 0.f;
     if (lane < SLICE) {
       const int ti = lane >> 4, rr = lane & 15;   // column 16 ti + rr of the slice
@@ -562,17 +570,16 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds
     const float amax = wave_max(fabsf(hv));
     int e;
     frexpf(amax, &e);
-    if (lane == 0) L.hs = ldexpf(1.0f, e - XF - (BITS == 4 ? 4 : 0));
+    if (tid == 0) L.hs = ldexpf(1.0f, e - XF - (BITS == 4 ? 4 : 0));
+    uint8_t* hb = (uint8_t*)L.ha[wv];
     if (lane < SLICE) {
       const uint32_t M = (uint32_t)((int)rintf(ldexpf(hv, XF - e)) + (int)XOFF);
-      uint8_t* hb = (uint8_t*)L.ha;
       const int at = (lane >> 3) * 8 + digit_pos<BITS>(lane & 7);
 #pragma unroll
       for (int p = 0; p < 3; ++p) hb[p * 32 + at] = (uint8_t)(((M >> (8 * p)) & 255u) ^ 0x80u);
     }
+    Ah = *(const uint64_t*)&L.ha[wv][(pl * 4 + q) * 2];
   }
-  __syncthreads();
-  const uint64_t Ah = *(const uint64_t*)&L.ha[(pl * 4 + q) * 2];
   // all products first, then the recombination (lanes 0..15 hold the rows);
   // the last tile of waves with one tile fewer is all zeros (range-checked loads)
   float dv[IR::D_TPW][IR::RS];
@@ -812,7 +819,9 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const Lay
   }
   part = group_sum<8>(part);
   sq = group_sum<8>(sq);
-  const float inv = a.norm ? 1.0f / sqrtf(sq / (float)H + a.eps) : 1.0f;
+  // 1/rms with the hardware reciprocal square root (about 1 ulp): this sits on
+  // the path from the records to the routed weight loads of every layer
+  const float inv = a.norm ? __builtin_amdgcn_rsqf(sq * (1.0f / H) + a.eps) : 1.0f;
   if (routed) {
     const float lge = part * inv + bias_e;
     if (sub == 0) S.lg[e] = lge;
