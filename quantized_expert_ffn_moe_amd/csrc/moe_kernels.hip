@@ -130,9 +130,9 @@ __device__ __forceinline__ float inv_rms(const float* red4, float eps) {
 // per-thread sums and reduction order as the standalone RMSNorm, so both give
 // bit-identical z) into LDS and to z; pass 2: 16 lanes per expert row read
 // W_r in coalesced float4 runs (the 327 KB matrix stays in L2) against z from
-// LDS and add up across the 16 lanes in a fixed order.  The selection
-// ranks every expert against the others: the softmax is increasing in the
-// logit, so the 6 largest logits (ties to the lower index) are the 6 largest
+// LDS and add up across the 16 lanes in a fixed order.  The selection takes
+// the largest remaining logit six times (ties to the lower index): the
+// softmax is increasing in the logit, so these are the 6 largest
 // probabilities.
 // ---------------------------------------------------------------------------
 // Pass 1 of both routers (256 threads): the TB rows of x starting at token t0
@@ -184,16 +184,31 @@ __device__ __forceinline__ void router_rows(const RouterArgs& a, int t0, float* 
   }
   __syncthreads();
   if (!a.norm) return;
+  // all rows' per-thread sums first, then the wave reductions (independent
+  // chains the scheduler interleaves); the same sums in the same order as the
+  // standalone RMSNorm
+  float ssr[TB];
+#pragma unroll
   for (int tt = 0; tt < TB; ++tt) {
     float v[5];
 #pragma unroll
     for (int i = 0; i < 5; ++i) v[i] = zs[tt * ROW + tid + 256 * i];
-    const float ss = wave_sum(thread_sumsq(v));
+    ssr[tt] = thread_sumsq(v);
+  }
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt) {
+    const float ss = wave_sum(ssr[tt]);
     if (lane == 0) red[tt * 4 + wv] = ss;
   }
   __syncthreads();
+  // 1/rms of row tt once, by thread tt, into red[tt][0]
+  float invt = 0.f;
+  if (tid < nt) invt = inv_rms(&red[tid * 4], a.eps);
+  __syncthreads();
+  if (tid < nt) red[tid * 4] = invt;
+  __syncthreads();
   for (int tt = 0; tt < nt; ++tt) {
-    const float inv = inv_rms(&red[tt * 4], a.eps);
+    const float inv = red[tt * 4];
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int k = tid + 256 * i;
@@ -208,6 +223,29 @@ __device__ __forceinline__ void router_rows(const RouterArgs& a, int t0, float* 
     }
   }
   __syncthreads();
+}
+
+// Greedy top-6 of one token's 64 logits, lane = expert (all lanes active):
+// six rounds of "largest remaining logit, lowest index among equals", which
+// is the order of the 6 largest softmax probabilities (the softmax is
+// increasing).  Lane e_j writes pick j: its expert id and exp(l - max) / sum.
+__device__ __forceinline__ void select_top6(float le, int32_t* ids, float* w) {
+  const int lane = threadIdx.x & 63;
+  const float mx = wave_max(le);
+  const float ex = expf(le - mx);
+  const float sm = wave_sum(ex);
+  float rem = le;
+#pragma unroll
+  for (int j = 0; j < TOPK; ++j) {
+    const float m = wave_max(rem);
+    const uint64_t hit = __ballot(rem == m);
+    const int ej = (int)__builtin_ctzll(hit);
+    if (lane == ej) {
+      ids[j] = lane;
+      w[j] = ex / sm;
+      rem = -__builtin_inff();
+    }
+  }
 }
 
 constexpr int RT_TB = 4;       // tokens per workgroup
@@ -253,25 +291,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   }
   __syncthreads();
   // selection: wave = token, lane = expert
-  {
-    const int tt = wv, e = lane;
-    if (tt < nt) {
-      const float le = lg[tt][e];
-      const float mx = wave_max(le);
-      const float ex = expf(le - mx);
-      const float sm = wave_sum(ex);
-      int rank = 0;
-#pragma unroll 4
-      for (int k = 0; k < E; ++k) {
-        const float lk = lg[tt][k];
-        rank += (lk > le || (lk == le && k < e)) ? 1 : 0;
-      }
-      if (rank < TOPK) {
-        a.ids[(size_t)(t0 + tt) * TOPK + rank] = e;
-        a.w[(size_t)(t0 + tt) * TOPK + rank] = ex / sm;
-      }
-    }
-  }
+  if (wv < nt) select_top6(lg[wv][lane], a.ids + (size_t)(t0 + wv) * TOPK, a.w + (size_t)(t0 + wv) * TOPK);
 }
 
 // ---------------------------------------------------------------------------
@@ -1120,23 +1140,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
   }
   __syncthreads();
   // selection: wave w handles tokens w, w + 4, w + 8, w + 12; lane = expert
-  for (int tt = wv; tt < nt; tt += 4) {
-    const int e = lane;
-    const float le = lg[tt][e];
-    const float mx = wave_max(le);
-    const float ex = expf(le - mx);
-    const float sm = wave_sum(ex);
-    int rank = 0;
-#pragma unroll 4
-    for (int k = 0; k < E; ++k) {
-      const float lk = lg[tt][k];
-      rank += (lk > le || (lk == le && k < e)) ? 1 : 0;
-    }
-    if (rank < TOPK) {
-      a.ids[(size_t)(t0 + tt) * TOPK + rank] = e;
-      a.w[(size_t)(t0 + tt) * TOPK + rank] = ex / sm;
-    }
-  }
+  for (int tt = wv; tt < nt; tt += 4)
+    select_top6(lg[tt][lane], a.ids + (size_t)(t0 + tt) * TOPK, a.w + (size_t)(t0 + tt) * TOPK);
 }
 
 // ---------------------------------------------------------------------------
