@@ -1236,28 +1236,27 @@ __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(
 // every nibble into n = code + 8; 0x6400 | n is the f16 value 1024 + n, and
 // 0x6400 | (n << 4) is 1024 + 16n.
 __device__ __forceinline__ half8 unpack_int4(uint32_t w) {
-  w ^= 0x88888888u;
+  // (nibble ^ 8) = code + 8 under the f16 exponent of 1024: one AND-XOR per
+  // pair (the XOR also sets the exponent bits, which the AND cleared)
   const half2v m1032 = {(_Float16)-1032.f, (_Float16)-1032.f};
   const half2v m72 = {(_Float16)-72.f, (_Float16)-72.f};
   const half2v inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
   const uint32_t w8 = w >> 8;
-  const half2v a = as_h2((w & 0x000F000Fu) | 0x64006400u) + m1032;
-  const half2v b = as_h2((w & 0x00F000F0u) | 0x64006400u) * inv16 + m72;
-  const half2v c = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + m1032;
-  const half2v d = as_h2((w8 & 0x00F000F0u) | 0x64006400u) * inv16 + m72;
+  const half2v a = as_h2((w & 0x000F000Fu) ^ 0x64086408u) + m1032;
+  const half2v b = as_h2((w & 0x00F000F0u) ^ 0x64806480u) * inv16 + m72;
+  const half2v c = as_h2((w8 & 0x000F000Fu) ^ 0x64086408u) + m1032;
+  const half2v d = as_h2((w8 & 0x00F000F0u) ^ 0x64806480u) * inv16 + m72;
   return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 // two int8 words (codes k0..k3, k4..k7 in bytes, two's complement) -> exact
-// f16 codes in order [k0, k2, k1, k3, k4, k6, k5, k7] (XOR: byte = code + 128).
+// f16 codes in order [k0, k2, k1, k3, k4, k6, k5, k7] (byte ^ 0x80 = code + 128).
 __device__ __forceinline__ half8 unpack_int8(uint32_t w0, uint32_t w1) {
-  w0 ^= 0x80808080u;
-  w1 ^= 0x80808080u;
   const half2v m1152 = {(_Float16)-1152.f, (_Float16)-1152.f};
-  const half2v a = as_h2((w0 & 0x00FF00FFu) | 0x64006400u) + m1152;
-  const half2v b = as_h2(((w0 >> 8) & 0x00FF00FFu) | 0x64006400u) + m1152;
-  const half2v c = as_h2((w1 & 0x00FF00FFu) | 0x64006400u) + m1152;
-  const half2v d = as_h2(((w1 >> 8) & 0x00FF00FFu) | 0x64006400u) + m1152;
+  const half2v a = as_h2((w0 & 0x00FF00FFu) ^ 0x64806480u) + m1152;
+  const half2v b = as_h2(((w0 >> 8) & 0x00FF00FFu) ^ 0x64806480u) + m1152;
+  const half2v c = as_h2((w1 & 0x00FF00FFu) ^ 0x64806480u) + m1152;
+  const half2v d = as_h2(((w1 >> 8) & 0x00FF00FFu) ^ 0x64806480u) + m1152;
   return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
