@@ -1371,6 +1371,24 @@ __device__ __forceinline__ void fetch_a(AStage<F32>& A, __amdgpu_buffer_rsrc_t r
   }
 }
 
+// The same for an A whose 8-element groups are stored as f16 hi8 then lo8,
+// already in operand order (the grouped gate/up output): a copy.
+__device__ __forceinline__ void store_a_h16(_Float16* lds, const AStage<true>& A) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < A_SEG; ++j) {
+    const int seg = tid + GT * j, row = seg >> 4, kk = 8 * (seg & 15);
+    *(uint4*)(lds + row * LDS_ROW + kk) = A.raw[j][0];
+    *(uint4*)(lds + MT * LDS_ROW + row * LDS_ROW + kk) = A.raw[j][1];
+  }
+}
+
+// Position of element k (0..7) of an 8-element group in the operand order
+// (the inverse of perm_k).
+template <int BITS> __device__ __forceinline__ int perm_pos(int k) {
+  return BITS == 4 ? (((k & 3) << 1) | (k >> 2)) : ((k & 4) | ((k & 1) << 1) | ((k >> 1) & 1));
+}
+
 // A plane layout in LDS: [row][LDS_ROW] f16 (hi), then the lo plane.
 template <int BITS, bool F32, bool SPLIT>
 __device__ __forceinline__ void store_a(_Float16* lds, const AStage<F32>& A) {
@@ -1565,21 +1583,39 @@ __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
     step(st, R0, R1, 0);
     step(st + 1, R1, R0, 1);
   }
+  // h = SiLU(gate) * up as f16 hi/lo pairs per 8-column group in the down
+  // tiles' operand order (h16 layout), staged in LDS (the A buffers are free)
+  // and written as whole 16-byte runs: [64 rows][16 groups][hi8, lo8].
+  __syncthreads();
+  _Float16* hs = &lds_a[0][0];
+  static_assert(sizeof(lds_a) >= MT * 128 * 4, "h staging fits the A buffers");
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int m = 16 * ms + 4 * q4 + k;
-      if (m < ti.nrows) {
-        const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
-        a.out[orow * inter + 16 * nt + r] = silu_mul(acc[0][ms][k], acc[1][ms][k]);
-      }
+      const int m = 16 * ms + 4 * q4 + k, cl = 16 * wv + r;
+      const float x = silu_mul(acc[0][ms][k], acc[1][ms][k]);
+      const _Float16 xh = (_Float16)x;
+      _Float16* g = hs + (m * 16 + (cl >> 3)) * 16;
+      const int p = perm_pos<BITS>(cl & 7);
+      g[p] = xh;
+      g[8 + p] = (_Float16)(x - (float)xh);
     }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < MT * 32 / GT; ++j) {
+    const int u = tid + GT * j, m = u >> 5, c16 = u & 31;
+    if (m < ti.nrows) {
+      const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
+      *(uint4*)((char*)a.out + (orow * inter + 128 * cb) * 4 + c16 * 16) = *(const uint4*)(hs + (m * 16) * 16 + c16 * 8);
+    }
+  }
 }
 
 // Down: output block cb covers rows 256 cb .. 256 cb + 255 of W_d (output
 // columns of the layer), i.e. NRTB packed row tiles of DR rows; wave (wm, wn)
-// owns 64 of them (four 16-row n-subtiles).  A = h in f32 (hi and lo planes).
+// owns 64 of them (four 16-row n-subtiles).  A = h as the f16 hi/lo pairs the
+// grouped gate/up kernel writes, copied to LDS as they are.
 // B per stage: 4 K-chunks of 32 x NRTB row tiles.
 template <int BITS, int G, int INTER>
 __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
@@ -1639,7 +1675,7 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
     }
   };
   auto put = [&](const Stage& R, int buf) {
-    store_a<BITS, true, true>(lds_a[buf], R.A);
+    store_a_h16(lds_a[buf], R.A);
 #pragma unroll
     for (int k = 0; k < BU; ++k) lds_b[buf][tid + GT * k] = R.B[k];
   };
