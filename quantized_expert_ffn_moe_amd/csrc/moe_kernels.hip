@@ -1282,7 +1282,7 @@ constexpr int LDS_ROW = KS + 8;     // f16 per LDS row (16-byte pad against bank
 // flight precisely.
 template <int MTL, bool F32>
 struct AStageS {
-  static constexpr int NSEG = MTL / 16;
+  static constexpr int NSEG = MTL / 16;       // segments per thread with 256 threads
   uint4 raw[NSEG][F32 ? 2 : 1];
 };
 
@@ -1760,22 +1760,22 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
     }
 }
 
-// Small tiles (few rows per expert): gate/up, a workgroup of 4 waves owns one
-// 32-row tile of one expert and 128
-// intermediate columns; wave w computes gate and up for columns 32w..32w+31
-// of them (n-subtiles 8cb + 2w, 8cb + 2w + 1 of both matrices) and writes
-// h = SiLU(gate) * up.  Software pipeline over K stages of 128: the packed B
+// Small tiles (few rows per expert): gate/up, a workgroup of 8 waves owns one
+// 32-row tile of one expert and 128 intermediate columns; wave w computes
+// gate and up for columns 16w..16w+15 of them (n-subtile 8cb + w of both
+// matrices) and writes h = SiLU(gate) * up.  Software pipeline over K stages of 128: the packed B
 // tiles and their group scales are fetched D stages ahead into a register
 // ring, A two stages ahead into registers and one stage ahead into a double
 // buffer in LDS, so that the memory latency hides behind the MFMA work.
 template <int BITS, bool SPLIT, int G>
-__global__ __launch_bounds__(256) void gateup_small_kernel(GroupedArgs a) {
+__global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
   constexpr int MTL = MT_SMALL;
   constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MTL / 16;
   constexpr int CPG = G / 32, GPS = KS / G, NG = H / G;
-  constexpr int D = BITS == 4 ? 3 : 2;      // B stages in flight
+  constexpr int D = BITS == 4 ? 4 : 3;      // B stages in flight
   constexpr bool F32 = SPLIT;
   constexpr int APL = SPLIT ? 2 : 1;
+  constexpr int NSEG = MTL * KS / 8 / 512;  // A segments per thread (1)
   const int inter = a.w.inter, ncb = inter / 128;
   const int tile = blockIdx.x / ncb, cb = blockIdx.x % ncb;
   const TileInfo ti = tile_info(a, tile, MTL);
@@ -1793,58 +1793,94 @@ __global__ __launch_bounds__(256) void gateup_small_kernel(GroupedArgs a) {
   const uint8_t* eq = a.w.q + (size_t)e * a.w.e_bytes;
   const float* es = a.w.s + (size_t)e * a.w.e_scales;
   const size_t mbytes = matrix_bytes(BITS, inter, H), mscales = (size_t)inter * NG;
-  // B tiles of this wave: i = 0,1 gate n-subtiles, 2,3 up n-subtiles; each
-  // descriptor spans one n-tile's row of K tiles (later stages read zeros)
-  __amdgpu_buffer_rsrc_t rb[4], rs[4];
+  // B tiles of this wave: n-subtile 8 cb + w of the gate (i = 0) and the up
+  // (i = 1) matrix; each descriptor spans one n-tile's row of K tiles
+  const int nt = 8 * cb + wv;
+  __amdgpu_buffer_rsrc_t rb[2], rs[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nt = 8 * cb + 2 * wv + (i & 1);
-    rb[i] = weight_rsrc(eq + (i >> 1) * mbytes + (size_t)nt * NKB * TILE, NKB * TILE);
-    rs[i] = weight_rsrc(es + (i >> 1) * mscales + (size_t)16 * nt * NG, 16 * NG * 4);
+  for (int i = 0; i < 2; ++i) {
+    rb[i] = weight_rsrc(eq + i * mbytes + (size_t)nt * NKB * TILE, NKB * TILE);
+    rs[i] = weight_rsrc(es + i * mscales + (size_t)16 * nt * NG, 16 * NG * 4);
   }
   const __amdgpu_buffer_rsrc_t ra =
       weight_rsrc(F32 ? (const void*)a.af : (const void*)a.ab, (uint32_t)a.a_rows * H * (F32 ? 4 : 2));
 
-  uint4 bq[D][4][NB];
-  float sq[D][4][GPS];
-  auto load_b = [&](uint4 (&bd)[4][NB], float (&sd)[4][GPS], int st) {
+  uint4 bq[D][2][NB];
+  float sq[D][2][GPS];
+  auto load_b = [&](uint4 (&bd)[2][NB], float (&sd)[2][GPS], int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int g = 0; g < GPS; ++g) sd[i][g] = wload4(rs[i], (uint32_t)(r * NG + st * GPS + g) * 4);
 #pragma unroll
       for (int h = 0; h < NB; ++h) bd[i][h] = wload16(rb[i], (uint32_t)(st * NB + h) * TILE + lane * 16);
     }
   };
-  float4v acc[4][MS], ctmp[4][MS];
+  // A: one 8-element segment per thread per stage (row tid / 16, columns 8 (tid % 16))
+  auto fetch_a1 = [&](uint4 (&ar)[APL], int k0, bool live) {
+    const int row = tid >> 4, kk = 8 * (tid & 15);
+    const int src = arow[row];
+    constexpr uint32_t ELT = F32 ? 4 : 2;
+    const uint32_t off = (live && src >= 0) ? ((uint32_t)src * H + k0 + kk) * ELT : 0x80000000u;
+    ar[0] = wload16(ra, off);
+    if (F32) ar[APL - 1] = wload16(ra, off + 16);
+  };
+  auto store_a1 = [&](_Float16* l, const uint4 (&ar)[APL]) {
+    const int row = tid >> 4, kk = 8 * (tid & 15);
+    float v[8];
+    if (F32) {
+      const uint4 a0 = ar[0], a1 = ar[APL - 1];
+      v[0] = __uint_as_float(a0.x); v[1] = __uint_as_float(a0.y); v[2] = __uint_as_float(a0.z); v[3] = __uint_as_float(a0.w);
+      v[4] = __uint_as_float(a1.x); v[5] = __uint_as_float(a1.y); v[6] = __uint_as_float(a1.z); v[7] = __uint_as_float(a1.w);
+    } else {
+      const uint32_t uw[4] = {ar[0].x, ar[0].y, ar[0].z, ar[0].w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(uw[i] << 16);
+        v[2 * i + 1] = __uint_as_float(uw[i] & 0xFFFF0000u);
+      }
+    }
+    half8 hi, lo;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const float x = v[perm_k<BITS>(p)];
+      const _Float16 xh = (_Float16)x;
+      hi[p] = xh;
+      lo[p] = (_Float16)(x - (float)xh);
+    }
+    *(half8*)(l + row * LDS_ROW + kk) = hi;
+    if (SPLIT) *(half8*)(l + MTL * LDS_ROW + row * LDS_ROW + kk) = lo;
+  };
+  static_assert(NSEG == 1, "one A segment per thread");
+  float4v acc[2][MS], ctmp[2][MS];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) { acc[i][ms] = float4v{0, 0, 0, 0}; ctmp[i][ms] = float4v{0, 0, 0, 0}; }
   __syncthreads();   // arow
 
   // Fully unrolled stage loop: every ring slot is a fixed register set, so no
   // value is copied while its load is still in flight.
-  AStageS<MTL, F32> A[3];   // A(s) lives in slot s % 3 until it is stored to LDS
+  uint4 A[3][APL];   // A(s) lives in slot s % 3 until it is stored to LDS
 #pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0) fetch_a_s<MTL, F32>(A[s0], ra, arow, H, s0 * KS, s0 < NSTAGE);
+  for (int s0 = 0; s0 < 3; ++s0) fetch_a1(A[s0], s0 * KS, s0 < NSTAGE);
 #pragma unroll
   for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
-  store_a_s<BITS, MTL, F32, SPLIT>(lds[0], A[0]);
+  store_a1(lds[0], A[0]);
 
 #pragma unroll
   for (int st = 0; st < NSTAGE; ++st) {
     __syncthreads();   // lds[st & 1] holds A(st); lds[(st + 1) & 1] is free
-    if (st + 1 < NSTAGE) store_a_s<BITS, MTL, F32, SPLIT>(lds[(st + 1) & 1], A[(st + 1) % 3]);
-    if (st + 3 < NSTAGE) fetch_a_s<MTL, F32>(A[st % 3], ra, arow, H, (st + 3) * KS, true);
+    if (st + 1 < NSTAGE) store_a1(lds[(st + 1) & 1], A[(st + 1) % 3]);
+    if (st + 3 < NSTAGE) fetch_a1(A[st % 3], (st + 3) * KS, true);
     const _Float16* la = lds[st & 1];
     const int sl = st % D;
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
       const bool first = (c % CPG) == 0, last = (c % CPG) == CPG - 1;
-      half8 bfr[4];
+      half8 bfr[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         if (BITS == 4) bfr[i] = unpack_int4(word_of(bq[sl][i][0], c));
         else bfr[i] = unpack_int8(word_of(bq[sl][i][c >> 1], 2 * (c & 1)), word_of(bq[sl][i][c >> 1], 2 * (c & 1) + 1));
       }
@@ -1855,7 +1891,7 @@ __global__ __launch_bounds__(256) void gateup_small_kernel(GroupedArgs a) {
         half8 alo;
         if (SPLIT) alo = *(const half8*)(la + MTL * LDS_ROW + lrow * LDS_ROW + lcol);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
           float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[i][ms];
           cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bfr[i], cc, 0, 0, 0);
           if (SPLIT) cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bfr[i], cc, 0, 0, 0);
@@ -1864,7 +1900,7 @@ __global__ __launch_bounds__(256) void gateup_small_kernel(GroupedArgs a) {
       }
       if (last) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
           const float sv = sq[sl][i][c / CPG];
 #pragma unroll
           for (int ms = 0; ms < MS; ++ms) acc[i][ms] += sv * ctmp[i][ms];
@@ -1880,9 +1916,7 @@ __global__ __launch_bounds__(256) void gateup_small_kernel(GroupedArgs a) {
       const int m = ms * 16 + 4 * q4 + k;
       if (m < ti.nrows) {
         const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          a.out[orow * inter + 16 * (8 * cb + 2 * wv + j) + r] = silu_mul(acc[j][ms][k], acc[2 + j][ms][k]);
+        a.out[orow * inter + 16 * nt + r] = silu_mul(acc[0][ms][k], acc[1][ms][k]);
       }
     }
 }
@@ -2108,8 +2142,8 @@ template <int BITS, int G>
 static void gateup_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
   if (small) {
     const dim3 grid(max_tiles * (a.w.inter / 128));
-    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<BITS, true, G>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gateup_small_kernel<BITS, false, G>), grid, dim3(256), 0, s, a);
+    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<BITS, true, G>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gateup_small_kernel<BITS, false, G>), grid, dim3(512), 0, s, a);
   } else {
     const dim3 grid(max_tiles * (a.w.inter / 128));   // 128 gate + 128 up columns per workgroup
     if (a.af) hipLaunchKernelGGL((grouped_gateup_kernel<BITS, true, G>), grid, dim3(GT), 0, s, a);
