@@ -1921,17 +1921,18 @@ __global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
     }
 }
 
-// Small tiles: down, a workgroup owns one 32-row tile of A (h, fp32 split hi/lo) and four
-// packed down tiles' worth of output rows: wave w covers row tile 4cb + w,
-// i.e. 64 (int4) or 32 (int8) output columns, one 16-column MFMA n-subtile
-// per 16 rows.  Each 16-byte lane load of a down tile feeds every n-subtile of
-// the row tile for one 32-wide K chunk.  Same software pipeline as gate/up.
+// Small tiles: down, a workgroup of 8 waves owns one 32-row tile of A (h,
+// fp32 split hi/lo) and four packed down tiles' worth of output rows: waves
+// 2i and 2i + 1 share row tile 4cb + i (64 int4 or 32 int8 output columns),
+// each taking half of its 16-row n-subtiles (the matching half of every
+// 16-byte lane word).  Same software pipeline as gate/up.
 template <int BITS, int G, int INTER>
-__global__ __launch_bounds__(256) void down_small_kernel(GroupedArgs a) {
+__global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
   constexpr int MTL = MT_SMALL;
   constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4, MS = MTL / 16;
+  constexpr int NSW = NSUB / 2;             // n-subtiles per wave (half a row tile)
   constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS;
-  constexpr int D = 3;
+  constexpr int D = 4;
   const int inter = INTER;
   const int tile = blockIdx.x / NCB, cb = blockIdx.x % NCB;
   const TileInfo ti = tile_info(a, tile, MTL);
@@ -1944,50 +1945,78 @@ __global__ __launch_bounds__(256) void down_small_kernel(GroupedArgs a) {
   const int e = wave_uniform(ti.e);
   const size_t mbytes = matrix_bytes(BITS, inter, H);
   const int ngk = inter / G;
-  const int rt = 4 * cb + wv;
+  const int rt = 4 * cb + (wv >> 1), hh = wv & 1;
   const __amdgpu_buffer_rsrc_t rb = weight_rsrc(a.w.q + (size_t)e * a.w.e_bytes + 2 * mbytes, (uint32_t)mbytes);
   const __amdgpu_buffer_rsrc_t rs =
       weight_rsrc(a.w.s + (size_t)e * a.w.e_scales + 2 * (size_t)inter * (H / G), (uint32_t)ngk * H * 4);
   const __amdgpu_buffer_rsrc_t ra = weight_rsrc(a.af, (uint32_t)a.a_rows * inter * 4);
 
-  uint4 bq[D][KS / 32];
-  float sq[D][GPS][NSUB];
-  auto load_b = [&](uint4 (&bd)[KS / 32], float (&sd)[GPS][NSUB], int st) {
+  // this wave's half of each 16-byte lane word of a down tile: words 2hh, 2hh+1
+  uint2 bq[D][KS / 32];
+  float sq[D][GPS][NSW];
+  auto load_b = [&](uint2 (&bd)[KS / 32], float (&sd)[GPS][NSW], int st) {
 #pragma unroll
     for (int g = 0; g < GPS; ++g) {
-      const uint32_t so = ((((uint32_t)(st * GPS + g) * NRT + rt) * 16 + r) * NSUB) * 4;
-      if (NSUB == 4) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0);
-#pragma unroll
-        for (int j = 0; j < NSUB; ++j) sd[g][j] = __uint_as_float(v[j]);
-      } else {
+      const uint32_t so = ((((uint32_t)(st * GPS + g) * NRT + rt) * 16 + r) * NSUB + NSW * hh) * 4;
+      if (NSW == 2) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0);
-#pragma unroll
-        for (int j = 0; j < NSUB; ++j) sd[g][j] = __uint_as_float(v[j]);
+        sd[g][0] = __uint_as_float(v[0]);
+        sd[g][NSW - 1] = __uint_as_float(v[1]);
+      } else {
+        sd[g][0] = wload4(rs, so);
       }
     }
 #pragma unroll
-    for (int c = 0; c < KS / 32; ++c) bd[c] = wload16(rb, ((uint32_t)(st * (KS / 32) + c) * NRT + rt) * TILE + lane * 16);
+    for (int c = 0; c < KS / 32; ++c) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+          rb, ((uint32_t)(st * (KS / 32) + c) * NRT + rt) * TILE + lane * 16 + 8 * hh, 0, 0);
+      bd[c] = make_uint2(v[0], v[1]);
+    }
   };
-  float4v acc[NSUB][MS], ctmp[NSUB][MS];
+  // A (h, f32 as hi/lo f16 planes): one 8-element segment per thread per stage
+  auto fetch_a1 = [&](uint4 (&ar)[2], int k0, bool live) {
+    const int row = tid >> 4, kk = 8 * (tid & 15);
+    const int src = arow[row];
+    const uint32_t off = (live && src >= 0) ? ((uint32_t)src * INTER + k0 + kk) * 4 : 0x80000000u;
+    ar[0] = wload16(ra, off);
+    ar[1] = wload16(ra, off + 16);
+  };
+  auto store_a1 = [&](_Float16* l, const uint4 (&ar)[2]) {
+    const int row = tid >> 4, kk = 8 * (tid & 15);
+    const float v[8] = {__uint_as_float(ar[0].x), __uint_as_float(ar[0].y), __uint_as_float(ar[0].z),
+                        __uint_as_float(ar[0].w), __uint_as_float(ar[1].x), __uint_as_float(ar[1].y),
+                        __uint_as_float(ar[1].z), __uint_as_float(ar[1].w)};
+    half8 hi, lo;
 #pragma unroll
-  for (int j = 0; j < NSUB; ++j)
+    for (int p = 0; p < 8; ++p) {
+      const float x = v[perm_k<BITS>(p)];
+      const _Float16 xh = (_Float16)x;
+      hi[p] = xh;
+      lo[p] = (_Float16)(x - (float)xh);
+    }
+    *(half8*)(l + row * LDS_ROW + kk) = hi;
+    *(half8*)(l + MTL * LDS_ROW + row * LDS_ROW + kk) = lo;
+  };
+  static_assert(MTL * KS / 8 == 512, "one A segment per thread");
+  float4v acc[NSW][MS], ctmp[NSW][MS];
+#pragma unroll
+  for (int j = 0; j < NSW; ++j)
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) { acc[j][ms] = float4v{0, 0, 0, 0}; ctmp[j][ms] = float4v{0, 0, 0, 0}; }
   __syncthreads();   // arow
 
-  AStageS<MTL, true> A[3];
+  uint4 A[3][2];
 #pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0) fetch_a_s<MTL, true>(A[s0], ra, arow, INTER, s0 * KS, s0 < NSTAGE);
+  for (int s0 = 0; s0 < 3; ++s0) fetch_a1(A[s0], s0 * KS, s0 < NSTAGE);
 #pragma unroll
   for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
-  store_a_s<BITS, MTL, true, true>(lds[0], A[0]);
+  store_a1(lds[0], A[0]);
 
 #pragma unroll
   for (int st = 0; st < NSTAGE; ++st) {
     __syncthreads();
-    if (st + 1 < NSTAGE) store_a_s<BITS, MTL, true, true>(lds[(st + 1) & 1], A[(st + 1) % 3]);
-    if (st + 3 < NSTAGE) fetch_a_s<MTL, true>(A[st % 3], ra, arow, INTER, (st + 3) * KS, true);
+    if (st + 1 < NSTAGE) store_a1(lds[(st + 1) & 1], A[(st + 1) % 3]);
+    if (st + 3 < NSTAGE) fetch_a1(A[st % 3], (st + 3) * KS, true);
     const _Float16* la = lds[st & 1];
     const int sl = st % D;
 #pragma unroll
@@ -2001,9 +2030,9 @@ __global__ __launch_bounds__(256) void down_small_kernel(GroupedArgs a) {
         alo[ms] = *(const half8*)(la + MTL * LDS_ROW + (ms * 16 + r) * LDS_ROW + lcol);
       }
 #pragma unroll
-      for (int j = 0; j < NSUB; ++j) {
-        const half8 bfr = BITS == 4 ? unpack_int4(word_of(bq[sl][c], j))
-                                    : unpack_int8(word_of(bq[sl][c], 2 * j), word_of(bq[sl][c], 2 * j + 1));
+      for (int j = 0; j < NSW; ++j) {
+        const uint2 w2 = bq[sl][c];
+        const half8 bfr = BITS == 4 ? unpack_int4(j == 0 ? w2.x : w2.y) : unpack_int8(w2.x, w2.y);
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
           float4v cc = first ? float4v{0, 0, 0, 0} : ctmp[j][ms];
@@ -2014,7 +2043,7 @@ __global__ __launch_bounds__(256) void down_small_kernel(GroupedArgs a) {
       }
       if (last) {
 #pragma unroll
-        for (int j = 0; j < NSUB; ++j) {
+        for (int j = 0; j < NSW; ++j) {
           const float sj = sq[sl][c / CPG][j];
 #pragma unroll
           for (int ms = 0; ms < MS; ++ms) acc[j][ms] += sj * ctmp[j][ms];
@@ -2031,7 +2060,7 @@ __global__ __launch_bounds__(256) void down_small_kernel(GroupedArgs a) {
       if (m < ti.nrows) {
         const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
 #pragma unroll
-        for (int j = 0; j < NSUB; ++j) a.out[orow * H + DR * rt + 16 * j + r] = acc[j][ms][k];
+        for (int j = 0; j < NSW; ++j) a.out[orow * H + DR * rt + 16 * (NSW * hh + j) + r] = acc[j][ms][k];
       }
     }
 }
@@ -2168,8 +2197,8 @@ template <int BITS, int G>
 static void down_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
   if (small) {
     const dim3 grid(max_tiles * (H / (4 * down_rows(BITS))));
-    if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<BITS, G, IS>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((down_small_kernel<BITS, G, I>), grid, dim3(256), 0, s, a);
+    if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<BITS, G, IS>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((down_small_kernel<BITS, G, I>), grid, dim3(512), 0, s, a);
   } else {
     const dim3 grid(max_tiles * (H / 256));             // 256 output columns per workgroup
     if (a.w.inter == IS) hipLaunchKernelGGL((grouped_down_kernel<BITS, G, IS>), grid, dim3(GT), 0, s, a);
