@@ -29,7 +29,7 @@ struct Workspace {
   float* h_routed;   // [T*6][I]
   float* h_shared;   // [T][IS]
   float* ysorted;    // [T*6][H]
-  float* ys;         // [T][H]
+  float* ys;         // [2][T][H]: the shared expert's down projection in two K halves
   int32_t* counts;   // [E]
   int32_t* offsets;  // [E+1]
   int32_t* ntiles;   // [1]
@@ -63,7 +63,7 @@ Workspace carve(void* base, int T) {
   w.h_routed = (float*)c.take(slots * I * 4);
   w.h_shared = (float*)c.take((size_t)T * IS * 4);
   w.ysorted = (float*)c.take(slots * H * 4);
-  w.ys = (float*)c.take((size_t)T * H * 4);
+  w.ys = (float*)c.take(2 * (size_t)T * H * 4);
   w.counts = (int32_t*)c.take(E * 4);
   w.offsets = (int32_t*)c.take((E + 1) * 4);
   w.ntiles = (int32_t*)c.take(4);
@@ -304,6 +304,7 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
 
   GroupedArgs ga;
   ga.T = T; ga.tiles = ws.tiles; ga.ntiles = ws.ntiles; ga.offsets = ws.offsets; ga.perm = ws.perm;
+  ga.ksplit = 1;
   // routed gate/up: A rows are tokens gathered through the permutation
   ga.af = xf; ga.ab = xb; ga.shared = 0; ga.a_by_token = 1; ga.a_rows = T; ga.w = rw; ga.out = ws.h_routed;
   if (launch_grouped_gateup(ga, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
@@ -314,10 +315,12 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   ga.af = ws.h_routed; ga.ab = nullptr; ga.shared = 0; ga.a_by_token = 0; ga.a_rows = T * TOPK; ga.w = rw;
   ga.out = ws.ysorted;
   if (launch_grouped_down(ga, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
-  ga.af = ws.h_shared; ga.shared = 1; ga.a_rows = T; ga.w = sw; ga.out = ws.ys;
+  // with small tiles the shared down has few row tiles: two K halves double
+  // its workgroups
+  ga.af = ws.h_shared; ga.shared = 1; ga.a_rows = T; ga.w = sw; ga.out = ws.ys; ga.ksplit = small ? 2 : 1;
   if (launch_grouped_down(ga, (T + mtl - 1) / mtl, small, s) != hipSuccess) return MOE_E_HIP;
   CombineArgs ca;
-  ca.ys = ws.ys; ca.ysorted = ws.ysorted; ca.pos_of = ws.pos_of; ca.tw = topk_w;
+  ca.ys = ws.ys; ca.ys2 = small ? ws.ys + (size_t)T * H : nullptr; ca.ysorted = ws.ysorted; ca.pos_of = ws.pos_of; ca.tw = topk_w;
   ca.y = y; ca.T = T; ca.accumulate = accumulate;
   if (launch_combine(ca, s) != hipSuccess) return MOE_E_HIP;
   return MOE_OK;

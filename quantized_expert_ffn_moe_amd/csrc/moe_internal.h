@@ -110,10 +110,12 @@ struct GroupedArgs {
   int a_rows;                           // rows of the A matrix (bounds its buffer descriptor)
   QW w;
   float* out;                           // routed: [T*6][N] by sorted position; shared: [T][N]
+  int ksplit;                           // down of the shared expert: 2 = two K halves, half k to out + k T H
 };
 
 struct CombineArgs {
-  const float* ys; const float* ysorted; const int32_t* pos_of; const float* tw;
+  const float* ys; const float* ys2;    // shared expert output (ys2: second K half, or null)
+  const float* ysorted; const int32_t* pos_of; const float* tw;
   float* y; int T; int accumulate;
 };
 

@@ -1617,14 +1617,18 @@ __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
 // owns 64 of them (four 16-row n-subtiles).  A = h as the f16 hi/lo pairs the
 // grouped gate/up kernel writes, copied to LDS as they are.
 // B per stage: 4 K-chunks of 32 x NRTB row tiles.
-template <int BITS, int G, int INTER>
+template <int BITS, int G, int INTER, int KSPLIT = 1>
 __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
   constexpr int DR = down_rows(BITS), NRT = H / DR, NRTB = 256 / DR, MS = 2, NSUB = DR / 16;
-  constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS, NCB = H / 256;
+  constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS / KSPLIT, NCB = H / 256;
+  static_assert((INTER / KS) % KSPLIT == 0, "K halves of whole stages");
   constexpr int BT = 4 * NRTB;                      // B tiles per stage (16 or 32)
   constexpr int BU = BT * 64 / GT;
   constexpr int WRT = 4 / NSUB;                     // row tiles per wave (1 or 2)
-  const int tile = blockIdx.x / NCB, cb = blockIdx.x % NCB;
+  // KSPLIT > 1: workgroup kh takes stages kh NSTAGE .. and writes its partial
+  // sum to out + kh T H (the combine adds the parts)
+  const int kh = blockIdx.x % KSPLIT, tb = blockIdx.x / KSPLIT, s0 = kh * NSTAGE;
+  const int tile = tb / NCB, cb = tb % NCB;
   const TileInfo ti = tile_info(a, tile, MT);
   if (!ti.valid) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
@@ -1648,13 +1652,13 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
   };
   // B uint4 u: tile bt = u / 64 = c * NRTB + rtl, lane slot u % 64
   auto fetch = [&](Stage& R, int st) {
-    fetch_a<true>(R.A, ra, arow, INTER, st * KS, st < NSTAGE);
+    fetch_a<true>(R.A, ra, arow, INTER, (s0 + st) * KS, st < NSTAGE);
 #pragma unroll
     for (int g = 0; g < GPS; ++g)
 #pragma unroll
       for (int w2 = 0; w2 < WRT; ++w2) {
         const int rt = cb * NRTB + WRT * wn + w2;
-        const uint32_t so = ((((uint32_t)(st * GPS + g) * NRT + rt) * 16 + r) * NSUB) * 4;
+        const uint32_t so = ((((uint32_t)((s0 + st) * GPS + g) * NRT + rt) * 16 + r) * NSUB) * 4;
         if (NSUB == 4) {
           const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0);
 #pragma unroll
@@ -1670,7 +1674,7 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
       const int u = tid + GT * k, bt = u >> 6, sl = u & 63;
       const int c = bt / NRTB, rtl = bt % NRTB;
       const uint32_t off =
-          (st < NSTAGE) ? ((uint32_t)((4 * st + c) * NRT + cb * NRTB + rtl) * TILE + sl * 16) : 0x80000000u;
+          (st < NSTAGE) ? ((uint32_t)((4 * (s0 + st) + c) * NRT + cb * NRTB + rtl) * TILE + sl * 16) : 0x80000000u;
       R.B[k] = wload16(rb, off);
     }
   };
@@ -1754,7 +1758,7 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int rt = cb * NRTB + WRT * wn + j / NSUB;
-          a.out[orow * H + DR * rt + 16 * (j % NSUB) + r] = acc[j][ms][k];
+          a.out[(size_t)kh * a.T * H + orow * H + DR * rt + 16 * (j % NSUB) + r] = acc[j][ms][k];
         }
       }
     }
@@ -1926,15 +1930,17 @@ __global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
 // 2i and 2i + 1 share row tile 4cb + i (64 int4 or 32 int8 output columns),
 // each taking half of its 16-row n-subtiles (the matching half of every
 // 16-byte lane word).  Same software pipeline as gate/up.
-template <int BITS, int G, int INTER>
+template <int BITS, int G, int INTER, int KSPLIT = 1>
 __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
   constexpr int MTL = MT_SMALL;
   constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4, MS = MTL / 16;
   constexpr int NSW = NSUB / 2;             // n-subtiles per wave (half a row tile)
-  constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS;
+  constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS / KSPLIT;
+  static_assert((INTER / KS) % KSPLIT == 0, "K halves of whole stages");
   constexpr int D = 4;
   const int inter = INTER;
-  const int tile = blockIdx.x / NCB, cb = blockIdx.x % NCB;
+  const int kh = blockIdx.x % KSPLIT, tb = blockIdx.x / KSPLIT, s0 = kh * NSTAGE;   // K part kh
+  const int tile = tb / NCB, cb = tb % NCB;
   const TileInfo ti = tile_info(a, tile, MTL);
   if (!ti.valid) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
@@ -1957,7 +1963,7 @@ __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
   auto load_b = [&](uint2 (&bd)[KS / 32], float (&sd)[GPS][NSW], int st) {
 #pragma unroll
     for (int g = 0; g < GPS; ++g) {
-      const uint32_t so = ((((uint32_t)(st * GPS + g) * NRT + rt) * 16 + r) * NSUB + NSW * hh) * 4;
+      const uint32_t so = ((((uint32_t)((s0 + st) * GPS + g) * NRT + rt) * 16 + r) * NSUB + NSW * hh) * 4;
       if (NSW == 2) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0);
         sd[g][0] = __uint_as_float(v[0]);
@@ -1969,7 +1975,7 @@ __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b64(
-          rb, ((uint32_t)(st * (KS / 32) + c) * NRT + rt) * TILE + lane * 16 + 8 * hh, 0, 0);
+          rb, ((uint32_t)((s0 + st) * (KS / 32) + c) * NRT + rt) * TILE + lane * 16 + 8 * hh, 0, 0);
       bd[c] = make_uint2(v[0], v[1]);
     }
   };
@@ -2007,7 +2013,7 @@ __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
 
   uint4 A[3][2];
 #pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0) fetch_a1(A[s0], s0 * KS, s0 < NSTAGE);
+  for (int sp = 0; sp < 3; ++sp) fetch_a1(A[sp], (s0 + sp) * KS, sp < NSTAGE);
 #pragma unroll
   for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
   store_a1(lds[0], A[0]);
@@ -2016,7 +2022,7 @@ __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
   for (int st = 0; st < NSTAGE; ++st) {
     __syncthreads();
     if (st + 1 < NSTAGE) store_a1(lds[(st + 1) & 1], A[(st + 1) % 3]);
-    if (st + 3 < NSTAGE) fetch_a1(A[st % 3], (st + 3) * KS, true);
+    if (st + 3 < NSTAGE) fetch_a1(A[st % 3], (s0 + st + 3) * KS, true);
     const _Float16* la = lds[st & 1];
     const int sl = st % D;
 #pragma unroll
@@ -2060,15 +2066,20 @@ __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
       if (m < ti.nrows) {
         const size_t orow = a.shared ? (size_t)(ti.row0 + m) : (size_t)(ti.pbase + m);
 #pragma unroll
-        for (int j = 0; j < NSW; ++j) a.out[orow * H + DR * rt + 16 * (NSW * hh + j) + r] = acc[j][ms][k];
+        for (int j = 0; j < NSW; ++j)
+          a.out[(size_t)kh * a.T * H + orow * H + DR * rt + 16 * (NSW * hh + j) + r] = acc[j][ms][k];
       }
     }
 }
 
-// y[t] (+)= ys[t] + sum_j w[t,j] * ysorted[pos_of[t*6+j]], picks added in order.
+// y[t] (+)= ys[t] (+ ys2[t]) + sum_j w[t,j] * ysorted[pos_of[t*6+j]], picks added in order.
 __global__ __launch_bounds__(320) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x, c = threadIdx.x * 4;
   float4 v = *(const float4*)(a.ys + (size_t)t * H + c);
+  if (a.ys2) {   // the second K part of the shared expert's down projection
+    const float4 v2 = *(const float4*)(a.ys2 + (size_t)t * H + c);
+    v.x += v2.x; v.y += v2.y; v.z += v2.z; v.w += v2.w;
+  }
 #pragma unroll
   for (int j = 0; j < TOPK; ++j) {
     const float wj = a.tw[(size_t)t * TOPK + j];
@@ -2197,11 +2208,15 @@ template <int BITS, int G>
 static void down_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
   if (small) {
     const dim3 grid(max_tiles * (H / (4 * down_rows(BITS))));
-    if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<BITS, G, IS>), grid, dim3(512), 0, s, a);
+    if (a.w.inter == IS && a.ksplit == 2)
+      hipLaunchKernelGGL((down_small_kernel<BITS, G, IS, 2>), dim3(2 * grid.x), dim3(512), 0, s, a);
+    else if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<BITS, G, IS>), grid, dim3(512), 0, s, a);
     else hipLaunchKernelGGL((down_small_kernel<BITS, G, I>), grid, dim3(512), 0, s, a);
   } else {
     const dim3 grid(max_tiles * (H / 256));             // 256 output columns per workgroup
-    if (a.w.inter == IS) hipLaunchKernelGGL((grouped_down_kernel<BITS, G, IS>), grid, dim3(GT), 0, s, a);
+    if (a.w.inter == IS && a.ksplit == 2)
+      hipLaunchKernelGGL((grouped_down_kernel<BITS, G, IS, 2>), dim3(2 * grid.x), dim3(GT), 0, s, a);
+    else if (a.w.inter == IS) hipLaunchKernelGGL((grouped_down_kernel<BITS, G, IS>), grid, dim3(GT), 0, s, a);
     else hipLaunchKernelGGL((grouped_down_kernel<BITS, G, I>), grid, dim3(GT), 0, s, a);
   }
 }
