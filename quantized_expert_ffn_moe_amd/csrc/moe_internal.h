@@ -65,11 +65,13 @@ constexpr int MAX_LAYERS = 16;
 constexpr int N_RED = 32;                 // reducer workgroups
 constexpr int RED_ROWS = H / N_RED;       // 40 rows each
 constexpr int Q_STRIDE = 68;              // 64 partial logits + sum of squares, padded
-// Tagged 16-byte words (three f32 values + the epoch tag of the writer's stage).
-constexpr int PART_U4 = (RED_ROWS + 2) / 3;      // 14 words: one item's partial for one reducer
-constexpr int ITEM_U4 = N_RED * PART_U4;         // 448 words per item
+// Exchanged 16-byte words: four f32 values, the lowest mantissa bit of each
+// set to the parity of the writer's stage.
+constexpr int PART_U4 = RED_ROWS / 4;            // 10 words: one item's partial for one reducer
+static_assert(RED_ROWS % 4 == 0, "reducer bands of whole words");
+constexpr int ITEM_U4 = N_RED * PART_U4;         // 320 words per item
 constexpr int REC_VALS = RED_ROWS + E + 1;       // reducer record: h rows, partial logits, sum of squares
-constexpr int REC_U4 = (REC_VALS + 2) / 3;       // 35 words
+constexpr int REC_U4 = (REC_VALS + 3) / 4;       // 27 words
 struct LayerPtrs {
   const float* wr; const float* bias;
   const uint8_t* eq; const float* es;
@@ -84,9 +86,9 @@ struct ChainArgs {
   float eps;
   int rbits, rgroup, sbits, sgroup;
   int32_t* ids; float* tw;                // [n_layers][6]
-  uint32_t* hdr;                          // [0] call sequence, [1] done count, [2] error
-  uint32_t* ipart;                        // [N_ITEMS][N_RED][PART_U4] tagged words (16 B each)
-  uint32_t* rec;                          // [N_RED][REC_U4] tagged words
+  uint32_t* hdr;                          // [0] stage counter (tags of a call are hdr[0] + 1 ..), [1] done count, [2] error
+  uint32_t* ipart;                        // [N_ITEMS][N_RED][PART_U4] parity words (16 B each)
+  uint32_t* rec;                          // [N_RED][REC_U4] parity words
 #ifdef MOE_DEVICE_TRACE
   unsigned long long* trace;              // [256][16][16] timestamps (timeline studies only)
 #endif

@@ -538,6 +538,23 @@ __device__ __forceinline__ void item_planes(const float* z, float mul, ItemLds& 
   __syncthreads();
 }
 
+// x with its lowest bit set to the parity of tag
+__device__ __forceinline__ uint32_t with_parity(float x, uint32_t tag) {
+  return (__float_as_uint(x) & ~1u) | (tag & 1u);
+}
+// a value as readers use it: the parity bit cleared, so that what they see
+// does not depend on the stage tag (repeated calls give the same bits)
+__device__ __forceinline__ float word_value(uint32_t u) { return __uint_as_float(u & ~1u); }
+// all four values of a word carry the parity of tag
+__device__ __forceinline__ bool word_of_tag(const u32x4& v, uint32_t tag) {
+  const uint32_t all1 = v[0] & v[1] & v[2] & v[3], any1 = v[0] | v[1] | v[2] | v[3];
+  return ((tag & 1u) ? all1 : ~any1) & 1u;
+}
+
+__device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, CPOL_SC1);
+}
+
 // Input digits in L.xa/L.xs (item_planes) -> L.dout (the item's down rows) and
 // L.hs.  Wave w multiplies the 16 gate/up rows of its n-tile over its K half
 // (x64 products, one scale group per G/64 of them; G = 32 splits each into two
@@ -702,35 +719,39 @@ __global__ __launch_bounds__(256) void dec_reduce_kernel(DecReduceArgs a) {
 //   items (layer s): read all 32 records, rebuild RMSNorm(h_s), the 64
 //     logits, softmax and top-6 (every routed item computes the same routing),
 //     stream their expert slice and write their partial for each reducer.
-// Exchange without flags: every 16-byte word carries three f32 values and the
-// epoch tag of the stage that wrote it (call sequence * 64 + stage + 1).  A
-// 16-byte aligned vector store lands as one piece, so a reader that sees the
-// current tag in a word also sees that word's values; it polls the words
-// themselves with device-scope (L2-coherent) loads.  Writers never wait for
-// their stores, and nothing is cleared between calls.
+// Exchange without flags: every 16-byte word carries four f32 values whose
+// lowest mantissa bits all hold the parity of the writer's stage tag (a
+// counter that runs on across calls: the tags of a call are base + 1 ..
+// base + n_layers, and the next call starts at base + n_layers).  A 16-byte
+// aligned vector store lands as one piece, so a reader that sees the expected
+// parity in all four values sees the word of the current stage.  One bit is
+// enough because the chain runs in lock step: an item writes its layer-s
+// partial only after every reducer has published its stage-s record, which a
+// reducer does only after reading all layer-(s-1) partials (and the same the
+// other way round), so a word holds the current stage or the one before it.
+// Readers poll the words themselves with device-scope (L2-coherent) loads.
+// Writers never wait for their stores, and nothing is cleared between calls.
+// (Readers clear the bit: a value moves by at most one ulp, the same in every
+// call.)
 // ---------------------------------------------------------------------------
 constexpr long SPIN_LIMIT = 1L << 20;  // polls before a wait gives up (about a second)
 
-__device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, CPOL_SC1);
-}
-
 // Lane 0 of each wave polls one word (off[0], valid in lane 0) until it
-// carries `tag`: a few bytes per wave while the writers are still busy.  The
+// carries the parity of `tag`: a few bytes per wave while the writers are still busy.  The
 // full loads follow (load_tagged), which check every word.
 __device__ __forceinline__ void wait_first(__amdgpu_buffer_rsrc_t r, uint32_t off0, uint32_t tag, long& spins) {
   const int lane = threadIdx.x & 63;
   while (true) {
     bool ok = true;
-    if (lane == 0) ok = load16_coherent(r, off0)[3] == tag;
+    if (lane == 0) ok = word_of_tag(load16_coherent(r, off0), tag);
     if (__all(ok)) break;
     __builtin_amdgcn_s_sleep(1);
     if (++spins > SPIN_LIMIT) break;
   }
 }
 
-// Load the tagged words at off[m] (where valid[m]) and poll until every one
-// carries `tag` (after wait_first this usually takes one round trip).
+// Load the words at off[m] (where valid[m]) and poll until every one
+// carries the parity of `tag` (after wait_first this usually takes one round trip).
 // Branch-free: every round issues all N loads back to back, a word that is
 // not wanted (invalid, or already carrying the tag) at an offset past the end
 // of the buffer, which returns zeros without a memory access; a conditional
@@ -752,7 +773,7 @@ __device__ __forceinline__ void load_tagged(__amdgpu_buffer_rsrc_t r, const uint
     for (int m = 0; m < N; ++m) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) v[m][k] = need[m] ? nv[m][k] : v[m][k];
-      need[m] = need[m] && v[m][3] != tag;
+      need[m] = need[m] && !word_of_tag(v[m], tag);
       done = done && !need[m];
     }
     if (__all(done)) break;
@@ -773,9 +794,9 @@ struct ItemSide {
   int pick_e[TOPK];
 };
 struct ReducerSide {
-  float red[N_ITEMS / 7][PART_U4 * 3];   // per item group, per row (42 slots, 40 used)
+  float red[N_ITEMS / 7][RED_ROWS];      // per item group, per row
   float hrow[RED_ROWS];
-  float rec[REC_U4 * 3];
+  float rec[REC_U4 * 4];
 };
 union ChainLds {
   ItemSide it;
@@ -798,8 +819,8 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const Lay
   const float bias_e = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
       coherent_rsrc(bias, bias ? E * 4 : 0), (uint32_t)(tid >> 3) * 4, 0, 0));
   {
-    constexpr int NR = N_RED * REC_U4;          // 1120 words
-    constexpr int PT = (NR + 511) / 512;        // 3 per thread
+    constexpr int NR = N_RED * REC_U4;          // 864 words
+    constexpr int PT = (NR + 511) / 512;        // 2 per thread
     const __amdgpu_buffer_rsrc_t rr = coherent_rsrc(a.rec, NR * 16);
     uint32_t off[PT];
     bool valid[PT];
@@ -819,9 +840,9 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const Lay
       if (!valid[m]) continue;
       const int f = tid + 512 * m, rid = f / REC_U4, k = f % REC_U4;
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int vi = 3 * k + i;
-        const float val = __uint_as_float(v[m][i]);
+      for (int i = 0; i < 4; ++i) {
+        const int vi = 4 * k + i;
+        const float val = word_value(v[m][i]);
         if (vi < RED_ROWS) S.z[RED_ROWS * rid + vi] = val;
         else if (vi < RED_ROWS + E) S.qs[rid * Q_STRIDE + vi - RED_ROWS] = val;
         else if (vi == REC_VALS - 1) S.qs[rid * Q_STRIDE + E] = val;
@@ -866,21 +887,16 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const Lay
   return inv;
 }
 
-// An item's partial (item_compute done, cs = coef * unit of h) as tagged words
-// [reducer][14]: word c of reducer r holds rows 40r + 3c .. 40r + 3c + 2.
-__device__ __forceinline__ void chain_item_store(const ChainArgs& a, const ItemLds& L, float cs, int b,
-                                                 uint32_t tag) {
+// An item's partial (item_compute done, cs = coef * unit of h) as parity
+// words [reducer][10]: word w of the item holds rows 4w .. 4w + 3.
+__device__ __forceinline__ void chain_item_store(const ChainArgs& a, const ItemLds& L, float cs, int b, uint32_t tag) {
   const int tid = threadIdx.x;
   if (tid < ITEM_U4) {
     const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(a.ipart, N_ITEMS * ITEM_U4 * 16);
-    const int r = tid / PART_U4, c = tid % PART_U4;
+    const float4 d = *(const float4*)&L.dout[4 * tid];
     u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int rr = 3 * c + i;
-      w[i] = __float_as_uint(rr < RED_ROWS ? item_row(L, cs, RED_ROWS * r + rr) : 0.f);
-    }
-    w[3] = tag;
+    w[0] = with_parity(cs * d.x, tag); w[1] = with_parity(cs * d.y, tag);
+    w[2] = with_parity(cs * d.z, tag); w[3] = with_parity(cs * d.w, tag);
     store16_coherent(rp, ((uint32_t)b * ITEM_U4 + tid) * 16, w);
   }
 }
@@ -956,8 +972,8 @@ __device__ void chain_reducer(const ChainArgs& a, const LayerPtrs* LP, ReducerSi
   const int tid = threadIdx.x;
   const int r0 = rid * RED_ROWS;
   const int e = tid >> 3, sub = tid & 7;      // partial logits: expert e, rows sub + 8m
-  // summation: thread t < 448 owns word c = t % 14 (rows 3c..3c+2 of this
-  // reducer) of items ig + 32j, ig = t / 14, j = 0..6
+  // summation: thread t < 320 owns word c = t % 10 (rows 4c..4c+3 of this
+  // reducer) of items ig + 32j, ig = t / 10, j = 0..6
   constexpr int NG = N_ITEMS / 7;             // 32 item groups
   const bool summer = tid < NG * PART_U4;
   const int c = tid % PART_U4, ig = tid / PART_U4;
@@ -991,13 +1007,13 @@ __device__ void chain_reducer(const ChainArgs& a, const LayerPtrs* LP, ReducerSi
       load_tagged<7>(rp, off, valid, v, base + s, spins, err);
       MOE_TRACE(a, N_ITEMS + rid, s, 1);
       if (summer) {
-        float acc[3] = {0.f, 0.f, 0.f};
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 7; ++j)
 #pragma unroll
-          for (int i = 0; i < 3; ++i) acc[i] += __uint_as_float(v[j][i]);
+          for (int i = 0; i < 4; ++i) acc[i] += word_value(v[j][i]);
 #pragma unroll
-        for (int i = 0; i < 3; ++i) S.red[ig][3 * c + i] = acc[i];
+        for (int i = 0; i < 4; ++i) S.red[ig][4 * c + i] = acc[i];
       }
       __syncthreads();
       // row r = t / 8: groups k, k + 8, k + 16, k + 24 (k = t % 8), then over the 8 lanes
@@ -1031,11 +1047,10 @@ __device__ void chain_reducer(const ChainArgs& a, const LayerPtrs* LP, ReducerSi
       if (tid < REC_U4) {
         u32x4 w;
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-          const int vi = 3 * tid + i;
-          w[i] = vi < REC_VALS ? __float_as_uint(S.rec[vi]) : 0u;
+        for (int i = 0; i < 4; ++i) {
+          const int vi = 4 * tid + i;
+          w[i] = with_parity(vi < REC_VALS ? S.rec[vi] : 0.f, base + s + 1);
         }
-        w[3] = base + s + 1;
         store16_coherent(rr, ((uint32_t)rid * REC_U4 + tid) * 16, w);
       }
     }
@@ -1054,7 +1069,7 @@ __global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
     ((uint64_t*)LP)[threadIdx.x] = ((const uint64_t*)a.layer)[threadIdx.x];
   __syncthreads();
   const int b = blockIdx.x;
-  const uint32_t base = load_coherent_u32(a.hdr) * 64u;
+  const uint32_t base = load_coherent_u32(a.hdr);   // this call's stage tags are base + 1 .. base + n_layers
   uint32_t* err = a.hdr + 2;
   if (b < R_ITEMS) {
     switch (a.rgroup) {
@@ -1071,14 +1086,14 @@ __global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
   } else {
     chain_reducer(a, LP, S.rd, b - N_ITEMS, base, err);
   }
-  // the last workgroup to finish advances the call sequence
+  // the last workgroup to finish advances the stage counter
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t old = __hip_atomic_fetch_add(a.hdr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == gridDim.x - 1) {
       store_coherent_u32(a.hdr + 1, 0u);
-      store_coherent_u32(a.hdr, load_coherent_u32(a.hdr) + 1u);
+      store_coherent_u32(a.hdr, base + (uint32_t)a.n_layers);
     }
   }
 }
