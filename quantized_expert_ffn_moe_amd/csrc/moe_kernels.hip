@@ -1283,9 +1283,9 @@ template <int BITS> __device__ __forceinline__ int perm_k(int p) {
 constexpr int KS = 128;             // K staged in LDS per step
 constexpr int LDS_ROW = KS + 8;     // f16 per LDS row (16-byte pad against bank conflicts)
 
-// Grouped GEMMs come in two tile shapes: 32-row tiles with 4 waves (two
-// workgroups per compute unit) when experts see few rows each, 64 x 256 tiles
-// with 8 waves when they see many.  Both stage A (f16, hi and lo planes for
+// Grouped GEMMs come in two tile shapes, both with 8 waves per workgroup:
+// 32-row tiles when experts see few rows each, 64 x 256 tiles when they see
+// many.  Both stage A (f16, hi and lo planes for
 // f32 inputs, permuted within each 8-group into the B operand order) and use
 // the same exact-integer B unpacking; the large tiles share B through LDS.
 // Small-tile A staging, split into a global fetch (into registers, issued two
