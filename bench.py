@@ -90,8 +90,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--path", choices=["chain", "layers"], default="chain")
-    ap.add_argument("--workload", choices=["decode", "prefill273", "multipage2184"], default="decode",
-                    help="decode = the headline 11-layer decode step; the prefill workloads report MFMA figures")
+    ap.add_argument("--workload", choices=["decode", "prefill273", "multipage2184", "batch128", "batch256"],
+                    default="decode",
+                    help="decode = the headline 11-layer decode step; the prefill workloads report MFMA "
+                         "figures; batchN = one continuous-batch decode step of N streams (HBM figures)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
@@ -217,6 +219,23 @@ def prefill_flops(T, ids, routed_fmt):
     return 2 * (T * 6 * 3 * H * I + T * 3 * H * IS + T * E * H)
 
 
+def grouped_step_bytes(wl, ids_per_layer):
+    """Algorithmic bytes of one step of a many-token workload: every routed
+    expert the step touches once per layer (codes and scales), the shared
+    expert and the router, plus the activations (residual in, layer output
+    read-modify-write, ids and weights out)."""
+    H, I, IS, E = 1280, 896, 1792, 64
+    rf, sf = wl.routed, wl.shared
+    per_expert = 3 * H * I * rf.bits // 8 + 3 * H * I // rf.group * 4
+    shared = 3 * H * IS * sf.bits // 8 + 3 * H * IS // sf.group * 4
+    T = wl.n_tokens
+    total = 0
+    for ids in ids_per_layer:
+        u = len(set(ids.reshape(-1).tolist()))
+        total += u * per_expert + shared + E * H * 4 + T * (H * 4 * 3 + 6 * 8)
+    return total
+
+
 def bench_prefill(args):
     import numpy as np
     import torch
@@ -224,13 +243,16 @@ def bench_prefill(args):
     from quantized_expert_ffn_moe_amd import binding as B
     from synth import WORKLOADS, make_layer, make_tokens
 
-    wl = WORKLOADS[3] if args.workload == "prefill273" else WORKLOADS[4]
+    wl = WORKLOADS[{"prefill273": 3, "multipage2184": 4, "batch128": 5, "batch256": 6}[args.workload]]
     L = wl.n_layers
     layers = [make_layer(wl, li) for li in range(L)]
     packed = [B.pack_layer(layer) for layer in layers]
     T = wl.n_tokens
     x, bits = make_tokens(wl)
-    xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    if bits is not None:
+        xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        xt = torch.from_numpy(x).cuda()
     h = torch.empty(T, 1280, dtype=torch.float32, device="cuda")
     ids = torch.empty(L, T, 6, dtype=torch.int32, device="cuda")
     w = torch.empty(L, T, 6, dtype=torch.float32, device="cuda")
@@ -259,11 +281,18 @@ def bench_prefill(args):
     ms = e0.elapsed_time(e1) / args.steps
     flops = L * prefill_flops(T, None, wl.routed)
     tflops = flops / (ms * 1e-3) / 1e12
-    print(json.dumps({"metric": f"{wl.name}: tokens/s", "value": T / (ms * 1e-3), "unit": "tokens/s",
-                      "ms_per_step": ms, "steps": args.steps, "warmup": args.warmup, "dtype": "f16 MFMA, fp32 acc",
-                      "config": {"workload": wl.name, "tokens": T, "layers": L},
-                      "achieved_tflops": tflops, "bf16_peak_tflops": 2500.0, "mfma_frac": tflops / 2500.0}),
-          flush=True)
+    out = {"metric": f"{wl.name}: tokens/s", "value": T / (ms * 1e-3), "unit": "tokens/s",
+           "ms_per_step": ms, "steps": args.steps, "warmup": args.warmup, "dtype": "f16 MFMA, fp32 acc",
+           "config": {"workload": wl.name, "tokens": T, "layers": L},
+           "achieved_tflops": tflops, "bf16_peak_tflops": 2500.0, "mfma_frac": tflops / 2500.0}
+    if args.workload.startswith("batch"):
+        # a decode step of many streams reads (nearly) every expert once per
+        # layer: the HBM roofline bounds it
+        nbytes = grouped_step_bytes(wl, list(ids[:L].cpu().numpy()))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_step": nbytes}
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -25,6 +25,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Workspace {
   float* z;          // [T][H] normalised input
+  float* logits;     // [T][E] router logits (two-pass router)
   // grouped path
   float* h_routed;   // [T*6][I]
   float* h_shared;   // [T][IS]
@@ -59,6 +60,7 @@ Workspace carve(void* base, int T) {
   const size_t slots = (size_t)T * TOPK;
   w.max_tiles = (int)(slots / MT_SMALL) + E + 1;   // enough for either tile height
   w.z = (float*)c.take((size_t)T * H * 4);
+  w.logits = (float*)c.take((size_t)T * E * 4);
   const size_t union_start = c.off;
   w.h_routed = (float*)c.take(slots * I * 4);
   w.h_shared = (float*)c.take((size_t)T * IS * 4);
@@ -269,7 +271,7 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   ra.x = x; ra.x_bf16 = x_dtype == MOE_BF16; ra.T = T;
   ra.wr = router_w; ra.bias = router_b;
   ra.norm = norm; ra.norm_bf16 = (flags & MOE_NORM_BF16) != 0; ra.eps = 1e-6f;
-  ra.z = ws.z; ra.ids = topk_ids; ra.w = topk_w;
+  ra.z = ws.z; ra.ids = topk_ids; ra.w = topk_w; ra.logits = ws.logits;
   if (launch_router(ra, s) != hipSuccess) return MOE_E_HIP;
 
   // input rows of the experts: the normalised z (f32, or bf16 when rounded to

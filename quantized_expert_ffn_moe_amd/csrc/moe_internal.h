@@ -38,6 +38,7 @@ struct RouterArgs {
   int norm, norm_bf16; float eps;
   void* z;             // [T][H] normalised input (written when norm): f32, or bf16 with norm_bf16
   int32_t* ids; float* w;
+  float* logits;       // [T][E] scratch of the two-pass router (null: one-pass routers only)
 };
 
 // Decode items: one item = 32 intermediate columns of one (token, expert):

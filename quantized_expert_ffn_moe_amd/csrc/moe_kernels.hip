@@ -141,7 +141,8 @@ __device__ __forceinline__ float inv_rms(const float* red4, float eps) {
 // written out.  The per-token sums of squares use the standalone RMSNorm's
 // per-thread order and reduction, so the two give bit-identical z.
 template <int TB, int ROW>
-__device__ __forceinline__ void router_rows(const RouterArgs& a, int t0, float* zs, float* red) {
+__device__ __forceinline__ void router_rows(const RouterArgs& a, int t0, float* zs, float* red,
+                                            bool store_z = true) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nt = min(TB, a.T - t0);
   const uint32_t elt = a.x_bf16 ? 2 : 4;
@@ -215,8 +216,8 @@ __device__ __forceinline__ void router_rows(const RouterArgs& a, int t0, float* 
       float z = zs[tt * ROW + k] * inv;
       if (a.norm_bf16) {
         z = bf16_rne(z);
-        ((uint16_t*)a.z)[(size_t)(t0 + tt) * H + k] = (uint16_t)(__float_as_uint(z) >> 16);
-      } else {
+        if (store_z) ((uint16_t*)a.z)[(size_t)(t0 + tt) * H + k] = (uint16_t)(__float_as_uint(z) >> 16);
+      } else if (store_z) {
         ((float*)a.z)[(size_t)(t0 + tt) * H + k] = z;
       }
       zs[tt * ROW + k] = z;
@@ -292,6 +293,66 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   __syncthreads();
   // selection: wave = token, lane = expert
   if (wv < nt) select_top6(lg[wv][lane], a.ids + (size_t)(t0 + wv) * TOPK, a.w + (size_t)(t0 + wv) * TOPK);
+}
+
+// ---------------------------------------------------------------------------
+// Two-pass router for a few hundred tokens: the logits pass splits the experts
+// over four workgroups per 4 tokens (each reads a quarter of W_r, 80 KB, from
+// L2, so every compute unit has work and none streams the whole matrix), and
+// a selection pass turns each token's 64 logits into its top 6.
+// Logits pass: wave w of workgroup (bx, by) owns experts 16 by + 4 w .. + 3;
+// lane l owns the columns 4 (64 j + l) .. + 3 (j < 5) and keeps its z values
+// in registers, its W_r values in flight all at once; every (expert, token)
+// sum is then added across the wave in a fixed order.  The workgroups with
+// by = 0 write z.
+// ---------------------------------------------------------------------------
+constexpr int RS_TB = 4;       // tokens per workgroup
+constexpr int RS_EW = 16;      // experts per workgroup
+
+__global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
+  __shared__ __attribute__((aligned(16))) float zs[RS_TB][H];
+  __shared__ float red[RS_TB][4];
+  const int t0 = blockIdx.x * RS_TB;
+  const int nt = min(RS_TB, a.T - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e0 = RS_EW * blockIdx.y + 4 * wv;
+  float4 w[4][H / 256];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int j = 0; j < H / 256; ++j) w[e][j] = *(const float4*)(a.wr + (size_t)(e0 + e) * H + 4 * (64 * j + lane));
+  router_rows<RS_TB, H>(a, t0, &zs[0][0], &red[0][0], blockIdx.y == 0);
+  float acc[4][RS_TB];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int t = 0; t < RS_TB; ++t) acc[e][t] = 0.f;
+#pragma unroll
+  for (int j = 0; j < H / 256; ++j)
+#pragma unroll
+    for (int t = 0; t < RS_TB; ++t) {
+      const float4 z4 = *(const float4*)&zs[t][4 * (64 * j + lane)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[e][t] += w[e][j].x * z4.x + w[e][j].y * z4.y + w[e][j].z * z4.z + w[e][j].w * z4.w;
+    }
+  float mine = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int t = 0; t < RS_TB; ++t) {
+      const float v = wave_sum(acc[e][t]);
+      if (lane == e * RS_TB + t) mine = v;
+    }
+  const int e = lane / RS_TB, t = lane % RS_TB;
+  if (lane < 4 * RS_TB && t < nt)
+    a.logits[(size_t)(t0 + t) * E + e0 + e] = mine + (a.bias ? a.bias[e0 + e] : 0.f);
+}
+
+// Selection pass: wave = token, lane = expert.
+__global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t < a.T) select_top6(a.logits[(size_t)t * E + (threadIdx.x & 63)], a.ids + (size_t)t * TOPK, a.w + (size_t)t * TOPK);
 }
 
 // ---------------------------------------------------------------------------
@@ -2131,12 +2192,19 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, void* z, i
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+constexpr int RS_MIN_T = 8, RS_MAX_T = 1 << 30;
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   // measured: 4-token VALU workgroups win up to about a thousand tokens, where
   // re-reading W_r per workgroup starts to dominate and the 16-token MFMA
   // workgroups take over
-  if (a.T >= 1024) hipLaunchKernelGGL(router_mfma_kernel, dim3((a.T + RM_TB - 1) / RM_TB), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(router_kernel, dim3((a.T + RT_TB - 1) / RT_TB), dim3(256), 0, s, a);
+  if (a.logits && a.T >= RS_MIN_T && a.T < RS_MAX_T) {
+    hipLaunchKernelGGL(router_logits_kernel, dim3((a.T + RS_TB - 1) / RS_TB, E / RS_EW), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(router_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  } else if (a.T >= 1024) {
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((a.T + RM_TB - 1) / RM_TB), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(router_kernel, dim3((a.T + RT_TB - 1) / RT_TB), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

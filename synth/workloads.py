@@ -4,11 +4,14 @@ Shapes follow the decoder described on the franken_ocr pages: hidden 1280,
 64 routed experts with top-6 routing, expert intermediate 896 and the two
 shared experts fused into one SwiGLU of intermediate 1792 ("DeepSeek-V2 MoE
 decoder" in the Architecture section of the franken_ocr README; "One forward
-pass, left to right", step 6, of the browser demo page).  The five workloads
+pass, left to right", step 6, of the browser demo page).  The workloads
 are the synthetic stand-ins for the pages' workloads: one decode token, the
 11-layer decode step, 32 concurrent pages, the 273-row visual prefill
 (splice layout in the I/O contract of the Unlimited-OCR DeepEncoder ONNX
-model card) and an 8-page multi-page prefill.
+model card) and an 8-page multi-page prefill.  Two more are decode steps of
+the continuous-batch spine at its default of 128 active streams and its
+clamp of 256 (the batch-size setting under "focr ocr-batch" in the franken_ocr
+README's command reference): every stream adds one token per step.
 
 Every tensor comes from its own numpy ``SeedSequence(0, spawn_key=(w, l, t))``
 stream (w = workload index, l = layer, t = tensor id), so any layer can be
@@ -81,6 +84,12 @@ WORKLOADS = [
              QFmt(4, 128), QFmt(4, 128), "none", False, False),
     Workload(4, "multipage_prefill_2184tok_11layers_int4g64_zipf", 2184, 11, "bf16",
              QFmt(4, 64), QFmt(4, 64), "zipf2", True, True),
+    # continuous-batch decode: one step advances every active stream by one
+    # token; 128 streams is the batch spine's default, 256 its clamp
+    Workload(5, "continuous_batch_decode_128streams_11layers_int4g64_shared_int8g128", 128, 11, "f32",
+             QFmt(4, 64), QFmt(8, 128), "none", True, False),
+    Workload(6, "continuous_batch_decode_256streams_11layers_int4g64_shared_int8g128", 256, 11, "f32",
+             QFmt(4, 64), QFmt(8, 128), "none", True, False),
 ]
 
 

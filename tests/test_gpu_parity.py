@@ -179,6 +179,15 @@ def test_chain_multipage_prefill_11_layers_sampled(lib):
     _chain(4, 2184, sample)
 
 
+@pytest.mark.parametrize("wi", [5, 6])
+def test_chain_continuous_batch_decode_sampled(lib, wi):
+    """One continuous-batch decode step (128 or 256 streams, 11 chained layers)."""
+    T = WORKLOADS[wi].n_tokens
+    say(f"11-layer continuous-batch decode step, {T} streams, 16 sampled")
+    sample = np.sort(np.random.default_rng(wi).choice(T, 16, replace=False))
+    _chain(wi, T, sample)
+
+
 def _decode_step(wi, n_layers, xt, flags):
     from quantized_expert_ffn_moe_amd import binding as B
     packed = [packed_of(wi, li) for li in range(n_layers)]
