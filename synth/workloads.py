@@ -191,3 +191,48 @@ def make_tiny_layer(seed: int, E: int, H: int, I: int, Is: int, fmt: QFmt,
         "routed_fmt": fmt,
         "shared_fmt": sf,
     }
+
+
+# --------------------------------------------------------------------------
+# the decoder's dense ends: layer-0 SwiGLU MLP and lm_head (seed space 7)
+# --------------------------------------------------------------------------
+VOCAB = 129280
+DENSE_INTER = 6848
+_W_DENSE_HEAD = 7
+_T_HEAD_W, _T_HEAD_S = 20, 21
+_T_DG, _T_DU, _T_DD, _T_DGS, _T_DUS, _T_DDS = 22, 23, 24, 25, 26, 27
+_T_HIDDEN = 28
+
+
+def make_lm_head(dtype: str, group: int = 128, vocab: int = VOCAB) -> dict:
+    """lm_head weights [vocab][1280]: "bf16" (N(0, 0.02) rounded to bf16, as
+    16-bit patterns) or "int8" (codes in [-127, 127], f32 scales per group of
+    K).  Smaller vocabularies are prefixes of the full one."""
+    if dtype == "bf16":
+        w = (_rng(_W_DENSE_HEAD, 0, _T_HEAD_W).standard_normal((VOCAB, HIDDEN)) * 0.02).astype(np.float32)
+        return {"dtype": "bf16", "w": f32_to_bf16_bits(w[:vocab]), "vocab": vocab}
+    if dtype == "int8":
+        q = _codes(_rng(_W_DENSE_HEAD, 0, _T_HEAD_W), (VOCAB, HIDDEN), QFmt(8, group))
+        s = _scales(_rng(_W_DENSE_HEAD, 0, _T_HEAD_S), (VOCAB, HIDDEN // group))
+        return {"dtype": "int8", "q": q[:vocab], "s": s[:vocab], "group": group, "vocab": vocab}
+    raise ValueError(dtype)
+
+
+def make_dense_ffn(fmt: QFmt, inter: int = DENSE_INTER) -> dict:
+    """Codes and scales of a dense SwiGLU MLP 1280 -> inter -> 1280 (gate and
+    up [inter][1280], down [1280][inter]; scales per group of K)."""
+    H, g = HIDDEN, fmt.group
+    return {
+        "gate_q": _codes(_rng(_W_DENSE_HEAD, 1, _T_DG), (inter, H), fmt),
+        "up_q": _codes(_rng(_W_DENSE_HEAD, 1, _T_DU), (inter, H), fmt),
+        "down_q": _codes(_rng(_W_DENSE_HEAD, 1, _T_DD), (H, inter), fmt),
+        "gate_s": _scales(_rng(_W_DENSE_HEAD, 1, _T_DGS), (inter, H // g)),
+        "up_s": _scales(_rng(_W_DENSE_HEAD, 1, _T_DUS), (inter, H // g)),
+        "down_s": _scales(_rng(_W_DENSE_HEAD, 1, _T_DDS), (H, inter // g)),
+        "bits": fmt.bits, "group": g, "inter": inter,
+    }
+
+
+def make_hidden(n: int, batch: int = 0) -> np.ndarray:
+    """Residual-stream stand-in rows h ~ N(0, 1), f32 [n][1280]."""
+    return _rng(_W_DENSE_HEAD, _TOKEN_LAYER, _T_HIDDEN + 16 * batch).standard_normal((n, HIDDEN)).astype(np.float32)
