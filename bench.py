@@ -90,7 +90,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--path", choices=["chain", "layers"], default="chain")
-    ap.add_argument("--workload", choices=["decode", "prefill273", "multipage2184", "batch128", "batch256"],
+    ap.add_argument("--workload", choices=["decode", "prefill273", "multipage2184", "batch128", "batch256",
+                                           "lmhead_bf16", "lmhead_int8", "dense0"],
                     default="decode",
                     help="decode = the headline 11-layer decode step; the prefill workloads report MFMA "
                          "figures; batchN = one continuous-batch decode step of N streams (HBM figures)")
@@ -121,6 +122,8 @@ def main():
     from quantized_expert_ffn_moe_amd import binding as B
     from synth import WORKLOADS, make_layer, make_tokens
 
+    if args.workload.startswith("lmhead") or args.workload == "dense0":
+        return bench_dense(args)
     if args.workload != "decode":
         return bench_prefill(args)
 
@@ -293,6 +296,66 @@ def bench_prefill(args):
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_step": nbytes}
     print(json.dumps(out), flush=True)
+
+
+def bench_dense(args):
+    """The decoder's dense ends for one decode token: lm_head (bf16 or int8 G128,
+    129,280 rows) with the final norm and the greedy token, or the layer-0
+    SwiGLU MLP (int8 G64, intermediate 6848) with its input norm and residual
+    add.  Weight replicas rotate so that the 256 MiB last-level cache cannot
+    hold a call's weights."""
+    import numpy as np
+    import torch
+
+    from quantized_expert_ffn_moe_amd import binding as B
+    from synth import QFmt, make_dense_ffn, make_hidden, make_lm_head
+
+    H = 1280
+    stream = torch.cuda.Stream()
+    h = torch.from_numpy(make_hidden(1)).cuda()
+    if args.workload.startswith("lmhead"):
+        dtype = args.workload.split("_")[1]
+        head = make_lm_head(dtype)
+        reps = [B.lm_head_to_device(head) for _ in range(2)]
+        V = head["vocab"]
+        wbytes = V * H * (2 if dtype == "bf16" else 1) + (0 if dtype == "bf16" else V * (H // 128) * 4)
+        nbytes = wbytes + H * 4 + 8
+        tok = torch.empty(1, dtype=torch.int32, device="cuda")
+        tl = torch.empty(1, dtype=torch.float32, device="cuda")
+        ws = torch.empty(B.moe_lm_head_workspace_bytes(1, V), dtype=torch.uint8, device="cuda")
+        name = f"lm_head_{dtype}_129280_greedy_1tok"
+
+        def step(i):
+            B.moe_lm_head_argmax(h, reps[i % len(reps)], tok, tl, ws, B.MOE_NORM_INPUT, None, stream=stream)
+    else:
+        ffn = make_dense_ffn(QFmt(8, 64))
+        reps = [B.dense_ffn_to_device(ffn) for _ in range(12)]
+        I = ffn["inter"]
+        nbytes = 3 * I * H + 3 * I * (H // 64) * 4 + H * 4 * 3
+        ws = torch.empty(B.moe_dense_ffn_workspace_bytes(1, I), dtype=torch.uint8, device="cuda")
+        name = "dense_layer0_swiglu_int8g64_6848_1tok"
+
+        def step(i):
+            B.moe_dense_ffn_forward(h, reps[i % len(reps)], h, ws, B.MOE_NORM_INPUT | B.MOE_ACCUMULATE,
+                                    stream=stream)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": f"{name}: calls/s", "value": 1e3 / ms, "unit": "calls/s", "ms_per_step": ms,
+                      "steps": args.steps, "warmup": args.warmup, "dtype": "f32 FMA on decoded weights",
+                      "config": {"workload": name, "tokens": 1},
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_call": nbytes}}),
+          flush=True)
 
 
 if __name__ == "__main__":

@@ -19,7 +19,9 @@ MOE_FORCE_DECODE, MOE_FORCE_GROUPED = 8, 16
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 EXPORTS = ("moe_status_str", "moe_expert_code_bytes", "moe_expert_scale_count", "moe_pack_expert",
            "moe_workspace_bytes", "moe_layer_forward", "moe_rmsnorm", "moe_decode_workspace_bytes",
-           "moe_decode_workspace_init", "moe_decode_forward")
+           "moe_decode_workspace_init", "moe_decode_forward", "moe_lm_head_workspace_bytes",
+           "moe_lm_head_argmax", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_forward")
+MOE_HEAD_INT8, MOE_HEAD_BF16 = 8, 16
 DECODE_MAX_LAYERS = 16
 
 
@@ -67,6 +69,14 @@ def load():
     L.moe_decode_forward.restype = i32
     L.moe_decode_forward.argtypes = [vp, i32, vp, i32, ctypes.POINTER(LayerWeights), i32, i32, i32, i32,
                                      vp, vp, vp, sz, u32, vp]
+    L.moe_lm_head_workspace_bytes.restype = sz
+    L.moe_lm_head_workspace_bytes.argtypes = [i32, i32]
+    L.moe_lm_head_argmax.restype = i32
+    L.moe_lm_head_argmax.argtypes = [vp, i32, u32, vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.moe_dense_ffn_workspace_bytes.restype = sz
+    L.moe_dense_ffn_workspace_bytes.argtypes = [i32, i32]
+    L.moe_dense_ffn_forward.restype = i32
+    L.moe_dense_ffn_forward.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, u32, vp, sz, vp]
     _lib = L
     return L
 
@@ -210,3 +220,59 @@ def moe_decode_forward(x, y, packed_layers, topk_ids, topk_w, ws, flags=0, weigh
     check(load().moe_decode_forward(_ptr(x), x_dtype, _ptr(y), len(packed_layers), arr,
                                     p0["expert_bits"], p0["expert_group"], p0["shared_bits"], p0["shared_group"],
                                     _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), flags, _stream(stream)))
+
+
+# ----------------------------------------------------------------- dense ends (include/moe_dense.h)
+def _nibbles(codes):
+    """int4 codes [rows][K] (one per int8) -> [rows][K/2] bytes, element 2j in the low nibble."""
+    c = np.asarray(codes, dtype=np.int8).astype(np.uint8) & 0x0F
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _rows(codes, bits):
+    return np.ascontiguousarray(codes, dtype=np.int8).view(np.uint8) if bits == 8 else _nibbles(codes)
+
+
+def lm_head_to_device(head: dict, device="cuda"):
+    """lm_head weights as moe_lm_head_argmax takes them (row-major, no repacking)."""
+    import torch
+    if head["dtype"] == "bf16":
+        w = torch.from_numpy(np.ascontiguousarray(head["w"]).view(np.int16)).to(device)
+        return {"w": w, "bits": MOE_HEAD_BF16, "s": None, "group": 0, "vocab": head["vocab"]}
+    w = torch.from_numpy(np.ascontiguousarray(head["q"])).to(device)
+    s = torch.from_numpy(np.ascontiguousarray(head["s"], dtype=np.float32)).to(device)
+    return {"w": w, "bits": MOE_HEAD_INT8, "s": s, "group": head["group"], "vocab": head["vocab"]}
+
+
+def dense_ffn_to_device(ffn: dict, device="cuda"):
+    """Dense MLP codes (gate | up | down rows, int4 two per byte) and scales as
+    moe_dense_ffn_forward takes them."""
+    import torch
+    b = ffn["bits"]
+    codes = np.concatenate([_rows(ffn["gate_q"], b).reshape(-1), _rows(ffn["up_q"], b).reshape(-1),
+                            _rows(ffn["down_q"], b).reshape(-1)])
+    scales = np.concatenate([np.asarray(ffn[k], dtype=np.float32).reshape(-1) for k in ("gate_s", "up_s", "down_s")])
+    return {"q": torch.from_numpy(codes).to(device), "s": torch.from_numpy(scales).to(device),
+            "bits": b, "group": ffn["group"], "inter": ffn["inter"]}
+
+
+def moe_lm_head_workspace_bytes(n_tokens: int, vocab: int) -> int:
+    return load().moe_lm_head_workspace_bytes(n_tokens, vocab)
+
+
+def moe_lm_head_argmax(h, head: dict, token, token_logit, ws, flags: int = 0, logits=None, stream=None):
+    """Enqueue lm_head + greedy token for h [T,1280] f32."""
+    check(load().moe_lm_head_argmax(_ptr(h), h.shape[0], flags, _ptr(head["w"]), head["bits"], _ptr(head["s"]),
+                                    head["group"], head["vocab"], _ptr(logits), _ptr(token), _ptr(token_logit),
+                                    _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_dense_ffn_workspace_bytes(n_tokens: int, inter: int) -> int:
+    return load().moe_dense_ffn_workspace_bytes(n_tokens, inter)
+
+
+def moe_dense_ffn_forward(x, dense: dict, y, ws, flags: int = 0, stream=None):
+    """Enqueue the dense SwiGLU MLP for x [T,1280] f32 into y [T,1280] f32."""
+    check(load().moe_dense_ffn_forward(_ptr(x), x.shape[0], _ptr(dense["q"]), _ptr(dense["s"]), dense["bits"],
+                                       dense["group"], dense["inter"], _ptr(y), flags, _ptr(ws), ws.numel(),
+                                       _stream(stream)))

@@ -122,6 +122,37 @@ struct CombineArgs {
   float* y; int T; int accumulate;
 };
 
+// Dense ends of the decoder for a few tokens (lm_head + greedy token, the
+// layer-0 SwiGLU MLP): GEMVs over row-major weights.
+constexpr int DENSE_MAX_T = 4;
+constexpr int DENSE_MAX_INTER = 8192;
+constexpr int HEAD_STEPS = 8;                 // wave steps of 4 rows
+constexpr int HEAD_ROWS = 4 * 4 * HEAD_STEPS; // rows per workgroup (128)
+constexpr int DENSE_GU_STEPS = 2;
+struct HeadArgs {
+  const float* h; int T; int norm; float eps;   // [T][H]
+  const void* w; const float* s; int group;     // [vocab][H] bf16 or int8 (+ [vocab][H/group] scales)
+  int vocab;
+  float* logits;                                // [T][vocab] or null
+  float* cand;                                  // [workgroups][T][2]: best logit, its id (int bits)
+  int32_t* token; float* token_logit;           // [T]
+};
+struct DenseGateUpArgs {
+  const float* x; int T; int norm; float eps;   // [T][H]
+  const uint8_t* q; const float* s;             // gate [inter][H] then up [inter][H]; scales likewise
+  int bits, group, inter;
+  float* hmid;                                  // [T][inter]
+};
+struct DenseDownArgs {
+  const float* hmid; int T;
+  const uint8_t* q; const float* s;             // down [H][inter]; scales [H][inter/group]
+  int bits, group, inter;
+  float* y; int accumulate;                     // [T][H]
+};
+int head_workgroups(int vocab);
+hipError_t launch_head(const HeadArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_dense(const DenseGateUpArgs& g, const DenseDownArgs& d, hipStream_t s);
+
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 hipError_t launch_dec_items(const DecItemsArgs& a, int T, hipStream_t s);
 hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s);

@@ -10,11 +10,11 @@ import pytest
 from quantized_expert_ffn_moe_amd import binding as B
 from synth import QFmt, make_tiny_layer
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 
 def test_every_declared_symbol_is_exported(lib):
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(INCLUDE, f)).read() for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h"))
     names = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, re.M))
     assert names == set(B.EXPORTS), names
     for n in names:
@@ -191,3 +191,45 @@ def test_decode_forward_validation(lib):
     assert lib.moe_decode_workspace_init(None, 0, None) == 1
     assert lib.moe_decode_workspace_init(A, 16, None) == 5
     assert B.moe_decode_workspace_bytes() > 224 * 1280 * 4
+
+
+# ----------------------------------------------------------------- dense ends: validation only
+def test_lm_head_validation(lib):
+    A = 0x10000                                  # aligned fake device addresses: nothing is launched
+    ok = dict(h=A, T=1, flags=0, w=A, bits=16, s=None, g=0, vocab=129280, logits=None, tok=A, tl=A, ws=A,
+              wsb=B.moe_lm_head_workspace_bytes(1, 129280))
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.moe_lm_head_argmax(a["h"], a["T"], a["flags"], a["w"], a["bits"], a["s"], a["g"], a["vocab"],
+                                      a["logits"], a["tok"], a["tl"], a["ws"], a["wsb"], None)
+    assert call(h=None) == 1 and call(tok=None) == 1
+    assert call(bits=4) == 3 and call(bits=8, s=A, g=48) == 3 and call(bits=8, s=None, g=128) == 1
+    assert call(T=5) == 2 and call(vocab=0) == 2 and call(T=-1) == 2
+    assert call(flags=4) == 7
+    assert call(h=A + 4) == 4 and call(tl=A + 2) == 4
+    assert call(wsb=16) == 5
+    assert call(T=0) == 0                        # nothing to do
+    assert B.moe_lm_head_workspace_bytes(5, 10) == 0 and B.moe_lm_head_workspace_bytes(1, 0) == 0
+    assert B.moe_lm_head_workspace_bytes(4, 129280) >= 1010 * 4 * 8
+
+
+def test_dense_ffn_validation(lib):
+    A = 0x10000
+    ok = dict(x=A, T=2, q=A, s=A, bits=8, g=64, inter=6848, y=A, flags=0, ws=A,
+              wsb=B.moe_dense_ffn_workspace_bytes(2, 6848))
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.moe_dense_ffn_forward(a["x"], a["T"], a["q"], a["s"], a["bits"], a["g"], a["inter"], a["y"],
+                                         a["flags"], a["ws"], a["wsb"], None)
+    assert call(x=None) == 1 and call(s=None) == 1
+    assert call(bits=2) == 3 and call(g=16) == 3
+    assert call(inter=6848 + 32) == 2 and call(g=128) == 2      # 6848 is not a multiple of 128
+    assert call(T=5) == 2 and call(inter=8192 + 64) == 2
+    assert call(flags=8) == 7
+    assert call(y=A + 8) == 4 and call(s=A + 2) == 4
+    assert call(wsb=100) == 5
+    assert call(T=0) == 0
+    assert B.moe_dense_ffn_workspace_bytes(2, 6848) >= 2 * 6848 * 4
+    assert B.moe_dense_ffn_workspace_bytes(1, 100) == 0
