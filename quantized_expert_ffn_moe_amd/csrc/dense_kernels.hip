@@ -28,8 +28,11 @@ typedef unsigned int u32x4d __attribute__((vector_size(16)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dense_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
+// weights are read once per call: non-temporal loads (they would only evict
+// the activations from the caches)
+constexpr int CPOL_NT = 2;
 __device__ __forceinline__ uint4 dload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4d v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  const u32x4d v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_NT);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ float dload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -97,7 +100,8 @@ __device__ __forceinline__ void rows_to_lds(const float* x, int T, int norm, flo
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int u = tid + 256 * j;
-    v[j] = dload16(rx, u < NU ? (uint32_t)u * 16 : OUT_OF_RANGE);
+    const u32x4d q = __builtin_amdgcn_raw_buffer_load_b128(rx, u < NU ? (uint32_t)u * 16 : OUT_OF_RANGE, 0, 0);
+    v[j] = make_uint4(q[0], q[1], q[2], q[3]);
   }
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -220,36 +224,32 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
 #pragma unroll
     for (int w = 1; w < 4; ++w)
       if (better(cv[w][tid], ci[w][tid], v, i)) { v = cv[w][tid]; i = ci[w][tid]; }
-    a.cand[((size_t)blockIdx.x * NT + tid) * 2] = v;
-    a.cand[((size_t)blockIdx.x * NT + tid) * 2 + 1] = __int_as_float(i);
+    a.cand[((size_t)tid * gridDim.x + blockIdx.x) * 2] = v;
+    a.cand[((size_t)tid * gridDim.x + blockIdx.x) * 2 + 1] = __int_as_float(i);
   }
 }
 
-// Greedy token of token t (= blockIdx.x) from the n_wg workgroup candidates.
-__global__ __launch_bounds__(256) void head_select_kernel(HeadArgs a, int n_wg) {
-  __shared__ float sv[256];
-  __shared__ int si[256];
-  const int t = blockIdx.x, tid = threadIdx.x;
+// Greedy token of token t (= blockIdx.x) from the n_wg workgroup candidates
+// ([T][n_wg] (logit, id) pairs): one wave, each lane scans a strided share,
+// then a butterfly over the lanes.
+__global__ __launch_bounds__(64) void head_select_kernel(HeadArgs a, int n_wg) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const float2* c = (const float2*)a.cand + (size_t)t * n_wg;
   float v = -__builtin_inff();
   int i = -1;
-  for (int w = tid; w < n_wg; w += 256) {
-    const float cvv = a.cand[((size_t)w * a.T + t) * 2];
-    const int cii = __float_as_int(a.cand[((size_t)w * a.T + t) * 2 + 1]);
-    if (better(cvv, cii, v, i)) { v = cvv; i = cii; }
+  for (int w = lane; w < n_wg; w += 64) {
+    const float2 q = c[w];
+    if (better(q.x, __float_as_int(q.y), v, i)) { v = q.x; i = __float_as_int(q.y); }
   }
-  sv[tid] = v;
-  si[tid] = i;
-  __syncthreads();
-  for (int half = 128; half > 0; half >>= 1) {
-    if (tid < half && better(sv[tid + half], si[tid + half], sv[tid], si[tid])) {
-      sv[tid] = sv[tid + half];
-      si[tid] = si[tid + half];
-    }
-    __syncthreads();
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    const float ov = __shfl_xor(v, d);
+    const int oi = __shfl_xor(i, d);
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
   }
-  if (tid == 0) {
-    a.token[t] = si[0];
-    a.token_logit[t] = sv[0];
+  if (lane == 0) {
+    a.token[t] = i;
+    a.token_logit[t] = v;
   }
 }
 
@@ -287,11 +287,12 @@ __global__ __launch_bounds__(256) void dense_gateup_kernel(DenseGateUpArgs a) {
       sc[slot][m] = dload4(rs, live ? (row * ng + (EPP * p) / a.group) * 4 : OUT_OF_RANGE);
     }
   };
+  static_assert(DENSE_GU_STEPS == 2, "both steps' weights are in flight from the start");
   load(0, 0);
+  load(1, 1);
   rows_to_lds<NT>(a.x, a.T, a.norm, a.eps, xs, red);
 #pragma unroll
   for (int s = 0; s < DENSE_GU_STEPS; ++s) {
-    if (s + 1 < DENSE_GU_STEPS) load(s + 1, (s + 1) & 1);
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.f;
@@ -337,7 +338,8 @@ __global__ __launch_bounds__(256) void dense_down_kernel(DenseDownArgs a) {
   for (int u = tid; u < NT * XS / 4; u += 256) {
     const int t = u / (XS / 4), k = u % (XS / 4);
     const bool live = t < a.T && k < nq;
-    *(uint4*)&xs[4 * u] = dload16(rh, live ? ((uint32_t)t * a.inter + 4 * k) * 4 : OUT_OF_RANGE);
+    const u32x4d q = __builtin_amdgcn_raw_buffer_load_b128(rh, live ? ((uint32_t)t * a.inter + 4 * k) * 4 : OUT_OF_RANGE, 0, 0);
+    *(uint4*)&xs[4 * u] = make_uint4(q[0], q[1], q[2], q[3]);
   }
   __syncthreads();
   float acc[NT];
@@ -374,7 +376,7 @@ hipError_t launch_head(const HeadArgs& a, bool bf16, hipStream_t s) {
     case 3: launch_head_nt<3>(a, bf16, s); break;
     default: launch_head_nt<4>(a, bf16, s); break;
   }
-  hipLaunchKernelGGL(head_select_kernel, dim3(a.T), dim3(256), 0, s, a, head_workgroups(a.vocab));
+  hipLaunchKernelGGL(head_select_kernel, dim3(a.T), dim3(64), 0, s, a, head_workgroups(a.vocab));
   return hipGetLastError();
 }
 

@@ -126,15 +126,15 @@ struct CombineArgs {
 // layer-0 SwiGLU MLP): GEMVs over row-major weights.
 constexpr int DENSE_MAX_T = 4;
 constexpr int DENSE_MAX_INTER = 8192;
-constexpr int HEAD_STEPS = 8;                 // wave steps of 4 rows
-constexpr int HEAD_ROWS = 4 * 4 * HEAD_STEPS; // rows per workgroup (128)
+constexpr int HEAD_STEPS = 16;                // wave steps of 4 rows
+constexpr int HEAD_ROWS = 4 * 4 * HEAD_STEPS; // rows per workgroup (256)
 constexpr int DENSE_GU_STEPS = 2;
 struct HeadArgs {
   const float* h; int T; int norm; float eps;   // [T][H]
   const void* w; const float* s; int group;     // [vocab][H] bf16 or int8 (+ [vocab][H/group] scales)
   int vocab;
   float* logits;                                // [T][vocab] or null
-  float* cand;                                  // [workgroups][T][2]: best logit, its id (int bits)
+  float* cand;                                  // [T][workgroups][2]: best logit, its id (int bits)
   int32_t* token; float* token_logit;           // [T]
 };
 struct DenseGateUpArgs {
