@@ -236,3 +236,36 @@ def make_dense_ffn(fmt: QFmt, inter: int = DENSE_INTER) -> dict:
 def make_hidden(n: int, batch: int = 0) -> np.ndarray:
     """Residual-stream stand-in rows h ~ N(0, 1), f32 [n][1280]."""
     return _rng(_W_DENSE_HEAD, _TOKEN_LAYER, _T_HIDDEN + 16 * batch).standard_normal((n, HIDDEN)).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# R-SWA attention decode inputs (seed space 8)
+# --------------------------------------------------------------------------
+HEADS = 10
+HEAD_DIM = 128
+RSWA_WINDOW = 128
+_W_RSWA = 8
+
+
+def make_rswa(n_streams: int, n_ref: int, n_gen=None, seed: int = 0) -> dict:
+    """One decode step of n_streams independent streams: q, the new key and
+    value [S][10][128] f32 ~ N(0, 1); the frozen reference block and the ring
+    [S][10][n][128] as bf16 bit patterns of N(0, 1) draws (the ring as left by
+    earlier steps); n_gen [S] int32, generated tokens before this one (by
+    default a spread from 0 to past several ring wraps)."""
+    r = _rng(_W_RSWA, seed, 0)
+    S, Hh, D, W = n_streams, HEADS, HEAD_DIM, RSWA_WINDOW
+    d = {
+        "q": r.standard_normal((S, Hh, D)).astype(np.float32),
+        "k_new": r.standard_normal((S, Hh, D)).astype(np.float32),
+        "v_new": r.standard_normal((S, Hh, D)).astype(np.float32),
+        "ref_k": f32_to_bf16_bits(r.standard_normal((S, Hh, n_ref, D)).astype(np.float32)),
+        "ref_v": f32_to_bf16_bits(r.standard_normal((S, Hh, n_ref, D)).astype(np.float32)),
+        "ring_k": f32_to_bf16_bits(r.standard_normal((S, Hh, W, D)).astype(np.float32)),
+        "ring_v": f32_to_bf16_bits(r.standard_normal((S, Hh, W, D)).astype(np.float32)),
+    }
+    if n_gen is None:
+        n_gen = r.integers(0, 4 * W, size=S)
+    d["n_gen"] = np.asarray(n_gen, dtype=np.int32).reshape(S)
+    d["n_ref"] = n_ref
+    return d
