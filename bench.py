@@ -91,7 +91,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--path", choices=["chain", "layers"], default="chain")
     ap.add_argument("--workload", choices=["decode", "prefill273", "multipage2184", "batch128", "batch256",
-                                           "lmhead_bf16", "lmhead_int8", "dense0"],
+                                           "lmhead_bf16", "lmhead_int8", "dense0", "rswa128"],
                     default="decode",
                     help="decode = the headline 11-layer decode step; the prefill workloads report MFMA "
                          "figures; batchN = one continuous-batch decode step of N streams (HBM figures)")
@@ -124,6 +124,8 @@ def main():
 
     if args.workload.startswith("lmhead") or args.workload == "dense0":
         return bench_dense(args)
+    if args.workload == "rswa128":
+        return bench_rswa(args)
     if args.workload != "decode":
         return bench_prefill(args)
 
@@ -355,6 +357,43 @@ def bench_dense(args):
                       "config": {"workload": name, "tokens": 1},
                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_call": nbytes}}),
+          flush=True)
+
+
+def bench_rswa(args):
+    """One R-SWA attention decode step of 128 streams (reference block 288 =
+    the 273-row visual prefill plus a 15-token prompt, ring full), three KV
+    replicas rotated so that the last-level cache cannot hold a step's KV."""
+    import torch
+
+    from quantized_expert_ffn_moe_amd import binding as B
+    from synth import make_rswa
+
+    S, n_ref = 128, 288
+    reps = [B.rswa_to_device(make_rswa(S, n_ref, n_gen=[127 + 37 * s for s in range(S)], seed=r)) for r in range(3)]
+    out = torch.empty(S, 10, 128, dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.moe_rswa_workspace_bytes(S, n_ref), dtype=torch.uint8, device="cuda")
+    kv = S * 10 * (n_ref + 128) * 128 * 2 * 2
+    nbytes = kv + S * 10 * 128 * 4 * 4 + S * 10 * 128 * 2 * 2 + S * 4
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            B.moe_rswa_decode(reps[i % 3], out, ws, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            B.moe_rswa_decode(reps[i % 3], out, ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    name = "rswa_decode_128streams_ref288_ring128"
+    print(json.dumps({"metric": f"{name}: tokens/s", "value": S / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+                      "steps": args.steps, "warmup": args.warmup, "dtype": "f32 on bf16 KV",
+                      "config": {"workload": name, "streams": S, "n_ref": n_ref},
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_step": nbytes}}),
           flush=True)
 
 

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 EXPORTS = ("moe_status_str", "moe_expert_code_bytes", "moe_expert_scale_count", "moe_pack_expert",
            "moe_workspace_bytes", "moe_layer_forward", "moe_rmsnorm", "moe_decode_workspace_bytes",
            "moe_decode_workspace_init", "moe_decode_forward", "moe_lm_head_workspace_bytes",
-           "moe_lm_head_argmax", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_forward")
+           "moe_lm_head_argmax", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_forward",
+           "moe_rswa_workspace_bytes", "moe_rswa_decode")
 MOE_HEAD_INT8, MOE_HEAD_BF16 = 8, 16
 DECODE_MAX_LAYERS = 16
 
@@ -77,6 +78,10 @@ def load():
     L.moe_dense_ffn_workspace_bytes.argtypes = [i32, i32]
     L.moe_dense_ffn_forward.restype = i32
     L.moe_dense_ffn_forward.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, u32, vp, sz, vp]
+    L.moe_rswa_workspace_bytes.restype = sz
+    L.moe_rswa_workspace_bytes.argtypes = [i32, i32]
+    L.moe_rswa_decode.restype = i32
+    L.moe_rswa_decode.argtypes = [i32, i32] + [vp] * 9 + [vp, sz, vp]
     _lib = L
     return L
 
@@ -276,3 +281,26 @@ def moe_dense_ffn_forward(x, dense: dict, y, ws, flags: int = 0, stream=None):
     check(load().moe_dense_ffn_forward(_ptr(x), x.shape[0], _ptr(dense["q"]), _ptr(dense["s"]), dense["bits"],
                                        dense["group"], dense["inter"], _ptr(y), flags, _ptr(ws), ws.numel(),
                                        _stream(stream)))
+
+
+# ----------------------------------------------------------------- R-SWA decode step (include/moe_attn.h)
+def rswa_to_device(d: dict, device="cuda"):
+    """Inputs of one R-SWA decode step as device tensors (bf16 KV as int16 bit patterns)."""
+    import torch
+    out = {k: torch.from_numpy(np.ascontiguousarray(d[k])).to(device) for k in ("q", "k_new", "v_new", "n_gen")}
+    for k in ("ref_k", "ref_v", "ring_k", "ring_v"):
+        out[k] = torch.from_numpy(np.ascontiguousarray(d[k]).view(np.int16)).to(device)
+    out["n_ref"] = d["n_ref"]
+    return out
+
+
+def moe_rswa_workspace_bytes(n_streams: int, n_ref: int) -> int:
+    return load().moe_rswa_workspace_bytes(n_streams, n_ref)
+
+
+def moe_rswa_decode(dev: dict, out, ws, stream=None):
+    """Enqueue one R-SWA decode step (updates dev["ring_k"], dev["ring_v"] in place)."""
+    S = dev["q"].shape[0]
+    check(load().moe_rswa_decode(S, dev["n_ref"], _ptr(dev["q"]), _ptr(dev["k_new"]), _ptr(dev["v_new"]),
+                                 _ptr(dev["ref_k"]), _ptr(dev["ref_v"]), _ptr(dev["ring_k"]), _ptr(dev["ring_v"]),
+                                 _ptr(dev["n_gen"]), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))

@@ -3,7 +3,8 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["csrc/moe_kernels.hip", "csrc/dense_kernels.hip", "csrc/moe_api.cpp", "csrc/dense_api.cpp"]
+SOURCES = ["csrc/moe_kernels.hip", "csrc/dense_kernels.hip", "csrc/attn_kernels.hip", "csrc/moe_api.cpp",
+           "csrc/dense_api.cpp", "csrc/attn_api.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # no packed-FP32 instructions in any generated code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -153,6 +153,23 @@ int head_workgroups(int vocab);
 hipError_t launch_head(const HeadArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_dense(const DenseGateUpArgs& g, const DenseDownArgs& d, hipStream_t s);
 
+// One R-SWA attention decode step for S independent streams.
+constexpr int ATT_HEADS = 10, ATT_D = 128;
+constexpr int RSWA_W = 128;                   // ring slots of generated tokens
+constexpr int RSWA_CHUNK = 64;                // keys per split-KV workgroup
+constexpr int RSWA_PART = 132;                // floats per partial: m, l, 128 outputs, pad
+struct RswaArgs {
+  int S, n_ref, n_chunks; float scale;
+  const float* q; const float* k_new; const float* v_new;   // [S][10][128]
+  const uint16_t* ref_k; const uint16_t* ref_v;             // [S][10][n_ref][128] bf16
+  uint16_t* ring_k; uint16_t* ring_v;                       // [S][10][128][128] bf16
+  const int32_t* n_gen;                                     // [S]
+  float* part;                                              // [S][10][n_chunks][RSWA_PART]
+  float* out;                                               // [S][10][128]
+};
+int rswa_chunks(int n_ref);
+hipError_t launch_rswa(const RswaArgs& a, hipStream_t s);
+
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 hipError_t launch_dec_items(const DecItemsArgs& a, int T, hipStream_t s);
 hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s);

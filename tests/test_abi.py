@@ -233,3 +233,21 @@ def test_dense_ffn_validation(lib):
     assert call(T=0) == 0
     assert B.moe_dense_ffn_workspace_bytes(2, 6848) >= 2 * 6848 * 4
     assert B.moe_dense_ffn_workspace_bytes(1, 100) == 0
+
+
+def test_rswa_validation(lib):
+    A = 0x10000
+    ok = dict(S=2, n_ref=288, q=A, k=A, v=A, rk=A, rv=A, gk=A, gv=A, ng=A, out=A, ws=A,
+              wsb=B.moe_rswa_workspace_bytes(2, 288))
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.moe_rswa_decode(a["S"], a["n_ref"], a["q"], a["k"], a["v"], a["rk"], a["rv"], a["gk"], a["gv"],
+                                   a["ng"], a["out"], a["ws"], a["wsb"], None)
+    assert call(q=None) == 1 and call(ng=None) == 1 and call(rk=None) == 1
+    assert call(S=-1) == 2 and call(S=4097) == 2 and call(n_ref=65537) == 2
+    assert call(q=A + 4) == 4 and call(ng=A + 2) == 4 and call(rk=A + 8) == 4
+    assert call(wsb=64) == 5
+    assert call(S=0) == 0
+    assert B.moe_rswa_workspace_bytes(1, 0) >= 10 * 2 * 132 * 4       # ring only: two chunks of 64
+    assert B.moe_rswa_workspace_bytes(2, 288) >= 2 * 10 * 7 * 132 * 4
