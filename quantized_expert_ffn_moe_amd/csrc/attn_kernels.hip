@@ -6,15 +6,19 @@
 // model. In this tab.", "One forward pass, left to right", step 6: ten heads
 // of dimension 128).
 //
-// Three launches per step:
-//  1. the new key and value, rounded to bf16, go into ring slot n_gen mod 128;
-//  2. split-KV partials: a workgroup takes one (stream, head, chunk of 64 keys)
-//     of the key list [reference block | live ring slots], stages the chunk's
-//     keys and values in LDS with coalesced 16-byte loads, and leaves the
-//     chunk's max score m, sum of exp(s - m) and unnormalised output;
-//  3. per (stream, head) the chunks merge in chunk order (fixed, so the result
-//     is bitwise reproducible) into softmax(q k / sqrt(128)) v.
-// The KV streams through once per step: HBM-bound for many streams.
+// The key list of a (stream, head) is [reference block | live ring slots],
+// taken in chunks of 64 keys whose keys and values are staged in LDS as bf16
+// with coalesced 16-byte loads.  The new token's key and value, rounded to
+// bf16, stand in for ring slot n_gen mod 128 and are written there by the one
+// workgroup whose chunk holds that slot (no other workgroup reads it).
+//  * Many streams: one workgroup per (stream, head) walks its chunks with an
+//    online softmax (running max, sum and output rescaled per chunk), the next
+//    chunk's loads in flight while the current one is multiplied.
+//  * Few streams: split-KV, one workgroup per (stream, head, chunk) leaving
+//    the chunk's max score, sum of exp(s - max) and unnormalised output, then
+//    a merge in chunk order.
+// Both orders are fixed, so results are bitwise reproducible.  The KV streams
+// through once per step: HBM-bound for many streams.
 #include "moe_internal.h"
 #include "moe_wave.h"
 
@@ -30,64 +34,75 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ int live_slots(int n_gen) { return min(max(n_gen, 0) + 1, RSWA_W); }
 }  // namespace
 
-// 1. ring write: one workgroup per stream, thread = (head, 5 dims)
-__global__ __launch_bounds__(256) void rswa_ring_write_kernel(RswaArgs a) {
-  const int s = blockIdx.x;
-  const int slot = max(a.n_gen[s], 0) % RSWA_W;
-  for (int f = threadIdx.x; f < ATT_HEADS * ATT_D; f += 256) {
-    const int h = f / ATT_D, d = f % ATT_D;
-    const size_t src = ((size_t)s * ATT_HEADS + h) * ATT_D + d;
-    const size_t dst = (((size_t)s * ATT_HEADS + h) * RSWA_W + slot) * ATT_D + d;
-    a.ring_k[dst] = to_bf16(a.k_new[src]);
-    a.ring_v[dst] = to_bf16(a.v_new[src]);
-  }
-}
-
-// 2. partials of one chunk: blockIdx = (chunk, head, stream)
-__global__ __launch_bounds__(256) void rswa_chunk_kernel(RswaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t kl[RSWA_CHUNK * ATT_D];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[RSWA_CHUNK * ATT_D];
-  __shared__ __attribute__((aligned(16))) float ql[ATT_D];
-  __shared__ float pl[RSWA_CHUNK];
-  __shared__ float red[8];
-  __shared__ float acc2[ATT_D];
-  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n_live = live_slots(a.n_gen[s]);
-  const int n_keys = a.n_ref + n_live;
-  const int j0 = c * RSWA_CHUNK;
-  float* part = a.part + (((size_t)s * ATT_HEADS + h) * a.n_chunks + c) * RSWA_PART;
-  if (j0 >= n_keys) {                       // past this stream's keys: an empty partial
-    if (tid < RSWA_PART) part[tid] = tid == 0 ? -__builtin_inff() : 0.f;
-    return;
-  }
+// The key list of one (stream, head).
+struct KeyList {
+  const uint16_t *rk, *rv;      // reference block rows [n_ref][128]
+  uint16_t *gk, *gv;            // ring rows [128][128]
+  const float *kn, *vn;         // the new token's key and value [128]
+  int n_ref, n_keys, slot;      // the new token sits in ring slot `slot`
+};
+__device__ __forceinline__ KeyList key_list(const RswaArgs& a, int s, int h) {
+  KeyList L;
   const size_t sh = (size_t)s * ATT_HEADS + h;
-  const uint16_t* rk = a.ref_k + sh * a.n_ref * ATT_D;
-  const uint16_t* rv = a.ref_v + sh * a.n_ref * ATT_D;
-  const uint16_t* gk = a.ring_k + sh * RSWA_W * ATT_D;
-  const uint16_t* gv = a.ring_v + sh * RSWA_W * ATT_D;
-  // stage the chunk: 64 rows x 16 uint4 per matrix, 4 of each per thread
-  uint4 kb[4], vb[4];
+  L.rk = a.ref_k + sh * a.n_ref * ATT_D;
+  L.rv = a.ref_v + sh * a.n_ref * ATT_D;
+  L.gk = a.ring_k + sh * RSWA_W * ATT_D;
+  L.gv = a.ring_v + sh * RSWA_W * ATT_D;
+  L.kn = a.k_new + sh * ATT_D;
+  L.vn = a.v_new + sh * ATT_D;
+  const int g = max(a.n_gen[s], 0);
+  L.n_ref = a.n_ref;
+  L.n_keys = a.n_ref + min(g + 1, RSWA_W);
+  L.slot = g % RSWA_W;
+  return L;
+}
+// The 16-byte pieces f = tid + 256 i (i < 4) of a chunk's key and value rows
+// (row f / 16, piece f % 16): loaded from the reference block or the ring, or
+// for the new token's slot formed from its f32 key and value (and written to
+// the ring).  Keys past the end read as zeros.
+__device__ __forceinline__ uint4 pack8(const float* p) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  return make_uint4((uint32_t)to_bf16(a.x) | ((uint32_t)to_bf16(a.y) << 16),
+                    (uint32_t)to_bf16(a.z) | ((uint32_t)to_bf16(a.w) << 16),
+                    (uint32_t)to_bf16(b.x) | ((uint32_t)to_bf16(b.y) << 16),
+                    (uint32_t)to_bf16(b.z) | ((uint32_t)to_bf16(b.w) << 16));
+}
+__device__ __forceinline__ void fetch_chunk(const KeyList& L, int j0, uint4 (&kb)[4], uint4 (&vb)[4]) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int f = tid + 256 * i, j = j0 + f / 16, u = f % 16;
-    const uint16_t* pk = nullptr;
-    const uint16_t* pv = nullptr;
-    if (j < a.n_ref) { pk = rk + (size_t)j * ATT_D; pv = rv + (size_t)j * ATT_D; }
-    else if (j < n_keys) { pk = gk + (size_t)(j - a.n_ref) * ATT_D; pv = gv + (size_t)(j - a.n_ref) * ATT_D; }
-    kb[i] = pk ? *((const uint4*)pk + u) : make_uint4(0, 0, 0, 0);
-    vb[i] = pv ? *((const uint4*)pv + u) : make_uint4(0, 0, 0, 0);
+    kb[i] = make_uint4(0, 0, 0, 0);
+    vb[i] = make_uint4(0, 0, 0, 0);
+    if (j < L.n_ref) {
+      kb[i] = *((const uint4*)(L.rk + (size_t)j * ATT_D) + u);
+      vb[i] = *((const uint4*)(L.rv + (size_t)j * ATT_D) + u);
+    } else if (j < L.n_keys) {
+      const int r = j - L.n_ref;
+      if (r == L.slot) {
+        kb[i] = pack8(L.kn + 8 * u);
+        vb[i] = pack8(L.vn + 8 * u);
+        *((uint4*)(L.gk + (size_t)r * ATT_D) + u) = kb[i];
+        *((uint4*)(L.gv + (size_t)r * ATT_D) + u) = vb[i];
+      } else {
+        kb[i] = *((const uint4*)(L.gk + (size_t)r * ATT_D) + u);
+        vb[i] = *((const uint4*)(L.gv + (size_t)r * ATT_D) + u);
+      }
+    }
   }
-  if (tid < ATT_D) ql[tid] = a.q[sh * ATT_D + tid] * a.scale;
+}
+__device__ __forceinline__ void stage_chunk(uint16_t* kl, uint16_t* vl, const uint4 (&kb)[4], const uint4 (&vb)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int f = tid + 256 * i;
+    const int f = threadIdx.x + 256 * i;
     *((uint4*)kl + f) = kb[i];
     *((uint4*)vl + f) = vb[i];
   }
-  __syncthreads();
-  // scores: thread (key j = tid / 4, quarter qq = tid % 4 of the 128 dims)
-  const int j = tid >> 2, qq = tid & 3;
+}
+// score of key j = tid / 4 over the quarter tid % 4 of the dims, summed over
+// the 4 lanes of the key (all four hold it)
+__device__ __forceinline__ float chunk_score(const uint16_t* kl, const float* ql) {
+  const int j = threadIdx.x >> 2, qq = threadIdx.x & 3;
   float sc = 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -99,8 +114,87 @@ __global__ __launch_bounds__(256) void rswa_chunk_kernel(RswaArgs a) {
     sc = __fmaf_rn(bf16_lo(w.z), q1.x, sc); sc = __fmaf_rn(bf16_hi(w.z), q1.y, sc);
     sc = __fmaf_rn(bf16_lo(w.w), q1.z, sc); sc = __fmaf_rn(bf16_hi(w.w), q1.w, sc);
   }
-  sc = group_sum<4>(sc);
-  const bool valid = j0 + j < n_keys;
+  return group_sum<4>(sc);
+}
+// sum over the keys of this thread's half (tid / 128) of p_j v_j[d], d = tid % 128
+__device__ __forceinline__ float chunk_pv(const uint16_t* vl, const float* pl) {
+  const int d = threadIdx.x & (ATT_D - 1), half = threadIdx.x >> 7;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int jj = 0; jj < RSWA_CHUNK / 2; ++jj) {
+    const int k = half * (RSWA_CHUNK / 2) + jj;
+    acc = __fmaf_rn(pl[k], __uint_as_float((uint32_t)vl[k * ATT_D + d] << 16), acc);
+  }
+  return acc;
+}
+
+// Many streams: one workgroup per (head, stream) = blockIdx (x, y).
+__global__ __launch_bounds__(256) void rswa_row_kernel(RswaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t kl[RSWA_CHUNK * ATT_D];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[RSWA_CHUNK * ATT_D];
+  __shared__ __attribute__((aligned(16))) float ql[ATT_D];
+  __shared__ float pl[RSWA_CHUNK];
+  __shared__ float red[8];
+  __shared__ float acc2[ATT_D];
+  const int h = blockIdx.x, s = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid >> 2, qq = tid & 3;
+  const KeyList L = key_list(a, s, h);
+  const int nch = (L.n_keys + RSWA_CHUNK - 1) / RSWA_CHUNK;
+  uint4 kb[4], vb[4];
+  fetch_chunk(L, 0, kb, vb);
+  if (tid < ATT_D) ql[tid] = a.q[((size_t)s * ATT_HEADS + h) * ATT_D + tid] * a.scale;
+  float m_run = -__builtin_inff(), l_run = 0.f, acc = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    __syncthreads();                              // previous chunk's LDS reads are done
+    stage_chunk(kl, vl, kb, vb);
+    if (c + 1 < nch) fetch_chunk(L, (c + 1) * RSWA_CHUNK, kb, vb);
+    __syncthreads();
+    const bool valid = c * RSWA_CHUNK + j < L.n_keys;
+    float sc = chunk_score(kl, ql);
+    if (!valid) sc = -__builtin_inff();
+    const float wm = wave_max(sc);
+    if (lane == 0) red[wv] = wm;
+    __syncthreads();
+    const float m_new = fmaxf(m_run, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    const float p = valid ? expf(sc - m_new) : 0.f;
+    if (qq == 0) pl[j] = p;
+    const float ws = wave_sum(qq == 0 ? p : 0.f);
+    if (lane == 0) red[4 + wv] = ws;
+    __syncthreads();
+    const float resc = expf(m_run - m_new);       // 0 on the first chunk
+    l_run = __fmaf_rn(l_run, resc, (red[4] + red[5]) + (red[6] + red[7]));
+    acc = __fmaf_rn(acc, resc, chunk_pv(vl, pl));
+    m_run = m_new;
+  }
+  if (tid >= ATT_D) acc2[tid & (ATT_D - 1)] = acc;
+  __syncthreads();
+  if (tid < ATT_D) a.out[((size_t)s * ATT_HEADS + h) * ATT_D + tid] = (acc + acc2[tid]) / l_run;
+}
+
+// 2. partials of one chunk: blockIdx = (chunk, head, stream)
+__global__ __launch_bounds__(256) void rswa_chunk_kernel(RswaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t kl[RSWA_CHUNK * ATT_D];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[RSWA_CHUNK * ATT_D];
+  __shared__ __attribute__((aligned(16))) float ql[ATT_D];
+  __shared__ float pl[RSWA_CHUNK];
+  __shared__ float red[8];
+  __shared__ float acc2[ATT_D];
+  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid >> 2, qq = tid & 3;
+  const KeyList L = key_list(a, s, h);
+  const int j0 = c * RSWA_CHUNK;
+  float* part = a.part + (((size_t)s * ATT_HEADS + h) * a.n_chunks + c) * RSWA_PART;
+  if (j0 >= L.n_keys) {                     // past this stream's keys: an empty partial
+    if (tid < RSWA_PART) part[tid] = tid == 0 ? -__builtin_inff() : 0.f;
+    return;
+  }
+  uint4 kb[4], vb[4];
+  fetch_chunk(L, j0, kb, vb);
+  if (tid < ATT_D) ql[tid] = a.q[((size_t)s * ATT_HEADS + h) * ATT_D + tid] * a.scale;
+  stage_chunk(kl, vl, kb, vb);
+  __syncthreads();
+  const bool valid = j0 + j < L.n_keys;
+  float sc = chunk_score(kl, ql);
   if (!valid) sc = -__builtin_inff();
   const float wm = wave_max(sc);
   if (lane == 0) red[wv] = wm;
@@ -109,17 +203,10 @@ __global__ __launch_bounds__(256) void rswa_chunk_kernel(RswaArgs a) {
   const float p = valid ? expf(sc - m) : 0.f;
   if (qq == 0) pl[j] = p;
   const float ws = wave_sum(qq == 0 ? p : 0.f);
-  __syncthreads();
   if (lane == 0) red[4 + wv] = ws;
-  // p v: thread (dim d = tid % 128, key half = tid / 128)
-  const int d = tid & (ATT_D - 1), half = tid >> 7;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int jj = 0; jj < RSWA_CHUNK / 2; ++jj) {
-    const int k = half * (RSWA_CHUNK / 2) + jj;
-    acc = __fmaf_rn(pl[k], __uint_as_float((uint32_t)vl[k * ATT_D + d] << 16), acc);
-  }
-  if (half == 1) acc2[d] = acc;
+  __syncthreads();
+  const float acc = chunk_pv(vl, pl);
+  if (tid >= ATT_D) acc2[tid & (ATT_D - 1)] = acc;
   __syncthreads();
   if (tid < ATT_D) {
     part[2 + tid] = acc + acc2[tid];
@@ -150,9 +237,12 @@ __global__ __launch_bounds__(ATT_D) void rswa_merge_kernel(RswaArgs a) {
 int rswa_chunks(int n_ref) { return (n_ref + RSWA_W + RSWA_CHUNK - 1) / RSWA_CHUNK; }
 
 hipError_t launch_rswa(const RswaArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(rswa_ring_write_kernel, dim3(a.S), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(rswa_chunk_kernel, dim3(a.n_chunks, ATT_HEADS, a.S), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(rswa_merge_kernel, dim3(ATT_HEADS, a.S), dim3(ATT_D), 0, st, a);
+  if (a.S * ATT_HEADS >= RSWA_ROW_MIN_WG) {
+    hipLaunchKernelGGL(rswa_row_kernel, dim3(ATT_HEADS, a.S), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(rswa_chunk_kernel, dim3(a.n_chunks, ATT_HEADS, a.S), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(rswa_merge_kernel, dim3(ATT_HEADS, a.S), dim3(ATT_D), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -53,16 +53,19 @@ def check(d, streams=None):
     return worst
 
 
+@pytest.mark.parametrize("S", [4, 16])
 @pytest.mark.parametrize("n_ref", [0, 1, 63, 64, 65, 288, 1000])
-def test_rswa_reference_lengths(lib, n_ref):
-    d = make_rswa(4, n_ref, n_gen=[0, 5, 127, 300], seed=n_ref)
+def test_rswa_reference_lengths(lib, n_ref, S):
+    """4 streams take the split-KV path, 16 the one-workgroup-per-row path."""
+    d = make_rswa(S, n_ref, n_gen=[0, 5, 127, 300] * (S // 4), seed=n_ref)
     worst = check(d)
-    say(f"n_ref {n_ref}: err/rms {worst:.2e}")
+    say(f"{S} streams, n_ref {n_ref}: err/rms {worst:.2e}")
 
 
-def test_rswa_first_token_without_reference_is_its_value(lib):
+@pytest.mark.parametrize("S", [3, 16])
+def test_rswa_first_token_without_reference_is_its_value(lib, S):
     """n_ref = 0 and n_gen = 0: one key, so the output is the new value (as bf16)."""
-    d = make_rswa(3, 0, n_gen=[0, 0, 0], seed=5)
+    d = make_rswa(S, 0, n_gen=[0] * S, seed=5)
     out, _, _ = run(d)
     np.testing.assert_array_equal(out, bf16_bits_value(f32_to_bf16_bits(d["v_new"])).astype(np.float32))
 
