@@ -307,20 +307,28 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   GroupedArgs ga;
   ga.T = T; ga.tiles = ws.tiles; ga.ntiles = ws.ntiles; ga.offsets = ws.offsets; ga.perm = ws.perm;
   ga.ksplit = 1;
-  // routed gate/up: A rows are tokens gathered through the permutation
-  ga.af = xf; ga.ab = xb; ga.shared = 0; ga.a_by_token = 1; ga.a_rows = T; ga.w = rw; ga.out = ws.h_routed;
-  if (launch_grouped_gateup(ga, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
+  const int s_tiles = (T + mtl - 1) / mtl;
+  // routed gate/up: A rows are tokens gathered through the permutation;
   // shared gate/up over all tokens
-  ga.shared = 1; ga.w = sw; ga.out = ws.h_shared;
-  if (launch_grouped_gateup(ga, (T + mtl - 1) / mtl, small, s) != hipSuccess) return MOE_E_HIP;
-  // routed down: A rows are h in sorted order
-  ga.af = ws.h_routed; ga.ab = nullptr; ga.shared = 0; ga.a_by_token = 0; ga.a_rows = T * TOPK; ga.w = rw;
-  ga.out = ws.ysorted;
-  if (launch_grouped_down(ga, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
-  // with small tiles the shared down has few row tiles: two K halves double
-  // its workgroups
-  ga.af = ws.h_shared; ga.shared = 1; ga.a_rows = T; ga.w = sw; ga.out = ws.ys; ga.ksplit = small ? 2 : 1;
-  if (launch_grouped_down(ga, (T + mtl - 1) / mtl, small, s) != hipSuccess) return MOE_E_HIP;
+  GroupedArgs gr = ga, gs = ga;
+  gr.af = xf; gr.ab = xb; gr.shared = 0; gr.a_by_token = 1; gr.a_rows = T; gr.w = rw; gr.out = ws.h_routed;
+  gs.af = xf; gs.ab = xb; gs.shared = 1; gs.a_by_token = 1; gs.a_rows = T; gs.w = sw; gs.out = ws.h_shared;
+  // routed down: A rows are h in sorted order; with small tiles the shared
+  // down has few row tiles, so two K halves double its workgroups
+  GroupedArgs dr = ga, ds = ga;
+  dr.af = ws.h_routed; dr.ab = nullptr; dr.shared = 0; dr.a_by_token = 0; dr.a_rows = T * TOPK; dr.w = rw;
+  dr.out = ws.ysorted;
+  ds.af = ws.h_shared; ds.ab = nullptr; ds.shared = 1; ds.a_by_token = 0; ds.a_rows = T; ds.w = sw; ds.out = ws.ys;
+  ds.ksplit = small ? 2 : 1;
+  if (small && launch_small_pair(gr, max_tiles, gs, s_tiles, false, s)) {
+    if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
+    if (!launch_small_pair(dr, max_tiles, ds, s_tiles, true, s) || hipGetLastError() != hipSuccess) return MOE_E_HIP;
+  } else {
+    if (launch_grouped_gateup(gr, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
+    if (launch_grouped_gateup(gs, s_tiles, small, s) != hipSuccess) return MOE_E_HIP;
+    if (launch_grouped_down(dr, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
+    if (launch_grouped_down(ds, s_tiles, small, s) != hipSuccess) return MOE_E_HIP;
+  }
   CombineArgs ca;
   ca.ys = ws.ys; ca.ys2 = small ? ws.ys + (size_t)T * H : nullptr; ca.ysorted = ws.ysorted; ca.pos_of = ws.pos_of; ca.tw = topk_w;
   ca.y = y; ca.T = T; ca.accumulate = accumulate;

@@ -180,6 +180,10 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s);
 hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+// Routed and shared small-tile GEMMs in one launch (gate/up, or down with the
+// shared expert in two K halves); false if the format pair has no fused kernel.
+bool launch_small_pair(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down,
+                       hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps, hipStream_t s);
 
 }  // namespace moe

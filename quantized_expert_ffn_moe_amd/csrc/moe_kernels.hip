@@ -1808,7 +1808,7 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
 // ring, A two stages ahead into registers and one stage ahead into a double
 // buffer in LDS, so that the memory latency hides behind the MFMA work.
 template <int BITS, bool SPLIT, int G>
-__global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
+__device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid) {
   constexpr int MTL = MT_SMALL;
   constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MTL / 16;
   constexpr int CPG = G / 32, GPS = KS / G, NG = H / G;
@@ -1817,7 +1817,7 @@ __global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
   constexpr int APL = SPLIT ? 2 : 1;
   constexpr int NSEG = MTL * KS / 8 / 512;  // A segments per thread (1)
   const int inter = a.w.inter, ncb = inter / 128;
-  const int tile = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+  const int tile = bid / ncb, cb = bid % ncb;
   const TileInfo ti = tile_info(a, tile, MTL);
   if (!ti.valid) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
@@ -1967,7 +1967,7 @@ __global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
 // each taking half of its 16-row n-subtiles (the matching half of every
 // 16-byte lane word).  Same software pipeline as gate/up.
 template <int BITS, int G, int INTER, int KSPLIT = 1>
-__global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
+__device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
   constexpr int MTL = MT_SMALL;
   constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4, MS = MTL / 16;
   constexpr int NSW = NSUB / 2;             // n-subtiles per wave (half a row tile)
@@ -1975,7 +1975,7 @@ __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
   static_assert((INTER / KS) % KSPLIT == 0, "K halves of whole stages");
   constexpr int D = 4;
   const int inter = INTER;
-  const int kh = blockIdx.x % KSPLIT, tb = blockIdx.x / KSPLIT, s0 = kh * NSTAGE;   // K part kh
+  const int kh = bid % KSPLIT, tb = bid / KSPLIT, s0 = kh * NSTAGE;   // K part kh
   const int tile = tb / NCB, cb = tb % NCB;
   const TileInfo ti = tile_info(a, tile, MTL);
   if (!ti.valid) return;
@@ -2106,6 +2106,29 @@ __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
           a.out[(size_t)kh * a.T * H + orow * H + DR * rt + 16 * (NSW * hh + j) + r] = acc[j][ms][k];
       }
     }
+}
+
+template <int BITS, bool SPLIT, int G>
+__global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
+  gateup_small_body<BITS, SPLIT, G>(a, blockIdx.x);
+}
+template <int BITS, int G, int INTER, int KSPLIT = 1>
+__global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
+  down_small_body<BITS, G, INTER, KSPLIT>(a, blockIdx.x);
+}
+// The shared expert does not depend on routing: with small tiles its
+// workgroups run in the same launch as the routed experts' (shared tiles
+// first, so they start at once; routed tiles past the histogram's count exit
+// at once), which fills the compute units the few shared tiles would leave idle.
+template <int BR, int GR, int BS, int GS, bool SPLIT>
+__global__ __launch_bounds__(512) void gateup_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
+  if ((int)blockIdx.x < n_shared) gateup_small_body<BS, SPLIT, GS>(sh, blockIdx.x);
+  else gateup_small_body<BR, SPLIT, GR>(r, blockIdx.x - n_shared);
+}
+template <int BR, int GR, int BS, int GS>
+__global__ __launch_bounds__(512) void down_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
+  if ((int)blockIdx.x < n_shared) down_small_body<BS, GS, IS, 2>(sh, blockIdx.x);
+  else down_small_body<BR, GR, I, 1>(r, blockIdx.x - n_shared);
 }
 
 // y[t] (+)= ys[t] (+ ys2[t]) + sum_j w[t,j] * ysorted[pos_of[t*6+j]], picks added in order.
@@ -2275,6 +2298,41 @@ hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, bool small, 
     default: down_dispatch<8, 128>(a, max_tiles, small, s); break;
   }
   return hipGetLastError();
+}
+
+template <int BR, int GR, int BS, int GS>
+static void pair_dispatch(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down,
+                          hipStream_t s) {
+  if (!down) {
+    const int ns = s_tiles * (IS / 128), nr = r_tiles * (I / 128);
+    if (r.af) hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, true>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
+    else hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, false>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
+  } else {
+    const int ns = 2 * s_tiles * (H / (4 * down_rows(BS))), nr = r_tiles * (H / (4 * down_rows(BR)));
+    hipLaunchKernelGGL((down_small_pair_kernel<BR, GR, BS, GS>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
+  }
+}
+
+bool launch_small_pair(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down,
+                       hipStream_t s) {
+  const int rb = r.w.bits, rg = r.w.group, sb = sh.w.bits, sg = sh.w.group;
+  if (rb == sb && rg == sg) {
+    const int key = (rb == 8) * 3 + (rg == 64) + 2 * (rg == 128);
+    switch (key) {
+      case 0: pair_dispatch<4, 32, 4, 32>(r, r_tiles, sh, s_tiles, down, s); break;
+      case 1: pair_dispatch<4, 64, 4, 64>(r, r_tiles, sh, s_tiles, down, s); break;
+      case 2: pair_dispatch<4, 128, 4, 128>(r, r_tiles, sh, s_tiles, down, s); break;
+      case 3: pair_dispatch<8, 32, 8, 32>(r, r_tiles, sh, s_tiles, down, s); break;
+      case 4: pair_dispatch<8, 64, 8, 64>(r, r_tiles, sh, s_tiles, down, s); break;
+      default: pair_dispatch<8, 128, 8, 128>(r, r_tiles, sh, s_tiles, down, s); break;
+    }
+    return true;
+  }
+  if (rb == 4 && rg == 64 && sb == 8 && sg == 128) {
+    pair_dispatch<4, 64, 8, 128>(r, r_tiles, sh, s_tiles, down, s);
+    return true;
+  }
+  return false;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
