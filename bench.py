@@ -90,7 +90,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--path", choices=["chain", "layers"], default="chain")
-    ap.add_argument("--workload", choices=["decode", "prefill273", "multipage2184", "batch128", "batch256",
+    ap.add_argument("--workload", choices=["decode", "batched32", "prefill273", "multipage2184", "batch128", "batch256",
                                            "lmhead_bf16", "lmhead_int8", "dense0", "rswa128"],
                     default="decode",
                     help="decode = the headline 11-layer decode step; the prefill workloads report MFMA "
@@ -248,7 +248,7 @@ def bench_prefill(args):
     from quantized_expert_ffn_moe_amd import binding as B
     from synth import WORKLOADS, make_layer, make_tokens
 
-    wl = WORKLOADS[{"prefill273": 3, "multipage2184": 4, "batch128": 5, "batch256": 6}[args.workload]]
+    wl = WORKLOADS[{"batched32": 2, "prefill273": 3, "multipage2184": 4, "batch128": 5, "batch256": 6}[args.workload]]
     L = wl.n_layers
     layers = [make_layer(wl, li) for li in range(L)]
     packed = [B.pack_layer(layer) for layer in layers]
@@ -266,21 +266,25 @@ def bench_prefill(args):
     if wl.chained:
         flags = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE | (B.MOE_NORM_BF16 if wl.norm_bf16 else 0)
 
-        def step():
+        def step(i):
             h.copy_(xt.float())
             for li in range(L):
                 B.moe_layer_forward(h, packed[li], h, ids[li], w[li], ws, flags, stream=stream)
     else:
-        def step():
-            B.moe_layer_forward(xt, packed[0], h, ids[0], w[0], ws, 0, stream=stream)
+        # one layer fits the 256 MiB last-level cache: rotate weight replicas
+        # so that no step finds its weights there
+        packed += [B.pack_layer(layers[0]) for _ in range(3)]
+
+        def step(i):
+            B.moe_layer_forward(xt, packed[i % 4], h, ids[0], w[0], ws, 0, stream=stream)
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
+        for i in range(args.warmup):
+            step(i)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(args.steps):
-            step()
+        for i in range(args.steps):
+            step(i)
         e1.record(stream)
         torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -290,9 +294,10 @@ def bench_prefill(args):
            "ms_per_step": ms, "steps": args.steps, "warmup": args.warmup, "dtype": "f16 MFMA, fp32 acc",
            "config": {"workload": wl.name, "tokens": T, "layers": L},
            "achieved_tflops": tflops, "bf16_peak_tflops": 2500.0, "mfma_frac": tflops / 2500.0}
-    if args.workload.startswith("batch"):
-        # a decode step of many streams reads (nearly) every expert once per
-        # layer: the HBM roofline bounds it
+    if args.workload.startswith("batch") or args.workload == "prefill273":
+        # a decode step of many streams, 32 concurrent pages or the visual
+        # prefill read the experts their tokens touch once per layer: the HBM
+        # roofline bounds them
         nbytes = grouped_step_bytes(wl, list(ids[:L].cpu().numpy()))
         gbs = nbytes / (ms * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

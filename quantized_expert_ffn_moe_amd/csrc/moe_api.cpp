@@ -58,7 +58,7 @@ Workspace carve(void* base, int T) {
   Workspace w;
   Carver c{(char*)base, 0};
   const size_t slots = (size_t)T * TOPK;
-  w.max_tiles = (int)(slots / MT_SMALL) + E + 1;   // enough for either tile height
+  w.max_tiles = (int)(slots / MT_TINY) + E + 1;    // enough for every tile height
   w.z = (float*)c.take((size_t)T * H * 4);
   w.logits = (float*)c.take((size_t)T * E * 4);
   const size_t union_start = c.off;
@@ -297,7 +297,8 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   // tile shape: 32-row tiles while the experts see few rows each (about 64 or
   // fewer on average), 64-row tiles beyond
   const bool small = (size_t)T * TOPK <= (size_t)SMALL_TILE_MAX_SLOTS;
-  const int mtl = small ? MT_SMALL : MT;
+  const bool pair = small && small_pair_available(rw.bits, rw.group, sw.bits, sw.group);
+  const int mtl = !small ? MT : (pair && (size_t)T * TOPK <= TINY_TILE_MAX_SLOTS) ? MT_TINY : MT_SMALL;
   const int max_tiles = (int)((size_t)T * TOPK / mtl) + E + 1;
   HistArgs ha;
   ha.ids = topk_ids; ha.T = T; ha.counts = ws.counts; ha.offsets = ws.offsets;
@@ -320,9 +321,9 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   dr.out = ws.ysorted;
   ds.af = ws.h_shared; ds.ab = nullptr; ds.shared = 1; ds.a_by_token = 0; ds.a_rows = T; ds.w = sw; ds.out = ws.ys;
   ds.ksplit = small ? 2 : 1;
-  if (small && launch_small_pair(gr, max_tiles, gs, s_tiles, false, s)) {
+  if (pair && launch_small_pair(gr, max_tiles, gs, s_tiles, false, mtl, s)) {
     if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
-    if (!launch_small_pair(dr, max_tiles, ds, s_tiles, true, s) || hipGetLastError() != hipSuccess) return MOE_E_HIP;
+    if (!launch_small_pair(dr, max_tiles, ds, s_tiles, true, mtl, s) || hipGetLastError() != hipSuccess) return MOE_E_HIP;
   } else {
     if (launch_grouped_gateup(gr, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
     if (launch_grouped_gateup(gs, s_tiles, small, s) != hipSuccess) return MOE_E_HIP;

@@ -14,7 +14,9 @@ constexpr int IS = 1792;     // fused shared expert intermediate
 constexpr int TILE = 1024;   // bytes of one packed 16-row tile
 constexpr int MT = 64;       // token rows per tile of the grouped GEMMs (large tiles)
 constexpr int MT_SMALL = 32; // rows per tile when experts see few rows each
+constexpr int MT_TINY = 16;  // rows per tile when experts see very few rows each (fused shared/routed launches)
 constexpr int SMALL_TILE_MAX_SLOTS = 64 * 64;   // (token, pick) slots up to which the small tiles run
+constexpr int TINY_TILE_MAX_SLOTS = 64 * 8;     // ... and the 16-row tiles (about 8 rows per expert or fewer)
 constexpr int DECODE_MAX_T = 4;  // largest token count routed to the GEMV path by default
 constexpr int MAX_T = 8192;      // largest token count of one call
 constexpr int MOE_MAX_SLOTS = MAX_T * TOPK;
@@ -182,7 +184,8 @@ hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, bool small, 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 // Routed and shared small-tile GEMMs in one launch (gate/up, or down with the
 // shared expert in two K halves); false if the format pair has no fused kernel.
-bool launch_small_pair(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down,
+bool small_pair_available(int rbits, int rgroup, int sbits, int sgroup);
+bool launch_small_pair(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down, int mtl,
                        hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps, hipStream_t s);
 

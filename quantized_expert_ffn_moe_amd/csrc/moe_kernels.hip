@@ -1807,15 +1807,14 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
 // tiles and their group scales are fetched D stages ahead into a register
 // ring, A two stages ahead into registers and one stage ahead into a double
 // buffer in LDS, so that the memory latency hides behind the MFMA work.
-template <int BITS, bool SPLIT, int G>
+template <int BITS, bool SPLIT, int G, int MTL>
 __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid) {
-  constexpr int MTL = MT_SMALL;
   constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MTL / 16;
   constexpr int CPG = G / 32, GPS = KS / G, NG = H / G;
   constexpr int D = BITS == 4 ? 4 : 3;      // B stages in flight
   constexpr bool F32 = SPLIT;
   constexpr int APL = SPLIT ? 2 : 1;
-  constexpr int NSEG = MTL * KS / 8 / 512;  // A segments per thread (1)
+  constexpr int NSEG = MTL * KS / 8;        // A segments (8 elements) per stage: one per thread up to 512
   const int inter = a.w.inter, ncb = inter / 128;
   const int tile = bid / ncb, cb = bid % ncb;
   const TileInfo ti = tile_info(a, tile, MTL);
@@ -1856,10 +1855,12 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
       for (int h = 0; h < NB; ++h) bd[i][h] = wload16(rb[i], (uint32_t)(st * NB + h) * TILE + lane * 16);
     }
   };
-  // A: one 8-element segment per thread per stage (row tid / 16, columns 8 (tid % 16))
+  // A: one 8-element segment per thread per stage (row tid / 16, columns 8 (tid % 16));
+  // with 16-row tiles only the first 256 threads hold one
+  const bool a_act = NSEG >= 512 || tid < NSEG;
   auto fetch_a1 = [&](uint4 (&ar)[APL], int k0, bool live) {
-    const int row = tid >> 4, kk = 8 * (tid & 15);
-    const int src = arow[row];
+    const int row = a_act ? tid >> 4 : 0, kk = 8 * (tid & 15);
+    const int src = a_act ? arow[row] : -1;
     constexpr uint32_t ELT = F32 ? 4 : 2;
     const uint32_t off = (live && src >= 0) ? ((uint32_t)src * H + k0 + kk) * ELT : 0x80000000u;
     ar[0] = wload16(ra, off);
@@ -1888,10 +1889,11 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
       hi[p] = xh;
       lo[p] = (_Float16)(x - (float)xh);
     }
+    if (!a_act) return;
     *(half8*)(l + row * LDS_ROW + kk) = hi;
     if (SPLIT) *(half8*)(l + MTL * LDS_ROW + row * LDS_ROW + kk) = lo;
   };
-  static_assert(NSEG == 1, "one A segment per thread");
+  static_assert(NSEG <= 512, "at most one A segment per thread");
   float4v acc[2][MS], ctmp[2][MS];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -1966,9 +1968,8 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
 // 2i and 2i + 1 share row tile 4cb + i (64 int4 or 32 int8 output columns),
 // each taking half of its 16-row n-subtiles (the matching half of every
 // 16-byte lane word).  Same software pipeline as gate/up.
-template <int BITS, int G, int INTER, int KSPLIT = 1>
+template <int BITS, int G, int INTER, int KSPLIT, int MTL>
 __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
-  constexpr int MTL = MT_SMALL;
   constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4, MS = MTL / 16;
   constexpr int NSW = NSUB / 2;             // n-subtiles per wave (half a row tile)
   constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS / KSPLIT;
@@ -2015,10 +2016,12 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
       bd[c] = make_uint2(v[0], v[1]);
     }
   };
-  // A (h, f32 as hi/lo f16 planes): one 8-element segment per thread per stage
+  // A (h, f32 as hi/lo f16 planes): one 8-element segment per thread per
+  // stage; with 16-row tiles only the first 256 threads hold one
+  const bool a_act = MTL * KS / 8 >= 512 || tid < MTL * KS / 8;
   auto fetch_a1 = [&](uint4 (&ar)[2], int k0, bool live) {
-    const int row = tid >> 4, kk = 8 * (tid & 15);
-    const int src = arow[row];
+    const int row = a_act ? tid >> 4 : 0, kk = 8 * (tid & 15);
+    const int src = a_act ? arow[row] : -1;
     const uint32_t off = (live && src >= 0) ? ((uint32_t)src * INTER + k0 + kk) * 4 : 0x80000000u;
     ar[0] = wload16(ra, off);
     ar[1] = wload16(ra, off + 16);
@@ -2036,10 +2039,11 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
       hi[p] = xh;
       lo[p] = (_Float16)(x - (float)xh);
     }
+    if (!a_act) return;
     *(half8*)(l + row * LDS_ROW + kk) = hi;
     *(half8*)(l + MTL * LDS_ROW + row * LDS_ROW + kk) = lo;
   };
-  static_assert(MTL * KS / 8 == 512, "one A segment per thread");
+  static_assert(MTL * KS / 8 <= 512, "at most one A segment per thread");
   float4v acc[NSW][MS], ctmp[NSW][MS];
 #pragma unroll
   for (int j = 0; j < NSW; ++j)
@@ -2108,27 +2112,27 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
     }
 }
 
-template <int BITS, bool SPLIT, int G>
+template <int BITS, bool SPLIT, int G, int MTL>
 __global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
-  gateup_small_body<BITS, SPLIT, G>(a, blockIdx.x);
+  gateup_small_body<BITS, SPLIT, G, MTL>(a, blockIdx.x);
 }
-template <int BITS, int G, int INTER, int KSPLIT = 1>
+template <int BITS, int G, int INTER, int KSPLIT, int MTL>
 __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
-  down_small_body<BITS, G, INTER, KSPLIT>(a, blockIdx.x);
+  down_small_body<BITS, G, INTER, KSPLIT, MTL>(a, blockIdx.x);
 }
 // The shared expert does not depend on routing: with small tiles its
 // workgroups run in the same launch as the routed experts' (shared tiles
 // first, so they start at once; routed tiles past the histogram's count exit
 // at once), which fills the compute units the few shared tiles would leave idle.
-template <int BR, int GR, int BS, int GS, bool SPLIT>
+template <int BR, int GR, int BS, int GS, bool SPLIT, int MTL>
 __global__ __launch_bounds__(512) void gateup_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
-  if ((int)blockIdx.x < n_shared) gateup_small_body<BS, SPLIT, GS>(sh, blockIdx.x);
-  else gateup_small_body<BR, SPLIT, GR>(r, blockIdx.x - n_shared);
+  if ((int)blockIdx.x < n_shared) gateup_small_body<BS, SPLIT, GS, MTL>(sh, blockIdx.x);
+  else gateup_small_body<BR, SPLIT, GR, MTL>(r, blockIdx.x - n_shared);
 }
-template <int BR, int GR, int BS, int GS>
+template <int BR, int GR, int BS, int GS, int MTL>
 __global__ __launch_bounds__(512) void down_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
-  if ((int)blockIdx.x < n_shared) down_small_body<BS, GS, IS, 2>(sh, blockIdx.x);
-  else down_small_body<BR, GR, I, 1>(r, blockIdx.x - n_shared);
+  if ((int)blockIdx.x < n_shared) down_small_body<BS, GS, IS, 2, MTL>(sh, blockIdx.x);
+  else down_small_body<BR, GR, I, 1, MTL>(r, blockIdx.x - n_shared);
 }
 
 // y[t] (+)= ys[t] (+ ys2[t]) + sum_j w[t,j] * ysorted[pos_of[t*6+j]], picks added in order.
@@ -2248,8 +2252,8 @@ template <int BITS, int G>
 static void gateup_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
   if (small) {
     const dim3 grid(max_tiles * (a.w.inter / 128));
-    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<BITS, true, G>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gateup_small_kernel<BITS, false, G>), grid, dim3(512), 0, s, a);
+    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<BITS, true, G, MT_SMALL>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gateup_small_kernel<BITS, false, G, MT_SMALL>), grid, dim3(512), 0, s, a);
   } else {
     const dim3 grid(max_tiles * (a.w.inter / 128));   // 128 gate + 128 up columns per workgroup
     if (a.af) hipLaunchKernelGGL((grouped_gateup_kernel<BITS, true, G>), grid, dim3(GT), 0, s, a);
@@ -2275,9 +2279,9 @@ static void down_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipSt
   if (small) {
     const dim3 grid(max_tiles * (H / (4 * down_rows(BITS))));
     if (a.w.inter == IS && a.ksplit == 2)
-      hipLaunchKernelGGL((down_small_kernel<BITS, G, IS, 2>), dim3(2 * grid.x), dim3(512), 0, s, a);
-    else if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<BITS, G, IS>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((down_small_kernel<BITS, G, I>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((down_small_kernel<BITS, G, IS, 2, MT_SMALL>), dim3(2 * grid.x), dim3(512), 0, s, a);
+    else if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<BITS, G, IS, 1, MT_SMALL>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((down_small_kernel<BITS, G, I, 1, MT_SMALL>), grid, dim3(512), 0, s, a);
   } else {
     const dim3 grid(max_tiles * (H / 256));             // 256 output columns per workgroup
     if (a.w.inter == IS && a.ksplit == 2)
@@ -2300,39 +2304,49 @@ hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, bool small, 
   return hipGetLastError();
 }
 
-template <int BR, int GR, int BS, int GS>
+template <int BR, int GR, int BS, int GS, int MTL>
 static void pair_dispatch(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down,
                           hipStream_t s) {
   if (!down) {
     const int ns = s_tiles * (IS / 128), nr = r_tiles * (I / 128);
-    if (r.af) hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, true>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
-    else hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, false>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
+    if (r.af)
+      hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, true, MTL>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
+    else
+      hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, false, MTL>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
   } else {
     const int ns = 2 * s_tiles * (H / (4 * down_rows(BS))), nr = r_tiles * (H / (4 * down_rows(BR)));
-    hipLaunchKernelGGL((down_small_pair_kernel<BR, GR, BS, GS>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
+    hipLaunchKernelGGL((down_small_pair_kernel<BR, GR, BS, GS, MTL>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
   }
 }
+template <int BR, int GR, int BS, int GS>
+static void pair_dispatch_h(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down, int mtl,
+                            hipStream_t s) {
+  if (mtl == MT_TINY) pair_dispatch<BR, GR, BS, GS, MT_TINY>(r, r_tiles, sh, s_tiles, down, s);
+  else pair_dispatch<BR, GR, BS, GS, MT_SMALL>(r, r_tiles, sh, s_tiles, down, s);
+}
 
-bool launch_small_pair(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down,
+bool small_pair_available(int rbits, int rgroup, int sbits, int sgroup) {
+  return (rbits == sbits && rgroup == sgroup) || (rbits == 4 && rgroup == 64 && sbits == 8 && sgroup == 128);
+}
+
+bool launch_small_pair(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down, int mtl,
                        hipStream_t s) {
   const int rb = r.w.bits, rg = r.w.group, sb = sh.w.bits, sg = sh.w.group;
+  if (!small_pair_available(rb, rg, sb, sg)) return false;
   if (rb == sb && rg == sg) {
     const int key = (rb == 8) * 3 + (rg == 64) + 2 * (rg == 128);
     switch (key) {
-      case 0: pair_dispatch<4, 32, 4, 32>(r, r_tiles, sh, s_tiles, down, s); break;
-      case 1: pair_dispatch<4, 64, 4, 64>(r, r_tiles, sh, s_tiles, down, s); break;
-      case 2: pair_dispatch<4, 128, 4, 128>(r, r_tiles, sh, s_tiles, down, s); break;
-      case 3: pair_dispatch<8, 32, 8, 32>(r, r_tiles, sh, s_tiles, down, s); break;
-      case 4: pair_dispatch<8, 64, 8, 64>(r, r_tiles, sh, s_tiles, down, s); break;
-      default: pair_dispatch<8, 128, 8, 128>(r, r_tiles, sh, s_tiles, down, s); break;
+      case 0: pair_dispatch_h<4, 32, 4, 32>(r, r_tiles, sh, s_tiles, down, mtl, s); break;
+      case 1: pair_dispatch_h<4, 64, 4, 64>(r, r_tiles, sh, s_tiles, down, mtl, s); break;
+      case 2: pair_dispatch_h<4, 128, 4, 128>(r, r_tiles, sh, s_tiles, down, mtl, s); break;
+      case 3: pair_dispatch_h<8, 32, 8, 32>(r, r_tiles, sh, s_tiles, down, mtl, s); break;
+      case 4: pair_dispatch_h<8, 64, 8, 64>(r, r_tiles, sh, s_tiles, down, mtl, s); break;
+      default: pair_dispatch_h<8, 128, 8, 128>(r, r_tiles, sh, s_tiles, down, mtl, s); break;
     }
-    return true;
+  } else {
+    pair_dispatch_h<4, 64, 8, 128>(r, r_tiles, sh, s_tiles, down, mtl, s);
   }
-  if (rb == 4 && rg == 64 && sb == 8 && sg == 128) {
-    pair_dispatch<4, 64, 8, 128>(r, r_tiles, sh, s_tiles, down, s);
-    return true;
-  }
-  return false;
+  return true;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
