@@ -7,18 +7,20 @@
 // ("Four bits, one shared scale"), two fused shared experts, weighted combine.
 //
 // Two expert paths:
-//  * GEMV path (few tokens): every (token, pick) streams its expert's packed
-//    1 KiB tiles with 16-byte loads per lane and multiplies the codes as they
-//    are (two's complement) with integer dot-product instructions against a
-//    block-floating-point digit expansion of the input; the group scale
-//    multiplies the exact integer partial sum of its group.
+//  * GEMV path (few tokens; the persistent decode step and the per-token
+//    layer path): every (token, pick) streams its expert's packed 1 KiB tiles
+//    with 16-byte loads per lane.  The input is written in block floating
+//    point as three int8 digit planes, and the int8 matrix cores
+//    (v_mfma_i32_16x16x64_i8) multiply them with the codes exactly; the group
+//    scale multiplies the exact integer partial sum of its group.
 //  * Grouped path (many tokens): tokens are bucketed per expert (histogram +
 //    stable permutation) and each expert's bucket runs as a dense GEMM on the
 //    MFMA units (v_mfma_f32_16x16x32_f16).  The codes become exact f16 integers
-//    in registers (magic-exponent trick); activations are staged in LDS as f16,
-//    split into hi + lo halves when they are f32, so the products are exact and
-//    only the fp32 accumulation rounds.  Group scales are applied to the fp32
-//    partial sums of each group.
+//    in registers (one AND and one XOR per pair of codes, then one packed f16
+//    add); activations are staged in LDS as f16, split into hi + lo halves
+//    when they are f32, so the products are exact and only the fp32
+//    accumulation rounds.  Group scales are applied to the fp32 partial sums
+//    of each group.
 #include "moe_internal.h"
 #include "moe_wave.h"
 
