@@ -67,11 +67,14 @@ __device__ __forceinline__ uint4 pack8(const float* p) {
                     (uint32_t)to_bf16(b.x) | ((uint32_t)to_bf16(b.y) << 16),
                     (uint32_t)to_bf16(b.z) | ((uint32_t)to_bf16(b.w) << 16));
 }
+// (A workgroup of NT threads takes chunks of NT / 4 keys: 4 NT pieces of each
+// matrix, 4 per thread.)
+template <int NT>
 __device__ __forceinline__ void fetch_chunk(const KeyList& L, int j0, uint4 (&kb)[4], uint4 (&vb)[4]) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int f = tid + 256 * i, j = j0 + f / 16, u = f % 16;
+    const int f = tid + NT * i, j = j0 + f / 16, u = f % 16;
     kb[i] = make_uint4(0, 0, 0, 0);
     vb[i] = make_uint4(0, 0, 0, 0);
     if (j < L.n_ref) {
@@ -91,10 +94,11 @@ __device__ __forceinline__ void fetch_chunk(const KeyList& L, int j0, uint4 (&kb
     }
   }
 }
+template <int NT>
 __device__ __forceinline__ void stage_chunk(uint16_t* kl, uint16_t* vl, const uint4 (&kb)[4], const uint4 (&vb)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int f = threadIdx.x + 256 * i;
+    const int f = threadIdx.x + NT * i;
     *((uint4*)kl + f) = kb[i];
     *((uint4*)vl + f) = vb[i];
   }
@@ -116,59 +120,72 @@ __device__ __forceinline__ float chunk_score(const uint16_t* kl, const float* ql
   }
   return group_sum<4>(sc);
 }
-// sum over the keys of this thread's half (tid / 128) of p_j v_j[d], d = tid % 128
+// sum over the 32 keys of this thread's part (tid / 128) of the chunk of
+// p_j v_j[d], d = tid % 128
 __device__ __forceinline__ float chunk_pv(const uint16_t* vl, const float* pl) {
-  const int d = threadIdx.x & (ATT_D - 1), half = threadIdx.x >> 7;
+  const int d = threadIdx.x & (ATT_D - 1), part = threadIdx.x >> 7;
   float acc = 0.f;
 #pragma unroll 8
-  for (int jj = 0; jj < RSWA_CHUNK / 2; ++jj) {
-    const int k = half * (RSWA_CHUNK / 2) + jj;
+  for (int jj = 0; jj < 32; ++jj) {
+    const int k = part * 32 + jj;
     acc = __fmaf_rn(pl[k], __uint_as_float((uint32_t)vl[k * ATT_D + d] << 16), acc);
   }
   return acc;
 }
 
-// Many streams: one workgroup per (head, stream) = blockIdx (x, y).
-__global__ __launch_bounds__(256) void rswa_row_kernel(RswaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t kl[RSWA_CHUNK * ATT_D];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[RSWA_CHUNK * ATT_D];
+// Many streams: one workgroup of NT threads per (head, stream) = blockIdx
+// (x, y), chunks of NT / 4 keys.
+template <int NT>
+__global__ __launch_bounds__(NT) void rswa_row_kernel(RswaArgs a) {
+  constexpr int CH = NT / 4, NW = NT / 64;
+  __shared__ __attribute__((aligned(16))) uint16_t kl[CH * ATT_D];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[CH * ATT_D];
   __shared__ __attribute__((aligned(16))) float ql[ATT_D];
-  __shared__ float pl[RSWA_CHUNK];
-  __shared__ float red[8];
+  __shared__ float pl[CH];
+  __shared__ float red[2 * NW];
   __shared__ float acc2[ATT_D];
   const int h = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid >> 2, qq = tid & 3;
   const KeyList L = key_list(a, s, h);
-  const int nch = (L.n_keys + RSWA_CHUNK - 1) / RSWA_CHUNK;
+  const int nch = (L.n_keys + CH - 1) / CH;
   uint4 kb[4], vb[4];
-  fetch_chunk(L, 0, kb, vb);
+  fetch_chunk<NT>(L, 0, kb, vb);
   if (tid < ATT_D) ql[tid] = a.q[((size_t)s * ATT_HEADS + h) * ATT_D + tid] * a.scale;
   float m_run = -__builtin_inff(), l_run = 0.f, acc = 0.f;
   for (int c = 0; c < nch; ++c) {
     __syncthreads();                              // previous chunk's LDS reads are done
-    stage_chunk(kl, vl, kb, vb);
-    if (c + 1 < nch) fetch_chunk(L, (c + 1) * RSWA_CHUNK, kb, vb);
+    stage_chunk<NT>(kl, vl, kb, vb);
+    if (c + 1 < nch) fetch_chunk<NT>(L, (c + 1) * CH, kb, vb);
     __syncthreads();
-    const bool valid = c * RSWA_CHUNK + j < L.n_keys;
+    const bool valid = c * CH + j < L.n_keys;
     float sc = chunk_score(kl, ql);
     if (!valid) sc = -__builtin_inff();
     const float wm = wave_max(sc);
     if (lane == 0) red[wv] = wm;
     __syncthreads();
-    const float m_new = fmaxf(m_run, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    float cm = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) cm = fmaxf(cm, red[w]);
+    const float m_new = fmaxf(m_run, cm);
     const float p = valid ? expf(sc - m_new) : 0.f;
     if (qq == 0) pl[j] = p;
     const float ws = wave_sum(qq == 0 ? p : 0.f);
-    if (lane == 0) red[4 + wv] = ws;
+    if (lane == 0) red[NW + wv] = ws;
     __syncthreads();
+    float cs = red[NW];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) cs += red[NW + w];
     const float resc = expf(m_run - m_new);       // 0 on the first chunk
-    l_run = __fmaf_rn(l_run, resc, (red[4] + red[5]) + (red[6] + red[7]));
+    l_run = __fmaf_rn(l_run, resc, cs);
     acc = __fmaf_rn(acc, resc, chunk_pv(vl, pl));
     m_run = m_new;
   }
-  if (tid >= ATT_D) acc2[tid & (ATT_D - 1)] = acc;
-  __syncthreads();
-  if (tid < ATT_D) a.out[((size_t)s * ATT_HEADS + h) * ATT_D + tid] = (acc + acc2[tid]) / l_run;
+  if (NT > ATT_D) {
+    if (tid >= ATT_D) acc2[tid & (ATT_D - 1)] = acc;
+    __syncthreads();
+    if (tid < ATT_D) acc += acc2[tid];
+  }
+  if (tid < ATT_D) a.out[((size_t)s * ATT_HEADS + h) * ATT_D + tid] = acc / l_run;
 }
 
 // 2. partials of one chunk: blockIdx = (chunk, head, stream)
@@ -188,10 +205,11 @@ __global__ __launch_bounds__(256) void rswa_chunk_kernel(RswaArgs a) {
     if (tid < RSWA_PART) part[tid] = tid == 0 ? -__builtin_inff() : 0.f;
     return;
   }
+  static_assert(RSWA_CHUNK == 256 / 4, "split-KV chunks of a 256-thread workgroup");
   uint4 kb[4], vb[4];
-  fetch_chunk(L, j0, kb, vb);
+  fetch_chunk<256>(L, j0, kb, vb);
   if (tid < ATT_D) ql[tid] = a.q[((size_t)s * ATT_HEADS + h) * ATT_D + tid] * a.scale;
-  stage_chunk(kl, vl, kb, vb);
+  stage_chunk<256>(kl, vl, kb, vb);
   __syncthreads();
   const bool valid = j0 + j < L.n_keys;
   float sc = chunk_score(kl, ql);
@@ -238,7 +256,7 @@ int rswa_chunks(int n_ref) { return (n_ref + RSWA_W + RSWA_CHUNK - 1) / RSWA_CHU
 
 hipError_t launch_rswa(const RswaArgs& a, hipStream_t st) {
   if (a.S * ATT_HEADS >= RSWA_ROW_MIN_WG) {
-    hipLaunchKernelGGL(rswa_row_kernel, dim3(ATT_HEADS, a.S), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(rswa_row_kernel<RSWA_ROW_THREADS>, dim3(ATT_HEADS, a.S), dim3(RSWA_ROW_THREADS), 0, st, a);
   } else {
     hipLaunchKernelGGL(rswa_chunk_kernel, dim3(a.n_chunks, ATT_HEADS, a.S), dim3(256), 0, st, a);
     hipLaunchKernelGGL(rswa_merge_kernel, dim3(ATT_HEADS, a.S), dim3(ATT_D), 0, st, a);

@@ -161,6 +161,7 @@ constexpr int RSWA_W = 128;                   // ring slots of generated tokens
 constexpr int RSWA_CHUNK = 64;                // keys per split-KV workgroup
 constexpr int RSWA_PART = 132;                // floats per partial: m, l, 128 outputs, pad
 constexpr int RSWA_ROW_MIN_WG = 160;          // (stream, head) pairs from which one workgroup takes a whole row
+constexpr int RSWA_ROW_THREADS = 128;         // ... of this many threads (chunks of a quarter as many keys)
 struct RswaArgs {
   int S, n_ref, n_chunks; float scale;
   const float* q; const float* k_new; const float* v_new;   // [S][10][128]
