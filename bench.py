@@ -95,6 +95,9 @@ def main():
                     default="decode",
                     help="decode = the headline 11-layer decode step; the prefill workloads report MFMA "
                          "figures; batchN = one continuous-batch decode step of N streams (HBM figures)")
+    ap.add_argument("--group", type=int, default=64, choices=[32, 64, 128],
+                    help="decode: group size of the routed int4 experts (64 is the headline; 32 and 128 sweep "
+                         "the group-size trade of metadata bytes against time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
@@ -130,6 +133,10 @@ def main():
         return bench_prefill(args)
 
     wl = WORKLOADS[1]
+    if args.group != wl.routed.group:
+        from dataclasses import replace
+        from synth import QFmt
+        wl = replace(wl, routed=QFmt(4, args.group), name=f"decode_1tok_11layers_int4g{args.group}_shared_int8g128")
     L = wl.n_layers
     layers = [make_layer(wl, li) for li in range(L)]
     base = [B.pack_layer(layer) for layer in layers]
@@ -191,7 +198,7 @@ def main():
     achieved = step_bytes / (ms_kernel * 1e-3) / 1e9
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.group == 64 else METRIC.replace("G=64", f"G={args.group}"),
         "value": 1000.0 / ms_step,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -209,7 +216,8 @@ def main():
                    "weight_replicas": args.replicas, "path": args.path},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counted_traffic(), "bytes_per_launch": step_bytes, "ms_per_launch": ms_kernel},
+                     "traffic": counted_traffic() if args.group == 64 else None,
+                     "bytes_per_launch": step_bytes, "ms_per_launch": ms_kernel},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, xs[: args.warmup + args.steps])
