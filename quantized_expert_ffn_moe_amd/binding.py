@@ -1,4 +1,5 @@
-"""Thin ctypes binding of libmoe.so (the C ABI in include/moe.h).
+"""Thin ctypes binding of libmoe.so (the C ABI in include/moe.h,
+include/moe_dense.h and include/moe_attn.h).
 
 Argument marshalling only: torch tensors become device addresses and the
 current HIP stream, numpy arrays become host addresses.  Every step of the
@@ -227,6 +228,15 @@ def moe_decode_forward(x, y, packed_layers, topk_ids, topk_w, ws, flags=0, weigh
                                     _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), flags, _stream(stream)))
 
 
+def _want(t, dtype, shape, name):
+    """The C ABI cannot see dtypes or strides: check them here."""
+    if t is None:
+        raise MoeError(f"{name} is required")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise MoeError(f"{name}: expected a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                       f"got {t.dtype} {tuple(t.shape)}")
+
+
 # ----------------------------------------------------------------- dense ends (include/moe_dense.h)
 def _nibbles(codes):
     """int4 codes [rows][K] (one per int8) -> [rows][K/2] bytes, element 2j in the low nibble."""
@@ -267,6 +277,13 @@ def moe_lm_head_workspace_bytes(n_tokens: int, vocab: int) -> int:
 
 def moe_lm_head_argmax(h, head: dict, token, token_logit, ws, flags: int = 0, logits=None, stream=None):
     """Enqueue lm_head + greedy token for h [T,1280] f32."""
+    import torch
+    T = h.shape[0]
+    _want(h, torch.float32, (T, HIDDEN), "h")
+    _want(token, torch.int32, (T,), "token")
+    _want(token_logit, torch.float32, (T,), "token_logit")
+    if logits is not None:
+        _want(logits, torch.float32, (T, head["vocab"]), "logits")
     check(load().moe_lm_head_argmax(_ptr(h), h.shape[0], flags, _ptr(head["w"]), head["bits"], _ptr(head["s"]),
                                     head["group"], head["vocab"], _ptr(logits), _ptr(token), _ptr(token_logit),
                                     _ptr(ws), ws.numel(), _stream(stream)))
@@ -278,6 +295,9 @@ def moe_dense_ffn_workspace_bytes(n_tokens: int, inter: int) -> int:
 
 def moe_dense_ffn_forward(x, dense: dict, y, ws, flags: int = 0, stream=None):
     """Enqueue the dense SwiGLU MLP for x [T,1280] f32 into y [T,1280] f32."""
+    import torch
+    _want(x, torch.float32, (x.shape[0], HIDDEN), "x")
+    _want(y, torch.float32, (x.shape[0], HIDDEN), "y")
     check(load().moe_dense_ffn_forward(_ptr(x), x.shape[0], _ptr(dense["q"]), _ptr(dense["s"]), dense["bits"],
                                        dense["group"], dense["inter"], _ptr(y), flags, _ptr(ws), ws.numel(),
                                        _stream(stream)))
@@ -300,7 +320,16 @@ def moe_rswa_workspace_bytes(n_streams: int, n_ref: int) -> int:
 
 def moe_rswa_decode(dev: dict, out, ws, stream=None):
     """Enqueue one R-SWA decode step (updates dev["ring_k"], dev["ring_v"] in place)."""
-    S = dev["q"].shape[0]
+    import torch
+    S, n_ref = dev["q"].shape[0], dev["n_ref"]
+    for k in ("q", "k_new", "v_new"):
+        _want(dev[k], torch.float32, (S, 10, 128), k)
+    for k in ("ref_k", "ref_v"):
+        _want(dev[k], torch.int16, (S, 10, n_ref, 128), k)
+    for k in ("ring_k", "ring_v"):
+        _want(dev[k], torch.int16, (S, 10, 128, 128), k)
+    _want(dev["n_gen"], torch.int32, (S,), "n_gen")
+    _want(out, torch.float32, (S, 10, 128), "out")
     check(load().moe_rswa_decode(S, dev["n_ref"], _ptr(dev["q"]), _ptr(dev["k_new"]), _ptr(dev["v_new"]),
                                  _ptr(dev["ref_k"]), _ptr(dev["ref_v"]), _ptr(dev["ring_k"]), _ptr(dev["ring_v"]),
                                  _ptr(dev["n_gen"]), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))

@@ -1813,7 +1813,13 @@ template <int BITS, bool SPLIT, int G, int MTL>
 __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid) {
   constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MTL / 16;
   constexpr int CPG = G / 32, GPS = KS / G, NG = H / G;
-  constexpr int D = BITS == 4 ? 4 : 3;      // B stages in flight
+  constexpr int D = G == 32 ? 3 : (BITS == 4 ? 4 : 3);   // B stages in flight
+  // With G = 32 every K step is its own scale group, and a fully unrolled
+  // stage loop lets the compiler hoist matrix-core products far ahead of their
+  // scale multiply (and spill them): there the stages run in blocks of 6 with
+  // a loop between the blocks.
+  constexpr int SB = G == 32 ? 6 : NSTAGE;
+  static_assert(SB % D == 0 && SB % 6 == 0 || SB == NSTAGE, "ring slots fixed within a block");
   constexpr bool F32 = SPLIT;
   constexpr int APL = SPLIT ? 2 : 1;
   constexpr int NSEG = MTL * KS / 8;        // A segments (8 elements) per stage: one per thread up to 512
@@ -1912,13 +1918,17 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
   for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
   store_a1(lds[0], A[0]);
 
+#pragma unroll 1
+  for (int s0 = 0; s0 < NSTAGE; s0 += SB) {
 #pragma unroll
-  for (int st = 0; st < NSTAGE; ++st) {
+  for (int d = 0; d < SB; ++d) {
+    const int st = s0 + d;
+    if (SB != NSTAGE && st >= NSTAGE) break;
     __syncthreads();   // lds[st & 1] holds A(st); lds[(st + 1) & 1] is free
-    if (st + 1 < NSTAGE) store_a1(lds[(st + 1) & 1], A[(st + 1) % 3]);
-    if (st + 3 < NSTAGE) fetch_a1(A[st % 3], (st + 3) * KS, true);
-    const _Float16* la = lds[st & 1];
-    const int sl = st % D;
+    if (st + 1 < NSTAGE) store_a1(lds[(d + 1) & 1], A[(d + 1) % 3]);
+    if (st + 3 < NSTAGE) fetch_a1(A[d % 3], (st + 3) * KS, true);
+    const _Float16* la = lds[d & 1];
+    const int sl = d % D;
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
       const bool first = (c % CPG) == 0, last = (c % CPG) == CPG - 1;
@@ -1952,6 +1962,7 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
       }
     }
     if (st + D < NSTAGE) load_b(bq[sl], sq[sl], st + D);   // the slot just used takes stage st + D
+  }
   }
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
