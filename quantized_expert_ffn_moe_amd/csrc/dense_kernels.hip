@@ -60,14 +60,40 @@ __device__ __forceinline__ float piece_value(const uint4& w, int i) {
   }
 }
 
+// int8 code i of a piece as offset binary, code + 128 in [1, 255], one
+// unsigned-byte conversion each (the word is XORed with 0x80808080 once)
+__device__ __forceinline__ float ubyte_value(uint32_t u, int b) { return (float)((u >> (8 * b)) & 0xFFu); }
+
 // acc[t] += scale * sum_i value_i * x[t][e0 + i] over the EPP values of one
-// piece (x rows of stride XS floats in LDS).
+// piece (x rows of stride XS floats in LDS).  With xsum (int8 only: per token
+// and piece, the sum of the piece's x values) the codes are read in offset
+// binary and the sum corrected by -128 * xsum.
 template <int WT, int NT, int XS>
-__device__ __forceinline__ void piece_fma(const uint4& w, const float* x, int e0, float scale, float (&acc)[NT]) {
+__device__ __forceinline__ void piece_fma(const uint4& w, const float* x, int e0, float scale, float (&acc)[NT],
+                                          const float* xsum = nullptr, int xs_stride = 0) {
   constexpr int EPP = 128 / WT;
   float d[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) d[t] = 0.f;
+  if (WT == 8 && xsum) {
+    const uint32_t ob[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u, w.w ^ 0x80808080u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float4 x4 = *(const float4*)&x[t * XS + e0 + 4 * k];
+        d[t] = __fmaf_rn(ubyte_value(ob[k], 0), x4.x, d[t]);
+        d[t] = __fmaf_rn(ubyte_value(ob[k], 1), x4.y, d[t]);
+        d[t] = __fmaf_rn(ubyte_value(ob[k], 2), x4.z, d[t]);
+        d[t] = __fmaf_rn(ubyte_value(ob[k], 3), x4.w, d[t]);
+      }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      d[t] = __fmaf_rn(-128.0f, xsum[t * xs_stride + e0 / EPP], d[t]);
+      acc[t] = __fmaf_rn(scale, d[t], acc[t]);
+    }
+    return;
+  }
   // (with several tokens, unrolled in pairs: a full unroll keeps every x value
   // of the piece live at once)
 #pragma unroll (NT == 1 ? EPP / 4 : 2)
@@ -157,6 +183,7 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   constexpr int LPR = 16, KPL = P / LPR, RG = 64 / LPR;
   static_assert(P % LPR == 0, "whole pieces per lane");
   __shared__ __attribute__((aligned(16))) float xs[NT * H];
+  __shared__ float xsum[WT == 8 ? NT * P : 1];        // int8: per token and piece, the sum of its z
   __shared__ float red[4 * NT];
   __shared__ float cv[4][NT];
   __shared__ int ci[4][NT];
@@ -181,6 +208,16 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   };
   load(0, 0);
   rows_to_lds<NT>(a.h, a.T, a.norm, a.eps, xs, red);
+  if (WT == 8) {
+    for (int u = tid; u < NT * P; u += 256) {
+      const float* xp = xs + (u / P) * H + EPP * (u % P);
+      float sm = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPP; ++i) sm += xp[i];
+      xsum[u] = sm;
+    }
+    __syncthreads();
+  }
 
   float bv[NT];
   int bi[NT];
@@ -193,7 +230,8 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.f;
 #pragma unroll
-    for (int m = 0; m < KPL; ++m) piece_fma<WT, NT, H>(wb[s & 1][m], xs, EPP * (l + LPR * m), sc[s & 1][m], acc);
+    for (int m = 0; m < KPL; ++m)
+      piece_fma<WT, NT, H>(wb[s & 1][m], xs, EPP * (l + LPR * m), sc[s & 1][m], acc, WT == 8 ? xsum : nullptr, P);
     const int row = row0 + s * RG + rg;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
