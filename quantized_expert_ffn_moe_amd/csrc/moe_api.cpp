@@ -37,6 +37,7 @@ struct Workspace {
   int32_t* tiles;    // [max_tiles][2]
   int32_t* perm;     // [T*6]
   int32_t* pos_of;   // [T*6]
+  int32_t* blkcnt;   // [T*6/1024 + 1][E] per-block histogram counts
   // decode path (aliases the grouped buffers)
   float* part;       // [T][N_ITEMS][H]
   size_t bytes;
@@ -72,6 +73,7 @@ Workspace carve(void* base, int T) {
   w.tiles = (int32_t*)c.take((size_t)w.max_tiles * 2 * 4);
   w.perm = (int32_t*)c.take(slots * 4);
   w.pos_of = (int32_t*)c.take(slots * 4);
+  w.blkcnt = (int32_t*)c.take((slots / HIST_BLOCK + 1) * E * 4);
   const size_t grouped_end = c.off;
   c.off = union_start;
   w.part = T <= DECODE_FORCE_MAX_T ? (float*)c.take((size_t)T * N_ITEMS * H * 4) : nullptr;
@@ -303,6 +305,7 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   HistArgs ha;
   ha.ids = topk_ids; ha.T = T; ha.counts = ws.counts; ha.offsets = ws.offsets;
   ha.perm = ws.perm; ha.pos_of = ws.pos_of; ha.tiles = ws.tiles; ha.ntiles = ws.ntiles; ha.mt = mtl;
+  ha.blkcnt = ws.blkcnt;
   if (launch_hist(ha, s) != hipSuccess) return MOE_E_HIP;
 
   GroupedArgs ga;

@@ -103,7 +103,10 @@ struct HistArgs {
   int32_t* perm; int32_t* pos_of;       // [T*6]: sorted slot -> (t*6+j); (t*6+j) -> sorted position
   int32_t* tiles; int32_t* ntiles;      // [max][2] (expert, first row), count
   int mt;                               // rows per tile
+  int32_t* blkcnt;                      // [blocks][E] per-block counts (the multi-workgroup histogram)
 };
+constexpr int HIST_BLOCK = 1024;        // slots per workgroup of the multi-workgroup histogram
+constexpr int HIST_ONE_WG_MAX = 4096;   // slots up to which one workgroup does it all
 
 struct GroupedArgs {
   // A rows

@@ -1264,6 +1264,86 @@ __global__ __launch_bounds__(1024) void hist_kernel(HistArgs a) {
   }
 }
 
+// Many slots: the same result from one workgroup per block of HIST_BLOCK
+// slots (wave w of block b owns slots 1024 b + 64 w .. + 63), in two launches:
+// every block's counts, then every block places its slots after those of the
+// blocks before it (per expert, blocks in order, then waves, then lanes), so
+// the permutation is the same stable sort.
+__global__ __launch_bounds__(1024) void hist_count_kernel(HistArgs a) {
+  __shared__ int cnt[E];
+  const int N = a.T * TOPK, tid = threadIdx.x, i = blockIdx.x * HIST_BLOCK + tid;
+  if (tid < E) cnt[tid] = 0;
+  __syncthreads();
+  if (i < N) atomicAdd(&cnt[a.ids[i]], 1);
+  __syncthreads();
+  if (tid < E) a.blkcnt[blockIdx.x * E + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(1024) void hist_place_kernel(HistArgs a) {
+  __shared__ int cntw[16][E];
+  __shared__ int basew[16][E];
+  __shared__ int off[E + 1], toff[E + 1], before[E];
+  const int N = a.T * TOPK, nb = gridDim.x, b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int i = b * HIST_BLOCK + tid;
+  const bool valid = i < N;
+  const int my_e = valid ? a.ids[i] : 0;
+  (&cntw[0][0])[tid] = 0;   // 16 x 64 = 1024 entries
+  if (wv == 0) {   // totals and this block's start per expert (lane = expert), blocks in order
+    int tot = 0, bef = 0;
+    for (int u = 0; u < nb; ++u) {
+      const int c = a.blkcnt[u * E + lane];
+      bef += u < b ? c : 0;
+      tot += c;
+    }
+    before[lane] = bef;
+    const int tl = (tot + a.mt - 1) / a.mt;
+    int inc = tot, tinc = tl;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(inc, d), to = __shfl_up(tinc, d);
+      if (lane >= d) { inc += o; tinc += to; }
+    }
+    off[lane + 1] = inc;
+    toff[lane + 1] = tinc;
+    if (lane == 0) { off[0] = 0; toff[0] = 0; }
+    if (b == 0) {
+      a.counts[lane] = tot;
+      if (lane == 63) { *a.ntiles = tinc; a.offsets[E] = inc; }
+    }
+  }
+  __syncthreads();
+  if (valid) atomicAdd(&cntw[wv][my_e], 1);
+  if (b == 0 && tid < E) {
+    a.offsets[tid] = off[tid];
+    for (int j = 0; j < toff[tid + 1] - toff[tid]; ++j) {
+      a.tiles[2 * (toff[tid] + j)] = tid;
+      a.tiles[2 * (toff[tid] + j) + 1] = j * a.mt;
+    }
+  }
+  __syncthreads();
+  {   // thread (w, e): the expert's start for wave w of this block
+    int run = off[lane] + before[lane];
+    for (int u = 0; u < wv; ++u) run += cntw[u][lane];
+    basew[wv][lane] = run;
+  }
+  __syncthreads();
+  // one round of 64 slots per wave: lanes of the same expert matched by one
+  // ballot per bit of the expert id, positions by prefix popcount
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int bt = 0; bt < 6; ++bt) {
+    const uint64_t ones = __ballot(valid && ((my_e >> bt) & 1));
+    same &= ((my_e >> bt) & 1) ? ones : ~ones;
+  }
+  if (valid) {
+    const int p = basew[wv][my_e] + __popcll(same & below);
+    a.perm[p] = i;
+    a.pos_of[i] = p;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Grouped path: exact-integer f16 operands on v_mfma_f32_16x16x32_f16.
 // ---------------------------------------------------------------------------
@@ -2257,7 +2337,14 @@ hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s) {
 }
 
 hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(hist_kernel, dim3(1), dim3(1024), 0, s, a);
+  const int n = a.T * TOPK;
+  if (n <= HIST_ONE_WG_MAX) {
+    hipLaunchKernelGGL(hist_kernel, dim3(1), dim3(1024), 0, s, a);
+  } else {
+    const int nb = (n + HIST_BLOCK - 1) / HIST_BLOCK;
+    hipLaunchKernelGGL(hist_count_kernel, dim3(nb), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(hist_place_kernel, dim3(nb), dim3(1024), 0, s, a);
+  }
   return hipGetLastError();
 }
 
