@@ -91,7 +91,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--path", choices=["chain", "layers"], default="chain")
     ap.add_argument("--workload", choices=["decode", "batched32", "prefill273", "multipage2184", "batch128", "batch256",
-                                           "lmhead_bf16", "lmhead_int8", "dense0", "rswa128"],
+                                           "lmhead_bf16", "lmhead_int8", "dense0", "rswa128", "ffnstack"],
                     default="decode",
                     help="decode = the headline 11-layer decode step; the prefill workloads report MFMA "
                          "figures; batchN = one continuous-batch decode step of N streams (HBM figures)")
@@ -129,6 +129,8 @@ def main():
         return bench_dense(args)
     if args.workload == "rswa128":
         return bench_rswa(args)
+    if args.workload == "ffnstack":
+        return bench_ffnstack(args)
     if args.workload != "decode":
         return bench_prefill(args)
 
@@ -370,6 +372,73 @@ def bench_dense(args):
                       "config": {"workload": name, "tokens": 1},
                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_call": nbytes}}),
+          flush=True)
+
+
+def bench_ffnstack(args):
+    """One decode token through the decoder's FFN stack and head: the layer-0
+    dense MLP (int8 G64, residual in place), the 11 MoE layers in one
+    persistent launch, the final norm + lm_head (bf16) + greedy token; weight
+    replicas rotated.  Attention is not part of it."""
+    import numpy as np
+    import torch
+
+    from quantized_expert_ffn_moe_amd import binding as B
+    from synth import QFmt, WORKLOADS, make_dense_ffn, make_hidden, make_layer, make_lm_head
+
+    wl = WORKLOADS[1]
+    L = wl.n_layers
+    H = 1280
+    R = 2
+    layers = [make_layer(wl, li) for li in range(L)]
+    moe_sets = [[B.pack_layer(layer) for layer in layers] for _ in range(R)]
+    warr = [B.layer_weights(ms) for ms in moe_sets]
+    ffn = make_dense_ffn(QFmt(8, 64))
+    dense_sets = [B.dense_ffn_to_device(ffn) for _ in range(R)]
+    head = make_lm_head("bf16")
+    head_sets = [B.lm_head_to_device(head) for _ in range(R)]
+    stream = torch.cuda.Stream()
+    xs = torch.from_numpy(make_hidden(args.warmup + args.steps)).cuda()
+    h = torch.empty(1, H, dtype=torch.float32, device="cuda")
+    y = torch.empty(1, H, dtype=torch.float32, device="cuda")
+    ids = torch.empty(L, 6, dtype=torch.int32, device="cuda")
+    w = torch.empty(L, 6, dtype=torch.float32, device="cuda")
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    tl = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws_d = torch.empty(B.moe_dense_ffn_workspace_bytes(1, ffn["inter"]), dtype=torch.uint8, device="cuda")
+    ws_m = B.decode_workspace(stream=stream)
+    ws_h = torch.empty(B.moe_lm_head_workspace_bytes(1, head["vocab"]), dtype=torch.uint8, device="cuda")
+    flags = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE
+
+    def step(i):
+        r = i % R
+        h.copy_(xs[i:i + 1])
+        B.moe_dense_ffn_forward(h, dense_sets[r], h, ws_d, flags, stream=stream)
+        B.moe_decode_forward(h, y, moe_sets[r], ids, w, ws_m, flags, weights=warr[r], stream=stream)
+        B.moe_lm_head_argmax(y, head_sets[r], tok, tl, ws_h, B.MOE_NORM_INPUT, None, stream=stream)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.warmup, args.warmup + args.steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ids_last = ids.cpu().numpy()
+    moe_bytes = sum(layer_bytes(ids_last[li].tolist(), wl.routed, wl.shared) for li in range(L))
+    dense_bytes = 3 * ffn["inter"] * H + 3 * ffn["inter"] * (H // 64) * 4 + H * 4 * 3
+    head_bytes = head["vocab"] * H * 2 + H * 4 + 8
+    nbytes = moe_bytes + dense_bytes + head_bytes
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    name = "decoder_ffn_stack_dense0_11moe_lmhead_bf16_1tok"
+    print(json.dumps({"metric": f"{name}: tokens/s", "value": 1e3 / ms, "unit": "tokens/s", "ms_per_step": ms,
+                      "steps": args.steps, "warmup": args.warmup, "dtype": "f32",
+                      "config": {"workload": name, "tokens": 1, "moe_layers": L},
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_step": nbytes}}),
           flush=True)
 
 

