@@ -77,6 +77,20 @@ def test_ragged_token_counts_both_paths(lib, T):
     np.testing.assert_array_equal(a[0], b[0])
 
 
+@pytest.mark.parametrize("wi,T", [(2, 8), (2, 85), (2, 86), (2, 682), (2, 683), (5, 85), (5, 86), (5, 683)])
+def test_tile_shape_boundaries(lib, wi, T):
+    """Token counts on both sides of the grouped path's switches: the two-pass
+    router (from 8 tokens), 16- and 32-row fused tiles (512 slots), small and
+    large tiles (4096 slots, where the histogram also goes multi-workgroup
+    above); one format pair (int4 G32) and the mixed one (int4 G64 routed,
+    int8 G128 shared, f32 input)."""
+    say(f"workload {wi} T={T}")
+    x, xt = tokens(wi, n=T, batch=11)
+    ids, w, y = run(xt, packed_of(wi, 0), 0)
+    ratio, near = check_layer(x, layer_of(wi, 0), ids, w, y)
+    say(f"  err/rms {ratio:.2e} near-ties {near}")
+
+
 def test_mixed_formats_f32_input_grouped(lib):
     """int4 G64 routed + int8 G128 shared with f32 activations (hi/lo split operands)."""
     from quantized_expert_ffn_moe_amd import binding as B
