@@ -23,6 +23,14 @@ What it computes, and where the pages say so
   policy: router and norms stay high precision).
 * RMSNorm of the residual stream before each chained layer (the decoder's
   RMSNorm, demo page step 7; README "Architecture").
+* The two-level 4-bit format of the community K-quant decoder that the WebGPU
+  engine reads with its q4k storage (Unlimited-OCR DeepEncoder ONNX model
+  card, "The rest of the pipeline").  The pages name the format only; the
+  definition used here is the usual K-quant one: super-blocks of 256 weights
+  along K with f16 factors d and dmin, split into 8 sub-blocks of 32 with a
+  6-bit scale sc and a 6-bit minimum m each, unsigned 4-bit codes q, and
+  W = d * sc * q - dmin * m.  A row whose length is not a multiple of 256 ends
+  in a partial super-block (fewer sub-blocks, same d and dmin meaning).
 
 Readings where the pages are silent (each restated where it is used):
 ties in the greedy pick go to the lower expert index; the ids are returned in
@@ -34,7 +42,10 @@ input is the RMSNorm output rounded to bf16 (nearest, ties to even).
 
 Parity pins: every function here is checked in ``tests/test_oracle.py`` against
 closed forms, brute force, library routines on special cases, invariants and a
-hand-worked fixture (``tests/golden/tiny_layer.json``); none is unpinned.
+hand-worked fixture (``tests/golden/tiny_layer.json``); the two-level format in
+``tests/test_q4k_oracle.py`` against a hand-worked super-block
+(``tests/golden/q4k_superblock.json``), its reduction to the symmetric format
+and its affine structure; none is unpinned.
 """
 from __future__ import annotations
 
@@ -118,6 +129,36 @@ def dequantize(codes, scales, group: int) -> np.ndarray:
     return Q.astype(f64) * np.repeat(S.astype(f64), group, axis=1)
 
 
+def f16_value(bits) -> np.ndarray:
+    """f64 value of IEEE half-precision bit patterns."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(f64)
+
+
+def dequantize_q4k(q, d, dmin, sc, m, sub: int = 32, superblock: int = 256) -> np.ndarray:
+    """Two-level 4-bit format, per row r and column k:
+
+        W[r, k] = d[r, k // 256] * sc[r, k // 32] * q[r, k] - dmin[r, k // 256] * m[r, k // 32]
+
+    q: unsigned codes [N][K] in 0..15; sc, m: 6-bit integers [N][K/32];
+    d, dmin: f16 bit patterns [N][ceil(K/256)].  Computed in f64 (every product
+    is exact; the difference rounds at most once, in f64).
+    """
+    Q = np.asarray(q)
+    N, K = Q.shape
+    nsb = -(-K // superblock)
+    sc, m = np.asarray(sc), np.asarray(m)
+    if K % sub or sc.shape != (N, K // sub) or m.shape != sc.shape or np.shape(d) != (N, nsb) \
+            or np.shape(dmin) != (N, nsb):
+        raise ValueError("two-level format: field shapes do not match the codes")
+    if Q.max(initial=0) > 15 or sc.max(initial=0) > 63 or m.max(initial=0) > 63:
+        raise ValueError("two-level format: a field is out of range")
+    D = np.repeat(f16_value(d), superblock, axis=1)[:, :K]
+    Dm = np.repeat(f16_value(dmin), superblock, axis=1)[:, :K]
+    S = np.repeat(sc.astype(f64), sub, axis=1)
+    M = np.repeat(m.astype(f64), sub, axis=1)
+    return D * S * Q.astype(f64) - Dm * M
+
+
 def silu(v) -> np.ndarray:
     """SiLU(v) = v * sigmoid(v) = v / (1 + exp(-v))."""
     v = np.asarray(v, dtype=f64)
@@ -133,20 +174,24 @@ def swiglu_ffn(Wg, Wu, Wd, X) -> np.ndarray:
     return (silu(g) * u) @ Wd.T
 
 
+def _matrix(layer: dict, name: str, fmt, e=None) -> np.ndarray:
+    """Dequantised matrix ``name`` (of routed expert e, or the shared one)."""
+    get = (lambda k: layer[f"{name}_{k}"]) if e is None else (lambda k: layer[f"{name}_{k}"][e])
+    if getattr(fmt, "q4k", False):
+        return dequantize_q4k(get("q"), get("d"), get("dmin"), get("sc"), get("m"))
+    return dequantize(get("q"), get("s"), fmt.group)
+
+
 def expert_weights(layer: dict, e: int):
     """Dequantised (W_g, W_u, W_d) of routed expert e."""
-    G = layer["routed_fmt"].group
-    return (dequantize(layer["gate_q"][e], layer["gate_s"][e], G),
-            dequantize(layer["up_q"][e], layer["up_s"][e], G),
-            dequantize(layer["down_q"][e], layer["down_s"][e], G))
+    f = layer["routed_fmt"]
+    return tuple(_matrix(layer, n, f, e) for n in ("gate", "up", "down"))
 
 
 def shared_weights(layer: dict):
     """Dequantised (W_g, W_u, W_d) of the fused shared expert."""
-    G = layer["shared_fmt"].group
-    return (dequantize(layer["shared_gate_q"], layer["shared_gate_s"], G),
-            dequantize(layer["shared_up_q"], layer["shared_up_s"], G),
-            dequantize(layer["shared_down_q"], layer["shared_down_s"], G))
+    f = layer["shared_fmt"]
+    return tuple(_matrix(layer, n, f) for n in ("shared_gate", "shared_up", "shared_down"))
 
 
 # --------------------------------------------------------------------------

@@ -43,14 +43,23 @@ _T_SGATE_S, _T_SUP_S, _T_SDOWN_S = 11, 12, 13
 _TOKEN_LAYER = 0xFFFF  # "layer" slot used for token batches
 
 
+# group value that selects the two-level 4-bit format (see ``_q4k``)
+Q4K_GROUP = 256
+Q4K_SUB = 32
+
+
 @dataclass(frozen=True)
 class QFmt:
     bits: int   # 4 or 8
-    group: int  # consecutive K elements that share one f32 scale
+    group: int  # consecutive K elements that share one f32 scale (Q4K_GROUP: the two-level format)
 
     @property
     def code_range(self):
         return (-8, 7) if self.bits == 4 else (-127, 127)
+
+    @property
+    def q4k(self) -> bool:
+        return self.bits == 4 and self.group == Q4K_GROUP
 
 
 @dataclass(frozen=True)
@@ -90,6 +99,11 @@ WORKLOADS = [
              QFmt(4, 64), QFmt(8, 128), "none", True, False),
     Workload(6, "continuous_batch_decode_256streams_11layers_int4g64_shared_int8g128", 256, 11, "f32",
              QFmt(4, 64), QFmt(8, 128), "none", True, False),
+    # the decode step with the routed experts in the two-level (Q4_K-style)
+    # 4-bit format and the shared expert in int8: the q4k/q8 storage of the
+    # WebGPU engine the model card pairs with the community K-quant GGUF
+    Workload(7, "decode_1tok_11layers_q4k_shared_int8g128", 1, 11, "f32",
+             QFmt(4, Q4K_GROUP), QFmt(8, 128), "none", True, False),
 ]
 
 
@@ -108,6 +122,39 @@ def _codes(rng, shape, fmt: QFmt) -> np.ndarray:
 
 def _scales(rng, shape) -> np.ndarray:
     return rng.uniform(0.002, 0.02, size=shape).astype(np.float32)
+
+
+def _q4k(rng, lead: tuple, K: int) -> dict:
+    """One stack of matrices ``[*lead][K]`` in the two-level 4-bit format.
+
+    Fields: unsigned 4-bit codes q in [0, 15]; per 32 columns (a sub-block) a
+    6-bit scale sc and a 6-bit minimum m; per 256 columns (a super-block; the
+    last one of a row is partial when K is not a multiple of 256) the f16
+    factors d and dmin, returned as their 16-bit patterns.  Distribution: d
+    uniform in [1e-4, 4e-4], dmin = 8 d (rounded to f16), sc uniform in
+    [8, 63] and m = sc - U{0..8} clipped at 0, so that a sub-block's weights
+    d sc q - dmin m straddle zero with magnitudes like the symmetric formats'.
+    """
+    nsb, nsub = -(-K // Q4K_GROUP), K // Q4K_SUB
+    q = rng.integers(0, 15, size=lead + (K,), endpoint=True, dtype=np.uint8)
+    d = rng.uniform(1e-4, 4e-4, size=lead + (nsb,)).astype(np.float16)
+    dmin = (d.astype(np.float32) * 8.0).astype(np.float16)
+    sc = rng.integers(8, 63, size=lead + (nsub,), endpoint=True).astype(np.uint8)
+    m = np.clip(sc.astype(np.int16) - rng.integers(0, 8, size=lead + (nsub,), endpoint=True), 0, 63).astype(np.uint8)
+    return {"q": q, "d": d.view(np.uint16), "dmin": dmin.view(np.uint16), "sc": sc, "m": m}
+
+
+def _matrix(out: dict, name: str, rng_q, rng_s, lead: tuple, rows: int, K: int, fmt: QFmt):
+    """Codes and scales of one matrix stack into ``out`` under ``name``_*:
+    symmetric formats give ``_q`` (int8 codes) and ``_s`` (f32 scales); the
+    two-level format gives ``_q`` (uint8 codes 0..15), ``_d``, ``_dmin``,
+    ``_sc`` and ``_m``."""
+    if fmt.q4k:
+        for k, v in _q4k(rng_q, lead + (rows,), K).items():
+            out[f"{name}_{k}"] = v
+    else:
+        out[f"{name}_q"] = _codes(rng_q, lead + (rows, K), fmt)
+        out[f"{name}_s"] = _scales(rng_s, lead + (rows, K // fmt.group))
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -150,21 +197,15 @@ def make_layer(wl: Workload, layer: int) -> dict:
     d = {
         "router_w": (_rng(w, l, _T_ROUTER).standard_normal((E, H)) * 0.02).astype(np.float32),
         "router_b": _bias(wl, l),
-        "gate_q": _codes(_rng(w, l, _T_GATE), (E, I, H), rf),
-        "up_q": _codes(_rng(w, l, _T_UP), (E, I, H), rf),
-        "down_q": _codes(_rng(w, l, _T_DOWN), (E, H, I), rf),
-        "gate_s": _scales(_rng(w, l, _T_GATE_S), (E, I, H // rf.group)),
-        "up_s": _scales(_rng(w, l, _T_UP_S), (E, I, H // rf.group)),
-        "down_s": _scales(_rng(w, l, _T_DOWN_S), (E, H, I // rf.group)),
-        "shared_gate_q": _codes(_rng(w, l, _T_SGATE), (Is, H), sf),
-        "shared_up_q": _codes(_rng(w, l, _T_SUP), (Is, H), sf),
-        "shared_down_q": _codes(_rng(w, l, _T_SDOWN), (H, Is), sf),
-        "shared_gate_s": _scales(_rng(w, l, _T_SGATE_S), (Is, H // sf.group)),
-        "shared_up_s": _scales(_rng(w, l, _T_SUP_S), (Is, H // sf.group)),
-        "shared_down_s": _scales(_rng(w, l, _T_SDOWN_S), (H, Is // sf.group)),
         "routed_fmt": rf,
         "shared_fmt": sf,
     }
+    _matrix(d, "gate", _rng(w, l, _T_GATE), _rng(w, l, _T_GATE_S), (E,), I, H, rf)
+    _matrix(d, "up", _rng(w, l, _T_UP), _rng(w, l, _T_UP_S), (E,), I, H, rf)
+    _matrix(d, "down", _rng(w, l, _T_DOWN), _rng(w, l, _T_DOWN_S), (E,), H, I, rf)
+    _matrix(d, "shared_gate", _rng(w, l, _T_SGATE), _rng(w, l, _T_SGATE_S), (), Is, H, sf)
+    _matrix(d, "shared_up", _rng(w, l, _T_SUP), _rng(w, l, _T_SUP_S), (), Is, H, sf)
+    _matrix(d, "shared_down", _rng(w, l, _T_SDOWN), _rng(w, l, _T_SDOWN_S), (), H, Is, sf)
     return d
 
 
