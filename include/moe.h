@@ -47,12 +47,16 @@ extern "C" {
 #define MOE_INTER 896
 #define MOE_SHARED_INTER 1792
 #define MOE_MAX_TOKENS 8192
+/* Group value that, with 4-bit codes, selects the two-level (Q4_K-style)
+   expert format; see moe_pack_expert_q4k. */
+#define MOE_Q4K 256
 
 typedef enum {
   MOE_OK = 0,
   MOE_E_NULLPTR = 1,   /* a required pointer is NULL */
   MOE_E_SHAPE = 2,     /* token count or intermediate size out of range */
-  MOE_E_FORMAT = 3,    /* bits not in {4, 8}, group not in {32, 64, 128}, or a code out of range */
+  MOE_E_FORMAT = 3,    /* bits not in {4, 8}, group not in {32, 64, 128} (or MOE_Q4K with 4 bits),
+                          a code out of range, or a format the requested path does not run */
   MOE_E_ALIGN = 4,     /* a device pointer is not 16-byte aligned */
   MOE_E_WORKSPACE = 5, /* workspace smaller than moe_workspace_bytes() */
   MOE_E_HIP = 6,       /* the HIP runtime reported an error while enqueueing */
@@ -121,11 +125,58 @@ const char* moe_status_str(int32_t status);
  * float e * scale_count.
  * ------------------------------------------------------------------------ */
 size_t moe_expert_code_bytes(int32_t bits, int32_t inter);
+/* floats of packed scales per expert (group MOE_Q4K: 4-byte words of records) */
 size_t moe_expert_scale_count(int32_t group_size, int32_t inter);
 moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t* down,
                              const float* gate_scales, const float* up_scales,
                              const float* down_scales, int32_t inter, int32_t bits,
                              int32_t group_size, void* codes_out, float* scales_out);
+
+/* ------------------------------------------------------------------------
+ * Two-level 4-bit expert format (Q4_K-style).  The Unlimited-OCR DeepEncoder
+ * ONNX model card ("The rest of the pipeline") pairs the pipeline with a
+ * community K-quant GGUF of the decoder, read by the WebGPU engine's q4k
+ * storage; the pages define no layout, so the K-quant definition is taken:
+ * along K, super-blocks of 256 columns with f16 factors d and dmin, split
+ * into 8 sub-blocks of 32 columns with 6-bit unsigned sc and m, unsigned
+ * 4-bit codes q, and
+ *     W[r][k] = d[r][k/256] * sc[r][k/32] * q[r][k] - dmin[r][k/256] * m[r][k/32].
+ * A row whose length is not a multiple of 256 (the routed down projection,
+ * K = 896) ends in a partial super-block of 4 sub-blocks.
+ *
+ * Canonical input of one matrix [N rows][K] (moe_q4k_matrix_t, host memory):
+ *   q [N][K] codes 0..15, one per byte; d, dmin [N][ceil(K/256)] f16 bit
+ *   patterns (finite); sc, m [N][K/32] values 0..63, one per byte.
+ * moe_pack_expert_q4k writes:
+ *   codes_out: moe_expert_code_bytes(4, inter) bytes, the int4 tile layout
+ *     above holding q - 8 (so W = s (q - 8) + beta with s = d sc and
+ *     beta = 8 s - dmin m per sub-block);
+ *   meta_out: 4 * moe_expert_scale_count(MOE_Q4K, inter) bytes of 16-byte
+ *     records: gate [inter][5], up [inter][5], down [ceil(inter/256)][1280]
+ *     (record (b, r) of down = row r, super-block b).  Record words:
+ *     w0 = d | dmin << 16; w1 = low 4 bits of sc_0..sc_7 (bits 4j..4j+3);
+ *     w2 = low 4 bits of m_0..m_7; w3 = high 2 bits of sc_j at bit 2j and of
+ *     m_j at bit 16 + 2j; sub-blocks past the end of a row are zero.
+ * Experts are concatenated as for moe_pack_expert.  The records travel in
+ * the expert_scales / shared_scales arguments with group = MOE_Q4K and
+ * bits = 4 (4.5 bits per weight where K is a multiple of 256).
+ * This format runs on the per-token (GEMV) path: moe_decode_forward, and
+ * moe_layer_forward with n_tokens <= 64 (always on that path, whatever the
+ * token count); MOE_FORCE_GROUPED or more tokens give MOE_E_FORMAT.
+ * Returns MOE_E_NULLPTR for a missing pointer, MOE_E_SHAPE for an
+ * intermediate size other than 896 or 1792, MOE_E_FORMAT for a field out of
+ * range (nothing is written then).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const uint8_t* q;      /* [N][K] codes 0..15 */
+  const uint16_t* d;     /* [N][ceil(K/256)] f16 */
+  const uint16_t* dmin;  /* [N][ceil(K/256)] f16 */
+  const uint8_t* sc;     /* [N][K/32] 0..63 */
+  const uint8_t* m;      /* [N][K/32] 0..63 */
+} moe_q4k_matrix_t;
+moe_status_t moe_pack_expert_q4k(const moe_q4k_matrix_t* gate, const moe_q4k_matrix_t* up,
+                                 const moe_q4k_matrix_t* down, int32_t inter, void* codes_out,
+                                 void* meta_out);
 
 /* Bytes of device workspace moe_layer_forward needs for n_tokens tokens. */
 size_t moe_workspace_bytes(int32_t n_tokens);

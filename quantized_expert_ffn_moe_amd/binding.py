@@ -19,11 +19,13 @@ MOE_FORCE_DECODE, MOE_FORCE_GROUPED = 8, 16
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 EXPORTS = ("moe_status_str", "moe_expert_code_bytes", "moe_expert_scale_count", "moe_pack_expert",
+           "moe_pack_expert_q4k",
            "moe_workspace_bytes", "moe_layer_forward", "moe_rmsnorm", "moe_decode_workspace_bytes",
            "moe_decode_workspace_init", "moe_decode_forward", "moe_lm_head_workspace_bytes",
            "moe_lm_head_argmax", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_forward",
            "moe_rswa_workspace_bytes", "moe_rswa_decode")
 MOE_HEAD_INT8, MOE_HEAD_BF16 = 8, 16
+MOE_Q4K = 256   # group value of the two-level 4-bit format
 DECODE_MAX_LAYERS = 16
 
 
@@ -32,6 +34,14 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("expert_q", ctypes.c_void_p), ("expert_scales", ctypes.c_void_p),
                 ("shared_q", ctypes.c_void_p), ("shared_scales", ctypes.c_void_p)]
+
+
+
+class Q4kMatrix(ctypes.Structure):
+    """moe_q4k_matrix_t: host pointers of one two-level matrix."""
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("dmin", ctypes.c_void_p),
+                ("sc", ctypes.c_void_p), ("m", ctypes.c_void_p)]
+
 
 _lib = None
 
@@ -57,6 +67,8 @@ def load():
     L.moe_expert_scale_count.argtypes = [i32, i32]
     L.moe_pack_expert.restype = i32
     L.moe_pack_expert.argtypes = [vp] * 6 + [i32, i32, i32, vp, vp]
+    L.moe_pack_expert_q4k.restype = i32
+    L.moe_pack_expert_q4k.argtypes = [ctypes.POINTER(Q4kMatrix)] * 3 + [i32, vp, vp]
     L.moe_workspace_bytes.restype = sz
     L.moe_workspace_bytes.argtypes = [i32]
     L.moe_layer_forward.restype = i32
@@ -128,6 +140,31 @@ def moe_pack_expert(gate, up, down, gate_s, up_s, down_s, bits: int, group: int)
     return codes, scales
 
 
+def moe_pack_expert_q4k(gate: dict, up: dict, down: dict):
+    """Pack one two-level expert: dicts with q, d, dmin, sc, m (host numpy) ->
+    (codes uint8, records as float32 words)."""
+    inter = gate["q"].shape[0]
+    keep, mats = [], []
+    for f in (gate, up, down):
+        arrs = {k: np.ascontiguousarray(f[k], dtype=np.uint16 if k in ("d", "dmin") else np.uint8)
+                for k in ("q", "d", "dmin", "sc", "m")}
+        keep.append(arrs)
+        mats.append(Q4kMatrix(*[_np_ptr(arrs[k]) for k in ("q", "d", "dmin", "sc", "m")]))
+    codes = np.empty(moe_expert_code_bytes(4, inter), np.uint8)
+    meta = np.empty(moe_expert_scale_count(MOE_Q4K, inter), np.float32)
+    check(load().moe_pack_expert_q4k(*[ctypes.byref(m) for m in mats], inter, _np_ptr(codes), _np_ptr(meta)))
+    return codes, meta
+
+
+def _pack_one(layer: dict, prefix: str, fmt, e=None):
+    get = (lambda k: layer[f"{prefix}{k}"]) if e is None else (lambda k: layer[f"{prefix}{k}"][e])
+    if fmt.bits == 4 and fmt.group == MOE_Q4K:
+        return moe_pack_expert_q4k(*[{k: get(f"{n}_{k}") for k in ("q", "d", "dmin", "sc", "m")}
+                                     for n in ("gate", "up", "down")])
+    return moe_pack_expert(get("gate_q"), get("up_q"), get("down_q"), get("gate_s"), get("up_s"), get("down_s"),
+                           fmt.bits, fmt.group)
+
+
 def pack_layer(layer: dict, device="cuda"):
     """Pack one layer's codes/scales on the host and move them to the device."""
     import torch
@@ -137,13 +174,10 @@ def pack_layer(layer: dict, device="cuda"):
     codes = np.empty(E * cb, np.uint8)
     scales = np.empty(E * sc, np.float32)
     for e in range(E):
-        c, s = moe_pack_expert(layer["gate_q"][e], layer["up_q"][e], layer["down_q"][e],
-                               layer["gate_s"][e], layer["up_s"][e], layer["down_s"][e], rf.bits, rf.group)
+        c, s = _pack_one(layer, "", rf, e)
         codes[e * cb:(e + 1) * cb] = c
         scales[e * sc:(e + 1) * sc] = s
-    scodes, sscales = moe_pack_expert(layer["shared_gate_q"], layer["shared_up_q"], layer["shared_down_q"],
-                                      layer["shared_gate_s"], layer["shared_up_s"], layer["shared_down_s"],
-                                      sf.bits, sf.group)
+    scodes, sscales = _pack_one(layer, "shared_", sf)
     t = lambda a: torch.from_numpy(a).to(device)
     return {
         "router_w": t(np.ascontiguousarray(layer["router_w"], np.float32)),

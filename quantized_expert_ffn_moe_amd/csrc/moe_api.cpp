@@ -8,7 +8,7 @@
 using namespace moe;
 
 static_assert(MOE_HIDDEN == H && MOE_EXPERTS == E && MOE_TOPK == TOPK && MOE_INTER == I &&
-                  MOE_SHARED_INTER == IS && MOE_MAX_TOKENS == MAX_T,
+                  MOE_SHARED_INTER == IS && MOE_MAX_TOKENS == MAX_T && MOE_Q4K == Q4K,
               "public and internal shape constants disagree");
 
 namespace {
@@ -18,7 +18,7 @@ unsigned long long* g_trace_buffer = nullptr;
 #endif
 
 bool fmt_ok(int bits, int group) {
-  return (bits == 4 || bits == 8) && (group == 32 || group == 64 || group == 128);
+  return ((bits == 4 || bits == 8) && (group == 32 || group == 64 || group == 128)) || (bits == 4 && group == Q4K);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -106,23 +106,25 @@ QW make_qw(const void* q, const float* s, int bits, int group, int inter, bool r
   w.group = group;
   w.inter = inter;
   w.e_bytes = routed ? moe_expert_code_bytes(bits, inter) : 0;
-  w.e_scales = routed ? moe_expert_scale_count(group, inter) : 0;
+  w.e_scales = routed ? scale_words(group, inter) : 0;
   return w;
 }
 
-// gate/up matrices: 1 KiB tiles of 16 rows x KB columns, tile (nt, kb)
-void pack_rows(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
+// gate/up matrices: 1 KiB tiles of 16 rows x KB columns, tile (nt, kb); the
+// stored code of an element is its value plus `off` (-8: two-level codes)
+template <typename C>
+void pack_rows(const C* Q, int N, int K, int bits, uint8_t* out, int off = 0) {
   const int KB = kb_cols(bits), nkb = K / KB;
   for (int nt = 0; nt < N / 16; ++nt)
     for (int kb = 0; kb < nkb; ++kb) {
       uint8_t* tile = out + ((size_t)nt * nkb + kb) * TILE;
       for (int lane = 0; lane < 64; ++lane) {
         const int row = nt * 16 + (lane & 15), q = lane >> 4;
-        const int8_t* src = Q + (size_t)row * K + (size_t)kb * KB;
+        const C* src = Q + (size_t)row * K + (size_t)kb * KB;
         for (int j = 0; j < 4; ++j) {
           uint32_t word = 0;
           if (bits == 4) {
-            for (int i = 0; i < 8; ++i) word |= (uint32_t)(src[32 * j + 8 * q + i] & 15) << (4 * i);
+            for (int i = 0; i < 8; ++i) word |= (uint32_t)(((int)src[32 * j + 8 * q + i] + off) & 15) << (4 * i);
           } else {
             for (int i = 0; i < 4; ++i)
               word |= (uint32_t)(uint8_t)src[32 * (j >> 1) + 8 * q + 4 * (j & 1) + i] << (8 * i);
@@ -134,7 +136,8 @@ void pack_rows(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
 }
 
 // down matrices: 1 KiB tiles of DR rows x 32 columns, tile (kc, rt)
-void pack_slabs(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
+template <typename C>
+void pack_slabs(const C* Q, int N, int K, int bits, uint8_t* out, int off = 0) {
   const int DR = down_rows(bits), nrt = N / DR, nkc = K / 32;
   for (int kc = 0; kc < nkc; ++kc)
     for (int rt = 0; rt < nrt; ++rt) {
@@ -144,10 +147,10 @@ void pack_slabs(const int8_t* Q, int N, int K, int bits, uint8_t* out) {
         for (int j = 0; j < 4; ++j) {
           uint32_t word = 0;
           if (bits == 4) {
-            const int8_t* src = Q + (size_t)(DR * rt + 16 * j + r) * K + 32 * kc + 8 * q;
-            for (int i = 0; i < 8; ++i) word |= (uint32_t)(src[i] & 15) << (4 * i);
+            const C* src = Q + (size_t)(DR * rt + 16 * j + r) * K + 32 * kc + 8 * q;
+            for (int i = 0; i < 8; ++i) word |= (uint32_t)(((int)src[i] + off) & 15) << (4 * i);
           } else {
-            const int8_t* src = Q + (size_t)(DR * rt + 16 * (j >> 1) + r) * K + 32 * kc + 8 * q + 4 * (j & 1);
+            const C* src = Q + (size_t)(DR * rt + 16 * (j >> 1) + r) * K + 32 * kc + 8 * q + 4 * (j & 1);
             for (int i = 0; i < 4; ++i) word |= (uint32_t)(uint8_t)src[i] << (8 * i);
           }
           memcpy(tile + lane * 16 + 4 * j, &word, 4);
@@ -168,6 +171,36 @@ void pack_slab_scales(const float* S, int N, int K, int group, int bits, float* 
       for (int r = 0; r < 16; ++r)
         for (int j = 0; j < ns; ++j)
           out[(((size_t)g * nrt + rt) * 16 + r) * ns + j] = S[(size_t)(DR * rt + 16 * j + r) * ng + g];
+}
+
+// One two-level record (row r, super-block b) of a matrix with K columns:
+// word 0 = d | dmin << 16; word 1 = the low nibbles of sc_0..7 (nibble j),
+// word 2 = those of m_0..7, word 3 = the high 2 bits of sc_j at bit 2j and of
+// m_j at bit 16 + 2j.  Sub-blocks past the end of the row stay zero.
+void q4k_record(const moe_q4k_matrix_t& M, int K, int r, int b, uint8_t* out) {
+  const int nsb = q4k_superblocks(K), nsub = K / Q4K_SUB;
+  uint32_t w[4] = {(uint32_t)M.d[(size_t)r * nsb + b] | ((uint32_t)M.dmin[(size_t)r * nsb + b] << 16), 0u, 0u, 0u};
+  for (int j = 0; j < Q4K_SB / Q4K_SUB; ++j) {
+    const int g = b * (Q4K_SB / Q4K_SUB) + j;
+    if (g >= nsub) break;
+    const uint32_t sc = M.sc[(size_t)r * nsub + g], m = M.m[(size_t)r * nsub + g];
+    w[1] |= (sc & 15u) << (4 * j);
+    w[2] |= (m & 15u) << (4 * j);
+    w[3] |= ((sc >> 4) << (2 * j)) | ((m >> 4) << (16 + 2 * j));
+  }
+  memcpy(out, w, sizeof(w));
+}
+
+// every field in range: codes <= 15, sc and m <= 63, d and dmin finite f16
+bool q4k_fields_ok(const moe_q4k_matrix_t& M, int N, int K) {
+  if (!M.q || !M.d || !M.dmin || !M.sc || !M.m) return false;
+  for (size_t i = 0; i < (size_t)N * K; ++i)
+    if (M.q[i] > 15) return false;
+  for (size_t i = 0; i < (size_t)N * (K / Q4K_SUB); ++i)
+    if (M.sc[i] > 63 || M.m[i] > 63) return false;
+  for (size_t i = 0; i < (size_t)N * q4k_superblocks(K); ++i)
+    if ((M.d[i] & 0x7C00u) == 0x7C00u || (M.dmin[i] & 0x7C00u) == 0x7C00u) return false;
+  return true;
 }
 
 bool codes_in_range(const int8_t* Q, size_t n, int bits) {
@@ -201,8 +234,35 @@ size_t moe_expert_code_bytes(int32_t bits, int32_t inter) {
 }
 
 size_t moe_expert_scale_count(int32_t group_size, int32_t inter) {
-  if (group_size != 32 && group_size != 64 && group_size != 128) return 0;
-  return 3 * (size_t)inter * H / group_size;
+  if (group_size != 32 && group_size != 64 && group_size != 128 && group_size != Q4K) return 0;
+  return scale_words(group_size, inter);
+}
+
+moe_status_t moe_pack_expert_q4k(const moe_q4k_matrix_t* gate, const moe_q4k_matrix_t* up,
+                                 const moe_q4k_matrix_t* down, int32_t inter, void* codes_out, void* meta_out) {
+  if (!gate || !up || !down || !codes_out || !meta_out) return MOE_E_NULLPTR;
+  if (inter != I && inter != IS) return MOE_E_SHAPE;
+  if (!gate->q || !gate->d || !gate->dmin || !gate->sc || !gate->m || !up->q || !up->d || !up->dmin || !up->sc ||
+      !up->m || !down->q || !down->d || !down->dmin || !down->sc || !down->m)
+    return MOE_E_NULLPTR;
+  if (!q4k_fields_ok(*gate, inter, H) || !q4k_fields_ok(*up, inter, H) || !q4k_fields_ok(*down, H, inter))
+    return MOE_E_FORMAT;
+  uint8_t* out = (uint8_t*)codes_out;
+  const size_t mb = matrix_bytes(4, inter, H);
+  pack_rows(gate->q, inter, H, 4, out, -8);
+  pack_rows(up->q, inter, H, 4, out + mb, -8);
+  pack_slabs(down->q, H, inter, 4, out + 2 * mb, -8);
+  uint8_t* meta = (uint8_t*)meta_out;
+  const int nsb = q4k_superblocks(H);
+  for (int r = 0; r < inter; ++r)
+    for (int b = 0; b < nsb; ++b) {
+      q4k_record(*gate, H, r, b, meta + ((size_t)r * nsb + b) * Q4K_REC);
+      q4k_record(*up, H, r, b, meta + ((size_t)(inter + r) * nsb + b) * Q4K_REC);
+    }
+  uint8_t* dmeta = meta + 2 * (size_t)inter * nsb * Q4K_REC;
+  for (int b = 0; b < q4k_superblocks(inter); ++b)
+    for (int r = 0; r < H; ++r) q4k_record(*down, inter, r, b, dmeta + ((size_t)b * H + r) * Q4K_REC);
+  return MOE_OK;
 }
 
 moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t* down,
@@ -212,7 +272,7 @@ moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t*
   if (!gate || !up || !down || !gate_scales || !up_scales || !down_scales || !codes_out || !scales_out)
     return MOE_E_NULLPTR;
   if (inter != I && inter != IS) return MOE_E_SHAPE;
-  if (!fmt_ok(bits, group_size)) return MOE_E_FORMAT;
+  if (!fmt_ok(bits, group_size) || group_size == Q4K) return MOE_E_FORMAT;
   const size_t n = (size_t)inter * H;
   if (!codes_in_range(gate, n, bits) || !codes_in_range(up, n, bits) || !codes_in_range(down, n, bits))
     return MOE_E_FORMAT;
@@ -253,6 +313,9 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   if ((flags & ~known) || (x_dtype != MOE_F32 && x_dtype != MOE_BF16)) return MOE_E_ARG;
   if ((flags & MOE_FORCE_DECODE) && (flags & MOE_FORCE_GROUPED)) return MOE_E_ARG;
   if ((flags & MOE_FORCE_DECODE) && T > DECODE_FORCE_MAX_T) return MOE_E_SHAPE;
+  // the two-level format runs on the per-token path only
+  const bool two_level = expert_group == Q4K || shared_group == Q4K;
+  if (two_level && ((flags & MOE_FORCE_GROUPED) || T > DECODE_FORCE_MAX_T)) return MOE_E_FORMAT;
   if ((flags & MOE_NORM_BF16) && !(flags & MOE_NORM_INPUT)) return MOE_E_ARG;
   if ((flags & MOE_NORM_INPUT) && x_dtype != MOE_F32) return MOE_E_ARG;
   if (x && x == (const void*)y && !((flags & MOE_ACCUMULATE) && x_dtype == MOE_F32)) return MOE_E_ARG;
@@ -285,7 +348,7 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   const QW sw = make_qw(shared_q, shared_scales, shared_bits, shared_group, IS, false);
   const int accumulate = (flags & MOE_ACCUMULATE) != 0;
 
-  const bool decode = (flags & MOE_FORCE_DECODE) || (!(flags & MOE_FORCE_GROUPED) && T <= DECODE_MAX_T);
+  const bool decode = two_level || (flags & MOE_FORCE_DECODE) || (!(flags & MOE_FORCE_GROUPED) && T <= DECODE_MAX_T);
   if (decode) {
     DecItemsArgs d;
     d.xf = xf; d.xb = xb; d.ids = topk_ids; d.tw = topk_w; d.rw = rw; d.sw = sw; d.part = ws.part;

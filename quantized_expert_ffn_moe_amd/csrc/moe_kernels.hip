@@ -12,7 +12,11 @@
 //    with 16-byte loads per lane.  The input is written in block floating
 //    point as three int8 digit planes, and the int8 matrix cores
 //    (v_mfma_i32_16x16x64_i8) multiply them with the codes exactly; the group
-//    scale multiplies the exact integer partial sum of its group.
+//    scale multiplies the exact integer partial sum of its group.  The
+//    two-level 4-bit format (Q4_K-style, GEMV path only) runs on the int4
+//    tiles of q - 8: W = d sc q - dmin m = s (q - 8) + beta with s = d sc and
+//    beta = 8 s - dmin m, so each sub-block adds beta times the sum of its
+//    inputs to the scaled integer product.
 //  * Grouped path (many tokens): tokens are bucketed per expert (histogram +
 //    stable permutation) and each expert's bucket runs as a dense GEMM on the
 //    MFMA units (v_mfma_f32_16x16x32_f16).  The codes become exact f16 integers
@@ -384,11 +388,13 @@ __device__ __forceinline__ int digit_pos(int i) {
 // one wave) share an exponent.  xa: [unit k / 64][plane 0..3][q][4 words] (the
 // unused plane 3 is never written: it only feeds C rows that are not read);
 // xs[block] = 2^(e - XF) (2^(e - XF - 4) for int4: the 16x codes).
-template <int BITS>
+// With SUMS (blocks of 32 only), xsum[block] = the f32 sum of the block's
+// elements of x * mul (the two-level format's minimum term).
+template <int BITS, bool SUMS = false>
 __device__ __forceinline__ void x_digits(const float* x, float mul, int kg, int blk, uint32_t* xa, float* xs,
-                                         bool active) {
+                                         bool active, float* xsum = nullptr) {
   float v[8];
-  float amax = 0.f;
+  float amax = 0.f, vsum = 0.f;
   if (active) {
     *(float4*)&v[0] = *(const float4*)&x[8 * kg];
     *(float4*)&v[4] = *(const float4*)&x[8 * kg + 4];
@@ -397,12 +403,15 @@ __device__ __forceinline__ void x_digits(const float* x, float mul, int kg, int 
       v[i] *= mul;
       amax = fmaxf(amax, fabsf(v[i]));
     }
+    if (SUMS) vsum = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
   }
   amax = blk >= 128 ? group_max<16>(amax) : blk >= 64 ? group_max<8>(amax) : group_max<4>(amax);
+  if (SUMS) vsum = group_sum<4>(vsum);
   if (!active) return;
   int e;
   frexpf(amax, &e);                       // amax < 2^e (e = 0 when the block is zero)
   if ((kg & (blk / 8 - 1)) == 0) xs[(8 * kg) / blk] = ldexpf(1.0f, e - XF - (BITS == 4 ? 4 : 0));
+  if (SUMS && (kg & 3) == 0) xsum[kg / 4] = vsum;
   uint32_t M[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) M[i] = (uint32_t)((int)rintf(ldexpf(v[i], XF - e)) + (int)XOFF);
@@ -442,15 +451,36 @@ __device__ __forceinline__ uint4 wload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 
 template <int BITS, int G>
 struct ItemRegs {
+  static constexpr bool K4 = G == Q4K;     // two-level format (4-bit codes, 32-column sub-blocks)
+  static_assert(!K4 || BITS == 4, "the two-level format has 4-bit codes");
+  static constexpr int SG = K4 ? Q4K_SUB : G;   // columns per scale
   static constexpr int KB = kb_cols(BITS), NKB = H / KB, CPT = KB / 32;
   static constexpr int GU_TPW = NKB / 2;   // wave w: n-tile w/2 (gate 2J, gate 2J+1, up 2J, up 2J+1), K half w%2
-  static constexpr int NGW = (H / 2) / G;  // scale groups in a K half
+  static constexpr int NGW = (H / 2) / SG; // scale groups in a K half
+  static constexpr int NSB = H / Q4K_SB;   // two-level: super-blocks of a gate/up row (5)
+  static constexpr int NREC = 3;           // ... that a K half touches (640 columns from 0 or 640)
   static constexpr int DR = down_rows(BITS), NRT = H / DR, D_TPW = (NRT + 7) / 8, RS = DR / 16;
   uint4 gu[GU_TPW];
-  float gsc[NGW];
+  float gsc[K4 ? 1 : NGW];
+  u32x4 gm[K4 ? NREC : 1];                 // two-level: this lane's row, the K half's super-blocks
   uint4 dn[D_TPW];
-  float dns[D_TPW][RS];
+  float dns[D_TPW][K4 ? 1 : RS];
+  u32x4 dm[K4 ? D_TPW : 1];               // two-level: lane (r, q) holds the record of down row DR rt + 16 q + r
 };
+
+// Sub-block j (0..7) of a two-level record: word 0 = d | dmin << 16 (f16);
+// word 1 = the low 4 bits of sc_0..sc_7 (nibble j), word 2 = those of
+// m_0..m_7, word 3 = the high 2 bits of sc_j at bit 2j and of m_j at bit
+// 16 + 2j.  Returns s = d sc_j and beta = 8 s - dmin m_j (one rounding).
+__device__ __forceinline__ float f16_bits_value(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+__device__ __forceinline__ void q4k_sub(const u32x4& r, int j, float& s, float& beta) {
+  const uint32_t sc = ((r[1] >> (4 * j)) & 15u) | (((r[3] >> (2 * j)) & 3u) << 4);
+  const uint32_t m = ((r[2] >> (4 * j)) & 15u) | (((r[3] >> (16 + 2 * j)) & 3u) << 4);
+  s = f16_bits_value(r[0] & 0xFFFFu) * (float)sc;
+  beta = fmaf(-f16_bits_value(r[0] >> 16), (float)m, 8.0f * s);
+}
 
 // A pointer or index the whole wave agrees on, as a scalar value (lets buffer
 // descriptors live in scalar registers).
@@ -483,6 +513,15 @@ __device__ __forceinline__ void item_load(ItemRegs<BITS, G>& R, const uint8_t* e
   // gate/up scales are row-major [row][group]: this lane's row, this wave's K half
   // (buffer loads throughout: a pending flat load would make the compiler wait
   // for every outstanding load before the first use of any of them)
+  if constexpr (IR::K4) {
+    // two-level records [mat][row][5]: this lane's row, super-blocks 2h .. 2h + 2 of K half h
+    const uint8_t* gmb = (const uint8_t*)es + (size_t)mat * inter * IR::NSB * Q4K_REC;
+    const __amdgpu_buffer_rsrc_t rgm = weight_rsrc(
+        gmb + ((size_t)(16 * ntile) * IR::NSB + 2 * (wv & 1)) * Q4K_REC, 16 * IR::NSB * Q4K_REC);
+    const uint32_t mo = (uint32_t)(r * IR::NSB) * Q4K_REC;
+#pragma unroll
+    for (int k = 0; k < IR::NREC; ++k) R.gm[k] = __builtin_amdgcn_raw_buffer_load_b128(rgm, mo + k * Q4K_REC, 0, 0);
+  } else {
   const __amdgpu_buffer_rsrc_t rgs =
       weight_rsrc(es + mat * mscales + (size_t)(16 * ntile) * NG + (wv & 1) * IR::NGW, 16 * NG * 4);
   const uint32_t go = (uint32_t)(r * NG) * 4;
@@ -504,14 +543,30 @@ __device__ __forceinline__ void item_load(ItemRegs<BITS, G>& R, const uint8_t* e
 #pragma unroll
     for (int g = 0; g < IR::NGW; ++g) R.gsc[g] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rgs, go + 4 * g, 0, 0));
   }
+  }
   const __amdgpu_buffer_rsrc_t rg =
       weight_rsrc(eq + mat * mbytes + ((size_t)ntile * IR::NKB + kb0) * TILE, IR::GU_TPW * TILE);
 #pragma unroll
   for (int m = 0; m < IR::GU_TPW; ++m) R.gu[m] = wload16(rg, m * TILE + lane * 16);
+  const __amdgpu_buffer_rsrc_t rd = weight_rsrc(eq + 2 * mbytes + (size_t)J * IR::NRT * TILE, IR::NRT * TILE);
+  if constexpr (IR::K4) {
+    // two-level down records [super-block][row]: the slice's super-block;
+    // lane (r, q) takes row DR rt + 16 q + r of each tile (rows past the end
+    // read as zeros), the 4 lane groups sharing out a tile's 4 rows per r
+    const __amdgpu_buffer_rsrc_t rdm = weight_rsrc((const uint8_t*)es + 2 * (size_t)inter * IR::NSB * Q4K_REC +
+                                                       (size_t)(J / (Q4K_SB / SLICE)) * H * Q4K_REC,
+                                                   H * Q4K_REC);
+#pragma unroll
+    for (int m = 0; m < IR::D_TPW; ++m) {
+      const uint32_t rt = wv + 8 * m;
+      R.dm[m] = __builtin_amdgcn_raw_buffer_load_b128(rdm, (rt * IR::DR + 16 * (lane >> 4) + r) * Q4K_REC, 0, 0);
+      R.dn[m] = wload16(rd, rt * TILE + lane * 16);
+    }
+    return;
+  }
   const int gd = (SLICE * J) / G;
   const __amdgpu_buffer_rsrc_t rds =
       weight_rsrc(es + 2 * mscales + (size_t)gd * IR::NRT * 16 * IR::RS, IR::NRT * 16 * IR::RS * 4);
-  const __amdgpu_buffer_rsrc_t rd = weight_rsrc(eq + 2 * mbytes + (size_t)J * IR::NRT * TILE, IR::NRT * TILE);
 #pragma unroll
   for (int m = 0; m < IR::D_TPW; ++m) {
     const uint32_t rt = wv + 8 * m;
@@ -551,13 +606,14 @@ struct ItemLds {
   uint32_t ha[8][4 * 4 * 2];           // per wave: A-operand digits of h: [plane][q][2]
   float hs;                            // unit of the h digits (times 2^-4 for int4 codes)
   float dout[H];                       // down rows of the item in units of hs
+  float xsum[H / 32];                  // two-level format: per-32-block sums of the input
 };
 
 // Digits of the layer input z (in LDS) for weights of format (BITS, G).
 template <int BITS, int G>
 __device__ __forceinline__ void item_planes(const float* z, float mul, ItemLds& L) {
   const int tid = threadIdx.x;
-  x_digits<BITS>(z, mul, tid, G, L.xa, L.xs, tid < H / 8);
+  x_digits<BITS, G == Q4K>(z, mul, tid, G == Q4K ? Q4K_SUB : G, L.xa, L.xs, tid < H / 8, L.xsum);
   __syncthreads();
 }
 
@@ -584,8 +640,35 @@ __device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint3
 // x32 products), every wave forms h = SiLU(g) * u and its digits, then each wave
 // takes its down tiles (x32 products over the 32-column slice).  Ends with a
 // workgroup barrier.
+// Gate/up sums of a two-level item over K half HH (lanes 0..15 hold rows):
+// per 32-column sub-block, s times the scaled integer product plus beta times
+// the sum of the sub-block's inputs.
+template <int HH>
+__device__ __forceinline__ float q4k_gateup(const ItemRegs<4, Q4K>& R, const ItemLds& L, int pl, int q) {
+  using IR = ItemRegs<4, Q4K>;
+  constexpr int NU = IR::GU_TPW * 2;            // x64 units in a K half
+  constexpr int u0 = HH * NU;
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const uint4 a4 = *(const uint4*)&L.xa[(((u0 + u) * 4 + pl) * 4 + q) * 4];
+    const i32x4 B = unit_b<4>(R.gu[u / 2], u % 2);
+    const i32x4 c[2] = {mfma_x32(pack64(a4.x, a4.y), pack64((uint32_t)B[0], (uint32_t)B[1])),
+                        mfma_x32(pack64(a4.z, a4.w), pack64((uint32_t)B[2], (uint32_t)B[3]))};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int gg = IR::NGW * HH + 2 * u + t;    // sub-block of the row (0..39)
+      float s, beta;
+      q4k_sub(R.gm[gg / 8 - 2 * HH], gg % 8, s, beta);
+      acc = fmaf(s * L.xs[gg], digits_value(c[t]), acc);
+      acc = fmaf(beta, L.xsum[gg], acc);
+    }
+  }
+  return acc;
+}
+
 template <int BITS, int G>
-__device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds& L) {
+__device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds& L, int J) {
   using IR = ItemRegs<BITS, G>;
   constexpr int UPT = BITS == 4 ? 2 : 1;          // x64 units per tile
   constexpr int NU = IR::GU_TPW * UPT;            // units in a K half
@@ -595,6 +678,9 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds
   const i32x4 zero = {0, 0, 0, 0};
   float acc = 0.f;
   i32x4 C = zero;
+  if constexpr (IR::K4) {
+    acc = (wv & 1) ? q4k_gateup<1>(R, L, pl, q) : q4k_gateup<0>(R, L, pl, q);
+  } else {
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     const uint32_t* ap = &L.xa[(((u0 + u) * 4 + pl) * 4 + q) * 4];
@@ -613,12 +699,14 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds
       acc = fmaf(R.gsc[2 * u + 1] * L.xs[2 * u0 + 2 * u + 1], digits_value(c1), acc);
     }
   }
+  }
   if (lane < 16) L.gpart[wv][lane] = acc;
   __syncthreads();
   // every wave: h for the 32 slice columns and its digits, into its own copy
   // of the A operand (identical arithmetic in every wave; a wave reads back its
   // own LDS writes in order, so no workgroup barrier is needed)
   uint64_t Ah;
+  float xh = 0.f;
   {
     float hv = 0.f;
     if (lane < SLICE) {
@@ -631,6 +719,9 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds
     int e;
     frexpf(amax, &e);
     if (tid == 0) L.hs = ldexpf(1.0f, e - XF - (BITS == 4 ? 4 : 0));
+    // two-level format: the slice's inputs summed in units of L.hs (16 x the
+    // integer mantissas: the unit carries the 2^-4 of the 4-bit codes)
+    if (IR::K4) xh = 16.0f * wave_sum(rintf(ldexpf(hv, XF - e)));
     uint8_t* hb = (uint8_t*)L.ha[wv];
     if (lane < SLICE) {
       const uint32_t M = (uint32_t)((int)rintf(ldexpf(hv, XF - e)) + (int)XOFF);
@@ -642,15 +733,26 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds
   }
   // all products first, then the recombination (lanes 0..15 hold the rows);
   // the last tile of waves with one tile fewer is all zeros (range-checked loads)
+  static_assert(!IR::K4 || IR::RS == 4, "one down record per lane group");
   float dv[IR::D_TPW][IR::RS];
 #pragma unroll
-  for (int m = 0; m < IR::D_TPW; ++m)
+  for (int m = 0; m < IR::D_TPW; ++m) {
+    float s_own = 0.f, beta_own = 0.f;   // two-level: s and beta of this lane's record
+    if constexpr (IR::K4) q4k_sub(R.dm[m], J % (Q4K_SB / SLICE), s_own, beta_own);
 #pragma unroll
     for (int j = 0; j < IR::RS; ++j) {
       const uint64_t Bd = BITS == 4 ? pack64(even_codes(word_of(R.dn[m], j)), odd_codes(word_of(R.dn[m], j)))
                                     : pack64(word_of(R.dn[m], 2 * j), word_of(R.dn[m], 2 * j + 1));
-      dv[m][j] = R.dns[m][j] * digits_value(mfma_x32(Ah, Bd));
+      if constexpr (IR::K4) {
+        // row DR rt + 16 j + r: its record sits in lane r + 16 j
+        const int src = (lane & 15) + 16 * j;
+        const float s = __shfl(s_own, src), beta = __shfl(beta_own, src);
+        dv[m][j] = fmaf(s, digits_value(mfma_x32(Ah, Bd)), beta * xh);
+      } else {
+        dv[m][j] = R.dns[m][j] * digits_value(mfma_x32(Ah, Bd));
+      }
     }
+  }
   if (lane < 16) {
 #pragma unroll
     for (int m = 0; m < IR::D_TPW; ++m) {
@@ -675,14 +777,18 @@ __device__ __forceinline__ void run_item(const uint8_t* eq, const float* es, int
   ItemRegs<BITS, G> R;
   item_load<BITS, G>(R, eq, es, inter, J, tid >> 6, tid & 63);
   item_planes<BITS, G>(z, 1.0f, L);
-  item_compute<BITS, G>(R, L);
+  item_compute<BITS, G>(R, L, J);
   const float cs = coef * L.hs;
   for (int row = tid; row < H; row += 512) out[row] = item_row(L, cs, row);
 }
 
-template <int BITS>
+template <int BITS, bool K4>
 __device__ __forceinline__ void run_item_g(int group, const uint8_t* eq, const float* es, int inter, int J,
                                            const float* z, float coef, float* out, ItemLds& L) {
+  if constexpr (K4) {
+    run_item<4, Q4K>(eq, es, inter, J, z, coef, out, L);
+    return;
+  }
   switch (group) {
     case 32: run_item<BITS, 32>(eq, es, inter, J, z, coef, out, L); break;
     case 64: run_item<BITS, 64>(eq, es, inter, J, z, coef, out, L); break;
@@ -691,7 +797,9 @@ __device__ __forceinline__ void run_item_g(int group, const uint8_t* eq, const f
 }
 
 // Decode path of moe_layer_forward: one workgroup per (token, item).
-template <int BR, int BS>
+// QK: bit 0 = routed experts in the two-level format, bit 1 = shared expert
+// (separate instantiations keep the symmetric kernels' registers as they were)
+template <int BR, int BS, int QK>
 __global__ __launch_bounds__(512) void dec_items_kernel(DecItemsArgs a) {
   __shared__ __attribute__((aligned(16))) float z[H];
   __shared__ __attribute__((aligned(16))) ItemLds L;
@@ -703,10 +811,10 @@ __global__ __launch_bounds__(512) void dec_items_kernel(DecItemsArgs a) {
   if (item < R_ITEMS) {
     const int p = item / (I / SLICE), J = item % (I / SLICE);
     const int e = a.ids[(size_t)t * TOPK + p];
-    run_item_g<BR>(a.rw.group, a.rw.q + (size_t)e * a.rw.e_bytes, a.rw.s + (size_t)e * a.rw.e_scales, I, J, z,
+    run_item_g<BR, (QK & 1) != 0>(a.rw.group, a.rw.q + (size_t)e * a.rw.e_bytes, a.rw.s + (size_t)e * a.rw.e_scales, I, J, z,
                           a.tw[(size_t)t * TOPK + p], out, L);
   } else {
-    run_item_g<BS>(a.sw.group, a.sw.q, a.sw.s, IS, item - R_ITEMS, z, 1.0f, out, L);
+    run_item_g<BS, (QK & 2) != 0>(a.sw.group, a.sw.q, a.sw.s, IS, item - R_ITEMS, z, 1.0f, out, L);
   }
 }
 
@@ -939,7 +1047,7 @@ template <int BR, int GR>
 __device__ void chain_routed(const ChainArgs& a, const LayerPtrs* LP, ItemSide& S, int b, uint32_t base, uint32_t* err) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int p = b / (I / SLICE), J = b % (I / SLICE);
-  const size_t ebytes = 3 * matrix_bytes(BR, I, H), escales = 3 * (size_t)I * H / GR;
+  const size_t ebytes = 3 * matrix_bytes(BR, I, H), escales = scale_words(GR, I);
   for (int l = 0; l < a.n_layers; ++l) {
     MOE_TRACE(a, b, l, 0);
     const float inv = chain_layer_input(a, LP, S, l, base + l + 1, true, b == 0, err);
@@ -955,7 +1063,7 @@ __device__ void chain_routed(const ChainArgs& a, const LayerPtrs* LP, ItemSide& 
     }
     item_planes<BR, GR>(S.z, inv, S.item);
     MOE_TRACE(a, b, l, 13);
-    item_compute<BR, GR>(R, S.item);
+    item_compute<BR, GR>(R, S.item, J);
     MOE_TRACE(a, b, l, 4);
     chain_item_store(a, S.item, coef * S.item.hs, b, base + l + 1);
     MOE_TRACE(a, b, l, 5);
@@ -984,7 +1092,7 @@ __device__ void chain_shared(const ChainArgs& a, const LayerPtrs* LP, ItemSide& 
     MOE_TRACE(a, b, l, 2);
     item_planes<BS, GS>(S.z, inv, S.item);
     MOE_TRACE(a, b, l, 13);
-    item_compute<BS, GS>(R, S.item);
+    item_compute<BS, GS>(R, S.item, J);
     MOE_TRACE(a, b, l, 4);
     chain_item_store(a, S.item, S.item.hs, b, base + l + 1);
     MOE_TRACE(a, b, l, 5);
@@ -1081,7 +1189,7 @@ __device__ void chain_reducer(const ChainArgs& a, const LayerPtrs* LP, ReducerSi
   }
 }
 
-template <int BR, int BS>
+template <int BR, int BS, int QK>   // QK as for dec_items_kernel
 __global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
   __shared__ __attribute__((aligned(16))) ChainLds S;
   // the per-layer pointer table, read once from the kernel arguments
@@ -1095,16 +1203,24 @@ __global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
   const uint32_t base = load_coherent_u32(a.hdr);   // this call's stage tags are base + 1 .. base + n_layers
   uint32_t* err = a.hdr + 2;
   if (b < R_ITEMS) {
-    switch (a.rgroup) {
-      case 32: chain_routed<BR, 32>(a, LP, S.it, b, base, err); break;
-      case 64: chain_routed<BR, 64>(a, LP, S.it, b, base, err); break;
-      default: chain_routed<BR, 128>(a, LP, S.it, b, base, err); break;
+    if constexpr ((QK & 1) != 0) {
+      chain_routed<4, Q4K>(a, LP, S.it, b, base, err);
+    } else {
+      switch (a.rgroup) {
+        case 32: chain_routed<BR, 32>(a, LP, S.it, b, base, err); break;
+        case 64: chain_routed<BR, 64>(a, LP, S.it, b, base, err); break;
+        default: chain_routed<BR, 128>(a, LP, S.it, b, base, err); break;
+      }
     }
   } else if (b < N_ITEMS) {
-    switch (a.sgroup) {
-      case 32: chain_shared<BS, 32>(a, LP, S.it, b, base, err); break;
-      case 64: chain_shared<BS, 64>(a, LP, S.it, b, base, err); break;
-      default: chain_shared<BS, 128>(a, LP, S.it, b, base, err); break;
+    if constexpr ((QK & 2) != 0) {
+      chain_shared<4, Q4K>(a, LP, S.it, b, base, err);
+    } else {
+      switch (a.sgroup) {
+        case 32: chain_shared<BS, 32>(a, LP, S.it, b, base, err); break;
+        case 64: chain_shared<BS, 64>(a, LP, S.it, b, base, err); break;
+        default: chain_shared<BS, 128>(a, LP, S.it, b, base, err); break;
+      }
     }
   } else {
     chain_reducer(a, LP, S.rd, b - N_ITEMS, base, err);
@@ -2290,12 +2406,19 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
 
 hipError_t launch_dec_items(const DecItemsArgs& a, int T, hipStream_t s) {
   const dim3 grid(T * N_ITEMS);
-  const int key = (a.rw.bits == 8) * 2 + (a.sw.bits == 8);
+  const int qk = (a.rw.group == Q4K) + 2 * (a.sw.group == Q4K);
+  const int key = (a.rw.bits == 8) * 2 + (a.sw.bits == 8) + 4 * qk;
   switch (key) {
-    case 0: hipLaunchKernelGGL((dec_items_kernel<4, 4>), grid, dim3(512), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((dec_items_kernel<4, 8>), grid, dim3(512), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dec_items_kernel<8, 4>), grid, dim3(512), 0, s, a); break;
-    default: hipLaunchKernelGGL((dec_items_kernel<8, 8>), grid, dim3(512), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((dec_items_kernel<4, 4, 0>), grid, dim3(512), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dec_items_kernel<4, 8, 0>), grid, dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dec_items_kernel<8, 4, 0>), grid, dim3(512), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((dec_items_kernel<8, 8, 0>), grid, dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((dec_items_kernel<4, 4, 1>), grid, dim3(512), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((dec_items_kernel<4, 8, 1>), grid, dim3(512), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((dec_items_kernel<4, 4, 2>), grid, dim3(512), 0, s, a); break;
+    case 10: hipLaunchKernelGGL((dec_items_kernel<8, 4, 2>), grid, dim3(512), 0, s, a); break;
+    case 12: hipLaunchKernelGGL((dec_items_kernel<4, 4, 3>), grid, dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;   // the two-level format has 4-bit codes
   }
   return hipGetLastError();
 }
@@ -2314,12 +2437,19 @@ hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s) {
 // kernels occupying CUs) ends in the workspace error word, not in a hang.
 hipError_t launch_chain(const ChainArgs& a, hipStream_t s) {
   const void* fn;
-  const int key = (a.rbits == 8) * 2 + (a.sbits == 8);
+  const int qk = (a.rgroup == Q4K) + 2 * (a.sgroup == Q4K);
+  const int key = (a.rbits == 8) * 2 + (a.sbits == 8) + 4 * qk;
   switch (key) {
-    case 0: fn = (const void*)chain_kernel<4, 4>; break;
-    case 1: fn = (const void*)chain_kernel<4, 8>; break;
-    case 2: fn = (const void*)chain_kernel<8, 4>; break;
-    default: fn = (const void*)chain_kernel<8, 8>; break;
+    case 0: fn = (const void*)chain_kernel<4, 4, 0>; break;
+    case 1: fn = (const void*)chain_kernel<4, 8, 0>; break;
+    case 2: fn = (const void*)chain_kernel<8, 4, 0>; break;
+    case 3: fn = (const void*)chain_kernel<8, 8, 0>; break;
+    case 4: fn = (const void*)chain_kernel<4, 4, 1>; break;
+    case 5: fn = (const void*)chain_kernel<4, 8, 1>; break;
+    case 8: fn = (const void*)chain_kernel<4, 4, 2>; break;
+    case 10: fn = (const void*)chain_kernel<8, 4, 2>; break;
+    case 12: fn = (const void*)chain_kernel<4, 4, 3>; break;
+    default: return hipErrorInvalidValue;   // the two-level format has 4-bit codes
   }
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);

@@ -119,6 +119,73 @@ def test_pack_rejects_bad_codes_and_formats(lib):
     assert B.moe_expert_code_bytes(5, 896) == 0 and B.moe_expert_scale_count(16, 896) == 0
 
 
+def _q4k_matrix(rng, N, K):
+    return {"q": rng.integers(0, 16, (N, K)).astype(np.uint8),
+            "d": rng.uniform(1e-4, 1e-2, (N, -(-K // 256))).astype(np.float16).view(np.uint16),
+            "dmin": rng.uniform(1e-4, 1e-2, (N, -(-K // 256))).astype(np.float16).view(np.uint16),
+            "sc": rng.integers(0, 64, (N, K // 32)).astype(np.uint8),
+            "m": rng.integers(0, 64, (N, K // 32)).astype(np.uint8)}
+
+
+def _record_fields(w):
+    """(d bits, dmin bits, sc[8], m[8]) of one 16-byte record, decoded from the
+    layout in include/moe.h (independent of the packer)."""
+    w = [int(v) for v in w]
+    sc = [((w[1] >> (4 * j)) & 15) | (((w[3] >> (2 * j)) & 3) << 4) for j in range(8)]
+    m = [((w[2] >> (4 * j)) & 15) | (((w[3] >> (16 + 2 * j)) & 3) << 4) for j in range(8)]
+    return w[0] & 0xFFFF, w[0] >> 16, sc, m
+
+
+@pytest.mark.parametrize("inter", [896, 1792])
+def test_pack_q4k_layout(lib, inter):
+    rng = np.random.default_rng(inter)
+    g, u, d = _q4k_matrix(rng, inter, 1280), _q4k_matrix(rng, inter, 1280), _q4k_matrix(rng, 1280, inter)
+    codes, meta = B.moe_pack_expert_q4k(g, u, d)
+    mb = inter * 1280 // 2
+    assert codes.size == 3 * mb
+    nsbd = -(-inter // 256)
+    assert meta.size * 4 == 16 * (2 * inter * 5 + nsbd * 1280) == 4 * B.moe_expert_scale_count(B.MOE_Q4K, inter)
+    # codes: the int4 tiles of q - 8
+    np.testing.assert_array_equal(_unpack_rows(codes[:mb][: 16 * 1280], 32, 1280, 4), g["q"][:32].astype(int) - 8)
+    np.testing.assert_array_equal(_unpack_rows(codes[mb:2 * mb][: 8 * 1280], 16, 1280, 4), u["q"][:16].astype(int) - 8)
+    np.testing.assert_array_equal(_unpack_slabs(codes[2 * mb:], inter, 4, 2), d["q"][:, :64].astype(int) - 8)
+    rec = meta.view(np.uint32).reshape(-1, 4)
+    for mat, base in ((g, 0), (u, inter * 5)):
+        for r in (0, 7, inter - 1):
+            for b in range(5):
+                db, dmb, sc, m = _record_fields(rec[base + r * 5 + b])
+                assert (db, dmb) == (mat["d"][r, b], mat["dmin"][r, b])
+                assert sc == mat["sc"][r, 8 * b:8 * b + 8].tolist() and m == mat["m"][r, 8 * b:8 * b + 8].tolist()
+    base = 2 * inter * 5
+    for b in range(nsbd):
+        for r in (0, 641, 1279):
+            db, dmb, sc, m = _record_fields(rec[base + b * 1280 + r])
+            n = min(8, inter // 32 - 8 * b)                  # the routed row ends in a half super-block
+            assert (db, dmb) == (d["d"][r, b], d["dmin"][r, b])
+            assert sc[:n] == d["sc"][r, 8 * b:8 * b + n].tolist() and m[:n] == d["m"][r, 8 * b:8 * b + n].tolist()
+            assert sc[n:] == [0] * (8 - n) and m[n:] == [0] * (8 - n)
+
+
+def test_pack_q4k_rejects_bad_fields(lib):
+    rng = np.random.default_rng(0)
+    mats = [_q4k_matrix(rng, 896, 1280), _q4k_matrix(rng, 896, 1280), _q4k_matrix(rng, 1280, 896)]
+    for key, idx, val in (("q", (3, 9), 16), ("sc", (5, 2), 64), ("m", (0, 0), 200), ("d", (1, 1), 0x7C00),
+                          ("dmin", (2, 3), 0xFE00)):
+        bad = [dict(x) for x in mats]
+        bad[2] = {k: v.copy() for k, v in mats[2].items()}
+        bad[2][key][idx] = val
+        with pytest.raises(B.MoeError, match="FORMAT"):
+            B.moe_pack_expert_q4k(*bad)
+    q = B.Q4kMatrix(None, None, None, None, None)
+    assert lib.moe_pack_expert_q4k(ctypes.byref(q), ctypes.byref(q), ctypes.byref(q), 896, 0x100, 0x100) == 1
+    assert lib.moe_pack_expert_q4k(ctypes.byref(q), ctypes.byref(q), ctypes.byref(q), 100, 0x100, 0x100) == 2
+    # the symmetric packer does not take the two-level group
+    lay = make_tiny_layer(1, E=1, H=1280, I=896, Is=896, fmt=QFmt(4, 32))
+    with pytest.raises(B.MoeError, match="FORMAT"):
+        B.moe_pack_expert(lay["gate_q"][0], lay["up_q"][0], lay["down_q"][0], lay["gate_s"][0], lay["up_s"][0],
+                          lay["down_s"][0], 4, B.MOE_Q4K)
+
+
 def _fwd(lib, **kw):
     A = 0x10000  # fake, aligned device addresses: validation never dereferences them
     a = dict(x=A, x_dtype=0, T=4, rw=A, rb=None, eq=A, es=A, eb=4, eg=64, sq=A, ss=A, sb=8, sg=128,
@@ -150,6 +217,13 @@ def test_forward_validation_codes(lib):
     assert _fwd(lib, T=0) == 0                               # empty call: nothing enqueued
     assert _fwd(lib, T=0, x=None, y=None, ids=None, w=None) == 0
     assert _fwd(lib, T=0, ws=None) == 1
+    # the two-level format: 4-bit codes only, per-token path only (at most 64 tokens, not forced grouped)
+    assert _fwd(lib, eg=B.MOE_Q4K, T=65) == 3
+    assert _fwd(lib, sb=4, sg=B.MOE_Q4K, T=65) == 3
+    assert _fwd(lib, eg=B.MOE_Q4K, flags=B.MOE_FORCE_GROUPED) == 3
+    assert _fwd(lib, eb=8, eg=B.MOE_Q4K) == 3
+    assert _fwd(lib, sg=B.MOE_Q4K) == 3                     # shared codes are int8 here
+    assert _fwd(lib, eg=B.MOE_Q4K, T=0) == 0
 
 
 def test_workspace_bytes(lib):
@@ -179,6 +253,7 @@ def test_decode_forward_validation(lib):
     assert fwd(x=None) == 1
     assert fwd(n=0) == 2 and fwd(n=17) == 2
     assert fwd(eg=16) == 3
+    assert fwd(eb=8, eg=B.MOE_Q4K) == 3 and fwd(sg=B.MOE_Q4K) == 3
     assert fwd(flags=B.MOE_NORM_BF16 | B.MOE_NORM_INPUT) == 7
     assert fwd(flags=B.MOE_FORCE_DECODE) == 7
     assert fwd(xd=1) == 7                    # bf16 input cannot alias the f32 output
