@@ -25,13 +25,26 @@ METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s (% peak), int4 G=64, 1 G
 HBM_PEAK_GBS = 8000.0
 
 
+def expert_bytes(fmt, inter):
+    """Packed bytes of one expert (gate, up, down): codes plus f32 group scales,
+    or, for the two-level 4-bit format (group 256), codes plus one 16-byte
+    record per gate/up row and 256-column super-block, and for down one
+    4-byte d/dmin word per row and super-block (the routed down rows, 896
+    columns, end in a half super-block) and one 2-byte sc/m entry per row and
+    32-column sub-block."""
+    H = 1280
+    if fmt.bits == 4 and fmt.group == 256:
+        return 3 * H * inter // 2 + 16 * 2 * inter * (H // 256) + 4 * -(-inter // 256) * H + 2 * (inter // 32) * H
+    return 3 * H * inter * fmt.bits // 8 + 3 * H * inter // fmt.group * 4
+
+
 def layer_bytes(layer_ids, routed_fmt, shared_fmt):
     """Algorithmic bytes of one decode layer for one token: the packed codes and
     scales of the 6 picked experts, the shared expert and the router, plus the
     token's activations in and out."""
     H, I, IS, E = 1280, 896, 1792, 64
-    per_expert = 3 * H * I * routed_fmt.bits // 8 + 3 * H * I // routed_fmt.group * 4
-    shared = 3 * H * IS * shared_fmt.bits // 8 + 3 * H * IS // shared_fmt.group * 4
+    per_expert = expert_bytes(routed_fmt, I)
+    shared = expert_bytes(shared_fmt, IS)
     router = E * H * 4
     acts = H * 4 * 3 + 6 * 8  # h read, y read-modify-write, ids/w out
     return len(set(layer_ids)) * per_expert + shared + router + acts
@@ -95,9 +108,10 @@ def main():
                     default="decode",
                     help="decode = the headline 11-layer decode step; the prefill workloads report MFMA "
                          "figures; batchN = one continuous-batch decode step of N streams (HBM figures)")
-    ap.add_argument("--group", type=int, default=64, choices=[32, 64, 128],
+    ap.add_argument("--group", type=int, default=64, choices=[32, 64, 128, 256],
                     help="decode: group size of the routed int4 experts (64 is the headline; 32 and 128 sweep "
-                         "the group-size trade of metadata bytes against time)")
+                         "the group-size trade of metadata bytes against time; 256 = the two-level "
+                         "Q4_K-style format)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
@@ -135,7 +149,9 @@ def main():
         return bench_prefill(args)
 
     wl = WORKLOADS[1]
-    if args.group != wl.routed.group:
+    if args.group == 256:
+        wl = WORKLOADS[7]      # routed experts in the two-level 4-bit format, shared int8 G128
+    elif args.group != wl.routed.group:
         from dataclasses import replace
         from synth import QFmt
         wl = replace(wl, routed=QFmt(4, args.group), name=f"decode_1tok_11layers_int4g{args.group}_shared_int8g128")
@@ -200,7 +216,8 @@ def main():
     achieved = step_bytes / (ms_kernel * 1e-3) / 1e9
 
     out = {
-        "metric": METRIC if args.group == 64 else METRIC.replace("G=64", f"G={args.group}"),
+        "metric": METRIC if args.group == 64 else METRIC.replace(
+            "int4 G=64", "two-level 4-bit (Q4_K-style)" if args.group == 256 else f"int4 G={args.group}"),
         "value": 1000.0 / ms_step,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -213,7 +230,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded weights and tokens)",
         "config": {"workload": wl.name, "tokens_per_step": 1, "layers": L,
-                   "routed": f"int{wl.routed.bits} g{wl.routed.group}",
+                   "routed": "q4k (two-level)" if wl.routed.q4k else f"int{wl.routed.bits} g{wl.routed.group}",
                    "shared": f"int{wl.shared.bits} g{wl.shared.group}",
                    "weight_replicas": args.replicas, "path": args.path},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
@@ -241,8 +258,8 @@ def grouped_step_bytes(wl, ids_per_layer):
     read-modify-write, ids and weights out)."""
     H, I, IS, E = 1280, 896, 1792, 64
     rf, sf = wl.routed, wl.shared
-    per_expert = 3 * H * I * rf.bits // 8 + 3 * H * I // rf.group * 4
-    shared = 3 * H * IS * sf.bits // 8 + 3 * H * IS // sf.group * 4
+    per_expert = expert_bytes(rf, I)
+    shared = expert_bytes(sf, IS)
     T = wl.n_tokens
     total = 0
     for ids in ids_per_layer:

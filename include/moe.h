@@ -125,7 +125,7 @@ const char* moe_status_str(int32_t status);
  * float e * scale_count.
  * ------------------------------------------------------------------------ */
 size_t moe_expert_code_bytes(int32_t bits, int32_t inter);
-/* floats of packed scales per expert (group MOE_Q4K: 4-byte words of records) */
+/* floats of packed scales per expert (group MOE_Q4K: 4-byte words of metadata) */
 size_t moe_expert_scale_count(int32_t group_size, int32_t inter);
 moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t* down,
                              const float* gate_scales, const float* up_scales,
@@ -151,15 +151,21 @@ moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t*
  *   codes_out: moe_expert_code_bytes(4, inter) bytes, the int4 tile layout
  *     above holding q - 8 (so W = s (q - 8) + beta with s = d sc and
  *     beta = 8 s - dmin m per sub-block);
- *   meta_out: 4 * moe_expert_scale_count(MOE_Q4K, inter) bytes of 16-byte
- *     records: gate [inter][5], up [inter][5], down [ceil(inter/256)][1280]
- *     (record (b, r) of down = row r, super-block b).  Record words:
- *     w0 = d | dmin << 16; w1 = low 4 bits of sc_0..sc_7 (bits 4j..4j+3);
- *     w2 = low 4 bits of m_0..m_7; w3 = high 2 bits of sc_j at bit 2j and of
- *     m_j at bit 16 + 2j; sub-blocks past the end of a row are zero.
- * Experts are concatenated as for moe_pack_expert.  The records travel in
+ *   meta_out: 4 * moe_expert_scale_count(MOE_Q4K, inter) bytes:
+ *     gate records [inter][5] then up records [inter][5], 16 bytes each (row,
+ *     super-block): w0 = d | dmin << 16; byte j (j < 4) of w1 = sc_j |
+ *     (m_j >> 4) << 6, of w2 = sc_{4+j} | (m_{4+j} >> 4) << 6, of w3 =
+ *     (m_j & 15) | (m_{4+j} & 15) << 4;
+ *     then the down matrix in its tiles' row order, slot (rt, r, j) =
+ *     rt * 64 + r * 4 + j holding row 64 rt + 16 j + r (rt < 20, r < 16,
+ *     j < 4): uint32 d | dmin << 16 [ceil(inter/256)][1280 slots], then
+ *     uint16 sc | m << 8 [inter/32][1280 slots] (one 32-column slice of the
+ *     down matrix reads 6 bytes per row).
+ *   Metadata bits per weight: 0.5 for gate and up, 0.625 for down (0.64 for
+ *   the routed down, whose last super-block is half full).
+ * Experts are concatenated as for moe_pack_expert.  The metadata travels in
  * the expert_scales / shared_scales arguments with group = MOE_Q4K and
- * bits = 4 (4.5 bits per weight where K is a multiple of 256).
+ * bits = 4.
  * This format runs on the per-token (GEMV) path: moe_decode_forward, and
  * moe_layer_forward with n_tokens <= 64 (always on that path, whatever the
  * token count); MOE_FORCE_GROUPED or more tokens give MOE_E_FORMAT.

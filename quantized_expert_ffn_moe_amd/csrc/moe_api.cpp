@@ -173,22 +173,44 @@ void pack_slab_scales(const float* S, int N, int K, int group, int bits, float* 
           out[(((size_t)g * nrt + rt) * 16 + r) * ns + j] = S[(size_t)(DR * rt + 16 * j + r) * ng + g];
 }
 
-// One two-level record (row r, super-block b) of a matrix with K columns:
-// word 0 = d | dmin << 16; word 1 = the low nibbles of sc_0..7 (nibble j),
-// word 2 = those of m_0..7, word 3 = the high 2 bits of sc_j at bit 2j and of
-// m_j at bit 16 + 2j.  Sub-blocks past the end of the row stay zero.
+// One gate/up record (row r, super-block b) of a matrix with K columns:
+// word 0 = d | dmin << 16; word 1 byte j = sc_j | (m_j >> 4) << 6; word 2
+// byte j = sc_{4+j} | (m_{4+j} >> 4) << 6; word 3 byte j = (m_j & 15) |
+// (m_{4+j} & 15) << 4.  Sub-blocks past the end of the row stay zero.
 void q4k_record(const moe_q4k_matrix_t& M, int K, int r, int b, uint8_t* out) {
   const int nsb = q4k_superblocks(K), nsub = K / Q4K_SUB;
-  uint32_t w[4] = {(uint32_t)M.d[(size_t)r * nsb + b] | ((uint32_t)M.dmin[(size_t)r * nsb + b] << 16), 0u, 0u, 0u};
+  uint8_t sc[8] = {0}, m[8] = {0};
   for (int j = 0; j < Q4K_SB / Q4K_SUB; ++j) {
     const int g = b * (Q4K_SB / Q4K_SUB) + j;
     if (g >= nsub) break;
-    const uint32_t sc = M.sc[(size_t)r * nsub + g], m = M.m[(size_t)r * nsub + g];
-    w[1] |= (sc & 15u) << (4 * j);
-    w[2] |= (m & 15u) << (4 * j);
-    w[3] |= ((sc >> 4) << (2 * j)) | ((m >> 4) << (16 + 2 * j));
+    sc[j] = M.sc[(size_t)r * nsub + g];
+    m[j] = M.m[(size_t)r * nsub + g];
+  }
+  uint32_t w[4] = {(uint32_t)M.d[(size_t)r * nsb + b] | ((uint32_t)M.dmin[(size_t)r * nsb + b] << 16), 0u, 0u, 0u};
+  for (int j = 0; j < 4; ++j) {
+    w[1] |= (uint32_t)(sc[j] | ((m[j] >> 4) << 6)) << (8 * j);
+    w[2] |= (uint32_t)(sc[4 + j] | ((m[4 + j] >> 4) << 6)) << (8 * j);
+    w[3] |= (uint32_t)((m[j] & 15) | ((m[4 + j] & 15) << 4)) << (8 * j);
   }
   memcpy(out, w, sizeof(w));
+}
+
+// Down metadata of a [H][K] matrix in the down tiles' row order (row
+// 64 rt + 16 j + r at [rt][r][j]): d | dmin words per super-block, then
+// sc | m << 8 halfwords per sub-block.
+void q4k_down_meta(const moe_q4k_matrix_t& M, int K, uint8_t* out) {
+  const int nsb = q4k_superblocks(K), nsub = K / Q4K_SUB;
+  uint32_t* dd = (uint32_t*)out;
+  uint16_t* sm = (uint16_t*)(out + (size_t)4 * nsb * H);
+  for (int rt = 0; rt < H / 64; ++rt)
+    for (int r = 0; r < 16; ++r)
+      for (int j = 0; j < 4; ++j) {
+        const size_t row = (size_t)64 * rt + 16 * j + r, slot = ((size_t)rt * 16 + r) * 4 + j;
+        for (int b = 0; b < nsb; ++b)
+          dd[(size_t)b * H + slot] = (uint32_t)M.d[row * nsb + b] | ((uint32_t)M.dmin[row * nsb + b] << 16);
+        for (int g = 0; g < nsub; ++g)
+          sm[(size_t)g * H + slot] = (uint16_t)(M.sc[row * nsub + g] | (M.m[row * nsub + g] << 8));
+      }
 }
 
 // every field in range: codes <= 15, sc and m <= 63, d and dmin finite f16
@@ -259,9 +281,7 @@ moe_status_t moe_pack_expert_q4k(const moe_q4k_matrix_t* gate, const moe_q4k_mat
       q4k_record(*gate, H, r, b, meta + ((size_t)r * nsb + b) * Q4K_REC);
       q4k_record(*up, H, r, b, meta + ((size_t)(inter + r) * nsb + b) * Q4K_REC);
     }
-  uint8_t* dmeta = meta + 2 * (size_t)inter * nsb * Q4K_REC;
-  for (int b = 0; b < q4k_superblocks(inter); ++b)
-    for (int r = 0; r < H; ++r) q4k_record(*down, inter, r, b, dmeta + ((size_t)b * H + r) * Q4K_REC);
+  q4k_down_meta(*down, inter, meta + q4k_rec_bytes(inter));
   return MOE_OK;
 }
 

@@ -27,19 +27,29 @@ __host__ __device__ constexpr int down_rows(int bits) { return bits == 4 ? 64 : 
 __host__ __device__ constexpr size_t matrix_bytes(int bits, int n, int k) { return (size_t)n * k * bits / 8; }
 
 // Two-level 4-bit (Q4_K-style) format, selected by group == Q4K with 4-bit
-// codes: super-blocks of Q4K_SB columns along K, each with one 16-byte record
-// per row (f16 d and dmin, a 6-bit scale and a 6-bit minimum per sub-block of
-// Q4K_SUB columns); the codes are the int4 tiles of q - 8.
+// codes: super-blocks of Q4K_SB columns along K with f16 d and dmin, split
+// into sub-blocks of Q4K_SUB columns with a 6-bit scale and a 6-bit minimum;
+// the codes are the int4 tiles of q - 8.  Metadata of one expert:
+//   gate and up: one 16-byte record per (row, super-block), [N][H / 256];
+//   down, in the down tiles' row order (row 64 rt + 16 j + r at [rt][r][j]):
+//     [ceil(inter / 256)][H / 64][16][4] words d | dmin << 16, then
+//     [inter / 32][H / 64][16][4] halfwords sc | m << 8,
+//   so that a down slice (one sub-block) reads 6 bytes per row.
 constexpr int Q4K = 256;
 constexpr int Q4K_SB = 256;
 constexpr int Q4K_SUB = 32;
 constexpr int Q4K_REC = 16;
 __host__ __device__ constexpr int q4k_superblocks(int k) { return (k + Q4K_SB - 1) / Q4K_SB; }
-// bytes of one expert's records: gate and up [inter][H / 256], down [ceil(inter / 256)][H]
-__host__ __device__ constexpr size_t q4k_meta_bytes(int inter) {
-  return (size_t)Q4K_REC * (2 * (size_t)inter * q4k_superblocks(H) + (size_t)q4k_superblocks(inter) * H);
+__host__ __device__ constexpr size_t q4k_rec_bytes(int inter) {   // gate + up records
+  return (size_t)Q4K_REC * 2 * (size_t)inter * q4k_superblocks(H);
 }
-// 4-byte words of one expert's scale data (f32 group scales, or two-level records)
+__host__ __device__ constexpr size_t q4k_dd_bytes(int inter) {    // down d/dmin words
+  return (size_t)4 * q4k_superblocks(inter) * H;
+}
+__host__ __device__ constexpr size_t q4k_meta_bytes(int inter) {
+  return q4k_rec_bytes(inter) + q4k_dd_bytes(inter) + (size_t)2 * (inter / Q4K_SUB) * H;
+}
+// 4-byte words of one expert's scale data (f32 group scales, or two-level metadata)
 __host__ __device__ constexpr size_t scale_words(int group, int inter) {
   return group == Q4K ? q4k_meta_bytes(inter) / 4 : 3 * (size_t)inter * H / group;
 }

@@ -388,8 +388,8 @@ __device__ __forceinline__ int digit_pos(int i) {
 // one wave) share an exponent.  xa: [unit k / 64][plane 0..3][q][4 words] (the
 // unused plane 3 is never written: it only feeds C rows that are not read);
 // xs[block] = 2^(e - XF) (2^(e - XF - 4) for int4: the 16x codes).
-// With SUMS (blocks of 32 only), xsum[block] = the f32 sum of the block's
-// elements of x * mul (the two-level format's minimum term).
+// With SUMS (blocks of 32 only), xsum[block] = 8 x the f32 sum of the
+// block's elements of x * mul (the two-level format's minimum term).
 template <int BITS, bool SUMS = false>
 __device__ __forceinline__ void x_digits(const float* x, float mul, int kg, int blk, uint32_t* xa, float* xs,
                                          bool active, float* xsum = nullptr) {
@@ -411,7 +411,7 @@ __device__ __forceinline__ void x_digits(const float* x, float mul, int kg, int 
   int e;
   frexpf(amax, &e);                       // amax < 2^e (e = 0 when the block is zero)
   if ((kg & (blk / 8 - 1)) == 0) xs[(8 * kg) / blk] = ldexpf(1.0f, e - XF - (BITS == 4 ? 4 : 0));
-  if (SUMS && (kg & 3) == 0) xsum[kg / 4] = vsum;
+  if (SUMS && (kg & 3) == 0) xsum[kg / 4] = 8.0f * vsum;
   uint32_t M[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) M[i] = (uint32_t)((int)rintf(ldexpf(v[i], XF - e)) + (int)XOFF);
@@ -465,21 +465,27 @@ struct ItemRegs {
   u32x4 gm[K4 ? NREC : 1];                 // two-level: this lane's row, the K half's super-blocks
   uint4 dn[D_TPW];
   float dns[D_TPW][K4 ? 1 : RS];
-  u32x4 dm[K4 ? D_TPW : 1];               // two-level: lane (r, q) holds the record of down row DR rt + 16 q + r
+  u32x4 dd[K4 ? D_TPW : 1];               // two-level: d | dmin << 16 of this lane's 4 down rows per tile
+  uint2 dsm[K4 ? D_TPW : 1];              // ... and their sc | m << 8 halfwords for the slice
 };
 
-// Sub-block j (0..7) of a two-level record: word 0 = d | dmin << 16 (f16);
-// word 1 = the low 4 bits of sc_0..sc_7 (nibble j), word 2 = those of
-// m_0..m_7, word 3 = the high 2 bits of sc_j at bit 2j and of m_j at bit
-// 16 + 2j.  Returns s = d sc_j and beta = 8 s - dmin m_j (one rounding).
 __device__ __forceinline__ float f16_bits_value(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
-__device__ __forceinline__ void q4k_sub(const u32x4& r, int j, float& s, float& beta) {
-  const uint32_t sc = ((r[1] >> (4 * j)) & 15u) | (((r[3] >> (2 * j)) & 3u) << 4);
-  const uint32_t m = ((r[2] >> (4 * j)) & 15u) | (((r[3] >> (16 + 2 * j)) & 3u) << 4);
-  s = f16_bits_value(r[0] & 0xFFFFu) * (float)sc;
-  beta = fmaf(-f16_bits_value(r[0] >> 16), (float)m, 8.0f * s);
+__device__ __forceinline__ float byte_value(uint32_t w, int k) { return (float)((w >> (8 * k)) & 255u); }
+// The scales and minimums of a gate/up record as bytes: w1 byte j = sc_j |
+// (m_j >> 4) << 6, w2 byte j = sc_{4+j} | (m_{4+j} >> 4) << 6, w3 byte j =
+// (m_j & 15) | (m_{4+j} & 15) << 4 (word 0 = d | dmin << 16, f16).
+struct Q4kBytes {
+  uint32_t sc[2], m[2];   // sc_0..3, sc_4..7, m_0..3, m_4..7, one per byte
+};
+__device__ __forceinline__ Q4kBytes q4k_bytes(const u32x4& r) {
+  Q4kBytes b;
+  b.sc[0] = r[1] & 0x3F3F3F3Fu;
+  b.sc[1] = r[2] & 0x3F3F3F3Fu;
+  b.m[0] = (r[3] & 0x0F0F0F0Fu) | ((r[1] >> 2) & 0x30303030u);
+  b.m[1] = ((r[3] >> 4) & 0x0F0F0F0Fu) | ((r[2] >> 2) & 0x30303030u);
+  return b;
 }
 
 // A pointer or index the whole wave agrees on, as a scalar value (lets buffer
@@ -550,16 +556,21 @@ __device__ __forceinline__ void item_load(ItemRegs<BITS, G>& R, const uint8_t* e
   for (int m = 0; m < IR::GU_TPW; ++m) R.gu[m] = wload16(rg, m * TILE + lane * 16);
   const __amdgpu_buffer_rsrc_t rd = weight_rsrc(eq + 2 * mbytes + (size_t)J * IR::NRT * TILE, IR::NRT * TILE);
   if constexpr (IR::K4) {
-    // two-level down records [super-block][row]: the slice's super-block;
-    // lane (r, q) takes row DR rt + 16 q + r of each tile (rows past the end
-    // read as zeros), the 4 lane groups sharing out a tile's 4 rows per r
-    const __amdgpu_buffer_rsrc_t rdm = weight_rsrc((const uint8_t*)es + 2 * (size_t)inter * IR::NSB * Q4K_REC +
-                                                       (size_t)(J / (Q4K_SB / SLICE)) * H * Q4K_REC,
-                                                   H * Q4K_REC);
+    // two-level down metadata in tile row order: the d | dmin words of the
+    // slice's super-block and the sc | m << 8 halfwords of its sub-block (= the
+    // slice), for rows DR rt + 16 j + r, j = 0..3 (tiles past the end read
+    // as zeros)
+    static_assert(IR::RS == 4, "4 down rows per lane and tile");
+    const uint8_t* dmeta = (const uint8_t*)es + q4k_rec_bytes(inter);
+    const __amdgpu_buffer_rsrc_t rdd =
+        weight_rsrc(dmeta + (size_t)(J / (Q4K_SB / SLICE)) * H * 4, H * 4);
+    const __amdgpu_buffer_rsrc_t rsm = weight_rsrc(dmeta + q4k_dd_bytes(inter) + (size_t)J * H * 2, H * 2);
 #pragma unroll
     for (int m = 0; m < IR::D_TPW; ++m) {
       const uint32_t rt = wv + 8 * m;
-      R.dm[m] = __builtin_amdgcn_raw_buffer_load_b128(rdm, (rt * IR::DR + 16 * (lane >> 4) + r) * Q4K_REC, 0, 0);
+      R.dd[m] = __builtin_amdgcn_raw_buffer_load_b128(rdd, (rt * 16 + r) * 16, 0, 0);
+      const auto sm = __builtin_amdgcn_raw_buffer_load_b64(rsm, (rt * 16 + r) * 8, 0, 0);
+      R.dsm[m] = make_uint2(sm[0], sm[1]);
       R.dn[m] = wload16(rd, rt * TILE + lane * 16);
     }
     return;
@@ -606,7 +617,7 @@ struct ItemLds {
   uint32_t ha[8][4 * 4 * 2];           // per wave: A-operand digits of h: [plane][q][2]
   float hs;                            // unit of the h digits (times 2^-4 for int4 codes)
   float dout[H];                       // down rows of the item in units of hs
-  float xsum[H / 32];                  // two-level format: per-32-block sums of the input
+  float xsum[H / 32];                  // two-level format: 8 x the per-32-block sums of the input
 };
 
 // Digits of the layer input z (in LDS) for weights of format (BITS, G).
@@ -640,15 +651,23 @@ __device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint3
 // x32 products), every wave forms h = SiLU(g) * u and its digits, then each wave
 // takes its down tiles (x32 products over the 32-column slice).  Ends with a
 // workgroup barrier.
-// Gate/up sums of a two-level item over K half HH (lanes 0..15 hold rows):
-// per 32-column sub-block, s times the scaled integer product plus beta times
-// the sum of the sub-block's inputs.
+// Gate/up sums of a two-level item over K half HH (lanes 0..15 hold rows).
+// Per super-block record: d * sum_j sc_j (scaled integer product_j + 8 X_j)
+// - dmin * sum_j m_j X_j over its sub-blocks j, X_j the sum of the
+// sub-block's inputs (W = d sc (q - 8) + 8 d sc - dmin m).
 template <int HH>
 __device__ __forceinline__ float q4k_gateup(const ItemRegs<4, Q4K>& R, const ItemLds& L, int pl, int q) {
   using IR = ItemRegs<4, Q4K>;
   constexpr int NU = IR::GU_TPW * 2;            // x64 units in a K half
   constexpr int u0 = HH * NU;
-  float acc = 0.f;
+  Q4kBytes fb[IR::NREC];
+  float Dk[IR::NREC], Mk[IR::NREC];
+#pragma unroll
+  for (int k = 0; k < IR::NREC; ++k) {
+    fb[k] = q4k_bytes(R.gm[k]);
+    Dk[k] = 0.f;
+    Mk[k] = 0.f;
+  }
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     const uint4 a4 = *(const uint4*)&L.xa[(((u0 + u) * 4 + pl) * 4 + q) * 4];
@@ -658,11 +677,18 @@ __device__ __forceinline__ float q4k_gateup(const ItemRegs<4, Q4K>& R, const Ite
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int gg = IR::NGW * HH + 2 * u + t;    // sub-block of the row (0..39)
-      float s, beta;
-      q4k_sub(R.gm[gg / 8 - 2 * HH], gg % 8, s, beta);
-      acc = fmaf(s * L.xs[gg], digits_value(c[t]), acc);
-      acc = fmaf(beta, L.xsum[gg], acc);
+      const int k = gg / 8 - 2 * HH, j = gg % 8;
+      const float x8 = L.xsum[gg];
+      const float tt = fmaf(L.xs[gg], digits_value(c[t]), x8);
+      Dk[k] = fmaf(byte_value(fb[k].sc[j / 4], j % 4), tt, Dk[k]);
+      Mk[k] = fmaf(byte_value(fb[k].m[j / 4], j % 4), x8, Mk[k]);
     }
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < IR::NREC; ++k) {
+    acc = fmaf(f16_bits_value(R.gm[k][0] & 0xFFFFu), Dk[k], acc);
+    acc = fmaf(-0.125f * f16_bits_value(R.gm[k][0] >> 16), Mk[k], acc);
   }
   return acc;
 }
@@ -706,7 +732,7 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds
   // of the A operand (identical arithmetic in every wave; a wave reads back its
   // own LDS writes in order, so no workgroup barrier is needed)
   uint64_t Ah;
-  float xh = 0.f;
+  float xh = 0.f, xh8 = 0.f;
   {
     float hv = 0.f;
     if (lane < SLICE) {
@@ -721,7 +747,10 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds
     if (tid == 0) L.hs = ldexpf(1.0f, e - XF - (BITS == 4 ? 4 : 0));
     // two-level format: the slice's inputs summed in units of L.hs (16 x the
     // integer mantissas: the unit carries the 2^-4 of the 4-bit codes)
-    if (IR::K4) xh = 16.0f * wave_sum(rintf(ldexpf(hv, XF - e)));
+    if (IR::K4) {
+      xh = 16.0f * wave_sum(rintf(ldexpf(hv, XF - e)));
+      xh8 = 8.0f * xh;
+    }
     uint8_t* hb = (uint8_t*)L.ha[wv];
     if (lane < SLICE) {
       const uint32_t M = (uint32_t)((int)rintf(ldexpf(hv, XF - e)) + (int)XOFF);
@@ -733,21 +762,20 @@ __device__ __forceinline__ void item_compute(const ItemRegs<BITS, G>& R, ItemLds
   }
   // all products first, then the recombination (lanes 0..15 hold the rows);
   // the last tile of waves with one tile fewer is all zeros (range-checked loads)
-  static_assert(!IR::K4 || IR::RS == 4, "one down record per lane group");
   float dv[IR::D_TPW][IR::RS];
 #pragma unroll
   for (int m = 0; m < IR::D_TPW; ++m) {
-    float s_own = 0.f, beta_own = 0.f;   // two-level: s and beta of this lane's record
-    if constexpr (IR::K4) q4k_sub(R.dm[m], J % (Q4K_SB / SLICE), s_own, beta_own);
 #pragma unroll
     for (int j = 0; j < IR::RS; ++j) {
       const uint64_t Bd = BITS == 4 ? pack64(even_codes(word_of(R.dn[m], j)), odd_codes(word_of(R.dn[m], j)))
                                     : pack64(word_of(R.dn[m], 2 * j), word_of(R.dn[m], 2 * j + 1));
       if constexpr (IR::K4) {
-        // row DR rt + 16 j + r: its record sits in lane r + 16 j
-        const int src = (lane & 15) + 16 * j;
-        const float s = __shfl(s_own, src), beta = __shfl(beta_own, src);
-        dv[m][j] = fmaf(s, digits_value(mfma_x32(Ah, Bd)), beta * xh);
+        // halfword j = sc | m << 8: W = d sc (q - 8) + 8 d sc - dmin m
+        const uint32_t hw = j < 2 ? R.dsm[m].x : R.dsm[m].y;
+        const float sc = byte_value(hw, 2 * (j & 1)), mm = byte_value(hw, 2 * (j & 1) + 1);
+        const float ds = f16_bits_value(R.dd[m][j] & 0xFFFFu) * sc;
+        const float dm = f16_bits_value(R.dd[m][j] >> 16) * mm;
+        dv[m][j] = fmaf(ds, digits_value(mfma_x32(Ah, Bd)) + xh8, -dm * xh);
       } else {
         dv[m][j] = R.dns[m][j] * digits_value(mfma_x32(Ah, Bd));
       }
@@ -1204,7 +1232,10 @@ __global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
   uint32_t* err = a.hdr + 2;
   if (b < R_ITEMS) {
     if constexpr ((QK & 1) != 0) {
-      chain_routed<4, Q4K>(a, LP, S.it, b, base, err);
+      // two-level: workgroup b (on XCD b % 8) takes item 21 (b % 8) + b / 8,
+      // so each XCD runs a contiguous run of slices and the 8 slices of a
+      // super-block, which share its d | dmin words, mostly share one L2
+      chain_routed<4, Q4K>(a, LP, S.it, (b % 8) * (R_ITEMS / 8) + b / 8, base, err);
     } else {
       switch (a.rgroup) {
         case 32: chain_routed<BR, 32>(a, LP, S.it, b, base, err); break;
@@ -1214,7 +1245,7 @@ __global__ __launch_bounds__(512) void chain_kernel(ChainArgs a) {
     }
   } else if (b < N_ITEMS) {
     if constexpr ((QK & 2) != 0) {
-      chain_shared<4, Q4K>(a, LP, S.it, b, base, err);
+      chain_shared<4, Q4K>(a, LP, S.it, R_ITEMS + (b % 8) * (S_ITEMS / 8) + (b - R_ITEMS) / 8, base, err);
     } else {
       switch (a.sgroup) {
         case 32: chain_shared<BS, 32>(a, LP, S.it, b, base, err); break;

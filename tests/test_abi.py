@@ -131,8 +131,9 @@ def _record_fields(w):
     """(d bits, dmin bits, sc[8], m[8]) of one 16-byte record, decoded from the
     layout in include/moe.h (independent of the packer)."""
     w = [int(v) for v in w]
-    sc = [((w[1] >> (4 * j)) & 15) | (((w[3] >> (2 * j)) & 3) << 4) for j in range(8)]
-    m = [((w[2] >> (4 * j)) & 15) | (((w[3] >> (16 + 2 * j)) & 3) << 4) for j in range(8)]
+    byte = lambda x, k: (x >> (8 * k)) & 255
+    sc = [byte(w[1 + j // 4], j % 4) & 63 for j in range(8)]
+    m = [((byte(w[3], j % 4) >> (4 * (j // 4))) & 15) | ((byte(w[1 + j // 4], j % 4) >> 6) << 4) for j in range(8)]
     return w[0] & 0xFFFF, w[0] >> 16, sc, m
 
 
@@ -144,26 +145,30 @@ def test_pack_q4k_layout(lib, inter):
     mb = inter * 1280 // 2
     assert codes.size == 3 * mb
     nsbd = -(-inter // 256)
-    assert meta.size * 4 == 16 * (2 * inter * 5 + nsbd * 1280) == 4 * B.moe_expert_scale_count(B.MOE_Q4K, inter)
+    assert meta.size * 4 == 16 * 2 * inter * 5 + 4 * nsbd * 1280 + 2 * (inter // 32) * 1280 \
+        == 4 * B.moe_expert_scale_count(B.MOE_Q4K, inter)
     # codes: the int4 tiles of q - 8
     np.testing.assert_array_equal(_unpack_rows(codes[:mb][: 16 * 1280], 32, 1280, 4), g["q"][:32].astype(int) - 8)
     np.testing.assert_array_equal(_unpack_rows(codes[mb:2 * mb][: 8 * 1280], 16, 1280, 4), u["q"][:16].astype(int) - 8)
     np.testing.assert_array_equal(_unpack_slabs(codes[2 * mb:], inter, 4, 2), d["q"][:, :64].astype(int) - 8)
-    rec = meta.view(np.uint32).reshape(-1, 4)
+    rec = meta.view(np.uint32)[: 2 * inter * 5 * 4].reshape(-1, 4)
     for mat, base in ((g, 0), (u, inter * 5)):
         for r in (0, 7, inter - 1):
             for b in range(5):
                 db, dmb, sc, m = _record_fields(rec[base + r * 5 + b])
                 assert (db, dmb) == (mat["d"][r, b], mat["dmin"][r, b])
                 assert sc == mat["sc"][r, 8 * b:8 * b + 8].tolist() and m == mat["m"][r, 8 * b:8 * b + 8].tolist()
-    base = 2 * inter * 5
-    for b in range(nsbd):
-        for r in (0, 641, 1279):
-            db, dmb, sc, m = _record_fields(rec[base + b * 1280 + r])
-            n = min(8, inter // 32 - 8 * b)                  # the routed row ends in a half super-block
-            assert (db, dmb) == (d["d"][r, b], d["dmin"][r, b])
-            assert sc[:n] == d["sc"][r, 8 * b:8 * b + n].tolist() and m[:n] == d["m"][r, 8 * b:8 * b + n].tolist()
-            assert sc[n:] == [0] * (8 - n) and m[n:] == [0] * (8 - n)
+    # down: slot rt * 64 + r * 4 + j holds row 64 rt + 16 j + r
+    raw = meta.view(np.uint8)[16 * 2 * inter * 5:]
+    dd = raw[: 4 * nsbd * 1280].view(np.uint32).reshape(nsbd, 1280)
+    sm = raw[4 * nsbd * 1280:].view(np.uint16).reshape(inter // 32, 1280)
+    slot = np.arange(1280)
+    row = 64 * (slot // 64) + 16 * (slot % 4) + (slot // 4) % 16
+    assert sorted(row.tolist()) == list(range(1280))
+    np.testing.assert_array_equal(dd & 0xFFFF, d["d"][row].T)
+    np.testing.assert_array_equal(dd >> 16, d["dmin"][row].T)
+    np.testing.assert_array_equal(sm & 255, d["sc"][row].T)
+    np.testing.assert_array_equal(sm >> 8, d["m"][row].T)
 
 
 def test_pack_q4k_rejects_bad_fields(lib):
