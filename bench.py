@@ -51,7 +51,9 @@ def layer_bytes(layer_ids, routed_fmt, shared_fmt):
 
 
 KERNEL_SOURCES = ("quantized_expert_ffn_moe_amd/csrc/moe_kernels.hip", "quantized_expert_ffn_moe_amd/csrc/moe_internal.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_chain_kernel_11layers_traffic.json")
+# HBM counter summaries of the decode kernel, per routed group size
+TRAFFIC_FILES = {64: os.path.join(ROOT, "profiles", "decode_chain_kernel_11layers_traffic.json"),
+                 256: os.path.join(ROOT, "profiles", "decode_chain_kernel_11layers_q4k_traffic.json")}
 
 
 def kernel_source_hash():
@@ -63,12 +65,15 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def counted_traffic():
+def counted_traffic(group=64):
     """HBM bytes per dispatch of the decode kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE passes (scaled by the copy-kernel calibration), or
-    None when the kernel sources have changed since those counters were taken."""
+    None when there are none for this routed format or the kernel sources have
+    changed since those counters were taken."""
+    if group not in TRAFFIC_FILES:
+        return None
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(TRAFFIC_FILES[group]) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -235,7 +240,7 @@ def main():
                    "weight_replicas": args.replicas, "path": args.path},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counted_traffic() if args.group == 64 else None,
+                     "traffic": counted_traffic(args.group),
                      "bytes_per_launch": step_bytes, "ms_per_launch": ms_kernel},
     }
     if not args.no_cpu_baseline:
