@@ -56,7 +56,7 @@ typedef enum {
   MOE_E_NULLPTR = 1,   /* a required pointer is NULL */
   MOE_E_SHAPE = 2,     /* token count or intermediate size out of range */
   MOE_E_FORMAT = 3,    /* bits not in {4, 8}, group not in {32, 64, 128} (or MOE_Q4K with 4 bits),
-                          a code out of range, or a format the requested path does not run */
+                          or a code out of range */
   MOE_E_ALIGN = 4,     /* a device pointer is not 16-byte aligned */
   MOE_E_WORKSPACE = 5, /* workspace smaller than moe_workspace_bytes() */
   MOE_E_HIP = 6,       /* the HIP runtime reported an error while enqueueing */
@@ -166,9 +166,10 @@ moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t*
  * Experts are concatenated as for moe_pack_expert.  The metadata travels in
  * the expert_scales / shared_scales arguments with group = MOE_Q4K and
  * bits = 4.
- * This format runs on the per-token (GEMV) path: moe_decode_forward, and
- * moe_layer_forward with n_tokens <= 64 (always on that path, whatever the
- * token count); MOE_FORCE_GROUPED or more tokens give MOE_E_FORMAT.
+ * Every path takes this format: moe_decode_forward, and moe_layer_forward
+ * on the per-token path and on the grouped path (there a call with a
+ * two-level expert set runs 32-row tiles without the fused shared/routed
+ * launches).
  * Returns MOE_E_NULLPTR for a missing pointer, MOE_E_SHAPE for an
  * intermediate size other than 896 or 1792, MOE_E_FORMAT for a field out of
  * range (nothing is written then).

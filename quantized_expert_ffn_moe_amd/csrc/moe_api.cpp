@@ -333,9 +333,9 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   if ((flags & ~known) || (x_dtype != MOE_F32 && x_dtype != MOE_BF16)) return MOE_E_ARG;
   if ((flags & MOE_FORCE_DECODE) && (flags & MOE_FORCE_GROUPED)) return MOE_E_ARG;
   if ((flags & MOE_FORCE_DECODE) && T > DECODE_FORCE_MAX_T) return MOE_E_SHAPE;
-  // the two-level format runs on the per-token path only
+  // a two-level expert set runs on the grouped path's 32-row tiles (so does
+  // the other set of that call), without the fused shared/routed launches
   const bool two_level = expert_group == Q4K || shared_group == Q4K;
-  if (two_level && ((flags & MOE_FORCE_GROUPED) || T > DECODE_FORCE_MAX_T)) return MOE_E_FORMAT;
   if ((flags & MOE_NORM_BF16) && !(flags & MOE_NORM_INPUT)) return MOE_E_ARG;
   if ((flags & MOE_NORM_INPUT) && x_dtype != MOE_F32) return MOE_E_ARG;
   if (x && x == (const void*)y && !((flags & MOE_ACCUMULATE) && x_dtype == MOE_F32)) return MOE_E_ARG;
@@ -368,7 +368,7 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   const QW sw = make_qw(shared_q, shared_scales, shared_bits, shared_group, IS, false);
   const int accumulate = (flags & MOE_ACCUMULATE) != 0;
 
-  const bool decode = two_level || (flags & MOE_FORCE_DECODE) || (!(flags & MOE_FORCE_GROUPED) && T <= DECODE_MAX_T);
+  const bool decode = (flags & MOE_FORCE_DECODE) || (!(flags & MOE_FORCE_GROUPED) && T <= DECODE_MAX_T);
   if (decode) {
     DecItemsArgs d;
     d.xf = xf; d.xb = xb; d.ids = topk_ids; d.tw = topk_w; d.rw = rw; d.sw = sw; d.part = ws.part;
@@ -381,8 +381,8 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
 
   // tile shape: 32-row tiles while the experts see few rows each (about 64 or
   // fewer on average), 64-row tiles beyond
-  const bool small = (size_t)T * TOPK <= (size_t)SMALL_TILE_MAX_SLOTS;
-  const bool pair = small && small_pair_available(rw.bits, rw.group, sw.bits, sw.group);
+  const bool small = two_level || (size_t)T * TOPK <= (size_t)SMALL_TILE_MAX_SLOTS;
+  const bool pair = !two_level && small && small_pair_available(rw.bits, rw.group, sw.bits, sw.group);
   const int mtl = !small ? MT : (pair && (size_t)T * TOPK <= TINY_TILE_MAX_SLOTS) ? MT_TINY : MT_SMALL;
   const int max_tiles = (int)((size_t)T * TOPK / mtl) + E + 1;
   HistArgs ha;
@@ -407,7 +407,17 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   dr.out = ws.ysorted;
   ds.af = ws.h_shared; ds.ab = nullptr; ds.shared = 1; ds.a_by_token = 0; ds.a_rows = T; ds.w = sw; ds.out = ws.ys;
   ds.ksplit = small ? 2 : 1;
-  if (pair && launch_small_pair(gr, max_tiles, gs, s_tiles, false, mtl, s)) {
+  if (two_level) {
+    auto gateup = [&](const GroupedArgs& g, int tiles) {
+      return g.w.group == Q4K ? launch_grouped_q4k(g, tiles, false, s) : launch_grouped_gateup(g, tiles, true, s);
+    };
+    auto down = [&](const GroupedArgs& g, int tiles) {
+      return g.w.group == Q4K ? launch_grouped_q4k(g, tiles, true, s) : launch_grouped_down(g, tiles, true, s);
+    };
+    if (gateup(gr, max_tiles) != hipSuccess || gateup(gs, s_tiles) != hipSuccess ||
+        down(dr, max_tiles) != hipSuccess || down(ds, s_tiles) != hipSuccess)
+      return MOE_E_HIP;
+  } else if (pair && launch_small_pair(gr, max_tiles, gs, s_tiles, false, mtl, s)) {
     if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
     if (!launch_small_pair(dr, max_tiles, ds, s_tiles, true, mtl, s) || hipGetLastError() != hipSuccess) return MOE_E_HIP;
   } else {

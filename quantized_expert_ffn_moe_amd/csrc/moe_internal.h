@@ -214,6 +214,8 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s);
 hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+// Grouped gate/up (down = false) or down GEMMs of a two-level expert set (32-row tiles).
+hipError_t launch_grouped_q4k(const GroupedArgs& a, int max_tiles, bool down, hipStream_t s);
 // Routed and shared small-tile GEMMs in one launch (gate/up, or down with the
 // shared expert in two K halves); false if the format pair has no fused kernel.
 bool small_pair_available(int rbits, int rgroup, int sbits, int sgroup);

@@ -2036,17 +2036,26 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
 // tiles and their group scales are fetched D stages ahead into a register
 // ring, A two stages ahead into registers and one stage ahead into a double
 // buffer in LDS, so that the memory latency hides behind the MFMA work.
+// G = Q4K: the two-level format.  The codes are the int4 tiles of q - 8 and
+// each 32-column sub-block adds beta * X to its scaled product (X = the sum of
+// the row's inputs over the sub-block, formed while A is staged; s and beta
+// from the row's super-block record, fetched with the B tiles).
 template <int BITS, bool SPLIT, int G, int MTL>
 __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid) {
+  constexpr bool K4 = G == Q4K;
+  static_assert(!K4 || BITS == 4, "two-level codes are 4-bit");
+  constexpr int GG = K4 ? Q4K_SUB : G;     // columns per scale
   constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MTL / 16;
-  constexpr int CPG = G / 32, GPS = KS / G, NG = H / G;
-  constexpr int D = G == 32 ? 3 : (BITS == 4 ? 4 : 3);   // B stages in flight
+  constexpr int CPG = GG / 32, GPS = KS / GG, NG = H / GG;
+  constexpr int NSB = H / Q4K_SB;          // two-level records per gate/up row
+  constexpr int D = GG == 32 ? 3 : (BITS == 4 ? 4 : 3);   // B stages in flight
   // With G = 32 every K step is its own scale group, and a fully unrolled
   // stage loop lets the compiler hoist matrix-core products far ahead of their
   // scale multiply (and spill them): there the stages run in blocks of 6 with
   // a loop between the blocks.
-  constexpr int SB = G == 32 ? 6 : NSTAGE;
+  constexpr int SB = GG == 32 ? 6 : NSTAGE;
   static_assert(SB % D == 0 && SB % 6 == 0 || SB == NSTAGE, "ring slots fixed within a block");
+  static_assert(!K4 || (SB % 2 == 0 && Q4K_SB == 2 * KS), "a stage is a fixed half of a super-block");
   constexpr bool F32 = SPLIT;
   constexpr int APL = SPLIT ? 2 : 1;
   constexpr int NSEG = MTL * KS / 8;        // A segments (8 elements) per stage: one per thread up to 512
@@ -2057,6 +2066,7 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
             q4 = lane >> 4;
   __shared__ __attribute__((aligned(16))) _Float16 lds[2][APL * MTL * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) float xsl[2][K4 ? KS / 32 : 1][MTL];   // two-level: 8 X per row, sub-block
   __shared__ int arow[MTL];
   if (tid < MTL) {
     int src = -1;
@@ -2074,18 +2084,24 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     rb[i] = weight_rsrc(eq + i * mbytes + (size_t)nt * NKB * TILE, NKB * TILE);
-    rs[i] = weight_rsrc(es + i * mscales + (size_t)16 * nt * NG, 16 * NG * 4);
+    rs[i] = K4 ? weight_rsrc((const uint8_t*)es + ((size_t)i * inter + 16 * nt) * NSB * Q4K_REC, 16 * NSB * Q4K_REC)
+               : weight_rsrc(es + i * mscales + (size_t)16 * nt * NG, 16 * NG * 4);
   }
   const __amdgpu_buffer_rsrc_t ra =
       weight_rsrc(F32 ? (const void*)a.af : (const void*)a.ab, (uint32_t)a.a_rows * H * (F32 ? 4 : 2));
 
   uint4 bq[D][2][NB];
-  float sq[D][2][GPS];
-  auto load_b = [&](uint4 (&bd)[2][NB], float (&sd)[2][GPS], int st) {
+  float sq[D][2][K4 ? 1 : GPS];
+  u32x4 rq[K4 ? D : 1][2];                 // two-level: the row's record of the stage's super-block
+  auto load_b = [&](uint4 (&bd)[2][NB], float (&sd)[2][K4 ? 1 : GPS], u32x4 (&rd)[2], int st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      if constexpr (K4) {
+        rd[i] = __builtin_amdgcn_raw_buffer_load_b128(rs[i], (uint32_t)(r * NSB + st / 2) * Q4K_REC, 0, 0);
+      } else {
 #pragma unroll
-      for (int g = 0; g < GPS; ++g) sd[i][g] = wload4(rs[i], (uint32_t)(r * NG + st * GPS + g) * 4);
+        for (int g = 0; g < GPS; ++g) sd[i][g] = wload4(rs[i], (uint32_t)(r * NG + st * GPS + g) * 4);
+      }
 #pragma unroll
       for (int h = 0; h < NB; ++h) bd[i][h] = wload16(rb[i], (uint32_t)(st * NB + h) * TILE + lane * 16);
     }
@@ -2101,7 +2117,7 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
     ar[0] = wload16(ra, off);
     if (F32) ar[APL - 1] = wload16(ra, off + 16);
   };
-  auto store_a1 = [&](_Float16* l, const uint4 (&ar)[APL]) {
+  auto store_a1 = [&](_Float16* l, float* xl, const uint4 (&ar)[APL]) {
     const int row = tid >> 4, kk = 8 * (tid & 15);
     float v[8];
     if (F32) {
@@ -2124,6 +2140,13 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
       hi[p] = xh;
       lo[p] = (_Float16)(x - (float)xh);
     }
+    if constexpr (K4) {
+      // 8 x the sub-block sum: the 4 threads of a 32-column sub-block are 4
+      // consecutive lanes (whole waves are active or idle together)
+      float xs = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+      xs = group_sum<4>(xs);
+      if (a_act && (tid & 3) == 0) xl[((tid & 15) >> 2) * MTL + row] = 8.0f * xs;
+    }
     if (!a_act) return;
     *(half8*)(l + row * LDS_ROW + kk) = hi;
     if (SPLIT) *(half8*)(l + MTL * LDS_ROW + row * LDS_ROW + kk) = lo;
@@ -2142,8 +2165,8 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
 #pragma unroll
   for (int s0 = 0; s0 < 3; ++s0) fetch_a1(A[s0], s0 * KS, s0 < NSTAGE);
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
-  store_a1(lds[0], A[0]);
+  for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], rq[K4 ? d : 0], d);
+  store_a1(lds[0], &xsl[0][0][0], A[0]);
 
 #pragma unroll 1
   for (int s0 = 0; s0 < NSTAGE; s0 += SB) {
@@ -2152,10 +2175,16 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
     const int st = s0 + d;
     if (SB != NSTAGE && st >= NSTAGE) break;
     __syncthreads();   // lds[st & 1] holds A(st); lds[(st + 1) & 1] is free
-    if (st + 1 < NSTAGE) store_a1(lds[(d + 1) & 1], A[(d + 1) % 3]);
+    if (st + 1 < NSTAGE) store_a1(lds[(d + 1) & 1], &xsl[(d + 1) & 1][0][0], A[(d + 1) % 3]);
     if (st + 3 < NSTAGE) fetch_a1(A[d % 3], (st + 3) * KS, true);
     const _Float16* la = lds[d & 1];
     const int sl = d % D;
+    // two-level: this stage is half d % 2 of its super-block (s0 is even)
+    Q4kBytes fb[2];
+    if constexpr (K4) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fb[i] = q4k_bytes(rq[sl][i]);
+    }
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
       const bool first = (c % CPG) == 0, last = (c % CPG) == CPG - 1;
@@ -2180,15 +2209,30 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
         }
       }
       if (last) {
+        if constexpr (K4) {
+          const int j = 4 * (d & 1) + c;          // sub-block within the super-block
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const float sv = f16_bits_value(rq[sl][i][0] & 0xFFFFu) * byte_value(fb[i].sc[j / 4], j % 4);
+            const float mdm = f16_bits_value(rq[sl][i][0] >> 16) * byte_value(fb[i].m[j / 4], j % 4);
+            const float bv = fmaf(-0.125f, mdm, sv);   // per unit of 8X: s - dmin m / 8
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms) {
+              const float4v x8 = *(const float4v*)&xsl[d & 1][c][ms * 16 + 4 * q4];
+              acc[i][ms] += sv * ctmp[i][ms] + bv * x8;
+            }
+          }
+        } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const float sv = sq[sl][i][c / CPG];
 #pragma unroll
           for (int ms = 0; ms < MS; ++ms) acc[i][ms] += sv * ctmp[i][ms];
         }
+        }
       }
     }
-    if (st + D < NSTAGE) load_b(bq[sl], sq[sl], st + D);   // the slot just used takes stage st + D
+    if (st + D < NSTAGE) load_b(bq[sl], sq[sl], rq[K4 ? sl : 0], st + D);   // the slot just used takes stage st + D
   }
   }
 #pragma unroll
@@ -2210,9 +2254,12 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
 // 16-byte lane word).  Same software pipeline as gate/up.
 template <int BITS, int G, int INTER, int KSPLIT, int MTL>
 __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
+  constexpr bool K4 = G == Q4K;            // two-level format (see gateup_small_body)
+  static_assert(!K4 || BITS == 4, "two-level codes are 4-bit");
+  constexpr int GG = K4 ? Q4K_SUB : G;
   constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4, MS = MTL / 16;
   constexpr int NSW = NSUB / 2;             // n-subtiles per wave (half a row tile)
-  constexpr int CPG = G / 32, GPS = KS / G, NSTAGE = INTER / KS / KSPLIT;
+  constexpr int CPG = GG / 32, GPS = KS / GG, NSTAGE = INTER / KS / KSPLIT;
   static_assert((INTER / KS) % KSPLIT == 0, "K halves of whole stages");
   constexpr int D = 4;
   const int inter = INTER;
@@ -2223,30 +2270,48 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
             q4 = lane >> 4;
   __shared__ __attribute__((aligned(16))) _Float16 lds[2][2 * MTL * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) float xsl[2][K4 ? KS / 32 : 1][MTL];   // two-level: 8 X per row, sub-block
   __shared__ int arow[MTL];
   if (tid < MTL) arow[tid] = tid < ti.nrows ? (a.shared ? ti.row0 + tid : ti.pbase + tid) : -1;
   const int e = wave_uniform(ti.e);
   const size_t mbytes = matrix_bytes(BITS, inter, H);
-  const int ngk = inter / G;
+  const int ngk = inter / GG;
   const int rt = 4 * cb + (wv >> 1), hh = wv & 1;
   const __amdgpu_buffer_rsrc_t rb = weight_rsrc(a.w.q + (size_t)e * a.w.e_bytes + 2 * mbytes, (uint32_t)mbytes);
+  // two-level: d | dmin words [super-block][slot] and sc | m << 8 halfwords
+  // [sub-block][slot], slot (rt, r, j) = row DR rt + 16 j + r
+  const uint8_t* dmeta = (const uint8_t*)(a.w.s + (size_t)e * a.w.e_scales) + q4k_rec_bytes(inter);
   const __amdgpu_buffer_rsrc_t rs =
-      weight_rsrc(a.w.s + (size_t)e * a.w.e_scales + 2 * (size_t)inter * (H / G), (uint32_t)ngk * H * 4);
+      K4 ? weight_rsrc(dmeta, (uint32_t)q4k_dd_bytes(inter))
+         : weight_rsrc(a.w.s + (size_t)e * a.w.e_scales + 2 * (size_t)inter * (H / GG), (uint32_t)ngk * H * 4);
+  const __amdgpu_buffer_rsrc_t rsm = weight_rsrc(dmeta + q4k_dd_bytes(inter), (uint32_t)ngk * H * 2);
   const __amdgpu_buffer_rsrc_t ra = weight_rsrc(a.af, (uint32_t)a.a_rows * inter * 4);
+  const uint32_t slot0 = ((uint32_t)rt * 16 + r) * 4 + NSW * hh;   // this lane's first row slot
 
   // this wave's half of each 16-byte lane word of a down tile: words 2hh, 2hh+1
   uint2 bq[D][KS / 32];
   float sq[D][GPS][NSW];
-  auto load_b = [&](uint2 (&bd)[KS / 32], float (&sd)[GPS][NSW], int st) {
+  uint2 dq[K4 ? D : 1];                    // two-level: d | dmin of the lane's NSW rows
+  uint32_t mq[K4 ? D : 1][GPS];            // ... and their sc | m << 8 halfwords per sub-block
+  auto load_b = [&](uint2 (&bd)[KS / 32], float (&sd)[GPS][NSW], uint2& dd, uint32_t (&mm)[GPS], int st) {
+    if constexpr (K4) {
+      static_assert(NSW == 2 && Q4K_SB == 2 * KS, "two rows per lane, two stages per super-block");
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, (((uint32_t)(s0 + st) / 2) * H + slot0) * 4, 0, 0);
+      dd = make_uint2(v[0], v[1]);
 #pragma unroll
-    for (int g = 0; g < GPS; ++g) {
-      const uint32_t so = ((((uint32_t)((s0 + st) * GPS + g) * NRT + rt) * 16 + r) * NSUB + NSW * hh) * 4;
-      if (NSW == 2) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0);
-        sd[g][0] = __uint_as_float(v[0]);
-        sd[g][NSW - 1] = __uint_as_float(v[1]);
-      } else {
-        sd[g][0] = wload4(rs, so);
+      for (int g = 0; g < GPS; ++g)
+        mm[g] = __builtin_amdgcn_raw_buffer_load_b32(rsm, ((uint32_t)((s0 + st) * GPS + g) * H + slot0) * 2, 0, 0);
+    } else {
+#pragma unroll
+      for (int g = 0; g < GPS; ++g) {
+        const uint32_t so = ((((uint32_t)((s0 + st) * GPS + g) * NRT + rt) * 16 + r) * NSUB + NSW * hh) * 4;
+        if (NSW == 2) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0);
+          sd[g][0] = __uint_as_float(v[0]);
+          sd[g][NSW - 1] = __uint_as_float(v[1]);
+        } else {
+          sd[g][0] = wload4(rs, so);
+        }
       }
     }
 #pragma unroll
@@ -2266,7 +2331,7 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
     ar[0] = wload16(ra, off);
     ar[1] = wload16(ra, off + 16);
   };
-  auto store_a1 = [&](_Float16* l, const uint4 (&ar)[2]) {
+  auto store_a1 = [&](_Float16* l, float* xl, const uint4 (&ar)[2]) {
     const int row = tid >> 4, kk = 8 * (tid & 15);
     const float v[8] = {__uint_as_float(ar[0].x), __uint_as_float(ar[0].y), __uint_as_float(ar[0].z),
                         __uint_as_float(ar[0].w), __uint_as_float(ar[1].x), __uint_as_float(ar[1].y),
@@ -2278,6 +2343,11 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
       const _Float16 xh = (_Float16)x;
       hi[p] = xh;
       lo[p] = (_Float16)(x - (float)xh);
+    }
+    if constexpr (K4) {
+      float xs = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+      xs = group_sum<4>(xs);
+      if (a_act && (tid & 3) == 0) xl[((tid & 15) >> 2) * MTL + row] = 8.0f * xs;
     }
     if (!a_act) return;
     *(half8*)(l + row * LDS_ROW + kk) = hi;
@@ -2295,13 +2365,13 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
 #pragma unroll
   for (int sp = 0; sp < 3; ++sp) fetch_a1(A[sp], (s0 + sp) * KS, sp < NSTAGE);
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], d);
-  store_a1(lds[0], A[0]);
+  for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], dq[K4 ? d : 0], mq[K4 ? d : 0], d);
+  store_a1(lds[0], &xsl[0][0][0], A[0]);
 
 #pragma unroll
   for (int st = 0; st < NSTAGE; ++st) {
     __syncthreads();
-    if (st + 1 < NSTAGE) store_a1(lds[(st + 1) & 1], A[(st + 1) % 3]);
+    if (st + 1 < NSTAGE) store_a1(lds[(st + 1) & 1], &xsl[(st + 1) & 1][0][0], A[(st + 1) % 3]);
     if (st + 3 < NSTAGE) fetch_a1(A[st % 3], (s0 + st + 3) * KS, true);
     const _Float16* la = lds[st & 1];
     const int sl = st % D;
@@ -2328,15 +2398,30 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
         }
       }
       if (last) {
+        if constexpr (K4) {
+#pragma unroll
+          for (int j = 0; j < NSW; ++j) {
+            const uint32_t ddw = j == 0 ? dq[sl].x : dq[sl].y;
+            const float sv = f16_bits_value(ddw & 0xFFFFu) * byte_value(mq[sl][c], 2 * j);
+            const float mdm = f16_bits_value(ddw >> 16) * byte_value(mq[sl][c], 2 * j + 1);
+            const float bv = fmaf(-0.125f, mdm, sv);   // per unit of 8X: s - dmin m / 8
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms) {
+              const float4v x8 = *(const float4v*)&xsl[st & 1][c][ms * 16 + 4 * q4];
+              acc[j][ms] += sv * ctmp[j][ms] + bv * x8;
+            }
+          }
+        } else {
 #pragma unroll
         for (int j = 0; j < NSW; ++j) {
           const float sj = sq[sl][c / CPG][j];
 #pragma unroll
           for (int ms = 0; ms < MS; ++ms) acc[j][ms] += sj * ctmp[j][ms];
         }
+        }
       }
     }
-    if (st + D < NSTAGE) load_b(bq[sl], sq[sl], st + D);
+    if (st + D < NSTAGE) load_b(bq[sl], sq[sl], dq[K4 ? sl : 0], mq[K4 ? sl : 0], st + D);
   }
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
@@ -2550,6 +2635,22 @@ static void down_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipSt
     else if (a.w.inter == IS) hipLaunchKernelGGL((grouped_down_kernel<BITS, G, IS>), grid, dim3(GT), 0, s, a);
     else hipLaunchKernelGGL((grouped_down_kernel<BITS, G, I>), grid, dim3(GT), 0, s, a);
   }
+}
+
+// Two-level format: the 32-row small tiles at every token count.
+hipError_t launch_grouped_q4k(const GroupedArgs& a, int max_tiles, bool down, hipStream_t s) {
+  if (!down) {
+    const dim3 grid(max_tiles * (a.w.inter / 128));
+    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<4, true, Q4K, MT_SMALL>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gateup_small_kernel<4, false, Q4K, MT_SMALL>), grid, dim3(512), 0, s, a);
+  } else {
+    const dim3 grid(max_tiles * (H / (4 * down_rows(4))));
+    if (a.w.inter == IS && a.ksplit == 2)
+      hipLaunchKernelGGL((down_small_kernel<4, Q4K, IS, 2, MT_SMALL>), dim3(2 * grid.x), dim3(512), 0, s, a);
+    else if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<4, Q4K, IS, 1, MT_SMALL>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((down_small_kernel<4, Q4K, I, 1, MT_SMALL>), grid, dim3(512), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {

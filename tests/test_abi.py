@@ -222,10 +222,7 @@ def test_forward_validation_codes(lib):
     assert _fwd(lib, T=0) == 0                               # empty call: nothing enqueued
     assert _fwd(lib, T=0, x=None, y=None, ids=None, w=None) == 0
     assert _fwd(lib, T=0, ws=None) == 1
-    # the two-level format: 4-bit codes only, per-token path only (at most 64 tokens, not forced grouped)
-    assert _fwd(lib, eg=B.MOE_Q4K, T=65) == 3
-    assert _fwd(lib, sb=4, sg=B.MOE_Q4K, T=65) == 3
-    assert _fwd(lib, eg=B.MOE_Q4K, flags=B.MOE_FORCE_GROUPED) == 3
+    # the two-level format has 4-bit codes
     assert _fwd(lib, eb=8, eg=B.MOE_Q4K) == 3
     assert _fwd(lib, sg=B.MOE_Q4K) == 3                     # shared codes are int8 here
     assert _fwd(lib, eg=B.MOE_Q4K, T=0) == 0

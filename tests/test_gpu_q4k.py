@@ -1,7 +1,7 @@
 """GPU two-level 4-bit (Q4_K-style) experts vs the float64 oracle, through the
-C ABI (needs an MI355X): the per-token layer path and the persistent decode
-step, with routed experts (and, in one case, the shared expert too) in the
-format."""
+C ABI (needs an MI355X): the per-token layer path, the grouped path and the
+persistent decode step, with the routed experts (and in some cases the
+shared expert too) in the format."""
 import dataclasses
 import functools
 import sys
@@ -57,6 +57,37 @@ def test_q4k_layer(lib, T, both):
     torch.cuda.synchronize()
     ratio, near = check_layer(x, layer_of(both, 0), ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy())
     say(f"  err/rms {ratio:.2e} near-ties {near}")
+
+
+@pytest.mark.parametrize("both", [False, True])
+@pytest.mark.parametrize("T", [5, 65, 300, 1000])
+def test_q4k_grouped(lib, T, both):
+    """The grouped path (forced below its default token count), f32 input:
+    32-row tiles over several tiles per expert and a ragged last tile."""
+    from quantized_expert_ffn_moe_amd import binding as B
+    say(f"grouped T={T} shared two-level={both}")
+    x, xt = tokens(T, batch=100 + T)
+    ids, w, y = B.layer(xt, packed_of(both, 0), B.MOE_FORCE_GROUPED)
+    torch.cuda.synchronize()
+    ratio, near = check_layer(x, layer_of(both, 0), ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy())
+    say(f"  err/rms {ratio:.2e} near-ties {near}")
+
+
+def test_q4k_grouped_bf16_and_paths_agree(lib):
+    """bf16 activations on the grouped path, and the same 40 tokens through the
+    per-token path: both within the bar, identical routing."""
+    from quantized_expert_ffn_moe_amd import binding as B
+    x, xt = tokens(40, batch=7)
+    xb = xt.to(torch.bfloat16)
+    xv = xb.float().cpu().numpy().astype(np.float64)
+    res = []
+    for flags in (B.MOE_FORCE_GROUPED, B.MOE_FORCE_DECODE):
+        ids, w, y = B.layer(xb, packed_of(True, 2), flags)
+        torch.cuda.synchronize()
+        ratio, _ = check_layer(xv, layer_of(True, 2), ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy())
+        say(f"bf16 input, flags {flags}: err/rms {ratio:.2e}")
+        res.append(ids.cpu().numpy())
+    np.testing.assert_array_equal(res[0], res[1])
 
 
 def test_q4k_normalised_bf16_input(lib):
