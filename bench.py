@@ -116,7 +116,7 @@ def main():
     ap.add_argument("--group", type=int, default=64, choices=[32, 64, 128, 256],
                     help="decode: group size of the routed int4 experts (64 is the headline; 32 and 128 sweep "
                          "the group-size trade of metadata bytes against time; 256 = the two-level "
-                         "Q4_K-style format)")
+                         "Q4_K-style format); grouped workloads: 256 puts every expert in the two-level format")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
@@ -281,6 +281,11 @@ def bench_prefill(args):
     from synth import WORKLOADS, make_layer, make_tokens
 
     wl = WORKLOADS[{"batched32": 2, "prefill273": 3, "multipage2184": 4, "batch128": 5, "batch256": 6}[args.workload]]
+    if args.group == 256:
+        # the same workload with every expert (routed and shared) in the two-level format
+        from dataclasses import replace
+        from synth import QFmt
+        wl = replace(wl, routed=QFmt(4, 256), shared=QFmt(4, 256), name=wl.name + "_all_q4k")
     L = wl.n_layers
     layers = [make_layer(wl, li) for li in range(L)]
     packed = [B.pack_layer(layer) for layer in layers]

@@ -2048,13 +2048,17 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
   constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MTL / 16;
   constexpr int CPG = GG / 32, GPS = KS / GG, NG = H / GG;
   constexpr int NSB = H / Q4K_SB;          // two-level records per gate/up row
-  constexpr int D = GG == 32 ? 3 : (BITS == 4 ? 4 : 3);   // B stages in flight
+  // B stages in flight, and A stages fetched ahead into registers (AR - 1 of
+  // them beyond the one in LDS)
+  constexpr int D = K4 ? 2 : GG == 32 ? 3 : (BITS == 4 ? 4 : 3);
+  constexpr int AR = K4 ? 2 : 3;
   // With G = 32 every K step is its own scale group, and a fully unrolled
   // stage loop lets the compiler hoist matrix-core products far ahead of their
   // scale multiply (and spill them): there the stages run in blocks of 6 with
-  // a loop between the blocks.
-  constexpr int SB = GG == 32 ? 6 : NSTAGE;
-  static_assert(SB % D == 0 && SB % 6 == 0 || SB == NSTAGE, "ring slots fixed within a block");
+  // a loop between the blocks (blocks of 2 and shallower rings for the
+  // two-level format, whose records and sums would spill otherwise).
+  constexpr int SB = K4 ? 2 : GG == 32 ? 6 : NSTAGE;
+  static_assert((SB % D == 0 && SB % AR == 0 && SB % 2 == 0) || SB == NSTAGE, "ring slots fixed within a block");
   static_assert(!K4 || (SB % 2 == 0 && Q4K_SB == 2 * KS), "a stage is a fixed half of a super-block");
   constexpr bool F32 = SPLIT;
   constexpr int APL = SPLIT ? 2 : 1;
@@ -2161,9 +2165,9 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
 
   // Fully unrolled stage loop: every ring slot is a fixed register set, so no
   // value is copied while its load is still in flight.
-  uint4 A[3][APL];   // A(s) lives in slot s % 3 until it is stored to LDS
+  uint4 A[AR][APL];   // A(s) lives in slot s % AR until it is stored to LDS
 #pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0) fetch_a1(A[s0], s0 * KS, s0 < NSTAGE);
+  for (int s0 = 0; s0 < AR; ++s0) fetch_a1(A[s0], s0 * KS, s0 < NSTAGE);
 #pragma unroll
   for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], rq[K4 ? d : 0], d);
   store_a1(lds[0], &xsl[0][0][0], A[0]);
@@ -2175,8 +2179,8 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
     const int st = s0 + d;
     if (SB != NSTAGE && st >= NSTAGE) break;
     __syncthreads();   // lds[st & 1] holds A(st); lds[(st + 1) & 1] is free
-    if (st + 1 < NSTAGE) store_a1(lds[(d + 1) & 1], &xsl[(d + 1) & 1][0][0], A[(d + 1) % 3]);
-    if (st + 3 < NSTAGE) fetch_a1(A[d % 3], (st + 3) * KS, true);
+    if (st + 1 < NSTAGE) store_a1(lds[(d + 1) & 1], &xsl[(d + 1) & 1][0][0], A[(d + 1) % AR]);
+    if (st + AR < NSTAGE) fetch_a1(A[d % AR], (st + AR) * KS, true);
     const _Float16* la = lds[d & 1];
     const int sl = d % D;
     // two-level: this stage is half d % 2 of its super-block (s0 is even)
@@ -2261,7 +2265,13 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
   constexpr int NSW = NSUB / 2;             // n-subtiles per wave (half a row tile)
   constexpr int CPG = GG / 32, GPS = KS / GG, NSTAGE = INTER / KS / KSPLIT;
   static_assert((INTER / KS) % KSPLIT == 0, "K halves of whole stages");
-  constexpr int D = 4;
+  // B stages in flight, A stages ahead (as in gateup_small_body), and the
+  // stage block: the whole K range unrolled, or for the two-level format
+  // blocks of 2 stages with a loop between them (fewer registers)
+  constexpr int D = K4 ? 2 : 4;
+  constexpr int AR = K4 ? 2 : 3;
+  constexpr int SB = K4 ? 2 : NSTAGE;
+  static_assert((SB % D == 0 && SB % AR == 0 && SB % 2 == 0) || SB == NSTAGE, "ring slots fixed within a block");
   const int inter = INTER;
   const int kh = bid % KSPLIT, tb = bid / KSPLIT, s0 = kh * NSTAGE;   // K part kh
   const int tile = tb / NCB, cb = tb % NCB;
@@ -2361,20 +2371,24 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
     for (int ms = 0; ms < MS; ++ms) { acc[j][ms] = float4v{0, 0, 0, 0}; ctmp[j][ms] = float4v{0, 0, 0, 0}; }
   __syncthreads();   // arow
 
-  uint4 A[3][2];
+  uint4 A[AR][2];
 #pragma unroll
-  for (int sp = 0; sp < 3; ++sp) fetch_a1(A[sp], (s0 + sp) * KS, sp < NSTAGE);
+  for (int sp = 0; sp < AR; ++sp) fetch_a1(A[sp], (s0 + sp) * KS, sp < NSTAGE);
 #pragma unroll
   for (int d = 0; d < D; ++d) load_b(bq[d], sq[d], dq[K4 ? d : 0], mq[K4 ? d : 0], d);
   store_a1(lds[0], &xsl[0][0][0], A[0]);
 
+#pragma unroll 1
+  for (int b0 = 0; b0 < NSTAGE; b0 += SB) {
 #pragma unroll
-  for (int st = 0; st < NSTAGE; ++st) {
+  for (int d = 0; d < SB; ++d) {
+    const int st = b0 + d;
+    if (SB != NSTAGE && st >= NSTAGE) break;
     __syncthreads();
-    if (st + 1 < NSTAGE) store_a1(lds[(st + 1) & 1], &xsl[(st + 1) & 1][0][0], A[(st + 1) % 3]);
-    if (st + 3 < NSTAGE) fetch_a1(A[st % 3], (s0 + st + 3) * KS, true);
-    const _Float16* la = lds[st & 1];
-    const int sl = st % D;
+    if (st + 1 < NSTAGE) store_a1(lds[(d + 1) & 1], &xsl[(d + 1) & 1][0][0], A[(d + 1) % AR]);
+    if (st + AR < NSTAGE) fetch_a1(A[d % AR], (s0 + st + AR) * KS, true);
+    const _Float16* la = lds[d & 1];
+    const int sl = d % D;
 #pragma unroll
     for (int c = 0; c < KS / 32; ++c) {
       const bool first = (c % CPG) == 0, last = (c % CPG) == CPG - 1;
@@ -2407,7 +2421,7 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
             const float bv = fmaf(-0.125f, mdm, sv);   // per unit of 8X: s - dmin m / 8
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms) {
-              const float4v x8 = *(const float4v*)&xsl[st & 1][c][ms * 16 + 4 * q4];
+              const float4v x8 = *(const float4v*)&xsl[d & 1][c][ms * 16 + 4 * q4];
               acc[j][ms] += sv * ctmp[j][ms] + bv * x8;
             }
           }
@@ -2422,6 +2436,7 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
       }
     }
     if (st + D < NSTAGE) load_b(bq[sl], sq[sl], dq[K4 ? sl : 0], mq[K4 ? sl : 0], st + D);
+  }
   }
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
