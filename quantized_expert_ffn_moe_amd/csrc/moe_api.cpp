@@ -382,7 +382,7 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   // tile shape: 32-row tiles while the experts see few rows each (about 64 or
   // fewer on average), 64-row tiles beyond
   const bool small = two_level || (size_t)T * TOPK <= (size_t)SMALL_TILE_MAX_SLOTS;
-  const bool pair = !two_level && small && small_pair_available(rw.bits, rw.group, sw.bits, sw.group);
+  const bool pair = small && small_pair_available(rw.bits, rw.group, sw.bits, sw.group);
   const int mtl = !small ? MT : (pair && (size_t)T * TOPK <= TINY_TILE_MAX_SLOTS) ? MT_TINY : MT_SMALL;
   const int max_tiles = (int)((size_t)T * TOPK / mtl) + E + 1;
   HistArgs ha;
@@ -407,7 +407,10 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   dr.out = ws.ysorted;
   ds.af = ws.h_shared; ds.ab = nullptr; ds.shared = 1; ds.a_by_token = 0; ds.a_rows = T; ds.w = sw; ds.out = ws.ys;
   ds.ksplit = small ? 2 : 1;
-  if (two_level) {
+  if (pair && launch_small_pair(gr, max_tiles, gs, s_tiles, false, mtl, s)) {
+    if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
+    if (!launch_small_pair(dr, max_tiles, ds, s_tiles, true, mtl, s) || hipGetLastError() != hipSuccess) return MOE_E_HIP;
+  } else if (two_level) {
     auto gateup = [&](const GroupedArgs& g, int tiles) {
       return g.w.group == Q4K ? launch_grouped_q4k(g, tiles, false, s) : launch_grouped_gateup(g, tiles, true, s);
     };
@@ -417,9 +420,6 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
     if (gateup(gr, max_tiles) != hipSuccess || gateup(gs, s_tiles) != hipSuccess ||
         down(dr, max_tiles) != hipSuccess || down(ds, s_tiles) != hipSuccess)
       return MOE_E_HIP;
-  } else if (pair && launch_small_pair(gr, max_tiles, gs, s_tiles, false, mtl, s)) {
-    if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
-    if (!launch_small_pair(dr, max_tiles, ds, s_tiles, true, mtl, s) || hipGetLastError() != hipSuccess) return MOE_E_HIP;
   } else {
     if (launch_grouped_gateup(gr, max_tiles, small, s) != hipSuccess) return MOE_E_HIP;
     if (launch_grouped_gateup(gs, s_tiles, small, s) != hipSuccess) return MOE_E_HIP;

@@ -2703,14 +2703,18 @@ static void pair_dispatch_h(const GroupedArgs& r, int r_tiles, const GroupedArgs
 }
 
 bool small_pair_available(int rbits, int rgroup, int sbits, int sgroup) {
-  return (rbits == sbits && rgroup == sgroup) || (rbits == 4 && rgroup == 64 && sbits == 8 && sgroup == 128);
+  return (rbits == sbits && rgroup == sgroup) ||
+         (rbits == 4 && (rgroup == 64 || rgroup == Q4K) && sbits == 8 && sgroup == 128);
 }
 
 bool launch_small_pair(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down, int mtl,
                        hipStream_t s) {
   const int rb = r.w.bits, rg = r.w.group, sb = sh.w.bits, sg = sh.w.group;
   if (!small_pair_available(rb, rg, sb, sg)) return false;
-  if (rb == sb && rg == sg) {
+  if (rg == Q4K) {
+    if (sg == Q4K) pair_dispatch_h<4, Q4K, 4, Q4K>(r, r_tiles, sh, s_tiles, down, mtl, s);
+    else pair_dispatch_h<4, Q4K, 8, 128>(r, r_tiles, sh, s_tiles, down, mtl, s);
+  } else if (rb == sb && rg == sg) {
     const int key = (rb == 8) * 3 + (rg == 64) + 2 * (rg == 128);
     switch (key) {
       case 0: pair_dispatch_h<4, 32, 4, 32>(r, r_tiles, sh, s_tiles, down, mtl, s); break;
