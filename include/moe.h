@@ -151,7 +151,7 @@ moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t*
  *   codes_out: moe_expert_code_bytes(4, inter) bytes, the int4 tile layout
  *     above holding q - 8 (so W = s (q - 8) + beta with s = d sc and
  *     beta = 8 s - dmin m per sub-block);
- *   meta_out: 4 * moe_expert_scale_count(MOE_Q4K, inter) bytes:
+ *   meta_out: 4 * moe_expert_scale_count(MOE_Q4K, inter) bytes, 4-byte aligned:
  *     gate records [inter][5] then up records [inter][5], 16 bytes each (row,
  *     super-block): w0 = d | dmin << 16; byte j (j < 4) of w1 = sc_j |
  *     (m_j >> 4) << 6, of w2 = sc_{4+j} | (m_{4+j} >> 4) << 6, of w3 =
@@ -171,8 +171,9 @@ moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t*
  * two-level expert set runs 32-row tiles without the fused shared/routed
  * launches).
  * Returns MOE_E_NULLPTR for a missing pointer, MOE_E_SHAPE for an
- * intermediate size other than 896 or 1792, MOE_E_FORMAT for a field out of
- * range (nothing is written then).
+ * intermediate size other than 896 or 1792, MOE_E_ALIGN for a meta_out not
+ * 4-byte aligned, MOE_E_FORMAT for a field out of range (nothing is written
+ * then).
  * ------------------------------------------------------------------------ */
 typedef struct {
   const uint8_t* q;      /* [N][K] codes 0..15 */

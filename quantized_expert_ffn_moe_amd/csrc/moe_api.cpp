@@ -264,6 +264,7 @@ moe_status_t moe_pack_expert_q4k(const moe_q4k_matrix_t* gate, const moe_q4k_mat
                                  const moe_q4k_matrix_t* down, int32_t inter, void* codes_out, void* meta_out) {
   if (!gate || !up || !down || !codes_out || !meta_out) return MOE_E_NULLPTR;
   if (inter != I && inter != IS) return MOE_E_SHAPE;
+  if ((uintptr_t)meta_out & 3u) return MOE_E_ALIGN;
   if (!gate->q || !gate->d || !gate->dmin || !gate->sc || !gate->m || !up->q || !up->d || !up->dmin || !up->sc ||
       !up->m || !down->q || !down->d || !down->dmin || !down->sc || !down->m)
     return MOE_E_NULLPTR;
