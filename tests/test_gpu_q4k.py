@@ -141,3 +141,45 @@ def test_q4k_decode_step_11_layers(lib, both):
     b = _decode(both, 11, xt, ws)
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u, v)
+
+
+@pytest.mark.parametrize("both", [False, True])
+def test_q4k_grouped_chain_sampled(lib, both):
+    """300 tokens through 3 two-level layers in place (RMSNorm + residual inside
+    each call, grouped path), every layer checked on 12 sampled tokens against
+    the oracle fed the GPU's own residual stream."""
+    from quantized_expert_ffn_moe_amd import binding as B
+    T, L = 300, 3
+    x, xt = tokens(T, batch=31)
+    h = xt.clone()
+    flags = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE
+    ws = B.workspace(T)
+    ids = torch.empty(T, 6, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, 6, dtype=torch.float32, device="cuda")
+    sample = np.sort(np.random.default_rng(3).choice(T, 12, replace=False))
+    for li in range(L):
+        h_in = h[sample].cpu().numpy().astype(np.float64)
+        B.moe_layer_forward(h, packed_of(both, li), h, ids, w, ws, flags)
+        torch.cuda.synchronize()
+        out = h[sample].cpu().numpy().astype(np.float64) - h_in
+        ratio, near = check_layer(O.rmsnorm(h_in, NORM_EPS), layer_of(both, li), ids.cpu().numpy()[sample],
+                                  w.cpu().numpy()[sample], out)
+        say(f"  grouped chain layer {li + 1}: err/rms {ratio:.2e} near-ties {near}")
+
+
+def test_q4k_decode_step_bf16_input(lib):
+    """The decode step with a bf16 input row (the residual stream widened from
+    bf16 by the reducers)."""
+    from quantized_expert_ffn_moe_amd import binding as B
+    x, xt = tokens(1, batch=9)
+    xb = xt.to(torch.bfloat16)
+    xv = xb.float().cpu().numpy().astype(np.float64)
+    ws = B.decode_workspace()
+    ids, w, y = _decode(False, 2, xb, ws)
+    z1 = O.rmsnorm(xv, NORM_EPS)
+    ids1, w1, y1 = _decode(False, 1, xb, ws)
+    check_layer(z1, layer_of(False, 0), ids1, w1, y1 - xv)
+    np.testing.assert_array_equal(ids[:1], ids1)
+    ratio, _ = check_layer(O.rmsnorm(y1.astype(np.float64), NORM_EPS), layer_of(False, 1), ids[1:], w[1:],
+                           y - y1)
+    say(f"bf16 input decode, layer 2: err/rms {ratio:.2e}")
