@@ -2214,17 +2214,12 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
       }
       if (last) {
         if constexpr (K4) {
-          const int j = 4 * (d & 1) + c;          // sub-block within the super-block
+          // sub-block 4 (d % 2) + c of the super-block: s = d sc
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            const float sv = f16_bits_value(rq[sl][i][0] & 0xFFFFu) * byte_value(fb[i].sc[j / 4], j % 4);
-            const float mdm = f16_bits_value(rq[sl][i][0] >> 16) * byte_value(fb[i].m[j / 4], j % 4);
-            const float bv = fmaf(-0.125f, mdm, sv);   // per unit of 8X: s - dmin m / 8
+            const float sv = f16_bits_value(rq[sl][i][0] & 0xFFFFu) * byte_value(fb[i].sc[d & 1], c);
 #pragma unroll
-            for (int ms = 0; ms < MS; ++ms) {
-              const float4v x8 = *(const float4v*)&xsl[d & 1][c][ms * 16 + 4 * q4];
-              acc[i][ms] += sv * ctmp[i][ms] + bv * x8;
-            }
+            for (int ms = 0; ms < MS; ++ms) acc[i][ms] += sv * ctmp[i][ms];
           }
         } else {
 #pragma unroll
@@ -2234,6 +2229,22 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
           for (int ms = 0; ms < MS; ++ms) acc[i][ms] += sv * ctmp[i][ms];
         }
         }
+      }
+    }
+    if constexpr (K4) {
+      // the minimum term of the stage's 4 sub-blocks in one f32 product per
+      // 16 x 16 output block: A = 8X [rows][sub-blocks], B = beta / 8 =
+      // s - dmin m / 8 [sub-blocks][columns] (lane (r, q4): row / column r,
+      // sub-block q4)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float bsc = (float)((fb[i].sc[d & 1] >> (8 * q4)) & 255u);
+        const float bm = (float)((fb[i].m[d & 1] >> (8 * q4)) & 255u);
+        const float bv = fmaf(-0.125f * f16_bits_value(rq[sl][i][0] >> 16), bm,
+                              f16_bits_value(rq[sl][i][0] & 0xFFFFu) * bsc);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+          acc[i][ms] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsl[d & 1][q4][ms * 16 + r], bv, acc[i][ms], 0, 0, 0);
       }
     }
     if (st + D < NSTAGE) load_b(bq[sl], sq[sl], rq[K4 ? sl : 0], st + D);   // the slot just used takes stage st + D
@@ -2417,13 +2428,8 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
           for (int j = 0; j < NSW; ++j) {
             const uint32_t ddw = j == 0 ? dq[sl].x : dq[sl].y;
             const float sv = f16_bits_value(ddw & 0xFFFFu) * byte_value(mq[sl][c], 2 * j);
-            const float mdm = f16_bits_value(ddw >> 16) * byte_value(mq[sl][c], 2 * j + 1);
-            const float bv = fmaf(-0.125f, mdm, sv);   // per unit of 8X: s - dmin m / 8
 #pragma unroll
-            for (int ms = 0; ms < MS; ++ms) {
-              const float4v x8 = *(const float4v*)&xsl[d & 1][c][ms * 16 + 4 * q4];
-              acc[j][ms] += sv * ctmp[j][ms] + bv * x8;
-            }
+            for (int ms = 0; ms < MS; ++ms) acc[j][ms] += sv * ctmp[j][ms];
           }
         } else {
 #pragma unroll
@@ -2433,6 +2439,20 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
           for (int ms = 0; ms < MS; ++ms) acc[j][ms] += sj * ctmp[j][ms];
         }
         }
+      }
+    }
+    if constexpr (K4) {
+      // the minimum term of the stage's sub-blocks as in gateup_small_body:
+      // lane (r, q4) supplies 8X of row r and beta / 8 of column r, sub-block q4
+      const uint32_t mw = q4 == 0 ? mq[sl][0] : q4 == 1 ? mq[sl][1] : q4 == 2 ? mq[sl][2] : mq[sl][3];
+#pragma unroll
+      for (int j = 0; j < NSW; ++j) {
+        const uint32_t ddw = j == 0 ? dq[sl].x : dq[sl].y;
+        const float bv = fmaf(-0.125f * f16_bits_value(ddw >> 16), byte_value(mw, 2 * j + 1),
+                              f16_bits_value(ddw & 0xFFFFu) * byte_value(mw, 2 * j));
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+          acc[j][ms] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsl[d & 1][q4][ms * 16 + r], bv, acc[j][ms], 0, 0, 0);
       }
     }
     if (st + D < NSTAGE) load_b(bq[sl], sq[sl], dq[K4 ? sl : 0], mq[K4 ? sl : 0], st + D);
