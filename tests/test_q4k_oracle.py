@@ -120,3 +120,37 @@ def test_layer_with_two_level_weights_matches_the_symmetric_layer():
     ids_t, w_t, y_t, _ = O.moe_layer(X, two, top_k=3)
     np.testing.assert_array_equal(ids_s, ids_t)
     np.testing.assert_allclose(y_t, y_s, rtol=1e-12, atol=1e-12)
+
+
+def _variant(q, d, dmin, sc, m, mistake):
+    """The two-level formula with one planted mistake (CPU only; never used
+    outside this test)."""
+    Q = np.asarray(q).astype(np.float64)
+    K = Q.shape[1]
+    D = np.repeat(O.f16_value(d), 256, axis=1)[:, :K]
+    Dm = np.repeat(O.f16_value(dmin), 256, axis=1)[:, :K]
+    S = np.repeat(np.asarray(sc, np.float64), 32, axis=1)
+    M = np.repeat(np.asarray(m, np.float64), 32, axis=1)
+    if mistake == "swap_d_dmin":
+        D, Dm = Dm, D
+    elif mistake == "swap_sc_m":
+        S, M = M, S
+    elif mistake == "plus_min":
+        return D * S * Q + Dm * M
+    elif mistake == "signed_codes":
+        Q = Q - 8
+    elif mistake == "sub_by_superblock":
+        S = np.repeat(np.asarray(sc, np.float64)[:, ::8], 256, axis=1)[:, :K]
+    return D * S * Q - Dm * M
+
+
+@pytest.mark.parametrize("mistake", ["swap_d_dmin", "swap_sc_m", "plus_min", "signed_codes", "sub_by_superblock"])
+def test_the_hand_worked_superblock_catches_planted_mistakes(mistake):
+    g = json.loads(GOLDEN.read_text())
+    K = g["row_length"]
+    args = ((np.arange(K) % 16).astype(np.uint8)[None, :], np.array([g["d_bits"]], np.uint16),
+            np.array([g["dmin_bits"]], np.uint16), np.array([g["sc"]], np.uint8), np.array([g["m"]], np.uint8))
+    W = _variant(*args, mistake)
+    assert any(W[0, e["k"]] != e["w"] for e in g["expected"]), mistake
+    # and the unmutated formula agrees with the oracle
+    np.testing.assert_array_equal(_variant(*args, "none"), O.dequantize_q4k(*args))
