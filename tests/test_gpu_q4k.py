@@ -183,3 +183,18 @@ def test_q4k_decode_step_bf16_input(lib):
     ratio, _ = check_layer(O.rmsnorm(y1.astype(np.float64), NORM_EPS), layer_of(False, 1), ids[1:], w[1:],
                            y - y1)
     say(f"bf16 input decode, layer 2: err/rms {ratio:.2e}")
+
+
+@pytest.mark.parametrize("both", [False, True])
+@pytest.mark.parametrize("T", [8, 85, 86, 682, 683])
+def test_q4k_grouped_switch_points(lib, T, both):
+    """Token counts on both sides of the grouped path's switches with two-level
+    experts: the two-pass router (8), 16- and 32-row fused tiles (512 slots)
+    and fused against unfused 32-row tiles (4096 slots)."""
+    from quantized_expert_ffn_moe_amd import binding as B
+    say(f"switch point T={T} shared two-level={both}")
+    x, xt = tokens(T, batch=200 + T)
+    ids, w, y = B.layer(xt, packed_of(both, 1))
+    torch.cuda.synchronize()
+    ratio, near = check_layer(x, layer_of(both, 1), ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy())
+    say(f"  err/rms {ratio:.2e} near-ties {near}")
