@@ -168,8 +168,8 @@ moe_status_t moe_pack_expert(const int8_t* gate, const int8_t* up, const int8_t*
  * bits = 4.
  * Every path takes this format: moe_decode_forward, and moe_layer_forward
  * on the per-token path and on the grouped path (there a call with a
- * two-level expert set runs 32-row tiles without the fused shared/routed
- * launches).
+ * two-level expert set runs the small 16- or 32-row tiles at every token
+ * count).
  * Returns MOE_E_NULLPTR for a missing pointer, MOE_E_SHAPE for an
  * intermediate size other than 896 or 1792, MOE_E_ALIGN for a meta_out not
  * 4-byte aligned, MOE_E_FORMAT for a field out of range (nothing is written

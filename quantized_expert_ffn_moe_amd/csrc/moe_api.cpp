@@ -334,8 +334,8 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   if ((flags & ~known) || (x_dtype != MOE_F32 && x_dtype != MOE_BF16)) return MOE_E_ARG;
   if ((flags & MOE_FORCE_DECODE) && (flags & MOE_FORCE_GROUPED)) return MOE_E_ARG;
   if ((flags & MOE_FORCE_DECODE) && T > DECODE_FORCE_MAX_T) return MOE_E_SHAPE;
-  // a two-level expert set runs on the grouped path's 32-row tiles (so does
-  // the other set of that call), without the fused shared/routed launches
+  // a call with a two-level expert set runs the grouped path's small (16- or
+  // 32-row) tiles at every token count, both expert sets alike
   const bool two_level = expert_group == Q4K || shared_group == Q4K;
   if ((flags & MOE_NORM_BF16) && !(flags & MOE_NORM_INPUT)) return MOE_E_ARG;
   if ((flags & MOE_NORM_INPUT) && x_dtype != MOE_F32) return MOE_E_ARG;
