@@ -2050,14 +2050,15 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
   constexpr int NSB = H / Q4K_SB;          // two-level records per gate/up row
   // B stages in flight, and A stages fetched ahead into registers (AR - 1 of
   // them beyond the one in LDS)
-  constexpr int D = K4 ? 2 : GG == 32 ? 3 : (BITS == 4 ? 4 : 3);
-  constexpr int AR = K4 ? 2 : 3;
-  // With G = 32 every K step is its own scale group, and a fully unrolled
-  // stage loop lets the compiler hoist matrix-core products far ahead of their
-  // scale multiply (and spill them): there the stages run in blocks of 6 with
-  // a loop between the blocks (blocks of 2 and shallower rings for the
-  // two-level format, whose records and sums would spill otherwise).
-  constexpr int SB = K4 ? 2 : GG == 32 ? 6 : NSTAGE;
+  constexpr int D = GG == 32 ? 2 : (BITS == 4 ? 4 : 3);
+  constexpr int AR = GG == 32 ? 2 : 3;
+  // With 32-column scale groups (G = 32 and the two-level format) every K
+  // step is its own scale group, and a fully unrolled stage loop lets the
+  // compiler hoist matrix-core products far ahead of their scale multiply and
+  // spill them to scratch: there the stages run in blocks of 2 with a loop
+  // between the blocks and 2-deep B and A rings (no scratch; blocks of 6 with
+  // 3-deep rings spilled up to 0.8 KiB per lane and ran 2.3-2.6x slower).
+  constexpr int SB = GG == 32 ? 2 : NSTAGE;
   static_assert((SB % D == 0 && SB % AR == 0 && SB % 2 == 0) || SB == NSTAGE, "ring slots fixed within a block");
   static_assert(!K4 || (SB % 2 == 0 && Q4K_SB == 2 * KS), "a stage is a fixed half of a super-block");
   constexpr bool F32 = SPLIT;
@@ -2277,11 +2278,11 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
   constexpr int CPG = GG / 32, GPS = KS / GG, NSTAGE = INTER / KS / KSPLIT;
   static_assert((INTER / KS) % KSPLIT == 0, "K halves of whole stages");
   // B stages in flight, A stages ahead (as in gateup_small_body), and the
-  // stage block: the whole K range unrolled, or for the two-level format
-  // blocks of 2 stages with a loop between them (fewer registers)
-  constexpr int D = K4 ? 2 : 4;
-  constexpr int AR = K4 ? 2 : 3;
-  constexpr int SB = K4 ? 2 : NSTAGE;
+  // stage block: the whole K range unrolled, or with 32-column scale groups
+  // blocks of 2 stages with a loop between them (no scratch)
+  constexpr int D = GG == 32 ? 2 : 4;
+  constexpr int AR = GG == 32 ? 2 : 3;
+  constexpr int SB = GG == 32 ? 2 : NSTAGE;
   static_assert((SB % D == 0 && SB % AR == 0 && SB % 2 == 0) || SB == NSTAGE, "ring slots fixed within a block");
   const int inter = INTER;
   const int kh = bid % KSPLIT, tb = bid / KSPLIT, s0 = kh * NSTAGE;   // K part kh
