@@ -382,7 +382,9 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
 
   // tile shape: 32-row tiles while the experts see few rows each (about 64 or
   // fewer on average), 64-row tiles beyond
-  const bool small = two_level || (size_t)T * TOPK <= (size_t)SMALL_TILE_MAX_SLOTS;
+  // (32-column scale groups, the two-level format included, stay on the small
+  // tiles at every token count: measured faster than the 64-row tiles there)
+  const bool small = two_level || rw.group == 32 || sw.group == 32 || (size_t)T * TOPK <= (size_t)SMALL_TILE_MAX_SLOTS;
   const bool pair = small && small_pair_available(rw.bits, rw.group, sw.bits, sw.group);
   const int mtl = !small ? MT : (pair && (size_t)T * TOPK <= TINY_TILE_MAX_SLOTS) ? MT_TINY : MT_SMALL;
   const int max_tiles = (int)((size_t)T * TOPK / mtl) + E + 1;

@@ -91,20 +91,21 @@ def test_tile_shape_boundaries(lib, wi, T):
     say(f"  err/rms {ratio:.2e} near-ties {near}")
 
 
-@pytest.mark.parametrize("T", [150, 700])
-def test_int8_g32_grouped(lib, T):
-    """int8 codes with groups of 32 (routed and shared) on the grouped path:
-    32-row fused tiles (150 tokens) and unfused small tiles (700 tokens)."""
+@pytest.mark.parametrize("bits,T", [(8, 150), (8, 700), (4, 1100)])
+def test_g32_grouped_small_tiles(lib, bits, T):
+    """Groups of 32 (routed and shared) on the grouped path, which keeps them on
+    the 32-row fused small tiles at every token count: int8 at 150 and 700
+    tokens, int4 at 1100 (6600 slots)."""
     from dataclasses import replace
     from quantized_expert_ffn_moe_amd import binding as B
     from synth import QFmt
-    wl = replace(WORKLOADS[2], routed=QFmt(8, 32), shared=QFmt(8, 32))
+    wl = replace(WORKLOADS[2], routed=QFmt(bits, 32), shared=QFmt(bits, 32))
     layer = make_layer(wl, 0)
     x, bits = make_tokens(wl, batch=5, n_tokens=T)
     xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
     ids, w, y = run(xt, B.pack_layer(layer), B.MOE_FORCE_GROUPED)
     ratio, near = check_layer(x.astype(np.float64), layer, ids, w, y)
-    say(f"int8 G32 T={T}: err/rms {ratio:.2e} near-ties {near}")
+    say(f"int{bits} G32 T={T}: err/rms {ratio:.2e} near-ties {near}")
 
 
 def test_mixed_formats_f32_input_grouped(lib):
