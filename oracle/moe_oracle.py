@@ -42,7 +42,11 @@ input is the RMSNorm output rounded to bf16 (nearest, ties to even).
 
 Parity pins: every function here is checked in ``tests/test_oracle.py`` against
 closed forms, brute force, library routines on special cases, invariants and a
-hand-worked fixture (``tests/golden/tiny_layer.json``); the two-level format in
+hand-worked fixture (``tests/golden/tiny_layer.json``); the residual chain
+against a hand-worked two-layer case (``tests/golden/tiny_chain.json``) that
+rejects planted wiring mistakes (norm of x at every layer, residual onto x,
+norm after the residual, eps outside the root, rounding before the norm); the
+two-level format in
 ``tests/test_q4k_oracle.py`` against a hand-worked super-block
 (``tests/golden/q4k_superblock.json``), its reduction to the symmetric format
 and its affine structure; none is unpinned.

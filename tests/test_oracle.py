@@ -302,3 +302,127 @@ def test_chain_single_layer_is_norm_then_residual():
     _, _, y, _ = O.moe_layer(z, layer, top_k=3)
     np.testing.assert_array_equal(h, x + y)
     np.testing.assert_array_equal(trace[0][2], z)
+
+
+# ---------------------------------------------------------------- hand-worked chain
+CHAIN_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tiny_chain.json")
+
+
+def _chain_fixture():
+    d = json.load(open(CHAIN_GOLDEN))
+    fmt = QFmt(d["bits"], d["group"])
+    layers = []
+    for raw in d["layers"]:
+        lay = {}
+        for k, v in raw.items():
+            if k == "router_w":
+                lay[k] = np.asarray(v, dtype=np.float64)
+            elif k.endswith("_q"):
+                lay[k] = np.asarray(v, dtype=np.int8)
+            else:
+                lay[k] = np.asarray(v, dtype=np.float32)
+        lay.update(router_b=None, routed_fmt=fmt, shared_fmt=fmt)
+        layers.append(lay)
+    return d, layers
+
+
+def test_tiny_chain_two_layers_hand_worked():
+    d, layers = _chain_fixture()
+    ex = d["expected"]
+    x = np.asarray(d["x"], dtype=np.float64)[None]
+    h, trace = O.moe_chain(x, layers, d["eps"], False, top_k=d["top_k"])
+    np.testing.assert_allclose(trace[0][2][0], ex["z0"], rtol=1e-15)
+    assert trace[0][0][0].tolist() == ex["ids1"]
+    np.testing.assert_allclose(trace[0][1][0], ex["w1"], rtol=1e-14)
+    np.testing.assert_allclose(trace[1][2][0], ex["z1"], rtol=1e-13)
+    assert trace[1][0][0].tolist() == ex["ids2"]
+    np.testing.assert_allclose(trace[1][1][0], ex["w2"], rtol=1e-13)
+    np.testing.assert_allclose(h[0], ex["h2"], rtol=1e-13, atol=1e-14)
+    h1, _ = O.moe_chain(x, layers[:1], d["eps"], False, top_k=d["top_k"])
+    np.testing.assert_allclose(h1[0], ex["h1"], rtol=1e-13, atol=1e-14)
+
+
+def test_tiny_chain_bf16_norm_hand_worked():
+    d, layers = _chain_fixture()
+    ex = d["expected"]["bf16_one_layer"]
+    x = np.asarray(d["x"], dtype=np.float64)[None]
+    h, trace = O.moe_chain(x, layers[:1], d["eps"], True, top_k=d["top_k"])
+    np.testing.assert_array_equal(trace[0][2][0], ex["z0"])
+    assert trace[0][0][0].tolist() == ex["ids1"]
+    np.testing.assert_allclose(trace[0][1][0], ex["w1"], rtol=1e-14)
+    np.testing.assert_allclose(h[0], ex["h1"], rtol=1e-13, atol=1e-14)
+
+
+def _planted_chains():
+    """Copies of the chain, each with one plausible wiring mistake."""
+    def norm_of_x_every_layer(x, layers, eps, bf16, k):
+        h = x.copy()
+        for lay in layers:
+            z = O.rmsnorm(x, eps)
+            z = O.bf16_round(z) if bf16 else z
+            h = h + O.moe_layer(z, lay, k)[2]
+        return h
+
+    def residual_onto_x(x, layers, eps, bf16, k):
+        h = x.copy()
+        for lay in layers:
+            z = O.rmsnorm(h, eps)
+            z = O.bf16_round(z) if bf16 else z
+            h = x + O.moe_layer(z, lay, k)[2]
+        return h
+
+    def norm_after_residual(x, layers, eps, bf16, k):
+        h = x.copy()
+        for lay in layers:
+            z = O.bf16_round(h) if bf16 else h
+            h = O.rmsnorm(h + O.moe_layer(z, lay, k)[2], eps)
+        return h
+
+    def residual_onto_z(x, layers, eps, bf16, k):
+        h = x.copy()
+        for lay in layers:
+            z = O.rmsnorm(h, eps)
+            z = O.bf16_round(z) if bf16 else z
+            h = z + O.moe_layer(z, lay, k)[2]
+        return h
+
+    def eps_outside_sqrt(x, layers, eps, bf16, k):
+        h = x.copy()
+        for lay in layers:
+            z = h / (np.sqrt(np.mean(h * h, axis=-1, keepdims=True)) + eps)
+            z = O.bf16_round(z) if bf16 else z
+            h = h + O.moe_layer(z, lay, k)[2]
+        return h
+
+    def no_residual(x, layers, eps, bf16, k):
+        h = x.copy()
+        for lay in layers:
+            z = O.rmsnorm(h, eps)
+            z = O.bf16_round(z) if bf16 else z
+            h = O.moe_layer(z, lay, k)[2]
+        return h
+
+    def rounding_before_norm(x, layers, eps, bf16, k):
+        h = x.copy()
+        for lay in layers:
+            z = O.rmsnorm(O.bf16_round(h) if bf16 else h, eps)
+            h = h + O.moe_layer(z, lay, k)[2]
+        return h
+
+    def layers_reversed(x, layers, eps, bf16, k):
+        return O.moe_chain(x, layers[::-1], eps, bf16, top_k=k)[0]
+
+    return [norm_of_x_every_layer, residual_onto_x, norm_after_residual, residual_onto_z,
+            eps_outside_sqrt, no_residual, rounding_before_norm, layers_reversed]
+
+
+@pytest.mark.parametrize("planted", _planted_chains(), ids=lambda f: f.__name__)
+def test_tiny_chain_catches_planted_wiring_mistakes(planted):
+    d, layers = _chain_fixture()
+    x = np.asarray(d["x"], dtype=np.float64)[None]
+    ex = d["expected"]
+    wrong2 = planted(x, layers, d["eps"], False, d["top_k"])[0]
+    wrong1b = planted(x, layers[:1], d["eps"], True, d["top_k"])[0]
+    caught = (not np.allclose(wrong2, ex["h2"], rtol=1e-9, atol=1e-9)
+              or not np.allclose(wrong1b, ex["bf16_one_layer"]["h1"], rtol=1e-9, atol=1e-9))
+    assert caught, planted.__name__
