@@ -221,6 +221,10 @@ size_t moe_workspace_bytes(int32_t n_tokens);
  * RMSNorm, which bounds it by sqrt(1280)) must be below 65504 in magnitude,
  * the f16 range; larger inputs give non-finite outputs there.  The per-token
  * path has no such limit.
+ * Inputs are meant to be finite.  A token whose row holds a NaN or an
+ * infinity gets non-finite outputs and weights, but its ids are still six
+ * distinct experts in 0..63 (a NaN logit ranks below every number), so no
+ * access goes out of bounds and the other tokens are unaffected.
  * ------------------------------------------------------------------------ */
 moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
                                const float* router_w, const float* router_b,
@@ -247,6 +251,8 @@ moe_status_t moe_rmsnorm(const float* h, void* z, int32_t z_dtype, int32_t n_tok
  * which is exactly n_layers calls of moe_layer_forward with those flags.
  * Without MOE_ACCUMULATE, h_l = MoE_l(...); without MOE_NORM_INPUT the layer
  * input is h_{l-1} itself.  MOE_NORM_BF16 and the FORCE flags are not accepted.
+ * A non-finite x gives non-finite outputs with valid ids, as for
+ * moe_layer_forward.
  *
  * x          [1280] f32 or bf16 (x_dtype); may equal y when f32.
  * y          [1280] f32 output (the residual stream after the last layer).

@@ -196,21 +196,25 @@ __device__ __forceinline__ void router_rows(const RouterArgs& a, int t0, float* 
 // six rounds of "largest remaining logit, lowest index among equals", which
 // is the order of the 6 largest softmax probabilities (the softmax is
 // increasing).  Lane e_j writes pick j: its expert id and exp(l - max) / sum.
+// A NaN logit (a non-finite input row) ranks below every number, and a round
+// only looks at lanes not yet picked, so six distinct ids in 0..63 are written
+// whatever the values are.
 __device__ __forceinline__ void select_top6(float le, int32_t* ids, float* w) {
   const int lane = threadIdx.x & 63;
   const float mx = wave_max(le);
   const float ex = expf(le - mx);
   const float sm = wave_sum(ex);
-  float rem = le;
+  const float key = le == le ? le : -__builtin_inff();
+  bool picked = false;
 #pragma unroll
   for (int j = 0; j < TOPK; ++j) {
-    const float m = wave_max(rem);
-    const uint64_t hit = __ballot(rem == m);
+    const float m = wave_max(picked ? -__builtin_inff() : key);
+    const uint64_t hit = __ballot(!picked && key == m);
     const int ej = (int)__builtin_ctzll(hit);
     if (lane == ej) {
       ids[j] = lane;
       w[j] = ex / sm;
-      rem = -__builtin_inff();
+      picked = true;
     }
   }
 }
@@ -1023,7 +1027,10 @@ __device__ __forceinline__ float chain_layer_input(const ChainArgs& a, const Lay
   // the path from the records to the routed weight loads of every layer
   const float inv = a.norm ? __builtin_amdgcn_rsqf(sq * (1.0f / H) + a.eps) : 1.0f;
   if (routed) {
-    const float lge = part * inv + bias_e;
+    // a NaN logit (non-finite input) ranks below every number, so the ranks
+    // below are a permutation of 0..63 whatever the values are
+    const float lraw = part * inv + bias_e;
+    const float lge = lraw == lraw ? lraw : -__builtin_inff();
     if (sub == 0) S.lg[e] = lge;
     __syncthreads();
     MOE_TRACE(a, blockIdx.x, l, 7);

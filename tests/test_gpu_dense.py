@@ -9,6 +9,7 @@ import pytest
 from oracle import dense_head as D
 from synth import NORM_EPS, QFmt, make_dense_ffn, make_hidden, make_lm_head
 from tests.conftest import gpu_available
+from tests.parity import check_routing
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -216,10 +217,17 @@ def test_decoder_ffn_stack_one_token(lib):
     h_prev = h1n
     ids_n, w_n = ids.cpu().numpy(), w.cpu().numpy()
     yn = y.cpu().numpy().astype(np.float64)
-    out_o, trace = MO.moe_chain(h1n, layers, NORM_EPS, False)
-    same = all(np.array_equal(trace[li][0][0], ids_n[li]) for li in range(wl.n_layers))
-    if same:
-        check_ffn(yn - h1n, out_o - h1n)
+    _, free = MO.moe_chain(h1n, layers, NORM_EPS, False)
+    same = all(np.array_equal(free[li][0][0], ids_n[li]) for li in range(wl.n_layers))
+    # the chain is checked whatever the routing: the oracle takes the GPU's ids
+    # (a near-tie admits both answers), and each layer's ids and weights must be
+    # a valid greedy pick of the oracle's own probabilities at that layer
+    out_o, trace = MO.moe_chain(h1n, layers, NORM_EPS, False,
+                                forced_ids=[ids_n[li][None] for li in range(wl.n_layers)])
+    for li in range(wl.n_layers):
+        P = MO.softmax(MO.router_logits(trace[li][2], layers[li]["router_w"], layers[li].get("router_b")))
+        check_routing(ids_n[li][None], w_n[li][None], P)
+    check_ffn(yn - h1n, out_o - h1n)
     # head on the GPU's final residual
     ref = D.lm_head_logits(yn, head_weights_f64("bf16"), True, NORM_EPS)
     check_head(ref, tok.cpu().numpy(), tl.cpu().numpy(), logits.cpu().numpy())

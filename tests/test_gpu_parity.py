@@ -195,7 +195,7 @@ def _chain(wi, T, sample):
     for li in range(wl.n_layers):
         same &= np.all(trace[li][0] == ids_l[li][sample], axis=1)
     assert same.sum() >= len(sample) // 2
-    e2e = check_output(h_l[-1][sample][same].cpu().numpy() - x[sample][same], h_o[same] - x[sample][same], tol=1e-2)
+    e2e = check_output(h_l[-1][sample][same].cpu().numpy() - x[sample][same], h_o[same] - x[sample][same])
     say(f"  end-to-end err/rms {e2e:.2e} on {same.sum()}/{len(sample)} tokens (worst layer {worst:.2e})")
 
 
