@@ -236,6 +236,35 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
                                void* workspace, size_t workspace_bytes,
                                uint32_t flags, void* stream);
 
+/* ------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * layer as moe_layer_forward, same arguments, results and flags, without a
+ * workspace argument.  Its scratch is a file-scope device array of the
+ * library, MOE_STATIC_SCRATCH_BYTES per GPU, held by every GPU the library
+ * runs on until the process ends; its device address is looked up once per
+ * GPU (with that GPU current) at the first call there.  The call allocates
+ * nothing and frees nothing.
+ * n_tokens      0 .. MOE_STATIC_MAX_TOKENS; more returns MOE_E_SHAPE without
+ *               enqueueing anything.  MOE_FORCE_DECODE is accepted only up to
+ *               4 tokens (MOE_E_SHAPE beyond).
+ * All calls on one GPU share that GPU's scratch: two calls whose executions
+ * overlap on one GPU (on different streams, or from different threads without
+ * ordering) race and give undefined results.  Calls ordered on one stream are
+ * safe.  The scratch needs no initialisation; it holds the last call's
+ * intermediates afterwards.
+ * ------------------------------------------------------------------------ */
+#define MOE_STATIC_MAX_TOKENS 256
+#define MOE_STATIC_SCRATCH_BYTES (20u << 20)
+moe_status_t moe_layer_forward_static(const void* x, int32_t x_dtype, int32_t n_tokens,
+                                      const float* router_w, const float* router_b,
+                                      const void* expert_q, const float* expert_scales,
+                                      int32_t expert_bits, int32_t expert_group,
+                                      const void* shared_q, const float* shared_scales,
+                                      int32_t shared_bits, int32_t shared_group,
+                                      float* y, int32_t* topk_ids, float* topk_w,
+                                      uint32_t flags, void* stream);
+
 /* z[t] = h[t] / sqrt(mean(h[t]^2) + eps) over the 1280 features (no gain);
  * h [n_tokens][1280] f32, z [n_tokens][1280] of z_dtype (bf16: nearest, ties
  * to even).  The decoder's RMSNorm (demo page step 7; README "Architecture"). */

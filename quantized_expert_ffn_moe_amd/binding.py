@@ -23,7 +23,7 @@ EXPORTS = ("moe_status_str", "moe_expert_code_bytes", "moe_expert_scale_count", 
            "moe_workspace_bytes", "moe_layer_forward", "moe_rmsnorm", "moe_decode_workspace_bytes",
            "moe_decode_workspace_init", "moe_decode_forward", "moe_lm_head_workspace_bytes",
            "moe_lm_head_argmax", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_forward",
-           "moe_rswa_workspace_bytes", "moe_rswa_decode")
+           "moe_rswa_workspace_bytes", "moe_rswa_decode", "moe_layer_forward_static")
 MOE_HEAD_INT8, MOE_HEAD_BF16 = 8, 16
 MOE_Q4K = 256   # group value of the two-level 4-bit format
 DECODE_MAX_LAYERS = 16
@@ -74,6 +74,9 @@ def load():
     L.moe_layer_forward.restype = i32
     L.moe_layer_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32,
                                     vp, vp, vp, vp, sz, u32, vp]
+    L.moe_layer_forward_static.restype = i32
+    L.moe_layer_forward_static.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32,
+                                           vp, vp, vp, u32, vp]
     L.moe_rmsnorm.restype = i32
     L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, ctypes.c_float, vp]
     L.moe_decode_workspace_bytes.restype = sz
@@ -207,6 +210,22 @@ def moe_layer_forward(x, packed: dict, y, topk_ids, topk_w, ws, flags: int = 0, 
         _ptr(packed["expert_q"]), _ptr(packed["expert_s"]), packed["expert_bits"], packed["expert_group"],
         _ptr(packed["shared_q"]), _ptr(packed["shared_s"]), packed["shared_bits"], packed["shared_group"],
         _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), flags, _stream(stream)))
+
+
+STATIC_MAX_TOKENS = 256
+
+
+def moe_layer_forward_static(x, packed: dict, y, topk_ids, topk_w, flags: int = 0, stream=None):
+    """moe_layer_forward without a workspace: the library's own per-GPU scratch
+    (at most STATIC_MAX_TOKENS tokens; calls that overlap on one GPU race)."""
+    import torch
+    T = x.shape[0] if x.dim() == 2 else 0
+    x_dtype = MOE_BF16 if x.dtype == torch.bfloat16 else MOE_F32
+    check(load().moe_layer_forward_static(
+        _ptr(x), x_dtype, T, _ptr(packed["router_w"]), _ptr(packed["router_b"]),
+        _ptr(packed["expert_q"]), _ptr(packed["expert_s"]), packed["expert_bits"], packed["expert_group"],
+        _ptr(packed["shared_q"]), _ptr(packed["shared_s"]), packed["shared_bits"], packed["shared_group"],
+        _ptr(y), _ptr(topk_ids), _ptr(topk_w), flags, _stream(stream)))
 
 
 def moe_rmsnorm(h, z, eps: float = 1e-6, stream=None):

@@ -10,6 +10,8 @@ using namespace moe;
 static_assert(MOE_HIDDEN == H && MOE_EXPERTS == E && MOE_TOPK == TOPK && MOE_INTER == I &&
                   MOE_SHARED_INTER == IS && MOE_MAX_TOKENS == MAX_T && MOE_Q4K == Q4K,
               "public and internal shape constants disagree");
+static_assert(MOE_STATIC_MAX_TOKENS == STATIC_MAX_T && MOE_STATIC_SCRATCH_BYTES == STATIC_SCRATCH_BYTES,
+              "public and internal scratch constants disagree");
 
 namespace {
 
@@ -55,7 +57,9 @@ struct Carver {
   }
 };
 
-Workspace carve(void* base, int T) {
+// part_max_t: largest token count that may take the per-token path (its
+// partials share the bytes of the grouped path's buffers)
+Workspace carve(void* base, int T, int part_max_t = DECODE_FORCE_MAX_T) {
   Workspace w;
   Carver c{(char*)base, 0};
   const size_t slots = (size_t)T * TOPK;
@@ -76,7 +80,7 @@ Workspace carve(void* base, int T) {
   w.blkcnt = (int32_t*)c.take((slots / HIST_BLOCK + 1) * E * 4);
   const size_t grouped_end = c.off;
   c.off = union_start;
-  w.part = T <= DECODE_FORCE_MAX_T ? (float*)c.take((size_t)T * N_ITEMS * H * 4) : nullptr;
+  w.part = T <= part_max_t ? (float*)c.take((size_t)T * N_ITEMS * H * 4) : nullptr;
   w.bytes = c.off > grouped_end ? c.off : grouped_end;
   return w;
 }
@@ -314,15 +318,21 @@ size_t moe_workspace_bytes(int32_t n_tokens) {
   return carve(nullptr, n_tokens).bytes;
 }
 
-moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
-                               const float* router_w, const float* router_b,
-                               const void* expert_q, const float* expert_scales,
-                               int32_t expert_bits, int32_t expert_group,
-                               const void* shared_q, const float* shared_scales,
-                               int32_t shared_bits, int32_t shared_group,
-                               float* y, int32_t* topk_ids, float* topk_w,
-                               void* workspace, size_t workspace_bytes,
-                               uint32_t flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_layer_forward with the largest per-token-path call as a parameter
+// (the workspace-free entry point keeps that path to its default range)
+moe_status_t layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
+                           const float* router_w, const float* router_b,
+                           const void* expert_q, const float* expert_scales,
+                           int32_t expert_bits, int32_t expert_group,
+                           const void* shared_q, const float* shared_scales,
+                           int32_t shared_bits, int32_t shared_group,
+                           float* y, int32_t* topk_ids, float* topk_w,
+                           void* workspace, size_t workspace_bytes,
+                           uint32_t flags, void* stream, int part_max_t) {
   const int T = n_tokens;
   if (T < 0 || T > MAX_T) return MOE_E_SHAPE;
   // an empty call may pass NULL for the per-token buffers (empty tensors)
@@ -333,7 +343,7 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   const uint32_t known = MOE_ACCUMULATE | MOE_NORM_INPUT | MOE_NORM_BF16 | MOE_FORCE_DECODE | MOE_FORCE_GROUPED;
   if ((flags & ~known) || (x_dtype != MOE_F32 && x_dtype != MOE_BF16)) return MOE_E_ARG;
   if ((flags & MOE_FORCE_DECODE) && (flags & MOE_FORCE_GROUPED)) return MOE_E_ARG;
-  if ((flags & MOE_FORCE_DECODE) && T > DECODE_FORCE_MAX_T) return MOE_E_SHAPE;
+  if ((flags & MOE_FORCE_DECODE) && T > part_max_t) return MOE_E_SHAPE;
   // a call with a two-level expert set runs the grouped path's small (16- or
   // 32-row) tiles at every token count, both expert sets alike
   const bool two_level = expert_group == Q4K || shared_group == Q4K;
@@ -346,7 +356,7 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   const void* word_ptrs[] = {router_b, expert_scales, shared_scales, topk_ids, topk_w};
   for (const void* p : word_ptrs)
     if (p && ((uintptr_t)p & 3u)) return MOE_E_ALIGN;
-  const Workspace ws = carve(workspace, T);
+  const Workspace ws = carve(workspace, T, part_max_t);
   if (workspace_bytes < ws.bytes) return MOE_E_WORKSPACE;
   if (T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -434,6 +444,41 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   ca.y = y; ca.T = T; ca.accumulate = accumulate;
   if (launch_combine(ca, s) != hipSuccess) return MOE_E_HIP;
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
+                               const float* router_w, const float* router_b,
+                               const void* expert_q, const float* expert_scales,
+                               int32_t expert_bits, int32_t expert_group,
+                               const void* shared_q, const float* shared_scales,
+                               int32_t shared_bits, int32_t shared_group,
+                               float* y, int32_t* topk_ids, float* topk_w,
+                               void* workspace, size_t workspace_bytes,
+                               uint32_t flags, void* stream) {
+  return layer_forward(x, x_dtype, n_tokens, router_w, router_b, expert_q, expert_scales, expert_bits,
+                       expert_group, shared_q, shared_scales, shared_bits, shared_group, y, topk_ids, topk_w,
+                       workspace, workspace_bytes, flags, stream, DECODE_FORCE_MAX_T);
+}
+
+moe_status_t moe_layer_forward_static(const void* x, int32_t x_dtype, int32_t n_tokens,
+                                      const float* router_w, const float* router_b,
+                                      const void* expert_q, const float* expert_scales,
+                                      int32_t expert_bits, int32_t expert_group,
+                                      const void* shared_q, const float* shared_scales,
+                                      int32_t shared_bits, int32_t shared_group,
+                                      float* y, int32_t* topk_ids, float* topk_w,
+                                      uint32_t flags, void* stream) {
+  if (n_tokens < 0 || n_tokens > STATIC_MAX_T) return MOE_E_SHAPE;
+  if (carve(nullptr, n_tokens, DECODE_MAX_T).bytes > STATIC_SCRATCH_BYTES) return MOE_E_WORKSPACE;
+  void* ws = nullptr;
+  if (static_scratch(&ws) != hipSuccess) return MOE_E_HIP;
+  return layer_forward(x, x_dtype, n_tokens, router_w, router_b, expert_q, expert_scales, expert_bits,
+                       expert_group, shared_q, shared_scales, shared_bits, shared_group, y, topk_ids, topk_w,
+                       ws, STATIC_SCRATCH_BYTES, flags, stream, DECODE_MAX_T);
 }
 
 moe_status_t moe_rmsnorm(const float* h, void* z, int32_t z_dtype, int32_t n_tokens, float eps, void* stream) {

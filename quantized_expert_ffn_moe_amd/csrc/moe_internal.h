@@ -19,6 +19,8 @@ constexpr int SMALL_TILE_MAX_SLOTS = 64 * 64;   // (token, pick) slots up to whi
 constexpr int TINY_TILE_MAX_SLOTS = 64 * 8;     // ... and the 16-row tiles (about 8 rows per expert or fewer)
 constexpr int DECODE_MAX_T = 4;  // largest token count routed to the GEMV path by default
 constexpr int MAX_T = 8192;      // largest token count of one call
+constexpr int STATIC_MAX_T = 256;                      // largest call of the workspace-free entry point
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)20 << 20;  // its per-GPU scratch (the carve for 256 tokens fits)
 constexpr int MOE_MAX_SLOTS = MAX_T * TOPK;
 
 __host__ __device__ constexpr int kb_cols(int bits) { return bits == 4 ? 128 : 64; }
@@ -210,6 +212,9 @@ hipError_t launch_dec_items(const DecItemsArgs& a, int T, hipStream_t s);
 hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s);
 hipError_t launch_chain(const ChainArgs& a, hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s);
+// device address of the current GPU's copy of the workspace-free entry
+// point's scratch array (STATIC_SCRATCH_BYTES, 256-byte aligned)
+hipError_t static_scratch(void** out);
 hipError_t launch_hist(const HistArgs& a, hipStream_t s);
 hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s);

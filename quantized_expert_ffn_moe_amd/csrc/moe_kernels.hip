@@ -28,6 +28,8 @@
 #include "moe_internal.h"
 #include "moe_wave.h"
 
+#include <mutex>
+
 namespace moe {
 
 // Optional device timestamps for timeline studies: compiled only when
@@ -2766,6 +2768,34 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps, hipStream_t s) {
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, s, h, z, z_bf16, eps);
   return hipGetLastError();
+}
+
+// Scratch of the workspace-free layer entry point: every GPU the library runs
+// on holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel or a copy (on the host it is only a stand-in for
+// the symbol): the device address of each GPU's copy is taken once, with that
+// GPU current, and kept per device.
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+
+hipError_t static_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || ((uintptr_t)p & 255u)) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace moe
