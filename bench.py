@@ -377,6 +377,58 @@ def grouped_step_bytes(wl, ids_per_layer):
     return total
 
 
+def chain_gate(args, wl, layers, packed, xt, ws, stream, h_last, ids_last, w_last, rows):
+    """Gate and CPU baseline of a chained many-token step, layer by layer on the
+    GPU's own residual stream (a bf16-rounded layer input turns tiny residual
+    differences into whole bf16 steps, so the chain is compared teacher-forced,
+    as the GPU tests do): the step is run once more keeping every layer's
+    residual, which must reproduce the timed step bit for bit; then, on sampled
+    tokens, each layer's ids, weights and output against the oracle at the
+    input the GPU used (the GPU's RMSNorm of its residual).  The oracle's time
+    over the sample (all layers) is the baseline."""
+    import numpy as np
+    import torch
+
+    from quantized_expert_ffn_moe_amd import binding as B
+    from synth import NORM_EPS
+
+    L, T = wl.n_layers, wl.n_tokens
+    flags = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE | (B.MOE_NORM_BF16 if wl.norm_bf16 else 0)
+    h = xt.float().contiguous()
+    hs = [h.clone()]
+    ids = torch.empty(L, T, 6, dtype=torch.int32, device="cuda")
+    w = torch.empty(L, T, 6, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(stream):
+        for li in range(L):
+            B.moe_layer_forward(h, packed[li], h, ids[li], w[li], ws, flags, stream=stream)
+            hs.append(h.clone())
+    torch.cuda.synchronize()
+    if not (np.array_equal(hs[-1].cpu().numpy(), h_last) and np.array_equal(ids.cpu().numpy(), ids_last[:L])):
+        raise GateError("the repeated step differs from the timed step")
+    sample = np.sort(rows[:(4 if args.no_cpu_baseline else min(T, 64))])
+    zdt = torch.bfloat16 if wl.norm_bf16 else torch.float32
+    used, worst, near = 0.0, 0.0, 0
+    for li in range(L):
+        z = torch.empty(len(sample), 1280, dtype=zdt, device="cuda")
+        B.moe_rmsnorm(hs[li][sample].contiguous(), z, NORM_EPS)
+        zin = z.float().cpu().numpy().astype(np.float64)
+        out = (hs[li + 1][sample] - hs[li][sample]).cpu().numpy()
+        x64 = np.zeros((T, 1280)); x64[sample] = zin
+        y64 = np.zeros((T, 1280), np.float32); y64[sample] = out
+        cpu, g = moe_oracle_leg([layers[li]], x64, sample, [ids_last[li]], [w_last[li]], y64, chained=False,
+                                norm_bf16=False, block=len(sample), what=f"{wl.name} layer {li + 1}")
+        used += len(sample) / cpu["value"]
+        worst = max(worst, g["max_err_over_rms"])
+        near += g["near_ties"]
+    base = {"value": len(sample) / used, "unit": "tokens/s", "cores": host_threads(), "kind": "oracle",
+            "sample": f"{len(sample)} of the timed tokens through the {L} layers, each layer on the GPU's own "
+                      f"residual (float64 numpy oracle), {used:.1f} s"}
+    gate = {"tokens": len(sample), "layers": L, "max_err_over_rms": worst, "near_ties": near,
+            "bar": "per layer on the GPU's residual: ids exact where gaps > 1e-6, w rtol 1e-5, max|err| <= 1e-3 rms",
+            "repeat_bitwise": True}
+    return base, gate
+
+
 def bench_grouped(args):
     import numpy as np
     import torch
@@ -437,12 +489,13 @@ def bench_grouped(args):
     flops = L * prefill_flops(T)
     tflops = flops / (ms * 1e-3) / 1e12
     rows = np.random.default_rng(T).permutation(T)
-    block = T if T <= 300 and L == 1 else 8
     try:
-        cpu, gate = moe_oracle_leg(layers, x.astype(np.float64), rows, [ids_last[li] for li in range(L)],
-                                   [w_last[li] for li in range(L)], h_last, chained=wl.chained,
-                                   norm_bf16=wl.norm_bf16, block=block, what=wl.name,
-                                   budget_s=0.0 if args.no_cpu_baseline else BUDGET_S)
+        if wl.chained:
+            cpu, gate = chain_gate(args, wl, layers, packed, xt, ws, stream, h_last, ids_last, w_last, rows)
+        else:
+            cpu, gate = moe_oracle_leg(layers, x.astype(np.float64), rows, [ids_last[0]], [w_last[0]], h_last,
+                                       chained=False, norm_bf16=False, block=T if T <= 300 else 8, what=wl.name,
+                                       budget_s=0.0 if args.no_cpu_baseline else BUDGET_S)
     except GateError as e:
         gate_exit(wl.name, str(e))
     out = {"metric": f"{wl.name}: tokens/s", "value": T / (ms * 1e-3), "unit": "tokens/s",
@@ -739,6 +792,165 @@ def bench_rswa(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_layer(args):
+    """One whole decoder layer step: the attention half (RMSNorm, q/k/v
+    projections, R-SWA over a 288-row reference block and the 128-slot ring, o
+    projection and residual) and the MoE half (int4 G64 routed, int8 G128
+    shared; the persistent decode step for one token, moe_layer_forward for
+    128 streams).  Weight and KV replicas rotate so that the last-level cache
+    cannot hold a step's bytes; the rings advance in place every step."""
+    import numpy as np
+    import torch
+
+    from quantized_expert_ffn_moe_amd import binding as B
+    from synth import (NORM_EPS, WORKLOADS, bf16_bits_to_f32, make_attn_weights, make_hidden, make_layer,
+                       make_rswa)
+
+    S = 1 if args.workload == "layer1" else 128
+    n_ref, H = 288, 1280
+    wl = WORKLOADS[1] if S == 1 else WORKLOADS[5]
+    R = 8 if S == 1 else 2
+    layer = make_layer(wl, 0)
+    aw = make_attn_weights(0)
+    attn = [B.attn_weights_to_device(**aw) for _ in range(R)]
+    moe = [B.pack_layer(layer) for _ in range(R)]
+    n_gen = [127 + 37 * s for s in range(S)]
+    kvs = [B.rswa_to_device(make_rswa(S, n_ref, n_gen=n_gen, seed=r)) for r in range(R)]
+    xs = torch.from_numpy(make_hidden(S * (args.warmup + args.steps + 1), batch=500)).cuda()
+    h = torch.empty(S, H, dtype=torch.float32, device="cuda")
+    ids = torch.empty(S, 6, dtype=torch.int32, device="cuda")
+    w = torch.empty(S, 6, dtype=torch.float32, device="cuda")
+    y = torch.empty(S, H, dtype=torch.float32, device="cuda")
+    ws_a = torch.empty(B.moe_attn_block_workspace_bytes(S, n_ref), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    ws_m = B.decode_workspace(stream=stream) if S == 1 else B.workspace(S)
+    flags = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE
+    warr = [B.layer_weights([m]) for m in moe]
+
+    def step(i):
+        r = i % R
+        h.copy_(xs[S * i:S * i + S])
+        B.moe_attn_block_forward(h, attn[r], kvs[r], ws_a, stream=stream)
+        if S == 1:
+            B.moe_decode_forward(h, y, [moe[r]], ids, w, ws_m, flags, weights=warr[r], stream=stream)
+        else:
+            B.moe_layer_forward(h, moe[r], h, ids, w, ws_m, flags, stream=stream)
+    ms = timed_loop(step, stream, args.warmup, args.steps)
+    name = f"decoder_layer_step_{S}stream{'s' if S > 1 else ''}_ref288_attn_bf16_moe_int4g64_int8g128"
+    if S == 1:
+        check_error_word(ws_m, name)
+    ids_last = ids.cpu().numpy()
+    live = [min(g + 1, 128) for g in n_gen]
+    kv_bytes = sum(10 * (n_ref + lv) * 128 * 2 * 2 + 10 * 128 * 2 * 2 for lv in live)
+    attn_bytes = 4 * H * H * 2
+    moe_bytes = (layer_bytes(ids_last[0].tolist(), wl.routed, wl.shared) if S == 1
+                 else grouped_step_bytes(wl, [ids_last]))
+    nbytes = kv_bytes + attn_bytes + moe_bytes + S * H * 4 * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+
+    # gate and baseline: one more step on fresh inputs, each half checked on
+    # sampled streams against the oracle on the GPU's own input to it
+    from oracle import decoder_layer as DL
+    from oracle import moe_oracle as O
+    from tests.parity import check_layer
+    kvh = make_rswa(S, n_ref, n_gen=n_gen, seed=99)
+    dev = B.rswa_to_device(kvh)
+    h0 = make_hidden(S, batch=777)
+    hg = torch.from_numpy(h0).cuda()
+    with torch.cuda.stream(stream):
+        B.moe_attn_block_forward(hg, attn[0], dev, ws_a, stream=stream)
+    torch.cuda.synchronize()
+    h1 = hg.cpu().numpy().astype(np.float64)
+    with torch.cuda.stream(stream):
+        if S == 1:
+            B.moe_decode_forward(hg, y, [moe[0]], ids, w, ws_m, flags, weights=warr[0], stream=stream)
+        else:
+            B.moe_layer_forward(hg, moe[0], hg, ids, w, ws_m, flags, stream=stream)
+    torch.cuda.synchronize()
+    h2 = (y if S == 1 else hg).cpu().numpy().astype(np.float64)
+    w64 = {k: bf16_bits_to_f32(v).astype(np.float64) for k, v in aw.items()}
+    f64 = lambda b: bf16_bits_to_f32(b).astype(np.float64)
+    sample = np.arange(S) if S == 1 else np.sort(np.random.default_rng(5).choice(S, 4 if args.no_cpu_baseline else 12,
+                                                                                   replace=False))
+    t0 = time.perf_counter()
+    refs, outs = [], []
+    for s_ in sample:
+        ho, _ = DL.attn_block(h0[s_:s_ + 1].astype(np.float64), w64["w_q"], w64["w_k"], w64["w_v"], w64["w_o"],
+                              f64(kvh["ref_k"][s_:s_ + 1]), f64(kvh["ref_v"][s_:s_ + 1]),
+                              f64(kvh["ring_k"][s_:s_ + 1]), f64(kvh["ring_v"][s_:s_ + 1]),
+                              kvh["n_gen"][s_:s_ + 1], NORM_EPS)
+        refs.append(ho[0] - h0[s_])
+        outs.append(h1[s_] - h0[s_])
+    refs, outs = np.array(refs), np.array(outs)
+    r_attn = float(np.abs(outs - refs).max() / np.sqrt(np.mean(refs ** 2)))
+    try:
+        if not r_attn <= 1e-3:
+            raise GateError(f"attention half max|err|/rms {r_attn:.3e}")
+        r_moe, _ = check_layer(O.rmsnorm(h1[sample], NORM_EPS), layer, ids.cpu().numpy()[sample],
+                               w.cpu().numpy()[sample], h2[sample] - h1[sample])
+    except (AssertionError, GateError) as e:
+        gate_exit(name, str(e))
+    used = time.perf_counter() - t0
+    out = {"metric": f"{name}: tokens/s", "value": S / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+           "steps": args.steps, "warmup": args.warmup,
+           "dtype": "bf16 MFMA on bf16 weights x f32 activations as bf16 hi/lo (projections); f32 on bf16 KV "
+                    "(attention); " + (DTYPE_DECODE if S == 1 else DTYPE_GROUPED) + " (MoE)",
+           "data": "synthetic (seeded weights, KV and rows)",
+           "config": {"workload": name, "streams": S, "n_ref": n_ref, "replicas": R},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_step": nbytes},
+           "parity_gate": {"streams": int(len(sample)), "attention_err_over_rms": r_attn, "moe_err_over_rms": r_moe,
+                           "bar": "each half on the GPU's input to it: max|err| <= 1e-3 rms; routing as the tests"}}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = {"value": len(sample) / used, "unit": "tokens/s", "cores": host_threads(),
+                               "kind": "oracle",
+                               "sample": f"{len(sample)} stream{'s' if len(sample) > 1 else ''} of one step (float64 "
+                                         f"numpy oracle: attention half and MoE layer), {used:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
+def bench_crossover(args):
+    """Where the per-token (GEMV) path and the grouped (MFMA) path of
+    moe_layer_forward cross: one layer at T tokens through each path (forced),
+    for the continuous-batch decode formats (int4 G64 routed, int8 G128
+    shared, f32 input with the norm and residual in the call) and for int4 G32
+    (bf16 input, biased router); 4 weight replicas rotated.  Prints one JSON
+    line with the table (microseconds per layer call)."""
+    import numpy as np
+    import torch
+
+    from quantized_expert_ffn_moe_amd import binding as B
+    from synth import WORKLOADS, make_layer, make_tokens
+
+    counts = [1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 48, 64]
+    table = {}
+    stream = torch.cuda.Stream()
+    for wi in (5, 2):
+        wl = WORKLOADS[wi]
+        lay = make_layer(wl, 0)
+        reps = [B.pack_layer(lay) for _ in range(4)]
+        flags0 = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE if wl.x_dtype == "f32" else 0
+        rows = {}
+        for T in counts:
+            x, bits = make_tokens(wl, n_tokens=T, batch=60)
+            xt = (torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16) if bits is not None
+                  else torch.from_numpy(x)).cuda()
+            xin = xt.float().contiguous() if wl.x_dtype == "f32" else xt
+            y = torch.zeros(T, 1280, dtype=torch.float32, device="cuda")
+            ids = torch.empty(T, 6, dtype=torch.int32, device="cuda")
+            w = torch.empty(T, 6, dtype=torch.float32, device="cuda")
+            ws = B.workspace(T)
+            row = {}
+            for name, f in (("per_token", B.MOE_FORCE_DECODE), ("grouped", B.MOE_FORCE_GROUPED), ("default", 0)):
+                ms = timed_loop(lambda i: B.moe_layer_forward(xin, reps[i % 4], y, ids, w, ws, flags0 | f,
+                                                              stream=stream), stream, args.warmup, args.steps)
+                row[name] = round(ms * 1e3, 2)
+            rows[T] = row
+        table[wl.name.split("_")[0] + "_" + ("int4g64_int8g128_f32" if wi == 5 else "int4g32_bf16_biased")] = rows
+    print(json.dumps({"metric": "moe_layer_forward per-token vs grouped path: us per layer call",
+                      "unit": "us", "steps": args.steps, "warmup": args.warmup, "table": table}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -746,7 +958,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--workload", choices=["decode", "decode1", "batched32", "prefill273", "multipage2184", "batch128",
-                                           "batch256", "lmhead_bf16", "lmhead_int8", "dense0", "rswa128", "ffnstack"],
+                                           "batch256", "lmhead_bf16", "lmhead_int8", "dense0", "rswa128", "ffnstack",
+                                           "crossover", "layer1", "layer128"],
                     default="decode",
                     help="decode = the headline 11-layer decode step; decode1 = one token through one int8 G128 "
                          "layer; the prefill workloads report MFMA figures; batchN = one continuous-batch decode "
@@ -787,6 +1000,10 @@ def main():
         return bench_ffnstack(args)
     if args.workload in ("decode", "decode1"):
         return bench_decode(args)
+    if args.workload == "crossover":
+        return bench_crossover(args)
+    if args.workload in ("layer1", "layer128"):
+        return bench_layer(args)
     return bench_grouped(args)
 
 

@@ -60,6 +60,36 @@ moe_status_t moe_rswa_decode(int32_t n_streams, int32_t n_ref, const float* q, c
                              const int32_t* n_gen, float* out, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * The attention half of a decoder layer for n_streams streams (the layer's
+ * MoE half is moe_layer_forward with MOE_NORM_INPUT | MOE_ACCUMULATE, or
+ * moe_decode_forward): browser demo page "One forward pass, left to right",
+ * step 6 (R-SWA attention of ten heads of 128, then the MoE FFN); model card
+ * "The rest of the pipeline" (plain multi-head attention).
+ *   z = RMSNorm(h) (no gain, eps 1e-6 inside the root)
+ *   q = W_q z, k = W_k z, v = W_v z        (1280 -> 1280 each)
+ *   a = the R-SWA step of moe_rswa_decode on q, k, v (ring updated in place)
+ *   h = h + W_o a                          (in place)
+ * h        [S][1280] f32, device, read and updated in place.
+ * w_qkv    [3840][1280] bf16 bit patterns, device: rows 0..1279 W_q,
+ *          1280..2559 W_k, 2560..3839 W_v (y = W x: row n gives output n).
+ * w_o      [1280][1280] bf16 bit patterns, device.
+ * ref_k, ref_v, ring_k, ring_v, n_gen: as for moe_rswa_decode.
+ * workspace >= moe_attn_block_workspace_bytes(n_streams, n_ref) bytes,
+ *          16-byte aligned; garbage before and after the call.
+ * No bias and no positional transform (the pages name none).  Projections
+ * multiply bf16 weights with the f32 activations split into two bf16 halves
+ * (16 significant bits) on the matrix cores, fp32 accumulation.
+ * n_streams in [0, MOE_RSWA_MAX_STREAMS] (0 enqueues nothing, and h, the KV
+ * and n_gen may then be NULL); errors as for moe_rswa_decode.  Stream ordered; the persistent decode step
+ * (moe_decode_forward) takes every compute unit, so the two are enqueued one
+ * after the other on one stream, never concurrently.
+ */
+size_t moe_attn_block_workspace_bytes(int32_t n_streams, int32_t n_ref);
+moe_status_t moe_attn_block_forward(int32_t n_streams, int32_t n_ref, float* h, const void* w_qkv, const void* w_o,
+                                    const void* ref_k, const void* ref_v, void* ring_k, void* ring_v,
+                                    const int32_t* n_gen, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

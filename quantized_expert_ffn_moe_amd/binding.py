@@ -23,7 +23,8 @@ EXPORTS = ("moe_status_str", "moe_expert_code_bytes", "moe_expert_scale_count", 
            "moe_workspace_bytes", "moe_layer_forward", "moe_rmsnorm", "moe_decode_workspace_bytes",
            "moe_decode_workspace_init", "moe_decode_forward", "moe_lm_head_workspace_bytes",
            "moe_lm_head_argmax", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_forward",
-           "moe_rswa_workspace_bytes", "moe_rswa_decode", "moe_layer_forward_static")
+           "moe_rswa_workspace_bytes", "moe_rswa_decode", "moe_layer_forward_static",
+           "moe_attn_block_workspace_bytes", "moe_attn_block_forward")
 MOE_HEAD_INT8, MOE_HEAD_BF16 = 8, 16
 MOE_Q4K = 256   # group value of the two-level 4-bit format
 DECODE_MAX_LAYERS = 16
@@ -96,6 +97,10 @@ def load():
     L.moe_dense_ffn_forward.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, u32, vp, sz, vp]
     L.moe_rswa_workspace_bytes.restype = sz
     L.moe_rswa_workspace_bytes.argtypes = [i32, i32]
+    L.moe_attn_block_workspace_bytes.restype = sz
+    L.moe_attn_block_workspace_bytes.argtypes = [i32, i32]
+    L.moe_attn_block_forward.restype = i32
+    L.moe_attn_block_forward.argtypes = [i32, i32] + [vp] * 8 + [vp, sz, vp]
     L.moe_rswa_decode.restype = i32
     L.moe_rswa_decode.argtypes = [i32, i32] + [vp] * 9 + [vp, sz, vp]
     _lib = L
@@ -365,6 +370,37 @@ def rswa_to_device(d: dict, device="cuda"):
         out[k] = torch.from_numpy(np.ascontiguousarray(d[k]).view(np.int16)).to(device)
     out["n_ref"] = d["n_ref"]
     return out
+
+
+def moe_attn_block_workspace_bytes(n_streams: int, n_ref: int) -> int:
+    return load().moe_attn_block_workspace_bytes(n_streams, n_ref)
+
+
+def attn_weights_to_device(w_q, w_k, w_v, w_o, device="cuda"):
+    """bf16 bit patterns (uint16) of the projections as moe_attn_block_forward
+    takes them: W_q | W_k | W_v stacked [3840][1280], W_o [1280][1280]."""
+    import torch
+    qkv = np.ascontiguousarray(np.concatenate([w_q, w_k, w_v]).view(np.int16))
+    return {"w_qkv": torch.from_numpy(qkv).to(device),
+            "w_o": torch.from_numpy(np.ascontiguousarray(np.asarray(w_o).view(np.int16))).to(device)}
+
+
+def moe_attn_block_forward(h, attn: dict, kv: dict, ws, stream=None):
+    """Enqueue the attention half of a decoder layer: h [S,1280] f32 updated in
+    place; kv as for moe_rswa_decode (its rings updated in place)."""
+    import torch
+    S, n_ref = h.shape[0], kv["n_ref"]
+    _want(h, torch.float32, (S, HIDDEN), "h")
+    _want(attn["w_qkv"], torch.int16, (3 * HIDDEN, HIDDEN), "w_qkv")
+    _want(attn["w_o"], torch.int16, (HIDDEN, HIDDEN), "w_o")
+    for k in ("ref_k", "ref_v"):
+        _want(kv[k], torch.int16, (S, 10, n_ref, 128), k)
+    for k in ("ring_k", "ring_v"):
+        _want(kv[k], torch.int16, (S, 10, 128, 128), k)
+    _want(kv["n_gen"], torch.int32, (S,), "n_gen")
+    check(load().moe_attn_block_forward(S, n_ref, _ptr(h), _ptr(attn["w_qkv"]), _ptr(attn["w_o"]), _ptr(kv["ref_k"]),
+                                        _ptr(kv["ref_v"]), _ptr(kv["ring_k"]), _ptr(kv["ring_v"]), _ptr(kv["n_gen"]),
+                                        _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def moe_rswa_workspace_bytes(n_streams: int, n_ref: int) -> int:

@@ -17,7 +17,7 @@ constexpr int MT_SMALL = 32; // rows per tile when experts see few rows each
 constexpr int MT_TINY = 16;  // rows per tile when experts see very few rows each (fused shared/routed launches)
 constexpr int SMALL_TILE_MAX_SLOTS = 64 * 64;   // (token, pick) slots up to which the small tiles run
 constexpr int TINY_TILE_MAX_SLOTS = 64 * 8;     // ... and the 16-row tiles (about 8 rows per expert or fewer)
-constexpr int DECODE_MAX_T = 4;  // largest token count routed to the GEMV path by default
+constexpr int DECODE_MAX_T = 5;  // largest token count routed to the GEMV path by default (measured crossover)
 constexpr int MAX_T = 8192;      // largest token count of one call
 constexpr int STATIC_MAX_T = 256;                      // largest call of the workspace-free entry point
 constexpr size_t STATIC_SCRATCH_BYTES = (size_t)20 << 20;  // its per-GPU scratch (the carve for 256 tokens fits)
@@ -206,6 +206,15 @@ struct RswaArgs {
 };
 int rswa_chunks(int n_ref);
 hipError_t launch_rswa(const RswaArgs& a, hipStream_t s);
+
+// Attention projections: y[t][n] (+)= sum_k a[t][k] W[n][k], K = H, bf16 W
+// [N][H]; output column n of token t at y[((n / H) * T + t) * H + n % H]
+// (so q, k and v of a [3H][H] weight land in three [T][H] arrays).
+struct ProjArgs {
+  const float* a; const uint16_t* w; float* y;
+  int T, N, accumulate;
+};
+hipError_t launch_proj(const ProjArgs& p, hipStream_t s);
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 hipError_t launch_dec_items(const DecItemsArgs& a, int T, hipStream_t s);

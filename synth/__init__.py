@@ -11,5 +11,5 @@ from .workloads import (  # noqa: F401
     QFmt, Workload, WORKLOADS, workload, make_layer, make_tokens,
     make_tiny_layer, bf16_bits_to_f32, f32_to_bf16_bits,
     VOCAB, DENSE_INTER, make_lm_head, make_dense_ffn, make_hidden,
-    HEADS, HEAD_DIM, RSWA_WINDOW, make_rswa,
+    HEADS, HEAD_DIM, RSWA_WINDOW, make_rswa, make_attn_weights,
 )

@@ -310,3 +310,16 @@ def make_rswa(n_streams: int, n_ref: int, n_gen=None, seed: int = 0) -> dict:
     d["n_gen"] = np.asarray(n_gen, dtype=np.int32).reshape(S)
     d["n_ref"] = n_ref
     return d
+
+
+# --------------------------------------------------------------------------
+# attention projections of a decoder layer (seed space 9)
+# --------------------------------------------------------------------------
+_W_ATTN = 9
+
+
+def make_attn_weights(seed: int = 0) -> dict:
+    """W_q, W_k, W_v, W_o [1280][1280] as bf16 bit patterns of N(0, 0.02)
+    draws (the router's draw; y = W x, row n gives output n)."""
+    return {k: f32_to_bf16_bits((_rng(_W_ATTN, seed, t).standard_normal((HIDDEN, HIDDEN)) * 0.02).astype(np.float32))
+            for t, k in enumerate(("w_q", "w_k", "w_v", "w_o"))}

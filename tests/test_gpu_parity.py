@@ -77,6 +77,22 @@ def test_ragged_token_counts_both_paths(lib, T):
     np.testing.assert_array_equal(a[0], b[0])
 
 
+@pytest.mark.parametrize("wi,T", [(5, 5), (5, 6), (2, 5), (2, 6)])
+def test_default_path_switch(lib, wi, T):
+    """Default flags on both sides of the per-token / grouped switch (5 | 6
+    tokens, the measured crossover): the default call must equal the forced
+    call of the path it takes, and both paths match the oracle."""
+    from quantized_expert_ffn_moe_amd import binding as B
+    say(f"{WORKLOADS[wi].name}: {T} tokens, default path")
+    x, xt = tokens(wi, n=T, batch=17)
+    d = run(xt, packed_of(wi, 0))
+    f = run(xt, packed_of(wi, 0), B.MOE_FORCE_DECODE if T <= 5 else B.MOE_FORCE_GROUPED)
+    for u, v in zip(d, f):
+        np.testing.assert_array_equal(u, v)
+    ratio, _ = check_layer(x, layer_of(wi, 0), *d)
+    say(f"  err/rms {ratio:.2e}")
+
+
 @pytest.mark.parametrize("wi,T", [(2, 8), (2, 85), (2, 86), (2, 682), (2, 683), (5, 85), (5, 86), (5, 683)])
 def test_tile_shape_boundaries(lib, wi, T):
     """Token counts on both sides of the grouped path's switches: the two-pass
