@@ -1699,6 +1699,24 @@ __device__ __forceinline__ void store_a(_Float16* lds, const AStage<F32>& A) {
 
 struct TileInfo { int valid, nrows, pbase, row0, e; };
 
+// Workgroup b of a launch is dispatched to XCD b mod 8.  xcd_run(b, n) maps the
+// n live workgroups to logical indices so that every XCD takes one contiguous
+// run of them: the column blocks of a row tile, and the row tiles of one
+// expert, then run on the same XCD and share its L2 (each A tile and each
+// expert's B tiles come from HBM about once per XCD that uses them, not once
+// per workgroup).  Indices from n on keep their number, find no tile and exit.
+__device__ __forceinline__ int xcd_run(int b, int n) {
+  if (b >= n) return b;
+  const int x = b & 7, j = b >> 3, q = n >> 3, rem = n & 7;
+  return x * q + min(x, rem) + j;
+}
+
+// Row tiles of a grouped launch: the histogram's count (routed) or the token
+// tiles (shared expert).
+__device__ __forceinline__ int live_tiles(const GroupedArgs& a, int mtl) {
+  return a.shared ? (a.T + mtl - 1) / mtl : *a.ntiles;
+}
+
 __device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile, int mtl) {
   TileInfo ti;
   if (a.shared) {
@@ -1733,7 +1751,8 @@ __global__ __launch_bounds__(GT) void grouped_gateup_kernel(GroupedArgs a) {
   constexpr int BT = 16 * NB;                       // B tiles per stage
   constexpr int BU = BT * 64 / GT;                  // B uint4 per thread per stage (2 or 4)
   const int inter = a.w.inter, ncb = inter / 128;
-  const int tile = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+  const int lb = xcd_run(blockIdx.x, live_tiles(a, MT) * ncb);
+  const int tile = lb / ncb, cb = lb % ncb;
   const TileInfo ti = tile_info(a, tile, MT);
   if (!ti.valid) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_uniform((int)(threadIdx.x >> 6)), r = lane & 15,
@@ -1901,7 +1920,8 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
   constexpr int WRT = 4 / NSUB;                     // row tiles per wave (1 or 2)
   // KSPLIT > 1: workgroup kh takes stages kh NSTAGE .. and writes its partial
   // sum to out + kh T H (the combine adds the parts)
-  const int kh = blockIdx.x % KSPLIT, tb = blockIdx.x / KSPLIT, s0 = kh * NSTAGE;
+  const int lb = xcd_run(blockIdx.x, live_tiles(a, MT) * NCB * KSPLIT);
+  const int kh = lb % KSPLIT, tb = lb / KSPLIT, s0 = kh * NSTAGE;
   const int tile = tb / NCB, cb = tb % NCB;
   const TileInfo ti = tile_info(a, tile, MT);
   if (!ti.valid) return;
@@ -2482,13 +2502,19 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
     }
 }
 
+// Workgroups per row tile: gate/up 128 intermediate columns each; down four
+// packed row tiles each, times the K parts.
+__host__ __device__ constexpr int gateup_blocks(int inter) { return inter / 128; }
+__host__ __device__ constexpr int down_blocks(int bits, int ksplit) { return H / (4 * down_rows(bits)) * ksplit; }
+
 template <int BITS, bool SPLIT, int G, int MTL>
 __global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
-  gateup_small_body<BITS, SPLIT, G, MTL>(a, blockIdx.x);
+  const int nb = gateup_blocks(a.w.inter);
+  gateup_small_body<BITS, SPLIT, G, MTL>(a, xcd_run(blockIdx.x, live_tiles(a, MTL) * nb));
 }
 template <int BITS, int G, int INTER, int KSPLIT, int MTL>
 __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
-  down_small_body<BITS, G, INTER, KSPLIT, MTL>(a, blockIdx.x);
+  down_small_body<BITS, G, INTER, KSPLIT, MTL>(a, xcd_run(blockIdx.x, live_tiles(a, MTL) * down_blocks(BITS, KSPLIT)));
 }
 // The shared expert does not depend on routing: with small tiles its
 // workgroups run in the same launch as the routed experts' (shared tiles
@@ -2496,13 +2522,15 @@ __global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
 // at once), which fills the compute units the few shared tiles would leave idle.
 template <int BR, int GR, int BS, int GS, bool SPLIT, int MTL>
 __global__ __launch_bounds__(512) void gateup_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
-  if ((int)blockIdx.x < n_shared) gateup_small_body<BS, SPLIT, GS, MTL>(sh, blockIdx.x);
-  else gateup_small_body<BR, SPLIT, GR, MTL>(r, blockIdx.x - n_shared);
+  const int lb = xcd_run(blockIdx.x, n_shared + *r.ntiles * gateup_blocks(I));
+  if (lb < n_shared) gateup_small_body<BS, SPLIT, GS, MTL>(sh, lb);
+  else gateup_small_body<BR, SPLIT, GR, MTL>(r, lb - n_shared);
 }
 template <int BR, int GR, int BS, int GS, int MTL>
 __global__ __launch_bounds__(512) void down_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
-  if ((int)blockIdx.x < n_shared) down_small_body<BS, GS, IS, 2, MTL>(sh, blockIdx.x);
-  else down_small_body<BR, GR, I, 1, MTL>(r, blockIdx.x - n_shared);
+  const int lb = xcd_run(blockIdx.x, n_shared + *r.ntiles * down_blocks(BR, 1));
+  if (lb < n_shared) down_small_body<BS, GS, IS, 2, MTL>(sh, lb);
+  else down_small_body<BR, GR, I, 1, MTL>(r, lb - n_shared);
 }
 
 // y[t] (+)= ys[t] (+ ys2[t]) + sum_j w[t,j] * ysorted[pos_of[t*6+j]], picks added in order.
