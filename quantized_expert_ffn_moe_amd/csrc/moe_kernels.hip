@@ -1525,6 +1525,23 @@ __device__ __forceinline__ half8 unpack_int4(uint32_t w) {
 
 // two int8 words (codes k0..k3, k4..k7 in bytes, two's complement) -> exact
 // f16 codes in order [k0, k2, k1, k3, k4, k6, k5, k7] (byte ^ 0x80 = code + 128).
+// Values fetched stages ahead of their use: an empty asm that takes the
+// registers as in/out operands keeps every operation on them after this point
+// (its place after the stage's workgroup barrier is fixed).  Without it the
+// compiler moved the f32/bf16 -> f16 conversion of the A rows up to their
+// load, and the wait for that just-issued load drained every fetch in flight
+// (the in-order load counter), which left the software pipeline one stage deep.
+__device__ __forceinline__ void hold(uint4& v) {
+  u32x4 t = {v.x, v.y, v.z, v.w};
+  asm volatile("" : "+v"(t));
+  v = make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void hold(uint2& v) {
+  uint32_t x = v.x, y = v.y;
+  asm volatile("" : "+v"(x), "+v"(y));
+  v = make_uint2(x, y);
+}
+
 __device__ __forceinline__ half8 unpack_int8(uint32_t w0, uint32_t w1) {
   const half2v m1152 = {(_Float16)-1152.f, (_Float16)-1152.f};
   const half2v a = as_h2((w0 & 0x00FF00FFu) ^ 0x64806480u) + m1152;
@@ -1672,11 +1689,14 @@ __device__ __forceinline__ void store_a(_Float16* lds, const AStage<F32>& A) {
     const int seg = tid + GT * j, row = seg >> 4, kk = 8 * (seg & 15);
     float v[8];
     if (F32) {
-      const uint4 a0 = A.raw[j][0], a1 = A.raw[j][F32 ? 1 : 0];
+      uint4 a0 = A.raw[j][0], a1 = A.raw[j][F32 ? 1 : 0];
+      hold(a0);
+      hold(a1);
       v[0] = __uint_as_float(a0.x); v[1] = __uint_as_float(a0.y); v[2] = __uint_as_float(a0.z); v[3] = __uint_as_float(a0.w);
       v[4] = __uint_as_float(a1.x); v[5] = __uint_as_float(a1.y); v[6] = __uint_as_float(a1.z); v[7] = __uint_as_float(a1.w);
     } else {
-      const uint4 u = A.raw[j][0];
+      uint4 u = A.raw[j][0];
+      hold(u);
       const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -2154,12 +2174,15 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
   auto store_a1 = [&](_Float16* l, float* xl, const uint4 (&ar)[APL]) {
     const int row = tid >> 4, kk = 8 * (tid & 15);
     float v[8];
+    uint4 r0 = ar[0], r1 = ar[APL - 1];
+    hold(r0);
+    if (F32) hold(r1);
     if (F32) {
-      const uint4 a0 = ar[0], a1 = ar[APL - 1];
+      const uint4 a0 = r0, a1 = r1;
       v[0] = __uint_as_float(a0.x); v[1] = __uint_as_float(a0.y); v[2] = __uint_as_float(a0.z); v[3] = __uint_as_float(a0.w);
       v[4] = __uint_as_float(a1.x); v[5] = __uint_as_float(a1.y); v[6] = __uint_as_float(a1.z); v[7] = __uint_as_float(a1.w);
     } else {
-      const uint32_t uw[4] = {ar[0].x, ar[0].y, ar[0].z, ar[0].w};
+      const uint32_t uw[4] = {r0.x, r0.y, r0.z, r0.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v[2 * i] = __uint_as_float(uw[i] << 16);
@@ -2384,9 +2407,12 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
   };
   auto store_a1 = [&](_Float16* l, float* xl, const uint4 (&ar)[2]) {
     const int row = tid >> 4, kk = 8 * (tid & 15);
-    const float v[8] = {__uint_as_float(ar[0].x), __uint_as_float(ar[0].y), __uint_as_float(ar[0].z),
-                        __uint_as_float(ar[0].w), __uint_as_float(ar[1].x), __uint_as_float(ar[1].y),
-                        __uint_as_float(ar[1].z), __uint_as_float(ar[1].w)};
+    uint4 r0 = ar[0], r1 = ar[1];
+    hold(r0);
+    hold(r1);
+    const float v[8] = {__uint_as_float(r0.x), __uint_as_float(r0.y), __uint_as_float(r0.z),
+                        __uint_as_float(r0.w), __uint_as_float(r1.x), __uint_as_float(r1.y),
+                        __uint_as_float(r1.z), __uint_as_float(r1.w)};
     half8 hi, lo;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
