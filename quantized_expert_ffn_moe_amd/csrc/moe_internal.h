@@ -15,6 +15,7 @@ constexpr int TILE = 1024;   // bytes of one packed 16-row tile
 constexpr int MT = 64;       // token rows per tile of the grouped GEMMs (large tiles)
 constexpr int MT_SMALL = 32; // rows per tile when experts see few rows each
 constexpr int MT_TINY = 16;  // rows per tile when experts see very few rows each (fused shared/routed launches)
+constexpr int SMALL_WAVES = 8; // waves per workgroup of the small tiles (16 gate/up columns or half a down row tile each)
 constexpr int SMALL_TILE_MAX_SLOTS = 64 * 64;   // (token, pick) slots up to which the small tiles run
 constexpr int TINY_TILE_MAX_SLOTS = 64 * 8;     // ... and the 16-row tiles (about 8 rows per expert or fewer)
 constexpr int DECODE_MAX_T = 5;  // largest token count routed to the GEMV path by default (measured crossover)

@@ -2089,7 +2089,7 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
 // each 32-column sub-block adds beta * X to its scaled product (X = the sum of
 // the row's inputs over the sub-block, formed while A is staged; s and beta
 // from the row's super-block record, fetched with the B tiles).
-template <int BITS, bool SPLIT, int G, int MTL>
+template <int BITS, bool SPLIT, int G, int MTL, int NW>
 __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid) {
   constexpr bool K4 = G == Q4K;
   static_assert(!K4 || BITS == 4, "two-level codes are 4-bit");
@@ -2112,8 +2112,11 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
   static_assert(!K4 || (SB % 2 == 0 && Q4K_SB == 2 * KS), "a stage is a fixed half of a super-block");
   constexpr bool F32 = SPLIT;
   constexpr int APL = SPLIT ? 2 : 1;
-  constexpr int NSEG = MTL * KS / 8;        // A segments (8 elements) per stage: one per thread up to 512
-  const int inter = a.w.inter, ncb = inter / 128;
+  constexpr int NT = 64 * NW;               // threads of the workgroup
+  constexpr int NSEG = MTL * KS / 8;        // A segments (8 elements) per stage
+  constexpr int AS = NSEG > NT ? NSEG / NT : 1;   // ... per thread
+  static_assert(NSEG <= NT * AS, "every A segment has a thread");
+  const int inter = a.w.inter, ncb = inter / (16 * NW);
   const int tile = bid / ncb, cb = bid % ncb;
   const TileInfo ti = tile_info(a, tile, MTL);
   if (!ti.valid) return;
@@ -2131,9 +2134,9 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
   const uint8_t* eq = a.w.q + (size_t)e * a.w.e_bytes;
   const float* es = a.w.s + (size_t)e * a.w.e_scales;
   const size_t mbytes = matrix_bytes(BITS, inter, H), mscales = (size_t)inter * NG;
-  // B tiles of this wave: n-subtile 8 cb + w of the gate (i = 0) and the up
+  // B tiles of this wave: n-subtile NW cb + w of the gate (i = 0) and the up
   // (i = 1) matrix; each descriptor spans one n-tile's row of K tiles
-  const int nt = 8 * cb + wv;
+  const int nt = NW * cb + wv;
   __amdgpu_buffer_rsrc_t rb[2], rs[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -2160,21 +2163,29 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
       for (int h = 0; h < NB; ++h) bd[i][h] = wload16(rb[i], (uint32_t)(st * NB + h) * TILE + lane * 16);
     }
   };
-  // A: one 8-element segment per thread per stage (row tid / 16, columns 8 (tid % 16));
-  // with 16-row tiles only the first 256 threads hold one
-  const bool a_act = NSEG >= 512 || tid < NSEG;
-  auto fetch_a1 = [&](uint4 (&ar)[APL], int k0, bool live) {
-    const int row = a_act ? tid >> 4 : 0, kk = 8 * (tid & 15);
-    const int src = a_act ? arow[row] : -1;
-    constexpr uint32_t ELT = F32 ? 4 : 2;
-    const uint32_t off = (live && src >= 0) ? ((uint32_t)src * H + k0 + kk) * ELT : 0x80000000u;
-    ar[0] = wload16(ra, off);
-    if (F32) ar[APL - 1] = wload16(ra, off + 16);
+  // A: AS 8-element segments per thread per stage (segment u = tid + NT j:
+  // row u / 16, columns 8 (u % 16)); when the workgroup has more threads than
+  // segments only the first NSEG threads hold one
+  const bool a_act = NSEG >= NT || tid < NSEG;
+  auto fetch_a1 = [&](uint4 (&ar)[AS][APL], int k0, bool live) {
+#pragma unroll
+    for (int j = 0; j < AS; ++j) {
+      const int u = tid + NT * j;
+      const int row = a_act ? u >> 4 : 0, kk = 8 * (u & 15);
+      const int src = a_act ? arow[row] : -1;
+      constexpr uint32_t ELT = F32 ? 4 : 2;
+      const uint32_t off = (live && src >= 0) ? ((uint32_t)src * H + k0 + kk) * ELT : 0x80000000u;
+      ar[j][0] = wload16(ra, off);
+      if (F32) ar[j][APL - 1] = wload16(ra, off + 16);
+    }
   };
-  auto store_a1 = [&](_Float16* l, float* xl, const uint4 (&ar)[APL]) {
-    const int row = tid >> 4, kk = 8 * (tid & 15);
+  auto store_a1 = [&](_Float16* l, float* xl, const uint4 (&ar)[AS][APL]) {
+#pragma unroll
+  for (int j = 0; j < AS; ++j) {
+    const int u = tid + NT * j;
+    const int row = u >> 4, kk = 8 * (u & 15);
     float v[8];
-    uint4 r0 = ar[0], r1 = ar[APL - 1];
+    uint4 r0 = ar[j][0], r1 = ar[j][APL - 1];
     hold(r0);
     if (F32) hold(r1);
     if (F32) {
@@ -2202,13 +2213,13 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
       // consecutive lanes (whole waves are active or idle together)
       float xs = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
       xs = group_sum<4>(xs);
-      if (a_act && (tid & 3) == 0) xl[((tid & 15) >> 2) * MTL + row] = 8.0f * xs;
+      if (a_act && (u & 3) == 0) xl[((u & 15) >> 2) * MTL + row] = 8.0f * xs;
     }
-    if (!a_act) return;
+    if (!a_act) continue;
     *(half8*)(l + row * LDS_ROW + kk) = hi;
     if (SPLIT) *(half8*)(l + MTL * LDS_ROW + row * LDS_ROW + kk) = lo;
+  }
   };
-  static_assert(NSEG <= 512, "at most one A segment per thread");
   float4v acc[2][MS], ctmp[2][MS];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -2218,7 +2229,7 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
 
   // Fully unrolled stage loop: every ring slot is a fixed register set, so no
   // value is copied while its load is still in flight.
-  uint4 A[AR][APL];   // A(s) lives in slot s % AR until it is stored to LDS
+  uint4 A[AR][AS][APL];   // A(s) lives in slot s % AR until it is stored to LDS
 #pragma unroll
   for (int s0 = 0; s0 < AR; ++s0) fetch_a1(A[s0], s0 * KS, s0 < NSTAGE);
 #pragma unroll
@@ -2320,12 +2331,14 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
 // 2i and 2i + 1 share row tile 4cb + i (64 int4 or 32 int8 output columns),
 // each taking half of its 16-row n-subtiles (the matching half of every
 // 16-byte lane word).  Same software pipeline as gate/up.
-template <int BITS, int G, int INTER, int KSPLIT, int MTL>
+template <int BITS, int G, int INTER, int KSPLIT, int MTL, int NW>
 __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
   constexpr bool K4 = G == Q4K;            // two-level format (see gateup_small_body)
   static_assert(!K4 || BITS == 4, "two-level codes are 4-bit");
   constexpr int GG = K4 ? Q4K_SUB : G;
-  constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / 4, MS = MTL / 16;
+  constexpr int DR = down_rows(BITS), NRT = H / DR, NSUB = DR / 16, NCB = NRT / (NW / 2), MS = MTL / 16;
+  constexpr int NT = 64 * NW, NSEG = MTL * KS / 8, AS = NSEG > NT ? NSEG / NT : 1;
+  static_assert(NSEG <= NT * AS, "every A segment has a thread");
   constexpr int NSW = NSUB / 2;             // n-subtiles per wave (half a row tile)
   constexpr int CPG = GG / 32, GPS = KS / GG, NSTAGE = INTER / KS / KSPLIT;
   static_assert((INTER / KS) % KSPLIT == 0, "K halves of whole stages");
@@ -2350,7 +2363,7 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
   const int e = wave_uniform(ti.e);
   const size_t mbytes = matrix_bytes(BITS, inter, H);
   const int ngk = inter / GG;
-  const int rt = 4 * cb + (wv >> 1), hh = wv & 1;
+  const int rt = (NW / 2) * cb + (wv >> 1), hh = wv & 1;
   const __amdgpu_buffer_rsrc_t rb = weight_rsrc(a.w.q + (size_t)e * a.w.e_bytes + 2 * mbytes, (uint32_t)mbytes);
   // two-level: d | dmin words [super-block][slot] and sc | m << 8 halfwords
   // [sub-block][slot], slot (rt, r, j) = row DR rt + 16 j + r
@@ -2397,17 +2410,24 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
   };
   // A (h, f32 as hi/lo f16 planes): one 8-element segment per thread per
   // stage; with 16-row tiles only the first 256 threads hold one
-  const bool a_act = MTL * KS / 8 >= 512 || tid < MTL * KS / 8;
-  auto fetch_a1 = [&](uint4 (&ar)[2], int k0, bool live) {
-    const int row = a_act ? tid >> 4 : 0, kk = 8 * (tid & 15);
-    const int src = a_act ? arow[row] : -1;
-    const uint32_t off = (live && src >= 0) ? ((uint32_t)src * INTER + k0 + kk) * 4 : 0x80000000u;
-    ar[0] = wload16(ra, off);
-    ar[1] = wload16(ra, off + 16);
+  const bool a_act = NSEG >= NT || tid < NSEG;
+  auto fetch_a1 = [&](uint4 (&ar)[AS][2], int k0, bool live) {
+#pragma unroll
+    for (int j = 0; j < AS; ++j) {
+      const int u = tid + NT * j;
+      const int row = a_act ? u >> 4 : 0, kk = 8 * (u & 15);
+      const int src = a_act ? arow[row] : -1;
+      const uint32_t off = (live && src >= 0) ? ((uint32_t)src * INTER + k0 + kk) * 4 : 0x80000000u;
+      ar[j][0] = wload16(ra, off);
+      ar[j][1] = wload16(ra, off + 16);
+    }
   };
-  auto store_a1 = [&](_Float16* l, float* xl, const uint4 (&ar)[2]) {
-    const int row = tid >> 4, kk = 8 * (tid & 15);
-    uint4 r0 = ar[0], r1 = ar[1];
+  auto store_a1 = [&](_Float16* l, float* xl, const uint4 (&ar)[AS][2]) {
+#pragma unroll
+  for (int j = 0; j < AS; ++j) {
+    const int u = tid + NT * j;
+    const int row = u >> 4, kk = 8 * (u & 15);
+    uint4 r0 = ar[j][0], r1 = ar[j][1];
     hold(r0);
     hold(r1);
     const float v[8] = {__uint_as_float(r0.x), __uint_as_float(r0.y), __uint_as_float(r0.z),
@@ -2424,13 +2444,13 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
     if constexpr (K4) {
       float xs = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
       xs = group_sum<4>(xs);
-      if (a_act && (tid & 3) == 0) xl[((tid & 15) >> 2) * MTL + row] = 8.0f * xs;
+      if (a_act && (u & 3) == 0) xl[((u & 15) >> 2) * MTL + row] = 8.0f * xs;
     }
-    if (!a_act) return;
+    if (!a_act) continue;
     *(half8*)(l + row * LDS_ROW + kk) = hi;
     *(half8*)(l + MTL * LDS_ROW + row * LDS_ROW + kk) = lo;
+  }
   };
-  static_assert(MTL * KS / 8 <= 512, "at most one A segment per thread");
   float4v acc[NSW][MS], ctmp[NSW][MS];
 #pragma unroll
   for (int j = 0; j < NSW; ++j)
@@ -2438,7 +2458,7 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
     for (int ms = 0; ms < MS; ++ms) { acc[j][ms] = float4v{0, 0, 0, 0}; ctmp[j][ms] = float4v{0, 0, 0, 0}; }
   __syncthreads();   // arow
 
-  uint4 A[AR][2];
+  uint4 A[AR][AS][2];
 #pragma unroll
   for (int sp = 0; sp < AR; ++sp) fetch_a1(A[sp], (s0 + sp) * KS, sp < NSTAGE);
 #pragma unroll
@@ -2530,33 +2550,36 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
 
 // Workgroups per row tile: gate/up 128 intermediate columns each; down four
 // packed row tiles each, times the K parts.
-__host__ __device__ constexpr int gateup_blocks(int inter) { return inter / 128; }
-__host__ __device__ constexpr int down_blocks(int bits, int ksplit) { return H / (4 * down_rows(bits)) * ksplit; }
+__host__ __device__ constexpr int gateup_blocks(int inter) { return inter / (16 * SMALL_WAVES); }
+__host__ __device__ constexpr int down_blocks(int bits, int ksplit) {
+  return H / (SMALL_WAVES / 2 * down_rows(bits)) * ksplit;
+}
 
 template <int BITS, bool SPLIT, int G, int MTL>
-__global__ __launch_bounds__(512) void gateup_small_kernel(GroupedArgs a) {
+__global__ __launch_bounds__(64 * SMALL_WAVES) void gateup_small_kernel(GroupedArgs a) {
   const int nb = gateup_blocks(a.w.inter);
-  gateup_small_body<BITS, SPLIT, G, MTL>(a, xcd_run(blockIdx.x, live_tiles(a, MTL) * nb));
+  gateup_small_body<BITS, SPLIT, G, MTL, SMALL_WAVES>(a, xcd_run(blockIdx.x, live_tiles(a, MTL) * nb));
 }
 template <int BITS, int G, int INTER, int KSPLIT, int MTL>
-__global__ __launch_bounds__(512) void down_small_kernel(GroupedArgs a) {
-  down_small_body<BITS, G, INTER, KSPLIT, MTL>(a, xcd_run(blockIdx.x, live_tiles(a, MTL) * down_blocks(BITS, KSPLIT)));
+__global__ __launch_bounds__(64 * SMALL_WAVES) void down_small_kernel(GroupedArgs a) {
+  down_small_body<BITS, G, INTER, KSPLIT, MTL, SMALL_WAVES>(
+      a, xcd_run(blockIdx.x, live_tiles(a, MTL) * down_blocks(BITS, KSPLIT)));
 }
 // The shared expert does not depend on routing: with small tiles its
 // workgroups run in the same launch as the routed experts' (shared tiles
 // first, so they start at once; routed tiles past the histogram's count exit
 // at once), which fills the compute units the few shared tiles would leave idle.
 template <int BR, int GR, int BS, int GS, bool SPLIT, int MTL>
-__global__ __launch_bounds__(512) void gateup_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
+__global__ __launch_bounds__(64 * SMALL_WAVES) void gateup_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
   const int lb = xcd_run(blockIdx.x, n_shared + *r.ntiles * gateup_blocks(I));
-  if (lb < n_shared) gateup_small_body<BS, SPLIT, GS, MTL>(sh, lb);
-  else gateup_small_body<BR, SPLIT, GR, MTL>(r, lb - n_shared);
+  if (lb < n_shared) gateup_small_body<BS, SPLIT, GS, MTL, SMALL_WAVES>(sh, lb);
+  else gateup_small_body<BR, SPLIT, GR, MTL, SMALL_WAVES>(r, lb - n_shared);
 }
 template <int BR, int GR, int BS, int GS, int MTL>
-__global__ __launch_bounds__(512) void down_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
+__global__ __launch_bounds__(64 * SMALL_WAVES) void down_small_pair_kernel(GroupedArgs r, GroupedArgs sh, int n_shared) {
   const int lb = xcd_run(blockIdx.x, n_shared + *r.ntiles * down_blocks(BR, 1));
-  if (lb < n_shared) down_small_body<BS, GS, IS, 2, MTL>(sh, lb);
-  else down_small_body<BR, GR, I, 1, MTL>(r, lb - n_shared);
+  if (lb < n_shared) down_small_body<BS, GS, IS, 2, MTL, SMALL_WAVES>(sh, lb);
+  else down_small_body<BR, GR, I, 1, MTL, SMALL_WAVES>(r, lb - n_shared);
 }
 
 // y[t] (+)= ys[t] (+ ys2[t]) + sum_j w[t,j] * ysorted[pos_of[t*6+j]], picks added in order.
@@ -2696,9 +2719,9 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
 template <int BITS, int G>
 static void gateup_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
   if (small) {
-    const dim3 grid(max_tiles * (a.w.inter / 128));
-    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<BITS, true, G, MT_SMALL>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gateup_small_kernel<BITS, false, G, MT_SMALL>), grid, dim3(512), 0, s, a);
+    const dim3 grid(max_tiles * gateup_blocks(a.w.inter));
+    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<BITS, true, G, MT_SMALL>), grid, dim3(64 * SMALL_WAVES), 0, s, a);
+    else hipLaunchKernelGGL((gateup_small_kernel<BITS, false, G, MT_SMALL>), grid, dim3(64 * SMALL_WAVES), 0, s, a);
   } else {
     const dim3 grid(max_tiles * (a.w.inter / 128));   // 128 gate + 128 up columns per workgroup
     if (a.af) hipLaunchKernelGGL((grouped_gateup_kernel<BITS, true, G>), grid, dim3(GT), 0, s, a);
@@ -2722,11 +2745,11 @@ hipError_t launch_grouped_gateup(const GroupedArgs& a, int max_tiles, bool small
 template <int BITS, int G>
 static void down_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipStream_t s) {
   if (small) {
-    const dim3 grid(max_tiles * (H / (4 * down_rows(BITS))));
+    const dim3 grid(max_tiles * down_blocks(BITS, 1));
     if (a.w.inter == IS && a.ksplit == 2)
-      hipLaunchKernelGGL((down_small_kernel<BITS, G, IS, 2, MT_SMALL>), dim3(2 * grid.x), dim3(512), 0, s, a);
-    else if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<BITS, G, IS, 1, MT_SMALL>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((down_small_kernel<BITS, G, I, 1, MT_SMALL>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((down_small_kernel<BITS, G, IS, 2, MT_SMALL>), dim3(2 * grid.x), dim3(64 * SMALL_WAVES), 0, s, a);
+    else if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<BITS, G, IS, 1, MT_SMALL>), grid, dim3(64 * SMALL_WAVES), 0, s, a);
+    else hipLaunchKernelGGL((down_small_kernel<BITS, G, I, 1, MT_SMALL>), grid, dim3(64 * SMALL_WAVES), 0, s, a);
   } else {
     const dim3 grid(max_tiles * (H / 256));             // 256 output columns per workgroup
     if (a.w.inter == IS && a.ksplit == 2)
@@ -2739,15 +2762,15 @@ static void down_dispatch(const GroupedArgs& a, int max_tiles, bool small, hipSt
 // Two-level format: the 32-row small tiles at every token count.
 hipError_t launch_grouped_q4k(const GroupedArgs& a, int max_tiles, bool down, hipStream_t s) {
   if (!down) {
-    const dim3 grid(max_tiles * (a.w.inter / 128));
-    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<4, true, Q4K, MT_SMALL>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gateup_small_kernel<4, false, Q4K, MT_SMALL>), grid, dim3(512), 0, s, a);
+    const dim3 grid(max_tiles * gateup_blocks(a.w.inter));
+    if (a.af) hipLaunchKernelGGL((gateup_small_kernel<4, true, Q4K, MT_SMALL>), grid, dim3(64 * SMALL_WAVES), 0, s, a);
+    else hipLaunchKernelGGL((gateup_small_kernel<4, false, Q4K, MT_SMALL>), grid, dim3(64 * SMALL_WAVES), 0, s, a);
   } else {
-    const dim3 grid(max_tiles * (H / (4 * down_rows(4))));
+    const dim3 grid(max_tiles * down_blocks(4, 1));
     if (a.w.inter == IS && a.ksplit == 2)
-      hipLaunchKernelGGL((down_small_kernel<4, Q4K, IS, 2, MT_SMALL>), dim3(2 * grid.x), dim3(512), 0, s, a);
-    else if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<4, Q4K, IS, 1, MT_SMALL>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((down_small_kernel<4, Q4K, I, 1, MT_SMALL>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((down_small_kernel<4, Q4K, IS, 2, MT_SMALL>), dim3(2 * grid.x), dim3(64 * SMALL_WAVES), 0, s, a);
+    else if (a.w.inter == IS) hipLaunchKernelGGL((down_small_kernel<4, Q4K, IS, 1, MT_SMALL>), grid, dim3(64 * SMALL_WAVES), 0, s, a);
+    else hipLaunchKernelGGL((down_small_kernel<4, Q4K, I, 1, MT_SMALL>), grid, dim3(64 * SMALL_WAVES), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -2769,14 +2792,14 @@ template <int BR, int GR, int BS, int GS, int MTL>
 static void pair_dispatch(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down,
                           hipStream_t s) {
   if (!down) {
-    const int ns = s_tiles * (IS / 128), nr = r_tiles * (I / 128);
+    const int ns = s_tiles * gateup_blocks(IS), nr = r_tiles * gateup_blocks(I);
     if (r.af)
-      hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, true, MTL>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
+      hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, true, MTL>), dim3(ns + nr), dim3(64 * SMALL_WAVES), 0, s, r, sh, ns);
     else
-      hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, false, MTL>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
+      hipLaunchKernelGGL((gateup_small_pair_kernel<BR, GR, BS, GS, false, MTL>), dim3(ns + nr), dim3(64 * SMALL_WAVES), 0, s, r, sh, ns);
   } else {
-    const int ns = 2 * s_tiles * (H / (4 * down_rows(BS))), nr = r_tiles * (H / (4 * down_rows(BR)));
-    hipLaunchKernelGGL((down_small_pair_kernel<BR, GR, BS, GS, MTL>), dim3(ns + nr), dim3(512), 0, s, r, sh, ns);
+    const int ns = s_tiles * down_blocks(BS, 2), nr = r_tiles * down_blocks(BR, 1);
+    hipLaunchKernelGGL((down_small_pair_kernel<BR, GR, BS, GS, MTL>), dim3(ns + nr), dim3(64 * SMALL_WAVES), 0, s, r, sh, ns);
   }
 }
 template <int BR, int GR, int BS, int GS>
