@@ -32,6 +32,20 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ int live_slots(int n_gen) { return min(max(n_gen, 0) + 1, RSWA_W); }
+
+// one output element: f32, or as the bf16 halves of the split_row layout
+// (hi = bf16(v), lo = bf16(v - hi)) that the attention block's output
+// projection reads
+__device__ __forceinline__ void store_out(const RswaArgs& a, size_t idx, float v) {
+  if (a.out_hl) {
+    const uint16_t hi = to_bf16(v);
+    uint16_t* g = a.out_hl + (idx & ~(size_t)7) * 2 + (idx & 7);
+    g[0] = hi;
+    g[8] = to_bf16(v - __uint_as_float((uint32_t)hi << 16));
+  } else {
+    a.out[idx] = v;
+  }
+}
 }  // namespace
 
 // The key list of one (stream, head).
@@ -185,7 +199,7 @@ __global__ __launch_bounds__(NT) void rswa_row_kernel(RswaArgs a) {
     __syncthreads();
     if (tid < ATT_D) acc += acc2[tid];
   }
-  if (tid < ATT_D) a.out[((size_t)s * ATT_HEADS + h) * ATT_D + tid] = acc / l_run;
+  if (tid < ATT_D) store_out(a, ((size_t)s * ATT_HEADS + h) * ATT_D + tid, acc / l_run);
 }
 
 // 2. partials of one chunk: blockIdx = (chunk, head, stream)
@@ -249,7 +263,7 @@ __global__ __launch_bounds__(ATT_D) void rswa_merge_kernel(RswaArgs a) {
     L = __fmaf_rn(part[c * RSWA_PART + 1], w, L);
     o = __fmaf_rn(part[c * RSWA_PART + 2 + d], w, o);
   }
-  a.out[((size_t)s * ATT_HEADS + h) * ATT_D + d] = o / L;
+  store_out(a, ((size_t)s * ATT_HEADS + h) * ATT_D + d, o / L);
 }
 
 int rswa_chunks(int n_ref) { return (n_ref + RSWA_W + RSWA_CHUNK - 1) / RSWA_CHUNK; }

@@ -204,6 +204,7 @@ struct RswaArgs {
   const int32_t* n_gen;                                     // [S]
   float* part;                                              // [S][10][n_chunks][RSWA_PART]
   float* out;                                               // [S][10][128]
+  uint16_t* out_hl = nullptr;   // if set, the output goes here instead, as bf16 halves (split_row layout)
 };
 int rswa_chunks(int n_ref);
 hipError_t launch_rswa(const RswaArgs& a, hipStream_t s);
@@ -211,10 +212,16 @@ hipError_t launch_rswa(const RswaArgs& a, hipStream_t s);
 // Attention projections: y[t][n] (+)= sum_k a[t][k] W[n][k], K = H, bf16 W
 // [N][H]; output column n of token t at y[((n / H) * T + t) * H + n % H]
 // (so q, k and v of a [3H][H] weight land in three [T][H] arrays).
+// The activations come either as f32 rows (a) or already split into bf16
+// halves (a_hl, the split_row layout below); exactly one is set.
 struct ProjArgs {
-  const float* a; const uint16_t* w; float* y;
+  const float* a; const uint16_t* a_hl; const uint16_t* w; float* y;
   int T, N, accumulate;
 };
+// split_row layout of an f32 row [H] as bf16 halves: per 8-element group g,
+// 16 bytes of hi = bf16_rne(x) for its 8 elements, then 16 bytes of
+// lo = bf16_rne(x - hi); 4 bytes per element, like the f32 row.
+constexpr int PROJ_HL_MIN_T = 16;   // from this many streams the projections read split rows
 hipError_t launch_proj(const ProjArgs& p, hipStream_t s);
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
@@ -236,6 +243,7 @@ hipError_t launch_grouped_q4k(const GroupedArgs& a, int max_tiles, bool down, hi
 bool small_pair_available(int rbits, int rgroup, int sbits, int sgroup);
 bool launch_small_pair(const GroupedArgs& r, int r_tiles, const GroupedArgs& sh, int s_tiles, bool down, int mtl,
                        hipStream_t s);
-hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps, hipStream_t s);
+// z_mode: 0 f32, 1 bf16, 2 split_row bf16 halves
+hipError_t launch_rmsnorm(const float* h, void* z, int z_mode, int T, float eps, hipStream_t s);
 
 }  // namespace moe

@@ -2604,7 +2604,7 @@ __global__ __launch_bounds__(320) void combine_kernel(CombineArgs a) {
   *yp = v;
 }
 
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, void* z, int z_bf16, float eps) {
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, void* z, int z_mode, float eps) {
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   float v[5];
@@ -2618,8 +2618,17 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, void* z, i
   for (int i = 0; i < 5; ++i) {
     const float zz = v[i] * inv;
     const size_t idx = (size_t)t * H + tid + 256 * i;
-    if (z_bf16) ((uint16_t*)z)[idx] = (uint16_t)(__float_as_uint(bf16_rne(zz)) >> 16);
-    else ((float*)z)[idx] = zz;
+    if (z_mode == 1) {
+      ((uint16_t*)z)[idx] = (uint16_t)(__float_as_uint(bf16_rne(zz)) >> 16);
+    } else if (z_mode == 2) {
+      // split_row: bf16 hi and lo halves of the group's 8 elements, 16 bytes each
+      const float hi = bf16_rne(zz);
+      uint16_t* g = (uint16_t*)z + (idx & ~(size_t)7) * 2 + (idx & 7);
+      g[0] = (uint16_t)(__float_as_uint(hi) >> 16);
+      g[8] = (uint16_t)(__float_as_uint(bf16_rne(zz - hi)) >> 16);
+    } else {
+      ((float*)z)[idx] = zz;
+    }
   }
 }
 
@@ -2842,8 +2851,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(const float* h, void* z, int z_bf16, int T, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, s, h, z, z_bf16, eps);
+hipError_t launch_rmsnorm(const float* h, void* z, int z_mode, int T, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, s, h, z, z_mode, eps);
   return hipGetLastError();
 }
 

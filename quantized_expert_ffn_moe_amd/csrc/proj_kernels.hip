@@ -111,9 +111,111 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs p) {
   }
 }
 
+// The same product for many streams, with the activations already split into
+// bf16 halves by their producer (the RMSNorm, or the attention step, in the
+// split_row layout): the per-tile split, which every column workgroup
+// repeated for every stream, is gone, each lane's two 16-byte loads are its
+// A operands as they are, and the next 16-stream tile is fetched while the
+// current one is multiplied.  A workgroup owns NS 16-column subtiles (each
+// wave keeps its K quarter of all of them in registers), so the activations
+// are read once per 16 NS columns.  The four K-quarter partials are added by
+// all 256 threads in the order of proj_kernel, and every column sees
+// proj_kernel's MFMA sequence, so both give the same bits.
+template <int NS>
+__global__ __launch_bounds__(256) void proj_hl_kernel(ProjArgs p) {
+  constexpr int NC = 16 * NS;                    // columns of the workgroup
+  __shared__ float red[2][4][16][NC + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q = lane >> 4;
+  const int n0 = NC * blockIdx.x, tb = 64 * blockIdx.y;
+  const int k0 = PJ_KW * wv + 8 * q;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w), (short)0, (uint32_t)p.N * H * 2, 0x00020000);
+  uint4 b[NS][PJ_KS];
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+    for (int s = 0; s < PJ_KS; ++s) {
+      const u32x4p v =
+          __builtin_amdgcn_raw_buffer_load_b128(rw, ((uint32_t)(n0 + 16 * ns + r) * H + k0 + 32 * s) * 2, 0, 0);
+      b[ns][s] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  // rows past T read zeros (buffer range); 4 bytes per element
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.a_hl), (short)0, (uint32_t)p.T * H * 4, 0x00020000);
+  u32x4p x[2][PJ_KS][2];
+  auto load = [&](u32x4p (&xb)[PJ_KS][2], int t0) {
+#pragma unroll
+    for (int s = 0; s < PJ_KS; ++s) {
+      const uint32_t off = ((uint32_t)(t0 + r) * H + k0 + 32 * s) * 4;
+      xb[s][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);        // hi of the 8 elements
+      xb[s][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, off + 16, 0, 0);   // lo
+    }
+  };
+  load(x[0], tb);
+  // this thread's outputs of each tile: token row tid / 16, columns
+  // n0 + tid % 16 + 16 ns, through a descriptor over y (rows past T: loads
+  // read zeros, stores are dropped)
+  const int rr = tid >> 4, cc = tid & 15;
+  const __amdgpu_buffer_rsrc_t ry =
+      __builtin_amdgcn_make_buffer_rsrc(p.y, (short)0, (uint32_t)(p.N / H) * p.T * H * 4, 0x00020000);
+#pragma unroll
+  for (int tt = 0; tt < PJ_TT; ++tt) {
+    const int t0 = tb + 16 * tt;
+    if (t0 >= p.T) break;
+    const int t = t0 + rr;
+    uint32_t yo[NS];
+    float yold[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const int n = n0 + 16 * ns + cc;
+      yo[ns] = t < p.T ? (((uint32_t)(n / H) * p.T + t) * H + n % H) * 4 : 0x80000000u;
+      // the old output (accumulating) is requested before the next tile's
+      // activations, so waiting for it never waits for them (in-order counter)
+      yold[ns] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ry, p.accumulate ? yo[ns] : 0x80000000u, 0, 0));
+    }
+    asm volatile("" ::: "memory");
+    if (tt + 1 < PJ_TT) load(x[(tt + 1) & 1], t0 + 16);   // unconditional: rows past T read zeros
+    float4p c[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) c[ns] = float4p{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < PJ_KS; ++s) {
+      const bf16x8 hi = __builtin_bit_cast(bf16x8, x[tt & 1][s][0]);
+      const bf16x8 lo = __builtin_bit_cast(bf16x8, x[tt & 1][s][1]);
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const bf16x8 bw = __builtin_bit_cast(bf16x8, u32x4p{b[ns][s].x, b[ns][s].y, b[ns][s].z, b[ns][s].w});
+        c[ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bw, c[ns], 0, 0, 0);
+        c[ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bw, c[ns], 0, 0, 0);
+      }
+    }
+    // lane (r, q) holds tokens t0 + 4 q + j of column n0 + 16 ns + r; red is
+    // double buffered, so one barrier per tile separates its writes from its reads
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[tt & 1][wv][4 * q + j][16 * ns + r] = c[ns][j];
+    __syncthreads();
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const int cl = 16 * ns + cc;
+      const float v = ((red[tt & 1][0][rr][cl] + red[tt & 1][1][rr][cl]) + red[tt & 1][2][rr][cl]) + red[tt & 1][3][rr][cl];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.accumulate ? yold[ns] + v : v), ry, yo[ns], 0, 0);
+    }
+  }
+}
+
 hipError_t launch_proj(const ProjArgs& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(proj_kernel, dim3(p.N / 16, (p.T + 16 * PJ_TT - 1) / (16 * PJ_TT)), dim3(256), 0, s, p);
+  const int tblocks = (p.T + 16 * PJ_TT - 1) / (16 * PJ_TT);
+  if (!p.a_hl) {
+    hipLaunchKernelGGL(proj_kernel, dim3(p.N / 16, tblocks), dim3(256), 0, s, p);
+  } else if ((p.N / 32) * tblocks >= 200) {
+    // 32 columns per workgroup halve the activation reads while keeping enough workgroups
+    hipLaunchKernelGGL(proj_hl_kernel<2>, dim3(p.N / 32, tblocks), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(proj_hl_kernel<1>, dim3(p.N / 16, tblocks), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -98,12 +98,13 @@ def check_attn(kvh, dev, h0, h, sample):
     return ratio
 
 
-@pytest.mark.parametrize("S,n_ref", [(1, 288), (1, 0), (4, 288), (16, 64), (128, 288)])
+@pytest.mark.parametrize("S,n_ref", [(1, 288), (1, 0), (4, 288), (16, 64), (17, 288), (65, 64), (128, 288)])
 def test_attn_block(lib, S, n_ref):
     n_gen = [127 + 53 * s for s in range(S)]
     say(f"attention block, {S} streams, n_ref {n_ref}")
     kvh, dev, h0, h = run_attn(S, n_ref, n_gen, seed=S)
-    sample = np.arange(S) if S <= 16 else np.sort(np.random.default_rng(S).choice(S, 12, replace=False))
+    # every stream up to 17 (the split-row projections start at 16 streams); else 12, the last one included
+    sample = np.arange(S) if S <= 17 else np.sort(np.append(np.random.default_rng(S).choice(S - 1, 11, replace=False), S - 1))
     r = check_attn(kvh, dev, h0, h, sample)
     say(f"  attention half err/rms {r:.2e} on {len(sample)} streams")
 
