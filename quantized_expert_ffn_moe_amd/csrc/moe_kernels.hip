@@ -176,20 +176,34 @@ __device__ __forceinline__ void router_rows(const RouterArgs& a, int t0, float* 
   __syncthreads();
   if (tid < nt) red[tid * 4] = invt;
   __syncthreads();
-  for (int tt = 0; tt < nt; ++tt) {
-    const float inv = red[tt * 4];
+  // z = x / rms, element by element: thread u takes 8 consecutive columns of
+  // a row, so z leaves in 16-byte stores (the values do not depend on which
+  // thread forms them)
+  constexpr int NG = TB * H / 8;
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int k = tid + 256 * i;
-      float z = zs[tt * ROW + k] * inv;
-      if (a.norm_bf16) {
-        z = bf16_rne(z);
-        if (store_z) ((uint16_t*)a.z)[(size_t)(t0 + tt) * H + k] = (uint16_t)(__float_as_uint(z) >> 16);
-      } else if (store_z) {
-        ((float*)a.z)[(size_t)(t0 + tt) * H + k] = z;
-      }
-      zs[tt * ROW + k] = z;
+  for (int j = 0; j < (NG + 255) / 256; ++j) {
+    const int u = tid + 256 * j;
+    if (u >= NG) break;
+    const int tt = u / (H / 8), c0 = 8 * (u % (H / 8));
+    if (tt >= nt) continue;
+    const float inv = red[tt * 4];
+    float* zr = &zs[tt * ROW + c0];
+    const float4 x0 = *(const float4*)zr, x1 = *(const float4*)(zr + 4);
+    float z[8] = {x0.x * inv, x0.y * inv, x0.z * inv, x0.w * inv, x1.x * inv, x1.y * inv, x1.z * inv, x1.w * inv};
+    if (a.norm_bf16) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = bf16_rne(z[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (__float_as_uint(z[2 * i]) >> 16) | (__float_as_uint(z[2 * i + 1]) & 0xFFFF0000u);
+      if (store_z) *(uint4*)((uint16_t*)a.z + (size_t)(t0 + tt) * H + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if (store_z) {
+      float* zg = (float*)a.z + (size_t)(t0 + tt) * H + c0;
+      *(float4*)zg = make_float4(z[0], z[1], z[2], z[3]);
+      *(float4*)(zg + 4) = make_float4(z[4], z[5], z[6], z[7]);
     }
+    *(float4*)zr = make_float4(z[0], z[1], z[2], z[3]);
+    *(float4*)(zr + 4) = make_float4(z[4], z[5], z[6], z[7]);
   }
   __syncthreads();
 }
@@ -1309,19 +1323,24 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
     const uint32_t wo = (uint32_t)(r * H + 4 * q) * 4;
     const float* zr = &zs[r][4 * q];
     constexpr int PF = 8;
+    // workgroups start their K walk at different blocks of 128 columns, so
+    // that they do not all ask the same L2 lines of W_r at the same time
+    const int rot = 16 * PF * (int)(blockIdx.x % (H / (16 * PF)));
+    auto kwrap = [&](int k) { return k >= H ? k - H : k; };
     u32x4 wq[PF];
 #pragma unroll
-    for (int j = 0; j < PF; ++j) wq[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64 * j, 0, 0);
+    for (int j = 0; j < PF; ++j) wq[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 4 * kwrap(rot + 16 * j), 0, 0);
     // four independent accumulation chains (component j of each float4)
     float4v acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 1
     for (int kb0 = 0; kb0 < H; kb0 += 16 * PF) {
+      const int kb = kwrap(kb0 + rot);
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
         const u32x4 w4 = wq[j];
         const uint32_t nk = (uint32_t)(kb0 + 16 * PF + 16 * j);
-        wq[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, nk < (uint32_t)H ? wo + 4 * nk : 0x80000000u, 0, 0);
-        const float4 z4 = *(const float4*)(zr + kb0 + 16 * j);
+        wq[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, nk < (uint32_t)H ? wo + 4 * (uint32_t)kwrap((int)nk + rot) : 0x80000000u, 0, 0);
+        const float4 z4 = *(const float4*)(zr + kb + 16 * j);
         acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(z4.x, __uint_as_float(w4[0]), acc[0], 0, 0, 0);
         acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(z4.y, __uint_as_float(w4[1]), acc[1], 0, 0, 0);
         acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(z4.z, __uint_as_float(w4[2]), acc[2], 0, 0, 0);

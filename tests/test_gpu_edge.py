@@ -101,7 +101,7 @@ def assert_tie(ids, w, case):
 
 @pytest.mark.parametrize("case", sorted(TIE_CASES))
 @pytest.mark.parametrize("T,path", [(1, "decode"), (40, "decode"), (1, "grouped"), (40, "grouped"),
-                                    (700, "grouped")])
+                                    (700, "grouped"), (1100, "grouped")])
 def test_exact_router_tie_goes_to_lower_index(lib, case, T, path):
     from quantized_expert_ffn_moe_amd import binding as B
     lay, packed = tie_layer(case)
@@ -203,7 +203,7 @@ def test_max_tokens_grouped_sampled(lib):
 
 
 # ---------------------------------------------------------------- non-finite rows
-@pytest.mark.parametrize("T,path", [(5, "decode"), (5, "grouped"), (300, "grouped")])
+@pytest.mark.parametrize("T,path", [(5, "decode"), (5, "grouped"), (300, "grouped"), (1100, "grouped")])
 def test_non_finite_rows_keep_valid_ids(lib, T, path):
     from quantized_expert_ffn_moe_amd import binding as B
     wi = 0
