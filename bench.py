@@ -280,7 +280,12 @@ def bench_decode(args):
     ids_timed = ids_all.cpu().numpy()
     w_timed = w_all.cpu().numpy()
 
-    # per-launch kernel duration: an event pair around each launch, on the launch stream
+    # the step is one kernel launch, so the timed region's average (events on
+    # the launch stream around all K launches, divided by K) is the average
+    # launch duration, back-to-back dispatch gap included.  An event pair
+    # around each launch, reported beside it, also counts the events' own
+    # processing and overstates the kernel.
+    ms_kernel = ms_step
     with torch.cuda.stream(stream):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         for k, i in enumerate(range(args.warmup, n_tok)):
@@ -288,7 +293,7 @@ def bench_decode(args):
             step(i)
             evs[k][1].record(stream)
         torch.cuda.synchronize()
-    ms_kernel = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms_isolated = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     leg = wl.name
     check_error_word(ws, leg)
     # every launch is deterministic: the second pass must reproduce the first
@@ -341,7 +346,8 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counted_traffic(args.group) if not one_layer else None,
-                     "bytes_per_launch": step_bytes, "ms_per_launch": ms_kernel},
+                     "bytes_per_launch": step_bytes, "ms_per_launch": ms_kernel,
+                     "ms_per_launch_event_pair": ms_isolated},
         "parity_gate": gate,
     }
     if not args.no_cpu_baseline:
