@@ -76,14 +76,11 @@ moe_status_t moe_attn_block_forward(int32_t n_streams, int32_t n_ref, float* h, 
   void* part = ws + 5 * r256;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  // from PROJ_HL_MIN_T streams the norm and the attention step write their
-  // outputs as split bf16 halves (same bytes as f32), which the projections
-  // read as they are
-  const bool hl = S >= PROJ_HL_MIN_T;
-  if (launch_rmsnorm(h, z, hl ? 2 : 0, S, 1e-6f, s) != hipSuccess) return MOE_E_HIP;
+  // the norm and the attention step write their outputs as split bf16 halves
+  // (same bytes as f32), which the projections read as they are
+  if (launch_rmsnorm(h, z, 2, S, 1e-6f, s) != hipSuccess) return MOE_E_HIP;
   ProjArgs pq;
-  pq.a = hl ? nullptr : z; pq.a_hl = hl ? (const uint16_t*)z : nullptr;
-  pq.w = (const uint16_t*)w_qkv; pq.y = qkv; pq.T = S; pq.N = 3 * H; pq.accumulate = 0;
+  pq.a_hl = (const uint16_t*)z; pq.w = (const uint16_t*)w_qkv; pq.y = qkv; pq.T = S; pq.N = 3 * H; pq.accumulate = 0;
   static_assert(H * 4 % 256 == 0, "q, k and v arrays [S][1280] apart, as the projection writes them");
   if (launch_proj(pq, s) != hipSuccess) return MOE_E_HIP;
   RswaArgs a;
@@ -91,11 +88,10 @@ moe_status_t moe_attn_block_forward(int32_t n_streams, int32_t n_ref, float* h, 
   a.q = qkv; a.k_new = qkv + (size_t)S * H; a.v_new = qkv + 2 * (size_t)S * H;
   a.ref_k = (const uint16_t*)ref_k; a.ref_v = (const uint16_t*)ref_v;
   a.ring_k = (uint16_t*)ring_k; a.ring_v = (uint16_t*)ring_v;
-  a.n_gen = n_gen; a.part = (float*)part; a.out = hl ? nullptr : att; a.out_hl = hl ? (uint16_t*)att : nullptr;
+  a.n_gen = n_gen; a.part = (float*)part; a.out = nullptr; a.out_hl = (uint16_t*)att;
   if (launch_rswa(a, s) != hipSuccess) return MOE_E_HIP;
   ProjArgs po;
-  po.a = hl ? nullptr : att; po.a_hl = hl ? (const uint16_t*)att : nullptr;
-  po.w = (const uint16_t*)w_o; po.y = h; po.T = S; po.N = H; po.accumulate = 1;
+  po.a_hl = (const uint16_t*)att; po.w = (const uint16_t*)w_o; po.y = h; po.T = S; po.N = H; po.accumulate = 1;
   if (launch_proj(po, s) != hipSuccess) return MOE_E_HIP;
   return MOE_OK;
 }

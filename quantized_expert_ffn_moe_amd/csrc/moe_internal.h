@@ -212,16 +212,15 @@ hipError_t launch_rswa(const RswaArgs& a, hipStream_t s);
 // Attention projections: y[t][n] (+)= sum_k a[t][k] W[n][k], K = H, bf16 W
 // [N][H]; output column n of token t at y[((n / H) * T + t) * H + n % H]
 // (so q, k and v of a [3H][H] weight land in three [T][H] arrays).
-// The activations come either as f32 rows (a) or already split into bf16
-// halves (a_hl, the split_row layout below); exactly one is set.
+// The activations come already split into bf16 halves (a_hl, the split_row
+// layout below).
 struct ProjArgs {
-  const float* a; const uint16_t* a_hl; const uint16_t* w; float* y;
+  const uint16_t* a_hl; const uint16_t* w; float* y;
   int T, N, accumulate;
 };
 // split_row layout of an f32 row [H] as bf16 halves: per 8-element group g,
 // 16 bytes of hi = bf16_rne(x) for its 8 elements, then 16 bytes of
 // lo = bf16_rne(x - hi); 4 bytes per element, like the f32 row.
-constexpr int PROJ_HL_MIN_T = 16;   // from this many streams the projections read split rows
 hipError_t launch_proj(const ProjArgs& p, hipStream_t s);
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
