@@ -157,7 +157,7 @@ __global__ __launch_bounds__(NT) void rswa_row_kernel(RswaArgs a) {
   __shared__ __attribute__((aligned(16))) float ql[ATT_D];
   __shared__ float pl[CH];
   __shared__ float red[2 * NW];
-  __shared__ float acc2[ATT_D];
+  __shared__ float acc2[NT > ATT_D ? NT - ATT_D : 1];
   const int h = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid >> 2, qq = tid & 3;
   const KeyList L = key_list(a, s, h);
@@ -194,10 +194,12 @@ __global__ __launch_bounds__(NT) void rswa_row_kernel(RswaArgs a) {
     acc = __fmaf_rn(acc, resc, chunk_pv(vl, pl));
     m_run = m_new;
   }
-  if (NT > ATT_D) {
-    if (tid >= ATT_D) acc2[tid & (ATT_D - 1)] = acc;
+  if (NT > ATT_D) {                               // the key parts' sums, in part order
+    if (tid >= ATT_D) acc2[tid - ATT_D] = acc;
     __syncthreads();
-    if (tid < ATT_D) acc += acc2[tid];
+    if (tid < ATT_D)
+#pragma unroll
+      for (int p = 0; p < NT / ATT_D - 1; ++p) acc += acc2[ATT_D * p + tid];
   }
   if (tid < ATT_D) store_out(a, ((size_t)s * ATT_HEADS + h) * ATT_D + tid, acc / l_run);
 }
@@ -253,15 +255,33 @@ __global__ __launch_bounds__(256) void rswa_chunk_kernel(RswaArgs a) {
 __global__ __launch_bounds__(ATT_D) void rswa_merge_kernel(RswaArgs a) {
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const float* part = a.part + ((size_t)s * ATT_HEADS + h) * a.n_chunks * RSWA_PART;
+  // all loads of a batch of 8 chunks are issued before any is used (an empty
+  // chunk reads as m = -inf, l = 0, o = 0 and gets weight 0)
   float M = -__builtin_inff();
-  for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, part[c * RSWA_PART]);
+  for (int c0 = 0; c0 < a.n_chunks; c0 += 8) {
+    float mc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mc[i] = c0 + i < a.n_chunks ? part[(c0 + i) * RSWA_PART] : -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) M = fmaxf(M, mc[i]);
+  }
   float L = 0.f, o = 0.f;
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const float mc = part[c * RSWA_PART];
-    if (mc == -__builtin_inff()) continue;
-    const float w = expf(mc - M);
-    L = __fmaf_rn(part[c * RSWA_PART + 1], w, L);
-    o = __fmaf_rn(part[c * RSWA_PART + 2 + d], w, o);
+  for (int c0 = 0; c0 < a.n_chunks; c0 += 8) {
+    float mc[8], lc[8], oc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool in = c0 + i < a.n_chunks;
+      const float* pc = part + (c0 + i) * RSWA_PART;
+      mc[i] = in ? pc[0] : -__builtin_inff();
+      lc[i] = in ? pc[1] : 0.f;
+      oc[i] = in ? pc[2 + d] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float w = mc[i] == -__builtin_inff() ? 0.f : expf(mc[i] - M);
+      L = __fmaf_rn(lc[i], w, L);
+      o = __fmaf_rn(oc[i], w, o);
+    }
   }
   store_out(a, ((size_t)s * ATT_HEADS + h) * ATT_D + d, o / L);
 }
