@@ -293,7 +293,9 @@ def bench_decode(args):
             step(i)
             evs[k][1].record(stream)
         torch.cuda.synchronize()
-    ms_isolated = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    pair_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_isolated = float(pair_ms.mean())
+    pair_pct = [float(v) for v in np.percentile(pair_ms, [10, 50, 90])]
     leg = wl.name
     check_error_word(ws, leg)
     # every launch is deterministic: the second pass must reproduce the first
@@ -302,6 +304,7 @@ def bench_decode(args):
 
     step_bytes = np.mean([sum(layer_bytes(ids_timed[i, li].tolist(), wl.routed, wl.shared) for li in range(L))
                           for i in range(args.warmup, n_tok)])
+    practical = practical_read_gbs(stream)
     achieved = step_bytes / (ms_kernel * 1e-3) / 1e9
 
     # same-run parity gate and CPU baseline on the timed tokens
@@ -347,7 +350,9 @@ def bench_decode(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counted_traffic(args.group) if not one_layer else None,
                      "bytes_per_launch": step_bytes, "ms_per_launch": ms_kernel,
-                     "ms_per_launch_event_pair": ms_isolated},
+                     "ms_per_launch_event_pair": ms_isolated,
+                     "ms_per_launch_event_pair_p10_p50_p90": pair_pct,
+                     "practical_read_gbs": practical, "frac_of_practical": achieved / practical},
         "parity_gate": gate,
     }
     if not args.no_cpu_baseline:
@@ -529,6 +534,30 @@ def bench_grouped(args):
 # ----------------------------------------------------------------------------
 # the decoder's dense ends, the R-SWA step and the FFN stack
 # ----------------------------------------------------------------------------
+def practical_read_gbs(stream, mib=1024, reps=20):
+    """The device's practical streaming-read rate in GB/s: the library's
+    read probe over a 1 GiB buffer (four times the last-level cache), events
+    on the launch stream around `reps` reads after 3 untimed ones."""
+    import torch
+    from quantized_expert_ffn_moe_amd import binding as B
+    buf = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            B.moe_hbm_read_probe(buf, sink, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            B.moe_hbm_read_probe(buf, sink, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf
+    return (mib << 20) / (ms * 1e-3) / 1e9
+
+
 def timed_loop(step, stream, warmup, steps, first=0):
     import torch
     with torch.cuda.stream(stream):

@@ -321,6 +321,18 @@ moe_status_t moe_decode_forward(const void* x, int32_t x_dtype, float* y, int32_
                                 int32_t* topk_ids, float* topk_w, void* workspace,
                                 size_t workspace_bytes, uint32_t flags, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement helper (not a step of the layer): *sink ^= the XOR of every
+ * 32-bit word of the `bytes` bytes at src, read once with 16-byte loads spread
+ * over every compute unit.  Timed on `stream` over a buffer much larger than
+ * the last-level cache, it gives the device's practical streaming-read rate,
+ * against which the decode step's bandwidth is reported beside the HBM peak.
+ * src: device memory, 16-byte aligned, bytes a multiple of 16 (MOE_E_ALIGN
+ * otherwise); sink: one device word, 4-byte aligned, that the caller clears
+ * first.  bytes == 0 launches nothing.  Asynchronous on `stream`.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ EXPORTS = ("moe_status_str", "moe_expert_code_bytes", "moe_expert_scale_count", 
            "moe_decode_workspace_init", "moe_decode_forward", "moe_lm_head_workspace_bytes",
            "moe_lm_head_argmax", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_forward",
            "moe_rswa_workspace_bytes", "moe_rswa_decode", "moe_layer_forward_static",
-           "moe_attn_block_workspace_bytes", "moe_attn_block_forward")
+           "moe_attn_block_workspace_bytes", "moe_attn_block_forward", "moe_hbm_read_probe")
 MOE_HEAD_INT8, MOE_HEAD_BF16 = 8, 16
 MOE_Q4K = 256   # group value of the two-level 4-bit format
 DECODE_MAX_LAYERS = 16
@@ -103,6 +103,8 @@ def load():
     L.moe_attn_block_forward.argtypes = [i32, i32] + [vp] * 8 + [vp, sz, vp]
     L.moe_rswa_decode.restype = i32
     L.moe_rswa_decode.argtypes = [i32, i32] + [vp] * 9 + [vp, sz, vp]
+    L.moe_hbm_read_probe.restype = i32
+    L.moe_hbm_read_probe.argtypes = [vp, sz, vp, vp]
     _lib = L
     return L
 
@@ -422,3 +424,13 @@ def moe_rswa_decode(dev: dict, out, ws, stream=None):
     check(load().moe_rswa_decode(S, dev["n_ref"], _ptr(dev["q"]), _ptr(dev["k_new"]), _ptr(dev["v_new"]),
                                  _ptr(dev["ref_k"]), _ptr(dev["ref_v"]), _ptr(dev["ring_k"]), _ptr(dev["ring_v"]),
                                  _ptr(dev["n_gen"]), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ----------------------------------------------------------------- measurement
+def moe_hbm_read_probe(buf, sink, stream=None):
+    """Enqueue one streaming read of the device tensor `buf` (its bytes, 16-byte
+    multiple); sink: a cleared int32 device tensor of one element, XORed with
+    the buffer's 32-bit words."""
+    import torch
+    _want(sink, torch.int32, (1,), "sink")
+    check(load().moe_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))

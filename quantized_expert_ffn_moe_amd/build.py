@@ -3,7 +3,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["csrc/moe_kernels.hip", "csrc/dense_kernels.hip", "csrc/attn_kernels.hip", "csrc/proj_kernels.hip",
+SOURCES = ["csrc/moe_kernels.hip", "csrc/dense_kernels.hip", "csrc/attn_kernels.hip", "csrc/proj_kernels.hip", "csrc/probe_kernels.hip",
            "csrc/moe_api.cpp", "csrc/dense_api.cpp", "csrc/attn_api.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # no packed-FP32 instructions in any generated code

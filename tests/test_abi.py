@@ -243,6 +243,16 @@ def test_rmsnorm_validation(lib):
     assert lib.moe_rmsnorm(0x100, 0x200, 0, 0, 1e-6, None) == 0
 
 
+def test_hbm_read_probe_validation(lib):
+    # argument checks come before any HIP call, so they run without a GPU
+    assert lib.moe_hbm_read_probe(None, 16, 0x100, None) == 1
+    assert lib.moe_hbm_read_probe(0x100, 16, None, None) == 1
+    assert lib.moe_hbm_read_probe(0x108, 16, 0x100, None) == 4
+    assert lib.moe_hbm_read_probe(0x100, 24, 0x100, None) == 4
+    assert lib.moe_hbm_read_probe(0x100, 16, 0x102, None) == 4
+    assert lib.moe_hbm_read_probe(0x100, 0, 0x100, None) == 0
+
+
 def test_decode_forward_validation(lib):
     A = 0x10000
     L = (B.LayerWeights * 2)(B.LayerWeights(A, None, A, A, A, A), B.LayerWeights(A, None, A, A, A, A))
