@@ -528,7 +528,7 @@ def bench_grouped(args):
                            "frac": gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_step": nbytes}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu
-    print(json.dumps(out), flush=True)
+    print(json.dumps(add_practical(out)), flush=True)
 
 
 # ----------------------------------------------------------------------------
@@ -556,6 +556,18 @@ def practical_read_gbs(stream, mib=1024, reps=20):
     ms = e0.elapsed_time(e1) / reps
     del buf
     return (mib << 20) / (ms * 1e-3) / 1e9
+
+
+def add_practical(out):
+    """An HBM-bound line also carries the practical read rate measured in the
+    same run, and its achieved bandwidth as a fraction of it."""
+    import torch
+    r = out.get("roofline")
+    if r and r.get("bound") == "hbm":
+        p = practical_read_gbs(torch.cuda.current_stream())
+        r["practical_read_gbs"] = p
+        r["frac_of_practical"] = r["achieved"] / p
+    return out
 
 
 def timed_loop(step, stream, warmup, steps, first=0):
@@ -674,7 +686,7 @@ def bench_dense(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = {"value": 1.0 / used, "unit": "calls/s", "cores": host_threads(), "kind": "oracle",
                                "sample": f"one call (float64 numpy oracle, dequantisation included), {used:.1f} s"}
-    print(json.dumps(out), flush=True)
+    print(json.dumps(add_practical(out)), flush=True)
 
 
 def bench_ffnstack(args):
@@ -764,7 +776,7 @@ def bench_ffnstack(args):
         out["cpu_baseline"] = {"value": 1.0 / used, "unit": "tokens/s", "cores": host_threads(), "kind": "oracle",
                                "sample": f"the last timed token (float64 numpy oracle: dense MLP, 11 MoE layers, "
                                          f"lm_head), {used:.1f} s"}
-    print(json.dumps(out), flush=True)
+    print(json.dumps(add_practical(out)), flush=True)
 
 
 def bench_rswa(args):
@@ -824,7 +836,7 @@ def bench_rswa(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = {"value": done / used, "unit": "tokens/s", "cores": host_threads(), "kind": "oracle",
                                "sample": f"{done} of the 128 streams (float64 numpy oracle), {used:.1f} s"}
-    print(json.dumps(out), flush=True)
+    print(json.dumps(add_practical(out)), flush=True)
 
 
 def bench_layer(args):
@@ -941,7 +953,7 @@ def bench_layer(args):
                                "kind": "oracle",
                                "sample": f"{len(sample)} stream{'s' if len(sample) > 1 else ''} of one step (float64 "
                                          f"numpy oracle: attention half and MoE layer), {used:.2f} s"}
-    print(json.dumps(out), flush=True)
+    print(json.dumps(add_practical(out)), flush=True)
 
 
 def bench_crossover(args):

@@ -96,7 +96,8 @@ __device__ __forceinline__ void piece_fma(const uint4& w, const float* x, int e0
   }
   // (with several tokens, unrolled in pairs: a full unroll keeps every x value
   // of the piece live at once)
-#pragma unroll (NT == 1 ? EPP / 4 : 2)
+  constexpr int UNR = NT == 1 ? EPP / 4 : 2;
+#pragma unroll UNR
   for (int i4 = 0; i4 < EPP / 4; ++i4) {
     float v[4];
 #pragma unroll
@@ -115,9 +116,13 @@ __device__ __forceinline__ void piece_fma(const uint4& w, const float* x, int e0
 }
 
 // NT rows of H floats into LDS (stride H); with norm, each becomes
-// x / sqrt(mean(x^2) + eps).  256 threads; ends with a barrier.
-template <int NT>
-__device__ __forceinline__ void rows_to_lds(const float* x, int T, int norm, float eps, float* xs, float* red) {
+// x / sqrt(mean(x^2) + eps).  256 threads; ends with a barrier.  issue() runs
+// right after the rows' loads are issued: loads it issues (the first weight
+// steps) complete after the rows' (the load counter is in order), so waiting
+// for the rows does not wait for them.
+template <int NT, typename F>
+__device__ __forceinline__ void rows_to_lds(const float* x, int T, int norm, float eps, float* xs, float* red,
+                                            F&& issue) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const __amdgpu_buffer_rsrc_t rx = dense_rsrc(x, (uint32_t)T * H * 4);
   constexpr int NU = NT * H / 4;          // float4 in all
@@ -129,6 +134,7 @@ __device__ __forceinline__ void rows_to_lds(const float* x, int T, int norm, flo
     const u32x4d q = __builtin_amdgcn_raw_buffer_load_b128(rx, u < NU ? (uint32_t)u * 16 : OUT_OF_RANGE, 0, 0);
     v[j] = make_uint4(q[0], q[1], q[2], q[3]);
   }
+  issue();
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int u = tid + 256 * j;
@@ -175,12 +181,13 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 // with f32 group scales; every workgroup also leaves its best (logit, id) per
 // token, which the selection kernel reduces to the greedy token.
 // A workgroup of 4 waves covers HEAD_ROWS consecutive rows: 16 lanes per
-// row, 4 rows per wave step, HEAD_STEPS steps per wave.
+// row, 4 rows per wave step, HEAD_ROWS / 16 steps per wave.
 // ---------------------------------------------------------------------------
 template <int WT, int NT>
 __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   constexpr int EPP = 128 / WT, P = H / EPP;          // pieces per row: 160 (bf16), 80 (int8)
   constexpr int LPR = 16, KPL = P / LPR, RG = 64 / LPR;
+  constexpr int NSTEP = HEAD_ROWS / (4 * RG);         // wave steps
   static_assert(P % LPR == 0, "whole pieces per lane");
   __shared__ __attribute__((aligned(16))) float xs[NT * H];
   __shared__ float xsum[WT == 8 ? NT * P : 1];        // int8: per token and piece, the sum of its z
@@ -188,7 +195,7 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   __shared__ float cv[4][NT];
   __shared__ int ci[4][NT];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, rg = lane / LPR, l = lane % LPR;
-  const int row0 = (blockIdx.x * 4 + wv) * RG * HEAD_STEPS;
+  const int row0 = (blockIdx.x * 4 + wv) * RG * NSTEP;
   const uint32_t rb = H * WT / 8;                     // bytes per row
   const __amdgpu_buffer_rsrc_t rw = dense_rsrc(a.w, (uint32_t)a.vocab * rb);
   const int ng = H / a.group;
@@ -206,8 +213,7 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
       if (WT != 16) sc[slot][m] = dload4(rs, live ? ((uint32_t)row * ng + (EPP * p) / a.group) * 4 : OUT_OF_RANGE);
     }
   };
-  load(0, 0);
-  rows_to_lds<NT>(a.h, a.T, a.norm, a.eps, xs, red);
+  rows_to_lds<NT>(a.h, a.T, a.norm, a.eps, xs, red, [&] { load(0, 0); });
   if (WT == 8) {
     for (int u = tid; u < NT * P; u += 256) {
       const float* xp = xs + (u / P) * H + EPP * (u % P);
@@ -224,8 +230,8 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) { bv[t] = -__builtin_inff(); bi[t] = -1; }
 #pragma unroll
-  for (int s = 0; s < HEAD_STEPS; ++s) {
-    if (s + 1 < HEAD_STEPS) load(s + 1, (s + 1) & 1);
+  for (int s = 0; s < NSTEP; ++s) {
+    if (s + 1 < NSTEP) load(s + 1, (s + 1) & 1);
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.f;
@@ -326,9 +332,10 @@ __global__ __launch_bounds__(256) void dense_gateup_kernel(DenseGateUpArgs a) {
     }
   };
   static_assert(DENSE_GU_STEPS == 2, "both steps' weights are in flight from the start");
-  load(0, 0);
-  load(1, 1);
-  rows_to_lds<NT>(a.x, a.T, a.norm, a.eps, xs, red);
+  rows_to_lds<NT>(a.x, a.T, a.norm, a.eps, xs, red, [&] {
+    load(0, 0);
+    load(1, 1);
+  });
 #pragma unroll
   for (int s = 0; s < DENSE_GU_STEPS; ++s) {
     float acc[NT];
