@@ -77,10 +77,17 @@ moe_status_t moe_attn_block_forward(int32_t n_streams, int32_t n_ref, float* h, 
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   // the norm and the attention step write their outputs as split bf16 halves
-  // (same bytes as f32), which the projections read as they are
-  if (launch_rmsnorm(h, z, 2, S, 1e-6f, s) != hipSuccess) return MOE_E_HIP;
+  // (same bytes as f32), which the projections read as they are; for a few
+  // streams the q/k/v projection forms the normalised rows itself (one launch
+  // fewer)
   ProjArgs pq;
-  pq.a_hl = (const uint16_t*)z; pq.w = (const uint16_t*)w_qkv; pq.y = qkv; pq.T = S; pq.N = 3 * H; pq.accumulate = 0;
+  pq.w = (const uint16_t*)w_qkv; pq.y = qkv; pq.T = S; pq.N = 3 * H; pq.accumulate = 0;
+  if (S <= PJ_NORM_MAX_T) {
+    pq.a_hl = nullptr; pq.h_norm = h; pq.eps = 1e-6f;
+  } else {
+    if (launch_rmsnorm(h, z, 2, S, 1e-6f, s) != hipSuccess) return MOE_E_HIP;
+    pq.a_hl = (const uint16_t*)z;
+  }
   static_assert(H * 4 % 256 == 0, "q, k and v arrays [S][1280] apart, as the projection writes them");
   if (launch_proj(pq, s) != hipSuccess) return MOE_E_HIP;
   RswaArgs a;

@@ -217,7 +217,11 @@ hipError_t launch_rswa(const RswaArgs& a, hipStream_t s);
 struct ProjArgs {
   const uint16_t* a_hl; const uint16_t* w; float* y;
   int T, N, accumulate;
+  // instead of a_hl: the f32 rows h, whose RMSNorm (eps) the projection forms
+  // itself in split_row layout in LDS (T <= PJ_NORM_MAX_T)
+  const float* h_norm = nullptr; float eps = 0.f;
 };
+constexpr int PJ_NORM_MAX_T = 4;
 // split_row layout of an f32 row [H] as bf16 halves: per 8-element group g,
 // 16 bytes of hi = bf16_rne(x) for its 8 elements, then 16 bytes of
 // lo = bf16_rne(x - hi); 4 bytes per element, like the f32 row.

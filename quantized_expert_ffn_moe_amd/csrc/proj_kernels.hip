@@ -14,6 +14,7 @@
 // (v_mfma_f32_16x16x32_bf16): the products are exact in fp32 and only the
 // fp32 accumulation rounds.
 #include "moe_internal.h"
+#include "moe_wave.h"
 
 namespace moe {
 
@@ -25,23 +26,55 @@ namespace {
 constexpr int PJ_KW = H / 4;        // K columns of one wave (320)
 constexpr int PJ_KS = PJ_KW / 32;   // its 32-wide k-steps (10)
 constexpr int PJ_TT = 4;            // stream tiles of 16 per workgroup
+
+// RMSNorm of a row with the standalone norm's arithmetic (thread tid owns
+// features tid + 256 i, i < 5; squares added in that order, the four wave
+// sums in a fixed order), so that both give bit-identical z
+__device__ __forceinline__ float row_sumsq(const float (&v)[5]) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) ss = __fmaf_rn(v[i], v[i], ss);
+  return ss;
+}
+__device__ __forceinline__ uint32_t bf16_bits(float v) {   // nearest, ties to even
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 }  // namespace
 
 // A workgroup of 4 waves owns NS 16-column subtiles and up to 64 streams (four
-// tiles of 16).  The waves split K in quarters: each keeps its quarter of the
+// tiles of 16).  With NORM (at most PJ_NORM_MAX_T streams) the workgroup
+// first forms the split rows of RMSNorm(h) itself, in LDS, instead of reading
+// them from a norm launch before it.  The waves split K in quarters: each keeps its quarter of the
 // subtiles' weight rows in registers (read once) and multiplies every stream
 // tile with it, each lane's two 16-byte loads being its A operands as they
 // are (hi, then lo); the next tile is fetched while the current one is
 // multiplied, and rows past T read as zeros (buffer range), so every load is
 // issued without a branch.  The four K-quarter partials meet in LDS and are
 // added by all 256 threads in a fixed order, one output each per subtile.
-template <int NS>
+template <int NS, bool NORM>
 __global__ __launch_bounds__(256) void proj_hl_kernel(ProjArgs p) {
   constexpr int NC = 16 * NS;                    // columns of the workgroup
+  constexpr int NT = NORM ? PJ_NORM_MAX_T : 1;
   __shared__ float red[2][4][16][NC + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t als[NORM ? PJ_NORM_MAX_T * H * 2 : 8];
+  __shared__ float nred[NT][4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, q = lane >> 4;
   const int n0 = NC * blockIdx.x, tb = 64 * blockIdx.y;
   const int k0 = PJ_KW * wv + 8 * q;
+  // NORM: the rows of h are requested before the weights, so that waiting for
+  // them does not wait for the weights too (the load counter is in order);
+  // rows past T read zeros (buffer range)
+  float hv[NT][5];
+  if constexpr (NORM) {
+    const __amdgpu_buffer_rsrc_t rh =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.h_norm), (short)0, (uint32_t)p.T * H * 4, 0x00020000);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+        hv[t][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rh, (uint32_t)(t * H + tid + 256 * i) * 4, 0, 0));
+  }
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w), (short)0, (uint32_t)p.N * H * 2, 0x00020000);
   uint4 b[NS][PJ_KS];
@@ -55,7 +88,8 @@ __global__ __launch_bounds__(256) void proj_hl_kernel(ProjArgs p) {
     }
   // rows past T read zeros (buffer range); 4 bytes per element
   const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.a_hl), (short)0, (uint32_t)p.T * H * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.a_hl), (short)0, NORM ? 0u : (uint32_t)p.T * H * 4,
+                                        0x00020000);
   u32x4p x[2][PJ_KS][2];
   auto load = [&](u32x4p (&xb)[PJ_KS][2], int t0) {
 #pragma unroll
@@ -65,7 +99,38 @@ __global__ __launch_bounds__(256) void proj_hl_kernel(ProjArgs p) {
       xb[s][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, off + 16, 0, 0);   // lo
     }
   };
-  load(x[0], tb);
+  if constexpr (NORM) {
+    // z = h / sqrt(mean(h^2) + eps) per row, as split rows in LDS
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float ss = wave_sum(row_sumsq(hv[t]));
+      if (lane == 0) nred[t][wv] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float inv = 1.0f / sqrtf(((nred[t][0] + nred[t][1]) + (nred[t][2] + nred[t][3])) / (float)H + p.eps);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int idx = tid + 256 * i;
+        const float zz = hv[t][i] * inv;
+        const uint32_t hi = bf16_bits(zz);
+        uint16_t* g = als + (t * H + (idx & ~7)) * 2 + (idx & 7);
+        g[0] = (uint16_t)hi;
+        g[8] = (uint16_t)bf16_bits(zz - __uint_as_float(hi << 16));
+      }
+    }
+    __syncthreads();
+    // the single stream tile (rows from T on are zeros)
+#pragma unroll
+    for (int s = 0; s < PJ_KS; ++s) {
+      const u32x4p* ap = (const u32x4p*)(als + ((r < NT ? r : 0) * H + k0 + 32 * s) * 2);
+      x[0][s][0] = r < p.T ? ap[0] : u32x4p{0u, 0u, 0u, 0u};
+      x[0][s][1] = r < p.T ? ap[1] : u32x4p{0u, 0u, 0u, 0u};
+    }
+  } else {
+    load(x[0], tb);
+  }
   // this thread's outputs of each tile: token row tid / 16, columns
   // n0 + tid % 16 + 16 ns, through a descriptor over y (rows past T: loads
   // read zeros, stores are dropped)
@@ -88,7 +153,7 @@ __global__ __launch_bounds__(256) void proj_hl_kernel(ProjArgs p) {
       yold[ns] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ry, p.accumulate ? yo[ns] : 0x80000000u, 0, 0));
     }
     asm volatile("" ::: "memory");
-    if (tt + 1 < PJ_TT) load(x[(tt + 1) & 1], t0 + 16);   // unconditional: rows past T read zeros
+    if (!NORM && tt + 1 < PJ_TT) load(x[(tt + 1) & 1], t0 + 16);   // unconditional: rows past T read zeros
     float4p c[NS];
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) c[ns] = float4p{0.f, 0.f, 0.f, 0.f};
@@ -121,12 +186,17 @@ __global__ __launch_bounds__(256) void proj_hl_kernel(ProjArgs p) {
 
 hipError_t launch_proj(const ProjArgs& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
+  if (p.h_norm) {
+    if (p.T > PJ_NORM_MAX_T) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((proj_hl_kernel<1, true>), dim3(p.N / 16, 1), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   const int tblocks = (p.T + 16 * PJ_TT - 1) / (16 * PJ_TT);
   if ((p.N / 32) * tblocks >= 200) {
     // 32 columns per workgroup halve the activation reads while keeping enough workgroups
-    hipLaunchKernelGGL(proj_hl_kernel<2>, dim3(p.N / 32, tblocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((proj_hl_kernel<2, false>), dim3(p.N / 32, tblocks), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL(proj_hl_kernel<1>, dim3(p.N / 16, tblocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((proj_hl_kernel<1, false>), dim3(p.N / 16, tblocks), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

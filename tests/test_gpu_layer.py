@@ -98,7 +98,8 @@ def check_attn(kvh, dev, h0, h, sample):
     return ratio
 
 
-@pytest.mark.parametrize("S,n_ref", [(1, 288), (1, 0), (4, 288), (16, 64), (17, 288), (65, 64), (128, 288)])
+@pytest.mark.parametrize("S,n_ref", [(1, 288), (1, 0), (2, 0), (4, 288), (5, 288), (16, 64), (17, 288), (65, 64),
+                                     (128, 288)])
 def test_attn_block(lib, S, n_ref):
     n_gen = [127 + 53 * s for s in range(S)]
     say(f"attention block, {S} streams, n_ref {n_ref}")
