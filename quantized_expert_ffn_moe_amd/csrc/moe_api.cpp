@@ -36,7 +36,7 @@ struct Workspace {
   int32_t* counts;   // [E]
   int32_t* offsets;  // [E+1]
   int32_t* ntiles;   // [1]
-  int32_t* tiles;    // [max_tiles][2]
+  int32_t* tiles;    // [max_tiles][4]
   int32_t* perm;     // [T*6]
   int32_t* pos_of;   // [T*6]
   int32_t* blkcnt;   // [T*6/1024 + 1][E] per-block histogram counts
@@ -74,7 +74,7 @@ Workspace carve(void* base, int T, int part_max_t = DECODE_FORCE_MAX_T) {
   w.counts = (int32_t*)c.take(E * 4);
   w.offsets = (int32_t*)c.take((E + 1) * 4);
   w.ntiles = (int32_t*)c.take(4);
-  w.tiles = (int32_t*)c.take((size_t)w.max_tiles * 2 * 4);
+  w.tiles = (int32_t*)c.take((size_t)w.max_tiles * 4 * 4);
   w.perm = (int32_t*)c.take(slots * 4);
   w.pos_of = (int32_t*)c.take(slots * 4);
   w.blkcnt = (int32_t*)c.take((slots / HIST_BLOCK + 1) * E * 4);

@@ -132,7 +132,7 @@ struct HistArgs {
   const int32_t* ids; int T;
   int32_t* counts; int32_t* offsets;    // [E], [E+1]
   int32_t* perm; int32_t* pos_of;       // [T*6]: sorted slot -> (t*6+j); (t*6+j) -> sorted position
-  int32_t* tiles; int32_t* ntiles;      // [max][2] (expert, first row), count
+  int32_t* tiles; int32_t* ntiles;      // [max][4] (expert, first row, first sorted slot, rows), count
   int mt;                               // rows per tile
   int32_t* blkcnt;                      // [blocks][E] per-block counts (the multi-workgroup histogram)
 };

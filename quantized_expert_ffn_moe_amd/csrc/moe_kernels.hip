@@ -1357,6 +1357,14 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
     select_top6(lg[tt][lane], a.ids + (size_t)(t0 + tt) * TOPK, a.w + (size_t)(t0 + tt) * TOPK);
 }
 
+// Row tiles of expert e (tiles t0, t0 + 1, ... in row order): one 16-byte
+// record each, (expert, first row within the expert, first sorted slot, rows),
+// so that a grouped workgroup finds its rows with a single dependent load.
+__device__ __forceinline__ void write_tiles(const HistArgs& a, int e, int t0, int off0, int cnt) {
+  for (int r0 = 0, t = t0; r0 < cnt; r0 += a.mt, ++t)
+    *(int4*)&a.tiles[4 * t] = make_int4(e, r0, off0 + r0, min(a.mt, cnt - r0));
+}
+
 // ---------------------------------------------------------------------------
 // Histogram + stable permutation of the (token, pick) slots by expert, one
 // workgroup of 16 waves.  Wave w owns a contiguous chunk of slots: per-wave
@@ -1404,10 +1412,7 @@ __global__ __launch_bounds__(1024) void hist_kernel(HistArgs a) {
   if (tid < E) {
     a.counts[tid] = cnt[tid];
     a.offsets[tid] = off[tid];
-    for (int j = 0; j < toff[tid + 1] - toff[tid]; ++j) {
-      a.tiles[2 * (toff[tid] + j)] = tid;
-      a.tiles[2 * (toff[tid] + j) + 1] = j * a.mt;
-    }
+    write_tiles(a, tid, toff[tid], off[tid], cnt[tid]);
   }
   basew[wv][lane] += off[lane];
   __syncthreads();
@@ -1491,10 +1496,7 @@ __global__ __launch_bounds__(1024) void hist_place_kernel(HistArgs a) {
   if (valid) atomicAdd(&cntw[wv][my_e], 1);
   if (b == 0 && tid < E) {
     a.offsets[tid] = off[tid];
-    for (int j = 0; j < toff[tid + 1] - toff[tid]; ++j) {
-      a.tiles[2 * (toff[tid] + j)] = tid;
-      a.tiles[2 * (toff[tid] + j) + 1] = j * a.mt;
-    }
+    write_tiles(a, tid, toff[tid], off[tid], off[tid + 1] - off[tid]);
   }
   __syncthreads();
   {   // thread (w, e): the expert's start for wave w of this block
@@ -1766,11 +1768,10 @@ __device__ __forceinline__ TileInfo tile_info(const GroupedArgs& a, int tile, in
   } else {
     ti.valid = tile < *a.ntiles;
     if (!ti.valid) { ti.nrows = 0; ti.pbase = 0; ti.row0 = 0; ti.e = 0; return ti; }
-    ti.e = a.tiles[2 * tile];
-    const int r0 = a.tiles[2 * tile + 1];
-    const int cnt = a.offsets[ti.e + 1] - a.offsets[ti.e];
-    ti.nrows = min(mtl, cnt - r0);
-    ti.pbase = a.offsets[ti.e] + r0;
+    const int4 rec = *(const int4*)&a.tiles[4 * tile];   // the histogram's record
+    ti.e = rec.x;
+    ti.pbase = rec.z;
+    ti.nrows = rec.w;
     ti.row0 = 0;
   }
   return ti;
