@@ -274,16 +274,27 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
 }
 
 // Greedy token of token t (= blockIdx.x) from the n_wg workgroup candidates
-// ([T][n_wg] (logit, id) pairs): one wave, each lane scans a strided share,
-// then a butterfly over the lanes.
-__global__ __launch_bounds__(64) void head_select_kernel(HeadArgs a, int n_wg) {
-  const int t = blockIdx.x, lane = threadIdx.x;
+// ([T][n_wg] (logit, id) pairs): 256 threads, each with four candidates in
+// flight per round, then a butterfly over each wave's lanes and the four
+// wave winners in order.  "better" is a total order, so the winner does not
+// depend on the order of the comparisons.
+__global__ __launch_bounds__(256) void head_select_kernel(HeadArgs a, int n_wg) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float2* c = (const float2*)a.cand + (size_t)t * n_wg;
   float v = -__builtin_inff();
   int i = -1;
-  for (int w = lane; w < n_wg; w += 64) {
-    const float2 q = c[w];
-    if (better(q.x, __float_as_int(q.y), v, i)) { v = q.x; i = __float_as_int(q.y); }
+  for (int w0 = tid; w0 < n_wg; w0 += 4 * 256) {
+    float2 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int w = w0 + 256 * u;
+      q[u] = w < n_wg ? c[w] : make_float2(-__builtin_inff(), __int_as_float(-1));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (better(q[u].x, __float_as_int(q[u].y), v, i)) { v = q[u].x; i = __float_as_int(q[u].y); }
   }
 #pragma unroll
   for (int d = 32; d > 0; d >>= 1) {
@@ -291,7 +302,12 @@ __global__ __launch_bounds__(64) void head_select_kernel(HeadArgs a, int n_wg) {
     const int oi = __shfl_xor(i, d);
     if (better(ov, oi, v, i)) { v = ov; i = oi; }
   }
-  if (lane == 0) {
+  if (lane == 0) { sv[wv] = v; si[wv] = i; }
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], v, i)) { v = sv[w]; i = si[w]; }
     a.token[t] = i;
     a.token_logit[t] = v;
   }
@@ -421,7 +437,7 @@ hipError_t launch_head(const HeadArgs& a, bool bf16, hipStream_t s) {
     case 3: launch_head_nt<3>(a, bf16, s); break;
     default: launch_head_nt<4>(a, bf16, s); break;
   }
-  hipLaunchKernelGGL(head_select_kernel, dim3(a.T), dim3(64), 0, s, a, head_workgroups(a.vocab));
+  hipLaunchKernelGGL(head_select_kernel, dim3(a.T), dim3(256), 0, s, a, head_workgroups(a.vocab));
   return hipGetLastError();
 }
 
