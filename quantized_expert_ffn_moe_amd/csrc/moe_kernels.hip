@@ -872,17 +872,24 @@ __global__ __launch_bounds__(256) void dec_reduce_kernel(DecReduceArgs a) {
   const int t = blockIdx.x / (H / 32), r0 = (blockIdx.x % (H / 32)) * 32;
   const int tid = threadIdx.x, r = tid & 31, ig = tid >> 5;
   const float* base = a.part + (size_t)t * N_ITEMS * H + r0 + r;
+  // every load is issued before the first add (the old output too), so the
+  // kernel waits for one round of loads, not one per few items
+  static_assert(N_ITEMS % 8 == 0, "items per thread");
+  const size_t yi = (size_t)t * H + r0 + tid;
+  const float yold = (tid < 32 && a.accumulate) ? a.y[yi] : 0.f;
+  float pv[N_ITEMS / 8];
+#pragma unroll
+  for (int k = 0; k < N_ITEMS / 8; ++k) pv[k] = base[(size_t)(ig + 8 * k) * H];
   float s = 0.f;
-#pragma unroll 4
-  for (int it = ig; it < N_ITEMS; it += 8) s += base[(size_t)it * H];
+#pragma unroll
+  for (int k = 0; k < N_ITEMS / 8; ++k) s += pv[k];
   red[ig][r] = s;
   __syncthreads();
   if (tid < 32) {
     float v = 0.f;
 #pragma unroll
     for (int g = 0; g < 8; ++g) v += red[g][tid];
-    const size_t yi = (size_t)t * H + r0 + tid;
-    a.y[yi] = (a.accumulate ? a.y[yi] : 0.f) + v;
+    a.y[yi] = yold + v;
   }
 }
 
@@ -2605,6 +2612,9 @@ __global__ __launch_bounds__(64 * SMALL_WAVES) void down_small_pair_kernel(Group
 // y[t] (+)= ys[t] (+ ys2[t]) + sum_j w[t,j] * ysorted[pos_of[t*6+j]], picks added in order.
 __global__ __launch_bounds__(320) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x, c = threadIdx.x * 4;
+  float4* yp = (float4*)(a.y + (size_t)t * H + c);
+  // the old output is requested first: it does not wait behind the rows
+  const float4 o = a.accumulate ? *yp : make_float4(0.f, 0.f, 0.f, 0.f);
   float4 v = *(const float4*)(a.ys + (size_t)t * H + c);
   if (a.ys2) {   // the second K part of the shared expert's down projection
     const float4 v2 = *(const float4*)(a.ys2 + (size_t)t * H + c);
@@ -2616,9 +2626,7 @@ __global__ __launch_bounds__(320) void combine_kernel(CombineArgs a) {
     const float4 p = *(const float4*)(a.ysorted + (size_t)a.pos_of[(size_t)t * TOPK + j] * H + c);
     v.x += wj * p.x; v.y += wj * p.y; v.z += wj * p.z; v.w += wj * p.w;
   }
-  float4* yp = (float4*)(a.y + (size_t)t * H + c);
   if (a.accumulate) {
-    const float4 o = *yp;
     v.x = o.x + v.x; v.y = o.y + v.y; v.z = o.z + v.z; v.w = o.w + v.w;
   }
   *yp = v;
