@@ -73,6 +73,27 @@ moe_status_t moe_lm_head_argmax(const float* h, int32_t n_tokens, uint32_t flags
                                 int32_t vocab, float* logits, int32_t* token, float* token_logit,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the dense MLP's code buffer for (bits, inter): 3 * inter * 1280 *
+   bits / 8 (0 for arguments out of range). */
+size_t moe_dense_ffn_code_bytes(int32_t bits, int32_t inter);
+
+/*
+ * Dense MLP weight codes into the one code buffer moe_dense_ffn_forward takes
+ * (host memory in, host memory out; no GPU involved).
+ *   gate, up    [inter][1280] int8, one signed code per byte, row-major;
+ *   down        [1280][inter] int8, likewise;
+ *   bits        8: the codes are copied as bytes; 4: codes must lie in
+ *               [-8, 7] and two consecutive codes of a row share a byte,
+ *               element 2j in the low nibble (two's complement);
+ *   codes_out   moe_dense_ffn_code_bytes(bits, inter) bytes, gate | up | down.
+ * Returns MOE_E_NULLPTR for a missing pointer, MOE_E_SHAPE for an inter the
+ * forward call rejects, MOE_E_FORMAT for bits not in {4, 8} or an int4 code
+ * out of range (nothing is written then).  The scales need no packing: they
+ * are the plain concatenation gate | up | down of [rows][K / group] f32.
+ */
+moe_status_t moe_pack_dense_ffn(const int8_t* gate, const int8_t* up, const int8_t* down, int32_t bits,
+                                int32_t inter, void* codes_out);
+
 /* Workspace bytes of moe_dense_ffn_forward (0 for arguments out of range). */
 size_t moe_dense_ffn_workspace_bytes(int32_t n_tokens, int32_t inter);
 

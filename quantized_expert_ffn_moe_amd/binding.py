@@ -23,6 +23,7 @@ EXPORTS = ("moe_status_str", "moe_expert_code_bytes", "moe_expert_scale_count", 
            "moe_workspace_bytes", "moe_layer_forward", "moe_rmsnorm", "moe_decode_workspace_bytes",
            "moe_decode_workspace_init", "moe_decode_forward", "moe_lm_head_workspace_bytes",
            "moe_lm_head_argmax", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_forward",
+           "moe_dense_ffn_code_bytes", "moe_pack_dense_ffn",
            "moe_rswa_workspace_bytes", "moe_rswa_decode", "moe_layer_forward_static",
            "moe_attn_block_workspace_bytes", "moe_attn_block_forward", "moe_hbm_read_probe")
 MOE_HEAD_INT8, MOE_HEAD_BF16 = 8, 16
@@ -95,6 +96,10 @@ def load():
     L.moe_dense_ffn_workspace_bytes.argtypes = [i32, i32]
     L.moe_dense_ffn_forward.restype = i32
     L.moe_dense_ffn_forward.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, u32, vp, sz, vp]
+    L.moe_dense_ffn_code_bytes.restype = sz
+    L.moe_dense_ffn_code_bytes.argtypes = [i32, i32]
+    L.moe_pack_dense_ffn.restype = i32
+    L.moe_pack_dense_ffn.argtypes = [vp, vp, vp, i32, i32, vp]
     L.moe_rswa_workspace_bytes.restype = sz
     L.moe_rswa_workspace_bytes.argtypes = [i32, i32]
     L.moe_attn_block_workspace_bytes.restype = sz
@@ -298,14 +303,17 @@ def _want(t, dtype, shape, name):
 
 
 # ----------------------------------------------------------------- dense ends (include/moe_dense.h)
-def _nibbles(codes):
-    """int4 codes [rows][K] (one per int8) -> [rows][K/2] bytes, element 2j in the low nibble."""
-    c = np.asarray(codes, dtype=np.int8).astype(np.uint8) & 0x0F
-    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
-
-
-def _rows(codes, bits):
-    return np.ascontiguousarray(codes, dtype=np.int8).view(np.uint8) if bits == 8 else _nibbles(codes)
+def moe_pack_dense_ffn(gate, up, down, bits: int) -> np.ndarray:
+    """Dense MLP codes (one signed code per int8) -> the code buffer of moe_dense_ffn_forward."""
+    inter = int(np.shape(gate)[0])
+    g, u, d = (np.ascontiguousarray(c, dtype=np.int8) for c in (gate, up, down))
+    if g.shape != (inter, HIDDEN) or u.shape != (inter, HIDDEN) or d.shape != (HIDDEN, inter):
+        raise MoeError(f"dense codes: expected [inter][1280], [inter][1280], [1280][inter], "
+                       f"got {g.shape} {u.shape} {d.shape}")
+    L = load()
+    out = np.empty(L.moe_dense_ffn_code_bytes(bits, inter), dtype=np.uint8)
+    check(L.moe_pack_dense_ffn(_np_ptr(g), _np_ptr(u), _np_ptr(d), bits, inter, _np_ptr(out)))
+    return out
 
 
 def lm_head_to_device(head: dict, device="cuda"):
@@ -324,8 +332,7 @@ def dense_ffn_to_device(ffn: dict, device="cuda"):
     moe_dense_ffn_forward takes them."""
     import torch
     b = ffn["bits"]
-    codes = np.concatenate([_rows(ffn["gate_q"], b).reshape(-1), _rows(ffn["up_q"], b).reshape(-1),
-                            _rows(ffn["down_q"], b).reshape(-1)])
+    codes = moe_pack_dense_ffn(ffn["gate_q"], ffn["up_q"], ffn["down_q"], b)
     scales = np.concatenate([np.asarray(ffn[k], dtype=np.float32).reshape(-1) for k in ("gate_s", "up_s", "down_s")])
     return {"q": torch.from_numpy(codes).to(device), "s": torch.from_numpy(scales).to(device),
             "bits": b, "group": ffn["group"], "inter": ffn["inter"]}

@@ -46,6 +46,37 @@ moe_status_t moe_lm_head_argmax(const float* h, int32_t n_tokens, uint32_t flags
   return MOE_OK;
 }
 
+size_t moe_dense_ffn_code_bytes(int32_t bits, int32_t inter) {
+  if ((bits != 4 && bits != 8) || inter < 64 || inter > DENSE_MAX_INTER || inter % 64) return 0;
+  return (size_t)3 * inter * H * bits / 8;
+}
+
+moe_status_t moe_pack_dense_ffn(const int8_t* gate, const int8_t* up, const int8_t* down, int32_t bits,
+                                int32_t inter, void* codes_out) {
+  if (!gate || !up || !down || !codes_out) return MOE_E_NULLPTR;
+  if (bits != 4 && bits != 8) return MOE_E_FORMAT;
+  if (inter < 64 || inter > DENSE_MAX_INTER || inter % 64) return MOE_E_SHAPE;
+  const size_t n = (size_t)inter * H;   // codes per matrix
+  const int8_t* mats[3] = {gate, up, down};
+  if (bits == 4)
+    for (const int8_t* m : mats)
+      for (size_t i = 0; i < n; ++i)
+        if (m[i] < -8 || m[i] > 7) return MOE_E_FORMAT;
+  uint8_t* out = (uint8_t*)codes_out;
+  for (const int8_t* m : mats) {
+    if (bits == 8) {
+      for (size_t i = 0; i < n; ++i) out[i] = (uint8_t)m[i];
+      out += n;
+    } else {
+      // every row length (1280 or inter) is even, so pairs never straddle rows
+      for (size_t i = 0; i < n / 2; ++i)
+        out[i] = (uint8_t)(((uint8_t)m[2 * i] & 0x0Fu) | (((uint8_t)m[2 * i + 1] & 0x0Fu) << 4));
+      out += n / 2;
+    }
+  }
+  return MOE_OK;
+}
+
 size_t moe_dense_ffn_workspace_bytes(int32_t n_tokens, int32_t inter) {
   if (n_tokens < 0 || n_tokens > DENSE_MAX_T || inter < 64 || inter > DENSE_MAX_INTER || inter % 64) return 0;
   return round256((size_t)(n_tokens ? n_tokens : 1) * inter * 4);

@@ -338,3 +338,47 @@ def test_rswa_validation(lib):
     assert call(S=0) == 0
     assert B.moe_rswa_workspace_bytes(1, 0) >= 10 * 2 * 132 * 4       # ring only: two chunks of 64
     assert B.moe_rswa_workspace_bytes(2, 288) >= 2 * 10 * 7 * 132 * 4
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_pack_dense_ffn_layout(lib, bits):
+    """The dense MLP code buffer as include/moe_dense.h describes it: gate | up
+    | down rows, int8 one code per byte, int4 element 2j in the low nibble."""
+    rng = np.random.default_rng(7 + bits)
+    inter = 128
+    lo, hi = (-8, 8) if bits == 4 else (-128, 128)
+    g = rng.integers(lo, hi, (inter, 1280), dtype=np.int8)
+    u = rng.integers(lo, hi, (inter, 1280), dtype=np.int8)
+    d = rng.integers(lo, hi, (1280, inter), dtype=np.int8)
+    g[0, :4] = [lo, hi - 1, 0, -1]
+    out = B.moe_pack_dense_ffn(g, u, d, bits)
+    assert out.size == B.load().moe_dense_ffn_code_bytes(bits, inter) == 3 * inter * 1280 * bits // 8
+    parts = np.split(out, 3)
+    for part, m in zip(parts, (g, u, d)):
+        flat = m.reshape(-1).astype(np.int64)
+        if bits == 8:
+            got = part.view(np.int8).astype(np.int64)
+        else:
+            low, high = part & 0x0F, part >> 4
+            dec = np.empty(flat.size, np.int64)
+            dec[0::2] = np.where(low >= 8, low.astype(np.int64) - 16, low)
+            dec[1::2] = np.where(high >= 8, high.astype(np.int64) - 16, high)
+            got = dec
+        np.testing.assert_array_equal(got, flat)
+
+
+def test_pack_dense_ffn_rejects(lib):
+    inter = 64
+    g = np.zeros((inter, 1280), np.int8)
+    u = np.zeros((inter, 1280), np.int8)
+    d = np.zeros((1280, inter), np.int8)
+    out = np.zeros(3 * inter * 1280, np.uint8)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert lib.moe_pack_dense_ffn(p(g), p(u), p(d), 4, inter, p(out)) == 0
+    g[3, 5] = 8                                   # out of the int4 range
+    assert lib.moe_pack_dense_ffn(p(g), p(u), p(d), 4, inter, p(out)) == 3
+    assert lib.moe_pack_dense_ffn(p(g), p(u), p(d), 8, inter, p(out)) == 0
+    assert lib.moe_pack_dense_ffn(p(g), p(u), p(d), 2, inter, p(out)) == 3
+    assert lib.moe_pack_dense_ffn(p(g), p(u), p(d), 8, 96, p(out)) == 2
+    assert lib.moe_pack_dense_ffn(None, p(u), p(d), 8, inter, p(out)) == 1
+    assert lib.moe_dense_ffn_code_bytes(4, 6848) == 3 * 6848 * 640 and lib.moe_dense_ffn_code_bytes(3, 64) == 0
