@@ -2110,8 +2110,9 @@ __global__ __launch_bounds__(GT) void grouped_down_kernel(GroupedArgs a) {
 // gate and up for columns 16w..16w+15 of them (n-subtile 8cb + w of both
 // matrices) and writes h = SiLU(gate) * up.  Software pipeline over K stages of 128: the packed B
 // tiles and their group scales are fetched D stages ahead into a register
-// ring, A two stages ahead into registers and one stage ahead into a double
-// buffer in LDS, so that the memory latency hides behind the MFMA work.
+// ring, A two stages ahead (one in registers beyond the one in a double buffer
+// in LDS), so that memory latency hides behind the MFMA work and behind the
+// second workgroup on the compute unit.
 // G = Q4K: the two-level format.  The codes are the int4 tiles of q - 8 and
 // each 32-column sub-block adds beta * X to its scaled product (X = the sum of
 // the row's inputs over the sub-block, formed while A is staged; s and beta
@@ -2124,17 +2125,22 @@ __device__ __forceinline__ void gateup_small_body(const GroupedArgs& a, int bid)
   constexpr int KB = kb_cols(BITS), NKB = H / KB, NB = KS / KB, NSTAGE = H / KS, MS = MTL / 16;
   constexpr int CPG = GG / 32, GPS = KS / GG, NG = H / GG;
   constexpr int NSB = H / Q4K_SB;          // two-level records per gate/up row
-  // B stages in flight, and A stages fetched ahead into registers (AR - 1 of
-  // them beyond the one in LDS)
-  constexpr int D = GG == 32 ? 2 : (BITS == 4 ? 4 : 3);
-  constexpr int AR = GG == 32 ? 2 : 3;
-  // With 32-column scale groups (G = 32 and the two-level format) every K
-  // step is its own scale group, and a fully unrolled stage loop lets the
-  // compiler hoist matrix-core products far ahead of their scale multiply and
-  // spill them to scratch: there the stages run in blocks of 2 with a loop
-  // between the blocks and 2-deep B and A rings (no scratch; blocks of 6 with
-  // 3-deep rings spilled up to 0.8 KiB per lane and ran 2.3-2.6x slower).
-  constexpr int SB = GG == 32 ? 2 : NSTAGE;
+  // B stages in flight (D), and A stages fetched ahead into registers (AR - 1
+  // of them beyond the one in LDS); the stages run in blocks of SB with a
+  // loop between the blocks.  Blocks of 2 stages with 2-deep B and A rings
+  // keep every G >= 64 kernel within 128 VGPRs, so that two workgroups share
+  // a compute unit and each hides the other's memory waits: the fully
+  // unrolled stage loop with 3- and 4-deep rings took 150-250 VGPRs (one
+  // workgroup per CU), and measured slower (128-stream step 0.816 against
+  // 0.760 ms, 256 streams 1.002 against 0.932 ms, 273-token prefill 76.9
+  // against 76.2 us).  With 32-column scale groups (G = 32 and the two-level
+  // format) every K step is its own scale group; there a fully unrolled loop
+  // also let the compiler hoist matrix-core products far ahead of their scale
+  // multiply and spill them (blocks of 6 with 3-deep rings spilled up to 0.8
+  // KiB per lane and ran 2.3-2.6x slower).
+  constexpr int D = 2;
+  constexpr int AR = 2;
+  constexpr int SB = 2;
   static_assert((SB % D == 0 && SB % AR == 0 && SB % 2 == 0) || SB == NSTAGE, "ring slots fixed within a block");
   static_assert(!K4 || (SB % 2 == 0 && Q4K_SB == 2 * KS), "a stage is a fixed half of a super-block");
   constexpr bool F32 = SPLIT;
@@ -2369,12 +2375,12 @@ __device__ __forceinline__ void down_small_body(const GroupedArgs& a, int bid) {
   constexpr int NSW = NSUB / 2;             // n-subtiles per wave (half a row tile)
   constexpr int CPG = GG / 32, GPS = KS / GG, NSTAGE = INTER / KS / KSPLIT;
   static_assert((INTER / KS) % KSPLIT == 0, "K halves of whole stages");
-  // B stages in flight, A stages ahead (as in gateup_small_body), and the
-  // stage block: the whole K range unrolled, or with 32-column scale groups
-  // blocks of 2 stages with a loop between them (no scratch)
-  constexpr int D = GG == 32 ? 2 : 4;
-  constexpr int AR = GG == 32 ? 2 : 3;
-  constexpr int SB = GG == 32 ? 2 : NSTAGE;
+  // B stages in flight, A stages ahead and blocks of 2 stages with a loop
+  // between them, as in gateup_small_body (two workgroups per CU for G >= 64,
+  // no scratch)
+  constexpr int D = 2;
+  constexpr int AR = 2;
+  constexpr int SB = 2;
   static_assert((SB % D == 0 && SB % AR == 0 && SB % 2 == 0) || SB == NSTAGE, "ring slots fixed within a block");
   const int inter = INTER;
   const int kh = bid % KSPLIT, tb = bid / KSPLIT, s0 = kh * NSTAGE;   // K part kh
