@@ -218,9 +218,15 @@ size_t moe_workspace_bytes(int32_t n_tokens);
  * one shared power of two per scale group) and forms exact integer dot
  * products.  Both apply each group scale to the partial sum of its group.
  * Domain of the grouped path: every input element (after the optional
- * RMSNorm, which bounds it by sqrt(1280)) must be below 65504 in magnitude,
- * the f16 range; larger inputs give non-finite outputs there.  The per-token
- * path has no such limit.
+ * RMSNorm, which bounds it by sqrt(1280)) and every element of the SwiGLU
+ * intermediate h = SiLU(gate) * up (the down projection's input, split into
+ * f16 halves the same way) must be below 65504 in magnitude, the f16 range;
+ * beyond it the grouped path gives non-finite outputs for that token.  With
+ * normalised inputs and int4 codes with scales up to 0.02 (|W| <= 0.16),
+ * |gate|, |up| <= 0.16 * 1280 and h stays below 42,000 whatever the input;
+ * int8 codes allow a 16x larger |W|, so there only inputs aligned with the
+ * weights far beyond random ones could leave the range.  The per-token path
+ * has no such limit.
  * Inputs are meant to be finite.  A token whose row holds a NaN or an
  * infinity gets non-finite outputs and weights, but its ids are still six
  * distinct experts in 0..63 (a NaN logit ranks below every number), so no
