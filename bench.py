@@ -960,23 +960,28 @@ def bench_crossover(args):
     """Where the per-token (GEMV) path and the grouped (MFMA) path of
     moe_layer_forward cross: one layer at T tokens through each path (forced),
     for the continuous-batch decode formats (int4 G64 routed, int8 G128
-    shared, f32 input with the norm and residual in the call) and for int4 G32
-    (bf16 input, biased router); 4 weight replicas rotated.  Prints one JSON
-    line with the table (microseconds per layer call)."""
+    shared, f32 input with the norm and residual in the call), for int4 G32
+    (bf16 input, biased router), int8 G128 routed and shared (f32 input),
+    int4 G128 (bf16 input) and the two-level routed format with int8 G128
+    shared (f32 input, norm and residual); 4 weight replicas rotated.  Prints
+    one JSON line with the table (microseconds per layer call)."""
     import numpy as np
     import torch
 
     from quantized_expert_ffn_moe_amd import binding as B
     from synth import WORKLOADS, make_layer, make_tokens
 
-    counts = [1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 48, 64]
+    counts = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 16, 24, 32, 48, 64]
     table = {}
     stream = torch.cuda.Stream()
-    for wi in (5, 2):
+    def fmt(q):
+        return "q4k" if q.group == 256 else f"int{q.bits}g{q.group}"
+
+    for wi in (5, 2, 0, 3, 7):
         wl = WORKLOADS[wi]
         lay = make_layer(wl, 0)
         reps = [B.pack_layer(lay) for _ in range(4)]
-        flags0 = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE if wl.x_dtype == "f32" else 0
+        flags0 = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE if wl.x_dtype == "f32" and wl.n_layers > 1 else 0
         rows = {}
         for T in counts:
             x, bits = make_tokens(wl, n_tokens=T, batch=60)
@@ -993,7 +998,8 @@ def bench_crossover(args):
                                                               stream=stream), stream, args.warmup, args.steps)
                 row[name] = round(ms * 1e3, 2)
             rows[T] = row
-        table[wl.name.split("_")[0] + "_" + ("int4g64_int8g128_f32" if wi == 5 else "int4g32_bf16_biased")] = rows
+        key = f"{wl.name.split('_')[0]}_{fmt(wl.routed)}_{fmt(wl.shared)}_{wl.x_dtype}" + ("_biased" if wi == 2 else "")
+        table[key] = rows
     print(json.dumps({"metric": "moe_layer_forward per-token vs grouped path: us per layer call",
                       "unit": "us", "steps": args.steps, "warmup": args.warmup, "table": table}), flush=True)
 

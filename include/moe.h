@@ -253,7 +253,8 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
  * nothing and frees nothing.
  * n_tokens      0 .. MOE_STATIC_MAX_TOKENS; more returns MOE_E_SHAPE without
  *               enqueueing anything.  MOE_FORCE_DECODE is accepted only up to
- *               5 tokens (MOE_E_SHAPE beyond).
+ *               11 tokens (MOE_E_SHAPE beyond), the largest count any format
+ *               sends to the per-token path by default.
  * All calls on one GPU share that GPU's scratch: two calls whose executions
  * overlap on one GPU (on different streams, or from different threads without
  * ordering) race and give undefined results.  Calls ordered on one stream are

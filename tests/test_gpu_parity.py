@@ -77,19 +77,40 @@ def test_ragged_token_counts_both_paths(lib, T):
     np.testing.assert_array_equal(a[0], b[0])
 
 
-@pytest.mark.parametrize("wi,T", [(5, 5), (5, 6), (2, 5), (2, 6)])
+# the default per-token / grouped switch of each format (the last token count
+# that takes the per-token path; measured crossovers of one layer call)
+SWITCH = {5: 11, 2: 6, 0: 10, 3: 9, 7: 10}
+
+
+@pytest.mark.parametrize("wi,T", [(wi, SWITCH[wi] + d) for wi in (5, 2, 0, 3, 7) for d in (0, 1)])
 def test_default_path_switch(lib, wi, T):
-    """Default flags on both sides of the per-token / grouped switch (5 | 6
-    tokens, the measured crossover): the default call must equal the forced
+    """Default flags on both sides of the per-token / grouped switch of each
+    format (int4 G64 / int8 G128 f32, int4 G32 bf16, int8 G128 f32, int4 G128
+    bf16, two-level / int8 G128 f32): the default call must equal the forced
     call of the path it takes, and both paths match the oracle."""
     from quantized_expert_ffn_moe_amd import binding as B
     say(f"{WORKLOADS[wi].name}: {T} tokens, default path")
     x, xt = tokens(wi, n=T, batch=17)
-    d = run(xt, packed_of(wi, 0))
-    f = run(xt, packed_of(wi, 0), B.MOE_FORCE_DECODE if T <= 5 else B.MOE_FORCE_GROUPED)
-    for u, v in zip(d, f):
-        np.testing.assert_array_equal(u, v)
-    ratio, _ = check_layer(x, layer_of(wi, 0), *d)
+    flags = B.MOE_NORM_INPUT | B.MOE_ACCUMULATE if WORKLOADS[wi].n_layers > 1 else 0
+    if flags:
+        # the chained formats: the layer as a decoder calls it (norm and residual in the call)
+        y0 = torch.from_numpy(x.astype(np.float32)).cuda()
+        outs = []
+        for f in (0, B.MOE_FORCE_DECODE if T <= SWITCH[wi] else B.MOE_FORCE_GROUPED):
+            ids, w, y = B.layer(y0, packed_of(wi, 0), flags | f, y=y0.clone())
+            torch.cuda.synchronize()
+            outs.append((ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()))
+        for u, v in zip(*outs):
+            np.testing.assert_array_equal(u, v)
+        z = O.rmsnorm(x, NORM_EPS)
+        ids, w, y = outs[0]
+        ratio, _ = check_layer(z, layer_of(wi, 0), ids, w, y - x.astype(np.float32))
+    else:
+        d = run(xt, packed_of(wi, 0))
+        f = run(xt, packed_of(wi, 0), B.MOE_FORCE_DECODE if T <= SWITCH[wi] else B.MOE_FORCE_GROUPED)
+        for u, v in zip(d, f):
+            np.testing.assert_array_equal(u, v)
+        ratio, _ = check_layer(x, layer_of(wi, 0), *d)
     say(f"  err/rms {ratio:.2e}")
 
 
