@@ -79,7 +79,11 @@ enum {
   MOE_NORM_BF16 = 4u,
   /* Force the per-token GEMV path (at most 64 tokens) / the grouped MFMA
      path regardless of the token count (both give the same result up to fp32
-     rounding order). */
+     rounding order).  Without either flag a call takes the per-token path up
+     to a token count that depends on the routed format and the input type,
+     the measured crossover of the two paths: 6 for 32-column groups, 10 for
+     int8 codes and the two-level format, 9 for int4 G64 / G128 with a bf16
+     expert input and 11 with an f32 one; the grouped path beyond. */
   MOE_FORCE_DECODE = 8u,
   MOE_FORCE_GROUPED = 16u
 };
