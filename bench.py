@@ -971,7 +971,7 @@ def bench_crossover(args):
     from quantized_expert_ffn_moe_amd import binding as B
     from synth import WORKLOADS, make_layer, make_tokens
 
-    counts = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 16, 24, 32, 48, 64]
+    counts = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 20, 22, 24, 32, 48, 64]
     table = {}
     stream = torch.cuda.Stream()
     def fmt(q):

@@ -81,9 +81,9 @@ enum {
      path regardless of the token count (both give the same result up to fp32
      rounding order).  Without either flag a call takes the per-token path up
      to a token count that depends on the routed format and the input type,
-     the measured crossover of the two paths: 6 for 32-column groups, 10 for
-     int8 codes and the two-level format, 9 for int4 G64 / G128 with a bf16
-     expert input and 11 with an f32 one; the grouped path beyond. */
+     the measured crossover of the two paths: 6 for 32-column groups, 12 for
+     int8 codes, 16 for the two-level format, 13 for int4 G64 / G128 with a
+     bf16 expert input and 18 with an f32 one; the grouped path beyond. */
   MOE_FORCE_DECODE = 8u,
   MOE_FORCE_GROUPED = 16u
 };
@@ -257,7 +257,7 @@ moe_status_t moe_layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
  * nothing and frees nothing.
  * n_tokens      0 .. MOE_STATIC_MAX_TOKENS; more returns MOE_E_SHAPE without
  *               enqueueing anything.  MOE_FORCE_DECODE is accepted only up to
- *               11 tokens (MOE_E_SHAPE beyond), the largest count any format
+ *               18 tokens (MOE_E_SHAPE beyond), the largest count any format
  *               sends to the per-token path by default.
  * All calls on one GPU share that GPU's scratch: two calls whose executions
  * overlap on one GPU (on different streams, or from different threads without

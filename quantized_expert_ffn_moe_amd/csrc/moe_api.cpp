@@ -380,7 +380,8 @@ moe_status_t layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   const int accumulate = (flags & MOE_ACCUMULATE) != 0;
 
   const bool decode = (flags & MOE_FORCE_DECODE) ||
-                      (!(flags & MOE_FORCE_GROUPED) && T <= decode_switch_t(expert_bits, expert_group, xf != nullptr));
+                      (!(flags & MOE_FORCE_GROUPED) && T <= part_max_t &&
+                       T <= decode_switch_t(expert_bits, expert_group, xf != nullptr));
   if (decode) {
     DecItemsArgs d;
     d.xf = xf; d.xb = xb; d.ids = topk_ids; d.tw = topk_w; d.rw = rw; d.sw = sw; d.part = ws.part;

@@ -18,7 +18,7 @@ constexpr int MT_TINY = 16;  // rows per tile when experts see very few rows eac
 constexpr int SMALL_WAVES = 8; // waves per workgroup of the small tiles (16 gate/up columns or half a down row tile each)
 constexpr int SMALL_TILE_MAX_SLOTS = 64 * 64;   // (token, pick) slots up to which the small tiles run
 constexpr int TINY_TILE_MAX_SLOTS = 64 * 8;     // ... and the 16-row tiles (about 8 rows per expert or fewer)
-constexpr int DECODE_MAX_T = 11; // largest token count any format routes to the GEMV path by default
+constexpr int DECODE_MAX_T = 18; // largest token count any format routes to the GEMV path by default
 constexpr int MAX_T = 8192;      // largest token count of one call
 constexpr int STATIC_MAX_T = 256;                      // largest call of the workspace-free entry point
 constexpr size_t STATIC_SCRATCH_BYTES = (size_t)20 << 20;  // its per-GPU scratch (the carve for 256 tokens fits)
@@ -46,7 +46,7 @@ constexpr int Q4K_SUB = 32;
 // against the grouped path.  f32_in: the grouped path's expert input is f32
 // (two f16 planes on the matrix cores), which moves the crossover up.
 constexpr int decode_switch_t(int rbits, int rgroup, bool f32_in) {
-  return rgroup == 32 ? 6 : rgroup == Q4K ? 10 : rbits == 8 ? 10 : f32_in ? 11 : 9;
+  return rgroup == 32 ? 6 : rgroup == Q4K ? 16 : rbits == 8 ? 12 : f32_in ? 18 : 13;
 }
 constexpr int Q4K_REC = 16;
 __host__ __device__ constexpr int q4k_superblocks(int k) { return (k + Q4K_SB - 1) / Q4K_SB; }

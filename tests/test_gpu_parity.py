@@ -79,7 +79,7 @@ def test_ragged_token_counts_both_paths(lib, T):
 
 # the default per-token / grouped switch of each format (the last token count
 # that takes the per-token path; measured crossovers of one layer call)
-SWITCH = {5: 11, 2: 6, 0: 10, 3: 9, 7: 10}
+SWITCH = {5: 18, 2: 6, 0: 12, 3: 13, 7: 16}
 
 
 @pytest.mark.parametrize("wi,T", [(wi, SWITCH[wi] + d) for wi in (5, 2, 0, 3, 7) for d in (0, 1)])

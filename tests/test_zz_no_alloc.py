@@ -86,7 +86,7 @@ def test_static_entry_matches_workspace_entry_two_calls(lib, wi, counts):
 def test_static_entry_limits(lib):
     from quantized_expert_ffn_moe_amd import binding as B
     p = packed_of(2)
-    for T, flags in ((257, 0), (12, B.MOE_FORCE_DECODE)):
+    for T, flags in ((257, 0), (19, B.MOE_FORCE_DECODE)):
         xt = tokens(2, T, batch=50)
         y = torch.empty(T, 1280, dtype=torch.float32, device="cuda")
         ids = torch.empty(T, 6, dtype=torch.int32, device="cuda")
@@ -96,7 +96,7 @@ def test_static_entry_limits(lib):
     # an empty call enqueues nothing
     y = torch.empty(0, 1280, dtype=torch.float32, device="cuda")
     B.moe_layer_forward_static(tokens(2, 0, batch=51), p, y, y.view(torch.int32)[:, :6], y[:, :6])
-    # the per-token path still runs through it up to 11 tokens
-    xt = tokens(2, 11, batch=52)
+    # the per-token path still runs through it up to 18 tokens
+    xt = tokens(2, 18, batch=52)
     a, b = both(xt, p, B.MOE_FORCE_DECODE)
     assert_same(a, b)
