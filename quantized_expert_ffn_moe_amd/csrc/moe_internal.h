@@ -78,7 +78,7 @@ struct RouterArgs {
   int norm, norm_bf16; float eps;
   void* z;             // [T][H] normalised input (written when norm): f32, or bf16 with norm_bf16
   int32_t* ids; float* w;
-  float* logits;       // [T][E] scratch of the two-pass router (null: one-pass routers only)
+  float* logits;       // [T][E] scratch of the two-pass router (below 1024 tokens)
 };
 
 // Decode items: one item = 32 intermediate columns of one (token, expert):

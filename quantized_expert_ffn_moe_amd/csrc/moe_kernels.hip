@@ -235,82 +235,39 @@ __device__ __forceinline__ void select_top6(float le, int32_t* ids, float* w) {
   }
 }
 
-constexpr int RT_TB = 4;       // tokens per workgroup
-
-__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  __shared__ __attribute__((aligned(16))) float zs[RT_TB][H];          // 20 KB
-  __shared__ float red[RT_TB][4];
-  __shared__ __attribute__((aligned(16))) float lg[RT_TB][E];
-  const int t0 = blockIdx.x * RT_TB;
-  const int nt = min(RT_TB, a.T - t0);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  router_rows<RT_TB, H>(a, t0, &zs[0][0], &red[0][0]);
-  // pass 2: wave w owns experts 16w..16w+15, four at a time; lane = (expert
-  // eg = lane / 16 of the four, column group kk = lane % 16), so one wave load
-  // reads four 256-byte runs of W_r rows; the 16 column groups of each row add
-  // up with DPP in a fixed order.
-  {
-    const int eg = lane >> 4, kk = lane & 15;
-#pragma unroll 1
-    for (int it = 0; it < 4; ++it) {
-      const int e = 16 * wv + 4 * it + eg;
-      const float* wr = a.wr + (size_t)e * H;
-      float acc[RT_TB] = {0.f, 0.f, 0.f, 0.f};
-      float4 w[H / 64];   // the whole row slice in flight at once
-#pragma unroll
-      for (int j = 0; j < H / 64; ++j) w[j] = *(const float4*)(wr + 4 * (16 * j + kk));
-#pragma unroll
-      for (int j = 0; j < H / 64; ++j) {
-        const int k = 4 * (16 * j + kk);
-        const float4 w4 = w[j];
-#pragma unroll
-        for (int t = 0; t < RT_TB; ++t) {
-          const float4 z4 = *(const float4*)&zs[t][k];
-          acc[t] += w4.x * z4.x + w4.y * z4.y + w4.z * z4.z + w4.w * z4.w;
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < RT_TB; ++t) {
-        const float v = group_sum<16>(acc[t]);
-        if (kk == 0) lg[t][e] = v + (a.bias ? a.bias[e] : 0.f);
-      }
-    }
-  }
-  __syncthreads();
-  // selection: wave = token, lane = expert
-  if (wv < nt) select_top6(lg[wv][lane], a.ids + (size_t)(t0 + wv) * TOPK, a.w + (size_t)(t0 + wv) * TOPK);
-}
-
 // ---------------------------------------------------------------------------
-// Two-pass router for a few hundred tokens: the logits pass splits the experts
-// over four workgroups per 4 tokens (each reads a quarter of W_r, 80 KB, from
-// L2, so every compute unit has work and none streams the whole matrix), and
-// a selection pass turns each token's 64 logits into its top 6.
-// Logits pass: wave w of workgroup (bx, by) owns experts 16 by + 4 w .. + 3;
+// Two-pass router up to a thousand tokens: the logits pass splits the experts
+// over sixteen workgroups per 4 tokens (each reads one sixteenth of W_r, 20 KB,
+// so every compute unit has work and none streams the whole matrix), and a
+// selection pass turns each token's 64 logits into its top 6.
+// Logits pass: wave w of workgroup (bx, by) owns experts 4 EPW by + EPW w ..;
 // lane l owns the columns 4 (64 j + l) .. + 3 (j < 5) and keeps its z values
 // in registers, its W_r values in flight all at once; every (expert, token)
 // sum is then added across the wave in a fixed order.  The workgroups with
 // by = 0 write z.
 // ---------------------------------------------------------------------------
 constexpr int RS_TB = 4;       // tokens per workgroup
-constexpr int RS_EW = 16;      // experts per workgroup
 
+// EPW experts per wave (4 EPW per workgroup, E / (4 EPW) workgroups per
+// 4-token block): each workgroup reads 20 EPW KB of W_r.  The sums are the
+// same for every EPW (per lane in a fixed order, then across the wave).
+template <int EPW>
 __global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
   __shared__ __attribute__((aligned(16))) float zs[RS_TB][H];
   __shared__ float red[RS_TB][4];
   const int t0 = blockIdx.x * RS_TB;
   const int nt = min(RS_TB, a.T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int e0 = RS_EW * blockIdx.y + 4 * wv;
-  float4 w[4][H / 256];
+  const int e0 = 4 * EPW * blockIdx.y + EPW * wv;
+  float4 w[EPW][H / 256];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
+  for (int e = 0; e < EPW; ++e)
 #pragma unroll
     for (int j = 0; j < H / 256; ++j) w[e][j] = *(const float4*)(a.wr + (size_t)(e0 + e) * H + 4 * (64 * j + lane));
   router_rows<RS_TB, H>(a, t0, &zs[0][0], &red[0][0], blockIdx.y == 0);
-  float acc[4][RS_TB];
+  float acc[EPW][RS_TB];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
+  for (int e = 0; e < EPW; ++e)
 #pragma unroll
     for (int t = 0; t < RS_TB; ++t) acc[e][t] = 0.f;
 #pragma unroll
@@ -319,19 +276,19 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
     for (int t = 0; t < RS_TB; ++t) {
       const float4 z4 = *(const float4*)&zs[t][4 * (64 * j + lane)];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < EPW; ++e)
         acc[e][t] += w[e][j].x * z4.x + w[e][j].y * z4.y + w[e][j].z * z4.z + w[e][j].w * z4.w;
     }
   float mine = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
+  for (int e = 0; e < EPW; ++e)
 #pragma unroll
     for (int t = 0; t < RS_TB; ++t) {
       const float v = wave_sum(acc[e][t]);
       if (lane == e * RS_TB + t) mine = v;
     }
   const int e = lane / RS_TB, t = lane % RS_TB;
-  if (lane < 4 * RS_TB && t < nt)
+  if (lane < EPW * RS_TB && t < nt)
     a.logits[(size_t)(t0 + t) * E + e0 + e] = mine + (a.bias ? a.bias[e0 + e] : 0.f);
 }
 
@@ -1315,8 +1272,8 @@ __global__ void zero_words_kernel(uint32_t* p, size_t n) {
 // Wave w computes the 16 x 16 tile of experts 16w .. 16w + 15: lane (r, q)
 // feeds token r / expert 16w + r with inputs kb + 4q + j of each 16-wide K
 // step (component j of a float4), so one float4 of z (LDS) and one of W_r
-// (global, L2-resident) per lane feed four MFMAs.  Pass 1 and the selection
-// are those of router_kernel.
+// (global, L2-resident) per lane feed four MFMAs.  Pass 1 (router_rows) is
+// that of the two-pass router; the selection is select_top6 per token.
 // ---------------------------------------------------------------------------
 constexpr int RM_TB = 16;
 constexpr int RM_ROW = H + 4;   // padded z rows: the 16 rows an MFMA operand read touches hit distinct banks
@@ -2676,18 +2633,24 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, void* z, i
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-constexpr int RS_MIN_T = 8, RS_MAX_T = 1024;
+constexpr int RS_MAX_T = 1024;
+// experts per wave of the logits pass.  Measured: one expert per wave (16
+// workgroups of 20 KB of W_r per 4 tokens) against four (4 workgroups of 80
+// KB): one per-token layer call of 1 token 17.7 -> 16.2 us, 16 tokens 52.3 ->
+// 50.7 us, 128-stream step 0.762 -> 0.750 ms, 32 pages 41.3 -> 40.0 us, 273-token
+// prefill equal.  The one-pass router it replaced below 8 tokens (one
+// workgroup per 4 tokens streaming all 327 KB of W_r) took 12.6 us at 1 token.
+constexpr int RS_EPW = 1;
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
-  // measured: 4-token VALU workgroups win up to about a thousand tokens, where
-  // re-reading W_r per workgroup starts to dominate and the 16-token MFMA
+  // measured: the two-pass router wins up to about a thousand tokens, where
+  // re-reading W_r per 4-token block starts to dominate and the 16-token MFMA
   // workgroups take over (2184 tokens: 25 us per 11-layer step faster)
-  if (a.logits && a.T >= RS_MIN_T && a.T < RS_MAX_T) {
-    hipLaunchKernelGGL(router_logits_kernel, dim3((a.T + RS_TB - 1) / RS_TB, E / RS_EW), dim3(256), 0, s, a);
+  if (a.T < RS_MAX_T) {
+    hipLaunchKernelGGL(router_logits_kernel<RS_EPW>, dim3((a.T + RS_TB - 1) / RS_TB, E / (4 * RS_EPW)), dim3(256), 0,
+                       s, a);
     hipLaunchKernelGGL(router_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
-  } else if (a.T >= 1024) {
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((a.T + RM_TB - 1) / RM_TB), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(router_kernel, dim3((a.T + RT_TB - 1) / RT_TB), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((a.T + RM_TB - 1) / RM_TB), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
