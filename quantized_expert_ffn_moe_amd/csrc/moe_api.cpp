@@ -368,7 +368,6 @@ moe_status_t layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
   ra.wr = router_w; ra.bias = router_b;
   ra.norm = norm; ra.norm_bf16 = (flags & MOE_NORM_BF16) != 0; ra.eps = 1e-6f;
   ra.z = ws.z; ra.ids = topk_ids; ra.w = topk_w; ra.logits = ws.logits;
-  if (launch_router(ra, s) != hipSuccess) return MOE_E_HIP;
 
   // input rows of the experts: the normalised z (f32, or bf16 when rounded to
   // bf16, which the grouped path then feeds to the MFMAs without a lo half)
@@ -383,14 +382,19 @@ moe_status_t layer_forward(const void* x, int32_t x_dtype, int32_t n_tokens,
                       (!(flags & MOE_FORCE_GROUPED) && T <= part_max_t &&
                        T <= decode_switch_t(expert_bits, expert_group, xf != nullptr));
   if (decode) {
+    // few tokens: the items select their own picks from the logits (no
+    // selection launch)
+    const bool self_select = T <= DEC_SELF_SELECT_MAX_T;
+    if (launch_router(ra, s, !self_select) != hipSuccess) return MOE_E_HIP;
     DecItemsArgs d;
-    d.xf = xf; d.xb = xb; d.ids = topk_ids; d.tw = topk_w; d.rw = rw; d.sw = sw; d.part = ws.part;
+    d.xf = xf; d.xb = xb; d.logits = self_select ? ws.logits : nullptr; d.ids = topk_ids; d.tw = topk_w; d.rw = rw; d.sw = sw; d.part = ws.part;
     if (launch_dec_items(d, T, s) != hipSuccess) return MOE_E_HIP;
     DecReduceArgs rd;
     rd.part = ws.part; rd.y = y; rd.accumulate = accumulate;
     if (launch_dec_reduce(rd, T, s) != hipSuccess) return MOE_E_HIP;
     return MOE_OK;
   }
+  if (launch_router(ra, s) != hipSuccess) return MOE_E_HIP;
 
   // tile shape: 32-row tiles while the experts see few rows each (about 64 or
   // fewer on average), 64-row tiles beyond

@@ -90,9 +90,19 @@ constexpr int R_ITEMS = TOPK * (I / SLICE);       // 168
 constexpr int S_ITEMS = IS / SLICE;               // 56
 constexpr int N_ITEMS = R_ITEMS + S_ITEMS;        // 224 per token
 
+// Largest per-token call whose items select their own picks.  Measured: the
+// selection launch saved (one token 16.2 -> 14.1 us, four 23.7 -> 22.5 us for
+// int4 G64 / int8 G128) outweighs the selection each item then runs before its
+// weight loads up to 4 tokens; from 8 tokens on, with several items per CU,
+// it does not (16 tokens 50.8 -> 53.5 us).
+constexpr int DEC_SELF_SELECT_MAX_T = 4;
 struct DecItemsArgs {
   const float* xf; const uint16_t* xb;  // layer input rows (f32 or bf16), exactly one non-null
-  const int32_t* ids; const float* tw;  // routing [T][6]
+  // [T][E] router logits: every routed item selects its own pick and each
+  // token's first item writes ids / tw; null: ids / tw come from the
+  // selection launch
+  const float* logits;
+  int32_t* ids; float* tw;              // routing [T][6]
   QW rw, sw;
   float* part;                          // [T][N_ITEMS][H]
 };
@@ -234,7 +244,9 @@ constexpr int PJ_NORM_MAX_T = 4;
 // lo = bf16_rne(x - hi); 4 bytes per element, like the f32 row.
 hipError_t launch_proj(const ProjArgs& p, hipStream_t s);
 
-hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+// Router launches.  select = false (below 1024 tokens only): the logits pass
+// alone, for the per-token path, whose items select their picks themselves.
+hipError_t launch_router(const RouterArgs& a, hipStream_t s, bool select = true);
 hipError_t launch_dec_items(const DecItemsArgs& a, int T, hipStream_t s);
 hipError_t launch_dec_reduce(const DecReduceArgs& a, int T, hipStream_t s);
 hipError_t launch_chain(const ChainArgs& a, hipStream_t s);

@@ -246,6 +246,27 @@ __device__ __forceinline__ void select_top6(float le, int32_t* ids, float* w) {
 // sum is then added across the wave in a fixed order.  The workgroups with
 // by = 0 write z.
 // ---------------------------------------------------------------------------
+// Pick pj (0..5) of select_top6 for one token, lane = expert: the same rounds
+// and arithmetic, so the id and the weight are those select_top6 writes.
+// Returns the wave-uniform expert id; *w gets its softmax probability.
+__device__ __forceinline__ int select_pick(float le, int pj, float* w) {
+  const int lane = threadIdx.x & 63;
+  const float mx = wave_max(le);
+  const float ex = expf(le - mx);
+  const float sm = wave_sum(ex);
+  const float key = le == le ? le : -__builtin_inff();
+  bool picked = false;
+  int ej = 0;
+  for (int j = 0; j <= pj; ++j) {
+    const float m = wave_max(picked ? -__builtin_inff() : key);
+    const uint64_t hit = __ballot(!picked && key == m);
+    ej = (int)__builtin_ctzll(hit);
+    if (lane == ej) picked = true;
+  }
+  *w = lane_value(ex / sm, ej);
+  return ej;
+}
+
 constexpr int RS_TB = 4;       // tokens per workgroup
 
 // EPW experts per wave (4 EPW per workgroup, E / (4 EPW) workgroups per
@@ -818,13 +839,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int t = blockIdx.x / N_ITEMS, item = blockIdx.x % N_ITEMS;
   const int tid = threadIdx.x;
   float* out = a.part + ((size_t)t * N_ITEMS + item) * H;
+  // with a.logits (calls of at most DEC_SELF_SELECT_MAX_T tokens): the token's
+  // router logits (lane = expert), requested with the input row
+  const bool self_select = a.logits != nullptr;
+  const float le = self_select && item < R_ITEMS ? a.logits[(size_t)t * E + (tid & 63)] : 0.f;
   for (int k = tid; k < H; k += 512) z[k] = a.xf ? a.xf[(size_t)t * H + k] : bf16_to_f32(a.xb[(size_t)t * H + k]);
   __syncthreads();
   if (item < R_ITEMS) {
     const int p = item / (I / SLICE), J = item % (I / SLICE);
-    const int e = a.ids[(size_t)t * TOPK + p];
+    float coef;
+    int e;
+    if (self_select) {
+      // every wave selects the item's pick itself (no selection launch); the
+      // first item of each token reports the token's six picks
+      if (item == 0 && tid < 64) select_top6(le, a.ids + (size_t)t * TOPK, a.tw + (size_t)t * TOPK);
+      e = select_pick(le, p, &coef);
+    } else {
+      e = a.ids[(size_t)t * TOPK + p];
+      coef = a.tw[(size_t)t * TOPK + p];
+    }
     run_item_g<BR, (QK & 1) != 0>(a.rw.group, a.rw.q + (size_t)e * a.rw.e_bytes, a.rw.s + (size_t)e * a.rw.e_scales, I, J, z,
-                          a.tw[(size_t)t * TOPK + p], out, L);
+                          coef, out, L);
   } else {
     run_item_g<BS, (QK & 2) != 0>(a.sw.group, a.sw.q, a.sw.s, IS, item - R_ITEMS, z, 1.0f, out, L);
   }
@@ -2641,14 +2676,14 @@ constexpr int RS_MAX_T = 1024;
 // prefill equal.  The one-pass router it replaced below 8 tokens (one
 // workgroup per 4 tokens streaming all 327 KB of W_r) took 12.6 us at 1 token.
 constexpr int RS_EPW = 1;
-hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
+hipError_t launch_router(const RouterArgs& a, hipStream_t s, bool select) {
   // measured: the two-pass router wins up to about a thousand tokens, where
   // re-reading W_r per 4-token block starts to dominate and the 16-token MFMA
   // workgroups take over (2184 tokens: 25 us per 11-layer step faster)
   if (a.T < RS_MAX_T) {
     hipLaunchKernelGGL(router_logits_kernel<RS_EPW>, dim3((a.T + RS_TB - 1) / RS_TB, E / (4 * RS_EPW)), dim3(256), 0,
                        s, a);
-    hipLaunchKernelGGL(router_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+    if (select) hipLaunchKernelGGL(router_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(router_mfma_kernel, dim3((a.T + RM_TB - 1) / RM_TB), dim3(256), 0, s, a);
   }
